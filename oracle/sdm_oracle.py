@@ -1,0 +1,273 @@
+"""Plain, slow, fp64 CPU oracle of the Sparse Delta Memory (SDM) forward path.
+
+TEST INFRASTRUCTURE.  Only the tests, the package's smoke check and the
+benchmark's CPU-baseline leg may import or run this module.  It shares no code
+with the HIP path: it takes plain numpy arrays, converts them to fp64 exactly,
+and follows the method's steps one at a time.  It is never tuned for speed.
+
+Sources (the method has no published code; these web pages define it):
+  [rainbus]  "稀疏增量记忆：通过稀疏性扩展线性RNN的状态 / Sparse Delta Memory:
+             Scaling the State of Linear RNNs through Sparsity",
+             paper.rainbus.top/paper/2607.07386 -- the method paragraph, which
+             states the four steps (sparse key selection, gated delta write,
+             sparse read, normalisation + gating + head mixing) in formulas.
+  [analysis] "用稀疏内存把线性RNN的状态放大1000倍：Meta SDM 在 8B 规模反超 Full
+             Attention", ai-paper-analysis.pages.dev -- sections "步骤 1" to
+             "步骤 4" and Figure 2 (layer diagram).
+  [163]      m.163.com article on arXiv 2607.07386 -- section 二 (product-key
+             "outer sum" addressing; write = forget gate + delta rule; read =
+             weighted sum; unselected slots untouched).
+
+Readings taken where the pages are silent (each listed in the design notes):
+  * outer SUM of the two half-scores, slot id = i*n + j with i from the first
+    half and j from the second;
+  * the selection order is (score descending, slot id ascending); returned ids
+    are ascending, weights aligned with them;
+  * sparse key/query values k^(i), q^(i) = softmax over the selected scores;
+  * alpha and beta are one scalar per (token, head); the write happens before
+    the read of the same token; unselected slots are never touched;
+  * RMSNorm over d_v with epsilon eps and weight gamma, then the gate
+    activation (sigmoid unless stated) multiplies element-wise;
+  * the output projection W_o is not part of this path.
+
+Pins: every function here is checked by tests/test_oracle_pins.py against
+hand-worked fixtures (tests/golden/), closed forms, exact rational arithmetic
+and brute force.  No function of this module is "parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F64 = np.float64
+
+# gate activations for the output gate vector
+GATE_NONE, GATE_SIGMOID, GATE_SILU = 0, 1, 2
+
+
+# ----------------------------------------------------------------------------
+# Step 1a: input projections.  [rainbus] method paragraph, step 1: W_k and W_q
+# map x_t in R^d to R^{2 sqrt(N)}; [analysis] "步骤 1" and the isoFLOP section
+# (W_v).  One dense product Y = x W_proj^T covers every projection of a head;
+# per head its P = 4n + 2 d_v + 2 columns are, in order,
+#   [write half 1 (n) | write half 2 (n) | read half 1 (n) | read half 2 (n) |
+#    value v (d_v) | output-gate pre-activation (d_v) | forget pre-gate a |
+#    input pre-gate b].
+# ----------------------------------------------------------------------------
+def project(x, w_proj):
+    """Y = x @ W_proj^T in fp64.  x [..., d], w_proj [H*P, d] -> [..., H*P]."""
+    return np.asarray(x, F64) @ np.asarray(w_proj, F64).T
+
+
+def split_heads(Y, H: int, n: int, d_v: int):
+    """Split Y [..., H*P] into the per-head pieces listed above."""
+    P = 4 * n + 2 * d_v + 2
+    Y = np.asarray(Y, F64)
+    Yh = Y.reshape(Y.shape[:-1] + (H, P))
+    o = 4 * n
+    return dict(
+        kw1=Yh[..., 0:n], kw2=Yh[..., n:2 * n],
+        kr1=Yh[..., 2 * n:3 * n], kr2=Yh[..., 3 * n:4 * n],
+        v=Yh[..., o:o + d_v], g=Yh[..., o + d_v:o + 2 * d_v],
+        a=Yh[..., o + 2 * d_v], b=Yh[..., o + 2 * d_v + 1],
+    )
+
+
+# ----------------------------------------------------------------------------
+# Step 2 gates.  [rainbus] step 2 and [analysis] "步骤 2":
+#   alpha_t = exp(-A * softplus(W_a x_t + b_dt))   (per-head forget gate)
+#   beta_t  = sigma(W_b x_t)                        (input gate)
+# ----------------------------------------------------------------------------
+def softplus(z):
+    z = np.asarray(z, F64)
+    return np.maximum(z, 0.0) + np.log1p(np.exp(-np.abs(z)))
+
+
+def sigmoid(z):
+    z = np.asarray(z, F64)
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def forget_gate(a, A, b_dt):
+    """alpha = exp(-A * softplus(a + b_dt)); A and b_dt broadcast over heads."""
+    return np.exp(-np.asarray(A, F64) * softplus(np.asarray(a, F64) + np.asarray(b_dt, F64)))
+
+
+def input_gate(b):
+    return sigmoid(b)
+
+
+def gate_activation(g, kind: int = GATE_SIGMOID):
+    g = np.asarray(g, F64)
+    if kind == GATE_NONE:
+        return g
+    if kind == GATE_SIGMOID:
+        return sigmoid(g)
+    if kind == GATE_SILU:
+        return g * sigmoid(g)
+    raise ValueError(f"unknown gate activation {kind}")
+
+
+# ----------------------------------------------------------------------------
+# Step 1b: sparse slot selection.  [rainbus] step 1: the two halves of a
+# pre-index vector form N = n*n scores by an outer sum, one per memory slot;
+# top-W of the write scores and top-R of the read scores pick the slots.
+# [analysis] "步骤 1" and [163] section 二 state the same outer-sum addressing.
+# The product-key shortcut reaches exactly this set, so the oracle uses the
+# plain definition: score every slot and take the best `count`.
+# ----------------------------------------------------------------------------
+def slot_scores(half1, half2):
+    """All N outer-sum scores, slot id = i*n + j."""
+    h1 = np.asarray(half1, F64)
+    h2 = np.asarray(half2, F64)
+    return (h1[:, None] + h2[None, :]).reshape(-1)
+
+
+def top_slots(half1, half2, count: int):
+    """Best `count` slots by (score desc, id asc).
+
+    Returns (ids ascending [count] int64, their scores fp64, gap) where gap is
+    the difference between the count-th and (count+1)-th largest scores
+    (inf when every slot is selected).
+    """
+    S = slot_scores(half1, half2)
+    N = S.shape[0]
+    if not 1 <= count <= N:
+        raise ValueError("count must be in [1, N]")
+    if count < N:
+        part = np.partition(S, [N - count - 1, N - count])
+        kth, nxt = part[N - count], part[N - count - 1]
+        gap = float(kth - nxt)
+    else:
+        kth = S.min()
+        gap = float("inf")
+    above = np.flatnonzero(S > kth)
+    ties = np.flatnonzero(S == kth)           # ascending ids: lowest ids win
+    ids = np.concatenate([above, ties[:count - above.size]])
+    ids.sort()
+    return ids.astype(np.int64), S[ids], gap
+
+
+def softmax(s):
+    """Sparse key/query values over the selected scores (temperature 1)."""
+    s = np.asarray(s, F64)
+    e = np.exp(s - s.max())
+    return e / e.sum()
+
+
+def select(half1, half2, count: int):
+    """(ids ascending, softmax weights aligned with ids, gap)."""
+    ids, sc, gap = top_slots(half1, half2, count)
+    return ids, softmax(sc), gap
+
+
+# ----------------------------------------------------------------------------
+# Steps 2-3: the recurrent sparse scan of one (batch, head) memory.
+# [rainbus] step 2: for each selected write slot i, first the forget gate
+#   Mtilde[i] = alpha_t * M_{t-1}[i], then the delta update
+#   M_t[i] = Mtilde[i] + beta_t * k^(i) * (v_t - Mtilde[i]);
+# [analysis] "步骤 2": slots that are not selected keep M_t[i] = M_{t-1}[i].
+# [rainbus] step 3: y_t = sum_{i in I_r} q^(i) M_t[i]  (reads the state after
+# this token's write).
+# ----------------------------------------------------------------------------
+def scan(state0, idx_w, wt_w, idx_r, wt_r, v, alpha, beta):
+    """Walk tokens in order over one memory.
+
+    state0 [N, d_v]; idx_w/wt_w [T, W]; idx_r/wt_r [T, R]; v [T, d_v];
+    alpha, beta [T].  Returns (y_raw [T, d_v], final state [N, d_v]) in fp64.
+    """
+    M = np.array(state0, dtype=F64, copy=True)
+    idx_w = np.asarray(idx_w)
+    idx_r = np.asarray(idx_r)
+    wt_w = np.asarray(wt_w, F64)
+    wt_r = np.asarray(wt_r, F64)
+    v = np.asarray(v, F64)
+    alpha = np.asarray(alpha, F64)
+    beta = np.asarray(beta, F64)
+    T = idx_w.shape[0]
+    y = np.zeros((T, M.shape[1]), F64)
+    for t in range(T):
+        rows = idx_w[t]
+        assert np.unique(rows).size == rows.size, "write slots of one token must be distinct"
+        m_tilde = alpha[t] * M[rows]                                   # forget gate
+        M[rows] = m_tilde + (beta[t] * wt_w[t])[:, None] * (v[t][None, :] - m_tilde)
+        y[t] = wt_r[t] @ M[idx_r[t]]                                   # sparse read
+    return y, M
+
+
+# ----------------------------------------------------------------------------
+# Step 4 (without the head-mixing projection): [rainbus] step 4 and
+# [analysis] "步骤 4": RMS-Norm of the read vector, then element-wise gating.
+# ----------------------------------------------------------------------------
+def rms_norm_gate(y, gamma, gate, eps: float):
+    y = np.asarray(y, F64)
+    r = 1.0 / np.sqrt(np.mean(y * y, axis=-1, keepdims=True) + eps)
+    return y * r * np.asarray(gamma, F64) * np.asarray(gate, F64)
+
+
+# ----------------------------------------------------------------------------
+# Whole path.
+# ----------------------------------------------------------------------------
+def pass_a(x, w_proj, A, b_dt, H, n, d_v, W, R, gate_act=GATE_SIGMOID):
+    """Projections, gates and selections for tokens x [..., d].
+
+    Returns a dict of arrays shaped [..., H, *]: idx_w, wt_w, gap_w, idx_r, wt_r,
+    gap_r, v, g (activated), alpha, beta, and the four half-score blocks.
+    """
+    parts = split_heads(project(x, w_proj), H, n, d_v)
+    lead = parts["a"].shape            # [..., H]
+    out = dict(
+        v=parts["v"], g=gate_activation(parts["g"], gate_act),
+        alpha=forget_gate(parts["a"], np.asarray(A, F64), np.asarray(b_dt, F64)),
+        beta=input_gate(parts["b"]),
+        scores=np.concatenate([parts["kw1"], parts["kw2"], parts["kr1"], parts["kr2"]], axis=-1),
+    )
+    out.update(select_from_scores(out["scores"], n, W, R))
+    assert out["idx_w"].shape[:-1] == lead
+    return out
+
+
+def select_from_scores(scores, n, W, R):
+    """Selections from half-scores [..., 4n] (write half 1|2, read half 1|2)."""
+    scores = np.asarray(scores, F64)
+    lead = scores.shape[:-1]
+    flat = scores.reshape(-1, 4 * n)
+    res = {k: [] for k in ("idx_w", "wt_w", "gap_w", "idx_r", "wt_r", "gap_r")}
+    for s in flat:
+        i, w, gp = select(s[0:n], s[n:2 * n], W)
+        res["idx_w"].append(i); res["wt_w"].append(w); res["gap_w"].append(gp)
+        i, w, gp = select(s[2 * n:3 * n], s[3 * n:4 * n], R)
+        res["idx_r"].append(i); res["wt_r"].append(w); res["gap_r"].append(gp)
+    shp = {"idx_w": (W,), "wt_w": (W,), "gap_w": (), "idx_r": (R,), "wt_r": (R,), "gap_r": ()}
+    return {k: np.array(v).reshape(lead + shp[k]) for k, v in res.items()}
+
+
+def forward_walk(state0, sel, gamma_h, eps):
+    """Scan + norm/gate for one (batch, head) walk given its pass-(a) products.
+
+    sel holds [T, *] arrays for that walk: idx_w, wt_w, idx_r, wt_r, v, g,
+    alpha, beta.  Returns (out [T, d_v], y_raw [T, d_v], final state).
+    """
+    y, M = scan(state0, sel["idx_w"], sel["wt_w"], sel["idx_r"], sel["wt_r"],
+                sel["v"], sel["alpha"], sel["beta"])
+    return rms_norm_gate(y, gamma_h, sel["g"], eps), y, M
+
+
+def forward(x, w_proj, A, b_dt, gamma, state0, H, n, d_v, W, R, eps=1e-6,
+            gate_act=GATE_SIGMOID):
+    """Full path from x [B, T, d] and state0 [B, H, N, d_v].
+
+    Returns (out [B, T, H, d_v], final state [B, H, N, d_v], pass-(a) dict).
+    """
+    x = np.asarray(x, F64)
+    B, T = x.shape[:2]
+    a = pass_a(x, w_proj, A, b_dt, H, n, d_v, W, R, gate_act)
+    out = np.zeros((B, T, H, d_v), F64)
+    st = np.zeros(np.shape(state0), F64)
+    for b in range(B):
+        for h in range(H):
+            walk = {k: a[k][b, :, h] for k in ("idx_w", "wt_w", "idx_r", "wt_r", "v", "g",
+                                               "alpha", "beta")}
+            o, _, M = forward_walk(state0[b][h], walk, np.asarray(gamma, F64)[h], eps)
+            out[b, :, h] = o
+            st[b, h] = M
+    return out, st, a
