@@ -1,0 +1,208 @@
+/*
+ * sdm.h -- C ABI of the Sparse Delta Memory (SDM) forward path on MI355X (gfx950).
+ *
+ * The method (no published code; defined by these pages):
+ *   [rainbus]  "稀疏增量记忆：通过稀疏性扩展线性RNN的状态 / Sparse Delta Memory: Scaling
+ *              the State of Linear RNNs through Sparsity", paper.rainbus.top, method
+ *              paragraph (steps 1-4 with their formulas);
+ *   [analysis] "用稀疏内存把线性RNN的状态放大1000倍：Meta SDM 在 8B 规模反超 Full
+ *              Attention", ai-paper-analysis.pages.dev, sections "步骤 1" .. "步骤 4",
+ *              Figure 2, and the section on the learned initial state M0;
+ *   [163]      m.163.com article on arXiv 2607.07386, section 二 (outer-sum product-key
+ *              addressing, forget + delta write, weighted sparse read).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer argument is a DEVICE pointer (allocated by the caller, e.g. as a
+ *    torch tensor) unless stated otherwise; `dims` and `sel` structs live in host
+ *    memory.  The library never allocates, frees or keeps device memory, keeps no
+ *    global mutable state, and is reentrant across streams.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  All work is enqueued on it
+ *    asynchronously; no call synchronises the host, allocates, or copies through
+ *    pageable memory, so calls may be captured into a HIP graph.
+ *  - Every argument is validated BEFORE anything is enqueued: a call that returns a
+ *    nonzero status has enqueued nothing and left every output untouched.  Faults
+ *    inside kernels surface at the caller's next synchronisation.  A launch error
+ *    reported by the runtime right after a launch returns SDM_ERR_HIP.
+ *  - Device pointers must be 16-byte aligned (SDM_ERR_ALIGN).
+ *  - Layouts are row-major and contiguous.  Per-token tensors are [B, T, H, ...];
+ *    the state is [B, H, N, d_v] fp32 with N = n*n slots; slot id = i*n + j where i
+ *    indexes the first half-score vector and j the second.
+ *  - B*T == 0 is a valid empty call: SDM_OK, nothing enqueued.
+ *  - NaN or Inf inputs propagate per IEEE in the arithmetic; the selection order of
+ *    NaN scores is unspecified.
+ */
+#ifndef SDM_H
+#define SDM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define SDM_API __attribute__((visibility("default")))
+#else
+#define SDM_API
+#endif
+
+#define SDM_ABI_VERSION 1
+
+/* status codes */
+#define SDM_OK 0
+#define SDM_ERR_NULL (-1)        /* a required pointer is NULL */
+#define SDM_ERR_SHAPE (-2)       /* inconsistent or out-of-range sizes */
+#define SDM_ERR_DTYPE (-3)       /* unknown in_dtype or gate_act */
+#define SDM_ERR_ALIGN (-4)       /* a device pointer is not 16-byte aligned */
+#define SDM_ERR_WORKSPACE (-5)   /* workspace missing or smaller than sdm_workspace_bytes */
+#define SDM_ERR_UNSUPPORTED (-6) /* valid for the method but outside this build's limits */
+#define SDM_ERR_HIP (-7)         /* the HIP runtime reported a launch error */
+
+/* element type of x and W_proj */
+#define SDM_DTYPE_F32 0
+#define SDM_DTYPE_BF16 1
+
+/* activation of the output-gate vector */
+#define SDM_GATE_NONE 0
+#define SDM_GATE_SIGMOID 1
+#define SDM_GATE_SILU 2
+
+/* entry selector for sdm_workspace_bytes */
+#define SDM_ENTRY_SELECT 0
+#define SDM_ENTRY_SCAN 1
+#define SDM_ENTRY_FORWARD 2
+
+/* Limits of this build (SDM_ERR_UNSUPPORTED beyond them). */
+#define SDM_MAX_COUNT 128   /* W and R */
+#define SDM_MAX_HALF 1024   /* n = sqrt(N) */
+
+/*
+ * Sizes of one SDM layer.
+ *   B, T      batch and tokens per sequence (tokens are b*T + t)
+ *   d_model   width of x
+ *   H         heads; each head owns one memory of N = n*n slots of d_v floats per
+ *             batch entry ([analysis] Figure 2; M_t in R^{N x d_v})
+ *   n         half-score length sqrt(N); the pre-index vectors are in R^{2n}
+ *             ([rainbus] step 1: W_k, W_q in R^{d x 2 sqrt(N)})
+ *   W, R      write and read slots per token and head (top-W / top-R);
+ *             1 <= W, R <= min(N, SDM_MAX_COUNT)
+ *   d_v       value width; one of 16, 32, 64, 128, 256
+ *   in_dtype  SDM_DTYPE_F32 or SDM_DTYPE_BF16 (x and W_proj); d_model % 8 == 0
+ *   gate_act  activation of the output gate vector (SDM_GATE_*)
+ *   eps       RMSNorm epsilon (>= 0)
+ *   flags     reserved, must be 0
+ */
+typedef struct sdm_dims {
+  int64_t B, T, d_model;
+  int32_t H, n, W, R, d_v;
+  int32_t in_dtype;
+  int32_t gate_act;
+  float eps;
+  int32_t flags;
+} sdm_dims;
+
+/*
+ * Products of the selection pass, [B, T, H, ...] each (caller-allocated):
+ *   idx_w [.., W] int32  write slot ids, ascending          ([rainbus] step 1, I_w)
+ *   wt_w  [.., W] fp32   sparse key values k^(i), aligned   ([analysis] "步骤 2")
+ *   idx_r [.., R] int32  read slot ids, ascending           (I_r)
+ *   wt_r  [.., R] fp32   sparse query values q^(i)
+ *   v     [.., d_v]      value v_t
+ *   gate  [.., d_v]      activated output-gate vector
+ *   alpha [..]           forget gate exp(-A softplus(W_a x + b_dt))  ([rainbus] step 2)
+ *   beta  [..]           input gate sigma(W_b x)
+ *   scores[.., 4n]       nullable: fp32 half-scores (write half 1 | write half 2 |
+ *                        read half 1 | read half 2)
+ * The weights are the softmax of the selected outer-sum scores; ties in score are
+ * broken by the lower slot id.
+ */
+typedef struct sdm_sel {
+  int32_t* idx_w;
+  float* wt_w;
+  int32_t* idx_r;
+  float* wt_r;
+  float* v;
+  float* gate;
+  float* alpha;
+  float* beta;
+  float* scores;
+} sdm_sel;
+
+/* SDM_ABI_VERSION of the built library. */
+SDM_API int32_t sdm_abi_version(void);
+
+/* Static human-readable text of a status code (never NULL). */
+SDM_API const char* sdm_status_string(int32_t status);
+
+/*
+ * Device workspace, in bytes, that `entry` (SDM_ENTRY_*) needs for these sizes;
+ * 0 when none is needed or the sizes are invalid.  The workspace is scratch owned by
+ * the caller: its contents on entry do not matter and are undefined on return.
+ */
+SDM_API size_t sdm_workspace_bytes(const sdm_dims* dims, int32_t entry);
+
+/*
+ * Selection pass (parallel over tokens): [rainbus] steps 1-2 (projections, the
+ * outer-sum product-key selection of top-W write and top-R read slots, gates) and
+ * [analysis] "步骤 1".
+ *   x       [B*T, d_model]  in_dtype
+ *   w_proj  [H*P, d_model]  in_dtype, P = 4n + 2 d_v + 2; per head the P rows
+ *           produce, in order: write half 1 (n), write half 2 (n), read half 1 (n),
+ *           read half 2 (n), v (d_v), gate pre-activation (d_v), a (1), b (1)
+ *   A, b_dt [H] fp32        forget-gate scale and bias per head
+ *   out     every field but `scores` required; `scores` may be NULL
+ *   ws      >= sdm_workspace_bytes(dims, SDM_ENTRY_SELECT) bytes (may be NULL if 0)
+ * The projection accumulates in fp32 on matrix cores; the outer sums of the two fp32
+ * half-scores are formed in fp64 (exact) before ranking.
+ */
+SDM_API int32_t sdm_select(const sdm_dims* dims, const void* x, const void* w_proj, const float* A,
+                   const float* b_dt, const sdm_sel* out, void* ws, size_t ws_bytes,
+                   void* stream);
+
+/*
+ * Selection from given half-scores (diagnostic entry, same ranking as sdm_select):
+ *   scores [B, T, H, 4n] fp32 -> idx_w/wt_w [B,T,H,W], idx_r/wt_r [B,T,H,R].
+ * Given identical scores, the ids are bit-identical to the fp64 brute-force top-W.
+ */
+SDM_API int32_t sdm_select_from_scores(const sdm_dims* dims, const float* scores, int32_t* idx_w,
+                               float* wt_w, int32_t* idx_r, float* wt_r, void* stream);
+
+/*
+ * Recurrent sparse scan: [rainbus] steps 2-4 without the head-mixing projection.
+ * For each (b, h), tokens t = 0..T-1 in order:
+ *   for each write slot i (weight k):  c = beta_t * k;
+ *       M[i] <- (1 - c) * (alpha_t * M[i]) + c * v_t       (the pages' gated delta
+ *       rule Mtilde + beta k (v - Mtilde), Mtilde = alpha M, rearranged so that c = 1
+ *       stores v_t exactly and alpha = 1, c = 0 leaves M[i] unchanged)
+ *   y_t = sum_{i in I_r} q^(i) M[i]          (after this token's writes)
+ *   out_t = y_t / sqrt(mean(y_t^2) + eps) * norm_w[h] * gate_t
+ * Slots never selected for writing are never written (bit-identical on return).
+ *   in      pass-(a) products (every field but `scores` required)
+ *   norm_w  [H, d_v] fp32 RMSNorm weight, or NULL for ones
+ *   state   [B, H, N, d_v] fp32, IN/OUT: M_0 on entry (e.g. a learned initial state,
+ *           [analysis] section on M0), M_T on return.  Calling with T tokens equals
+ *           calling on consecutive token chunks with the same state buffer.
+ *   out     [B, T, H, d_v] fp32
+ *   y_raw   [B, T, H, d_v] fp32 or NULL: the read vector before normalisation
+ *   ws      >= sdm_workspace_bytes(dims, SDM_ENTRY_SCAN) bytes
+ */
+SDM_API int32_t sdm_scan(const sdm_dims* dims, const sdm_sel* in, const float* norm_w, float* state,
+                 float* out, float* y_raw, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Whole forward path: sdm_select followed by sdm_scan, with the pass-(a) products
+ * kept in the workspace (or in `debug` when given, which must then hold every field;
+ * `debug->scores` may be NULL).  Arguments as in those two calls.
+ *   ws >= sdm_workspace_bytes(dims, SDM_ENTRY_FORWARD) bytes
+ */
+SDM_API int32_t sdm_forward(const sdm_dims* dims, const void* x, const void* w_proj, const float* A,
+                    const float* b_dt, const float* norm_w, float* state, float* out,
+                    const sdm_sel* debug, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDM_H */

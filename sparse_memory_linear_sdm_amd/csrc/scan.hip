@@ -1,0 +1,115 @@
+// Recurrent sparse scan of the SDM layer (the state lives in HBM).
+//
+// Per (batch, head) memory M [N, d_v] and tokens t = 0..T-1 in order
+// ("Sparse Delta Memory" summary on paper.rainbus.top, method paragraph, steps
+// 2-4; ai-paper-analysis.pages.dev, sections "步骤 2" to "步骤 4"):
+//   write: for each selected write slot i with weight k: c = beta_t k,
+//          M[i] <- (1 - c) (alpha_t M[i]) + c v_t     (forget gate, then delta rule)
+//   read:  y_t = sum_{i in I_r} q^(i) M[i]            (after this token's writes)
+//   out:   y_t / sqrt(mean(y_t^2) + eps) * gamma_h * gate_t
+// Unselected slots are never touched.  The slot ids of every token are known
+// before the scan starts (selection pass), so the kernel only moves rows.
+#include "sdm_internal.h"
+
+namespace sdm {
+namespace {
+
+__device__ __forceinline__ float4 f4(float a) { return make_float4(a, a, a, a); }
+
+// One workgroup of 256 threads per (b, h).  A row of d_v floats is handled by
+// LPR = d_v/4 lanes (one float4 each); the G = 256/LPR row groups split the W
+// writes and R reads of a token.  Barriers order the write phase, the read phase
+// and the next token's writes (all accesses stay inside one workgroup, whose
+// waves share the CU's vector L1).
+template <int DV>
+__global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
+  constexpr int LPR = DV / 4;
+  constexpr int G = 256 / LPR;
+  __shared__ float4 red[G][LPR];
+
+  const int tid = threadIdx.x;
+  const int li = tid % LPR;
+  const int grp = tid / LPR;
+  const int64_t bh = blockIdx.x;
+  const int64_t b = bh / a.H;
+  const int h = (int)(bh - b * a.H);
+  float* M = a.state + bh * (int64_t)a.N * DV;
+  const float4 gam = a.norm_w ? reinterpret_cast<const float4*>(a.norm_w + (int64_t)h * DV)[li]
+                              : f4(1.0f);
+
+  for (int64_t t = 0; t < a.T; ++t) {
+    const int64_t tok = (b * a.T + t) * a.H + h;
+    const float al = a.alpha[tok];
+    const float be = a.beta[tok];
+    const float4 vv = reinterpret_cast<const float4*>(a.v + tok * DV)[li];
+    const int32_t* iw = a.idx_w + tok * a.W;
+    const float* ww = a.wt_w + tok * a.W;
+    for (int k = grp; k < a.W; k += G) {
+      const int64_t row = iw[k];
+      const float c = be * ww[k];
+      const float oc = 1.0f - c;
+      float4* p = reinterpret_cast<float4*>(M + row * DV) + li;
+      float4 m = *p;
+      m.x = fmaf(c, vv.x, oc * (al * m.x));
+      m.y = fmaf(c, vv.y, oc * (al * m.y));
+      m.z = fmaf(c, vv.z, oc * (al * m.z));
+      m.w = fmaf(c, vv.w, oc * (al * m.w));
+      *p = m;
+    }
+    __syncthreads();
+    const int32_t* ir = a.idx_r + tok * a.R;
+    const float* wr = a.wt_r + tok * a.R;
+    float4 acc = f4(0.0f);
+    for (int k = grp; k < a.R; k += G) {
+      const int64_t row = ir[k];
+      const float q = wr[k];
+      const float4 m = reinterpret_cast<const float4*>(M + row * DV)[li];
+      acc.x = fmaf(q, m.x, acc.x);
+      acc.y = fmaf(q, m.y, acc.y);
+      acc.z = fmaf(q, m.z, acc.z);
+      acc.w = fmaf(q, m.w, acc.w);
+    }
+    red[grp][li] = acc;
+    __syncthreads();
+    if (grp == 0) {
+      float4 y = red[0][li];
+      for (int g = 1; g < G; ++g) {
+        const float4 o = red[g][li];
+        y.x += o.x;
+        y.y += o.y;
+        y.z += o.z;
+        y.w += o.w;
+      }
+      float ss = y.x * y.x + y.y * y.y + y.z * y.z + y.w * y.w;
+      for (int off = LPR / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off, LPR);
+      const float rn = rsqrtf(ss / (float)DV + a.eps);
+      const float4 gt = reinterpret_cast<const float4*>(a.gate + tok * DV)[li];
+      float4 o;
+      o.x = y.x * rn * gam.x * gt.x;
+      o.y = y.y * rn * gam.y * gt.y;
+      o.z = y.z * rn * gam.z * gt.z;
+      o.w = y.w * rn * gam.w * gt.w;
+      reinterpret_cast<float4*>(a.out + tok * DV)[li] = o;
+      if (a.y_raw) reinterpret_cast<float4*>(a.y_raw + tok * DV)[li] = y;
+    }
+  }
+}
+
+}  // namespace
+
+size_t scan_workspace_bytes(const sdm_dims&) { return 0; }
+
+hipError_t launch_scan(const ScanArgs& a, void*, size_t, hipStream_t s) {
+  const dim3 grid((unsigned)(a.B * a.H));
+  switch (a.d_v) {
+    case 16: hipLaunchKernelGGL(scan_kernel<16>, grid, dim3(256), 0, s, a); break;
+    case 32: hipLaunchKernelGGL(scan_kernel<32>, grid, dim3(256), 0, s, a); break;
+    case 64: hipLaunchKernelGGL(scan_kernel<64>, grid, dim3(256), 0, s, a); break;
+    case 128: hipLaunchKernelGGL(scan_kernel<128>, grid, dim3(256), 0, s, a); break;
+    case 256: hipLaunchKernelGGL(scan_kernel<256>, grid, dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sdm

@@ -1,0 +1,290 @@
+// C ABI of libsdm: argument validation, workspace layout and kernel dispatch.
+// Every check runs before the first enqueue, so a failing call leaves all
+// outputs untouched and needs no GPU to be exercised.
+#include <math.h>
+#include <stdint.h>
+
+#include "sdm_internal.h"
+
+using namespace sdm;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int64_t kScoreChunkBytes = 512ll << 20;  // bound on the scores staging buffer
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Derived {
+  int64_t M;      // token rows B*T
+  int64_t N;      // slots per memory
+  int64_t P;      // projection columns per head
+  int64_t chunk;  // GEMM rows per scores chunk when staging in the workspace
+};
+
+int32_t check_dims(const sdm_dims* d, Derived* out) {
+  if (!d) return SDM_ERR_NULL;
+  if (d->flags != 0) return SDM_ERR_UNSUPPORTED;
+  if (d->in_dtype != SDM_DTYPE_F32 && d->in_dtype != SDM_DTYPE_BF16) return SDM_ERR_DTYPE;
+  if (d->gate_act < SDM_GATE_NONE || d->gate_act > SDM_GATE_SILU) return SDM_ERR_DTYPE;
+  if (d->B < 0 || d->T < 0 || d->d_model < 1 || d->H < 1 || d->n < 1 || d->W < 1 || d->R < 1 ||
+      d->d_v < 1)
+    return SDM_ERR_SHAPE;
+  if (!(d->eps >= 0.0f) || !isfinite(d->eps)) return SDM_ERR_SHAPE;
+  const int64_t N = (int64_t)d->n * d->n;
+  if (d->W > N || d->R > N) return SDM_ERR_SHAPE;
+  if (d->n > SDM_MAX_HALF || d->W > SDM_MAX_COUNT || d->R > SDM_MAX_COUNT)
+    return SDM_ERR_UNSUPPORTED;
+  if (!(d->d_v == 16 || d->d_v == 32 || d->d_v == 64 || d->d_v == 128 || d->d_v == 256))
+    return SDM_ERR_UNSUPPORTED;
+  if (d->d_model % 8 != 0 || d->d_model > (1ll << 30)) return SDM_ERR_UNSUPPORTED;
+  const int64_t P = 4ll * d->n + 2ll * d->d_v + 2;
+  if ((int64_t)d->H * P > (1ll << 30)) return SDM_ERR_UNSUPPORTED;
+  if (d->B > (1ll << 40) || d->T > (1ll << 40) || (d->B > 0 && d->T > (1ll << 40) / d->B))
+    return SDM_ERR_UNSUPPORTED;
+  const int64_t M = d->B * d->T;
+  if (M * d->H * 2 > INT32_MAX) return SDM_ERR_UNSUPPORTED;  // selection grid
+  if ((int64_t)d->B * d->H > INT32_MAX) return SDM_ERR_UNSUPPORTED;
+  if (out) {
+    out->M = M;
+    out->N = N;
+    out->P = P;
+    const int64_t row_bytes = (int64_t)d->H * 4 * d->n * 4;
+    int64_t c = kScoreChunkBytes / row_bytes;
+    c = c < 128 ? 128 : (c / 128) * 128;
+    out->chunk = M < c ? M : c;
+  }
+  return SDM_OK;
+}
+
+// Byte sizes of the pass-(a) products of one call.
+struct ProductSizes {
+  size_t idx_w, wt_w, idx_r, wt_r, v, gate, alpha, beta, total;
+};
+ProductSizes product_sizes(const sdm_dims* d, int64_t M) {
+  ProductSizes s;
+  const size_t th = (size_t)M * d->H;
+  s.idx_w = align_up(th * d->W * 4);
+  s.wt_w = align_up(th * d->W * 4);
+  s.idx_r = align_up(th * d->R * 4);
+  s.wt_r = align_up(th * d->R * 4);
+  s.v = align_up(th * d->d_v * 4);
+  s.gate = align_up(th * d->d_v * 4);
+  s.alpha = align_up(th * 4);
+  s.beta = align_up(th * 4);
+  s.total = s.idx_w + s.wt_w + s.idx_r + s.wt_r + s.v + s.gate + s.alpha + s.beta;
+  return s;
+}
+
+size_t select_ws_bytes(const sdm_dims* d, const Derived& dv, bool have_scores) {
+  if (have_scores || dv.M == 0) return 0;
+  return align_up((size_t)dv.chunk * d->H * 4 * d->n * 4);
+}
+
+int32_t check_sel(const sdm_sel* s, bool need_scores) {
+  if (!s) return SDM_ERR_NULL;
+  const void* req[] = {s->idx_w, s->wt_w, s->idx_r, s->wt_r, s->v, s->gate, s->alpha, s->beta};
+  for (const void* p : req)
+    if (!p) return SDM_ERR_NULL;
+  if (need_scores && !s->scores) return SDM_ERR_NULL;
+  for (const void* p : req)
+    if (!aligned16(p)) return SDM_ERR_ALIGN;
+  if (s->scores && !aligned16(s->scores)) return SDM_ERR_ALIGN;
+  return SDM_OK;
+}
+
+int32_t hip_status(hipError_t e) { return e == hipSuccess ? SDM_OK : SDM_ERR_HIP; }
+
+// Enqueue the selection pass (validated arguments only).
+int32_t run_select(const sdm_dims* d, const Derived& dv, const void* x, const void* w_proj,
+                   const float* A, const float* b_dt, const sdm_sel* out, void* ws,
+                   hipStream_t st) {
+  ProjDst dst;
+  dst.v = out->v;
+  dst.gate = out->gate;
+  dst.alpha = out->alpha;
+  dst.beta = out->beta;
+  dst.A = A;
+  dst.b_dt = b_dt;
+  dst.H = d->H;
+  dst.n = d->n;
+  dst.d_v = d->d_v;
+  dst.P = (int)dv.P;
+  dst.gate_act = d->gate_act;
+  if (out->scores) {  // full-size scores requested: one pass over every row
+    dst.scores = out->scores;
+    dst.scores_row0 = 0;
+    hipError_t e = launch_proj_gemm(*d, x, w_proj, 0, dv.M, dst, st);
+    if (e != hipSuccess) return SDM_ERR_HIP;
+    e = launch_select(*d, out->scores, dv.M, 0, out->idx_w, out->wt_w, out->idx_r, out->wt_r, st);
+    return hip_status(e);
+  }
+  dst.scores = static_cast<float*>(ws);
+  for (int64_t r0 = 0; r0 < dv.M; r0 += dv.chunk) {
+    const int64_t rows = dv.M - r0 < dv.chunk ? dv.M - r0 : dv.chunk;
+    dst.scores_row0 = r0;
+    hipError_t e = launch_proj_gemm(*d, x, w_proj, r0, rows, dst, st);
+    if (e != hipSuccess) return SDM_ERR_HIP;
+    e = launch_select(*d, static_cast<const float*>(ws), rows, r0, out->idx_w, out->wt_w,
+                      out->idx_r, out->wt_r, st);
+    if (e != hipSuccess) return SDM_ERR_HIP;
+  }
+  return SDM_OK;
+}
+
+int32_t run_scan(const sdm_dims* d, const Derived& dv, const sdm_sel* in, const float* norm_w,
+                 float* state, float* out, float* y_raw, void* ws, size_t ws_bytes,
+                 hipStream_t st) {
+  ScanArgs a;
+  a.idx_w = in->idx_w;
+  a.wt_w = in->wt_w;
+  a.idx_r = in->idx_r;
+  a.wt_r = in->wt_r;
+  a.v = in->v;
+  a.gate = in->gate;
+  a.alpha = in->alpha;
+  a.beta = in->beta;
+  a.norm_w = norm_w;
+  a.state = state;
+  a.out = out;
+  a.y_raw = y_raw;
+  a.B = d->B;
+  a.T = d->T;
+  a.H = d->H;
+  a.N = (int32_t)dv.N;
+  a.W = d->W;
+  a.R = d->R;
+  a.d_v = d->d_v;
+  a.eps = d->eps;
+  return hip_status(launch_scan(a, ws, ws_bytes, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t sdm_abi_version(void) { return SDM_ABI_VERSION; }
+
+const char* sdm_status_string(int32_t status) {
+  switch (status) {
+    case SDM_OK: return "ok";
+    case SDM_ERR_NULL: return "a required pointer is NULL";
+    case SDM_ERR_SHAPE: return "inconsistent or out-of-range sizes";
+    case SDM_ERR_DTYPE: return "unknown element type or gate activation";
+    case SDM_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+    case SDM_ERR_WORKSPACE: return "workspace missing or too small";
+    case SDM_ERR_UNSUPPORTED: return "sizes outside this build's limits";
+    case SDM_ERR_HIP: return "the HIP runtime reported a launch error";
+    default: return "unknown status";
+  }
+}
+
+size_t sdm_workspace_bytes(const sdm_dims* d, int32_t entry) {
+  Derived dv;
+  if (check_dims(d, &dv) != SDM_OK || dv.M == 0) return 0;
+  switch (entry) {
+    case SDM_ENTRY_SELECT: return select_ws_bytes(d, dv, false);
+    case SDM_ENTRY_SCAN: return align_up(scan_workspace_bytes(*d));
+    case SDM_ENTRY_FORWARD:
+      return product_sizes(d, dv.M).total + select_ws_bytes(d, dv, false) +
+             align_up(scan_workspace_bytes(*d));
+    default: return 0;
+  }
+}
+
+int32_t sdm_select(const sdm_dims* d, const void* x, const void* w_proj, const float* A,
+                   const float* b_dt, const sdm_sel* out, void* ws, size_t ws_bytes,
+                   void* stream) {
+  Derived dv;
+  int32_t st = check_dims(d, &dv);
+  if (st != SDM_OK) return st;
+  if (dv.M == 0) return SDM_OK;
+  if (!x || !w_proj || !A || !b_dt) return SDM_ERR_NULL;
+  if ((st = check_sel(out, false)) != SDM_OK) return st;
+  if (!aligned16(x) || !aligned16(w_proj) || !aligned16(A) || !aligned16(b_dt))
+    return SDM_ERR_ALIGN;
+  const size_t need = select_ws_bytes(d, dv, out->scores != nullptr);
+  if (need && (!ws || ws_bytes < need)) return SDM_ERR_WORKSPACE;
+  if (need && !aligned16(ws)) return SDM_ERR_ALIGN;
+  (void)hipGetLastError();
+  return run_select(d, dv, x, w_proj, A, b_dt, out, ws, (hipStream_t)stream);
+}
+
+int32_t sdm_select_from_scores(const sdm_dims* d, const float* scores, int32_t* idx_w,
+                               float* wt_w, int32_t* idx_r, float* wt_r, void* stream) {
+  Derived dv;
+  int32_t st = check_dims(d, &dv);
+  if (st != SDM_OK) return st;
+  if (dv.M == 0) return SDM_OK;
+  if (!scores || !idx_w || !wt_w || !idx_r || !wt_r) return SDM_ERR_NULL;
+  if (!aligned16(scores) || !aligned16(idx_w) || !aligned16(wt_w) || !aligned16(idx_r) ||
+      !aligned16(wt_r))
+    return SDM_ERR_ALIGN;
+  (void)hipGetLastError();
+  return hip_status(
+      launch_select(*d, scores, dv.M, 0, idx_w, wt_w, idx_r, wt_r, (hipStream_t)stream));
+}
+
+int32_t sdm_scan(const sdm_dims* d, const sdm_sel* in, const float* norm_w, float* state,
+                 float* out, float* y_raw, void* ws, size_t ws_bytes, void* stream) {
+  Derived dv;
+  int32_t st = check_dims(d, &dv);
+  if (st != SDM_OK) return st;
+  if (dv.M == 0) return SDM_OK;
+  if ((st = check_sel(in, false)) != SDM_OK) return st;
+  if (!state || !out) return SDM_ERR_NULL;
+  if (!aligned16(state) || !aligned16(out) || (y_raw && !aligned16(y_raw)) ||
+      (norm_w && !aligned16(norm_w)))
+    return SDM_ERR_ALIGN;
+  const size_t need = align_up(scan_workspace_bytes(*d));
+  if (need && (!ws || ws_bytes < need)) return SDM_ERR_WORKSPACE;
+  (void)hipGetLastError();
+  return run_scan(d, dv, in, norm_w, state, out, y_raw, ws, ws_bytes, (hipStream_t)stream);
+}
+
+int32_t sdm_forward(const sdm_dims* d, const void* x, const void* w_proj, const float* A,
+                    const float* b_dt, const float* norm_w, float* state, float* out,
+                    const sdm_sel* debug, void* ws, size_t ws_bytes, void* stream) {
+  Derived dv;
+  int32_t st = check_dims(d, &dv);
+  if (st != SDM_OK) return st;
+  if (dv.M == 0) return SDM_OK;
+  if (!x || !w_proj || !A || !b_dt || !state || !out) return SDM_ERR_NULL;
+  if (debug && (st = check_sel(debug, false)) != SDM_OK) return st;
+  if (!aligned16(x) || !aligned16(w_proj) || !aligned16(A) || !aligned16(b_dt) ||
+      !aligned16(state) || !aligned16(out) || (norm_w && !aligned16(norm_w)))
+    return SDM_ERR_ALIGN;
+  const ProductSizes ps = product_sizes(d, dv.M);
+  const size_t sel_ws = select_ws_bytes(d, dv, false);
+  const size_t scan_ws = align_up(scan_workspace_bytes(*d));
+  const size_t need = ps.total + sel_ws + scan_ws;
+  if (!ws || ws_bytes < need) return SDM_ERR_WORKSPACE;
+  if (!aligned16(ws)) return SDM_ERR_ALIGN;
+
+  char* base = static_cast<char*>(ws);
+  sdm_sel prod;
+  if (debug) {
+    prod = *debug;
+  } else {
+    char* p = base;
+    prod.idx_w = reinterpret_cast<int32_t*>(p); p += ps.idx_w;
+    prod.wt_w = reinterpret_cast<float*>(p); p += ps.wt_w;
+    prod.idx_r = reinterpret_cast<int32_t*>(p); p += ps.idx_r;
+    prod.wt_r = reinterpret_cast<float*>(p); p += ps.wt_r;
+    prod.v = reinterpret_cast<float*>(p); p += ps.v;
+    prod.gate = reinterpret_cast<float*>(p); p += ps.gate;
+    prod.alpha = reinterpret_cast<float*>(p); p += ps.alpha;
+    prod.beta = reinterpret_cast<float*>(p); p += ps.beta;
+    prod.scores = nullptr;
+  }
+  void* sel_space = base + ps.total;
+  void* scan_space = base + ps.total + sel_ws;
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  st = run_select(d, dv, x, w_proj, A, b_dt, &prod, sel_space, s);
+  if (st != SDM_OK) return st;
+  return run_scan(d, dv, &prod, norm_w, state, out, nullptr, scan_space, scan_ws, s);
+}
+
+}  // extern "C"

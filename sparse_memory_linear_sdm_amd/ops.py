@@ -1,0 +1,120 @@
+"""Tensor-level calls of the SDM forward path.
+
+Each function checks dtypes/devices/contiguity, allocates the outputs (and the
+workspace, unless one is passed) with torch, and calls the C entry point of the
+same name in libsdm.so.  Nothing here computes any part of the method.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import SdmDims
+
+PRODUCT_FIELDS = ("idx_w", "wt_w", "idx_r", "wt_r", "v", "gate", "alpha", "beta")
+
+
+def _need(t, dtype, shape, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def in_dtype(d: SdmDims):
+    return torch.bfloat16 if d.in_dtype == _lib.SDM_DTYPE_BF16 else torch.float32
+
+
+def alloc_products(d: SdmDims, device, with_scores=False) -> dict:
+    B, T, H = d.B, d.T, d.H
+    e = lambda *s, dt=torch.float32: torch.empty(s, dtype=dt, device=device)
+    p = dict(idx_w=e(B, T, H, d.W, dt=torch.int32), wt_w=e(B, T, H, d.W),
+             idx_r=e(B, T, H, d.R, dt=torch.int32), wt_r=e(B, T, H, d.R),
+             v=e(B, T, H, d.d_v), gate=e(B, T, H, d.d_v), alpha=e(B, T, H), beta=e(B, T, H))
+    if with_scores:
+        p["scores"] = e(B, T, H, 4 * d.n)
+    return p
+
+
+def _sel(p: dict) -> _lib.SdmSel:
+    return _lib.sel_struct(*(p[k] for k in PRODUCT_FIELDS), p.get("scores"))
+
+
+def _check_params(d: SdmDims, x, w_proj, A, b_dt):
+    P = 4 * d.n + 2 * d.d_v + 2
+    _need(x, in_dtype(d), (d.B, d.T, d.d_model), "x")
+    _need(w_proj, in_dtype(d), (d.H * P, d.d_model), "w_proj")
+    _need(A, torch.float32, (d.H,), "A")
+    _need(b_dt, torch.float32, (d.H,), "b_dt")
+
+
+def _check_products(d: SdmDims, p: dict):
+    shapes = dict(idx_w=(d.W,), wt_w=(d.W,), idx_r=(d.R,), wt_r=(d.R,), v=(d.d_v,),
+                  gate=(d.d_v,), alpha=(), beta=())
+    for k in PRODUCT_FIELDS:
+        dt = torch.int32 if k.startswith("idx") else torch.float32
+        _need(p[k], dt, (d.B, d.T, d.H) + shapes[k], k)
+
+
+def _workspace(d: SdmDims, entry: int, device, ws=None):
+    need = _lib.workspace_bytes(d, entry)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    elif ws.numel() * ws.element_size() < need:
+        raise ValueError(f"workspace of {need} bytes needed")
+    return ws, ws.numel() * ws.element_size()
+
+
+def select(d: SdmDims, x, w_proj, A, b_dt, with_scores=False, out=None, ws=None, stream=None):
+    _check_params(d, x, w_proj, A, b_dt)
+    p = out if out is not None else alloc_products(d, x.device, with_scores)
+    _check_products(d, p)
+    ws, nb = _workspace(d, _lib.SDM_ENTRY_SELECT, x.device, ws)
+    _lib.sdm_select(d, x, w_proj, A, b_dt, _sel(p), ws, nb, stream)
+    return p
+
+
+def select_from_scores(d: SdmDims, scores, stream=None):
+    _need(scores, torch.float32, (d.B, d.T, d.H, 4 * d.n), "scores")
+    p = alloc_products(d, scores.device)
+    _lib.sdm_select_from_scores(d, scores, p["idx_w"], p["wt_w"], p["idx_r"], p["wt_r"], stream)
+    return {k: p[k] for k in ("idx_w", "wt_w", "idx_r", "wt_r")}
+
+
+def scan(d: SdmDims, products: dict, norm_w, state, with_y_raw=False, out=None, ws=None,
+         stream=None):
+    _check_products(d, products)
+    N = d.n * d.n
+    _need(state, torch.float32, (d.B, d.H, N, d.d_v), "state")
+    if norm_w is not None:
+        _need(norm_w, torch.float32, (d.H, d.d_v), "norm_w")
+    dev = state.device
+    o = out if out is not None else torch.empty((d.B, d.T, d.H, d.d_v), device=dev)
+    _need(o, torch.float32, (d.B, d.T, d.H, d.d_v), "out")
+    y = torch.empty_like(o) if with_y_raw else None
+    ws, nb = _workspace(d, _lib.SDM_ENTRY_SCAN, dev, ws)
+    _lib.sdm_scan(d, _sel(products), norm_w, state, o, y, ws, nb, stream)
+    return (o, y) if with_y_raw else o
+
+
+def forward(d: SdmDims, x, w_proj, A, b_dt, norm_w, state, debug=False, with_scores=False,
+            out=None, ws=None, stream=None):
+    """Whole path; state is updated in place.  Returns out (and the products if debug)."""
+    _check_params(d, x, w_proj, A, b_dt)
+    N = d.n * d.n
+    _need(state, torch.float32, (d.B, d.H, N, d.d_v), "state")
+    if norm_w is not None:
+        _need(norm_w, torch.float32, (d.H, d.d_v), "norm_w")
+    o = out if out is not None else torch.empty((d.B, d.T, d.H, d.d_v), device=x.device)
+    _need(o, torch.float32, (d.B, d.T, d.H, d.d_v), "out")
+    prod = alloc_products(d, x.device, with_scores) if debug else None
+    ws, nb = _workspace(d, _lib.SDM_ENTRY_FORWARD, x.device, ws)
+    _lib.sdm_forward(d, x, w_proj, A, b_dt, norm_w, state, o, _sel(prod) if prod else None, ws,
+                     nb, stream)
+    return (o, prod) if debug else o

@@ -1,0 +1,118 @@
+"""Helpers of the GPU parity tests: device transfer of synthetic inputs and the
+comparison rules (tolerances, near-tie accounting)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from oracle import sdm_oracle as O
+from sparse_memory_linear_sdm_amd import synth
+
+RTOL, ATOL = 1e-4, 1e-5        # fp32 state / outputs / weights vs the fp64 oracle
+NEAR_TIE = 1e-6                # gap between the W-th and (W+1)-th oracle score
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def to_dev(a, dtype=None):
+    if isinstance(a, np.ndarray) and a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev())
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to(dev())
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def layer_inputs(wl: synth.Workload, seed=0, with_state=True):
+    """Synthetic inputs of a workload: host values (fp32) and device tensors."""
+    x_vals, x_store = synth.gen_x(wl, seed)
+    prm = synth.gen_params(wl, seed)
+    h = dict(x=x_vals, w_proj=prm["w_proj"], A=prm["A"], b_dt=prm["b_dt"], gamma=prm["gamma"])
+    d = dict(x=to_dev(x_store), w_proj=to_dev(prm["w_proj_store"]), A=to_dev(prm["A"]),
+             b_dt=to_dev(prm["b_dt"]), gamma=to_dev(prm["gamma"]))
+    if with_state:
+        m0 = synth.gen_m0(wl, seed)
+        h["m0"] = m0
+        d["m0"] = to_dev(m0)
+    return h, d
+
+
+def broadcast_state(m0_dev, B):
+    return m0_dev.unsqueeze(0).expand(B, *m0_dev.shape).contiguous()
+
+
+def assert_close(got, exp, what, rtol=RTOL, atol=ATOL):
+    got = np.asarray(got, np.float64)
+    exp = np.asarray(exp, np.float64)
+    err = np.abs(got - exp) - (atol + rtol * np.abs(exp))
+    bad = np.argwhere(err > 0)
+    if bad.size:
+        i = tuple(bad[0])
+        raise AssertionError(f"{what}: {bad.shape[0]} elements out of tolerance; first at {i}: "
+                             f"got {got[i]!r} expected {exp[i]!r}")
+
+
+def gemm_bound(x_rows, w, K):
+    """Deterministic fp32-accumulation error bound of Y = x W^T for K terms."""
+    return K * 2.0 ** -24 * (np.abs(np.asarray(x_rows, np.float64)) @ np.abs(np.asarray(w, np.float64)).T) + 1e-6
+
+
+def random_products(rng, B, T, H, n, W, R, d_v, mode="random"):
+    """Host-side selection products for scan tests (ids ascending and distinct).
+
+    mode: "random" (independent tokens), "repeat" (runs of identical selections),
+          "same" (every token selects the same slots).
+    """
+    N = n * n
+    shp = (B, T, H)
+
+    def ids(count):
+        out = np.empty(shp + (count,), np.int32)
+        for idx in np.ndindex(*shp):
+            out[idx] = np.sort(rng.choice(N, count, replace=False))
+        return out
+
+    iw, ir = ids(W), ids(R)
+    if mode == "repeat":
+        for t in range(1, T):
+            keep = rng.random((B, H)) < 0.7
+            iw[:, t][keep] = iw[:, t - 1][keep]
+            ir[:, t][keep] = ir[:, t - 1][keep]
+        if R <= W:  # half of the tokens read exactly slots they write
+            rd = rng.random(shp) < 0.5
+            ir[rd] = iw[rd][:, :R]
+    elif mode == "same":
+        iw[:] = iw[:, :1]
+        ir[:] = ir[:, :1]
+    wt_w = rng.dirichlet(np.ones(W), shp).astype(np.float32)
+    wt_r = rng.dirichlet(np.ones(R), shp).astype(np.float32)
+    return dict(idx_w=iw, wt_w=wt_w, idx_r=ir, wt_r=wt_r,
+                v=rng.standard_normal(shp + (d_v,)).astype(np.float32),
+                gate=rng.uniform(0, 1, shp + (d_v,)).astype(np.float32),
+                alpha=rng.uniform(0.3, 1.0, shp).astype(np.float32),
+                beta=rng.uniform(0.0, 1.0, shp).astype(np.float32))
+
+
+def oracle_walks(prod_h, m0_h, gamma, eps, walks):
+    """Oracle scan + norm for the listed (b, h) walks from given products."""
+    res = {}
+    for b, h in walks:
+        sel = {k: prod_h[k][b, :, h] for k in ("idx_w", "wt_w", "idx_r", "wt_r", "v", "gate",
+                                                "alpha", "beta")}
+        sel["g"] = sel.pop("gate")
+        out, y, M = O.forward_walk(m0_h[b, h] if m0_h.ndim == 4 else m0_h[h], sel, gamma[h], eps)
+        res[(b, h)] = (out, y, M)
+    return res

@@ -1,0 +1,147 @@
+"""The C ABI on a machine without a GPU: the library loads, exports every entry
+point include/sdm.h declares, sizes workspaces, and rejects bad arguments before
+anything would be enqueued (so no device is touched by these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_memory_linear_sdm_amd import _lib
+from sparse_memory_linear_sdm_amd import synth, dims_for
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sdm.h")
+FAKE = 0x100000  # an address that is never dereferenced: validation fails first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libsdm.so is not built (run __graft_entry__.build())")
+    return _lib.load()
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"SDM_API\s+[\w\s\*]*?\b(sdm_\w+)\s*\(", txt)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert set(names) == set(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_header_constants_match_binding():
+    txt = open(HEADER).read()
+    consts = dict(re.findall(r"#define (SDM_\w+) \(?(-?\d+)\)?", txt))
+    for k, v in consts.items():
+        if hasattr(_lib, k):
+            assert getattr(_lib, k) == int(v), k
+
+
+def test_version_and_status_strings(lib):
+    assert _lib.abi_version() == 1
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, 12345):
+        assert isinstance(_lib.status_string(code), str) and _lib.status_string(code)
+    assert _lib.status_string(-5) == "workspace missing or too small"
+
+
+def _d(**kw):
+    base = dict(B=2, T=8, d_model=64, H=2, n=8, W=4, R=4, d_v=16, in_dtype=1, gate_act=1,
+                eps=1e-6, flags=0)
+    base.update(kw)
+    return _lib.dims(**base)
+
+
+def _sel(**over):
+    f = {k: FAKE for k in ("idx_w", "wt_w", "idx_r", "wt_r", "v", "gate", "alpha", "beta")}
+    f["scores"] = None
+    f.update(over)
+    return _lib.SdmSel(*[f[k] for k in ("idx_w", "wt_w", "idx_r", "wt_r", "v", "gate", "alpha",
+                                        "beta", "scores")])
+
+
+def _select(lib, d, x=FAKE, w=FAKE, A=FAKE, b=FAKE, sel=None, ws=FAKE, nb=1 << 40):
+    sel = sel if sel is not None else _sel()
+    return lib.sdm_select(ctypes.byref(d), x, w, A, b, ctypes.byref(sel), ws, nb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=0), _lib.SDM_ERR_SHAPE), (dict(n=0), _lib.SDM_ERR_SHAPE),
+    (dict(W=0), _lib.SDM_ERR_SHAPE), (dict(R=-1), _lib.SDM_ERR_SHAPE),
+    (dict(n=2, W=5), _lib.SDM_ERR_SHAPE), (dict(B=-1), _lib.SDM_ERR_SHAPE),
+    (dict(eps=-1.0), _lib.SDM_ERR_SHAPE), (dict(eps=float("nan")), _lib.SDM_ERR_SHAPE),
+    (dict(n=16, W=129), _lib.SDM_ERR_UNSUPPORTED), (dict(n=1025), _lib.SDM_ERR_UNSUPPORTED),
+    (dict(d_v=48), _lib.SDM_ERR_UNSUPPORTED), (dict(d_model=60), _lib.SDM_ERR_UNSUPPORTED),
+    (dict(flags=1), _lib.SDM_ERR_UNSUPPORTED),
+    (dict(in_dtype=7), _lib.SDM_ERR_DTYPE), (dict(gate_act=3), _lib.SDM_ERR_DTYPE),
+])
+def test_bad_dims_rejected_by_every_entry(lib, kw, code):
+    d = _d(**kw)
+    assert _select(lib, d) == code
+    assert lib.sdm_select_from_scores(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None) == code
+    s = _sel()
+    assert lib.sdm_scan(ctypes.byref(d), ctypes.byref(s), None, FAKE, FAKE, None, FAKE, 1 << 40,
+                        None) == code
+    assert lib.sdm_forward(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, FAKE,
+                           1 << 40, None) == code
+    assert lib.sdm_workspace_bytes(ctypes.byref(d), 2) == 0
+
+
+def test_null_dims(lib):
+    assert lib.sdm_select(None, FAKE, FAKE, FAKE, FAKE, None, FAKE, 0, None) == _lib.SDM_ERR_NULL
+    assert lib.sdm_workspace_bytes(None, 0) == 0
+
+
+def test_null_and_misaligned_pointers(lib):
+    d = _d()
+    assert _select(lib, d, x=None) == _lib.SDM_ERR_NULL
+    assert _select(lib, d, sel=_sel(wt_r=None)) == _lib.SDM_ERR_NULL
+    assert _select(lib, d, x=FAKE + 4) == _lib.SDM_ERR_ALIGN
+    assert _select(lib, d, sel=_sel(v=FAKE + 8)) == _lib.SDM_ERR_ALIGN
+    assert _select(lib, d, sel=_sel(scores=FAKE + 2)) == _lib.SDM_ERR_ALIGN
+    s = _sel()
+    assert lib.sdm_scan(ctypes.byref(d), ctypes.byref(s), None, None, FAKE, None, None, 0,
+                        None) == _lib.SDM_ERR_NULL
+    assert lib.sdm_scan(ctypes.byref(d), ctypes.byref(s), FAKE + 4, FAKE, FAKE, None, None, 0,
+                        None) == _lib.SDM_ERR_ALIGN
+    assert lib.sdm_forward(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None, FAKE,
+                           1 << 40, None) == _lib.SDM_ERR_NULL
+
+
+def test_workspace_checks(lib):
+    d = _d()
+    need = lib.sdm_workspace_bytes(ctypes.byref(d), _lib.SDM_ENTRY_SELECT)
+    assert need == 16 * 2 * 4 * 8 * 4 or need >= 16 * 2 * 4 * 8 * 4
+    assert _select(lib, d, ws=None) == _lib.SDM_ERR_WORKSPACE
+    assert _select(lib, d, nb=need - 1) == _lib.SDM_ERR_WORKSPACE
+    fneed = lib.sdm_workspace_bytes(ctypes.byref(d), _lib.SDM_ENTRY_FORWARD)
+    assert fneed > need
+    assert lib.sdm_forward(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, FAKE,
+                           fneed - 1, None) == _lib.SDM_ERR_WORKSPACE
+    assert lib.sdm_workspace_bytes(ctypes.byref(d), 99) == 0
+
+
+def test_empty_calls_are_noops(lib):
+    for kw in (dict(B=0), dict(T=0)):
+        d = _d(**kw)
+        assert _select(lib, d, x=None, ws=None, nb=0) == _lib.SDM_OK
+        s = _sel()
+        assert lib.sdm_scan(ctypes.byref(d), ctypes.byref(s), None, None, None, None, None, 0,
+                            None) == _lib.SDM_OK
+        assert lib.sdm_forward(ctypes.byref(d), None, None, None, None, None, None, None, None,
+                               None, 0, None) == _lib.SDM_OK
+        assert lib.sdm_workspace_bytes(ctypes.byref(d), 2) == 0
+
+
+def test_workspace_sizes_of_the_workloads(lib):
+    for name, wl in synth.WORKLOADS.items():
+        d = dims_for(wl)
+        per_th = 4 * (2 * wl.W + 2 * wl.R + 2 * wl.d_v + 2)
+        fwd = lib.sdm_workspace_bytes(ctypes.byref(d), _lib.SDM_ENTRY_FORWARD)
+        assert fwd >= wl.tokens * wl.H * per_th, name
+        sel = lib.sdm_workspace_bytes(ctypes.byref(d), _lib.SDM_ENTRY_SELECT)
+        assert 0 < sel <= (512 << 20) + 256 or sel == wl.tokens * wl.H * 16 * wl.n, name

@@ -1,0 +1,254 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Stage A  projection + gates          vs oracle pass_a (fp32-accumulation bound)
+Stage B  selection from half-scores  ids bit-identical, weights within tolerance
+Stage C  scan from given selections  state / y / out within 1e-4 rel, 1e-5 abs;
+                                     never-written rows bit-identical
+Stage D  whole layer from x          ids equal except near-ties / GEMM-rounding flips
+                                     (reported, not failed); outputs within tolerance
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import sdm_oracle as O
+from sparse_memory_linear_sdm_amd import _lib, dims_for, ops, synth
+from tests.gpu_util import (ATOL, NEAR_TIE, RTOL, assert_close, broadcast_state, gemm_bound,
+                            host, layer_inputs, oracle_walks, random_products, say, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    say(f"\n[gpu] {request.node.nodeid}")
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    yield
+    torch.cuda.synchronize()
+
+
+def _dims(**kw):
+    base = dict(B=1, T=64, d_model=64, H=1, n=16, W=8, R=8, d_v=16, in_dtype=_lib.SDM_DTYPE_F32,
+                gate_act=_lib.SDM_GATE_SIGMOID, eps=1e-6)
+    base.update(kw)
+    return _lib.dims(**base)
+
+
+def _prod_dev(p):
+    return {k: to_dev(v) for k, v in p.items()}
+
+
+# ---------------------------------------------------------------------------
+# Stage A
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("wl", [
+    synth.WORKLOADS["tiny"],
+    synth.small("layer1p4b", B=2, T=160, d_model=256, n=40, W=16, R=16, d_v=32),
+    synth.small("layer1p4b", B=1, T=200, d_model=2048, H=2, n=362, W=64, R=64, d_v=128),
+])
+def test_stage_a_projection_and_gates(wl):
+    h, d = layer_inputs(wl, seed=1, with_state=False)
+    dm = dims_for(wl)
+    p = ops.select(dm, d["x"], d["w_proj"], d["A"], d["b_dt"], with_scores=True)
+    torch.cuda.synchronize()
+    a = O.pass_a(h["x"], h["w_proj"], h["A"], h["b_dt"], wl.H, wl.n, wl.d_v, wl.W, wl.R)
+    x2 = h["x"].reshape(-1, wl.d_model)
+    bound = gemm_bound(x2, h["w_proj"], wl.d_model).reshape(wl.B, wl.T, wl.H, wl.P)
+    sc = host(p["scores"]).astype(np.float64)
+    err = np.abs(sc - a["scores"])
+    assert np.all(err <= bound[..., :4 * wl.n]), f"scores max err {err.max()}"
+    o4 = 4 * wl.n
+    errv = np.abs(host(p["v"]) - a["v"])
+    assert np.all(errv <= bound[..., o4:o4 + wl.d_v]), f"v max err {errv.max()}"
+    assert_close(host(p["gate"]), a["g"], "gate")
+    assert_close(host(p["alpha"]), a["alpha"], "alpha")
+    assert_close(host(p["beta"]), a["beta"], "beta")
+    say(f"  scores max |err| {err.max():.3e}  (bound min {bound[..., :o4].min():.3e})")
+
+
+# ---------------------------------------------------------------------------
+# Stage B
+# ---------------------------------------------------------------------------
+def _scores_case(rng, B, T, H, n, kind):
+    shp = (B, T, H, 4 * n)
+    if kind == "normal":
+        return rng.standard_normal(shp).astype(np.float32)
+    if kind == "ties":        # few levels: many exact ties across the cut
+        return (rng.integers(-3, 4, shp) * 0.25).astype(np.float32)
+    if kind == "zeros":       # signed zeros and equal scores everywhere
+        s = np.zeros(shp, np.float32)
+        s[rng.random(shp) < 0.5] = -0.0
+        return s
+    if kind == "wide":        # magnitudes across many binades
+        return (rng.standard_normal(shp) * np.exp2(rng.integers(-30, 30, shp))).astype(np.float32)
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("n,W,R,kind", [
+    (32, 8, 8, "normal"), (362, 64, 64, "normal"), (362, 64, 64, "ties"),
+    (40, 128, 100, "normal"), (40, 128, 128, "ties"), (8, 64, 20, "normal"),
+    (4, 16, 16, "normal"), (16, 1, 1, "ties"), (16, 8, 8, "zeros"), (64, 64, 64, "wide"),
+    (1024, 64, 64, "normal"), (1000, 33, 65, "ties"), (1, 1, 1, "normal"),
+])
+def test_stage_b_selection_bit_exact(n, W, R, kind):
+    rng = np.random.default_rng(n * 1000 + W + R)
+    B, T, H = 2, 24, 3
+    s = _scores_case(rng, B, T, H, n, kind)
+    d = _dims(B=B, T=T, H=H, n=n, W=W, R=R)
+    g = ops.select_from_scores(d, to_dev(s))
+    torch.cuda.synchronize()
+    o = O.select_from_scores(s, n, W, R)
+    for role, cnt in (("w", W), ("r", R)):
+        gi = host(g[f"idx_{role}"])
+        assert gi.shape == o[f"idx_{role}"].shape
+        mism = np.argwhere(gi != o[f"idx_{role}"])
+        assert mism.size == 0, f"ids differ ({role}) at {mism[:3].tolist()}"
+        assert_close(host(g[f"wt_{role}"]), o[f"wt_{role}"], f"wt_{role}")
+
+
+# ---------------------------------------------------------------------------
+# Stage C
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("B,T,H,n,W,R,d_v,mode", [
+    (1, 64, 1, 32, 8, 8, 16, "random"),
+    (2, 50, 3, 8, 32, 32, 32, "random"),       # N = 64, W = R = 32: heavy slot reuse
+    (2, 50, 2, 8, 32, 32, 64, "repeat"),
+    (1, 40, 2, 8, 16, 8, 128, "same"),
+    (3, 33, 2, 20, 64, 64, 128, "repeat"),
+    (1, 30, 1, 16, 128, 128, 256, "random"),
+    (2, 17, 1, 4, 16, 16, 16, "random"),       # every slot written by every token
+])
+def test_stage_c_scan(B, T, H, n, W, R, d_v, mode):
+    rng = np.random.default_rng(B * 100 + T + W)
+    N = n * n
+    prod = random_products(rng, B, T, H, n, W, R, d_v, mode)
+    m0 = (rng.standard_normal((B, H, N, d_v)) * 0.02).astype(np.float32)
+    gamma = rng.uniform(0.5, 1.5, (H, d_v)).astype(np.float32)
+    d = _dims(B=B, T=T, H=H, n=n, W=W, R=R, d_v=d_v)
+    state = to_dev(m0)
+    out, y = ops.scan(d, _prod_dev(prod), to_dev(gamma), state, with_y_raw=True)
+    torch.cuda.synchronize()
+    st, oh, yh = host(state), host(out), host(y)
+    ref = oracle_walks(prod, m0, gamma, 1e-6, [(b, h) for b in range(B) for h in range(H)])
+    for (b, h), (o_out, o_y, o_M) in ref.items():
+        assert_close(yh[b, :, h], o_y, f"y_raw walk {(b, h)}")
+        assert_close(oh[b, :, h], o_out, f"out walk {(b, h)}")
+        assert_close(st[b, h], o_M, f"state walk {(b, h)}")
+        untouched = np.setdiff1d(np.arange(N), prod["idx_w"][b, :, h].ravel())
+        assert np.array_equal(st[b, h][untouched], m0[b, h][untouched]), "unwritten rows changed"
+
+
+def test_stage_c_identity_and_overwrite_exact():
+    rng = np.random.default_rng(7)
+    B, T, H, n, d_v = 2, 20, 2, 8, 32
+    prod = random_products(rng, B, T, H, n, 1, 1, d_v)
+    m0 = (rng.standard_normal((B, H, n * n, d_v)) * 0.02).astype(np.float32)
+    d = _dims(B=B, T=T, H=H, n=n, W=1, R=1, d_v=d_v)
+    # alpha = 1, beta = 0: the state must come back bit-identical
+    p1 = dict(prod, alpha=np.ones((B, T, H), np.float32), beta=np.zeros((B, T, H), np.float32))
+    st = to_dev(m0)
+    ops.scan(d, _prod_dev(p1), None, st)
+    assert np.array_equal(host(st), m0)
+    # beta = 1 with weight 1: each written slot holds exactly v_t; reading it returns v_t
+    p2 = dict(prod, beta=np.ones((B, T, H), np.float32), wt_w=np.ones((B, T, H, 1), np.float32),
+              wt_r=np.ones((B, T, H, 1), np.float32), idx_r=prod["idx_w"].copy())
+    st = to_dev(m0)
+    _, y = ops.scan(d, _prod_dev(p2), None, st, with_y_raw=True)
+    assert np.array_equal(host(y), p2["v"])
+    sth = host(st)
+    for b in range(B):
+        for h in range(H):
+            last = {int(p2["idx_w"][b, t, h, 0]): t for t in range(T)}
+            for s, t in last.items():
+                assert np.array_equal(sth[b, h, s], p2["v"][b, t, h])
+
+
+# ---------------------------------------------------------------------------
+# Stage D
+# ---------------------------------------------------------------------------
+def _compare_ids_from_x(gpu_p, orc, bound_rows):
+    """Count id mismatches; each must be a near-tie or a GEMM-rounding flip."""
+    flips = ties = 0
+    for role in ("w", "r"):
+        gi, oi = host(gpu_p[f"idx_{role}"]), orc[f"idx_{role}"]
+        bad = np.argwhere(np.any(gi != oi, axis=-1))
+        for idx in map(tuple, bad):
+            gap = orc[f"gap_{role}"][idx]
+            if gap < NEAR_TIE:
+                ties += 1
+            elif gap <= 2 * bound_rows[idx]:
+                flips += 1
+            else:
+                raise AssertionError(f"ids differ at {idx} ({role}) with oracle gap {gap}")
+    return ties, flips
+
+
+@pytest.mark.parametrize("wl", [
+    synth.WORKLOADS["tiny"],
+    synth.small("layer1p4b", B=2, T=96, d_model=512, H=2, n=64, W=32, R=48, d_v=64),
+])
+def test_stage_d_forward_from_x(wl):
+    h, d = layer_inputs(wl, seed=2)
+    dm = dims_for(wl)
+    state = broadcast_state(d["m0"], wl.B)
+    out, p = ops.forward(dm, d["x"], d["w_proj"], d["A"], d["b_dt"], d["gamma"], state,
+                         debug=True, with_scores=True)
+    torch.cuda.synchronize()
+    m0b = np.broadcast_to(h["m0"], (wl.B,) + h["m0"].shape)
+    o_out, o_st, o_a = O.forward(h["x"], h["w_proj"], h["A"], h["b_dt"], h["gamma"], m0b, wl.H,
+                                 wl.n, wl.d_v, wl.W, wl.R, wl.eps)
+    x2 = h["x"].reshape(-1, wl.d_model)
+    bnd = gemm_bound(x2, h["w_proj"], wl.d_model).reshape(wl.B, wl.T, wl.H, wl.P)
+    bound_rows = bnd[..., :4 * wl.n].max(-1)
+    ties, flips = _compare_ids_from_x(p, o_a, bound_rows)
+    say(f"  near-ties {ties}, rounding flips {flips}")
+    # ids from the GPU's own scores are bit-exact
+    s = O.select_from_scores(host(p["scores"]), wl.n, wl.W, wl.R)
+    assert np.array_equal(host(p["idx_w"]), s["idx_w"])
+    assert np.array_equal(host(p["idx_r"]), s["idx_r"])
+    if ties == 0 and flips == 0:
+        assert_close(host(out), o_out, "out")
+        assert_close(host(state), o_st, "state")
+    else:  # walks with a flip are checked from the GPU's own selection
+        ph = {k: host(v) for k, v in p.items()}
+        ref = oracle_walks(ph, h["m0"], h["gamma"], wl.eps,
+                           [(b, hh) for b in range(wl.B) for hh in range(wl.H)])
+        for (b, hh), (oo, _, oM) in ref.items():
+            assert_close(host(out)[b, :, hh], oo, f"out {(b, hh)}")
+            assert_close(host(state)[b, hh], oM, f"state {(b, hh)}")
+
+
+def test_chunked_calls_equal_one_call():
+    wl = synth.small("layer1p4b", B=2, T=80, d_model=256, H=2, n=24, W=16, R=16, d_v=32)
+    _, d = layer_inputs(wl, seed=3)
+    s1 = broadcast_state(d["m0"], wl.B)
+    o1 = ops.forward(dims_for(wl), d["x"], d["w_proj"], d["A"], d["b_dt"], d["gamma"], s1)
+    s2 = broadcast_state(d["m0"], wl.B)
+    outs = []
+    for t0, t1 in ((0, 30), (30, 31), (31, 80)):
+        xs = d["x"][:, t0:t1].contiguous()
+        outs.append(ops.forward(dims_for(wl, T=t1 - t0), xs, d["w_proj"], d["A"], d["b_dt"],
+                                d["gamma"], s2))
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat(outs, dim=1), o1)
+    assert torch.equal(s1, s2)
+
+
+def test_empty_call_changes_nothing():
+    wl = synth.small("tiny", T=0)
+    _, d = layer_inputs(synth.WORKLOADS["tiny"], seed=4)
+    st = broadcast_state(d["m0"], 1)
+    before = st.clone()
+    dm = dims_for(wl)
+    x = torch.empty((1, 0, wl.d_model), device="cuda")
+    out = ops.forward(dm, x, d["w_proj"], d["A"], d["b_dt"], d["gamma"], st)
+    torch.cuda.synchronize()
+    assert out.shape == (1, 0, 1, 16) and torch.equal(st, before)
+
+
+def test_hip_path_is_the_loaded_library():
+    lib = _lib.load()
+    assert lib._name.endswith("libsdm.so")
+    with open("/proc/self/maps") as f:
+        assert any("libsdm.so" in line for line in f)
