@@ -1,0 +1,160 @@
+"""Benchmark of the SDM layer forward path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload layer1p4b]
+
+A step is one pass of the whole path (projection GEMM + gates, product-key
+selection, recurrent sparse scan, RMSNorm + gate) over one batch of synthetic
+input already resident in HBM.  Prints one JSON line with tokens/s, the
+roofline of the dominant kernel (the scan, HBM-bound) and a CPU baseline (the
+fp64 oracle timed on a bounded sample of the same workload on the host).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "SDM layer tokens/s at N=131072,W=R=64,d_v=128; effective HBM GB/s vs peak"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--workload", default="layer1p4b")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-tokens", type=int, default=2048,
+                   help="tokens of batch entry 0 in the oracle's timed sample")
+    return p.parse_args()
+
+
+def cpu_baseline(wl, ntok: int) -> dict:
+    """The fp64 oracle, as it stands, on the first `ntok` tokens of batch entry 0."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import sdm_oracle as O
+    from sparse_memory_linear_sdm_amd import synth
+
+    x, _ = synth.gen_x(wl, seed=0, t0=0, t1=ntok, batches=[0])
+    prm = synth.gen_params(wl, seed=0)
+    m0 = synth.gen_m0(wl, seed=0)[None]
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        O.forward(x, prm["w_proj"], prm["A"], prm["b_dt"], prm["gamma"], m0, wl.H, wl.n, wl.d_v,
+                  wl.W, wl.R, wl.eps)
+        dt = time.perf_counter() - t0
+    return {"value": ntok / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{wl.name}: tokens 0..{ntok - 1} of batch entry 0, all {wl.H} heads, "
+                      f"from x (fp64 projection, brute-force top-{wl.W}/{wl.R} over "
+                      f"N={wl.N}, sequential scan, norm+gate); {dt:.1f} s on 1 host thread"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the SDM walks "
+              "of one GPU are measured at their real shape. Multi-GPU sharding is not built.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from sparse_memory_linear_sdm_amd import _lib, dims_for, ops, synth
+
+    wl = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = dims_for(wl)
+
+    # inputs resident in HBM before timing
+    _, x_store = synth.gen_x(wl, seed=0)
+    prm = synth.gen_params(wl, seed=0)
+    m0 = synth.gen_m0(wl, seed=0)
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    x = to_dev(x_store)
+    w = to_dev(prm["w_proj_store"])
+    A, b_dt, gamma = to_dev(prm["A"]), to_dev(prm["b_dt"]), to_dev(prm["gamma"])
+    m0_d = to_dev(m0)
+    state = m0_d.unsqueeze(0).expand(wl.B, *m0_d.shape).contiguous()
+    del m0
+    prod = ops.alloc_products(d, dev)
+    out = torch.empty((wl.B, wl.T, wl.H, wl.d_v), device=dev)
+    ws_sel = torch.empty(max(_lib.workspace_bytes(d, _lib.SDM_ENTRY_SELECT), 1), dtype=torch.uint8,
+                         device=dev)
+    ws_scan = torch.empty(max(_lib.workspace_bytes(d, _lib.SDM_ENTRY_SCAN), 1), dtype=torch.uint8,
+                          device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        ops.select(d, x, w, A, b_dt, out=prod, ws=ws_sel, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        ops.scan(d, prod, gamma, state, out=out, ws=ws_scan, stream=stream)
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_sel = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    ms_scan = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    ms_step = float(np.mean([e[0].elapsed_time(e[2]) for e in evs]))
+    ms_wall = wall * 1e3 / args.steps
+
+    tokens = wl.tokens
+    slot_bytes = tokens * wl.H * wl.slot_bytes_per_token_head()
+    achieved = slot_bytes / (ms_scan * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": tokens / (ms_wall * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_wall,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 projection, fp32 selection/scan",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "d_model": wl.d_model, "H": wl.H,
+                   "N": wl.N, "n": wl.n, "W": wl.W, "R": wl.R, "d_v": wl.d_v,
+                   "state": "fp32 [B,H,N,d_v]", "tokens_per_step": tokens},
+        "phases_ms": {"select": ms_sel, "scan": ms_scan, "step_events": ms_step},
+        "effective_hbm_gbs_step": slot_bytes / (ms_wall * 1e-3) / 1e9,
+        "roofline": {"bound": "hbm", "kernel": "scan", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None,
+                     "algorithmic_bytes_per_launch": slot_bytes},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_tokens)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
