@@ -97,9 +97,19 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
 
 }  // namespace
 
-size_t scan_workspace_bytes(const sdm_dims&) { return 0; }
+bool scan_uses_stream(const sdm_dims& d) {
+  if (d.flags & SDM_FLAG_SCAN_DIRECT) return false;
+  if (d.flags & SDM_FLAG_SCAN_STREAM) return true;
+  return d.T >= 16;
+}
 
-hipError_t launch_scan(const ScanArgs& a, void*, size_t, hipStream_t s) {
+size_t scan_workspace_bytes(const sdm_dims& d) {
+  if (!scan_uses_stream(d)) return 0;
+  return stream_workspace_bytes(d, plan_stream(d, (int64_t)d.n * d.n));
+}
+
+hipError_t launch_scan(const sdm_dims& d, const ScanArgs& a, void* ws, size_t, hipStream_t s) {
+  if (scan_uses_stream(d)) return launch_stream_scan(a, plan_stream(d, a.N), ws, s);
   const dim3 grid((unsigned)(a.B * a.H));
   switch (a.d_v) {
     case 16: hipLaunchKernelGGL(scan_kernel<16>, grid, dim3(256), 0, s, a); break;

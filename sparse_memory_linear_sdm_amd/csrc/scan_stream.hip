@@ -1,0 +1,478 @@
+// Recurrent sparse scan for long token runs: slot-owner lane groups.
+//
+// What is computed is the recurrence of the method ("Sparse Delta Memory" summary
+// on paper.rainbus.top, method paragraph, steps 2-3; ai-paper-analysis.pages.dev,
+// sections "步骤 2" and "步骤 3"): per (batch, head) memory and tokens in order,
+//   write slot i (weight k):  M[i] <- (1 - c)(alpha_t M[i]) + c v_t,  c = beta_t k
+//   read:                     y_t = sum_i q^(i) M[i]   (after the token's writes)
+// with unselected slots never touched.
+//
+// How it is scheduled on gfx950:
+//  * Every slot belongs to exactly one lane group (hash of the slot id).  A lane
+//    group is LPG lanes covering one SW-float segment of d_v (one float4 each).
+//  * A bucketing pre-pass lays the accesses of each walk out as per-group streams
+//    in token order (writes before reads within a token), split into rounds of
+//    ROUND tokens.  Because a slot's column chunk is only ever loaded and stored by
+//    one thread, program order alone orders every read-after-write and
+//    write-after-write on that address: no cross-wave synchronisation is needed
+//    for the state.
+//  * Each lane group keeps BQ row loads in flight; repeated slots inside a batch
+//    are forwarded in registers.
+//  * Reads accumulate q * M[i] into an LDS ring of per-token partial sums (float
+//    atomics); once per round the ring half is flushed to y_part[part] and the
+//    next round proceeds.  A small kernel then sums the parts, normalises and gates.
+//  * Work is split over (walk, column slice, part): parts divide the lane groups
+//    of a walk among workgroups, so few walks still fill the chip.
+#include "sdm_internal.h"
+
+namespace sdm {
+namespace {
+
+constexpr int ROUND = 256;       // tokens per round (ring half)
+constexpr int MAX_GT = 4096;     // lane groups per walk
+
+__device__ __forceinline__ uint32_t group_of(uint32_t slot, int log2gt) {
+  return (slot * 2654435761u) >> (32 - log2gt);
+}
+
+// ---------------------------------------------------------------------------
+// Pre-pass 1: per (walk, round) histogram of accesses per group.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bucket_count_kernel(StreamArgs a) {
+  __shared__ int cnt[MAX_GT];
+  const int64_t w = blockIdx.x / a.rounds;
+  const int r = (int)(blockIdx.x - w * a.rounds);
+  const int64_t b = w / a.H;
+  const int h = (int)(w - b * a.H);
+  for (int g = threadIdx.x; g < a.GT; g += 256) cnt[g] = 0;
+  __syncthreads();
+  const int64_t t_lo = (int64_t)r * ROUND;
+  const int64_t t_hi = min<int64_t>(a.Tc, t_lo + ROUND);
+  const int per = a.W + a.R;
+  const int64_t n = (t_hi - t_lo) * per;
+  for (int64_t e = threadIdx.x; e < n; e += 256) {
+    const int64_t t = t_lo + e / per;
+    const int k = (int)(e % per);
+    const int64_t tok = (b * a.T + a.t0 + t) * a.H + h;
+    const int32_t s = k < a.W ? a.idx_w[tok * a.W + k] : a.idx_r[tok * a.R + (k - a.W)];
+    atomicAdd(&cnt[group_of((uint32_t)s, a.log2GT)], 1);
+  }
+  __syncthreads();
+  int* out = a.counts + ((int64_t)w * a.rounds + r) * a.GT;
+  for (int g = threadIdx.x; g < a.GT; g += 256) out[g] = cnt[g];
+}
+
+// ---------------------------------------------------------------------------
+// Pre-pass 2: per walk, stream offsets of every (group, round), groups laid out
+// one after another.  offsets[w][g][r] for r in [0, rounds] (last = group end).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void bucket_offsets_kernel(StreamArgs a) {
+  __shared__ int tot[MAX_GT];
+  __shared__ int part[1024];
+  const int64_t w = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int* cnt = a.counts + (int64_t)w * a.rounds * a.GT;
+  for (int g = tid; g < a.GT; g += 1024) {
+    int acc = 0;
+    for (int r = 0; r < a.rounds; ++r) acc += cnt[(int64_t)r * a.GT + g];
+    tot[g] = acc;
+  }
+  __syncthreads();
+  // exclusive prefix over groups: each thread owns a contiguous run
+  const int per = (a.GT + 1023) / 1024;
+  int run = 0;
+  for (int q = 0; q < per; ++q) {
+    const int g = tid * per + q;
+    if (g < a.GT) run += tot[g];
+  }
+  part[tid] = run;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int base = part[tid] - run;  // exclusive
+  for (int q = 0; q < per; ++q) {
+    const int g = tid * per + q;
+    if (g < a.GT) {
+      const int t = tot[g];
+      tot[g] = base;
+      base += t;
+    }
+  }
+  __syncthreads();
+  for (int g = tid; g < a.GT; g += 1024) {
+    int acc = tot[g];
+    int* o = a.offsets + ((int64_t)w * a.GT + g) * (a.rounds + 1);
+    for (int r = 0; r < a.rounds; ++r) {
+      o[r] = acc;
+      acc += cnt[(int64_t)r * a.GT + g];
+    }
+    o[a.rounds] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pre-pass 3: scatter the accesses of one (walk, round) into the streams.  One
+// wavefront walks the round's tokens in order; LDS cursors hand out positions.
+// Within one instruction all slots are distinct (a token's write ids are distinct,
+// and so are its read ids), and writes are issued before reads, so accesses of
+// one slot keep token order with writes first.
+// Entry: {slot, weight bits, chunk-local token | (read ? 1<<31 : 0), position}.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void bucket_scatter_kernel(StreamArgs a) {
+  __shared__ int cur[MAX_GT];
+  const int64_t w = blockIdx.x / a.rounds;
+  const int r = (int)(blockIdx.x - w * a.rounds);
+  const int64_t b = w / a.H;
+  const int h = (int)(w - b * a.H);
+  const int lane = threadIdx.x;
+  for (int g = lane; g < a.GT; g += 64)
+    cur[g] = a.offsets[((int64_t)w * a.GT + g) * (a.rounds + 1) + r];
+  __syncthreads();
+  uint4* ent = a.entries + w * a.walk_entries;
+  const int64_t t_lo = (int64_t)r * ROUND;
+  const int64_t t_hi = min<int64_t>(a.Tc, t_lo + ROUND);
+  for (int64_t t = t_lo; t < t_hi; ++t) {
+    const int64_t tok = (b * a.T + a.t0 + t) * a.H + h;
+    for (int k = lane; k < a.W; k += 64) {
+      const int32_t s = a.idx_w[tok * a.W + k];
+      const float q = a.wt_w[tok * a.W + k];
+      const int pos = atomicAdd(&cur[group_of((uint32_t)s, a.log2GT)], 1);
+      ent[pos] = make_uint4((uint32_t)s, __float_as_uint(q), (uint32_t)t, (uint32_t)k);
+    }
+    for (int k = lane; k < a.R; k += 64) {
+      const int32_t s = a.idx_r[tok * a.R + k];
+      const float q = a.wt_r[tok * a.R + k];
+      const int pos = atomicAdd(&cur[group_of((uint32_t)s, a.log2GT)], 1);
+      ent[pos] = make_uint4((uint32_t)s, __float_as_uint(q), (uint32_t)t | 0x80000000u,
+                            (uint32_t)k);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The scan proper.  Workgroup = (walk, slice, part); NT threads; SW floats per
+// slice; LPG = SW/4 lanes per group; GW = NT/LPG groups; batches of BQ accesses.
+// Per round the slice of v and the gates of the round's tokens are staged in LDS,
+// so a batch only holds its BQ state rows in registers while they are in flight.
+// ---------------------------------------------------------------------------
+template <int NT, int SW, int BQ>
+__global__ __launch_bounds__(NT) void stream_scan_kernel(StreamArgs a) {
+  constexpr int LPG = SW / 4;
+  constexpr int GW = NT / LPG;
+  constexpr int EPL = (BQ + LPG - 1) / LPG;  // entries loaded per lane per batch
+  __shared__ __attribute__((aligned(16))) float yr[2 * ROUND * SW];  // read partial sums
+  __shared__ __attribute__((aligned(16))) float vs[ROUND * SW];      // v slice of the round
+  __shared__ float2 gab[ROUND];                                      // (alpha, beta)
+
+  const int tid = threadIdx.x;
+  const int li = tid % LPG;
+  const int g = tid / LPG;
+  const int64_t wg = blockIdx.x;
+  const int p = (int)(wg % a.parts);
+  const int64_t ws = wg / a.parts;
+  const int sl = (int)(ws % a.S);
+  const int64_t w = ws / a.S;
+  const int64_t b = w / a.H;
+  const int h = (int)(w - b * a.H);
+  const int gg = p * GW + g;
+  const int dv = a.d_v;
+
+  for (int x = tid; x < 2 * ROUND * SW; x += NT) yr[x] = 0.0f;
+
+  // state of this walk as a uniform base; rows addressed by 32-bit byte offsets
+  char* Mb = reinterpret_cast<char*>(a.state + w * (int64_t)a.N * dv);
+  const uint32_t col_bytes = (uint32_t)(sl * SW + li * 4) * 4u;
+  const uint32_t row_bytes = (uint32_t)dv * 4u;
+  const uint4* ent = a.entries + w * a.walk_entries;
+  const int* offs = a.offsets + ((int64_t)w * a.GT + gg) * (a.rounds + 1);
+  const int64_t tok_base = (b * a.T + a.t0) * a.H + h;  // token t -> tok_base + t*H
+  float4* trash = a.trash + wg * NT + tid;
+
+  for (int r = 0; r < a.rounds; ++r) {
+    const int half = r & 1;
+    const int64_t t_lo = (int64_t)r * ROUND;
+    const int nt = (int)min<int64_t>(ROUND, a.Tc - t_lo);
+    // stage v slice and gates of this round's tokens
+    for (int x = tid; x < nt * LPG; x += NT) {
+      const int tt = x / LPG, c4 = x % LPG;
+      const int64_t tok = tok_base + (t_lo + tt) * a.H;
+      *reinterpret_cast<float4*>(vs + tt * SW + c4 * 4) =
+          *reinterpret_cast<const float4*>(a.v + tok * dv + sl * SW + c4 * 4);
+    }
+    for (int x = tid; x < nt; x += NT) {
+      const int64_t tok = tok_base + (t_lo + x) * a.H;
+      gab[x] = make_float2(a.alpha[tok], a.beta[tok]);
+    }
+    __syncthreads();
+
+    const int beg = offs[r];
+    const int end = offs[r + 1];
+    uint4 e[EPL];
+#pragma unroll
+    for (int q = 0; q < EPL; ++q) e[q] = ent[max(min(beg + q * LPG + li, end - 1), 0)];
+    // once per round: the first batch's entries are complete before the batch loop,
+    // so the loop header carries no pending load
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    for (int i = beg; i < end; i += BQ) {
+      // next batch's entries travel with this batch's row loads
+      uint4 en[EPL];
+#pragma unroll
+      for (int q = 0; q < EPL; ++q) en[q] = ent[min(i + BQ + q * LPG + li, end - 1)];
+      uint32_t slot[BQ], tk[BQ];
+      float wq[BQ];
+      uint32_t wrm = 0, vam = 0;  // bit j: access j is a valid write / is valid
+      float4 mv[BQ];
+#pragma unroll
+      for (int j = 0; j < BQ; ++j) {
+        const int src = j % LPG, q = j / LPG;
+        slot[j] = (uint32_t)__shfl((int)e[q].x, src, LPG);
+        wq[j] = __uint_as_float((uint32_t)__shfl((int)e[q].y, src, LPG));
+        const uint32_t tf = (uint32_t)__shfl((int)e[q].z, src, LPG);
+        tk[j] = (tf & 0x7fffffffu) - (uint32_t)t_lo;  // token within the round
+        const bool valid = i + j < end;
+        vam |= (uint32_t)valid << j;
+        wrm |= (uint32_t)(valid && !(tf & 0x80000000u)) << j;
+      }
+#pragma unroll
+      for (int j = 0; j < BQ; ++j)
+        mv[j] = *reinterpret_cast<const float4*>(Mb + (slot[j] * row_bytes + col_bytes));
+#pragma unroll
+      for (int j = 0; j < BQ; ++j) {
+        float4 val = mv[j];
+#pragma unroll
+        for (int jj = 0; jj < j; ++jj) {
+          const bool fwd = ((wrm >> jj) & 1u) && slot[jj] == slot[j];
+          val.x = fwd ? mv[jj].x : val.x;
+          val.y = fwd ? mv[jj].y : val.y;
+          val.z = fwd ? mv[jj].z : val.z;
+          val.w = fwd ? mv[jj].w : val.w;
+        }
+        const bool isw = (wrm >> j) & 1u;
+        {
+          // every access stores once (the vector-memory counter then stays static);
+          // accesses that do not write go to this lane's trash slot
+          const float2 ab = gab[tk[j]];
+          const float4 vv = *reinterpret_cast<const float4*>(vs + tk[j] * SW + li * 4);
+          const float c = ab.y * wq[j];
+          const float oc = 1.0f - c;
+          float4 nv;
+          nv.x = fmaf(c, vv.x, oc * (ab.x * val.x));
+          nv.y = fmaf(c, vv.y, oc * (ab.x * val.y));
+          nv.z = fmaf(c, vv.z, oc * (ab.x * val.z));
+          nv.w = fmaf(c, vv.w, oc * (ab.x * val.w));
+          val.x = isw ? nv.x : val.x;
+          val.y = isw ? nv.y : val.y;
+          val.z = isw ? nv.z : val.z;
+          val.w = isw ? nv.w : val.w;
+          uint64_t dst = isw ? reinterpret_cast<uint64_t>(Mb + (slot[j] * row_bytes + col_bytes))
+                             : reinterpret_cast<uint64_t>(trash);
+          asm volatile("" : "+v"(dst));  // keep one unconditional store: hide the select
+          typedef float gvec4 __attribute__((ext_vector_type(4)));
+          *reinterpret_cast<__attribute__((address_space(1))) gvec4*>(dst) =
+              gvec4{val.x, val.y, val.z, val.w};
+        }
+        if (!isw && ((vam >> j) & 1u)) {
+          float* y = yr + (half * ROUND + tk[j]) * SW + li * 4;
+          atomicAdd(y + 0, wq[j] * val.x);
+          atomicAdd(y + 1, wq[j] * val.y);
+          atomicAdd(y + 2, wq[j] * val.z);
+          atomicAdd(y + 3, wq[j] * val.w);
+        }
+        mv[j] = val;  // value after this access (forward source for later ones)
+      }
+#pragma unroll
+      for (int q = 0; q < EPL; ++q) e[q] = en[q];
+    }
+    __syncthreads();
+    // flush this round's partial read vectors and clear the ring half
+    for (int x = tid; x < nt * LPG; x += NT) {
+      const int tt = x / LPG, c4 = x % LPG;
+      float4* src = reinterpret_cast<float4*>(yr + (half * ROUND + tt) * SW + c4 * 4);
+      const int64_t yi = ((((int64_t)p * a.B + b) * a.Tc + t_lo + tt) * a.H + h) * dv +
+                         sl * SW + c4 * 4;
+      *reinterpret_cast<float4*>(a.y_part + yi) = *src;
+      *src = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Sum of the parts, RMSNorm over d_v and the output gate; one wavefront per
+// (token, head), each lane DV/64 columns (DV >= 64) or a row of 4 (DV < 64).
+// ---------------------------------------------------------------------------
+template <int DV>
+__global__ __launch_bounds__(256) void norm_gate_kernel(StreamArgs a) {
+  constexpr int LPR = DV / 4 < 64 ? DV / 4 : 64;  // lanes per row
+  constexpr int CPL = DV / LPR;                  // columns per lane (multiple of 4)
+  constexpr int RPW = 64 / LPR;                  // rows per wavefront
+  const int lane = threadIdx.x & 63;
+  const int sub = lane / LPR, li = lane % LPR;
+  const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + sub;
+  const int64_t rows = a.B * a.Tc * a.H;
+  const bool ok = row < rows;
+  const int64_t rr = ok ? row : 0;
+  const int64_t h = rr % a.H;
+  const int64_t bt = rr / a.H;
+  const int64_t b = bt / a.Tc, t = bt % a.Tc;
+  const int64_t grow = (b * a.T + a.t0 + t) * a.H + h;  // row of the full [B,T,H] arrays
+  float y[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) y[c] = 0.0f;
+  for (int p = 0; p < a.parts; ++p) {
+    const float* src = a.y_part + ((int64_t)p * rows + rr) * DV + li * CPL;
+#pragma unroll
+    for (int c = 0; c < CPL; c += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(src + c);
+      y[c] += v.x;
+      y[c + 1] += v.y;
+      y[c + 2] += v.z;
+      y[c + 3] += v.w;
+    }
+  }
+  float ss = 0.0f;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) ss += y[c] * y[c];
+  for (int off = LPR / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off, LPR);
+  const float rn = rsqrtf(ss / (float)DV + a.eps);
+  if (!ok) return;
+  const float* gt = a.gate + grow * DV + li * CPL;
+  float* o = a.out + grow * DV + li * CPL;
+  float* yo = a.y_raw ? a.y_raw + grow * DV + li * CPL : nullptr;
+#pragma unroll
+  for (int c = 0; c < CPL; c += 4) {
+    const float4 gv = *reinterpret_cast<const float4*>(gt + c);
+    float4 nw = make_float4(1.f, 1.f, 1.f, 1.f);
+    if (a.norm_w) nw = *reinterpret_cast<const float4*>(a.norm_w + h * DV + li * CPL + c);
+    float4 ov;
+    ov.x = y[c] * rn * nw.x * gv.x;
+    ov.y = y[c + 1] * rn * nw.y * gv.y;
+    ov.z = y[c + 2] * rn * nw.z * gv.z;
+    ov.w = y[c + 3] * rn * nw.w * gv.w;
+    *reinterpret_cast<float4*>(o + c) = ov;
+    if (yo) *reinterpret_cast<float4*>(yo + c) = make_float4(y[c], y[c + 1], y[c + 2], y[c + 3]);
+  }
+}
+
+int ilog2(int x) {
+  int l = 0;
+  while ((1 << l) < x) ++l;
+  return l;
+}
+
+}  // namespace
+
+StreamPlan plan_stream(const sdm_dims& d, int64_t N) {
+  (void)N;
+  StreamPlan pl;
+  pl.SW = d.d_v >= 32 ? 32 : d.d_v;
+  pl.S = d.d_v / pl.SW;
+  pl.NT = 1024;
+  const int lpg = pl.SW / 4;
+  const int gw = pl.NT / lpg;
+  const int64_t walks = d.B * (int64_t)d.H;
+  // enough workgroups to give every CU one (256 CUs), within MAX_GT groups per walk
+  int parts = 1;
+  while (walks * pl.S * parts < 256 && gw * parts * 2 <= MAX_GT) parts *= 2;
+  pl.parts = parts;
+  pl.GT = gw * parts;
+  pl.log2GT = ilog2(pl.GT);
+  // token chunk: bound the entries + partial-read buffers to ~2 GiB
+  const int64_t per_tok = walks * (d.W + d.R) * 16 + (int64_t)parts * walks * d.d_v * 4;
+  int64_t tc = (2ll << 30) / per_tok;
+  tc = tc < ROUND ? ROUND : (tc / ROUND) * ROUND;
+  pl.Tc = d.T < tc ? d.T : tc;
+  pl.rounds = (int)((pl.Tc + ROUND - 1) / ROUND);
+  return pl;
+}
+
+size_t stream_workspace_bytes(const sdm_dims& d, const StreamPlan& pl) {
+  const int64_t walks = d.B * (int64_t)d.H;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  size_t s = 0;
+  s += al((size_t)walks * pl.rounds * pl.GT * 4);                 // counts
+  s += al((size_t)walks * pl.GT * (pl.rounds + 1) * 4);           // offsets
+  s += al((size_t)walks * pl.Tc * (d.W + d.R) * 16);              // entries
+  s += al((size_t)pl.parts * d.B * pl.Tc * d.H * d.d_v * 4);      // y_part
+  s += al((size_t)walks * pl.S * pl.parts * pl.NT * 16);          // trash
+  return s;
+}
+
+hipError_t launch_stream_scan(const ScanArgs& sa, const StreamPlan& pl, void* ws,
+                              hipStream_t st) {
+  StreamArgs a;
+  a.idx_w = sa.idx_w;
+  a.wt_w = sa.wt_w;
+  a.idx_r = sa.idx_r;
+  a.wt_r = sa.wt_r;
+  a.v = sa.v;
+  a.gate = sa.gate;
+  a.alpha = sa.alpha;
+  a.beta = sa.beta;
+  a.norm_w = sa.norm_w;
+  a.state = sa.state;
+  a.out = sa.out;
+  a.y_raw = sa.y_raw;
+  a.B = sa.B;
+  a.T = sa.T;
+  a.H = sa.H;
+  a.N = sa.N;
+  a.W = sa.W;
+  a.R = sa.R;
+  a.d_v = sa.d_v;
+  a.eps = sa.eps;
+  a.S = pl.S;
+  a.parts = pl.parts;
+  a.GT = pl.GT;
+  a.log2GT = pl.log2GT;
+  const int64_t walks = sa.B * (int64_t)sa.H;
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  for (int64_t t0 = 0; t0 < sa.T; t0 += pl.Tc) {
+    a.t0 = t0;
+    a.Tc = sa.T - t0 < pl.Tc ? sa.T - t0 : pl.Tc;
+    a.rounds = (int)((a.Tc + ROUND - 1) / ROUND);
+    char* p = static_cast<char*>(ws);
+    a.counts = reinterpret_cast<int*>(p);
+    p += al((size_t)walks * pl.rounds * pl.GT * 4);
+    a.offsets = reinterpret_cast<int*>(p);
+    p += al((size_t)walks * pl.GT * (pl.rounds + 1) * 4);
+    a.entries = reinterpret_cast<uint4*>(p);
+    p += al((size_t)walks * pl.Tc * (sa.W + sa.R) * 16);
+    a.walk_entries = a.Tc * (sa.W + sa.R);
+    a.y_part = reinterpret_cast<float*>(p);
+    p += al((size_t)pl.parts * sa.B * pl.Tc * sa.H * sa.d_v * 4);
+    a.trash = reinterpret_cast<float4*>(p);
+
+    hipLaunchKernelGGL(bucket_count_kernel, dim3((unsigned)(walks * a.rounds)), dim3(256), 0, st,
+                       a);
+    hipLaunchKernelGGL(bucket_offsets_kernel, dim3((unsigned)walks), dim3(1024), 0, st, a);
+    hipLaunchKernelGGL(bucket_scatter_kernel, dim3((unsigned)(walks * a.rounds)), dim3(64), 0, st,
+                       a);
+    const dim3 grid((unsigned)(walks * pl.S * pl.parts));
+    if (pl.SW == 32)
+      hipLaunchKernelGGL((stream_scan_kernel<1024, 32, 8>), grid, dim3(1024), 0, st, a);
+    else
+      hipLaunchKernelGGL((stream_scan_kernel<1024, 16, 8>), grid, dim3(1024), 0, st, a);
+    const int64_t rows = sa.B * a.Tc * sa.H;
+    // rows per 256-thread block: 4 wavefronts x (64 / lanes per row)
+    const int lpr = sa.d_v / 4 < 64 ? sa.d_v / 4 : 64;
+    const int64_t rpb = 4 * (64 / lpr);
+    const dim3 ng((unsigned)((rows + rpb - 1) / rpb));
+    switch (sa.d_v) {
+      case 16: hipLaunchKernelGGL(norm_gate_kernel<16>, ng, dim3(256), 0, st, a); break;
+      case 32: hipLaunchKernelGGL(norm_gate_kernel<32>, ng, dim3(256), 0, st, a); break;
+      case 64: hipLaunchKernelGGL(norm_gate_kernel<64>, ng, dim3(256), 0, st, a); break;
+      case 128: hipLaunchKernelGGL(norm_gate_kernel<128>, ng, dim3(256), 0, st, a); break;
+      case 256: hipLaunchKernelGGL(norm_gate_kernel<256>, ng, dim3(256), 0, st, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace sdm

@@ -25,7 +25,8 @@ struct Derived {
 
 int32_t check_dims(const sdm_dims* d, Derived* out) {
   if (!d) return SDM_ERR_NULL;
-  if (d->flags != 0) return SDM_ERR_UNSUPPORTED;
+  if (d->flags & ~(SDM_FLAG_SCAN_DIRECT | SDM_FLAG_SCAN_STREAM)) return SDM_ERR_UNSUPPORTED;
+  if ((d->flags & SDM_FLAG_SCAN_DIRECT) && (d->flags & SDM_FLAG_SCAN_STREAM)) return SDM_ERR_SHAPE;
   if (d->in_dtype != SDM_DTYPE_F32 && d->in_dtype != SDM_DTYPE_BF16) return SDM_ERR_DTYPE;
   if (d->gate_act < SDM_GATE_NONE || d->gate_act > SDM_GATE_SILU) return SDM_ERR_DTYPE;
   if (d->B < 0 || d->T < 0 || d->d_model < 1 || d->H < 1 || d->n < 1 || d->W < 1 || d->R < 1 ||
@@ -157,7 +158,7 @@ int32_t run_scan(const sdm_dims* d, const Derived& dv, const sdm_sel* in, const 
   a.R = d->R;
   a.d_v = d->d_v;
   a.eps = d->eps;
-  return hip_status(launch_scan(a, ws, ws_bytes, st));
+  return hip_status(launch_scan(*d, a, ws, ws_bytes, st));
 }
 
 }  // namespace

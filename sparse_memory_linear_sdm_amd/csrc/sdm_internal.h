@@ -50,7 +50,41 @@ struct ScanArgs {
   int32_t H, N, W, R, d_v;
   float eps;
 };
-hipError_t launch_scan(const ScanArgs& a, void* ws, size_t ws_bytes, hipStream_t s);
+hipError_t launch_scan(const sdm_dims& d, const ScanArgs& a, void* ws, size_t ws_bytes,
+                       hipStream_t s);
 size_t scan_workspace_bytes(const sdm_dims& d);
+
+// Slot-owner stream schedule of the scan (scan_stream.hip).
+struct StreamArgs {
+  const int32_t* idx_w;
+  const float* wt_w;
+  const int32_t* idx_r;
+  const float* wt_r;
+  const float* v;
+  const float* gate;
+  const float* alpha;
+  const float* beta;
+  const float* norm_w;
+  float* state;
+  float* out;
+  float* y_raw;
+  int* counts;     // [walks][rounds][GT]
+  int* offsets;    // [walks][GT][rounds + 1]
+  uint4* entries;  // [walks][walk_entries]
+  float* y_part;   // [parts][B][Tc][H][d_v]
+  float4* trash;   // one float4 per scan thread: sink of non-writing accesses' stores
+  int64_t B, T, t0, Tc, walk_entries;
+  int32_t H, N, W, R, d_v;
+  float eps;
+  int32_t S, parts, GT, log2GT, rounds;
+};
+struct StreamPlan {
+  int SW, S, NT, parts, GT, log2GT, rounds;
+  int64_t Tc;
+};
+StreamPlan plan_stream(const sdm_dims& d, int64_t N);
+size_t stream_workspace_bytes(const sdm_dims& d, const StreamPlan& pl);
+hipError_t launch_stream_scan(const ScanArgs& a, const StreamPlan& pl, void* ws, hipStream_t s);
+bool scan_uses_stream(const sdm_dims& d);
 
 }  // namespace sdm
