@@ -11,14 +11,57 @@
 //   2. of the k*k combinations keep only ranks (r1, r2) with (r1+1)(r2+1) <= count
 //      -- every pair (r1' <= r1, r2' <= r2) beats (r1, r2), so the others cannot
 //      make the cut (280 candidates instead of 4096 for count = 64);
-//   3. score the candidates in fp64 (the sum of two fp32 values is exact there),
-//      rank by (score desc, slot id asc), keep `count`;
+//   3. rank the candidates by (exact fp64 score desc, slot id asc), keep `count`;
 //   4. return the ids ascending with softmax weights of their scores.
-// One wavefront per problem; the ranking steps are bitonic sorts in LDS.
+//
+// One wavefront per problem, everything in registers but two 256-bin histograms:
+//  * a top-k is an exact radix select on order-preserving 32-bit keys (four 8-bit
+//    passes over a wave-wide histogram + prefix scan), then compaction and a
+//    register bitonic sort of the k survivors;
+//  * the candidates' fp32-rounded sums order them monotonically with the exact
+//    sums, so the radix select runs on them and only the candidates tied at the
+//    fp32 threshold are ordered by their exact fp64 sums and ids.
 #include "sdm_internal.h"
 
 namespace sdm {
 namespace {
+
+// ---------------------------------------------------------------------------
+// Candidate table: for every count c in [1, 128] the pairs (r1, r2) with
+// (r1+1)(r2+1) <= c, row by row, packed as r1 << 8 | r2.  Built at compile time.
+// ---------------------------------------------------------------------------
+constexpr int cand_count(int c) {
+  int s = 0;
+  for (int a = 1; a <= c; ++a) s += c / a;
+  return s;
+}
+constexpr int cand_total() {
+  int s = 0;
+  for (int c = 1; c <= SDM_MAX_COUNT; ++c) s += cand_count(c);
+  return s;
+}
+constexpr int kCandTotal = cand_total();
+
+struct CandTable {
+  uint16_t off[SDM_MAX_COUNT + 2];
+  uint16_t rc[kCandTotal];
+};
+
+constexpr CandTable make_cand_table() {
+  CandTable t{};
+  int p = 0;
+  t.off[0] = 0;
+  t.off[1] = 0;
+  for (int c = 1; c <= SDM_MAX_COUNT; ++c) {
+    t.off[c] = (uint16_t)p;
+    for (int r1 = 0; r1 < c; ++r1)
+      for (int r2 = 0; (r1 + 1) * (r2 + 1) <= c; ++r2) t.rc[p++] = (uint16_t)(r1 << 8 | r2);
+  }
+  t.off[SDM_MAX_COUNT + 1] = (uint16_t)p;
+  return t;
+}
+
+__device__ const CandTable kCand = make_cand_table();
 
 // fp32 -> uint32 whose unsigned order is the float order (-0 folded onto +0).
 __device__ __forceinline__ uint32_t ord32(float f) {
@@ -30,64 +73,325 @@ __device__ __forceinline__ float unord32(uint32_t k) {
   uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
   return __uint_as_float(u);
 }
-__device__ __forceinline__ uint64_t ord64(double d) {
-  uint64_t u = (uint64_t)__double_as_longlong(d);
-  if ((u << 1) == 0) u = 0;
-  return (u & 0x8000000000000000ull) ? ~u : (u | 0x8000000000000000ull);
-}
-__device__ __forceinline__ double unord64(uint64_t k) {
-  uint64_t u = (k & 0x8000000000000000ull) ? (k & 0x7fffffffffffffffull) : ~k;
-  return __longlong_as_double((long long)u);
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
 }
 
-// Bitonic sort of np (power of two) entries so that better() entries come first.
-// The block is a single wavefront, so __syncthreads() is a cheap wave barrier.
-template <typename Better>
-__device__ void bitonic_best_first(uint64_t* key, uint32_t* id, int np, Better better) {
-  const int lane = threadIdx.x;
-  for (int size = 2; size <= np; size <<= 1) {
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// Exact radix select over 32-bit keys (larger is better) held KPL per lane.
+// Returns T with (#keys > T) < need <= (#keys >= T); need_eq = need - #keys > T.
+// hist: 256 words of this wavefront's LDS.  The block is one wavefront, so
+// __syncthreads() only orders this wave's LDS traffic.
+template <int KPL>
+__device__ uint32_t radix_select(const uint32_t (&key)[KPL], uint32_t valid, int need,
+                                 uint32_t* hist, int& need_eq) {
+  const int lane = lane_id();
+  uint32_t prefix = 0;
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    reinterpret_cast<uint4*>(hist)[lane] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < KPL; ++q) {
+      const bool m = ((valid >> q) & 1u) &&
+                     (pass == 0 || (key[q] >> (shift + 8)) == (prefix >> (shift + 8)));
+      if (m) atomicAdd(&hist[(key[q] >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    // lane l owns bins 255-4l (highest) .. 252-4l
+    const uint4 hv = reinterpret_cast<const uint4*>(hist)[63 - lane];
+    const int local = (int)(hv.x + hv.y + hv.z + hv.w);
+    const int incl = wave_incl_scan(local);
+    const int excl = incl - local;
+    const unsigned long long bal = __ballot(incl >= need);
+    const int L = __ffsll((long long)bal) - 1;
+    int digit = 0, rest = 0;
+    if (lane == L) {
+      int acc = excl;
+      const int c3 = (int)hv.w, c2 = (int)hv.z, c1 = (int)hv.y;
+      if (acc + c3 >= need) {
+        digit = 255 - 4 * lane;
+      } else if ((acc += c3) + c2 >= need) {
+        digit = 254 - 4 * lane;
+      } else if ((acc += c2) + c1 >= need) {
+        digit = 253 - 4 * lane;
+      } else {
+        acc += c1;
+        digit = 252 - 4 * lane;
+      }
+      rest = need - acc;
+    }
+    digit = __shfl(digit, L);
+    need = __shfl(rest, L);
+    prefix |= (uint32_t)digit << shift;
+    __syncthreads();
+  }
+  need_eq = need;
+  return prefix;
+}
+
+// Bitonic sort of NE = 64*EPL 64-bit keys (element e = lane + 64*r in v[r]) so that
+// larger keys come first.
+template <int EPL>
+__device__ void bitonic_desc(uint64_t (&v)[EPL]) {
+  const int lane = lane_id();
+  constexpr int NE = 64 * EPL;
+#pragma unroll
+  for (int size = 2; size <= NE; size <<= 1) {
+#pragma unroll
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int p = lane; p < (np >> 1); p += 64) {
-        const int i = ((p / stride) * 2 * stride) + (p & (stride - 1));
-        const int j = i + stride;
-        const bool first_best = (i & size) == 0;
-        const uint64_t ki = key[i], kj = key[j];
-        const uint32_t ii = id ? id[i] : 0u, ij = id ? id[j] : 0u;
-        const bool swap = first_best ? better(kj, ij, ki, ii) : better(ki, ii, kj, ij);
-        if (swap) {
-          key[i] = kj;
-          key[j] = ki;
-          if (id) {
-            id[i] = ij;
-            id[j] = ii;
+      if (stride >= 64) {  // partner in the same lane
+#pragma unroll
+        for (int r = 0; r < EPL; ++r) {
+          const int e = lane + 64 * r;
+          const int pr = r ^ (stride >> 6);
+          if (pr > r) {
+            const bool desc = (e & size) == 0;
+            const uint64_t lo = v[r], hi = v[pr];
+            const bool sw = desc ? (hi > lo) : (lo > hi);
+            v[r] = sw ? hi : lo;
+            v[pr] = sw ? lo : hi;
           }
         }
+      } else {
+#pragma unroll
+        for (int r = 0; r < EPL; ++r) {
+          const int e = lane + 64 * r;
+          const uint32_t olo = (uint32_t)__shfl_xor((int)(uint32_t)v[r], stride);
+          const uint32_t ohi = (uint32_t)__shfl_xor((int)(uint32_t)(v[r] >> 32), stride);
+          const uint64_t o = ((uint64_t)ohi << 32) | olo;
+          const bool desc = (e & size) == 0;
+          const bool lower = (e & stride) == 0;
+          // in a descending run the lower position keeps the larger key
+          const bool keep_max = (desc == lower);
+          v[r] = keep_max ? (o > v[r] ? o : v[r]) : (o < v[r] ? o : v[r]);
+        }
       }
-      __syncthreads();
     }
   }
 }
 
-__device__ __forceinline__ int pow2_at_least(int x) {
-  int p = 1;
-  while (p < x) p <<= 1;
-  return p;
+// Best k (<= 128) of the n values of one half, by (value desc, index asc).
+// Writes the sorted survivors to val[0..k) / idx[0..k) (LDS).
+template <int KPL>
+__device__ void half_topk(const float* __restrict__ src, int n, int k, uint32_t* hist,
+                          uint64_t* stage, float* val, uint32_t* idx) {
+  const int lane = lane_id();
+  uint32_t key[KPL];
+  uint32_t valid = 0;
+#pragma unroll
+  for (int q = 0; q < KPL; ++q) {
+    const int i = lane * KPL + q;
+    const bool ok = i < n;
+    key[q] = ok ? ord32(src[i]) : 0u;
+    valid |= (uint32_t)ok << q;
+  }
+  int need_eq;
+  const uint32_t T = radix_select<KPL>(key, valid, k, hist, need_eq);
+  // compaction: keys above T, then the lowest-index keys equal to T
+  int eq_local = 0;
+#pragma unroll
+  for (int q = 0; q < KPL; ++q) eq_local += (((valid >> q) & 1u) && key[q] == T) ? 1 : 0;
+  const int eq_excl = wave_incl_scan(eq_local) - eq_local;
+  uint32_t sel = 0;
+  int eq_seen = 0;
+#pragma unroll
+  for (int q = 0; q < KPL; ++q) {
+    const bool v = (valid >> q) & 1u;
+    const bool eq = v && key[q] == T;
+    const bool s = (v && key[q] > T) || (eq && eq_excl + eq_seen < need_eq);
+    eq_seen += eq ? 1 : 0;
+    sel |= (uint32_t)s << q;
+  }
+  const int sel_local = __popc(sel);
+  int pos = wave_incl_scan(sel_local) - sel_local;
+#pragma unroll
+  for (int q = 0; q < KPL; ++q)
+    if ((sel >> q) & 1u) {
+      const uint32_t i = (uint32_t)(lane * KPL + q);
+      stage[pos++] = ((uint64_t)key[q] << 32) | (0xffffffffu - i);
+    }
+  __syncthreads();
+  if (k <= 64) {
+    uint64_t v[1] = {lane < k ? stage[lane] : 0ull};
+    bitonic_desc<1>(v);
+    if (lane < k) {
+      val[lane] = unord32((uint32_t)(v[0] >> 32));
+      idx[lane] = 0xffffffffu - (uint32_t)v[0];
+    }
+  } else {
+    uint64_t v[2] = {stage[lane], lane + 64 < k ? stage[lane + 64] : 0ull};
+    bitonic_desc<2>(v);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int e = lane + 64 * r;
+      if (e < k) {
+        val[e] = unord32((uint32_t)(v[r] >> 32));
+        idx[e] = 0xffffffffu - (uint32_t)v[r];
+      }
+    }
+  }
+  __syncthreads();
 }
 
-constexpr int KEYS_BYTES = 2 * SDM_MAX_HALF * 8;  // two halves of 64-bit keys (16 KB)
+// (exact score, id) order: a beats b
+__device__ __forceinline__ bool beats(double sa, uint32_t ia, double sb, uint32_t ib) {
+  return sa > sb || (sa == sb && ia < ib);
+}
 
+// Combine the two sorted top-k lists into the best `count` slots; KPC candidates
+// per lane.  Writes ascending ids and softmax weights to oi / ow.
+template <int KPC>
+__device__ void combine(int n, int k, int count, const float* av, const uint32_t* ai,
+                        const float* bv, const uint32_t* bi, uint32_t* hist, uint64_t* stage,
+                        int32_t* __restrict__ oi, float* __restrict__ ow) {
+  const int lane = lane_id();
+  const int c0 = kCand.off[count];
+  const int nc = kCand.off[count + 1] - c0;
+  uint32_t key[KPC];
+  double sc[KPC];
+  uint32_t id[KPC];
+  uint32_t valid = 0;
+#pragma unroll
+  for (int q = 0; q < KPC; ++q) {
+    const int c = lane * KPC + q;
+    const uint32_t rc = c < nc ? kCand.rc[c0 + c] : 0xffffu;
+    const int r1 = (int)(rc >> 8), r2 = (int)(rc & 255u);
+    const bool ok = c < nc && r1 < k && r2 < k;
+    const float a = ok ? av[r1] : 0.0f, b = ok ? bv[r2] : 0.0f;
+    key[q] = ok ? ord32(a + b) : 0u;                 // fp32-rounded sum: monotone
+    sc[q] = (double)a + (double)b;                   // exact
+    id[q] = ok ? ai[r1] * (uint32_t)n + bi[r2] : 0u;
+    valid |= (uint32_t)ok << q;
+  }
+  int need_eq;
+  const uint32_t T = radix_select<KPC>(key, valid, count, hist, need_eq);
+  // candidates tied at the fp32 threshold: order them exactly
+  uint32_t eqm = 0;
+#pragma unroll
+  for (int q = 0; q < KPC; ++q) eqm |= (uint32_t)(((valid >> q) & 1u) && key[q] == T) << q;
+  const int eq_local = __popc(eqm);
+  const int eq_total = wave_sum(eq_local);
+  uint32_t sel = 0;
+#pragma unroll
+  for (int q = 0; q < KPC; ++q) sel |= (uint32_t)(((valid >> q) & 1u) && key[q] > T) << q;
+  if (eq_total == need_eq) {
+    sel |= eqm;
+  } else {
+    // gather the tied candidates, rank each one against the others
+    double* tsc = reinterpret_cast<double*>(stage);
+    uint32_t* tid = reinterpret_cast<uint32_t*>(stage + 64 * KPC);
+    int pos = wave_incl_scan(eq_local) - eq_local;
+#pragma unroll
+    for (int q = 0; q < KPC; ++q)
+      if ((eqm >> q) & 1u) {
+        tsc[pos] = sc[q];
+        tid[pos] = id[q];
+        ++pos;
+      }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < KPC; ++q)
+      if ((eqm >> q) & 1u) {
+        int rank = 0;
+        for (int u = 0; u < eq_total; ++u) rank += beats(tsc[u], tid[u], sc[q], id[q]) ? 1 : 0;
+        if (rank < need_eq) sel |= 1u << q;
+      }
+    __syncthreads();
+  }
+  // compaction of the `count` survivors as (id, exact score)
+  uint32_t* cid = reinterpret_cast<uint32_t*>(stage);
+  double* csc = reinterpret_cast<double*>(stage + 64);  // after 128 ids
+  const int sel_local = __popc(sel);
+  int pos = wave_incl_scan(sel_local) - sel_local;
+#pragma unroll
+  for (int q = 0; q < KPC; ++q)
+    if ((sel >> q) & 1u) {
+      cid[pos] = id[q];
+      csc[pos] = sc[q];
+      ++pos;
+    }
+  __syncthreads();
+  // sort survivors by id ascending: key = ~id (larger first), payload = position
+  const int ne = count <= 64 ? 1 : 2;
+  double smax = -__builtin_inf();
+  for (int e = lane; e < count; e += 64) smax = fmax(smax, csc[e]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) smax = fmax(smax, __shfl_xor(smax, o));
+  float wsum = 0.0f;
+  if (ne == 1) {
+    uint64_t v[1] = {lane < count ? (((uint64_t)(0xffffffffu - cid[lane]) << 32) | (uint32_t)lane)
+                                  : 0ull};
+    bitonic_desc<1>(v);
+    float w = 0.0f;
+    if (lane < count) w = expf((float)(csc[(uint32_t)v[0]] - smax));
+    wsum = w;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) wsum += __shfl_xor(wsum, o);
+    if (lane < count) {
+      oi[lane] = (int32_t)(0xffffffffu - (uint32_t)(v[0] >> 32));
+      ow[lane] = w / wsum;
+    }
+  } else {
+    uint64_t v[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int e = lane + 64 * r;
+      v[r] = e < count ? (((uint64_t)(0xffffffffu - cid[e]) << 32) | (uint32_t)e) : 0ull;
+    }
+    bitonic_desc<2>(v);
+    float w[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int e = lane + 64 * r;
+      w[r] = e < count ? expf((float)(csc[(uint32_t)v[r]] - smax)) : 0.0f;
+    }
+    wsum = w[0] + w[1];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) wsum += __shfl_xor(wsum, o);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int e = lane + 64 * r;
+      if (e < count) {
+        oi[e] = (int32_t)(0xffffffffu - (uint32_t)(v[r] >> 32));
+        ow[e] = w[r] / wsum;
+      }
+    }
+  }
+}
+
+// 64-bit staging words a combine with KPC candidates per lane needs: tied
+// candidates (64*KPC doubles + 64*KPC ids) or the survivors (128 ids + 128 doubles).
+constexpr int stage_words(int kpc) { return 96 * kpc > 192 ? 96 * kpc : 192; }
+
+// One wavefront per (row, head, role).  LDS: histogram, staging, two top-k lists.
+template <int KPL, int KPC>
 __global__ __launch_bounds__(64) void select_kernel(const float* __restrict__ scores, int64_t rows,
                                                     int H, int n, int W, int R,
                                                     int64_t out_row0, int32_t* __restrict__ idx_w,
                                                     float* __restrict__ wt_w,
                                                     int32_t* __restrict__ idx_r,
                                                     float* __restrict__ wt_r) {
-  __shared__ __attribute__((aligned(16))) unsigned char keys_raw[KEYS_BYTES];
-  __shared__ float topv[2][SDM_MAX_COUNT];
-  __shared__ uint32_t topi[2][SDM_MAX_COUNT];
-  __shared__ float red[64];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[256];
+  __shared__ __attribute__((aligned(16))) uint64_t stage[stage_words(KPC)];
+  __shared__ float tv[2][SDM_MAX_COUNT];
+  __shared__ uint32_t ti[2][SDM_MAX_COUNT];
 
-  const int lane = threadIdx.x;
   const int64_t prob = blockIdx.x;
   const int role = (int)(prob & 1);  // 0 = write, 1 = read
   const int64_t rh = prob >> 1;
@@ -97,99 +401,30 @@ __global__ __launch_bounds__(64) void select_kernel(const float* __restrict__ sc
   const int count = role ? R : W;
   const int k = count < n ? count : n;
   const float* half = scores + (r * H + h) * (int64_t)(4 * n) + role * 2 * n;
-
-  // ---- 1. best k of each half, ranked by (value desc, index asc) ----
-  uint64_t* hk = reinterpret_cast<uint64_t*>(keys_raw);
-  const int np = pow2_at_least(n);
-  for (int s = 0; s < 2; ++s) {
-    uint64_t* kk = hk + s * SDM_MAX_HALF;
-    for (int i = lane; i < np; i += 64) {
-      // low word: larger for smaller index, so equal values rank lower index first
-      kk[i] = (i < n) ? (((uint64_t)ord32(half[s * n + i]) << 32) | (uint32_t)(0xffffffffu - i))
-                      : 0ull;
-    }
-  }
-  __syncthreads();
-  auto key_only = [](uint64_t a, uint32_t, uint64_t b, uint32_t) { return a > b; };
-  bitonic_best_first(hk, nullptr, np, key_only);
-  bitonic_best_first(hk + SDM_MAX_HALF, nullptr, np, key_only);
-  for (int s = 0; s < 2; ++s)
-    for (int i = lane; i < k; i += 64) {
-      const uint64_t key = hk[s * SDM_MAX_HALF + i];
-      topv[s][i] = unord32((uint32_t)(key >> 32));
-      topi[s][i] = 0xffffffffu - (uint32_t)(key & 0xffffffffu);
-    }
-  __syncthreads();
-
-  // ---- 2. dominance-pruned candidates (r1+1)(r2+1) <= count ----
-  uint64_t* ck = reinterpret_cast<uint64_t*>(keys_raw);
-  int total = 0;
-  for (int r1 = 0; r1 < k; ++r1) {
-    const int c = min(k, count / (r1 + 1));
-    total += c;
-  }
-  const int npc = pow2_at_least(total);
-  uint32_t* cid = reinterpret_cast<uint32_t*>(keys_raw + npc * 8);
-  for (int r1 = lane; r1 < k; r1 += 64) {
-    int off = 0;
-    for (int a = 0; a < r1; ++a) off += min(k, count / (a + 1));
-    const int c = min(k, count / (r1 + 1));
-    const double va = (double)topv[0][r1];
-    const uint32_t ia = topi[0][r1] * (uint32_t)n;
-    for (int r2 = 0; r2 < c; ++r2) {
-      const double s = va + (double)topv[1][r2];  // exact in fp64
-      ck[off + r2] = ord64(s);
-      cid[off + r2] = ia + topi[1][r2];
-    }
-  }
-  for (int i = total + lane; i < npc; i += 64) {
-    ck[i] = 0ull;
-    cid[i] = 0xffffffffu;
-  }
-  __syncthreads();
-
-  // ---- 3. rank by (score desc, id asc), keep `count` ----
-  auto score_then_id = [](uint64_t a, uint32_t ia, uint64_t b, uint32_t ib) {
-    return a > b || (a == b && ia < ib);
-  };
-  bitonic_best_first(ck, cid, npc, score_then_id);
-  const double smax = unord64(ck[0]);
-  __syncthreads();
-
-  // ---- 4. ids ascending, softmax weights ----
-  const int npo = pow2_at_least(count);
-  for (int i = count + lane; i < npo; i += 64) {
-    ck[i] = 0ull;
-    cid[i] = 0xffffffffu;
-  }
-  __syncthreads();
-  auto id_asc = [](uint64_t, uint32_t ia, uint64_t, uint32_t ib) { return ia < ib; };
-  bitonic_best_first(ck, cid, npo, id_asc);
-
-  float wsum = 0.0f;
-  float wloc[SDM_MAX_COUNT / 64];
-#pragma unroll
-  for (int q = 0; q < SDM_MAX_COUNT / 64; ++q) {
-    const int i = lane + q * 64;
-    wloc[q] = (i < count) ? expf((float)(unord64(ck[i]) - smax)) : 0.0f;
-    wsum += wloc[q];
-  }
-  red[lane] = wsum;
-  __syncthreads();
-  float tot = 0.0f;
-  for (int i = 0; i < 64; ++i) tot += red[i];
-  const float inv = 1.0f / tot;
+  half_topk<KPL>(half, n, k, hist, stage, tv[0], ti[0]);
+  half_topk<KPL>(half + n, n, k, hist, stage, tv[1], ti[1]);
   const int64_t base = ((out_row0 + r) * H + h) * (int64_t)count;
-  int32_t* oi = role ? idx_r : idx_w;
-  float* ow = role ? wt_r : wt_w;
-#pragma unroll
-  for (int q = 0; q < SDM_MAX_COUNT / 64; ++q) {
-    const int i = lane + q * 64;
-    if (i < count) {
-      oi[base + i] = (int32_t)cid[i];
-      ow[base + i] = wloc[q] * inv;
-    }
-  }
+  combine<KPC>(n, k, count, tv[0], ti[0], tv[1], ti[1], hist, stage,
+               (role ? idx_r : idx_w) + base, (role ? wt_r : wt_w) + base);
+}
+
+template <int KPL>
+hipError_t launch_kpl(const float* scores, int64_t rows, int H, int n, int W, int R,
+                      int64_t out_row0, int32_t* idx_w, float* wt_w, int32_t* idx_r,
+                      float* wt_r, hipStream_t s) {
+  const int maxc = W > R ? W : R;
+  const int nc = cand_count(maxc);
+  const int kpc = (nc + 63) / 64;
+  const dim3 grid((unsigned)(rows * H * 2));
+#define SDM_SEL_LAUNCH(KPC)                                                                   \
+  hipLaunchKernelGGL((select_kernel<KPL, KPC>), grid, dim3(64), 0, s, scores, rows, H, n, W, R, \
+                     out_row0, idx_w, wt_w, idx_r, wt_r)
+  if (kpc <= 1) SDM_SEL_LAUNCH(1);
+  else if (kpc <= 2) SDM_SEL_LAUNCH(2);
+  else if (kpc <= 5) SDM_SEL_LAUNCH(5);
+  else SDM_SEL_LAUNCH(11);
+#undef SDM_SEL_LAUNCH
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -197,10 +432,16 @@ __global__ __launch_bounds__(64) void select_kernel(const float* __restrict__ sc
 hipError_t launch_select(const sdm_dims& d, const float* scores, int64_t rows, int64_t out_row0,
                          int32_t* idx_w, float* wt_w, int32_t* idx_r, float* wt_r,
                          hipStream_t s) {
-  const int64_t probs = rows * d.H * 2;
-  hipLaunchKernelGGL(select_kernel, dim3((unsigned)probs), dim3(64), 0, s, scores, rows, d.H, d.n,
-                     d.W, d.R, out_row0, idx_w, wt_w, idx_r, wt_r);
-  return hipGetLastError();
+  const int kpl = (d.n + 63) / 64;
+#define SDM_KPL(K) \
+  return launch_kpl<K>(scores, rows, d.H, d.n, d.W, d.R, out_row0, idx_w, wt_w, idx_r, wt_r, s)
+  if (kpl <= 1) SDM_KPL(1);
+  if (kpl <= 2) SDM_KPL(2);
+  if (kpl <= 4) SDM_KPL(4);
+  if (kpl <= 6) SDM_KPL(6);
+  if (kpl <= 8) SDM_KPL(8);
+  SDM_KPL(16);
+#undef SDM_KPL
 }
 
 }  // namespace sdm
