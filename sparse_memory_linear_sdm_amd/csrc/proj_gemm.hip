@@ -23,103 +23,202 @@ __device__ __forceinline__ float softplus_f(float z) {
 }
 __device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + expf(-z)); }
 
-__device__ __forceinline__ void epilogue_store(const ProjDst& d, int64_t m, int c, float val) {
+// Destination of one output column: element (m, c) goes to base[m * stride],
+// transformed by `kind` (0 copy, 1 sigmoid, 2 silu, 3 forget gate, 4 input gate).
+struct ColDst {
+  float* base;
+  int64_t stride;
+  int kind;
+  float A, bdt;
+};
+
+__device__ __forceinline__ ColDst column_dst(const ProjDst& d, int c) {
   const int h = c / d.P;
   const int p = c - h * d.P;
   const int n4 = 4 * d.n;
-  const int64_t mh = m * d.H + h;
-  if (p < n4) {
-    d.scores[((m - d.scores_row0) * d.H + h) * n4 + p] = val;
-  } else if (p < n4 + d.d_v) {
-    d.v[mh * d.d_v + (p - n4)] = val;
+  ColDst o;
+  o.A = 0.0f;
+  o.bdt = 0.0f;
+  if (p < n4) {  // half-scores, rows relative to the staging buffer's first row
+    o.base = d.scores + (-d.scores_row0 * d.H + h) * n4 + p;
+    o.stride = (int64_t)d.H * n4;
+    o.kind = 0;
   } else if (p < n4 + 2 * d.d_v) {
-    float g = val;
-    if (d.gate_act == SDM_GATE_SIGMOID) g = sigmoid_f(val);
-    else if (d.gate_act == SDM_GATE_SILU) g = val * sigmoid_f(val);
-    d.gate[mh * d.d_v + (p - n4 - d.d_v)] = g;
-  } else if (p == n4 + 2 * d.d_v) {
-    d.alpha[mh] = expf(-d.A[h] * softplus_f(val + d.b_dt[h]));
+    const bool is_v = p < n4 + d.d_v;
+    o.base = (is_v ? d.v + (p - n4) : d.gate + (p - n4 - d.d_v)) + (int64_t)h * d.d_v;
+    o.stride = (int64_t)d.H * d.d_v;
+    o.kind = is_v ? 0 : (d.gate_act == SDM_GATE_SIGMOID ? 1 : d.gate_act == SDM_GATE_SILU ? 2 : 0);
   } else {
-    d.beta[mh] = sigmoid_f(val);
+    const bool is_a = p == n4 + 2 * d.d_v;
+    o.base = (is_a ? d.alpha : d.beta) + h;
+    o.stride = d.H;
+    o.kind = is_a ? 3 : 4;
+    if (is_a) {
+      o.A = d.A[h];
+      o.bdt = d.b_dt[h];
+    }
+  }
+  return o;
+}
+
+__device__ __forceinline__ float column_value(const ColDst& o, float val) {
+  switch (o.kind) {
+    case 1: return sigmoid_f(val);
+    case 2: return val * sigmoid_f(val);
+    case 3: return expf(-o.A * softplus_f(val + o.bdt));
+    case 4: return sigmoid_f(val);
+    default: return val;
   }
 }
 
-// ---------------------------------------------------------------------------
-// bf16 path: 128x128 block tile, K-step 32, 4 waves each owning 64x64 as 2x2
-// MFMA 32x32x16 blocks.  LDS rows padded by 16 B to spread banks.
-// ---------------------------------------------------------------------------
-constexpr int BM = 128, BN = 128, BK = 32, LDK = BK + 8;
+// Store through a ColDst; rows beyond M and columns beyond Ncol are skipped.
+__device__ __forceinline__ void epilogue_store(const ProjDst& d, int64_t m, int c, float val) {
+  const ColDst o = column_dst(d, c);
+  o.base[m * o.stride] = column_value(o, val);
+}
 
-__global__ __launch_bounds__(256) void proj_gemm_bf16_kernel(
+// ---------------------------------------------------------------------------
+// bf16 path: 256x256 block tile, K-step 64, 8 waves (2 x 4) each owning 128x64
+// as 4x2 MFMA 32x32x16 blocks (each A fragment feeds 2 MFMAs, each B fragment 4).
+// The next K-tile is fetched into registers while the current one is multiplied
+// out of LDS (double-buffered, one barrier per K-step).  LDS rows are padded by
+// 16 B.  Tiles are handed out XCD by XCD in groups of GROUP_M row tiles, so the
+// blocks resident on one XCD share A and B slices through its L2.
+// ---------------------------------------------------------------------------
+constexpr int BM = 256, BN = 256, BK = 64, LDK = BK + 8, NTH = 512, GROUP_M = 4;
+constexpr int A_CHUNKS = BM * BK / 8 / NTH;  // 16-byte chunks per thread per K-tile
+constexpr int B_CHUNKS = BN * BK / 8 / NTH;
+constexpr int NXCD = 8;
+
+__global__ __launch_bounds__(NTH) void proj_gemm_bf16_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wp, int64_t row0, int64_t M,
     int Ncol, int K, ProjDst dst) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDK];
+
+  // XCD-aware grouped tile order: consecutive workgroups go to different XCDs,
+  // so give each XCD a contiguous range of tiles, walked GROUP_M rows at a time.
+  const int ntn = (Ncol + BN - 1) / BN;
+  const int64_t ntm = (M + BM - 1) / BM;
+  const int64_t total = ntm * ntn;
+  const int64_t per_xcd = (total + NXCD - 1) / NXCD;
+  const int64_t t = (int64_t)(blockIdx.x % NXCD) * per_xcd + blockIdx.x / NXCD;
+  if (t >= total) return;
+  const int64_t grp = t / ((int64_t)GROUP_M * ntn);
+  const int64_t first_m = grp * GROUP_M;
+  const int gm_rows = (int)min<int64_t>(GROUP_M, ntm - first_m);
+  const int64_t in_grp = t - grp * GROUP_M * ntn;
+  const int64_t tile_m = (first_m + in_grp % gm_rows) * BM;  // local row within [0, M)
+  const int tile_n = (int)(in_grp / gm_rows) * BN;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t tile_m = (int64_t)blockIdx.y * BM;   // local row within [0, M)
-  const int tile_n = blockIdx.x * BN;
+  const int wm = wave >> 2, wn = wave & 3;
 
-  floatx16 acc[2][2];
-  for (int i = 0; i < 2; ++i)
+  floatx16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
     for (int j = 0; j < 2; ++j)
+#pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  for (int k0 = 0; k0 < K; k0 += BK) {
-    // global -> LDS: each tile is 128 rows x 64 B = 512 chunks of 16 B
+  uint4 ra[A_CHUNKS], rb[B_CHUNKS];
+  auto fetch = [&](int k0) {
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int q = tid + it * 256;
-      const int r = q >> 2;
-      const int kc = (q & 3) * 8;
-      uint4 va = make_uint4(0, 0, 0, 0), vb = make_uint4(0, 0, 0, 0);
+    for (int it = 0; it < A_CHUNKS; ++it) {
+      const int q = tid + it * NTH;
+      const int r = q >> 3, kc = (q & 7) * 8;
       const int64_t gm = tile_m + r;
-      if (gm < M && k0 + kc < K)
-        va = *reinterpret_cast<const uint4*>(X + (row0 + gm) * (int64_t)K + k0 + kc);
-      const int gn = tile_n + r;
-      if (gn < Ncol && k0 + kc < K)
-        vb = *reinterpret_cast<const uint4*>(Wp + (int64_t)gn * K + k0 + kc);
-      *reinterpret_cast<uint4*>(As + r * LDK + kc) = va;
-      *reinterpret_cast<uint4*>(Bs + r * LDK + kc) = vb;
+      ra[it] = (gm < M && k0 + kc < K)
+                   ? *reinterpret_cast<const uint4*>(X + (row0 + gm) * (int64_t)K + k0 + kc)
+                   : make_uint4(0, 0, 0, 0);
     }
-    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < B_CHUNKS; ++it) {
+      const int q = tid + it * NTH;
+      const int r = q >> 3, kc = (q & 7) * 8;
+      const int gn = tile_n + r;
+      rb[it] = (gn < Ncol && k0 + kc < K)
+                   ? *reinterpret_cast<const uint4*>(Wp + (int64_t)gn * K + k0 + kc)
+                   : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int it = 0; it < A_CHUNKS; ++it) {
+      const int q = tid + it * NTH;
+      *reinterpret_cast<uint4*>(&As[buf][(q >> 3) * LDK + (q & 7) * 8]) = ra[it];
+    }
+#pragma unroll
+    for (int it = 0; it < B_CHUNKS; ++it) {
+      const int q = tid + it * NTH;
+      *reinterpret_cast<uint4*>(&Bs[buf][(q >> 3) * LDK + (q & 7) * 8]) = rb[it];
+    }
+  };
+
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  int cur = 0;
+  for (int k0 = 0; k0 < K; k0 += BK) {
+    const bool more = k0 + BK < K;
+    if (more) fetch(k0 + BK);
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 16) {
-      bf16x8 af[2], bfr[2];
+      const int kq = kk + (lane >> 5) * 8;
+      bf16x8 af[4], bfr[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int ra = wm * 64 + i * 32 + (lane & 31);
-        const int rb = wn * 64 + i * 32 + (lane & 31);
-        const int kq = kk + (lane >> 5) * 8;
-        uint4 ua = *reinterpret_cast<const uint4*>(As + ra * LDK + kq);
-        uint4 ub = *reinterpret_cast<const uint4*>(Bs + rb * LDK + kq);
-        __builtin_memcpy(&af[i], &ua, 16);
-        __builtin_memcpy(&bfr[i], &ub, 16);
+      for (int i = 0; i < 4; ++i) {
+        const uint4 u = *reinterpret_cast<const uint4*>(
+            &As[cur][(wm * 128 + i * 32 + (lane & 31)) * LDK + kq]);
+        __builtin_memcpy(&af[i], &u, 16);
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < 2; ++j) {
+        const uint4 u = *reinterpret_cast<const uint4*>(
+            &Bs[cur][(wn * 64 + j * 32 + (lane & 31)) * LDK + kq]);
+        __builtin_memcpy(&bfr[j], &u, 16);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
+    if (more) stash(cur ^ 1);
     __syncthreads();
+    cur ^= 1;
   }
 
   // 32x32 output block layout: register r of lane l holds
-  // row (r/4)*8 + (l/32)*4 + r%4, column l%32.
+  // row (r/4)*8 + (l/32)*4 + r%4, column l%32.  Each lane owns two columns.
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int j = 0; j < 2; ++j) {
+    const int c = tile_n + wn * 64 + j * 32 + (lane & 31);
+    if (c >= Ncol) continue;
+    const ColDst o = column_dst(dst, c);
+    if (o.kind == 0) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t lm = tile_m + wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        const int c = tile_n + wn * 64 + j * 32 + (lane & 31);
-        if (lm < M && c < Ncol) epilogue_store(dst, row0 + lm, c, acc[i][j][r]);
-      }
+        for (int r = 0; r < 16; ++r) {
+          const int64_t lm =
+              tile_m + wm * 128 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          if (lm < M) o.base[(row0 + lm) * o.stride] = acc[i][j][r];
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t lm =
+              tile_m + wm * 128 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          if (lm < M) o.base[(row0 + lm) * o.stride] = column_value(o, acc[i][j][r]);
+        }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -181,8 +280,9 @@ hipError_t launch_proj_gemm(const sdm_dims& d, const void* x, const void* w_proj
   const int Ncol = d.H * dst.P;
   const int K = (int)d.d_model;
   if (d.in_dtype == SDM_DTYPE_BF16) {
-    dim3 grid((Ncol + BN - 1) / BN, (unsigned)((rows + BM - 1) / BM));
-    hipLaunchKernelGGL(proj_gemm_bf16_kernel, grid, dim3(256), 0, s,
+    const int64_t tiles = ((rows + BM - 1) / BM) * ((Ncol + BN - 1) / BN);
+    const dim3 grid((unsigned)(((tiles + NXCD - 1) / NXCD) * NXCD));
+    hipLaunchKernelGGL(proj_gemm_bf16_kernel, grid, dim3(NTH), 0, s,
                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_proj), row0,
                        rows, Ncol, K, dst);
   } else {

@@ -11,7 +11,7 @@ using namespace sdm;
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int64_t kScoreChunkBytes = 512ll << 20;  // bound on the scores staging buffer
+constexpr int64_t kScoreChunkBytes = 1ll << 30;  // bound on the scores staging buffer
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
