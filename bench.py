@@ -34,6 +34,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-tokens", type=int, default=2048,
                    help="tokens of batch entry 0 in the oracle's timed sample")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="after the timed steps, copy MIB MiB device-to-device (the reference "
+                        "kernel of known traffic for scaling hardware byte counters)")
     return p.parse_args()
 
 
@@ -151,6 +154,14 @@ def main():
                      "traffic": None,
                      "algorithmic_bytes_per_launch": slot_bytes},
     }
+    if args.copy_calibration:
+        nb = args.copy_calibration << 20
+        src = torch.empty(nb // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = {"read": nb, "write": nb}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_tokens)
     print(json.dumps(res), flush=True)

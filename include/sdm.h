@@ -75,8 +75,11 @@ extern "C" {
 #define SDM_ENTRY_FORWARD 2
 
 /* scan schedule flags (sdm_dims.flags) */
-#define SDM_FLAG_SCAN_DIRECT 1 /* one workgroup per (b,h), tokens in lock-step */
-#define SDM_FLAG_SCAN_STREAM 2 /* slot-owner lane groups fed by per-group streams */
+#define SDM_FLAG_SCAN_DIRECT 1    /* one workgroup per (b,h), tokens in lock-step */
+#define SDM_FLAG_SCAN_STREAM 2    /* slot-owner lane groups fed by per-group streams,
+                                     a walk's groups split over workgroups */
+#define SDM_FLAG_SCAN_TWO_PHASE 4 /* slot-owner writes, then token-major reads, one
+                                     workgroup per (b,h, d_v slice) */
 
 /* Limits of this build (SDM_ERR_UNSUPPORTED beyond them). */
 #define SDM_MAX_COUNT 128   /* W and R */
@@ -96,8 +99,8 @@ extern "C" {
  *   in_dtype  SDM_DTYPE_F32 or SDM_DTYPE_BF16 (x and W_proj); d_model % 8 == 0
  *   gate_act  activation of the output gate vector (SDM_GATE_*)
  *   eps       RMSNorm epsilon (>= 0)
- *   flags     0, or one SDM_FLAG_SCAN_* bit to force a scan schedule (both schedules
- *             compute the same recurrence; by default the library picks by T)
+ *   flags     0, or one SDM_FLAG_SCAN_* bit to force a scan schedule (all schedules
+ *             compute the same recurrence; by default the library picks by shape)
  */
 typedef struct sdm_dims {
   int64_t B, T, d_model;

@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
 
 bool scan_uses_stream(const sdm_dims& d) {
   if (d.flags & SDM_FLAG_SCAN_DIRECT) return false;
-  if (d.flags & SDM_FLAG_SCAN_STREAM) return true;
+  if (d.flags & (SDM_FLAG_SCAN_STREAM | SDM_FLAG_SCAN_TWO_PHASE)) return true;
   return d.T >= 16;
 }
 

@@ -35,6 +35,26 @@ __device__ __forceinline__ uint32_t group_of(uint32_t slot, int log2gt) {
   return (slot * 2654435761u) >> (32 - log2gt);
 }
 
+// Value of lane `src` of this lane's LPG-lane group (LPG = 4 or 8), moved by DPP in
+// the vector ALU (no LDS traffic).  quad_perm broadcasts within each quad; for
+// 8-lane groups row_half_mirror brings the other quad's broadcast across.
+template <int LPG>
+__device__ __forceinline__ uint32_t group_bcast(uint32_t v, int src) {
+  const int q = src & 3;
+  const int qp = q | (q << 2) | (q << 4) | (q << 6);  // quad_perm(q,q,q,q)
+  uint32_t x;
+  switch (qp) {
+    case 0x00: x = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x00, 0xf, 0xf, false); break;
+    case 0x55: x = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x55, 0xf, 0xf, false); break;
+    case 0xaa: x = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xaa, 0xf, 0xf, false); break;
+    default: x = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xff, 0xf, 0xf, false); break;
+  }
+  if (LPG == 4) return x;
+  const uint32_t m = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xf, 0xf, false);  // row_half_mirror
+  const bool own_quad = ((threadIdx.x >> 2) & 1) == ((src >> 2) & 1);
+  return own_quad ? x : m;
+}
+
 // ---------------------------------------------------------------------------
 // Pre-pass 1: per (walk, round) histogram of accesses per group.
 // ---------------------------------------------------------------------------
@@ -164,7 +184,11 @@ __global__ __launch_bounds__(NT) void stream_scan_kernel(StreamArgs a) {
   constexpr int LPG = SW / 4;
   constexpr int GW = NT / LPG;
   constexpr int EPL = (BQ + LPG - 1) / LPG;  // entries loaded per lane per batch
-  __shared__ __attribute__((aligned(16))) float yr[2 * ROUND * SW];  // read partial sums
+  // Read partial sums, one padded row of YS words per token.  Column 4*l + c of a
+  // lane l sits at word c*LPG + l, so one atomic instruction's lanes of a group hit
+  // consecutive banks, and the padding staggers the tokens' rows across banks.
+  constexpr int YS = SW + 8;
+  __shared__ __attribute__((aligned(16))) float yr[2 * ROUND * YS];
   __shared__ __attribute__((aligned(16))) float vs[ROUND * SW];      // v slice of the round
   __shared__ float2 gab[ROUND];                                      // (alpha, beta)
 
@@ -181,7 +205,7 @@ __global__ __launch_bounds__(NT) void stream_scan_kernel(StreamArgs a) {
   const int gg = p * GW + g;
   const int dv = a.d_v;
 
-  for (int x = tid; x < 2 * ROUND * SW; x += NT) yr[x] = 0.0f;
+  for (int x = tid; x < 2 * ROUND * YS; x += NT) yr[x] = 0.0f;
 
   // state of this walk as a uniform base; rows addressed by 32-bit byte offsets
   char* Mb = reinterpret_cast<char*>(a.state + w * (int64_t)a.N * dv);
@@ -229,9 +253,9 @@ __global__ __launch_bounds__(NT) void stream_scan_kernel(StreamArgs a) {
 #pragma unroll
       for (int j = 0; j < BQ; ++j) {
         const int src = j % LPG, q = j / LPG;
-        slot[j] = (uint32_t)__shfl((int)e[q].x, src, LPG);
-        wq[j] = __uint_as_float((uint32_t)__shfl((int)e[q].y, src, LPG));
-        const uint32_t tf = (uint32_t)__shfl((int)e[q].z, src, LPG);
+        slot[j] = min(group_bcast<LPG>(e[q].x, src), (uint32_t)a.N - 1u);  // stays in bounds
+        wq[j] = __uint_as_float(group_bcast<LPG>(e[q].y, src));
+        const uint32_t tf = group_bcast<LPG>(e[q].z, src);
         tk[j] = (tf & 0x7fffffffu) - (uint32_t)t_lo;  // token within the round
         const bool valid = i + j < end;
         vam |= (uint32_t)valid << j;
@@ -276,11 +300,11 @@ __global__ __launch_bounds__(NT) void stream_scan_kernel(StreamArgs a) {
               gvec4{val.x, val.y, val.z, val.w};
         }
         if (!isw && ((vam >> j) & 1u)) {
-          float* y = yr + (half * ROUND + tk[j]) * SW + li * 4;
-          atomicAdd(y + 0, wq[j] * val.x);
-          atomicAdd(y + 1, wq[j] * val.y);
-          atomicAdd(y + 2, wq[j] * val.z);
-          atomicAdd(y + 3, wq[j] * val.w);
+          float* y = yr + (half * ROUND + tk[j]) * YS + li;
+          atomicAdd(y + 0 * LPG, wq[j] * val.x);
+          atomicAdd(y + 1 * LPG, wq[j] * val.y);
+          atomicAdd(y + 2 * LPG, wq[j] * val.z);
+          atomicAdd(y + 3 * LPG, wq[j] * val.w);
         }
         mv[j] = val;  // value after this access (forward source for later ones)
       }
@@ -291,12 +315,259 @@ __global__ __launch_bounds__(NT) void stream_scan_kernel(StreamArgs a) {
     // flush this round's partial read vectors and clear the ring half
     for (int x = tid; x < nt * LPG; x += NT) {
       const int tt = x / LPG, c4 = x % LPG;
-      float4* src = reinterpret_cast<float4*>(yr + (half * ROUND + tt) * SW + c4 * 4);
+      float* src = yr + (half * ROUND + tt) * YS + c4;
       const int64_t yi = ((((int64_t)p * a.B + b) * a.Tc + t_lo + tt) * a.H + h) * dv +
                          sl * SW + c4 * 4;
-      *reinterpret_cast<float4*>(a.y_part + yi) = *src;
-      *src = make_float4(0.f, 0.f, 0.f, 0.f);
+      *reinterpret_cast<float4*>(a.y_part + yi) =
+          make_float4(src[0], src[LPG], src[2 * LPG], src[3 * LPG]);
+      src[0] = 0.f;
+      src[LPG] = 0.f;
+      src[2 * LPG] = 0.f;
+      src[3 * LPG] = 0.f;
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Two-phase schedule, pre-pass 3: scatter one (walk, round) in REVERSE token order.
+// An LDS bitmap over the N slots holds "written by a later token of this round".
+// A read whose slot is in it is "dirty": it must be served by the slot's owner at
+// its place in the stream (it sees a value that a later write of the round
+// replaces).  Every other read is clean and is served after the round's writes by
+// the read phase.  The owner streams get the writes and the dirty reads only,
+// packed at the end of each (group, round) segment; begins[] records where each
+// packed segment starts; dirty[] gets one bit per read position of each token.
+// Positions are handed out downwards, so a slot's accesses keep token order with
+// writes before reads.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void bucket_scatter_rev_kernel(StreamArgs a) {
+  extern __shared__ uint32_t dyn[];
+  int* cur = reinterpret_cast<int*>(dyn);
+  uint32_t* bm = dyn + a.GT;
+  const int nbw = (a.N + 31) >> 5;
+  const int64_t w = blockIdx.x / a.rounds;
+  const int r = (int)(blockIdx.x - w * a.rounds);
+  const int64_t b = w / a.H;
+  const int h = (int)(w - b * a.H);
+  const int lane = threadIdx.x;
+  for (int g = lane; g < a.GT; g += 64)
+    cur[g] = a.offsets[((int64_t)w * a.GT + g) * (a.rounds + 1) + r + 1];
+  for (int i = lane; i < nbw; i += 64) bm[i] = 0u;
+  __syncthreads();
+  uint4* ent = a.entries + w * a.walk_entries;
+  const int64_t t_lo = (int64_t)r * ROUND;
+  const int64_t t_hi = min<int64_t>(a.Tc, t_lo + ROUND);
+  for (int64_t t = t_hi - 1; t >= t_lo; --t) {
+    const int64_t tok = (b * a.T + a.t0 + t) * a.H + h;
+    const int64_t ltok = (b * a.Tc + t) * a.H + h;  // chunk-local token row
+    for (int k0 = 0; k0 < 128; k0 += 64) {
+      const int k = k0 + lane;
+      bool dirty = false;
+      if (k < a.R) {
+        const uint32_t s = (uint32_t)a.idx_r[tok * a.R + k];
+        dirty = (bm[s >> 5] >> (s & 31u)) & 1u;
+        if (dirty) {
+          const int pos = atomicSub(&cur[group_of(s, a.log2GT)], 1) - 1;
+          ent[pos] = make_uint4(s, __float_as_uint(a.wt_r[tok * a.R + k]),
+                                (uint32_t)t | 0x80000000u, (uint32_t)k);
+        }
+      }
+      const unsigned long long m = __ballot(dirty);
+      if (lane == 0) a.dirty[ltok * 2 + (k0 >> 6)] = m;
+    }
+    __syncthreads();
+    for (int k = lane; k < a.W; k += 64) {
+      const uint32_t s = (uint32_t)a.idx_w[tok * a.W + k];
+      const int pos = atomicSub(&cur[group_of(s, a.log2GT)], 1) - 1;
+      ent[pos] = make_uint4(s, __float_as_uint(a.wt_w[tok * a.W + k]), (uint32_t)t, (uint32_t)k);
+      atomicOr(&bm[s >> 5], 1u << (s & 31u));
+    }
+    __syncthreads();
+  }
+  for (int g = lane; g < a.GT; g += 64)
+    a.begins[((int64_t)w * a.GT + g) * a.rounds + r] = cur[g];
+}
+
+// ---------------------------------------------------------------------------
+// Two-phase scan.  Workgroup = (walk, slice) holding every lane group of the walk,
+// so all owners of the walk's slots share the CU.  Per round of ROUND tokens:
+//   write phase: owners run their streams (writes and dirty reads) in batches of
+//                BQ, dirty reads add q*M[i] into an LDS ring;
+//   read phase:  each lane group takes whole tokens, loads their clean read rows
+//                BR at a time and sums them in registers, adds the ring's dirty
+//                part and writes y.  Barriers separate the phases (the reads see the
+//                round's writes; the next round's writes come after the reads).
+// ---------------------------------------------------------------------------
+template <int NT, int SW, int BQ, int BR>
+__global__ __launch_bounds__(NT) void two_phase_scan_kernel(StreamArgs a) {
+  constexpr int LPG = SW / 4;
+  constexpr int GW = NT / LPG;
+  constexpr int EPL = (BQ + LPG - 1) / LPG;
+  constexpr int RPL = (BR + LPG - 1) / LPG;  // read ids loaded per lane per chunk
+  constexpr int YS = SW + 8;
+  __shared__ __attribute__((aligned(16))) float yr[ROUND * YS];  // dirty-read sums
+  __shared__ __attribute__((aligned(16))) float vs[ROUND * SW];  // v slice of the round
+  __shared__ float2 gab[ROUND];                                  // (alpha, beta)
+
+  const int tid = threadIdx.x;
+  const int li = tid % LPG;
+  const int g = tid / LPG;
+  const int64_t wg = blockIdx.x;
+  const int sl = (int)(wg % a.S);
+  const int64_t w = wg / a.S;
+  const int64_t b = w / a.H;
+  const int h = (int)(w - b * a.H);
+  const int dv = a.d_v;
+
+  for (int x = tid; x < ROUND * YS; x += NT) yr[x] = 0.0f;
+
+  char* Mb = reinterpret_cast<char*>(a.state + w * (int64_t)a.N * dv);
+  const uint32_t col_bytes = (uint32_t)(sl * SW + li * 4) * 4u;
+  const uint32_t row_bytes = (uint32_t)dv * 4u;
+  const uint4* ent = a.entries + w * a.walk_entries;
+  const int* offs = a.offsets + ((int64_t)w * a.GT + g) * (a.rounds + 1);
+  const int* begs = a.begins + ((int64_t)w * a.GT + g) * a.rounds;
+  const int64_t tok_base = (b * a.T + a.t0) * a.H + h;  // token t -> tok_base + t*H
+  float4* trash = a.trash + wg * NT + tid;
+
+  for (int r = 0; r < a.rounds; ++r) {
+    const int64_t t_lo = (int64_t)r * ROUND;
+    const int nt = (int)min<int64_t>(ROUND, a.Tc - t_lo);
+    for (int x = tid; x < nt * LPG; x += NT) {
+      const int tt = x / LPG, c4 = x % LPG;
+      const int64_t tok = tok_base + (t_lo + tt) * a.H;
+      *reinterpret_cast<float4*>(vs + tt * SW + c4 * 4) =
+          *reinterpret_cast<const float4*>(a.v + tok * dv + sl * SW + c4 * 4);
+    }
+    for (int x = tid; x < nt; x += NT) {
+      const int64_t tok = tok_base + (t_lo + x) * a.H;
+      gab[x] = make_float2(a.alpha[tok], a.beta[tok]);
+    }
+    __syncthreads();
+
+    // ---- write phase ----
+    const int beg = begs[r];
+    const int end = offs[r + 1];
+    uint4 e[EPL];
+#pragma unroll
+    for (int q = 0; q < EPL; ++q) e[q] = ent[max(min(beg + q * LPG + li, end - 1), 0)];
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the loop header carries no pending load
+    for (int i = beg; i < end; i += BQ) {
+      uint4 en[EPL];
+#pragma unroll
+      for (int q = 0; q < EPL; ++q) en[q] = ent[min(i + BQ + q * LPG + li, end - 1)];
+      uint32_t slot[BQ], tk[BQ];
+      float wq[BQ];
+      uint32_t wrm = 0, vam = 0;
+      float4 mv[BQ];
+#pragma unroll
+      for (int j = 0; j < BQ; ++j) {
+        const int src = j % LPG, q = j / LPG;
+        slot[j] = min(group_bcast<LPG>(e[q].x, src), (uint32_t)a.N - 1u);
+        wq[j] = __uint_as_float(group_bcast<LPG>(e[q].y, src));
+        const uint32_t tf = group_bcast<LPG>(e[q].z, src);
+        tk[j] = min((tf & 0x7fffffffu) - (uint32_t)t_lo, (uint32_t)ROUND - 1u);
+        const bool valid = i + j < end;
+        vam |= (uint32_t)valid << j;
+        wrm |= (uint32_t)(valid && !(tf & 0x80000000u)) << j;
+      }
+#pragma unroll
+      for (int j = 0; j < BQ; ++j)
+        mv[j] = *reinterpret_cast<const float4*>(Mb + (slot[j] * row_bytes + col_bytes));
+#pragma unroll
+      for (int j = 0; j < BQ; ++j) {
+        float4 val = mv[j];
+#pragma unroll
+        for (int jj = 0; jj < j; ++jj) {
+          const bool fwd = ((wrm >> jj) & 1u) && slot[jj] == slot[j];
+          val.x = fwd ? mv[jj].x : val.x;
+          val.y = fwd ? mv[jj].y : val.y;
+          val.z = fwd ? mv[jj].z : val.z;
+          val.w = fwd ? mv[jj].w : val.w;
+        }
+        const bool isw = (wrm >> j) & 1u;
+        {
+          const float2 ab = gab[tk[j]];
+          const float4 vv = *reinterpret_cast<const float4*>(vs + tk[j] * SW + li * 4);
+          const float c = ab.y * wq[j];
+          const float oc = 1.0f - c;
+          float4 nv;
+          nv.x = fmaf(c, vv.x, oc * (ab.x * val.x));
+          nv.y = fmaf(c, vv.y, oc * (ab.x * val.y));
+          nv.z = fmaf(c, vv.z, oc * (ab.x * val.z));
+          nv.w = fmaf(c, vv.w, oc * (ab.x * val.w));
+          val.x = isw ? nv.x : val.x;
+          val.y = isw ? nv.y : val.y;
+          val.z = isw ? nv.z : val.z;
+          val.w = isw ? nv.w : val.w;
+          uint64_t dst = isw ? reinterpret_cast<uint64_t>(Mb + (slot[j] * row_bytes + col_bytes))
+                             : reinterpret_cast<uint64_t>(trash);
+          asm volatile("" : "+v"(dst));  // keep one unconditional store: hide the select
+          typedef float gvec4 __attribute__((ext_vector_type(4)));
+          *reinterpret_cast<__attribute__((address_space(1))) gvec4*>(dst) =
+              gvec4{val.x, val.y, val.z, val.w};
+        }
+        if (!isw && ((vam >> j) & 1u)) {  // dirty read: its value at this point of the stream
+          float* y = yr + tk[j] * YS + li;
+          atomicAdd(y + 0 * LPG, wq[j] * val.x);
+          atomicAdd(y + 1 * LPG, wq[j] * val.y);
+          atomicAdd(y + 2 * LPG, wq[j] * val.z);
+          atomicAdd(y + 3 * LPG, wq[j] * val.w);
+        }
+        mv[j] = val;
+      }
+#pragma unroll
+      for (int q = 0; q < EPL; ++q) e[q] = en[q];
+    }
+    __syncthreads();
+
+    // ---- read phase: whole tokens per lane group, sums in registers ----
+    for (int tt = g; tt < nt; tt += GW) {
+      const int64_t tok = tok_base + (t_lo + tt) * a.H;
+      const int64_t ltok = (b * a.Tc + t_lo + tt) * a.H + h;
+      const uint64_t dm0 = a.dirty[ltok * 2], dm1 = a.dirty[ltok * 2 + 1];
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int k0 = 0; k0 < a.R; k0 += BR) {
+        uint32_t pid[RPL], pwt[RPL];
+#pragma unroll
+        for (int q = 0; q < RPL; ++q) {
+          const int k = min(k0 + q * LPG + li, a.R - 1);
+          pid[q] = (uint32_t)a.idx_r[tok * a.R + k];
+          pwt[q] = __float_as_uint(a.wt_r[tok * a.R + k]);
+        }
+        uint32_t rs[BR];
+        float rq[BR];
+        float4 rv[BR];
+#pragma unroll
+        for (int j = 0; j < BR; ++j) {
+          const int k = k0 + j;
+          const bool dirty = k >= a.R || ((k < 64 ? dm0 >> k : dm1 >> (k - 64)) & 1ull);
+          const uint32_t si = group_bcast<LPG>(pid[j / LPG], j % LPG);
+          const float qi = __uint_as_float(group_bcast<LPG>(pwt[j / LPG], j % LPG));
+          rs[j] = dirty ? 0u : min(si, (uint32_t)a.N - 1u);  // skipped rows: slot 0, weight 0
+          rq[j] = dirty ? 0.0f : qi;
+        }
+#pragma unroll
+        for (int j = 0; j < BR; ++j)
+          rv[j] = *reinterpret_cast<const float4*>(Mb + (rs[j] * row_bytes + col_bytes));
+#pragma unroll
+        for (int j = 0; j < BR; ++j) {
+          acc.x = fmaf(rq[j], rv[j].x, acc.x);
+          acc.y = fmaf(rq[j], rv[j].y, acc.y);
+          acc.z = fmaf(rq[j], rv[j].z, acc.z);
+          acc.w = fmaf(rq[j], rv[j].w, acc.w);
+        }
+      }
+      float* ring = yr + tt * YS + li;
+      const float4 y = make_float4(acc.x + ring[0], acc.y + ring[LPG], acc.z + ring[2 * LPG],
+                                   acc.w + ring[3 * LPG]);
+      ring[0] = 0.f;
+      ring[LPG] = 0.f;
+      ring[2 * LPG] = 0.f;
+      ring[3 * LPG] = 0.f;
+      *reinterpret_cast<float4*>(a.y_part + ltok * dv + sl * SW + li * 4) = y;
+    }
+    __syncthreads();
   }
 }
 
@@ -374,14 +645,21 @@ StreamPlan plan_stream(const sdm_dims& d, int64_t N) {
   const int lpg = pl.SW / 4;
   const int gw = pl.NT / lpg;
   const int64_t walks = d.B * (int64_t)d.H;
-  // enough workgroups to give every CU one (256 CUs), within MAX_GT groups per walk
+  // Two-phase needs every owner of a walk's slots in one workgroup; it is used once
+  // the (walk, slice) workgroups alone reach half the CUs.  Otherwise the lane groups
+  // of a walk are split over `parts` workgroups (reads then use LDS atomics).
+  pl.two_phase = (d.flags & SDM_FLAG_SCAN_TWO_PHASE) ? true
+                 : (d.flags & SDM_FLAG_SCAN_STREAM) ? false
+                                                     : walks * pl.S >= 128;
   int parts = 1;
-  while (walks * pl.S * parts < 256 && gw * parts * 2 <= MAX_GT) parts *= 2;
+  if (!pl.two_phase)
+    while (walks * pl.S * parts < 256 && gw * parts * 2 <= MAX_GT) parts *= 2;
   pl.parts = parts;
   pl.GT = gw * parts;
   pl.log2GT = ilog2(pl.GT);
   // token chunk: bound the entries + partial-read buffers to ~2 GiB
-  const int64_t per_tok = walks * (d.W + d.R) * 16 + (int64_t)parts * walks * d.d_v * 4;
+  const int64_t per_tok = walks * (d.W + d.R) * 16 + (int64_t)parts * walks * d.d_v * 4 +
+                          walks * 16;
   int64_t tc = (2ll << 30) / per_tok;
   tc = tc < ROUND ? ROUND : (tc / ROUND) * ROUND;
   pl.Tc = d.T < tc ? d.T : tc;
@@ -398,6 +676,8 @@ size_t stream_workspace_bytes(const sdm_dims& d, const StreamPlan& pl) {
   s += al((size_t)walks * pl.Tc * (d.W + d.R) * 16);              // entries
   s += al((size_t)pl.parts * d.B * pl.Tc * d.H * d.d_v * 4);      // y_part
   s += al((size_t)walks * pl.S * pl.parts * pl.NT * 16);          // trash
+  s += al((size_t)walks * pl.GT * pl.rounds * 4);                 // begins
+  s += al((size_t)d.B * pl.Tc * d.H * 16);                        // dirty bits
   return s;
 }
 
@@ -445,17 +725,35 @@ hipError_t launch_stream_scan(const ScanArgs& sa, const StreamPlan& pl, void* ws
     a.y_part = reinterpret_cast<float*>(p);
     p += al((size_t)pl.parts * sa.B * pl.Tc * sa.H * sa.d_v * 4);
     a.trash = reinterpret_cast<float4*>(p);
+    p += al((size_t)walks * pl.S * pl.parts * pl.NT * 16);
+    a.begins = reinterpret_cast<int*>(p);
+    p += al((size_t)walks * pl.GT * pl.rounds * 4);
+    a.dirty = reinterpret_cast<unsigned long long*>(p);
 
     hipLaunchKernelGGL(bucket_count_kernel, dim3((unsigned)(walks * a.rounds)), dim3(256), 0, st,
                        a);
     hipLaunchKernelGGL(bucket_offsets_kernel, dim3((unsigned)walks), dim3(1024), 0, st, a);
-    hipLaunchKernelGGL(bucket_scatter_kernel, dim3((unsigned)(walks * a.rounds)), dim3(64), 0, st,
-                       a);
-    const dim3 grid((unsigned)(walks * pl.S * pl.parts));
-    if (pl.SW == 32)
-      hipLaunchKernelGGL((stream_scan_kernel<1024, 32, 8>), grid, dim3(1024), 0, st, a);
-    else
-      hipLaunchKernelGGL((stream_scan_kernel<1024, 16, 8>), grid, dim3(1024), 0, st, a);
+    if (pl.two_phase) {
+      const size_t lds = (size_t)pl.GT * 4 + (size_t)((sa.N + 31) / 32) * 4;
+      if (lds > 65536)  // slot bitmaps beyond 64 KiB (N > ~500k) need the larger LDS limit
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(bucket_scatter_rev_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      hipLaunchKernelGGL(bucket_scatter_rev_kernel, dim3((unsigned)(walks * a.rounds)), dim3(64),
+                         lds, st, a);
+      const dim3 grid((unsigned)(walks * pl.S));
+      if (pl.SW == 32)
+        hipLaunchKernelGGL((two_phase_scan_kernel<1024, 32, 8, 8>), grid, dim3(1024), 0, st, a);
+      else
+        hipLaunchKernelGGL((two_phase_scan_kernel<1024, 16, 8, 8>), grid, dim3(1024), 0, st, a);
+    } else {
+      hipLaunchKernelGGL(bucket_scatter_kernel, dim3((unsigned)(walks * a.rounds)), dim3(64), 0,
+                         st, a);
+      const dim3 grid((unsigned)(walks * pl.S * pl.parts));
+      if (pl.SW == 32)
+        hipLaunchKernelGGL((stream_scan_kernel<1024, 32, 8>), grid, dim3(1024), 0, st, a);
+      else
+        hipLaunchKernelGGL((stream_scan_kernel<1024, 16, 8>), grid, dim3(1024), 0, st, a);
+    }
     const int64_t rows = sa.B * a.Tc * sa.H;
     // rows per 256-thread block: 4 wavefronts x (64 / lanes per row)
     const int lpr = sa.d_v / 4 < 64 ? sa.d_v / 4 : 64;

@@ -4,7 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/sdm.h"
+#include "sdm.h"
 
 namespace sdm {
 
@@ -73,6 +73,8 @@ struct StreamArgs {
   uint4* entries;  // [walks][walk_entries]
   float* y_part;   // [parts][B][Tc][H][d_v]
   float4* trash;   // one float4 per scan thread: sink of non-writing accesses' stores
+  int* begins;               // two-phase: [walks][GT][rounds] start of each packed segment
+  unsigned long long* dirty;  // two-phase: [B][Tc][H][2] dirty-read bits per read position
   int64_t B, T, t0, Tc, walk_entries;
   int32_t H, N, W, R, d_v;
   float eps;
@@ -80,6 +82,7 @@ struct StreamArgs {
 };
 struct StreamPlan {
   int SW, S, NT, parts, GT, log2GT, rounds;
+  bool two_phase;  // one workgroup per (walk, slice), reads summed in registers
   int64_t Tc;
 };
 StreamPlan plan_stream(const sdm_dims& d, int64_t N);

@@ -76,7 +76,8 @@ def _select(lib, d, x=FAKE, w=FAKE, A=FAKE, b=FAKE, sel=None, ws=FAKE, nb=1 << 4
     (dict(eps=-1.0), _lib.SDM_ERR_SHAPE), (dict(eps=float("nan")), _lib.SDM_ERR_SHAPE),
     (dict(n=16, W=129), _lib.SDM_ERR_UNSUPPORTED), (dict(n=1025), _lib.SDM_ERR_UNSUPPORTED),
     (dict(d_v=48), _lib.SDM_ERR_UNSUPPORTED), (dict(d_model=60), _lib.SDM_ERR_UNSUPPORTED),
-    (dict(flags=4), _lib.SDM_ERR_UNSUPPORTED), (dict(flags=3), _lib.SDM_ERR_SHAPE),
+    (dict(flags=8), _lib.SDM_ERR_UNSUPPORTED), (dict(flags=3), _lib.SDM_ERR_SHAPE),
+    (dict(flags=6), _lib.SDM_ERR_SHAPE),
     (dict(in_dtype=7), _lib.SDM_ERR_DTYPE), (dict(gate_act=3), _lib.SDM_ERR_DTYPE),
 ])
 def test_bad_dims_rejected_by_every_entry(lib, kw, code):
@@ -144,4 +145,4 @@ def test_workspace_sizes_of_the_workloads(lib):
         fwd = lib.sdm_workspace_bytes(ctypes.byref(d), _lib.SDM_ENTRY_FORWARD)
         assert fwd >= wl.tokens * wl.H * per_th, name
         sel = lib.sdm_workspace_bytes(ctypes.byref(d), _lib.SDM_ENTRY_SELECT)
-        assert 0 < sel <= (512 << 20) + 256 or sel == wl.tokens * wl.H * 16 * wl.n, name
+        assert 0 < sel <= (1 << 30) + 256 or sel == wl.tokens * wl.H * 16 * wl.n, name

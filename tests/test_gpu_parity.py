@@ -110,10 +110,11 @@ def test_stage_b_selection_bit_exact(n, W, R, kind):
 # ---------------------------------------------------------------------------
 # Stage C
 # ---------------------------------------------------------------------------
-SCHEDULES = {"direct": _lib.SDM_FLAG_SCAN_DIRECT, "stream": _lib.SDM_FLAG_SCAN_STREAM}
+SCHEDULES = {"direct": _lib.SDM_FLAG_SCAN_DIRECT, "stream": _lib.SDM_FLAG_SCAN_STREAM,
+             "two_phase": _lib.SDM_FLAG_SCAN_TWO_PHASE}
 
 
-@pytest.mark.parametrize("schedule", ["direct", "stream"])
+@pytest.mark.parametrize("schedule", ["direct", "stream", "two_phase"])
 @pytest.mark.parametrize("B,T,H,n,W,R,d_v,mode", [
     (1, 64, 1, 32, 8, 8, 16, "random"),
     (1, 700, 2, 32, 16, 16, 32, "repeat"),     # several rounds of the stream schedule
@@ -144,7 +145,7 @@ def test_stage_c_scan(B, T, H, n, W, R, d_v, mode, schedule):
         assert np.array_equal(st[b, h][untouched], m0[b, h][untouched]), "unwritten rows changed"
 
 
-@pytest.mark.parametrize("schedule", ["direct", "stream"])
+@pytest.mark.parametrize("schedule", ["direct", "stream", "two_phase"])
 def test_stage_c_identity_and_overwrite_exact(schedule):
     rng = np.random.default_rng(7)
     B, T, H, n, d_v = 2, 20, 2, 8, 32
@@ -254,8 +255,9 @@ def test_schedules_agree(T):
         dm.flags = flag
         o = ops.forward(dm, d["x"], d["w_proj"], d["A"], d["b_dt"], d["gamma"], st)
         res[name] = (host(o), host(st))
-    assert np.array_equal(res["direct"][1], res["stream"][1])
-    assert_close(res["stream"][0], res["direct"][0], "out", rtol=1e-5, atol=1e-6)
+    for name in ("stream", "two_phase"):
+        assert np.array_equal(res["direct"][1], res[name][1]), name
+        assert_close(res[name][0], res["direct"][0], f"out {name}", rtol=1e-5, atol=1e-6)
 
 
 def test_empty_call_changes_nothing():
