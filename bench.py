@@ -23,6 +23,24 @@ import numpy as np  # noqa: E402
 
 METRIC = "SDM layer tokens/s at N=131072,W=R=64,d_v=128; effective HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_traffic_layer1p4b.txt")
+SCAN_SOURCE = os.path.join(ROOT, "sparse_memory_linear_sdm_amd", "csrc", "scan_stream.hip")
+
+
+def measured_traffic(workload: str):
+    """Counter-measured HBM bytes of one scan launch, if taken on the current source."""
+    import hashlib
+    if workload != "layer1p4b" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    fields = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.split()[0] if v.split() else ""
+    cur = hashlib.sha256(open(SCAN_SOURCE, "rb").read()).hexdigest()
+    if fields.get("source_sha256") != cur:
+        return None  # the kernel changed since the counters were taken
+    return int(float(fields["traffic_bytes"]))
 
 
 def parse():
@@ -151,7 +169,7 @@ def main():
         "effective_hbm_gbs_step": slot_bytes / (ms_wall * 1e-3) / 1e9,
         "roofline": {"bound": "hbm", "kernel": "scan", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None,
+                     "traffic": measured_traffic(wl.name),
                      "algorithmic_bytes_per_launch": slot_bytes},
     }
     if args.copy_calibration:
