@@ -92,57 +92,123 @@ __device__ __forceinline__ int wave_sum(int x) {
   return x;
 }
 
-// Exact radix select over 32-bit keys (larger is better) held KPL per lane.
-// Returns T with (#keys > T) < need <= (#keys >= T); need_eq = need - #keys > T.
-// hist: 256 words of this wavefront's LDS.  The block is one wavefront, so
-// __syncthreads() only orders this wave's LDS traffic.
-template <int KPL>
-__device__ uint32_t radix_select(const uint32_t (&key)[KPL], uint32_t valid, int need,
-                                 uint32_t* hist, int& need_eq) {
-  const int lane = lane_id();
-  uint32_t prefix = 0;
+__device__ __forceinline__ float wave_min(float x) {
 #pragma unroll
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
+  for (int o = 32; o > 0; o >>= 1) x = fminf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+// fp64 -> uint64 whose unsigned order is the double order (-0 folded onto +0).
+__device__ __forceinline__ uint64_t ord64(double d) {
+  uint64_t u = (uint64_t)__double_as_longlong(d);
+  if ((u << 1) == 0) u = 0;
+  return (u & 0x8000000000000000ull) ? ~u : (u | 0x8000000000000000ull);
+}
+
+// Exact order of the selections: larger key first, then smaller id.
+__device__ __forceinline__ bool better(uint64_t ka, uint32_t ia, uint64_t kb, uint32_t ib) {
+  return ka > kb || (ka == kb && ia < ib);
+}
+
+// Choose exactly `need` of the valid elements (bit q of `valid`, KPL per lane): the best
+// under `better` on (key, id).  fv[q] is a float that never decreases along that order;
+// it is only used to bin.  Each round bins the remaining candidates into 256 equal-width
+// bins over their [min, max]; the bins above the one holding the need-th best are taken,
+// the bins below are dropped, and the rest continue.  Whatever remains after three rounds
+// (or once few are left) is ranked exactly.  Binning is monotone, so the result is exact.
+// hist: 256 words of LDS; tk/ti: LDS room for 64*KPL (key, id) pairs.
+template <int KPL>
+__device__ uint32_t select_exact(const float (&fv)[KPL], const uint64_t (&key)[KPL],
+                                 const uint32_t (&id)[KPL], uint32_t valid, int need,
+                                 uint32_t* hist, uint64_t* tk, uint32_t* ti) {
+  const int lane = lane_id();
+  uint32_t sel = 0, cand = valid;
+  for (int round = 0; round < 3; ++round) {
+    const int nc = wave_sum(__popc(cand));
+    if (nc == need) return sel | cand;
+    if (nc <= 32) break;
+    float lo = __builtin_inff(), hi = -__builtin_inff();
+#pragma unroll
+    for (int q = 0; q < KPL; ++q)
+      if ((cand >> q) & 1u) {
+        lo = fminf(lo, fv[q]);
+        hi = fmaxf(hi, fv[q]);
+      }
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    const float scale = 256.0f / (hi - lo);
+    if (!(hi > lo) || !(scale > 0.0f) || !(scale < __builtin_inff())) break;
+    int bin[KPL];
+#pragma unroll
+    for (int q = 0; q < KPL; ++q) {
+      const float f = (fv[q] - lo) * scale;
+      bin[q] = f >= 255.0f ? 255 : (f > 0.0f ? (int)f : 0);  // NaN -> 0
+    }
     reinterpret_cast<uint4*>(hist)[lane] = make_uint4(0, 0, 0, 0);
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < KPL; ++q) {
-      const bool m = ((valid >> q) & 1u) &&
-                     (pass == 0 || (key[q] >> (shift + 8)) == (prefix >> (shift + 8)));
-      if (m) atomicAdd(&hist[(key[q] >> shift) & 255u], 1u);
-    }
+    for (int q = 0; q < KPL; ++q)
+      if ((cand >> q) & 1u) atomicAdd(&hist[bin[q]], 1u);
     __syncthreads();
     // lane l owns bins 255-4l (highest) .. 252-4l
     const uint4 hv = reinterpret_cast<const uint4*>(hist)[63 - lane];
     const int local = (int)(hv.x + hv.y + hv.z + hv.w);
     const int incl = wave_incl_scan(local);
     const int excl = incl - local;
-    const unsigned long long bal = __ballot(incl >= need);
-    const int L = __ffsll((long long)bal) - 1;
-    int digit = 0, rest = 0;
+    const int L = __ffsll((long long)__ballot(incl >= need)) - 1;
+    int bstar = 0, rest = 0;
     if (lane == L) {
       int acc = excl;
       const int c3 = (int)hv.w, c2 = (int)hv.z, c1 = (int)hv.y;
       if (acc + c3 >= need) {
-        digit = 255 - 4 * lane;
+        bstar = 255 - 4 * lane;
       } else if ((acc += c3) + c2 >= need) {
-        digit = 254 - 4 * lane;
+        bstar = 254 - 4 * lane;
       } else if ((acc += c2) + c1 >= need) {
-        digit = 253 - 4 * lane;
+        bstar = 253 - 4 * lane;
       } else {
         acc += c1;
-        digit = 252 - 4 * lane;
+        bstar = 252 - 4 * lane;
       }
       rest = need - acc;
     }
-    digit = __shfl(digit, L);
+    bstar = __shfl(bstar, L);
     need = __shfl(rest, L);
-    prefix |= (uint32_t)digit << shift;
     __syncthreads();
+#pragma unroll
+    for (int q = 0; q < KPL; ++q) {
+      const bool c = (cand >> q) & 1u;
+      sel |= (uint32_t)(c && bin[q] > bstar) << q;
+      cand &= ~((uint32_t)(!(c && bin[q] == bstar)) << q);
+    }
   }
-  need_eq = need;
-  return prefix;
+  // exact ranking of the remaining candidates
+  const int cl = __popc(cand);
+  const int nc = wave_sum(cl);
+  if (nc == need) return sel | cand;
+  int pos = wave_incl_scan(cl) - cl;
+#pragma unroll
+  for (int q = 0; q < KPL; ++q)
+    if ((cand >> q) & 1u) {
+      tk[pos] = key[q];
+      ti[pos] = id[q];
+      ++pos;
+    }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < KPL; ++q)
+    if ((cand >> q) & 1u) {
+      int rank = 0;
+      for (int u = 0; u < nc; ++u) rank += better(tk[u], ti[u], key[q], id[q]) ? 1 : 0;
+      if (rank < need) sel |= 1u << q;
+    }
+  __syncthreads();
+  return sel;
 }
 
 // Bitonic sort of NE = 64*EPL 64-bit keys (element e = lane + 64*r in v[r]) so that
@@ -193,31 +259,23 @@ __device__ void half_topk(const float* __restrict__ src, int n, int k, uint32_t*
                           uint64_t* stage, float* val, uint32_t* idx) {
   const int lane = lane_id();
   uint32_t key[KPL];
+  float fv[KPL];
+  uint64_t ek[KPL];
+  uint32_t ei[KPL];
   uint32_t valid = 0;
 #pragma unroll
   for (int q = 0; q < KPL; ++q) {
     const int i = lane * KPL + q;
     const bool ok = i < n;
-    key[q] = ok ? ord32(src[i]) : 0u;
+    fv[q] = ok ? src[i] : 0.0f;
+    key[q] = ok ? ord32(fv[q]) : 0u;
+    ek[q] = key[q];
+    ei[q] = (uint32_t)i;
     valid |= (uint32_t)ok << q;
   }
-  int need_eq;
-  const uint32_t T = radix_select<KPL>(key, valid, k, hist, need_eq);
-  // compaction: keys above T, then the lowest-index keys equal to T
-  int eq_local = 0;
-#pragma unroll
-  for (int q = 0; q < KPL; ++q) eq_local += (((valid >> q) & 1u) && key[q] == T) ? 1 : 0;
-  const int eq_excl = wave_incl_scan(eq_local) - eq_local;
-  uint32_t sel = 0;
-  int eq_seen = 0;
-#pragma unroll
-  for (int q = 0; q < KPL; ++q) {
-    const bool v = (valid >> q) & 1u;
-    const bool eq = v && key[q] == T;
-    const bool s = (v && key[q] > T) || (eq && eq_excl + eq_seen < need_eq);
-    eq_seen += eq ? 1 : 0;
-    sel |= (uint32_t)s << q;
-  }
+  uint64_t* tk = stage;
+  uint32_t* ti = reinterpret_cast<uint32_t*>(stage + 64 * KPL);
+  const uint32_t sel = select_exact<KPL>(fv, ek, ei, valid, k, hist, tk, ti);
   const int sel_local = __popc(sel);
   int pos = wave_incl_scan(sel_local) - sel_local;
 #pragma unroll
@@ -249,11 +307,6 @@ __device__ void half_topk(const float* __restrict__ src, int n, int k, uint32_t*
   __syncthreads();
 }
 
-// (exact score, id) order: a beats b
-__device__ __forceinline__ bool beats(double sa, uint32_t ia, double sb, uint32_t ib) {
-  return sa > sb || (sa == sb && ia < ib);
-}
-
 // Combine the two sorted top-k lists into the best `count` slots; KPC candidates
 // per lane.  Writes ascending ids and softmax weights to oi / ow.
 template <int KPC>
@@ -263,8 +316,9 @@ __device__ void combine(int n, int k, int count, const float* av, const uint32_t
   const int lane = lane_id();
   const int c0 = kCand.off[count];
   const int nc = kCand.off[count + 1] - c0;
-  uint32_t key[KPC];
+  float fv[KPC];
   double sc[KPC];
+  uint64_t ek[KPC];
   uint32_t id[KPC];
   uint32_t valid = 0;
 #pragma unroll
@@ -274,46 +328,15 @@ __device__ void combine(int n, int k, int count, const float* av, const uint32_t
     const int r1 = (int)(rc >> 8), r2 = (int)(rc & 255u);
     const bool ok = c < nc && r1 < k && r2 < k;
     const float a = ok ? av[r1] : 0.0f, b = ok ? bv[r2] : 0.0f;
-    key[q] = ok ? ord32(a + b) : 0u;                 // fp32-rounded sum: monotone
-    sc[q] = (double)a + (double)b;                   // exact
+    fv[q] = a + b;                        // fp32-rounded sum: never decreases with the exact one
+    sc[q] = (double)a + (double)b;        // exact
+    ek[q] = ord64(sc[q]);
     id[q] = ok ? ai[r1] * (uint32_t)n + bi[r2] : 0u;
     valid |= (uint32_t)ok << q;
   }
-  int need_eq;
-  const uint32_t T = radix_select<KPC>(key, valid, count, hist, need_eq);
-  // candidates tied at the fp32 threshold: order them exactly
-  uint32_t eqm = 0;
-#pragma unroll
-  for (int q = 0; q < KPC; ++q) eqm |= (uint32_t)(((valid >> q) & 1u) && key[q] == T) << q;
-  const int eq_local = __popc(eqm);
-  const int eq_total = wave_sum(eq_local);
-  uint32_t sel = 0;
-#pragma unroll
-  for (int q = 0; q < KPC; ++q) sel |= (uint32_t)(((valid >> q) & 1u) && key[q] > T) << q;
-  if (eq_total == need_eq) {
-    sel |= eqm;
-  } else {
-    // gather the tied candidates, rank each one against the others
-    double* tsc = reinterpret_cast<double*>(stage);
-    uint32_t* tid = reinterpret_cast<uint32_t*>(stage + 64 * KPC);
-    int pos = wave_incl_scan(eq_local) - eq_local;
-#pragma unroll
-    for (int q = 0; q < KPC; ++q)
-      if ((eqm >> q) & 1u) {
-        tsc[pos] = sc[q];
-        tid[pos] = id[q];
-        ++pos;
-      }
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < KPC; ++q)
-      if ((eqm >> q) & 1u) {
-        int rank = 0;
-        for (int u = 0; u < eq_total; ++u) rank += beats(tsc[u], tid[u], sc[q], id[q]) ? 1 : 0;
-        if (rank < need_eq) sel |= 1u << q;
-      }
-    __syncthreads();
-  }
+  uint64_t* tk = stage;
+  uint32_t* ti = reinterpret_cast<uint32_t*>(stage + 64 * KPC);
+  const uint32_t sel = select_exact<KPC>(fv, ek, id, valid, count, hist, tk, ti);
   // compaction of the `count` survivors as (id, exact score)
   uint32_t* cid = reinterpret_cast<uint32_t*>(stage);
   double* csc = reinterpret_cast<double*>(stage + 64);  // after 128 ids
@@ -375,9 +398,13 @@ __device__ void combine(int n, int k, int count, const float* av, const uint32_t
   }
 }
 
-// 64-bit staging words a combine with KPC candidates per lane needs: tied
-// candidates (64*KPC doubles + 64*KPC ids) or the survivors (128 ids + 128 doubles).
-constexpr int stage_words(int kpc) { return 96 * kpc > 192 ? 96 * kpc : 192; }
+// 64-bit staging words: exact-ranking room for 64*K (key, id) pairs (K = max of the
+// per-lane element counts of the halves and the candidates), the half top-k survivors
+// (128 keys) or the combine's survivors (128 ids + 128 doubles).
+constexpr int stage_words(int kpl, int kpc) {
+  const int k = kpl > kpc ? kpl : kpc;
+  return 96 * k > 192 ? 96 * k : 192;
+}
 
 // One wavefront per (row, head, role).  LDS: histogram, staging, two top-k lists.
 template <int KPL, int KPC>
@@ -388,7 +415,7 @@ __global__ __launch_bounds__(64) void select_kernel(const float* __restrict__ sc
                                                     int32_t* __restrict__ idx_r,
                                                     float* __restrict__ wt_r) {
   __shared__ __attribute__((aligned(16))) uint32_t hist[256];
-  __shared__ __attribute__((aligned(16))) uint64_t stage[stage_words(KPC)];
+  __shared__ __attribute__((aligned(16))) uint64_t stage[stage_words(KPL, KPC)];
   __shared__ float tv[2][SDM_MAX_COUNT];
   __shared__ uint32_t ti[2][SDM_MAX_COUNT];
 
