@@ -10,6 +10,8 @@
 // How it is scheduled on gfx950:
 //  * Every slot belongs to exactly one lane group (hash of the slot id).  A lane
 //    group is LPG lanes covering one SW-float segment of d_v (one float4 each).
+//    The lane groups of a walk are split over `parts` workgroups, so that a few
+//    dozen walks still put one workgroup on every CU.
 //  * A bucketing pre-pass lays the accesses of each walk out as per-group streams
 //    in token order (writes before reads within a token), split into rounds of
 //    ROUND tokens.  Because a slot's column chunk is only ever loaded and stored by
@@ -18,11 +20,14 @@
 //    for the state.
 //  * Each lane group keeps BQ row loads in flight; repeated slots inside a batch
 //    are forwarded in registers.
-//  * Reads accumulate q * M[i] into an LDS ring of per-token partial sums (float
-//    atomics); once per round the ring half is flushed to y_part[part] and the
-//    next round proceeds.  A small kernel then sums the parts, normalises and gates.
-//  * Work is split over (walk, column slice, part): parts divide the lane groups
-//    of a walk among workgroups, so few walks still fill the chip.
+//  * Two schedules of the reads:
+//      stream:    every read sits in its owner's stream and adds q * M[i] into an
+//                 LDS ring of per-token partial sums (float atomics);
+//      two-phase: only reads whose slot a later token of the round rewrites stay in
+//                 the owner streams; all others are summed per token in registers
+//                 once the round's writes are done (see two_phase_scan_kernel).
+//    Each part writes its own partial read vectors; a small kernel sums the parts,
+//    normalises and gates.
 #include "sdm_internal.h"
 
 namespace sdm {
@@ -30,6 +35,15 @@ namespace {
 
 constexpr int ROUND = 256;       // tokens per round (ring half)
 constexpr int MAX_GT = 4096;     // lane groups per walk
+constexpr uint32_t SLOT_MASK = 0xFFFFFFu;
+static_assert(ROUND <= 256, "token-in-round must fit the entry's top 8 bits");
+
+// Owner-stream entry: slot ids < 2^24 (at most 1024^2 here) share a word with the
+// token's place in its round; softmax weights are >= 0, so their sign bit is free
+// for the read flag.
+__device__ __forceinline__ uint2 make_entry(uint32_t slot, int tt, float q, bool read) {
+  return make_uint2(slot | ((uint32_t)tt << 24), __float_as_uint(q) | (read ? 0x80000000u : 0u));
+}
 
 __device__ __forceinline__ uint32_t group_of(uint32_t slot, int log2gt) {
   return (slot * 2654435761u) >> (32 - log2gt);
@@ -140,7 +154,6 @@ __global__ __launch_bounds__(1024) void bucket_offsets_kernel(StreamArgs a) {
 // Within one instruction all slots are distinct (a token's write ids are distinct,
 // and so are its read ids), and writes are issued before reads, so accesses of
 // one slot keep token order with writes first.
-// Entry: {slot, weight bits, chunk-local token | (read ? 1<<31 : 0), position}.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void bucket_scatter_kernel(StreamArgs a) {
   __shared__ int cur[MAX_GT];
@@ -152,23 +165,23 @@ __global__ __launch_bounds__(64) void bucket_scatter_kernel(StreamArgs a) {
   for (int g = lane; g < a.GT; g += 64)
     cur[g] = a.offsets[((int64_t)w * a.GT + g) * (a.rounds + 1) + r];
   __syncthreads();
-  uint4* ent = a.entries + w * a.walk_entries;
+  uint2* ent = a.entries + w * a.walk_entries;
   const int64_t t_lo = (int64_t)r * ROUND;
   const int64_t t_hi = min<int64_t>(a.Tc, t_lo + ROUND);
   for (int64_t t = t_lo; t < t_hi; ++t) {
     const int64_t tok = (b * a.T + a.t0 + t) * a.H + h;
+    const int tt = (int)(t - t_lo);
     for (int k = lane; k < a.W; k += 64) {
       const int32_t s = a.idx_w[tok * a.W + k];
       const float q = a.wt_w[tok * a.W + k];
       const int pos = atomicAdd(&cur[group_of((uint32_t)s, a.log2GT)], 1);
-      ent[pos] = make_uint4((uint32_t)s, __float_as_uint(q), (uint32_t)t, (uint32_t)k);
+      ent[pos] = make_entry((uint32_t)s, tt, q, false);
     }
     for (int k = lane; k < a.R; k += 64) {
       const int32_t s = a.idx_r[tok * a.R + k];
       const float q = a.wt_r[tok * a.R + k];
       const int pos = atomicAdd(&cur[group_of((uint32_t)s, a.log2GT)], 1);
-      ent[pos] = make_uint4((uint32_t)s, __float_as_uint(q), (uint32_t)t | 0x80000000u,
-                            (uint32_t)k);
+      ent[pos] = make_entry((uint32_t)s, tt, q, true);
     }
   }
 }
@@ -211,7 +224,7 @@ __global__ __launch_bounds__(NT) void stream_scan_kernel(StreamArgs a) {
   char* Mb = reinterpret_cast<char*>(a.state + w * (int64_t)a.N * dv);
   const uint32_t col_bytes = (uint32_t)(sl * SW + li * 4) * 4u;
   const uint32_t row_bytes = (uint32_t)dv * 4u;
-  const uint4* ent = a.entries + w * a.walk_entries;
+  const uint2* ent = a.entries + w * a.walk_entries;
   const int* offs = a.offsets + ((int64_t)w * a.GT + gg) * (a.rounds + 1);
   const int64_t tok_base = (b * a.T + a.t0) * a.H + h;  // token t -> tok_base + t*H
   float4* trash = a.trash + wg * NT + tid;
@@ -235,7 +248,7 @@ __global__ __launch_bounds__(NT) void stream_scan_kernel(StreamArgs a) {
 
     const int beg = offs[r];
     const int end = offs[r + 1];
-    uint4 e[EPL];
+    uint2 e[EPL];
 #pragma unroll
     for (int q = 0; q < EPL; ++q) e[q] = ent[max(min(beg + q * LPG + li, end - 1), 0)];
     // once per round: the first batch's entries are complete before the batch loop,
@@ -243,7 +256,7 @@ __global__ __launch_bounds__(NT) void stream_scan_kernel(StreamArgs a) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     for (int i = beg; i < end; i += BQ) {
       // next batch's entries travel with this batch's row loads
-      uint4 en[EPL];
+      uint2 en[EPL];
 #pragma unroll
       for (int q = 0; q < EPL; ++q) en[q] = ent[min(i + BQ + q * LPG + li, end - 1)];
       uint32_t slot[BQ], tk[BQ];
@@ -253,13 +266,14 @@ __global__ __launch_bounds__(NT) void stream_scan_kernel(StreamArgs a) {
 #pragma unroll
       for (int j = 0; j < BQ; ++j) {
         const int src = j % LPG, q = j / LPG;
-        slot[j] = min(group_bcast<LPG>(e[q].x, src), (uint32_t)a.N - 1u);  // stays in bounds
-        wq[j] = __uint_as_float(group_bcast<LPG>(e[q].y, src));
-        const uint32_t tf = group_bcast<LPG>(e[q].z, src);
-        tk[j] = (tf & 0x7fffffffu) - (uint32_t)t_lo;  // token within the round
+        const uint32_t ex = group_bcast<LPG>(e[q].x, src);
+        const uint32_t ey = group_bcast<LPG>(e[q].y, src);
+        slot[j] = min(ex & SLOT_MASK, (uint32_t)a.N - 1u);  // stays in bounds
+        tk[j] = ex >> 24;                                   // token within the round
+        wq[j] = __uint_as_float(ey & 0x7fffffffu);
         const bool valid = i + j < end;
         vam |= (uint32_t)valid << j;
-        wrm |= (uint32_t)(valid && !(tf & 0x80000000u)) << j;
+        wrm |= (uint32_t)(valid && !(ey >> 31)) << j;
       }
 #pragma unroll
       for (int j = 0; j < BQ; ++j)
@@ -334,9 +348,10 @@ __global__ __launch_bounds__(NT) void stream_scan_kernel(StreamArgs a) {
 // A read whose slot is in it is "dirty": it must be served by the slot's owner at
 // its place in the stream (it sees a value that a later write of the round
 // replaces).  Every other read is clean and is served after the round's writes by
-// the read phase.  The owner streams get the writes and the dirty reads only,
-// packed at the end of each (group, round) segment; begins[] records where each
-// packed segment starts; dirty[] gets one bit per read position of each token.
+// the read phase of the part that owns its slot.  The owner streams get the writes
+// and the dirty reads only, packed at the end of each (group, round) segment;
+// begins[] records where each packed segment starts.  Each token's clean reads are
+// written grouped by owning part, cstart[] giving where each part's run begins.
 // Positions are handed out downwards, so a slot's accesses keep token order with
 // writes before reads.
 // ---------------------------------------------------------------------------
@@ -350,36 +365,57 @@ __global__ __launch_bounds__(64) void bucket_scatter_rev_kernel(StreamArgs a) {
   const int64_t b = w / a.H;
   const int h = (int)(w - b * a.H);
   const int lane = threadIdx.x;
+  const unsigned long long below = (1ull << lane) - 1ull;
   for (int g = lane; g < a.GT; g += 64)
     cur[g] = a.offsets[((int64_t)w * a.GT + g) * (a.rounds + 1) + r + 1];
   for (int i = lane; i < nbw; i += 64) bm[i] = 0u;
   __syncthreads();
-  uint4* ent = a.entries + w * a.walk_entries;
+  uint2* ent = a.entries + w * a.walk_entries;
   const int64_t t_lo = (int64_t)r * ROUND;
   const int64_t t_hi = min<int64_t>(a.Tc, t_lo + ROUND);
   for (int64_t t = t_hi - 1; t >= t_lo; --t) {
     const int64_t tok = (b * a.T + a.t0 + t) * a.H + h;
     const int64_t ltok = (b * a.Tc + t) * a.H + h;  // chunk-local token row
-    for (int k0 = 0; k0 < 128; k0 += 64) {
-      const int k = k0 + lane;
-      bool dirty = false;
+    const int tt = (int)(t - t_lo);
+    int pk[2];   // owning part of a clean read, -1 otherwise
+    uint2 ck[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int k = c * 64 + lane;
+      pk[c] = -1;
+      ck[c] = make_uint2(0u, 0u);
       if (k < a.R) {
         const uint32_t s = (uint32_t)a.idx_r[tok * a.R + k];
-        dirty = (bm[s >> 5] >> (s & 31u)) & 1u;
-        if (dirty) {
-          const int pos = atomicSub(&cur[group_of(s, a.log2GT)], 1) - 1;
-          ent[pos] = make_uint4(s, __float_as_uint(a.wt_r[tok * a.R + k]),
-                                (uint32_t)t | 0x80000000u, (uint32_t)k);
+        const float q = a.wt_r[tok * a.R + k];
+        const uint32_t grp = group_of(s, a.log2GT);
+        if ((bm[s >> 5] >> (s & 31u)) & 1u) {
+          const int pos = atomicSub(&cur[grp], 1) - 1;
+          ent[pos] = make_entry(s, tt, q, true);
+        } else {
+          pk[c] = (int)(grp >> a.log2GW);
+          ck[c] = make_uint2(s, __float_as_uint(q));
         }
       }
-      const unsigned long long m = __ballot(dirty);
-      if (lane == 0) a.dirty[ltok * 2 + (k0 >> 6)] = m;
     }
+    int* cs = a.cstart + ltok * (a.parts + 1);
+    uint2* cl = a.clean + ltok * a.R;
+    int base = 0;
+    for (int p = 0; p < a.parts; ++p) {
+      if (lane == 0) cs[p] = base;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const bool mine = pk[c] == p;
+        const unsigned long long m = __ballot(mine);
+        if (mine) cl[base + __popcll(m & below)] = ck[c];
+        base += __popcll(m);
+      }
+    }
+    if (lane == 0) cs[a.parts] = base;
     __syncthreads();
     for (int k = lane; k < a.W; k += 64) {
       const uint32_t s = (uint32_t)a.idx_w[tok * a.W + k];
       const int pos = atomicSub(&cur[group_of(s, a.log2GT)], 1) - 1;
-      ent[pos] = make_uint4(s, __float_as_uint(a.wt_w[tok * a.W + k]), (uint32_t)t, (uint32_t)k);
+      ent[pos] = make_entry(s, tt, a.wt_w[tok * a.W + k], false);
       atomicOr(&bm[s >> 5], 1u << (s & 31u));
     }
     __syncthreads();
@@ -389,21 +425,23 @@ __global__ __launch_bounds__(64) void bucket_scatter_rev_kernel(StreamArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Two-phase scan.  Workgroup = (walk, slice) holding every lane group of the walk,
-// so all owners of the walk's slots share the CU.  Per round of ROUND tokens:
+// Two-phase scan.  Workgroup = (walk, slice, part); the part's lane groups own its
+// share of the walk's slots.  Per round of ROUND tokens:
 //   write phase: owners run their streams (writes and dirty reads) in batches of
 //                BQ, dirty reads add q*M[i] into an LDS ring;
-//   read phase:  each lane group takes whole tokens, loads their clean read rows
-//                BR at a time and sums them in registers, adds the ring's dirty
-//                part and writes y.  Barriers separate the phases (the reads see the
-//                round's writes; the next round's writes come after the reads).
+//   read phase:  each lane group takes whole tokens, loads the token's clean reads
+//                of this part's slots BR rows at a time and sums them in registers,
+//                adds the ring's dirty part and writes the part's y.  Barriers
+//                separate the phases (the reads see the round's writes; the next
+//                round's writes come after the reads).  Parts never touch each
+//                other's slots, so they need no synchronisation with one another.
 // ---------------------------------------------------------------------------
 template <int NT, int SW, int BQ, int BR>
 __global__ __launch_bounds__(NT) void two_phase_scan_kernel(StreamArgs a) {
   constexpr int LPG = SW / 4;
   constexpr int GW = NT / LPG;
   constexpr int EPL = (BQ + LPG - 1) / LPG;
-  constexpr int RPL = (BR + LPG - 1) / LPG;  // read ids loaded per lane per chunk
+  constexpr int RPL = (BR + LPG - 1) / LPG;  // clean reads loaded per lane per batch
   constexpr int YS = SW + 8;
   __shared__ __attribute__((aligned(16))) float yr[ROUND * YS];  // dirty-read sums
   __shared__ __attribute__((aligned(16))) float vs[ROUND * SW];  // v slice of the round
@@ -413,10 +451,13 @@ __global__ __launch_bounds__(NT) void two_phase_scan_kernel(StreamArgs a) {
   const int li = tid % LPG;
   const int g = tid / LPG;
   const int64_t wg = blockIdx.x;
-  const int sl = (int)(wg % a.S);
-  const int64_t w = wg / a.S;
+  const int p = (int)(wg % a.parts);
+  const int64_t ws = wg / a.parts;
+  const int sl = (int)(ws % a.S);
+  const int64_t w = ws / a.S;
   const int64_t b = w / a.H;
   const int h = (int)(w - b * a.H);
+  const int gg = p * GW + g;
   const int dv = a.d_v;
 
   for (int x = tid; x < ROUND * YS; x += NT) yr[x] = 0.0f;
@@ -424,10 +465,11 @@ __global__ __launch_bounds__(NT) void two_phase_scan_kernel(StreamArgs a) {
   char* Mb = reinterpret_cast<char*>(a.state + w * (int64_t)a.N * dv);
   const uint32_t col_bytes = (uint32_t)(sl * SW + li * 4) * 4u;
   const uint32_t row_bytes = (uint32_t)dv * 4u;
-  const uint4* ent = a.entries + w * a.walk_entries;
-  const int* offs = a.offsets + ((int64_t)w * a.GT + g) * (a.rounds + 1);
-  const int* begs = a.begins + ((int64_t)w * a.GT + g) * a.rounds;
+  const uint2* ent = a.entries + w * a.walk_entries;
+  const int* offs = a.offsets + ((int64_t)w * a.GT + gg) * (a.rounds + 1);
+  const int* begs = a.begins + ((int64_t)w * a.GT + gg) * a.rounds;
   const int64_t tok_base = (b * a.T + a.t0) * a.H + h;  // token t -> tok_base + t*H
+  float* y_out = a.y_part + (int64_t)p * a.B * a.Tc * a.H * dv + sl * SW + li * 4;
   float4* trash = a.trash + wg * NT + tid;
 
   for (int r = 0; r < a.rounds; ++r) {
@@ -448,12 +490,12 @@ __global__ __launch_bounds__(NT) void two_phase_scan_kernel(StreamArgs a) {
     // ---- write phase ----
     const int beg = begs[r];
     const int end = offs[r + 1];
-    uint4 e[EPL];
+    uint2 e[EPL];
 #pragma unroll
     for (int q = 0; q < EPL; ++q) e[q] = ent[max(min(beg + q * LPG + li, end - 1), 0)];
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the loop header carries no pending load
     for (int i = beg; i < end; i += BQ) {
-      uint4 en[EPL];
+      uint2 en[EPL];
 #pragma unroll
       for (int q = 0; q < EPL; ++q) en[q] = ent[min(i + BQ + q * LPG + li, end - 1)];
       uint32_t slot[BQ], tk[BQ];
@@ -463,13 +505,14 @@ __global__ __launch_bounds__(NT) void two_phase_scan_kernel(StreamArgs a) {
 #pragma unroll
       for (int j = 0; j < BQ; ++j) {
         const int src = j % LPG, q = j / LPG;
-        slot[j] = min(group_bcast<LPG>(e[q].x, src), (uint32_t)a.N - 1u);
-        wq[j] = __uint_as_float(group_bcast<LPG>(e[q].y, src));
-        const uint32_t tf = group_bcast<LPG>(e[q].z, src);
-        tk[j] = min((tf & 0x7fffffffu) - (uint32_t)t_lo, (uint32_t)ROUND - 1u);
+        const uint32_t ex = group_bcast<LPG>(e[q].x, src);
+        const uint32_t ey = group_bcast<LPG>(e[q].y, src);
+        slot[j] = min(ex & SLOT_MASK, (uint32_t)a.N - 1u);
+        tk[j] = ex >> 24;
+        wq[j] = __uint_as_float(ey & 0x7fffffffu);
         const bool valid = i + j < end;
         vam |= (uint32_t)valid << j;
-        wrm |= (uint32_t)(valid && !(tf & 0x80000000u)) << j;
+        wrm |= (uint32_t)(valid && !(ey >> 31)) << j;
       }
 #pragma unroll
       for (int j = 0; j < BQ; ++j)
@@ -523,39 +566,42 @@ __global__ __launch_bounds__(NT) void two_phase_scan_kernel(StreamArgs a) {
 
     // ---- read phase: whole tokens per lane group, sums in registers ----
     for (int tt = g; tt < nt; tt += GW) {
-      const int64_t tok = tok_base + (t_lo + tt) * a.H;
       const int64_t ltok = (b * a.Tc + t_lo + tt) * a.H + h;
-      const uint64_t dm0 = a.dirty[ltok * 2], dm1 = a.dirty[ltok * 2 + 1];
+      const int* cs = a.cstart + ltok * (a.parts + 1) + p;
+      const int cb = cs[0], ce = cs[1];
+      const uint2* cl = a.clean + ltok * a.R;
       float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int k0 = 0; k0 < a.R; k0 += BR) {
-        uint32_t pid[RPL], pwt[RPL];
+      if (cb < ce) {
+        uint2 c[RPL];
 #pragma unroll
-        for (int q = 0; q < RPL; ++q) {
-          const int k = min(k0 + q * LPG + li, a.R - 1);
-          pid[q] = (uint32_t)a.idx_r[tok * a.R + k];
-          pwt[q] = __float_as_uint(a.wt_r[tok * a.R + k]);
-        }
-        uint32_t rs[BR];
-        float rq[BR];
-        float4 rv[BR];
+        for (int q = 0; q < RPL; ++q) c[q] = cl[min(cb + q * LPG + li, ce - 1)];
+        for (int i = cb; i < ce; i += BR) {
+          // next batch's ids travel with this batch's row loads
+          uint2 cn[RPL];
 #pragma unroll
-        for (int j = 0; j < BR; ++j) {
-          const int k = k0 + j;
-          const bool dirty = k >= a.R || ((k < 64 ? dm0 >> k : dm1 >> (k - 64)) & 1ull);
-          const uint32_t si = group_bcast<LPG>(pid[j / LPG], j % LPG);
-          const float qi = __uint_as_float(group_bcast<LPG>(pwt[j / LPG], j % LPG));
-          rs[j] = dirty ? 0u : min(si, (uint32_t)a.N - 1u);  // skipped rows: slot 0, weight 0
-          rq[j] = dirty ? 0.0f : qi;
-        }
+          for (int q = 0; q < RPL; ++q) cn[q] = cl[min(i + BR + q * LPG + li, ce - 1)];
+          uint32_t rs[BR];
+          float rq[BR];
+          float4 rv[BR];
 #pragma unroll
-        for (int j = 0; j < BR; ++j)
-          rv[j] = *reinterpret_cast<const float4*>(Mb + (rs[j] * row_bytes + col_bytes));
+          for (int j = 0; j < BR; ++j) {
+            const uint32_t si = group_bcast<LPG>(c[j / LPG].x, j % LPG);
+            const float qi = __uint_as_float(group_bcast<LPG>(c[j / LPG].y, j % LPG));
+            rs[j] = min(si, (uint32_t)a.N - 1u);
+            rq[j] = i + j < ce ? qi : 0.0f;  // the tail repeats the last row with weight 0
+          }
 #pragma unroll
-        for (int j = 0; j < BR; ++j) {
-          acc.x = fmaf(rq[j], rv[j].x, acc.x);
-          acc.y = fmaf(rq[j], rv[j].y, acc.y);
-          acc.z = fmaf(rq[j], rv[j].z, acc.z);
-          acc.w = fmaf(rq[j], rv[j].w, acc.w);
+          for (int j = 0; j < BR; ++j)
+            rv[j] = *reinterpret_cast<const float4*>(Mb + (rs[j] * row_bytes + col_bytes));
+#pragma unroll
+          for (int j = 0; j < BR; ++j) {
+            acc.x = fmaf(rq[j], rv[j].x, acc.x);
+            acc.y = fmaf(rq[j], rv[j].y, acc.y);
+            acc.z = fmaf(rq[j], rv[j].z, acc.z);
+            acc.w = fmaf(rq[j], rv[j].w, acc.w);
+          }
+#pragma unroll
+          for (int q = 0; q < RPL; ++q) c[q] = cn[q];
         }
       }
       float* ring = yr + tt * YS + li;
@@ -565,7 +611,7 @@ __global__ __launch_bounds__(NT) void two_phase_scan_kernel(StreamArgs a) {
       ring[LPG] = 0.f;
       ring[2 * LPG] = 0.f;
       ring[3 * LPG] = 0.f;
-      *reinterpret_cast<float4*>(a.y_part + ltok * dv + sl * SW + li * 4) = y;
+      *reinterpret_cast<float4*>(y_out + ltok * dv) = y;
     }
     __syncthreads();
   }
@@ -645,21 +691,17 @@ StreamPlan plan_stream(const sdm_dims& d, int64_t N) {
   const int lpg = pl.SW / 4;
   const int gw = pl.NT / lpg;
   const int64_t walks = d.B * (int64_t)d.H;
-  // Two-phase needs every owner of a walk's slots in one workgroup; it is used once
-  // the (walk, slice) workgroups alone reach half the CUs.  Otherwise the lane groups
-  // of a walk are split over `parts` workgroups (reads then use LDS atomics).
-  pl.two_phase = (d.flags & SDM_FLAG_SCAN_TWO_PHASE) ? true
-                 : (d.flags & SDM_FLAG_SCAN_STREAM) ? false
-                                                     : walks * pl.S >= 128;
+  pl.two_phase = !(d.flags & SDM_FLAG_SCAN_STREAM);
+  // the lane groups of a walk are split over `parts` workgroups until the grid
+  // reaches one workgroup per CU
   int parts = 1;
-  if (!pl.two_phase)
-    while (walks * pl.S * parts < 256 && gw * parts * 2 <= MAX_GT) parts *= 2;
+  while (walks * pl.S * parts < 256 && gw * parts * 2 <= MAX_GT) parts *= 2;
   pl.parts = parts;
   pl.GT = gw * parts;
   pl.log2GT = ilog2(pl.GT);
-  // token chunk: bound the entries + partial-read buffers to ~2 GiB
-  const int64_t per_tok = walks * (d.W + d.R) * 16 + (int64_t)parts * walks * d.d_v * 4 +
-                          walks * 16;
+  // token chunk: bound the per-token buffers to ~2 GiB
+  const int64_t per_tok = walks * ((d.W + d.R) * 8 + (int64_t)parts * d.d_v * 4 +
+                                   (pl.two_phase ? d.R * 8 + (parts + 1) * 4 : 0));
   int64_t tc = (2ll << 30) / per_tok;
   tc = tc < ROUND ? ROUND : (tc / ROUND) * ROUND;
   pl.Tc = d.T < tc ? d.T : tc;
@@ -667,18 +709,45 @@ StreamPlan plan_stream(const sdm_dims& d, int64_t N) {
   return pl;
 }
 
-size_t stream_workspace_bytes(const sdm_dims& d, const StreamPlan& pl) {
+namespace {
+
+// Byte offsets of the scan's buffers inside the workspace (256-byte aligned).
+struct StreamLayout {
+  size_t counts, offsets, entries, y_part, trash, begins, clean, cstart, total;
+};
+
+StreamLayout stream_layout(const sdm_dims& d, const StreamPlan& pl) {
   const int64_t walks = d.B * (int64_t)d.H;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  StreamLayout L;
   size_t s = 0;
-  s += al((size_t)walks * pl.rounds * pl.GT * 4);                 // counts
-  s += al((size_t)walks * pl.GT * (pl.rounds + 1) * 4);           // offsets
-  s += al((size_t)walks * pl.Tc * (d.W + d.R) * 16);              // entries
-  s += al((size_t)pl.parts * d.B * pl.Tc * d.H * d.d_v * 4);      // y_part
-  s += al((size_t)walks * pl.S * pl.parts * pl.NT * 16);          // trash
-  s += al((size_t)walks * pl.GT * pl.rounds * 4);                 // begins
-  s += al((size_t)d.B * pl.Tc * d.H * 16);                        // dirty bits
-  return s;
+  L.counts = s;
+  s += al((size_t)walks * pl.rounds * pl.GT * 4);
+  L.offsets = s;
+  s += al((size_t)walks * pl.GT * (pl.rounds + 1) * 4);
+  L.entries = s;
+  s += al((size_t)walks * pl.Tc * (d.W + d.R) * 8);
+  L.y_part = s;
+  s += al((size_t)pl.parts * walks * pl.Tc * d.d_v * 4);
+  L.trash = s;
+  s += al((size_t)walks * pl.S * pl.parts * pl.NT * 16);
+  L.begins = L.clean = L.cstart = s;
+  if (pl.two_phase) {
+    L.begins = s;
+    s += al((size_t)walks * pl.GT * pl.rounds * 4);
+    L.clean = s;
+    s += al((size_t)walks * pl.Tc * d.R * 8);
+    L.cstart = s;
+    s += al((size_t)walks * pl.Tc * (pl.parts + 1) * 4);
+  }
+  L.total = s;
+  return L;
+}
+
+}  // namespace
+
+size_t stream_workspace_bytes(const sdm_dims& d, const StreamPlan& pl) {
+  return stream_layout(d, pl).total;
 }
 
 hipError_t launch_stream_scan(const ScanArgs& sa, const StreamPlan& pl, void* ws,
@@ -708,27 +777,29 @@ hipError_t launch_stream_scan(const ScanArgs& sa, const StreamPlan& pl, void* ws
   a.parts = pl.parts;
   a.GT = pl.GT;
   a.log2GT = pl.log2GT;
+  a.log2GW = ilog2(pl.GT / pl.parts);
   const int64_t walks = sa.B * (int64_t)sa.H;
-  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  sdm_dims dd{};
+  dd.B = sa.B;
+  dd.H = sa.H;
+  dd.W = sa.W;
+  dd.R = sa.R;
+  dd.d_v = sa.d_v;
+  const StreamLayout L = stream_layout(dd, pl);
+  char* base = static_cast<char*>(ws);
+  a.counts = reinterpret_cast<int*>(base + L.counts);
+  a.offsets = reinterpret_cast<int*>(base + L.offsets);
+  a.entries = reinterpret_cast<uint2*>(base + L.entries);
+  a.y_part = reinterpret_cast<float*>(base + L.y_part);
+  a.trash = reinterpret_cast<float4*>(base + L.trash);
+  a.begins = reinterpret_cast<int*>(base + L.begins);
+  a.clean = reinterpret_cast<uint2*>(base + L.clean);
+  a.cstart = reinterpret_cast<int*>(base + L.cstart);
   for (int64_t t0 = 0; t0 < sa.T; t0 += pl.Tc) {
     a.t0 = t0;
     a.Tc = sa.T - t0 < pl.Tc ? sa.T - t0 : pl.Tc;
     a.rounds = (int)((a.Tc + ROUND - 1) / ROUND);
-    char* p = static_cast<char*>(ws);
-    a.counts = reinterpret_cast<int*>(p);
-    p += al((size_t)walks * pl.rounds * pl.GT * 4);
-    a.offsets = reinterpret_cast<int*>(p);
-    p += al((size_t)walks * pl.GT * (pl.rounds + 1) * 4);
-    a.entries = reinterpret_cast<uint4*>(p);
-    p += al((size_t)walks * pl.Tc * (sa.W + sa.R) * 16);
     a.walk_entries = a.Tc * (sa.W + sa.R);
-    a.y_part = reinterpret_cast<float*>(p);
-    p += al((size_t)pl.parts * sa.B * pl.Tc * sa.H * sa.d_v * 4);
-    a.trash = reinterpret_cast<float4*>(p);
-    p += al((size_t)walks * pl.S * pl.parts * pl.NT * 16);
-    a.begins = reinterpret_cast<int*>(p);
-    p += al((size_t)walks * pl.GT * pl.rounds * 4);
-    a.dirty = reinterpret_cast<unsigned long long*>(p);
 
     hipLaunchKernelGGL(bucket_count_kernel, dim3((unsigned)(walks * a.rounds)), dim3(256), 0, st,
                        a);
@@ -740,7 +811,7 @@ hipError_t launch_stream_scan(const ScanArgs& sa, const StreamPlan& pl, void* ws
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       hipLaunchKernelGGL(bucket_scatter_rev_kernel, dim3((unsigned)(walks * a.rounds)), dim3(64),
                          lds, st, a);
-      const dim3 grid((unsigned)(walks * pl.S));
+      const dim3 grid((unsigned)(walks * pl.S * pl.parts));
       if (pl.SW == 32)
         hipLaunchKernelGGL((two_phase_scan_kernel<1024, 32, 8, 8>), grid, dim3(1024), 0, st, a);
       else

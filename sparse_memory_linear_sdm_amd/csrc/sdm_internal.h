@@ -70,19 +70,21 @@ struct StreamArgs {
   float* y_raw;
   int* counts;     // [walks][rounds][GT]
   int* offsets;    // [walks][GT][rounds + 1]
-  uint4* entries;  // [walks][walk_entries]
+  // owner-stream entry: {slot | token-in-round << 24, weight bits | read << 31}
+  uint2* entries;  // [walks][walk_entries]
   float* y_part;   // [parts][B][Tc][H][d_v]
   float4* trash;   // one float4 per scan thread: sink of non-writing accesses' stores
-  int* begins;               // two-phase: [walks][GT][rounds] start of each packed segment
-  unsigned long long* dirty;  // two-phase: [B][Tc][H][2] dirty-read bits per read position
+  int* begins;    // two-phase: [walks][GT][rounds] start of each packed segment
+  uint2* clean;   // two-phase: [B][Tc][H][R] clean reads {slot, weight bits}, grouped by part
+  int* cstart;    // two-phase: [B][Tc][H][parts + 1] start of each part's clean reads
   int64_t B, T, t0, Tc, walk_entries;
   int32_t H, N, W, R, d_v;
   float eps;
-  int32_t S, parts, GT, log2GT, rounds;
+  int32_t S, parts, GT, log2GT, log2GW, rounds;
 };
 struct StreamPlan {
   int SW, S, NT, parts, GT, log2GT, rounds;
-  bool two_phase;  // one workgroup per (walk, slice), reads summed in registers
+  bool two_phase;  // clean reads summed in registers after each round's writes
   int64_t Tc;
 };
 StreamPlan plan_stream(const sdm_dims& d, int64_t N);
