@@ -355,6 +355,10 @@ __global__ __launch_bounds__(NT) void stream_scan_kernel(StreamArgs a) {
 // Positions are handed out downwards, so a slot's accesses keep token order with
 // writes before reads.
 // ---------------------------------------------------------------------------
+// The token loop is latency-bound (one wavefront, one token at a time), so the ids
+// and weights of the next D tokens are loaded while the current D are placed.
+// KC = number of 64-wide chunks of W and R (1 or 2).
+template <int KC, int D>
 __global__ __launch_bounds__(64) void bucket_scatter_rev_kernel(StreamArgs a) {
   extern __shared__ uint32_t dyn[];
   int* cur = reinterpret_cast<int*>(dyn);
@@ -373,52 +377,85 @@ __global__ __launch_bounds__(64) void bucket_scatter_rev_kernel(StreamArgs a) {
   uint2* ent = a.entries + w * a.walk_entries;
   const int64_t t_lo = (int64_t)r * ROUND;
   const int64_t t_hi = min<int64_t>(a.Tc, t_lo + ROUND);
-  for (int64_t t = t_hi - 1; t >= t_lo; --t) {
-    const int64_t tok = (b * a.T + a.t0 + t) * a.H + h;
-    const int64_t ltok = (b * a.Tc + t) * a.H + h;  // chunk-local token row
-    const int tt = (int)(t - t_lo);
-    int pk[2];   // owning part of a clean read, -1 otherwise
-    uint2 ck[2];
+  const int64_t tok0 = (b * a.T + a.t0) * a.H + h;  // token t -> tok0 + t*H
+
+  // ids / weight bits of the reads (r*) and writes (x*) of D tokens
+  uint32_t rs[D][KC], rq[D][KC], xs[D][KC], xq[D][KC];
+  auto fetch = [&](int64_t tb, uint32_t (&fs)[D][KC], uint32_t (&fq)[D][KC],
+                   uint32_t (&gs)[D][KC], uint32_t (&gq)[D][KC]) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int k = c * 64 + lane;
-      pk[c] = -1;
-      ck[c] = make_uint2(0u, 0u);
-      if (k < a.R) {
-        const uint32_t s = (uint32_t)a.idx_r[tok * a.R + k];
-        const float q = a.wt_r[tok * a.R + k];
-        const uint32_t grp = group_of(s, a.log2GT);
-        if ((bm[s >> 5] >> (s & 31u)) & 1u) {
-          const int pos = atomicSub(&cur[grp], 1) - 1;
-          ent[pos] = make_entry(s, tt, q, true);
-        } else {
-          pk[c] = (int)(grp >> a.log2GW);
-          ck[c] = make_uint2(s, __float_as_uint(q));
+    for (int u = 0; u < D; ++u) {
+      const int64_t tok = tok0 + max<int64_t>(tb - u, t_lo) * a.H;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        const int kr = min(c * 64 + lane, a.R - 1), kw = min(c * 64 + lane, a.W - 1);
+        fs[u][c] = (uint32_t)a.idx_r[tok * a.R + kr];
+        fq[u][c] = __float_as_uint(a.wt_r[tok * a.R + kr]);
+        gs[u][c] = (uint32_t)a.idx_w[tok * a.W + kw];
+        gq[u][c] = __float_as_uint(a.wt_w[tok * a.W + kw]);
+      }
+    }
+  };
+  fetch(t_hi - 1, rs, rq, xs, xq);
+  for (int64_t tb = t_hi - 1; tb >= t_lo; tb -= D) {
+    uint32_t ns[D][KC], nq[D][KC], ms[D][KC], mq[D][KC];
+    fetch(tb - D, ns, nq, ms, mq);
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      const int64_t t = tb - u;
+      if (t < t_lo) break;
+      const int64_t ltok = (b * a.Tc + t) * a.H + h;  // chunk-local token row
+      const int tt = (int)(t - t_lo);
+      int pk[KC];  // owning part of a clean read, -1 otherwise
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        const uint32_t sr = rs[u][c];
+        pk[c] = -1;
+        if (c * 64 + lane < a.R) {
+          const uint32_t grp = group_of(sr, a.log2GT);
+          if ((bm[sr >> 5] >> (sr & 31u)) & 1u) {
+            const int pos = atomicSub(&cur[grp], 1) - 1;
+            ent[pos] = make_entry(sr, tt, __uint_as_float(rq[u][c]), true);
+          } else {
+            pk[c] = (int)(grp >> a.log2GW);
+          }
         }
       }
-    }
-    int* cs = a.cstart + ltok * (a.parts + 1);
-    uint2* cl = a.clean + ltok * a.R;
-    int base = 0;
-    for (int p = 0; p < a.parts; ++p) {
-      if (lane == 0) cs[p] = base;
+      int* cs = a.cstart + ltok * (a.parts + 1);
+      uint2* cl = a.clean + ltok * a.R;
+      int base = 0;
+      for (int p = 0; p < a.parts; ++p) {
+        if (lane == 0) cs[p] = base;
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const bool mine = pk[c] == p;
-        const unsigned long long m = __ballot(mine);
-        if (mine) cl[base + __popcll(m & below)] = ck[c];
-        base += __popcll(m);
+        for (int c = 0; c < KC; ++c) {
+          const bool mine = pk[c] == p;
+          const unsigned long long m = __ballot(mine);
+          if (mine) cl[base + __popcll(m & below)] = make_uint2(rs[u][c], rq[u][c]);
+          base += __popcll(m);
+        }
       }
+      if (lane == 0) cs[a.parts] = base;
+      __syncthreads();
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        if (c * 64 + lane < a.W) {
+          const uint32_t sw = xs[u][c];
+          const int pos = atomicSub(&cur[group_of(sw, a.log2GT)], 1) - 1;
+          ent[pos] = make_entry(sw, tt, __uint_as_float(xq[u][c]), false);
+          atomicOr(&bm[sw >> 5], 1u << (sw & 31u));
+        }
+      }
+      __syncthreads();
     }
-    if (lane == 0) cs[a.parts] = base;
-    __syncthreads();
-    for (int k = lane; k < a.W; k += 64) {
-      const uint32_t s = (uint32_t)a.idx_w[tok * a.W + k];
-      const int pos = atomicSub(&cur[group_of(s, a.log2GT)], 1) - 1;
-      ent[pos] = make_entry(s, tt, a.wt_w[tok * a.W + k], false);
-      atomicOr(&bm[s >> 5], 1u << (s & 31u));
-    }
-    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < D; ++u)
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        rs[u][c] = ns[u][c];
+        rq[u][c] = nq[u][c];
+        xs[u][c] = ms[u][c];
+        xq[u][c] = mq[u][c];
+      }
   }
   for (int g = lane; g < a.GT; g += 64)
     a.begins[((int64_t)w * a.GT + g) * a.rounds + r] = cur[g];
@@ -806,11 +843,16 @@ hipError_t launch_stream_scan(const ScanArgs& sa, const StreamPlan& pl, void* ws
     hipLaunchKernelGGL(bucket_offsets_kernel, dim3((unsigned)walks), dim3(1024), 0, st, a);
     if (pl.two_phase) {
       const size_t lds = (size_t)pl.GT * 4 + (size_t)((sa.N + 31) / 32) * 4;
+      const void* rev = sa.W <= 64 && sa.R <= 64
+                            ? reinterpret_cast<const void*>(bucket_scatter_rev_kernel<1, 8>)
+                            : reinterpret_cast<const void*>(bucket_scatter_rev_kernel<2, 4>);
       if (lds > 65536)  // slot bitmaps beyond 64 KiB (N > ~500k) need the larger LDS limit
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(bucket_scatter_rev_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      hipLaunchKernelGGL(bucket_scatter_rev_kernel, dim3((unsigned)(walks * a.rounds)), dim3(64),
-                         lds, st, a);
+        (void)hipFuncSetAttribute(rev, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      const dim3 rg((unsigned)(walks * a.rounds));
+      if (sa.W <= 64 && sa.R <= 64)
+        hipLaunchKernelGGL((bucket_scatter_rev_kernel<1, 8>), rg, dim3(64), lds, st, a);
+      else
+        hipLaunchKernelGGL((bucket_scatter_rev_kernel<2, 4>), rg, dim3(64), lds, st, a);
       const dim3 grid((unsigned)(walks * pl.S * pl.parts));
       if (pl.SW == 32)
         hipLaunchKernelGGL((two_phase_scan_kernel<1024, 32, 8, 8>), grid, dim3(1024), 0, st, a);
