@@ -83,7 +83,8 @@ __device__ __forceinline__ void epilogue_store(const ProjDst& d, int64_t m, int 
 // The next K-tile is fetched into registers while the current one is multiplied
 // out of LDS (double-buffered, one barrier per K-step).  LDS rows are padded by
 // 16 B.  Tiles are handed out XCD by XCD in groups of GROUP_M row tiles, so the
-// blocks resident on one XCD share A and B slices through its L2.
+// blocks resident on one XCD share A and B slices through its L2.  The epilogue
+// goes through LDS so that every store writes a 16-byte row segment.
 // ---------------------------------------------------------------------------
 constexpr int BM = 256, BN = 256, BK = 64, LDK = BK + 8, NTH = 512, GROUP_M = 4;
 constexpr int A_CHUNKS = BM * BK / 8 / NTH;  // 16-byte chunks per thread per K-tile
@@ -192,31 +193,54 @@ __global__ __launch_bounds__(NTH) void proj_gemm_bf16_kernel(
     cur ^= 1;
   }
 
-  // 32x32 output block layout: register r of lane l holds
-  // row (r/4)*8 + (l/32)*4 + r%4, column l%32.  Each lane owns two columns.
+  // Epilogue through LDS: each wave writes one 32x32 block at a time into a private
+  // padded LDS patch (32 rows of 36 floats; register r of lane l of a 32x32 MFMA
+  // block holds row (r/4)*8 + (l/32)*4 + r%4, column l%32), then every lane stores
+  // 4-column row segments: one 16-byte store where the 4 columns are plain copies
+  // into consecutive addresses, else one routed store per column.  The A/B buffers
+  // are free after the last barrier.
+  float* patch = reinterpret_cast<float*>(&As[0][0]) + wave * (32 * 36);
+  const int sr = lane >> 3;        // row within an 8-row group
+  const int sc = (lane & 7) * 4;   // first of this lane's 4 columns
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int c = tile_n + wn * 64 + j * 32 + (lane & 31);
-    if (c >= Ncol) continue;
-    const ColDst o = column_dst(dst, c);
-    if (o.kind == 0) {
+    const int cb = tile_n + wn * 64 + j * 32;  // first column of the block
+    // this lane's 4 columns: contiguous float4 destination if all are plain copies
+    // of one region of one head
+    const int c0 = cb + sc;
+    ColDst od[4];
+    bool vec = c0 + 3 < Ncol;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int e = 0; e < 4; ++e) {
+      od[e] = column_dst(dst, min(c0 + e, Ncol - 1));
+      vec = vec && od[e].kind == 0 && od[e].stride == od[0].stride &&
+            od[e].base == od[0].base + e;
+    }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t lm =
-              tile_m + wm * 128 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          if (lm < M) o.base[(row0 + lm) * o.stride] = acc[i][j][r];
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        patch[((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * 36 + (lane & 31)] = acc[i][j][r];
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int rr = q * 8 + sr;
+        const int64_t lm = tile_m + wm * 128 + i * 32 + rr;
+        const float4 v = *reinterpret_cast<const float4*>(patch + rr * 36 + sc);
+        if (lm < M) {
+          if (vec) {
+            *reinterpret_cast<float4*>(od[0].base + (row0 + lm) * od[0].stride) = v;
+          } else {
+            const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (c0 + e < Ncol) od[e].base[(row0 + lm) * od[e].stride] = column_value(od[e], vv[e]);
+          }
         }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t lm =
-              tile_m + wm * 128 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          if (lm < M) o.base[(row0 + lm) * o.stride] = column_value(o, acc[i][j][r]);
-        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_wave_barrier();
     }
   }
 }
