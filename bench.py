@@ -133,7 +133,11 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    _lib.timing_read()  # drop records of earlier calls
 
+    # timed steps: the library brackets each of its kernel launches with HIP events
+    # on `stream` (SDM_FLAG_TIMING), so every kernel's duration comes from this run
+    d.flags |= _lib.SDM_FLAG_TIMING
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -141,14 +145,22 @@ def main():
         step(evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    d.flags &= ~_lib.SDM_FLAG_TIMING
     ms_sel = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     ms_scan = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     ms_step = float(np.mean([e[0].elapsed_time(e[2]) for e in evs]))
     ms_wall = wall * 1e3 / args.steps
+    per_kernel = {}
+    for name, ms in _lib.timing_read(1 << 16):
+        per_kernel.setdefault(name, []).append(ms)
+    kernels_ms = {k: {"avg": float(np.mean(v)), "launches": len(v)} for k, v in per_kernel.items()}
+    scan_kernel = next(k for k in ("two_phase_scan", "stream_scan", "scan_direct") if k in kernels_ms)
+    # launches per step (the scan can run in token chunks): time per step of that kernel
+    scan_ms = kernels_ms[scan_kernel]["avg"] * kernels_ms[scan_kernel]["launches"] / args.steps
 
     tokens = wl.tokens
     slot_bytes = tokens * wl.H * wl.slot_bytes_per_token_head()
-    achieved = slot_bytes / (ms_scan * 1e-3) / 1e9
+    achieved = slot_bytes / (scan_ms * 1e-3) / 1e9
     res = {
         "metric": METRIC,
         "value": tokens / (ms_wall * 1e-3),
@@ -166,11 +178,13 @@ def main():
                    "N": wl.N, "n": wl.n, "W": wl.W, "R": wl.R, "d_v": wl.d_v,
                    "state": "fp32 [B,H,N,d_v]", "tokens_per_step": tokens},
         "phases_ms": {"select": ms_sel, "scan": ms_scan, "step_events": ms_step},
+        "kernels_ms": kernels_ms,
         "effective_hbm_gbs_step": slot_bytes / (ms_wall * 1e-3) / 1e9,
-        "roofline": {"bound": "hbm", "kernel": "scan", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": scan_kernel, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic(wl.name),
-                     "algorithmic_bytes_per_launch": slot_bytes},
+                     "algorithmic_bytes_per_launch":
+                         slot_bytes * args.steps / kernels_ms[scan_kernel]["launches"]},
     }
     if args.copy_calibration:
         nb = args.copy_calibration << 20

@@ -78,8 +78,13 @@ extern "C" {
 #define SDM_FLAG_SCAN_DIRECT 1    /* one workgroup per (b,h), tokens in lock-step */
 #define SDM_FLAG_SCAN_STREAM 2    /* slot-owner lane groups fed by per-group streams,
                                      a walk's groups split over workgroups */
-#define SDM_FLAG_SCAN_TWO_PHASE 4 /* slot-owner writes, then token-major reads, one
-                                     workgroup per (b,h, d_v slice) */
+#define SDM_FLAG_SCAN_TWO_PHASE 4 /* slot-owner writes, then token-major reads of the
+                                     slots each workgroup owns */
+/* instrumentation flag (sdm_dims.flags, may be combined with one schedule flag):
+   every kernel launch of the call is bracketed by a pair of HIP events recorded on
+   the call's stream; sdm_timing_read returns the durations.  Results are the same
+   with and without it. */
+#define SDM_FLAG_TIMING 8
 
 /* Limits of this build (SDM_ERR_UNSUPPORTED beyond them). */
 #define SDM_MAX_COUNT 128   /* W and R */
@@ -100,7 +105,8 @@ extern "C" {
  *   gate_act  activation of the output gate vector (SDM_GATE_*)
  *   eps       RMSNorm epsilon (>= 0)
  *   flags     0, or one SDM_FLAG_SCAN_* bit to force a scan schedule (all schedules
- *             compute the same recurrence; by default the library picks by shape)
+ *             compute the same recurrence; by default the library picks by shape),
+ *             optionally OR-ed with SDM_FLAG_TIMING
  */
 typedef struct sdm_dims {
   int64_t B, T, d_model;
@@ -208,6 +214,21 @@ SDM_API int32_t sdm_scan(const sdm_dims* dims, const sdm_sel* in, const float* n
 SDM_API int32_t sdm_forward(const sdm_dims* dims, const void* x, const void* w_proj, const float* A,
                     const float* b_dt, const float* norm_w, float* state, float* out,
                     const sdm_sel* debug, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Kernel durations recorded by calls made with SDM_FLAG_TIMING (instrumentation;
+ * not a step of the method).  Fills out[0..k) with the oldest k records (k <= max),
+ * waiting for each to complete, removes them from the record and returns k; 0 when
+ * nothing is recorded.  `name` points to a static string naming the kernel.  The
+ * record is process-wide and holds at most 65536 launches (older ones are dropped).
+ * Returns SDM_ERR_NULL if out is NULL with max > 0, SDM_ERR_HIP if an event query
+ * fails.
+ */
+typedef struct sdm_kernel_time {
+  const char* name;
+  float ms;
+} sdm_kernel_time;
+SDM_API int32_t sdm_timing_read(sdm_kernel_time* out, int32_t max);
 
 #ifdef __cplusplus
 }

@@ -21,9 +21,10 @@ SDM_GATE_NONE, SDM_GATE_SIGMOID, SDM_GATE_SILU = 0, 1, 2
 SDM_ENTRY_SELECT, SDM_ENTRY_SCAN, SDM_ENTRY_FORWARD = 0, 1, 2
 SDM_MAX_COUNT, SDM_MAX_HALF = 128, 1024
 SDM_FLAG_SCAN_DIRECT, SDM_FLAG_SCAN_STREAM, SDM_FLAG_SCAN_TWO_PHASE = 1, 2, 4
+SDM_FLAG_TIMING = 8
 
 EXPORTS = ("sdm_abi_version", "sdm_status_string", "sdm_workspace_bytes", "sdm_select",
-           "sdm_select_from_scores", "sdm_scan", "sdm_forward")
+           "sdm_select_from_scores", "sdm_scan", "sdm_forward", "sdm_timing_read")
 
 
 class SdmDims(ctypes.Structure):
@@ -36,6 +37,10 @@ class SdmDims(ctypes.Structure):
 class SdmSel(ctypes.Structure):
     _fields_ = [(name, ctypes.c_void_p) for name in
                 ("idx_w", "wt_w", "idx_r", "wt_r", "v", "gate", "alpha", "beta", "scores")]
+
+
+class SdmKernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("ms", ctypes.c_float)]
 
 
 class SdmError(RuntimeError):
@@ -71,6 +76,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sdm_forward.restype = I32
     lib.sdm_forward.argtypes = [P(SdmDims), VP, VP, VP, VP, VP, VP, VP, P(SdmSel), VP,
                                 ctypes.c_size_t, VP]
+    lib.sdm_timing_read.restype = I32
+    lib.sdm_timing_read.argtypes = [P(SdmKernelTime), I32]
     del I64
     _lib = lib
     return lib
@@ -140,3 +147,12 @@ def sdm_forward(d: SdmDims, x, w_proj, A, b_dt, norm_w, state, out, debug: SdmSe
                               _ptr(norm_w), _ptr(state), _ptr(out),
                               ctypes.byref(debug) if debug is not None else None, _ptr(ws),
                               ws_bytes, _stream(stream)))
+
+
+def timing_read(max_records: int = 4096) -> list:
+    """[(kernel name, ms)] of launches recorded under SDM_FLAG_TIMING, oldest first."""
+    buf = (SdmKernelTime * max_records)()
+    n = load().sdm_timing_read(buf, max_records)
+    if n < 0:
+        raise SdmError(n, load().sdm_status_string(n).decode())
+    return [(buf[i].name.decode(), float(buf[i].ms)) for i in range(n)]

@@ -306,11 +306,13 @@ hipError_t launch_proj_gemm(const sdm_dims& d, const void* x, const void* w_proj
   if (d.in_dtype == SDM_DTYPE_BF16) {
     const int64_t tiles = ((rows + BM - 1) / BM) * ((Ncol + BN - 1) / BN);
     const dim3 grid((unsigned)(((tiles + NXCD - 1) / NXCD) * NXCD));
+    KernelTimer kt("proj_gemm_bf16", s);
     hipLaunchKernelGGL(proj_gemm_bf16_kernel, grid, dim3(NTH), 0, s,
                        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_proj), row0,
                        rows, Ncol, K, dst);
   } else {
     dim3 grid((Ncol + 63) / 64, (unsigned)((rows + 63) / 64));
+    KernelTimer kt("proj_gemm_f32", s);
     hipLaunchKernelGGL(proj_gemm_f32_kernel, grid, dim3(256), 0, s, static_cast<const float*>(x),
                        static_cast<const float*>(w_proj), row0, rows, Ncol, K, dst);
   }

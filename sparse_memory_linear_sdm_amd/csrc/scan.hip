@@ -111,6 +111,7 @@ size_t scan_workspace_bytes(const sdm_dims& d) {
 hipError_t launch_scan(const sdm_dims& d, const ScanArgs& a, void* ws, size_t, hipStream_t s) {
   if (scan_uses_stream(d)) return launch_stream_scan(a, plan_stream(d, a.N), ws, s);
   const dim3 grid((unsigned)(a.B * a.H));
+  KernelTimer kt("scan_direct", s);
   switch (a.d_v) {
     case 16: hipLaunchKernelGGL(scan_kernel<16>, grid, dim3(256), 0, s, a); break;
     case 32: hipLaunchKernelGGL(scan_kernel<32>, grid, dim3(256), 0, s, a); break;

@@ -838,9 +838,15 @@ hipError_t launch_stream_scan(const ScanArgs& sa, const StreamPlan& pl, void* ws
     a.rounds = (int)((a.Tc + ROUND - 1) / ROUND);
     a.walk_entries = a.Tc * (sa.W + sa.R);
 
-    hipLaunchKernelGGL(bucket_count_kernel, dim3((unsigned)(walks * a.rounds)), dim3(256), 0, st,
-                       a);
-    hipLaunchKernelGGL(bucket_offsets_kernel, dim3((unsigned)walks), dim3(1024), 0, st, a);
+    {
+      KernelTimer kt("bucket_count", st);
+      hipLaunchKernelGGL(bucket_count_kernel, dim3((unsigned)(walks * a.rounds)), dim3(256), 0,
+                         st, a);
+    }
+    {
+      KernelTimer kt("bucket_offsets", st);
+      hipLaunchKernelGGL(bucket_offsets_kernel, dim3((unsigned)walks), dim3(1024), 0, st, a);
+    }
     if (pl.two_phase) {
       const size_t lds = (size_t)pl.GT * 4 + (size_t)((sa.N + 31) / 32) * 4;
       const void* rev = sa.W <= 64 && sa.R <= 64
@@ -849,19 +855,27 @@ hipError_t launch_stream_scan(const ScanArgs& sa, const StreamPlan& pl, void* ws
       if (lds > 65536)  // slot bitmaps beyond 64 KiB (N > ~500k) need the larger LDS limit
         (void)hipFuncSetAttribute(rev, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       const dim3 rg((unsigned)(walks * a.rounds));
-      if (sa.W <= 64 && sa.R <= 64)
-        hipLaunchKernelGGL((bucket_scatter_rev_kernel<1, 8>), rg, dim3(64), lds, st, a);
-      else
-        hipLaunchKernelGGL((bucket_scatter_rev_kernel<2, 4>), rg, dim3(64), lds, st, a);
+      {
+        KernelTimer kt("bucket_scatter_rev", st);
+        if (sa.W <= 64 && sa.R <= 64)
+          hipLaunchKernelGGL((bucket_scatter_rev_kernel<1, 8>), rg, dim3(64), lds, st, a);
+        else
+          hipLaunchKernelGGL((bucket_scatter_rev_kernel<2, 4>), rg, dim3(64), lds, st, a);
+      }
       const dim3 grid((unsigned)(walks * pl.S * pl.parts));
+      KernelTimer kt("two_phase_scan", st);
       if (pl.SW == 32)
         hipLaunchKernelGGL((two_phase_scan_kernel<1024, 32, 8, 8>), grid, dim3(1024), 0, st, a);
       else
         hipLaunchKernelGGL((two_phase_scan_kernel<1024, 16, 8, 8>), grid, dim3(1024), 0, st, a);
     } else {
-      hipLaunchKernelGGL(bucket_scatter_kernel, dim3((unsigned)(walks * a.rounds)), dim3(64), 0,
-                         st, a);
+      {
+        KernelTimer kt("bucket_scatter", st);
+        hipLaunchKernelGGL(bucket_scatter_kernel, dim3((unsigned)(walks * a.rounds)), dim3(64), 0,
+                           st, a);
+      }
       const dim3 grid((unsigned)(walks * pl.S * pl.parts));
+      KernelTimer kt("stream_scan", st);
       if (pl.SW == 32)
         hipLaunchKernelGGL((stream_scan_kernel<1024, 32, 8>), grid, dim3(1024), 0, st, a);
       else
@@ -872,6 +886,7 @@ hipError_t launch_stream_scan(const ScanArgs& sa, const StreamPlan& pl, void* ws
     const int lpr = sa.d_v / 4 < 64 ? sa.d_v / 4 : 64;
     const int64_t rpb = 4 * (64 / lpr);
     const dim3 ng((unsigned)((rows + rpb - 1) / rpb));
+    KernelTimer kt("norm_gate", st);
     switch (sa.d_v) {
       case 16: hipLaunchKernelGGL(norm_gate_kernel<16>, ng, dim3(256), 0, st, a); break;
       case 32: hipLaunchKernelGGL(norm_gate_kernel<32>, ng, dim3(256), 0, st, a); break;

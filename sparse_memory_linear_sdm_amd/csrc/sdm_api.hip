@@ -26,8 +26,8 @@ struct Derived {
 int32_t check_dims(const sdm_dims* d, Derived* out) {
   if (!d) return SDM_ERR_NULL;
   const int32_t sched = SDM_FLAG_SCAN_DIRECT | SDM_FLAG_SCAN_STREAM | SDM_FLAG_SCAN_TWO_PHASE;
-  if (d->flags & ~sched) return SDM_ERR_UNSUPPORTED;
-  if (__builtin_popcount((unsigned)d->flags) > 1) return SDM_ERR_SHAPE;  // one schedule at most
+  if (d->flags & ~(sched | SDM_FLAG_TIMING)) return SDM_ERR_UNSUPPORTED;
+  if (__builtin_popcount((unsigned)(d->flags & sched)) > 1) return SDM_ERR_SHAPE;  // one schedule
   if (d->in_dtype != SDM_DTYPE_F32 && d->in_dtype != SDM_DTYPE_BF16) return SDM_ERR_DTYPE;
   if (d->gate_act < SDM_GATE_NONE || d->gate_act > SDM_GATE_SILU) return SDM_ERR_DTYPE;
   if (d->B < 0 || d->T < 0 || d->d_model < 1 || d->H < 1 || d->n < 1 || d->W < 1 || d->R < 1 ||
@@ -162,6 +162,15 @@ int32_t run_scan(const sdm_dims* d, const Derived& dv, const sdm_sel* in, const 
   return hip_status(launch_scan(*d, a, ws, ws_bytes, st));
 }
 
+// Switches kernel timing on for this thread while an entry point runs.
+struct TimingScope {
+  bool prev;
+  explicit TimingScope(const sdm_dims* d) : prev(timing_enabled()) {
+    timing_enable((d->flags & SDM_FLAG_TIMING) != 0);
+  }
+  ~TimingScope() { timing_enable(prev); }
+};
+
 }  // namespace
 
 extern "C" {
@@ -209,6 +218,7 @@ int32_t sdm_select(const sdm_dims* d, const void* x, const void* w_proj, const f
   const size_t need = select_ws_bytes(d, dv, out->scores != nullptr);
   if (need && (!ws || ws_bytes < need)) return SDM_ERR_WORKSPACE;
   if (need && !aligned16(ws)) return SDM_ERR_ALIGN;
+  TimingScope timing(d);
   (void)hipGetLastError();
   return run_select(d, dv, x, w_proj, A, b_dt, out, ws, (hipStream_t)stream);
 }
@@ -223,6 +233,7 @@ int32_t sdm_select_from_scores(const sdm_dims* d, const float* scores, int32_t* 
   if (!aligned16(scores) || !aligned16(idx_w) || !aligned16(wt_w) || !aligned16(idx_r) ||
       !aligned16(wt_r))
     return SDM_ERR_ALIGN;
+  TimingScope timing(d);
   (void)hipGetLastError();
   return hip_status(
       launch_select(*d, scores, dv.M, 0, idx_w, wt_w, idx_r, wt_r, (hipStream_t)stream));
@@ -241,6 +252,7 @@ int32_t sdm_scan(const sdm_dims* d, const sdm_sel* in, const float* norm_w, floa
     return SDM_ERR_ALIGN;
   const size_t need = align_up(scan_workspace_bytes(*d));
   if (need && (!ws || ws_bytes < need)) return SDM_ERR_WORKSPACE;
+  TimingScope timing(d);
   (void)hipGetLastError();
   return run_scan(d, dv, in, norm_w, state, out, y_raw, ws, ws_bytes, (hipStream_t)stream);
 }
@@ -283,6 +295,7 @@ int32_t sdm_forward(const sdm_dims* d, const void* x, const void* w_proj, const 
   void* sel_space = base + ps.total;
   void* scan_space = base + ps.total + sel_ws;
   hipStream_t s = (hipStream_t)stream;
+  TimingScope timing(d);
   (void)hipGetLastError();
   st = run_select(d, dv, x, w_proj, A, b_dt, &prod, sel_space, s);
   if (st != SDM_OK) return st;

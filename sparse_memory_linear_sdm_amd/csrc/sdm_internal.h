@@ -55,6 +55,23 @@ hipError_t launch_scan(const sdm_dims& d, const ScanArgs& a, void* ws, size_t ws
 size_t scan_workspace_bytes(const sdm_dims& d);
 
 // Slot-owner stream schedule of the scan (scan_stream.hip).
+// Instrumentation (SDM_FLAG_TIMING): the C entry points switch recording on for
+// the calling thread; every launch site holds a KernelTimer around its launch.
+void timing_enable(bool on);
+bool timing_enabled();
+class KernelTimer {
+ public:
+  KernelTimer(const char* name, hipStream_t s);
+  ~KernelTimer();
+  KernelTimer(const KernelTimer&) = delete;
+  KernelTimer& operator=(const KernelTimer&) = delete;
+
+ private:
+  const char* name_;
+  hipStream_t s_;
+  hipEvent_t a_ = nullptr;
+};
+
 struct StreamArgs {
   const int32_t* idx_w;
   const float* wt_w;

@@ -443,6 +443,7 @@ hipError_t launch_kpl(const float* scores, int64_t rows, int H, int n, int W, in
   const int nc = cand_count(maxc);
   const int kpc = (nc + 63) / 64;
   const dim3 grid((unsigned)(rows * H * 2));
+  KernelTimer kt("select", s);
 #define SDM_SEL_LAUNCH(KPC)                                                                   \
   hipLaunchKernelGGL((select_kernel<KPL, KPC>), grid, dim3(64), 0, s, scores, rows, H, n, W, R, \
                      out_row0, idx_w, wt_w, idx_r, wt_r)

@@ -76,8 +76,8 @@ def _select(lib, d, x=FAKE, w=FAKE, A=FAKE, b=FAKE, sel=None, ws=FAKE, nb=1 << 4
     (dict(eps=-1.0), _lib.SDM_ERR_SHAPE), (dict(eps=float("nan")), _lib.SDM_ERR_SHAPE),
     (dict(n=16, W=129), _lib.SDM_ERR_UNSUPPORTED), (dict(n=1025), _lib.SDM_ERR_UNSUPPORTED),
     (dict(d_v=48), _lib.SDM_ERR_UNSUPPORTED), (dict(d_model=60), _lib.SDM_ERR_UNSUPPORTED),
-    (dict(flags=8), _lib.SDM_ERR_UNSUPPORTED), (dict(flags=3), _lib.SDM_ERR_SHAPE),
-    (dict(flags=6), _lib.SDM_ERR_SHAPE),
+    (dict(flags=16), _lib.SDM_ERR_UNSUPPORTED), (dict(flags=3), _lib.SDM_ERR_SHAPE),
+    (dict(flags=6), _lib.SDM_ERR_SHAPE), (dict(flags=8 | 5), _lib.SDM_ERR_SHAPE),
     (dict(in_dtype=7), _lib.SDM_ERR_DTYPE), (dict(gate_act=3), _lib.SDM_ERR_DTYPE),
 ])
 def test_bad_dims_rejected_by_every_entry(lib, kw, code):
@@ -90,6 +90,19 @@ def test_bad_dims_rejected_by_every_entry(lib, kw, code):
     assert lib.sdm_forward(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, FAKE,
                            1 << 40, None) == code
     assert lib.sdm_workspace_bytes(ctypes.byref(d), 2) == 0
+
+
+def test_timing_flag_is_accepted_and_read_is_safe_without_records(lib):
+    # the instrumentation bit combines with one schedule bit; validation still runs first
+    for sched in (0, _lib.SDM_FLAG_SCAN_DIRECT, _lib.SDM_FLAG_SCAN_TWO_PHASE):
+        d0, d1 = _d(T=64, flags=sched), _d(T=64, flags=sched | _lib.SDM_FLAG_TIMING)
+        for entry in (_lib.SDM_ENTRY_SELECT, _lib.SDM_ENTRY_SCAN, _lib.SDM_ENTRY_FORWARD):
+            assert (lib.sdm_workspace_bytes(ctypes.byref(d1), entry) ==
+                    lib.sdm_workspace_bytes(ctypes.byref(d0), entry))
+        assert _select(lib, d1, x=None) == _lib.SDM_ERR_NULL
+    assert _lib.timing_read() == []
+    assert lib.sdm_timing_read(None, 0) == 0
+    assert lib.sdm_timing_read(None, 4) == _lib.SDM_ERR_NULL
 
 
 def test_null_dims(lib):
