@@ -14,13 +14,17 @@
 //   3. rank the candidates by (exact fp64 score desc, slot id asc), keep `count`;
 //   4. return the ids ascending with softmax weights of their scores.
 //
-// One wavefront per problem, everything in registers but two 256-bin histograms:
-//  * a top-k is an exact radix select on order-preserving 32-bit keys (four 8-bit
-//    passes over a wave-wide histogram + prefix scan), then compaction and a
-//    register bitonic sort of the k survivors;
-//  * the candidates' fp32-rounded sums order them monotonically with the exact
-//    sums, so the radix select runs on them and only the candidates tied at the
-//    fp32 threshold are ordered by their exact fp64 sums and ids.
+// One wavefront per problem, everything in registers but a 256-bin histogram and
+// small staging areas in LDS:
+//  * a top-k is an exact selection by value bins (wave min/max, 256 equal-width
+//    bins, the bin holding the k-th best refined at most three times, the rest
+//    ranked exactly), then compaction and a register bitonic sort of the k
+//    survivors;
+//  * the candidates' fp32-rounded sums never decrease with their exact sums, so
+//    they are binned on those and only the members of the last bin are ordered by
+//    exact fp64 sum and id;
+//  * all cross-lane traffic (reductions, scans, sorting exchanges) moves through
+//    DPP and the permlane swaps, never through the LDS crossbar.
 #include "sdm_internal.h"
 
 namespace sdm {
@@ -76,31 +80,92 @@ __device__ __forceinline__ float unord32(uint32_t k) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
-__device__ __forceinline__ int wave_incl_scan(int x) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  return x;
+// Cross-lane moves without the LDS crossbar: DPP within rows of 16 lanes
+// (quad_perm, row shifts under bank masks, row rotation, row broadcasts) and the
+// gfx950 permlane swaps across rows and halves of the wavefront.
+// dpp<CTRL>(old, src): lane i gets src of the lane CTRL names, or `old` where that
+// lane is outside the row or masked off.
+template <int CTRL, int RM = 0xf, int BM = 0xf>
+__device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t src) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)src, CTRL, RM, BM, false);
 }
 
+// x of lane (this lane ^ M)
+template <int M>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t x) {
+  if constexpr (M == 1) {
+    return dpp<0xB1>(x, x);  // quad_perm(1,0,3,2)
+  } else if constexpr (M == 2) {
+    return dpp<0x4E>(x, x);  // quad_perm(2,3,0,1)
+  } else if constexpr (M == 4) {
+    const uint32_t t = dpp<0x104, 0xf, 0x5>(x, x);  // banks 0,2: row_shl 4
+    return dpp<0x114, 0xf, 0xA>(t, x);              // banks 1,3: row_shr 4
+  } else if constexpr (M == 8) {
+    return dpp<0x128>(x, x);  // row_ror 8
+  } else if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return ((threadIdx.x >> 4) & 1) ? r[0] : r[1];
+  } else {
+    static_assert(M == 32, "xor distance");
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return ((threadIdx.x >> 5) & 1) ? r[0] : r[1];
+  }
+}
+// the same with a distance that is a constant after unrolling
+__device__ __forceinline__ uint32_t xor_lane(uint32_t x, int m) {
+  switch (m) {
+    case 1: return xor_lane<1>(x);
+    case 2: return xor_lane<2>(x);
+    case 4: return xor_lane<4>(x);
+    case 8: return xor_lane<8>(x);
+    case 16: return xor_lane<16>(x);
+    default: return xor_lane<32>(x);
+  }
+}
+__device__ __forceinline__ float xor_lane(float x, int m) {
+  return __uint_as_float(xor_lane(__float_as_uint(x), m));
+}
+__device__ __forceinline__ uint64_t xor_lane(uint64_t x, int m) {
+  return ((uint64_t)xor_lane((uint32_t)(x >> 32), m) << 32) | xor_lane((uint32_t)x, m);
+}
+__device__ __forceinline__ double xor_lane(double x, int m) {
+  return __longlong_as_double((long long)xor_lane((uint64_t)__double_as_longlong(x), m));
+}
+
+// Inclusive prefix over the wavefront: Hillis-Steele within rows (row_shr 1, 2, 4,
+// 8), then the last lane of row 0 / 2 into rows 1 / 3 (row_bcast 15) and lane 31
+// into rows 2, 3 (row_bcast 31).  `id` is the identity of `op`.
+template <class F>
+__device__ __forceinline__ uint32_t wave_scan(uint32_t v, uint32_t id, F op) {
+  v = op(v, dpp<0x111>(id, v));
+  v = op(v, dpp<0x112>(id, v));
+  v = op(v, dpp<0x114>(id, v));
+  v = op(v, dpp<0x118>(id, v));
+  v = op(v, dpp<0x142, 0xa>(id, v));
+  v = op(v, dpp<0x143, 0xc>(id, v));
+  return v;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  return (int)wave_scan((uint32_t)x, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+}
+
+// wave-uniform results (read from lane 63)
 __device__ __forceinline__ int wave_sum(int x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+  return __builtin_amdgcn_readlane(wave_incl_scan(x), 63);
 }
 
 __device__ __forceinline__ float wave_min(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fminf(x, __shfl_xor(x, o));
-  return x;
+  const uint32_t r = wave_scan(__float_as_uint(x), 0x7f800000u, [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fminf(__uint_as_float(a), __uint_as_float(b)));
+  });
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)r, 63));
 }
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
+  const uint32_t r = wave_scan(__float_as_uint(x), 0xff800000u, [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+  });
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)r, 63));
 }
 
 // fp64 -> uint64 whose unsigned order is the double order (-0 folded onto +0).
@@ -177,8 +242,8 @@ __device__ uint32_t select_exact(const float (&fv)[KPL], const uint64_t (&key)[K
       }
       rest = need - acc;
     }
-    bstar = __shfl(bstar, L);
-    need = __shfl(rest, L);
+    bstar = __builtin_amdgcn_readlane(bstar, L);
+    need = __builtin_amdgcn_readlane(rest, L);
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < KPL; ++q) {
@@ -238,9 +303,7 @@ __device__ void bitonic_desc(uint64_t (&v)[EPL]) {
 #pragma unroll
         for (int r = 0; r < EPL; ++r) {
           const int e = lane + 64 * r;
-          const uint32_t olo = (uint32_t)__shfl_xor((int)(uint32_t)v[r], stride);
-          const uint32_t ohi = (uint32_t)__shfl_xor((int)(uint32_t)(v[r] >> 32), stride);
-          const uint64_t o = ((uint64_t)ohi << 32) | olo;
+          const uint64_t o = xor_lane(v[r], stride);
           const bool desc = (e & size) == 0;
           const bool lower = (e & stride) == 0;
           // in a descending run the lower position keeps the larger key
@@ -355,7 +418,7 @@ __device__ void combine(int n, int k, int count, const float* av, const uint32_t
   double smax = -__builtin_inf();
   for (int e = lane; e < count; e += 64) smax = fmax(smax, csc[e]);
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) smax = fmax(smax, __shfl_xor(smax, o));
+  for (int o = 32; o > 0; o >>= 1) smax = fmax(smax, xor_lane(smax, o));
   float wsum = 0.0f;
   if (ne == 1) {
     uint64_t v[1] = {lane < count ? (((uint64_t)(0xffffffffu - cid[lane]) << 32) | (uint32_t)lane)
@@ -365,7 +428,7 @@ __device__ void combine(int n, int k, int count, const float* av, const uint32_t
     if (lane < count) w = expf((float)(csc[(uint32_t)v[0]] - smax));
     wsum = w;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) wsum += __shfl_xor(wsum, o);
+    for (int o = 32; o > 0; o >>= 1) wsum += xor_lane(wsum, o);
     if (lane < count) {
       oi[lane] = (int32_t)(0xffffffffu - (uint32_t)(v[0] >> 32));
       ow[lane] = w / wsum;
@@ -386,7 +449,7 @@ __device__ void combine(int n, int k, int count, const float* av, const uint32_t
     }
     wsum = w[0] + w[1];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) wsum += __shfl_xor(wsum, o);
+    for (int o = 32; o > 0; o >>= 1) wsum += xor_lane(wsum, o);
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int e = lane + 64 * r;
