@@ -252,11 +252,13 @@ __device__ uint32_t select_exact(const float (&fv)[KPL], const uint64_t (&key)[K
       cand &= ~((uint32_t)(!(c && bin[q] == bstar)) << q);
     }
   }
-  // exact ranking of the remaining candidates
+  // Exact ranking of the remaining candidates: compacted into LDS, each ranked by
+  // one lane against all of them, the verdicts handed back through LDS.
   const int cl = __popc(cand);
   const int nc = wave_sum(cl);
   if (nc == need) return sel | cand;
-  int pos = wave_incl_scan(cl) - cl;
+  const int p0 = wave_incl_scan(cl) - cl;
+  int pos = p0;
 #pragma unroll
   for (int q = 0; q < KPL; ++q)
     if ((cand >> q) & 1u) {
@@ -265,21 +267,36 @@ __device__ uint32_t select_exact(const float (&fv)[KPL], const uint64_t (&key)[K
       ++pos;
     }
   __syncthreads();
+  uint32_t verdict = 0;  // bit c: compacted entry 64 c + lane is among the `need` best
+  for (int c0 = 0, c = 0; c0 < nc; c0 += 64, ++c) {
+    const int e = c0 + lane;
+    if (e < nc) {
+      const uint64_t ke = tk[e];
+      const uint32_t ie = ti[e];
+      int rank = 0;
+      for (int u = 0; u < nc; ++u) rank += better(tk[u], ti[u], ke, ie) ? 1 : 0;
+      verdict |= (uint32_t)(rank < need) << c;
+    }
+  }
+  __syncthreads();
+  for (int c0 = 0, c = 0; c0 < nc; c0 += 64, ++c)
+    if (c0 + lane < nc) ti[c0 + lane] = (verdict >> c) & 1u;
+  __syncthreads();
+  pos = p0;
 #pragma unroll
   for (int q = 0; q < KPL; ++q)
     if ((cand >> q) & 1u) {
-      int rank = 0;
-      for (int u = 0; u < nc; ++u) rank += better(tk[u], ti[u], key[q], id[q]) ? 1 : 0;
-      if (rank < need) sel |= 1u << q;
+      if (ti[pos]) sel |= 1u << q;
+      ++pos;
     }
   __syncthreads();
   return sel;
 }
 
-// Bitonic sort of NE = 64*EPL 64-bit keys (element e = lane + 64*r in v[r]) so that
-// larger keys come first.
-template <int EPL>
-__device__ void bitonic_desc(uint64_t (&v)[EPL]) {
+// Bitonic sort of NE = 64*EPL unsigned keys (element e = lane + 64*r in v[r]) so
+// that larger keys come first.
+template <int EPL, class K>
+__device__ void bitonic_desc(K (&v)[EPL]) {
   const int lane = lane_id();
   constexpr int NE = 64 * EPL;
 #pragma unroll
@@ -293,7 +310,7 @@ __device__ void bitonic_desc(uint64_t (&v)[EPL]) {
           const int pr = r ^ (stride >> 6);
           if (pr > r) {
             const bool desc = (e & size) == 0;
-            const uint64_t lo = v[r], hi = v[pr];
+            const K lo = v[r], hi = v[pr];
             const bool sw = desc ? (hi > lo) : (lo > hi);
             v[r] = sw ? hi : lo;
             v[pr] = sw ? lo : hi;
@@ -303,7 +320,7 @@ __device__ void bitonic_desc(uint64_t (&v)[EPL]) {
 #pragma unroll
         for (int r = 0; r < EPL; ++r) {
           const int e = lane + 64 * r;
-          const uint64_t o = xor_lane(v[r], stride);
+          const K o = xor_lane(v[r], stride);
           const bool desc = (e & size) == 0;
           const bool lower = (e & stride) == 0;
           // in a descending run the lower position keeps the larger key
@@ -413,39 +430,41 @@ __device__ void combine(int n, int k, int count, const float* av, const uint32_t
       ++pos;
     }
   __syncthreads();
-  // sort survivors by id ascending: key = ~id (larger first), payload = position
+  // sort survivors by id ascending (a descending sort of complemented ids)
+  static_assert(SDM_MAX_HALF * SDM_MAX_HALF <= (1 << 20) && SDM_MAX_COUNT <= 128,
+                "ids and positions must fit the 32-bit sort key");
   const int ne = count <= 64 ? 1 : 2;
   double smax = -__builtin_inf();
   for (int e = lane; e < count; e += 64) smax = fmax(smax, csc[e]);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) smax = fmax(smax, xor_lane(smax, o));
   float wsum = 0.0f;
+  // key: (id descending-complemented, position), +1 so that padding (0) sorts last;
+  // ids < 2^20 and positions < 128
+  auto sort_key = [&](int e) -> uint32_t {
+    return e < count ? ((((0xFFFFFu - cid[e]) << 7) | (uint32_t)e) + 1u) : 0u;
+  };
   if (ne == 1) {
-    uint64_t v[1] = {lane < count ? (((uint64_t)(0xffffffffu - cid[lane]) << 32) | (uint32_t)lane)
-                                  : 0ull};
+    uint32_t v[1] = {sort_key(lane)};
     bitonic_desc<1>(v);
+    const uint32_t kk = v[0] - 1u;
     float w = 0.0f;
-    if (lane < count) w = expf((float)(csc[(uint32_t)v[0]] - smax));
+    if (lane < count) w = expf((float)(csc[kk & 127u] - smax));
     wsum = w;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) wsum += xor_lane(wsum, o);
     if (lane < count) {
-      oi[lane] = (int32_t)(0xffffffffu - (uint32_t)(v[0] >> 32));
+      oi[lane] = (int32_t)(0xFFFFFu - (kk >> 7));
       ow[lane] = w / wsum;
     }
   } else {
-    uint64_t v[2];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int e = lane + 64 * r;
-      v[r] = e < count ? (((uint64_t)(0xffffffffu - cid[e]) << 32) | (uint32_t)e) : 0ull;
-    }
+    uint32_t v[2] = {sort_key(lane), sort_key(lane + 64)};
     bitonic_desc<2>(v);
     float w[2];
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int e = lane + 64 * r;
-      w[r] = e < count ? expf((float)(csc[(uint32_t)v[r]] - smax)) : 0.0f;
+      w[r] = e < count ? expf((float)(csc[(v[r] - 1u) & 127u] - smax)) : 0.0f;
     }
     wsum = w[0] + w[1];
 #pragma unroll
@@ -454,7 +473,7 @@ __device__ void combine(int n, int k, int count, const float* av, const uint32_t
     for (int r = 0; r < 2; ++r) {
       const int e = lane + 64 * r;
       if (e < count) {
-        oi[e] = (int32_t)(0xffffffffu - (uint32_t)(v[r] >> 32));
+        oi[e] = (int32_t)(0xFFFFFu - ((v[r] - 1u) >> 7));
         ow[e] = w[r] / wsum;
       }
     }
