@@ -30,6 +30,10 @@ Readings taken where the pages are silent (each listed in the design notes):
     activation (sigmoid unless stated) multiplies element-wise;
   * the output projection W_o is not part of this path.
 
+Variant (not the pages' printed rule): scan_gdn uses Gated DeltaNet's
+key-weighted error term on the write set; it is pinned against a dense
+matrix-form gated delta recurrence with every slot selected.
+
 Pins: every function here is checked by tests/test_oracle_pins.py against
 hand-worked fixtures (tests/golden/), closed forms, exact rational arithmetic
 and brute force.  No function of this module is "parity unpinned".
@@ -195,6 +199,40 @@ def scan(state0, idx_w, wt_w, idx_r, wt_r, v, alpha, beta):
 
 
 # ----------------------------------------------------------------------------
+# Variant: the gated delta rule of Gated DeltaNet restricted to the write set.
+# [analysis] section "与 GDN 的关系" and [163] section 二 state that with every
+# slot selected (W = R = N = d_qk) and a dense key the layer becomes Gated
+# DeltaNet's update.  GDN's rule S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T)
+# + beta_t v_t k_t^T is not printed on the pages; written per key row i it is
+#   Mtilde = alpha_t * M_{t-1}            (forget gate, on the write set)
+#   M_t[i] = Mtilde[i] + beta_t k^(i) (v_t - sum_j k^(j) Mtilde[j])
+# i.e. the error term subtracts the key-weighted prediction of the whole write
+# set instead of the slot's own value.  Reads are unchanged.
+# ----------------------------------------------------------------------------
+def scan_gdn(state0, idx_w, wt_w, idx_r, wt_r, v, alpha, beta):
+    """Like scan(), with the key-weighted error term above."""
+    M = np.array(state0, dtype=F64, copy=True)
+    idx_w = np.asarray(idx_w)
+    idx_r = np.asarray(idx_r)
+    wt_w = np.asarray(wt_w, F64)
+    wt_r = np.asarray(wt_r, F64)
+    v = np.asarray(v, F64)
+    alpha = np.asarray(alpha, F64)
+    beta = np.asarray(beta, F64)
+    T = idx_w.shape[0]
+    y = np.zeros((T, M.shape[1]), F64)
+    for t in range(T):
+        rows = idx_w[t]
+        assert np.unique(rows).size == rows.size, "write slots of one token must be distinct"
+        k = wt_w[t]
+        m_tilde = alpha[t] * M[rows]                                   # forget gate
+        pred = k @ m_tilde                                             # key-weighted prediction
+        M[rows] = m_tilde + (beta[t] * k)[:, None] * (v[t] - pred)[None, :]
+        y[t] = wt_r[t] @ M[idx_r[t]]                                   # sparse read
+    return y, M
+
+
+# ----------------------------------------------------------------------------
 # Step 4 (without the head-mixing projection): [rainbus] step 4 and
 # [analysis] "步骤 4": RMS-Norm of the read vector, then element-wise gating.
 # ----------------------------------------------------------------------------
@@ -241,13 +279,16 @@ def select_from_scores(scores, n, W, R):
     return {k: np.array(v).reshape(lead + shp[k]) for k, v in res.items()}
 
 
-def forward_walk(state0, sel, gamma_h, eps):
+def forward_walk(state0, sel, gamma_h, eps, rule: str = "slot"):
     """Scan + norm/gate for one (batch, head) walk given its pass-(a) products.
 
     sel holds [T, *] arrays for that walk: idx_w, wt_w, idx_r, wt_r, v, g,
-    alpha, beta.  Returns (out [T, d_v], y_raw [T, d_v], final state).
+    alpha, beta.  rule "slot" is the pages' per-slot error term (scan), "gdn"
+    the key-weighted one (scan_gdn).  Returns (out [T, d_v], y_raw [T, d_v],
+    final state).
     """
-    y, M = scan(state0, sel["idx_w"], sel["wt_w"], sel["idx_r"], sel["wt_r"],
+    walk = {"slot": scan, "gdn": scan_gdn}[rule]
+    y, M = walk(state0, sel["idx_w"], sel["wt_w"], sel["idx_r"], sel["wt_r"],
                 sel["v"], sel["alpha"], sel["beta"])
     return rms_norm_gate(y, gamma_h, sel["g"], eps), y, M
 
