@@ -85,6 +85,15 @@ extern "C" {
    the call's stream; sdm_timing_read returns the durations.  Results are the same
    with and without it. */
 #define SDM_FLAG_TIMING 8
+/* variant flag (sdm_dims.flags): the write's error term is the key-weighted
+   prediction of the whole write set, M[i] <- aM[i] + b k_i (v - sum_j k_j aM[j]),
+   i.e. Gated DeltaNet's delta rule restricted to the selected slots (the form the
+   pages say the layer reduces to when every slot is selected with a dense key:
+   ai-paper-analysis.pages.dev, section "与 GDN 的关系"; m.163.com article on
+   arXiv 2607.07386, section 二).  It needs every row of a token's write set before
+   any is written, so it runs the direct schedule; combined with
+   SDM_FLAG_SCAN_STREAM or SDM_FLAG_SCAN_TWO_PHASE it is SDM_ERR_UNSUPPORTED. */
+#define SDM_FLAG_DELTA_GDN 16
 
 /* Limits of this build (SDM_ERR_UNSUPPORTED beyond them). */
 #define SDM_MAX_COUNT 128   /* W and R */

@@ -9,6 +9,10 @@
 //   out:   y_t / sqrt(mean(y_t^2) + eps) * gamma_h * gate_t
 // Unselected slots are never touched.  The slot ids of every token are known
 // before the scan starts (selection pass), so the kernel only moves rows.
+// Variant (SDM_FLAG_DELTA_GDN): the error term is the key-weighted prediction of
+// the write set, M[i] <- alpha M[i] + beta k_i (v - alpha sum_j k_j M[j]) -- Gated
+// DeltaNet's rule on the selected slots ("与 GDN 的关系" section of
+// ai-paper-analysis.pages.dev).
 #include "sdm_internal.h"
 
 namespace sdm {
@@ -21,7 +25,7 @@ __device__ __forceinline__ float4 f4(float a) { return make_float4(a, a, a, a); 
 // writes and R reads of a token.  Barriers order the write phase, the read phase
 // and the next token's writes (all accesses stay inside one workgroup, whose
 // waves share the CU's vector L1).
-template <int DV>
+template <int DV, bool GDN>
 __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   constexpr int LPR = DV / 4;
   constexpr int G = 256 / LPR;
@@ -44,6 +48,41 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     const float4 vv = reinterpret_cast<const float4*>(a.v + tok * DV)[li];
     const int32_t* iw = a.idx_w + tok * a.W;
     const float* ww = a.wt_w + tok * a.W;
+    if constexpr (GDN) {
+      // key-weighted prediction of the write set from the rows before this
+      // token's writes; row k is read here and written below by the same thread
+      float4 part = f4(0.0f);
+      for (int k = grp; k < a.W; k += G) {
+        const float w = ww[k];
+        const float4 m = reinterpret_cast<const float4*>(M + (int64_t)iw[k] * DV)[li];
+        part.x = fmaf(w, m.x, part.x);
+        part.y = fmaf(w, m.y, part.y);
+        part.z = fmaf(w, m.z, part.z);
+        part.w = fmaf(w, m.w, part.w);
+      }
+      red[grp][li] = part;
+      __syncthreads();
+      float4 pred = red[0][li];
+      for (int g = 1; g < G; ++g) {
+        const float4 o = red[g][li];
+        pred.x += o.x;
+        pred.y += o.y;
+        pred.z += o.z;
+        pred.w += o.w;
+      }
+      const float4 err = make_float4(vv.x - al * pred.x, vv.y - al * pred.y, vv.z - al * pred.z,
+                                     vv.w - al * pred.w);
+      for (int k = grp; k < a.W; k += G) {
+        const float c = be * ww[k];
+        float4* p = reinterpret_cast<float4*>(M + (int64_t)iw[k] * DV) + li;
+        float4 m = *p;
+        m.x = fmaf(c, err.x, al * m.x);
+        m.y = fmaf(c, err.y, al * m.y);
+        m.z = fmaf(c, err.z, al * m.z);
+        m.w = fmaf(c, err.w, al * m.w);
+        *p = m;
+      }
+    } else
     for (int k = grp; k < a.W; k += G) {
       const int64_t row = iw[k];
       const float c = be * ww[k];
@@ -95,10 +134,18 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   }
 }
 
+template <int DV>
+void launch_direct(bool gdn, dim3 grid, hipStream_t s, const ScanArgs& a) {
+  if (gdn)
+    hipLaunchKernelGGL((scan_kernel<DV, true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((scan_kernel<DV, false>), grid, dim3(256), 0, s, a);
+}
+
 }  // namespace
 
 bool scan_uses_stream(const sdm_dims& d) {
-  if (d.flags & SDM_FLAG_SCAN_DIRECT) return false;
+  if (d.flags & (SDM_FLAG_SCAN_DIRECT | SDM_FLAG_DELTA_GDN)) return false;
   if (d.flags & (SDM_FLAG_SCAN_STREAM | SDM_FLAG_SCAN_TWO_PHASE)) return true;
   return d.T >= 16;
 }
@@ -112,12 +159,13 @@ hipError_t launch_scan(const sdm_dims& d, const ScanArgs& a, void* ws, size_t, h
   if (scan_uses_stream(d)) return launch_stream_scan(a, plan_stream(d, a.N), ws, s);
   const dim3 grid((unsigned)(a.B * a.H));
   KernelTimer kt("scan_direct", s);
+  const bool gdn = (d.flags & SDM_FLAG_DELTA_GDN) != 0;
   switch (a.d_v) {
-    case 16: hipLaunchKernelGGL(scan_kernel<16>, grid, dim3(256), 0, s, a); break;
-    case 32: hipLaunchKernelGGL(scan_kernel<32>, grid, dim3(256), 0, s, a); break;
-    case 64: hipLaunchKernelGGL(scan_kernel<64>, grid, dim3(256), 0, s, a); break;
-    case 128: hipLaunchKernelGGL(scan_kernel<128>, grid, dim3(256), 0, s, a); break;
-    case 256: hipLaunchKernelGGL(scan_kernel<256>, grid, dim3(256), 0, s, a); break;
+    case 16: launch_direct<16>(gdn, grid, s, a); break;
+    case 32: launch_direct<32>(gdn, grid, s, a); break;
+    case 64: launch_direct<64>(gdn, grid, s, a); break;
+    case 128: launch_direct<128>(gdn, grid, s, a); break;
+    case 256: launch_direct<256>(gdn, grid, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -26,8 +26,11 @@ struct Derived {
 int32_t check_dims(const sdm_dims* d, Derived* out) {
   if (!d) return SDM_ERR_NULL;
   const int32_t sched = SDM_FLAG_SCAN_DIRECT | SDM_FLAG_SCAN_STREAM | SDM_FLAG_SCAN_TWO_PHASE;
-  if (d->flags & ~(sched | SDM_FLAG_TIMING)) return SDM_ERR_UNSUPPORTED;
+  if (d->flags & ~(sched | SDM_FLAG_TIMING | SDM_FLAG_DELTA_GDN)) return SDM_ERR_UNSUPPORTED;
   if (__builtin_popcount((unsigned)(d->flags & sched)) > 1) return SDM_ERR_SHAPE;  // one schedule
+  if ((d->flags & SDM_FLAG_DELTA_GDN) &&
+      (d->flags & (SDM_FLAG_SCAN_STREAM | SDM_FLAG_SCAN_TWO_PHASE)))
+    return SDM_ERR_UNSUPPORTED;  // the variant runs the direct schedule only
   if (d->in_dtype != SDM_DTYPE_F32 && d->in_dtype != SDM_DTYPE_BF16) return SDM_ERR_DTYPE;
   if (d->gate_act < SDM_GATE_NONE || d->gate_act > SDM_GATE_SILU) return SDM_ERR_DTYPE;
   if (d->B < 0 || d->T < 0 || d->d_model < 1 || d->H < 1 || d->n < 1 || d->W < 1 || d->R < 1 ||

@@ -106,13 +106,14 @@ def random_products(rng, B, T, H, n, W, R, d_v, mode="random"):
                 beta=rng.uniform(0.0, 1.0, shp).astype(np.float32))
 
 
-def oracle_walks(prod_h, m0_h, gamma, eps, walks):
+def oracle_walks(prod_h, m0_h, gamma, eps, walks, rule="slot"):
     """Oracle scan + norm for the listed (b, h) walks from given products."""
     res = {}
     for b, h in walks:
         sel = {k: prod_h[k][b, :, h] for k in ("idx_w", "wt_w", "idx_r", "wt_r", "v", "gate",
                                                 "alpha", "beta")}
         sel["g"] = sel.pop("gate")
-        out, y, M = O.forward_walk(m0_h[b, h] if m0_h.ndim == 4 else m0_h[h], sel, gamma[h], eps)
+        out, y, M = O.forward_walk(m0_h[b, h] if m0_h.ndim == 4 else m0_h[h], sel, gamma[h], eps,
+                                   rule)
         res[(b, h)] = (out, y, M)
     return res

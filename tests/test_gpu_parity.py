@@ -124,6 +124,7 @@ SCHEDULES = {"direct": _lib.SDM_FLAG_SCAN_DIRECT, "stream": _lib.SDM_FLAG_SCAN_S
     (3, 33, 2, 20, 64, 64, 128, "repeat"),
     (1, 30, 1, 16, 128, 128, 256, "random"),
     (2, 17, 1, 4, 16, 16, 16, "random"),       # every slot written by every token
+    (2, 300, 2, 16, 32, 128, 64, "random"),    # the pages' W = 32 / R = 128 ablation shape
 ])
 def test_stage_c_scan(B, T, H, n, W, R, d_v, mode, schedule):
     rng = np.random.default_rng(B * 100 + T + W)
@@ -143,6 +144,38 @@ def test_stage_c_scan(B, T, H, n, W, R, d_v, mode, schedule):
         assert_close(st[b, h], o_M, f"state walk {(b, h)}")
         untouched = np.setdiff1d(np.arange(N), prod["idx_w"][b, :, h].ravel())
         assert np.array_equal(st[b, h][untouched], m0[b, h][untouched]), "unwritten rows changed"
+
+
+@pytest.mark.parametrize("B,T,H,n,W,R,d_v,mode", [
+    (2, 64, 2, 8, 64, 64, 32, "random"),       # every slot selected (the GDN-reduction shape)
+    (1, 300, 2, 16, 32, 128, 64, "random"),    # W = 32 / R = 128
+    (2, 50, 1, 12, 16, 16, 256, "repeat"),
+    (1, 40, 1, 32, 8, 8, 16, "same"),
+])
+def test_stage_c_gdn_variant(B, T, H, n, W, R, d_v, mode):
+    """SDM_FLAG_DELTA_GDN: key-weighted error term, against the oracle's scan_gdn."""
+    rng = np.random.default_rng(B * 1000 + T + W + R)
+    N = n * n
+    prod = random_products(rng, B, T, H, n, W, R, d_v, mode)
+    m0 = (rng.standard_normal((B, H, N, d_v)) * 0.02).astype(np.float32)
+    gamma = rng.uniform(0.5, 1.5, (H, d_v)).astype(np.float32)
+    d = _dims(B=B, T=T, H=H, n=n, W=W, R=R, d_v=d_v, flags=_lib.SDM_FLAG_DELTA_GDN)
+    state = to_dev(m0)
+    out, y = ops.scan(d, _prod_dev(prod), to_dev(gamma), state, with_y_raw=True)
+    torch.cuda.synchronize()
+    st, oh, yh = host(state), host(out), host(y)
+    walks = [(b, h) for b in range(B) for h in range(H)]
+    ref = oracle_walks(prod, m0, gamma, 1e-6, walks, rule="gdn")
+    slot = oracle_walks(prod, m0, gamma, 1e-6, walks[:1], rule="slot")
+    for (b, h), (o_out, o_y, o_M) in ref.items():
+        assert_close(yh[b, :, h], o_y, f"y_raw walk {(b, h)}")
+        assert_close(oh[b, :, h], o_out, f"out walk {(b, h)}")
+        assert_close(st[b, h], o_M, f"state walk {(b, h)}")
+        untouched = np.setdiff1d(np.arange(N), prod["idx_w"][b, :, h].ravel())
+        assert np.array_equal(st[b, h][untouched], m0[b, h][untouched]), "unwritten rows changed"
+    if W > 1:  # the two rules really differ on these inputs
+        b, h = walks[0]
+        assert np.max(np.abs(slot[(b, h)][2] - ref[(b, h)][2])) > 1e-6
 
 
 @pytest.mark.parametrize("schedule", ["direct", "stream", "two_phase"])
