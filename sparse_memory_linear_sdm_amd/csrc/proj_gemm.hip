@@ -87,6 +87,7 @@ __device__ __forceinline__ void epilogue_store(const ProjDst& d, int64_t m, int 
 // goes through LDS so that every store writes a 16-byte row segment.
 // ---------------------------------------------------------------------------
 constexpr int BM = 256, BN = 256, BK = 64, LDK = BK + 8, NTH = 512, GROUP_M = 4;
+constexpr int CPR = BK / 8;                  // 16-byte chunks per tile row
 constexpr int A_CHUNKS = BM * BK / 8 / NTH;  // 16-byte chunks per thread per K-tile
 constexpr int B_CHUNKS = BN * BK / 8 / NTH;
 constexpr int NXCD = 8;
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(NTH) void proj_gemm_bf16_kernel(
 #pragma unroll
     for (int it = 0; it < A_CHUNKS; ++it) {
       const int q = tid + it * NTH;
-      const int r = q >> 3, kc = (q & 7) * 8;
+      const int r = q / CPR, kc = (q % CPR) * 8;
       const int64_t gm = tile_m + r;
       ra[it] = (gm < M && k0 + kc < K)
                    ? *reinterpret_cast<const uint4*>(X + (row0 + gm) * (int64_t)K + k0 + kc)
@@ -139,7 +140,7 @@ __global__ __launch_bounds__(NTH) void proj_gemm_bf16_kernel(
 #pragma unroll
     for (int it = 0; it < B_CHUNKS; ++it) {
       const int q = tid + it * NTH;
-      const int r = q >> 3, kc = (q & 7) * 8;
+      const int r = q / CPR, kc = (q % CPR) * 8;
       const int gn = tile_n + r;
       rb[it] = (gn < Ncol && k0 + kc < K)
                    ? *reinterpret_cast<const uint4*>(Wp + (int64_t)gn * K + k0 + kc)
@@ -150,12 +151,12 @@ __global__ __launch_bounds__(NTH) void proj_gemm_bf16_kernel(
 #pragma unroll
     for (int it = 0; it < A_CHUNKS; ++it) {
       const int q = tid + it * NTH;
-      *reinterpret_cast<uint4*>(&As[buf][(q >> 3) * LDK + (q & 7) * 8]) = ra[it];
+      *reinterpret_cast<uint4*>(&As[buf][(q / CPR) * LDK + (q % CPR) * 8]) = ra[it];
     }
 #pragma unroll
     for (int it = 0; it < B_CHUNKS; ++it) {
       const int q = tid + it * NTH;
-      *reinterpret_cast<uint4*>(&Bs[buf][(q >> 3) * LDK + (q & 7) * 8]) = rb[it];
+      *reinterpret_cast<uint4*>(&Bs[buf][(q / CPR) * LDK + (q % CPR) * 8]) = rb[it];
     }
   };
 
