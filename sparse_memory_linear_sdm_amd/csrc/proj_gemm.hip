@@ -86,17 +86,39 @@ __device__ __forceinline__ void epilogue_store(const ProjDst& d, int64_t m, int 
 // blocks resident on one XCD share A and B slices through its L2.  The epilogue
 // goes through LDS so that every store writes a 16-byte row segment.
 // ---------------------------------------------------------------------------
-constexpr int BM = 256, BN = 256, BK = 64, LDK = BK + 8, NTH = 512, GROUP_M = 4;
-constexpr int CPR = BK / 8;                  // 16-byte chunks per tile row
-constexpr int A_CHUNKS = BM * BK / 8 / NTH;  // 16-byte chunks per thread per K-tile
-constexpr int B_CHUNKS = BN * BK / 8 / NTH;
+// Tile shape: WM x WN waves, each owning FM x FN MFMA 32x32 blocks.
+template <int WM_, int WN_, int FM_, int FN_>
+struct Tile {
+  static constexpr int WM = WM_, WN = WN_, FM = FM_, FN = FN_;
+  static constexpr int BM = WM * FM * 32, BN = WN * FN * 32, BK = 64, LDK = BK + 8;
+  static constexpr int NTH = WM * WN * 64;
+  static constexpr int CPR = BK / 8;                  // 16-byte chunks per tile row
+  static constexpr int A_CHUNKS = BM * BK / 8 / NTH;  // 16-byte chunks per thread per K-tile
+  static constexpr int B_CHUNKS = BN * BK / 8 / NTH;
+  static constexpr int A_BYTES = BM * LDK * 2, B_BYTES = BN * LDK * 2;
+  static constexpr int LDS = 2 * (A_BYTES + B_BYTES);  // double-buffered A and B
+  static_assert(A_CHUNKS * NTH * 8 == BM * BK && B_CHUNKS * NTH * 8 == BN * BK, "even split");
+  static_assert(LDS >= WM * WN * 32 * 36 * 4, "epilogue patches fit in the tile buffers");
+};
+using BigTile = Tile<2, 4, 4, 2>;    // 256 x 256, 8 waves of 128 x 64
+using SmallTile = Tile<2, 2, 1, 1>;  // 64 x 64, 4 waves of 32 x 32 (few rows: decode)
+constexpr int GROUP_M = 4;
 constexpr int NXCD = 8;
 
-__global__ __launch_bounds__(NTH) void proj_gemm_bf16_kernel(
+template <class TL>
+__global__ __launch_bounds__(TL::NTH) void proj_gemm_bf16_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wp, int64_t row0, int64_t M,
     int Ncol, int K, ProjDst dst) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDK];
+  constexpr int BM = TL::BM, BN = TL::BN, BK = TL::BK, LDK = TL::LDK, NTH = TL::NTH;
+  constexpr int CPR = TL::CPR, A_CHUNKS = TL::A_CHUNKS, B_CHUNKS = TL::B_CHUNKS;
+  constexpr int FM = TL::FM, FN = TL::FN;
+  __shared__ __attribute__((aligned(16))) char smem[TL::LDS];
+  auto As = [&](int buf) {
+    return reinterpret_cast<uint16_t*>(smem + buf * (TL::A_BYTES + TL::B_BYTES));
+  };
+  auto Bs = [&](int buf) {
+    return reinterpret_cast<uint16_t*>(smem + buf * (TL::A_BYTES + TL::B_BYTES) + TL::A_BYTES);
+  };
 
   // XCD-aware grouped tile order: consecutive workgroups go to different XCDs,
   // so give each XCD a contiguous range of tiles, walked GROUP_M rows at a time.
@@ -116,13 +138,13 @@ __global__ __launch_bounds__(NTH) void proj_gemm_bf16_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave / TL::WN, wn = wave % TL::WN;
 
-  floatx16 acc[4][2];
+  floatx16 acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
@@ -151,12 +173,12 @@ __global__ __launch_bounds__(NTH) void proj_gemm_bf16_kernel(
 #pragma unroll
     for (int it = 0; it < A_CHUNKS; ++it) {
       const int q = tid + it * NTH;
-      *reinterpret_cast<uint4*>(&As[buf][(q / CPR) * LDK + (q % CPR) * 8]) = ra[it];
+      *reinterpret_cast<uint4*>(&As(buf)[(q / CPR) * LDK + (q % CPR) * 8]) = ra[it];
     }
 #pragma unroll
     for (int it = 0; it < B_CHUNKS; ++it) {
       const int q = tid + it * NTH;
-      *reinterpret_cast<uint4*>(&Bs[buf][(q / CPR) * LDK + (q % CPR) * 8]) = rb[it];
+      *reinterpret_cast<uint4*>(&Bs(buf)[(q / CPR) * LDK + (q % CPR) * 8]) = rb[it];
     }
   };
 
@@ -170,23 +192,23 @@ __global__ __launch_bounds__(NTH) void proj_gemm_bf16_kernel(
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 16) {
       const int kq = kk + (lane >> 5) * 8;
-      bf16x8 af[4], bfr[2];
+      bf16x8 af[FM], bfr[FN];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < FM; ++i) {
         const uint4 u = *reinterpret_cast<const uint4*>(
-            &As[cur][(wm * 128 + i * 32 + (lane & 31)) * LDK + kq]);
+            &As(cur)[(wm * FM * 32 + i * 32 + (lane & 31)) * LDK + kq]);
         __builtin_memcpy(&af[i], &u, 16);
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < FN; ++j) {
         const uint4 u = *reinterpret_cast<const uint4*>(
-            &Bs[cur][(wn * 64 + j * 32 + (lane & 31)) * LDK + kq]);
+            &Bs(cur)[(wn * FN * 32 + j * 32 + (lane & 31)) * LDK + kq]);
         __builtin_memcpy(&bfr[j], &u, 16);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
     if (more) stash(cur ^ 1);
@@ -200,12 +222,12 @@ __global__ __launch_bounds__(NTH) void proj_gemm_bf16_kernel(
   // 4-column row segments: one 16-byte store where the 4 columns are plain copies
   // into consecutive addresses, else one routed store per column.  The A/B buffers
   // are free after the last barrier.
-  float* patch = reinterpret_cast<float*>(&As[0][0]) + wave * (32 * 36);
+  float* patch = reinterpret_cast<float*>(smem) + wave * (32 * 36);
   const int sr = lane >> 3;        // row within an 8-row group
   const int sc = (lane & 7) * 4;   // first of this lane's 4 columns
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int cb = tile_n + wn * 64 + j * 32;  // first column of the block
+  for (int j = 0; j < FN; ++j) {
+    const int cb = tile_n + wn * FN * 32 + j * 32;  // first column of the block
     // this lane's 4 columns: contiguous float4 destination if all are plain copies
     // of one region of one head
     const int c0 = cb + sc;
@@ -218,7 +240,7 @@ __global__ __launch_bounds__(NTH) void proj_gemm_bf16_kernel(
             od[e].base == od[0].base + e;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < FM; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         patch[((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * 36 + (lane & 31)] = acc[i][j][r];
@@ -227,7 +249,7 @@ __global__ __launch_bounds__(NTH) void proj_gemm_bf16_kernel(
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int rr = q * 8 + sr;
-        const int64_t lm = tile_m + wm * 128 + i * 32 + rr;
+        const int64_t lm = tile_m + wm * FM * 32 + i * 32 + rr;
         const float4 v = *reinterpret_cast<const float4*>(patch + rr * 36 + sc);
         if (lm < M) {
           if (vec) {
@@ -305,12 +327,22 @@ hipError_t launch_proj_gemm(const sdm_dims& d, const void* x, const void* w_proj
   const int Ncol = d.H * dst.P;
   const int K = (int)d.d_model;
   if (d.in_dtype == SDM_DTYPE_BF16) {
-    const int64_t tiles = ((rows + BM - 1) / BM) * ((Ncol + BN - 1) / BN);
-    const dim3 grid((unsigned)(((tiles + NXCD - 1) / NXCD) * NXCD));
-    KernelTimer kt("proj_gemm_bf16", s);
-    hipLaunchKernelGGL(proj_gemm_bf16_kernel, grid, dim3(NTH), 0, s,
-                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_proj), row0,
-                       rows, Ncol, K, dst);
+    // the 256 x 256 tile when it gives the CUs enough workgroups, else 64 x 64
+    const int64_t big = ((rows + BigTile::BM - 1) / BigTile::BM) *
+                        ((Ncol + BigTile::BN - 1) / BigTile::BN);
+    auto go = [&](auto tl) {
+      using TL = decltype(tl);
+      const int64_t tiles = ((rows + TL::BM - 1) / TL::BM) * ((Ncol + TL::BN - 1) / TL::BN);
+      const dim3 grid((unsigned)(((tiles + NXCD - 1) / NXCD) * NXCD));
+      KernelTimer kt("proj_gemm_bf16", s);
+      hipLaunchKernelGGL(proj_gemm_bf16_kernel<TL>, grid, dim3(TL::NTH), 0, s,
+                         static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_proj),
+                         row0, rows, Ncol, K, dst);
+    };
+    if (big >= 256)
+      go(BigTile{});
+    else
+      go(SmallTile{});
   } else {
     dim3 grid((Ncol + 63) / 64, (unsigned)((rows + 63) / 64));
     KernelTimer kt("proj_gemm_f32", s);
