@@ -86,11 +86,12 @@ __device__ __forceinline__ void epilogue_store(const ProjDst& d, int64_t m, int 
 // blocks resident on one XCD share A and B slices through its L2.  The epilogue
 // goes through LDS so that every store writes a 16-byte row segment.
 // ---------------------------------------------------------------------------
-// Tile shape: WM x WN waves, each owning FM x FN MFMA 32x32 blocks.
-template <int WM_, int WN_, int FM_, int FN_>
+// Tile shape: WM x WN waves, each owning FM x FN MFMA 32x32 blocks; BK columns of K
+// per pipeline stage.
+template <int WM_, int WN_, int FM_, int FN_, int BK_>
 struct Tile {
   static constexpr int WM = WM_, WN = WN_, FM = FM_, FN = FN_;
-  static constexpr int BM = WM * FM * 32, BN = WN * FN * 32, BK = 64, LDK = BK + 8;
+  static constexpr int BM = WM * FM * 32, BN = WN * FN * 32, BK = BK_, LDK = BK + 8;
   static constexpr int NTH = WM * WN * 64;
   static constexpr int CPR = BK / 8;                  // 16-byte chunks per tile row
   static constexpr int A_CHUNKS = BM * BK / 8 / NTH;  // 16-byte chunks per thread per K-tile
@@ -100,8 +101,10 @@ struct Tile {
   static_assert(A_CHUNKS * NTH * 8 == BM * BK && B_CHUNKS * NTH * 8 == BN * BK, "even split");
   static_assert(LDS >= WM * WN * 32 * 36 * 4, "epilogue patches fit in the tile buffers");
 };
-using BigTile = Tile<2, 4, 4, 2>;    // 256 x 256, 8 waves of 128 x 64
-using SmallTile = Tile<2, 2, 1, 1>;  // 64 x 64, 4 waves of 32 x 32 (few rows: decode)
+using BigTile = Tile<2, 4, 4, 2, 64>;     // 256 x 256, 8 waves of 128 x 64
+// 64 x 64, 4 waves of 32 x 32, for few rows (decoding); the longer K-step halves the
+// steps of each workgroup's serial K loop while two workgroups still fit a CU's LDS
+using SmallTile = Tile<2, 2, 1, 1, 128>;
 constexpr int GROUP_M = 4;
 constexpr int NXCD = 8;
 
