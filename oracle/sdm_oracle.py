@@ -34,6 +34,10 @@ Variant (not the pages' printed rule): scan_gdn uses Gated DeltaNet's
 key-weighted error term on the write set; it is pinned against a dense
 matrix-form gated delta recurrence with every slot selected.
 
+Storage variant: scan(..., store=round_bf16) keeps a bf16 state (every written
+row rounded to nearest-even bf16 from the exact value); round_bf16 is pinned
+against torch's float32 -> bfloat16 conversion and hand-worked halfway cases.
+
 Pins: every function here is checked by tests/test_oracle_pins.py against
 hand-worked fixtures (tests/golden/), closed forms, exact rational arithmetic
 and brute force.  No function of this module is "parity unpinned".
@@ -173,13 +177,18 @@ def select(half1, half2, count: int):
 # [rainbus] step 3: y_t = sum_{i in I_r} q^(i) M_t[i]  (reads the state after
 # this token's write).
 # ----------------------------------------------------------------------------
-def scan(state0, idx_w, wt_w, idx_r, wt_r, v, alpha, beta):
+def scan(state0, idx_w, wt_w, idx_r, wt_r, v, alpha, beta, store=None):
     """Walk tokens in order over one memory.
 
     state0 [N, d_v]; idx_w/wt_w [T, W]; idx_r/wt_r [T, R]; v [T, d_v];
     alpha, beta [T].  Returns (y_raw [T, d_v], final state [N, d_v]) in fp64.
+    store: None (the state holds the exact values), or a rounding function applied
+    to every written row, the state then holding only its results (round_bf16 for
+    a bf16 state); state0 must then be representable already.
     """
     M = np.array(state0, dtype=F64, copy=True)
+    keep = store if store is not None else (lambda z: z)
+    assert np.array_equal(keep(M), M), "state0 is not representable in the state's format"
     idx_w = np.asarray(idx_w)
     idx_r = np.asarray(idx_r)
     wt_w = np.asarray(wt_w, F64)
@@ -193,7 +202,7 @@ def scan(state0, idx_w, wt_w, idx_r, wt_r, v, alpha, beta):
         rows = idx_w[t]
         assert np.unique(rows).size == rows.size, "write slots of one token must be distinct"
         m_tilde = alpha[t] * M[rows]                                   # forget gate
-        M[rows] = m_tilde + (beta[t] * wt_w[t])[:, None] * (v[t][None, :] - m_tilde)
+        M[rows] = keep(m_tilde + (beta[t] * wt_w[t])[:, None] * (v[t][None, :] - m_tilde))
         y[t] = wt_r[t] @ M[idx_r[t]]                                   # sparse read
     return y, M
 
@@ -209,9 +218,11 @@ def scan(state0, idx_w, wt_w, idx_r, wt_r, v, alpha, beta):
 # i.e. the error term subtracts the key-weighted prediction of the whole write
 # set instead of the slot's own value.  Reads are unchanged.
 # ----------------------------------------------------------------------------
-def scan_gdn(state0, idx_w, wt_w, idx_r, wt_r, v, alpha, beta):
+def scan_gdn(state0, idx_w, wt_w, idx_r, wt_r, v, alpha, beta, store=None):
     """Like scan(), with the key-weighted error term above."""
     M = np.array(state0, dtype=F64, copy=True)
+    keep = store if store is not None else (lambda z: z)
+    assert np.array_equal(keep(M), M), "state0 is not representable in the state's format"
     idx_w = np.asarray(idx_w)
     idx_r = np.asarray(idx_r)
     wt_w = np.asarray(wt_w, F64)
@@ -227,9 +238,28 @@ def scan_gdn(state0, idx_w, wt_w, idx_r, wt_r, v, alpha, beta):
         k = wt_w[t]
         m_tilde = alpha[t] * M[rows]                                   # forget gate
         pred = k @ m_tilde                                             # key-weighted prediction
-        M[rows] = m_tilde + (beta[t] * k)[:, None] * (v[t] - pred)[None, :]
+        M[rows] = keep(m_tilde + (beta[t] * k)[:, None] * (v[t] - pred)[None, :])
         y[t] = wt_r[t] @ M[idx_r[t]]                                   # sparse read
     return y, M
+
+
+# ----------------------------------------------------------------------------
+# Reduced-precision state storage (not a step of the pages, which keep the live
+# state in full precision and quantise only training checkpoints: [analysis]
+# section "训练效率", [163] section 八).  bf16 is IEEE binary32 with the low 16
+# fraction bits dropped: 8 significant bits, the same exponent range (normal
+# numbers down to 2^-126, subnormals spaced 2^-133).  Round to nearest, ties to
+# the even significand, from the exact fp64 value (one rounding).
+# ----------------------------------------------------------------------------
+def round_bf16(x):
+    """Nearest bf16 value of each element of x (ties to even), as fp64."""
+    x = np.asarray(x, F64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        _, e = np.frexp(x)                   # x = m 2^e, 0.5 <= |m| < 1
+        e = np.maximum(e, -125)              # below 2^-126: the subnormal spacing 2^-133
+        q = np.ldexp(np.rint(np.ldexp(x, 8 - e)), e - 8)   # 8 significant bits
+        q = np.where(np.abs(q) >= 2.0 ** 128, np.copysign(np.inf, x), q)
+    return np.where(np.isfinite(x), q, x)
 
 
 # ----------------------------------------------------------------------------
@@ -279,17 +309,19 @@ def select_from_scores(scores, n, W, R):
     return {k: np.array(v).reshape(lead + shp[k]) for k, v in res.items()}
 
 
-def forward_walk(state0, sel, gamma_h, eps, rule: str = "slot"):
+def forward_walk(state0, sel, gamma_h, eps, rule: str = "slot", state: str = "exact"):
     """Scan + norm/gate for one (batch, head) walk given its pass-(a) products.
 
     sel holds [T, *] arrays for that walk: idx_w, wt_w, idx_r, wt_r, v, g,
     alpha, beta.  rule "slot" is the pages' per-slot error term (scan), "gdn"
-    the key-weighted one (scan_gdn).  Returns (out [T, d_v], y_raw [T, d_v],
-    final state).
+    the key-weighted one (scan_gdn).  state "exact" keeps the state in fp64,
+    "bf16" stores every written row rounded to bf16.  Returns (out [T, d_v],
+    y_raw [T, d_v], final state).
     """
     walk = {"slot": scan, "gdn": scan_gdn}[rule]
+    store = {"exact": None, "bf16": round_bf16}[state]
     y, M = walk(state0, sel["idx_w"], sel["wt_w"], sel["idx_r"], sel["wt_r"],
-                sel["v"], sel["alpha"], sel["beta"])
+                sel["v"], sel["alpha"], sel["beta"], store=store)
     return rms_norm_gate(y, gamma_h, sel["g"], eps), y, M
 
 
