@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--workload", default="layer1p4b")
+    p.add_argument("--state", choices=("fp32", "bf16"), default="fp32",
+                   help="state storage: fp32 (the method's precision) or bf16 with fp32 "
+                        "arithmetic (SDM_FLAG_STATE_BF16)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-tokens", type=int, default=2048,
                    help="tokens of batch entry 0 in the oracle's timed sample")
@@ -95,6 +98,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     d = dims_for(wl)
+    bf16_state = args.state == "bf16"
+    if bf16_state:
+        d.flags |= _lib.SDM_FLAG_STATE_BF16
 
     # inputs resident in HBM before timing
     _, x_store = synth.gen_x(wl, seed=0)
@@ -110,6 +116,8 @@ def main():
     w = to_dev(prm["w_proj_store"])
     A, b_dt, gamma = to_dev(prm["A"]), to_dev(prm["b_dt"]), to_dev(prm["gamma"])
     m0_d = to_dev(m0)
+    if bf16_state:
+        m0_d = m0_d.to(torch.bfloat16)
     state = m0_d.unsqueeze(0).expand(wl.B, *m0_d.shape).contiguous()
     del m0
     prod = ops.alloc_products(d, dev)
@@ -159,7 +167,7 @@ def main():
     scan_ms = kernels_ms[scan_kernel]["avg"] * kernels_ms[scan_kernel]["launches"] / args.steps
 
     tokens = wl.tokens
-    slot_bytes = tokens * wl.H * wl.slot_bytes_per_token_head()
+    slot_bytes = tokens * wl.H * wl.slot_bytes_per_token_head(2 if bf16_state else 4)
     achieved = slot_bytes / (scan_ms * 1e-3) / 1e9
     res = {
         "metric": METRIC,
@@ -172,17 +180,18 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 projection, fp32 selection/scan",
+        "dtype": ("bf16 projection, fp32 selection/scan, bf16 state storage" if bf16_state
+                  else "bf16 projection, fp32 selection/scan"),
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "d_model": wl.d_model, "H": wl.H,
                    "N": wl.N, "n": wl.n, "W": wl.W, "R": wl.R, "d_v": wl.d_v,
-                   "state": "fp32 [B,H,N,d_v]", "tokens_per_step": tokens},
+                   "state": f"{args.state} [B,H,N,d_v]", "tokens_per_step": tokens},
         "phases_ms": {"select": ms_sel, "scan": ms_scan, "step_events": ms_step},
         "kernels_ms": kernels_ms,
         "effective_hbm_gbs_step": slot_bytes / (ms_wall * 1e-3) / 1e9,
         "roofline": {"bound": "hbm", "kernel": scan_kernel, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(wl.name),
+                     "traffic": None if bf16_state else measured_traffic(wl.name),
                      "algorithmic_bytes_per_launch":
                          slot_bytes * args.steps / kernels_ms[scan_kernel]["launches"]},
     }

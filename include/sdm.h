@@ -26,8 +26,9 @@
  *    reported by the runtime right after a launch returns SDM_ERR_HIP.
  *  - Device pointers must be 16-byte aligned (SDM_ERR_ALIGN).
  *  - Layouts are row-major and contiguous.  Per-token tensors are [B, T, H, ...];
- *    the state is [B, H, N, d_v] fp32 with N = n*n slots; slot id = i*n + j where i
- *    indexes the first half-score vector and j the second.
+ *    the state is [B, H, N, d_v] fp32 (bf16 with SDM_FLAG_STATE_BF16) with N = n*n
+ *    slots; slot id = i*n + j where i indexes the first half-score vector and j the
+ *    second.
  *  - B*T == 0 is a valid empty call: SDM_OK, nothing enqueued.
  *  - NaN or Inf inputs propagate per IEEE in the arithmetic; the selection order of
  *    NaN scores is unspecified.
@@ -94,6 +95,15 @@ extern "C" {
    any is written, so it runs the direct schedule; combined with
    SDM_FLAG_SCAN_STREAM or SDM_FLAG_SCAN_TWO_PHASE it is SDM_ERR_UNSUPPORTED. */
 #define SDM_FLAG_DELTA_GDN 16
+/* storage flag (sdm_dims.flags; sdm_scan and sdm_forward): the state buffer holds
+   bf16 values.  The arithmetic stays fp32; each written row element is rounded to
+   the nearest bf16 (ties to even) when stored, and later accesses of the token run
+   see that stored value.  Half the state bytes of the fp32 layout move per slot
+   access.  Not a step of the pages: they keep the live state in full precision and
+   quantise only training checkpoints (to fp8 or int4, for long fine-tuning runs:
+   ai-paper-analysis.pages.dev, section "训练效率"; m.163.com article on arXiv
+   2607.07386, section 八).  Every schedule and both write rules support it. */
+#define SDM_FLAG_STATE_BF16 32
 
 /* Limits of this build (SDM_ERR_UNSUPPORTED beyond them). */
 #define SDM_MAX_COUNT 128   /* W and R */
@@ -115,7 +125,8 @@ extern "C" {
  *   eps       RMSNorm epsilon (>= 0)
  *   flags     0, or one SDM_FLAG_SCAN_* bit to force a scan schedule (all schedules
  *             compute the same recurrence; by default the library picks by shape),
- *             optionally OR-ed with SDM_FLAG_TIMING
+ *             optionally OR-ed with SDM_FLAG_TIMING, SDM_FLAG_DELTA_GDN and
+ *             SDM_FLAG_STATE_BF16
  */
 typedef struct sdm_dims {
   int64_t B, T, d_model;
@@ -204,14 +215,15 @@ SDM_API int32_t sdm_select_from_scores(const sdm_dims* dims, const float* scores
  * Slots never selected for writing are never written (bit-identical on return).
  *   in      pass-(a) products (every field but `scores` required)
  *   norm_w  [H, d_v] fp32 RMSNorm weight, or NULL for ones
- *   state   [B, H, N, d_v] fp32, IN/OUT: M_0 on entry (e.g. a learned initial state,
+ *   state   [B, H, N, d_v] fp32 (bf16 with SDM_FLAG_STATE_BF16), IN/OUT: M_0 on entry
+ *           (e.g. a learned initial state,
  *           [analysis] section on M0), M_T on return.  Calling with T tokens equals
  *           calling on consecutive token chunks with the same state buffer.
  *   out     [B, T, H, d_v] fp32
  *   y_raw   [B, T, H, d_v] fp32 or NULL: the read vector before normalisation
  *   ws      >= sdm_workspace_bytes(dims, SDM_ENTRY_SCAN) bytes
  */
-SDM_API int32_t sdm_scan(const sdm_dims* dims, const sdm_sel* in, const float* norm_w, float* state,
+SDM_API int32_t sdm_scan(const sdm_dims* dims, const sdm_sel* in, const float* norm_w, void* state,
                  float* out, float* y_raw, void* ws, size_t ws_bytes, void* stream);
 
 /*
@@ -221,7 +233,7 @@ SDM_API int32_t sdm_scan(const sdm_dims* dims, const sdm_sel* in, const float* n
  *   ws >= sdm_workspace_bytes(dims, SDM_ENTRY_FORWARD) bytes
  */
 SDM_API int32_t sdm_forward(const sdm_dims* dims, const void* x, const void* w_proj, const float* A,
-                    const float* b_dt, const float* norm_w, float* state, float* out,
+                    const float* b_dt, const float* norm_w, void* state, float* out,
                     const sdm_sel* debug, void* ws, size_t ws_bytes, void* stream);
 
 /*

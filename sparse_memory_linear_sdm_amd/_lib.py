@@ -23,6 +23,7 @@ SDM_MAX_COUNT, SDM_MAX_HALF = 128, 1024
 SDM_FLAG_SCAN_DIRECT, SDM_FLAG_SCAN_STREAM, SDM_FLAG_SCAN_TWO_PHASE = 1, 2, 4
 SDM_FLAG_TIMING = 8
 SDM_FLAG_DELTA_GDN = 16
+SDM_FLAG_STATE_BF16 = 32
 
 EXPORTS = ("sdm_abi_version", "sdm_status_string", "sdm_workspace_bytes", "sdm_select",
            "sdm_select_from_scores", "sdm_scan", "sdm_forward", "sdm_timing_read")

@@ -12,7 +12,8 @@
 // Variant (SDM_FLAG_DELTA_GDN): the error term is the key-weighted prediction of
 // the write set, M[i] <- alpha M[i] + beta k_i (v - alpha sum_j k_j M[j]) -- Gated
 // DeltaNet's rule on the selected slots ("与 GDN 的关系" section of
-// ai-paper-analysis.pages.dev).
+// ai-paper-analysis.pages.dev).  Storage (SDM_FLAG_STATE_BF16): bf16 state rows,
+// fp32 arithmetic, each stored element rounded to nearest-even bf16.
 #include "sdm_internal.h"
 
 namespace sdm {
@@ -25,8 +26,9 @@ __device__ __forceinline__ float4 f4(float a) { return make_float4(a, a, a, a); 
 // writes and R reads of a token.  Barriers order the write phase, the read phase
 // and the next token's writes (all accesses stay inside one workgroup, whose
 // waves share the CU's vector L1).
-template <int DV, bool GDN>
+template <int DV, bool GDN, bool BF>
 __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
+  constexpr uint32_t ES = StateT<BF>::ES;
   constexpr int LPR = DV / 4;
   constexpr int G = 256 / LPR;
   __shared__ float4 red[G][LPR];
@@ -37,7 +39,9 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   const int64_t bh = blockIdx.x;
   const int64_t b = bh / a.H;
   const int h = (int)(bh - b * a.H);
-  float* M = a.state + bh * (int64_t)a.N * DV;
+  // row r, this lane's 4 columns
+  char* const Mb = static_cast<char*>(a.state) + bh * (int64_t)a.N * DV * ES + li * 4 * ES;
+  auto row = [&](int64_t r) { return Mb + r * (DV * ES); };
   const float4 gam = a.norm_w ? reinterpret_cast<const float4*>(a.norm_w + (int64_t)h * DV)[li]
                               : f4(1.0f);
 
@@ -54,7 +58,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
       float4 part = f4(0.0f);
       for (int k = grp; k < a.W; k += G) {
         const float w = ww[k];
-        const float4 m = reinterpret_cast<const float4*>(M + (int64_t)iw[k] * DV)[li];
+        const float4 m = state_load<BF>(row(iw[k]));
         part.x = fmaf(w, m.x, part.x);
         part.y = fmaf(w, m.y, part.y);
         part.z = fmaf(w, m.z, part.z);
@@ -74,35 +78,33 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
                                      vv.w - al * pred.w);
       for (int k = grp; k < a.W; k += G) {
         const float c = be * ww[k];
-        float4* p = reinterpret_cast<float4*>(M + (int64_t)iw[k] * DV) + li;
-        float4 m = *p;
+        char* p = row(iw[k]);
+        float4 m = state_load<BF>(p);
         m.x = fmaf(c, err.x, al * m.x);
         m.y = fmaf(c, err.y, al * m.y);
         m.z = fmaf(c, err.z, al * m.z);
         m.w = fmaf(c, err.w, al * m.w);
-        *p = m;
+        state_store<BF>(reinterpret_cast<uint64_t>(p), state_round<BF>(m));
       }
     } else
     for (int k = grp; k < a.W; k += G) {
-      const int64_t row = iw[k];
       const float c = be * ww[k];
       const float oc = 1.0f - c;
-      float4* p = reinterpret_cast<float4*>(M + row * DV) + li;
-      float4 m = *p;
+      char* p = row(iw[k]);
+      float4 m = state_load<BF>(p);
       m.x = fmaf(c, vv.x, oc * (al * m.x));
       m.y = fmaf(c, vv.y, oc * (al * m.y));
       m.z = fmaf(c, vv.z, oc * (al * m.z));
       m.w = fmaf(c, vv.w, oc * (al * m.w));
-      *p = m;
+      state_store<BF>(reinterpret_cast<uint64_t>(p), state_round<BF>(m));
     }
     __syncthreads();
     const int32_t* ir = a.idx_r + tok * a.R;
     const float* wr = a.wt_r + tok * a.R;
     float4 acc = f4(0.0f);
     for (int k = grp; k < a.R; k += G) {
-      const int64_t row = ir[k];
       const float q = wr[k];
-      const float4 m = reinterpret_cast<const float4*>(M + row * DV)[li];
+      const float4 m = state_load<BF>(row(ir[k]));
       acc.x = fmaf(q, m.x, acc.x);
       acc.y = fmaf(q, m.y, acc.y);
       acc.z = fmaf(q, m.z, acc.z);
@@ -136,10 +138,14 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
 
 template <int DV>
 void launch_direct(bool gdn, dim3 grid, hipStream_t s, const ScanArgs& a) {
-  if (gdn)
-    hipLaunchKernelGGL((scan_kernel<DV, true>), grid, dim3(256), 0, s, a);
+  if (gdn && a.state_bf16)
+    hipLaunchKernelGGL((scan_kernel<DV, true, true>), grid, dim3(256), 0, s, a);
+  else if (gdn)
+    hipLaunchKernelGGL((scan_kernel<DV, true, false>), grid, dim3(256), 0, s, a);
+  else if (a.state_bf16)
+    hipLaunchKernelGGL((scan_kernel<DV, false, true>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((scan_kernel<DV, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((scan_kernel<DV, false, false>), grid, dim3(256), 0, s, a);
 }
 
 }  // namespace

@@ -1,4 +1,5 @@
 // Recurrent sparse scan for long token runs: slot-owner lane groups.
+// State rows are fp32, or bf16 with fp32 arithmetic (SDM_FLAG_STATE_BF16).
 //
 // What is computed is the recurrence of the method ("Sparse Delta Memory" summary
 // on paper.rainbus.top, method paragraph, steps 2-3; ai-paper-analysis.pages.dev,
@@ -192,8 +193,9 @@ __global__ __launch_bounds__(64) void bucket_scatter_kernel(StreamArgs a) {
 // Per round the slice of v and the gates of the round's tokens are staged in LDS,
 // so a batch only holds its BQ state rows in registers while they are in flight.
 // ---------------------------------------------------------------------------
-template <int NT, int SW, int BQ>
+template <int NT, int SW, int BQ, bool BF>
 __global__ __launch_bounds__(NT) void stream_scan_kernel(StreamArgs a) {
+  constexpr uint32_t ES = StateT<BF>::ES;
   constexpr int LPG = SW / 4;
   constexpr int GW = NT / LPG;
   constexpr int EPL = (BQ + LPG - 1) / LPG;  // entries loaded per lane per batch
@@ -221,9 +223,9 @@ __global__ __launch_bounds__(NT) void stream_scan_kernel(StreamArgs a) {
   for (int x = tid; x < 2 * ROUND * YS; x += NT) yr[x] = 0.0f;
 
   // state of this walk as a uniform base; rows addressed by 32-bit byte offsets
-  char* Mb = reinterpret_cast<char*>(a.state + w * (int64_t)a.N * dv);
-  const uint32_t col_bytes = (uint32_t)(sl * SW + li * 4) * 4u;
-  const uint32_t row_bytes = (uint32_t)dv * 4u;
+  char* Mb = static_cast<char*>(a.state) + w * (int64_t)a.N * dv * ES;
+  const uint32_t col_bytes = (uint32_t)(sl * SW + li * 4) * ES;
+  const uint32_t row_bytes = (uint32_t)dv * ES;
   const uint2* ent = a.entries + w * a.walk_entries;
   const int* offs = a.offsets + ((int64_t)w * a.GT + gg) * (a.rounds + 1);
   const int64_t tok_base = (b * a.T + a.t0) * a.H + h;  // token t -> tok_base + t*H
@@ -277,7 +279,7 @@ __global__ __launch_bounds__(NT) void stream_scan_kernel(StreamArgs a) {
       }
 #pragma unroll
       for (int j = 0; j < BQ; ++j)
-        mv[j] = *reinterpret_cast<const float4*>(Mb + (slot[j] * row_bytes + col_bytes));
+        mv[j] = state_load<BF>(Mb + (slot[j] * row_bytes + col_bytes));
 #pragma unroll
       for (int j = 0; j < BQ; ++j) {
         float4 val = mv[j];
@@ -306,12 +308,11 @@ __global__ __launch_bounds__(NT) void stream_scan_kernel(StreamArgs a) {
           val.y = isw ? nv.y : val.y;
           val.z = isw ? nv.z : val.z;
           val.w = isw ? nv.w : val.w;
+          val = state_round<BF>(val);  // the stored value (exact for non-writes)
           uint64_t dst = isw ? reinterpret_cast<uint64_t>(Mb + (slot[j] * row_bytes + col_bytes))
                              : reinterpret_cast<uint64_t>(trash);
           asm volatile("" : "+v"(dst));  // keep one unconditional store: hide the select
-          typedef float gvec4 __attribute__((ext_vector_type(4)));
-          *reinterpret_cast<__attribute__((address_space(1))) gvec4*>(dst) =
-              gvec4{val.x, val.y, val.z, val.w};
+          state_store<BF>(dst, val);
         }
         if (!isw && ((vam >> j) & 1u)) {
           float* y = yr + (half * ROUND + tk[j]) * YS + li;
@@ -473,8 +474,9 @@ __global__ __launch_bounds__(64) void bucket_scatter_rev_kernel(StreamArgs a) {
 //                round's writes come after the reads).  Parts never touch each
 //                other's slots, so they need no synchronisation with one another.
 // ---------------------------------------------------------------------------
-template <int NT, int SW, int BQ, int BR>
+template <int NT, int SW, int BQ, int BR, bool BF>
 __global__ __launch_bounds__(NT) void two_phase_scan_kernel(StreamArgs a) {
+  constexpr uint32_t ES = StateT<BF>::ES;
   constexpr int LPG = SW / 4;
   constexpr int GW = NT / LPG;
   constexpr int EPL = (BQ + LPG - 1) / LPG;
@@ -499,9 +501,9 @@ __global__ __launch_bounds__(NT) void two_phase_scan_kernel(StreamArgs a) {
 
   for (int x = tid; x < ROUND * YS; x += NT) yr[x] = 0.0f;
 
-  char* Mb = reinterpret_cast<char*>(a.state + w * (int64_t)a.N * dv);
-  const uint32_t col_bytes = (uint32_t)(sl * SW + li * 4) * 4u;
-  const uint32_t row_bytes = (uint32_t)dv * 4u;
+  char* Mb = static_cast<char*>(a.state) + w * (int64_t)a.N * dv * ES;
+  const uint32_t col_bytes = (uint32_t)(sl * SW + li * 4) * ES;
+  const uint32_t row_bytes = (uint32_t)dv * ES;
   const uint2* ent = a.entries + w * a.walk_entries;
   const int* offs = a.offsets + ((int64_t)w * a.GT + gg) * (a.rounds + 1);
   const int* begs = a.begins + ((int64_t)w * a.GT + gg) * a.rounds;
@@ -553,7 +555,7 @@ __global__ __launch_bounds__(NT) void two_phase_scan_kernel(StreamArgs a) {
       }
 #pragma unroll
       for (int j = 0; j < BQ; ++j)
-        mv[j] = *reinterpret_cast<const float4*>(Mb + (slot[j] * row_bytes + col_bytes));
+        mv[j] = state_load<BF>(Mb + (slot[j] * row_bytes + col_bytes));
 #pragma unroll
       for (int j = 0; j < BQ; ++j) {
         float4 val = mv[j];
@@ -580,12 +582,11 @@ __global__ __launch_bounds__(NT) void two_phase_scan_kernel(StreamArgs a) {
           val.y = isw ? nv.y : val.y;
           val.z = isw ? nv.z : val.z;
           val.w = isw ? nv.w : val.w;
+          val = state_round<BF>(val);  // the stored value (exact for non-writes)
           uint64_t dst = isw ? reinterpret_cast<uint64_t>(Mb + (slot[j] * row_bytes + col_bytes))
                              : reinterpret_cast<uint64_t>(trash);
           asm volatile("" : "+v"(dst));  // keep one unconditional store: hide the select
-          typedef float gvec4 __attribute__((ext_vector_type(4)));
-          *reinterpret_cast<__attribute__((address_space(1))) gvec4*>(dst) =
-              gvec4{val.x, val.y, val.z, val.w};
+          state_store<BF>(dst, val);
         }
         if (!isw && ((vam >> j) & 1u)) {  // dirty read: its value at this point of the stream
           float* y = yr + tk[j] * YS + li;
@@ -629,7 +630,7 @@ __global__ __launch_bounds__(NT) void two_phase_scan_kernel(StreamArgs a) {
           }
 #pragma unroll
           for (int j = 0; j < BR; ++j)
-            rv[j] = *reinterpret_cast<const float4*>(Mb + (rs[j] * row_bytes + col_bytes));
+            rv[j] = state_load<BF>(Mb + (rs[j] * row_bytes + col_bytes));
 #pragma unroll
           for (int j = 0; j < BR; ++j) {
             acc.x = fmaf(rq[j], rv[j].x, acc.x);
@@ -864,10 +865,18 @@ hipError_t launch_stream_scan(const ScanArgs& sa, const StreamPlan& pl, void* ws
       }
       const dim3 grid((unsigned)(walks * pl.S * pl.parts));
       KernelTimer kt("two_phase_scan", st);
-      if (pl.SW == 32)
-        hipLaunchKernelGGL((two_phase_scan_kernel<1024, 32, 8, 8>), grid, dim3(1024), 0, st, a);
+      if (pl.SW == 32 && sa.state_bf16)
+        hipLaunchKernelGGL((two_phase_scan_kernel<1024, 32, 8, 8, true>), grid, dim3(1024), 0, st,
+                           a);
+      else if (pl.SW == 32)
+        hipLaunchKernelGGL((two_phase_scan_kernel<1024, 32, 8, 8, false>), grid, dim3(1024), 0, st,
+                           a);
+      else if (sa.state_bf16)
+        hipLaunchKernelGGL((two_phase_scan_kernel<1024, 16, 8, 8, true>), grid, dim3(1024), 0, st,
+                           a);
       else
-        hipLaunchKernelGGL((two_phase_scan_kernel<1024, 16, 8, 8>), grid, dim3(1024), 0, st, a);
+        hipLaunchKernelGGL((two_phase_scan_kernel<1024, 16, 8, 8, false>), grid, dim3(1024), 0, st,
+                           a);
     } else {
       {
         KernelTimer kt("bucket_scatter", st);
@@ -876,10 +885,14 @@ hipError_t launch_stream_scan(const ScanArgs& sa, const StreamPlan& pl, void* ws
       }
       const dim3 grid((unsigned)(walks * pl.S * pl.parts));
       KernelTimer kt("stream_scan", st);
-      if (pl.SW == 32)
-        hipLaunchKernelGGL((stream_scan_kernel<1024, 32, 8>), grid, dim3(1024), 0, st, a);
+      if (pl.SW == 32 && sa.state_bf16)
+        hipLaunchKernelGGL((stream_scan_kernel<1024, 32, 8, true>), grid, dim3(1024), 0, st, a);
+      else if (pl.SW == 32)
+        hipLaunchKernelGGL((stream_scan_kernel<1024, 32, 8, false>), grid, dim3(1024), 0, st, a);
+      else if (sa.state_bf16)
+        hipLaunchKernelGGL((stream_scan_kernel<1024, 16, 8, true>), grid, dim3(1024), 0, st, a);
       else
-        hipLaunchKernelGGL((stream_scan_kernel<1024, 16, 8>), grid, dim3(1024), 0, st, a);
+        hipLaunchKernelGGL((stream_scan_kernel<1024, 16, 8, false>), grid, dim3(1024), 0, st, a);
     }
     const int64_t rows = sa.B * a.Tc * sa.H;
     // rows per 256-thread block: 4 wavefronts x (64 / lanes per row)

@@ -26,7 +26,8 @@ struct Derived {
 int32_t check_dims(const sdm_dims* d, Derived* out) {
   if (!d) return SDM_ERR_NULL;
   const int32_t sched = SDM_FLAG_SCAN_DIRECT | SDM_FLAG_SCAN_STREAM | SDM_FLAG_SCAN_TWO_PHASE;
-  if (d->flags & ~(sched | SDM_FLAG_TIMING | SDM_FLAG_DELTA_GDN)) return SDM_ERR_UNSUPPORTED;
+  if (d->flags & ~(sched | SDM_FLAG_TIMING | SDM_FLAG_DELTA_GDN | SDM_FLAG_STATE_BF16))
+    return SDM_ERR_UNSUPPORTED;
   if (__builtin_popcount((unsigned)(d->flags & sched)) > 1) return SDM_ERR_SHAPE;  // one schedule
   if ((d->flags & SDM_FLAG_DELTA_GDN) &&
       (d->flags & (SDM_FLAG_SCAN_STREAM | SDM_FLAG_SCAN_TWO_PHASE)))
@@ -139,7 +140,7 @@ int32_t run_select(const sdm_dims* d, const Derived& dv, const void* x, const vo
 }
 
 int32_t run_scan(const sdm_dims* d, const Derived& dv, const sdm_sel* in, const float* norm_w,
-                 float* state, float* out, float* y_raw, void* ws, size_t ws_bytes,
+                 void* state, float* out, float* y_raw, void* ws, size_t ws_bytes,
                  hipStream_t st) {
   ScanArgs a;
   a.idx_w = in->idx_w;
@@ -162,6 +163,7 @@ int32_t run_scan(const sdm_dims* d, const Derived& dv, const sdm_sel* in, const 
   a.R = d->R;
   a.d_v = d->d_v;
   a.eps = d->eps;
+  a.state_bf16 = (d->flags & SDM_FLAG_STATE_BF16) != 0;
   return hip_status(launch_scan(*d, a, ws, ws_bytes, st));
 }
 
@@ -242,7 +244,7 @@ int32_t sdm_select_from_scores(const sdm_dims* d, const float* scores, int32_t* 
       launch_select(*d, scores, dv.M, 0, idx_w, wt_w, idx_r, wt_r, (hipStream_t)stream));
 }
 
-int32_t sdm_scan(const sdm_dims* d, const sdm_sel* in, const float* norm_w, float* state,
+int32_t sdm_scan(const sdm_dims* d, const sdm_sel* in, const float* norm_w, void* state,
                  float* out, float* y_raw, void* ws, size_t ws_bytes, void* stream) {
   Derived dv;
   int32_t st = check_dims(d, &dv);
@@ -261,7 +263,7 @@ int32_t sdm_scan(const sdm_dims* d, const sdm_sel* in, const float* norm_w, floa
 }
 
 int32_t sdm_forward(const sdm_dims* d, const void* x, const void* w_proj, const float* A,
-                    const float* b_dt, const float* norm_w, float* state, float* out,
+                    const float* b_dt, const float* norm_w, void* state, float* out,
                     const sdm_sel* debug, void* ws, size_t ws_bytes, void* stream) {
   Derived dv;
   int32_t st = check_dims(d, &dv);

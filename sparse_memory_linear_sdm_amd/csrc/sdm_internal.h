@@ -43,12 +43,13 @@ struct ScanArgs {
   const float* alpha;
   const float* beta;
   const float* norm_w;  // nullable
-  float* state;
+  void* state;          // fp32, or bf16 when state_bf16
   float* out;
   float* y_raw;         // nullable
   int64_t B, T;
   int32_t H, N, W, R, d_v;
   float eps;
+  bool state_bf16;
 };
 hipError_t launch_scan(const sdm_dims& d, const ScanArgs& a, void* ws, size_t ws_bytes,
                        hipStream_t s);
@@ -82,7 +83,7 @@ struct StreamArgs {
   const float* alpha;
   const float* beta;
   const float* norm_w;
-  float* state;
+  void* state;     // fp32, or bf16 when state_bf16
   float* out;
   float* y_raw;
   int* counts;     // [walks][rounds][GT]
@@ -108,5 +109,55 @@ StreamPlan plan_stream(const sdm_dims& d, int64_t N);
 size_t stream_workspace_bytes(const sdm_dims& d, const StreamPlan& pl);
 hipError_t launch_stream_scan(const ScanArgs& a, const StreamPlan& pl, void* ws, hipStream_t s);
 bool scan_uses_stream(const sdm_dims& d);
+
+// State element storage of the scan kernels: fp32, or bf16 (SDM_FLAG_STATE_BF16)
+// with fp32 arithmetic.  A lane moves 4 consecutive elements of a row: one 16-byte
+// (fp32) or 8-byte (bf16) access.  state_round returns a value as it will be stored
+// (nearest bf16, ties to even, by the hardware conversion), so that forwarded and
+// re-read values agree.
+template <bool BF>
+struct StateT {
+  static constexpr uint32_t ES = BF ? 2u : 4u;  // bytes per element
+};
+typedef float sdm_f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 sdm_b2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16_pack2(float a, float b) {
+  const sdm_b2 r = __builtin_convertvector((sdm_f2){a, b}, sdm_b2);
+  uint32_t u;
+  __builtin_memcpy(&u, &r, 4);
+  return u;
+}
+__device__ __forceinline__ float4 bf16_unpack4(uint2 u) {
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+}
+template <bool BF>
+__device__ __forceinline__ float4 state_load(const char* p) {
+  if constexpr (BF)
+    return bf16_unpack4(*reinterpret_cast<const uint2*>(p));
+  else
+    return *reinterpret_cast<const float4*>(p);
+}
+template <bool BF>
+__device__ __forceinline__ float4 state_round(float4 v) {
+  if constexpr (BF)
+    return bf16_unpack4(make_uint2(bf16_pack2(v.x, v.y), bf16_pack2(v.z, v.w)));
+  else
+    return v;
+}
+// Stores a value already passed through state_round (the conversion is then exact).
+// The address is a plain integer so callers can pick it without a branch.
+template <bool BF>
+__device__ __forceinline__ void state_store(uint64_t addr, float4 v) {
+  if constexpr (BF) {
+    typedef uint32_t gvec2 __attribute__((ext_vector_type(2)));
+    *reinterpret_cast<__attribute__((address_space(1))) gvec2*>(addr) =
+        gvec2{bf16_pack2(v.x, v.y), bf16_pack2(v.z, v.w)};
+  } else {
+    typedef float gvec4 __attribute__((ext_vector_type(4)));
+    *reinterpret_cast<__attribute__((address_space(1))) gvec4*>(addr) =
+        gvec4{v.x, v.y, v.z, v.w};
+  }
+}
 
 }  // namespace sdm

@@ -87,11 +87,15 @@ def select_from_scores(d: SdmDims, scores, stream=None):
     return {k: p[k] for k in ("idx_w", "wt_w", "idx_r", "wt_r")}
 
 
+def state_dtype(d: SdmDims):
+    return torch.bfloat16 if d.flags & _lib.SDM_FLAG_STATE_BF16 else torch.float32
+
+
 def scan(d: SdmDims, products: dict, norm_w, state, with_y_raw=False, out=None, ws=None,
          stream=None):
     _check_products(d, products)
     N = d.n * d.n
-    _need(state, torch.float32, (d.B, d.H, N, d.d_v), "state")
+    _need(state, state_dtype(d), (d.B, d.H, N, d.d_v), "state")
     if norm_w is not None:
         _need(norm_w, torch.float32, (d.H, d.d_v), "norm_w")
     dev = state.device
@@ -108,7 +112,7 @@ def forward(d: SdmDims, x, w_proj, A, b_dt, norm_w, state, debug=False, with_sco
     """Whole path; state is updated in place.  Returns out (and the products if debug)."""
     _check_params(d, x, w_proj, A, b_dt)
     N = d.n * d.n
-    _need(state, torch.float32, (d.B, d.H, N, d.d_v), "state")
+    _need(state, state_dtype(d), (d.B, d.H, N, d.d_v), "state")
     if norm_w is not None:
         _need(norm_w, torch.float32, (d.H, d.d_v), "norm_w")
     o = out if out is not None else torch.empty((d.B, d.T, d.H, d.d_v), device=x.device)

@@ -59,9 +59,10 @@ class Workload:
     def tokens(self) -> int:
         return self.B * self.T
 
-    def slot_bytes_per_token_head(self) -> int:
-        """Algorithmic slot-row bytes: W rows read + W rows written + R rows read."""
-        return (2 * self.W + self.R) * self.d_v * 4
+    def slot_bytes_per_token_head(self, elem_bytes: int = 4) -> int:
+        """Algorithmic slot-row bytes: W rows read + W rows written + R rows read
+        (elements of elem_bytes: 4 for an fp32 state, 2 for bf16)."""
+        return (2 * self.W + self.R) * self.d_v * elem_bytes
 
 
 WORKLOADS = {

@@ -76,7 +76,7 @@ def _select(lib, d, x=FAKE, w=FAKE, A=FAKE, b=FAKE, sel=None, ws=FAKE, nb=1 << 4
     (dict(eps=-1.0), _lib.SDM_ERR_SHAPE), (dict(eps=float("nan")), _lib.SDM_ERR_SHAPE),
     (dict(n=16, W=129), _lib.SDM_ERR_UNSUPPORTED), (dict(n=1025), _lib.SDM_ERR_UNSUPPORTED),
     (dict(d_v=48), _lib.SDM_ERR_UNSUPPORTED), (dict(d_model=60), _lib.SDM_ERR_UNSUPPORTED),
-    (dict(flags=32), _lib.SDM_ERR_UNSUPPORTED), (dict(flags=3), _lib.SDM_ERR_SHAPE),
+    (dict(flags=64), _lib.SDM_ERR_UNSUPPORTED), (dict(flags=3), _lib.SDM_ERR_SHAPE),
     (dict(flags=16 | 2), _lib.SDM_ERR_UNSUPPORTED), (dict(flags=16 | 4), _lib.SDM_ERR_UNSUPPORTED),
     (dict(flags=6), _lib.SDM_ERR_SHAPE), (dict(flags=8 | 5), _lib.SDM_ERR_SHAPE),
     (dict(in_dtype=7), _lib.SDM_ERR_DTYPE), (dict(gate_act=3), _lib.SDM_ERR_DTYPE),
@@ -104,6 +104,22 @@ def test_timing_flag_is_accepted_and_read_is_safe_without_records(lib):
     assert _lib.timing_read() == []
     assert lib.sdm_timing_read(None, 0) == 0
     assert lib.sdm_timing_read(None, 4) == _lib.SDM_ERR_NULL
+
+
+def test_bf16_state_flag_is_accepted_everywhere(lib):
+    # storage only: every schedule and both write rules accept it, workspaces are unchanged
+    bf = _lib.SDM_FLAG_STATE_BF16
+    for extra in (0, _lib.SDM_FLAG_SCAN_DIRECT, _lib.SDM_FLAG_SCAN_STREAM,
+                  _lib.SDM_FLAG_SCAN_TWO_PHASE, _lib.SDM_FLAG_DELTA_GDN,
+                  _lib.SDM_FLAG_DELTA_GDN | _lib.SDM_FLAG_SCAN_DIRECT):
+        d0, d1 = _d(T=64, flags=extra), _d(T=64, flags=extra | bf)
+        for entry in (_lib.SDM_ENTRY_SELECT, _lib.SDM_ENTRY_SCAN, _lib.SDM_ENTRY_FORWARD):
+            assert (lib.sdm_workspace_bytes(ctypes.byref(d1), entry) ==
+                    lib.sdm_workspace_bytes(ctypes.byref(d0), entry))
+        assert lib.sdm_workspace_bytes(ctypes.byref(d1), _lib.SDM_ENTRY_FORWARD) > 0
+        assert _select(lib, d1, x=None) == _lib.SDM_ERR_NULL
+    d = _d(T=64, flags=bf | _lib.SDM_FLAG_DELTA_GDN | _lib.SDM_FLAG_SCAN_TWO_PHASE)
+    assert _select(lib, d) == _lib.SDM_ERR_UNSUPPORTED
 
 
 def test_null_dims(lib):

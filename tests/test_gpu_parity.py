@@ -6,6 +6,10 @@ Stage C  scan from given selections  state / y / out within 1e-4 rel, 1e-5 abs;
                                      never-written rows bit-identical
 Stage D  whole layer from x          ids equal except near-ties / GEMM-rounding flips
                                      (reported, not failed); outputs within tolerance
+bf16 state storage (SDM_FLAG_STATE_BF16) against the oracle's bf16 scan: stored
+values equal except rare one-spacing rounding-boundary cases (bound derived in
+tests/gpu_util.py); the hardware rounding checked bit-exactly against torch's
+float32 -> bfloat16 conversion through exact overwrites.
 """
 import numpy as np
 import pytest
@@ -13,8 +17,9 @@ import torch
 
 from oracle import sdm_oracle as O
 from sparse_memory_linear_sdm_amd import _lib, dims_for, ops, synth
-from tests.gpu_util import (ATOL, NEAR_TIE, RTOL, assert_close, broadcast_state, gemm_bound,
-                            host, layer_inputs, oracle_walks, random_products, say, to_dev)
+from tests.gpu_util import (ATOL, NEAR_TIE, RTOL, assert_close, broadcast_state, check_bf16_reads,
+                            check_bf16_state, gemm_bound, host, layer_inputs, oracle_walks,
+                            random_products, say, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -202,6 +207,109 @@ def test_stage_c_identity_and_overwrite_exact(schedule):
             last = {int(p2["idx_w"][b, t, h, 0]): t for t in range(T)}
             for s, t in last.items():
                 assert np.array_equal(sth[b, h, s], p2["v"][b, t, h])
+
+
+# ---------------------------------------------------------------------------
+# bf16 state storage
+# ---------------------------------------------------------------------------
+def _bf16_state(rng, shape):
+    """Random bf16 state: host fp64 copy of the exact values, device bf16 tensor."""
+    m = torch.from_numpy((rng.standard_normal(shape) * 0.02).astype(np.float32)).to(torch.bfloat16)
+    return m.to(torch.float64).numpy(), m.to(torch.device("cuda:0"))
+
+
+@pytest.mark.parametrize("schedule,rule", [("direct", "slot"), ("stream", "slot"),
+                                           ("two_phase", "slot"), ("direct", "gdn")])
+@pytest.mark.parametrize("B,T,H,n,W,R,d_v,mode", [
+    (1, 64, 1, 32, 8, 8, 16, "random"),
+    (1, 700, 2, 32, 16, 16, 32, "repeat"),     # several rounds of the stream schedules
+    (2, 50, 2, 8, 32, 32, 64, "repeat"),       # heavy slot reuse
+    (3, 33, 2, 20, 64, 64, 128, "repeat"),
+    (1, 30, 1, 16, 128, 128, 256, "random"),
+    (2, 300, 2, 16, 32, 128, 64, "random"),    # W = 32 / R = 128
+])
+def test_stage_c_bf16_state(B, T, H, n, W, R, d_v, mode, schedule, rule):
+    rng = np.random.default_rng(B * 100 + T + W + 7)
+    N = n * n
+    prod = random_products(rng, B, T, H, n, W, R, d_v, mode)
+    m0, state = _bf16_state(rng, (B, H, N, d_v))
+    gamma = rng.uniform(0.5, 1.5, (H, d_v)).astype(np.float32)
+    flags = SCHEDULES[schedule] | _lib.SDM_FLAG_STATE_BF16
+    if rule == "gdn":
+        flags |= _lib.SDM_FLAG_DELTA_GDN
+    d = _dims(B=B, T=T, H=H, n=n, W=W, R=R, d_v=d_v, flags=flags)
+    out, y = ops.scan(d, _prod_dev(prod), to_dev(gamma), state, with_y_raw=True)
+    torch.cuda.synchronize()
+    st = state.to(torch.float64).cpu().numpy()
+    oh, yh = host(out), host(y)
+    walks = [(b, h) for b in range(B) for h in range(H)]
+    ref = oracle_walks(prod, m0, gamma, 1e-6, walks, rule=rule, state="bf16")
+    flips = late = 0
+    for (b, h), (o_out, o_y, o_M) in ref.items():
+        scale = max(np.abs(o_M).max(), np.abs(m0[b, h]).max())
+        flips += check_bf16_state(st[b, h], o_M, scale, f"state walk {(b, h)}")
+        late += check_bf16_reads(yh[b, :, h], o_y, oh[b, :, h], gamma[h],
+                                 prod["gate"][b, :, h], 1e-6, scale, R, f"walk {(b, h)}")
+        untouched = np.setdiff1d(np.arange(N), prod["idx_w"][b, :, h].ravel())
+        assert np.array_equal(st[b, h][untouched], m0[b, h][untouched]), "unwritten rows changed"
+    say(f"  state elements one rounding step apart: {flips}; tokens with such reads: {late}")
+
+
+@pytest.mark.parametrize("schedule", ["direct", "stream", "two_phase"])
+def test_stage_c_bf16_rounding_is_hardware_nearest_even(schedule):
+    """beta = 1, weight 1: every written row holds v rounded to bf16, bit for bit as
+    torch converts it; alpha = 1, beta = 0 leaves the state bit-identical."""
+    rng = np.random.default_rng(8)
+    B, T, H, n, d_v = 2, 40, 2, 8, 64
+    prod = random_products(rng, B, T, H, n, 1, 1, d_v)
+    # values with ties and near-ties of bf16 rounding in every row
+    ties = (1.0 + (2 * rng.integers(0, 128, (B, T, H, d_v)) + 1) * 2.0 ** -8) * \
+        rng.choice([-1.0, 1.0], (B, T, H, d_v)) * 2.0 ** rng.integers(-20, 20, (B, T, H, d_v))
+    v = np.where(rng.random((B, T, H, d_v)) < 0.5, ties, prod["v"]).astype(np.float32)
+    m0, st0 = _bf16_state(rng, (B, H, n * n, d_v))
+    d = _dims(B=B, T=T, H=H, n=n, W=1, R=1, d_v=d_v,
+              flags=SCHEDULES[schedule] | _lib.SDM_FLAG_STATE_BF16)
+    p1 = dict(prod, alpha=np.ones((B, T, H), np.float32), beta=np.zeros((B, T, H), np.float32))
+    st = st0.clone()
+    ops.scan(d, _prod_dev(p1), None, st)
+    assert torch.equal(st, st0)
+    p2 = dict(prod, v=v, beta=np.ones((B, T, H), np.float32),
+              wt_w=np.ones((B, T, H, 1), np.float32), wt_r=np.ones((B, T, H, 1), np.float32),
+              idx_r=prod["idx_w"].copy())
+    st = st0.clone()
+    _, y = ops.scan(d, _prod_dev(p2), None, st, with_y_raw=True)
+    torch.cuda.synchronize()
+    vb = torch.from_numpy(v).to(torch.bfloat16)
+    assert torch.equal(torch.from_numpy(host(y)), vb.to(torch.float32)), "reads of v"
+    stc = st.cpu()
+    for b in range(B):
+        for h in range(H):
+            last = {int(p2["idx_w"][b, t, h, 0]): t for t in range(T)}
+            for s_, t in last.items():
+                assert torch.equal(stc[b, h, s_], vb[b, t, h]), (b, h, s_, t)
+
+
+def test_bf16_state_forward_matches_scan_and_halves_nothing_else():
+    """sdm_forward with a bf16 state: same products as with fp32, the scan of them
+    equals sdm_scan with the same flags bit for bit."""
+    wl = synth.small("layer1p4b", B=2, T=160, d_model=256, n=40, W=16, R=16, d_v=32)
+    h, dd = layer_inputs(wl, seed=3)
+    d32, dbf = dims_for(wl), dims_for(wl)
+    dbf.flags = _lib.SDM_FLAG_STATE_BF16
+    m0b = dd["m0"].to(torch.bfloat16)
+    st_f = broadcast_state(m0b, wl.B)
+    out_f, p_f = ops.forward(dbf, dd["x"], dd["w_proj"], dd["A"], dd["b_dt"], dd["gamma"], st_f,
+                             debug=True)
+    st_32 = broadcast_state(dd["m0"], wl.B)
+    _, p_32 = ops.forward(d32, dd["x"], dd["w_proj"], dd["A"], dd["b_dt"], dd["gamma"], st_32,
+                          debug=True)
+    st_s = broadcast_state(m0b, wl.B)
+    out_s = ops.scan(dbf, p_f, dd["gamma"], st_s)
+    torch.cuda.synchronize()
+    for k in ("idx_w", "idx_r", "wt_w", "v", "alpha"):
+        assert torch.equal(p_f[k], p_32[k]), k
+    assert torch.equal(st_f, st_s)
+    assert_close(host(out_f), host(out_s), "forward vs scan", rtol=1e-5, atol=1e-6)
 
 
 # ---------------------------------------------------------------------------

@@ -75,6 +75,36 @@ def _walk_check(wl, h, p, state, out, walks, m0):
         say(f"  walk {(b, hh)}: {untouched.size} slots never written")
 
 
+def test_layer1p4b_full_size_bf16_state():
+    """The same layer with the state stored in bf16 (SDM_FLAG_STATE_BF16): two whole
+    walks against the oracle's bf16 scan run from the GPU's selection."""
+    from tests.gpu_util import check_bf16_reads, check_bf16_state
+    wl = synth.WORKLOADS["layer1p4b"]
+    h, d = layer_inputs(wl, seed=0)
+    dm = dims_for(wl)
+    dm.flags = _lib.SDM_FLAG_STATE_BF16
+    m0b = d["m0"].to(torch.bfloat16)
+    m0h = m0b.to(torch.float64).cpu().numpy()
+    state = broadcast_state(m0b, wl.B)
+    p = ops.select(dm, d["x"], d["w_proj"], d["A"], d["b_dt"])
+    out, y = ops.scan(dm, p, d["gamma"], state, with_y_raw=True)
+    torch.cuda.synchronize()
+    for b, hh in [(0, 0), (wl.B - 1, wl.H - 1)]:
+        sel = {k: host(p[k][b, :, hh]) for k in ("idx_w", "wt_w", "idx_r", "wt_r", "v", "gate",
+                                                  "alpha", "beta")}
+        sel["g"] = sel.pop("gate")
+        o_out, o_y, o_M = O.forward_walk(m0h[hh], sel, h["gamma"][hh], wl.eps, state="bf16")
+        st = state[b, hh].to(torch.float64).cpu().numpy()
+        scale = max(np.abs(o_M).max(), np.abs(m0h[hh]).max())
+        flips = check_bf16_state(st, o_M, scale, f"state walk {(b, hh)}")
+        late = check_bf16_reads(host(y[b, :, hh]), o_y, host(out[b, :, hh]), h["gamma"][hh],
+                                sel["g"], wl.eps, scale, wl.R, f"walk {(b, hh)}")
+        untouched = np.setdiff1d(np.arange(wl.N), sel["idx_w"].ravel())
+        assert np.array_equal(st[untouched], m0h[hh][untouched]), "unwritten rows changed"
+        say(f"  walk {(b, hh)}: {flips} state elements one rounding step apart, "
+            f"{late} tokens with such reads")
+
+
 def test_layer1p4b_full_size_as_benchmarked():
     wl = synth.WORKLOADS["layer1p4b"]
     h, d = layer_inputs(wl, seed=0)
