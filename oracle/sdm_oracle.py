@@ -263,6 +263,23 @@ def round_bf16(x):
 
 
 # ----------------------------------------------------------------------------
+# Slot-update histogram: the collapse monitor of the papers.ananclaw.com summary
+# (engineering-risks section, risk 3 "寻址坍缩"): how often each slot of each
+# head's memory is written, so that updates piling onto a few slots show up.
+# ----------------------------------------------------------------------------
+def slot_update_counts(idx_w, N: int):
+    """idx_w [B, T, H, W] write ids -> counts [H, N]: for each head and slot, the
+    number of (b, t) whose write set contains the slot."""
+    idx_w = np.asarray(idx_w)
+    B, T, H, W = idx_w.shape
+    counts = np.zeros((H, N), np.int64)
+    for h in range(H):
+        ids = idx_w[:, :, h, :].reshape(-1)
+        counts[h] = np.bincount(ids, minlength=N)[:N]
+    return counts
+
+
+# ----------------------------------------------------------------------------
 # Step 4 (without the head-mixing projection): [rainbus] step 4 and
 # [analysis] "步骤 4": RMS-Norm of the read vector, then element-wise gating.
 # ----------------------------------------------------------------------------
