@@ -237,6 +237,19 @@ SDM_API int32_t sdm_forward(const sdm_dims* dims, const void* x, const void* w_p
                     const sdm_sel* debug, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Slot-update histogram (monitoring; not a step of the layer): the papers.ananclaw.com
+ * summary (engineering-risks section, risk 3) watches how often each slot is updated
+ * to catch writes collapsing onto a few slots.
+ *   idx_w   [B, T, H, W] int32 write ids, as sdm_select returns them
+ *   counts  [H, N] int32, IN/OUT: counts[h][i] += the number of (b, t) whose write set
+ *           of head h holds slot i.  It accumulates over calls (clear it to start
+ *           over); a count wraps past 2^31 - 1.  Ids outside [0, N) are not counted.
+ * Exact: integer adds, independent of their order.
+ */
+SDM_API int32_t sdm_slot_histogram(const sdm_dims* dims, const int32_t* idx_w, int32_t* counts,
+                                   void* stream);
+
+/*
  * Kernel durations recorded by calls made with SDM_FLAG_TIMING (instrumentation;
  * not a step of the method).  Fills out[0..k) with the oldest k records (k <= max),
  * waiting for each to complete, removes them from the record and returns k; 0 when

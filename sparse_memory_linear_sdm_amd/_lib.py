@@ -26,7 +26,8 @@ SDM_FLAG_DELTA_GDN = 16
 SDM_FLAG_STATE_BF16 = 32
 
 EXPORTS = ("sdm_abi_version", "sdm_status_string", "sdm_workspace_bytes", "sdm_select",
-           "sdm_select_from_scores", "sdm_scan", "sdm_forward", "sdm_timing_read")
+           "sdm_select_from_scores", "sdm_scan", "sdm_forward", "sdm_slot_histogram",
+           "sdm_timing_read")
 
 
 class SdmDims(ctypes.Structure):
@@ -80,6 +81,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                 ctypes.c_size_t, VP]
     lib.sdm_timing_read.restype = I32
     lib.sdm_timing_read.argtypes = [P(SdmKernelTime), I32]
+    lib.sdm_slot_histogram.restype = I32
+    lib.sdm_slot_histogram.argtypes = [P(SdmDims), VP, VP, VP]
     del I64
     _lib = lib
     return lib
@@ -149,6 +152,10 @@ def sdm_forward(d: SdmDims, x, w_proj, A, b_dt, norm_w, state, out, debug: SdmSe
                               _ptr(norm_w), _ptr(state), _ptr(out),
                               ctypes.byref(debug) if debug is not None else None, _ptr(ws),
                               ws_bytes, _stream(stream)))
+
+
+def sdm_slot_histogram(d: SdmDims, idx_w, counts, stream=None):
+    _check(load().sdm_slot_histogram(ctypes.byref(d), _ptr(idx_w), _ptr(counts), _stream(stream)))
 
 
 def timing_read(max_records: int = 4096) -> list:

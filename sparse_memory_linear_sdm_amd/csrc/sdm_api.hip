@@ -262,6 +262,19 @@ int32_t sdm_scan(const sdm_dims* d, const sdm_sel* in, const float* norm_w, void
   return run_scan(d, dv, in, norm_w, state, out, y_raw, ws, ws_bytes, (hipStream_t)stream);
 }
 
+int32_t sdm_slot_histogram(const sdm_dims* d, const int32_t* idx_w, int32_t* counts,
+                           void* stream) {
+  Derived dv;
+  int32_t st = check_dims(d, &dv);
+  if (st != SDM_OK) return st;
+  if (dv.M == 0) return SDM_OK;
+  if (!idx_w || !counts) return SDM_ERR_NULL;
+  if (!aligned16(idx_w) || !aligned16(counts)) return SDM_ERR_ALIGN;
+  TimingScope timing(d);
+  (void)hipGetLastError();
+  return hip_status(launch_slot_histogram(*d, dv.N, idx_w, counts, (hipStream_t)stream));
+}
+
 int32_t sdm_forward(const sdm_dims* d, const void* x, const void* w_proj, const float* A,
                     const float* b_dt, const float* norm_w, void* state, float* out,
                     const sdm_sel* debug, void* ws, size_t ws_bytes, void* stream) {

@@ -110,6 +110,10 @@ size_t stream_workspace_bytes(const sdm_dims& d, const StreamPlan& pl);
 hipError_t launch_stream_scan(const ScanArgs& a, const StreamPlan& pl, void* ws, hipStream_t s);
 bool scan_uses_stream(const sdm_dims& d);
 
+// Slot-update histogram (monitor.hip): counts[h][id] += 1 for every write id.
+hipError_t launch_slot_histogram(const sdm_dims& d, int64_t N, const int32_t* idx_w,
+                                 int32_t* counts, hipStream_t s);
+
 // State element storage of the scan kernels: fp32, or bf16 (SDM_FLAG_STATE_BF16)
 // with fp32 arithmetic.  A lane moves 4 consecutive elements of a row: one 16-byte
 // (fp32) or 8-byte (bf16) access.  state_round returns a value as it will be stored

@@ -122,3 +122,14 @@ def forward(d: SdmDims, x, w_proj, A, b_dt, norm_w, state, debug=False, with_sco
     _lib.sdm_forward(d, x, w_proj, A, b_dt, norm_w, state, o, _sel(prod) if prod else None, ws,
                      nb, stream)
     return (o, prod) if debug else o
+
+
+def slot_histogram(d: SdmDims, idx_w, counts=None, stream=None):
+    """Per-head slot-update counts [H, N] int32; accumulates into `counts` if given."""
+    _need(idx_w, torch.int32, (d.B, d.T, d.H, d.W), "idx_w")
+    N = d.n * d.n
+    if counts is None:
+        counts = torch.zeros((d.H, N), dtype=torch.int32, device=idx_w.device)
+    _need(counts, torch.int32, (d.H, N), "counts")
+    _lib.sdm_slot_histogram(d, idx_w, counts, stream)
+    return counts
