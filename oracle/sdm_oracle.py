@@ -342,6 +342,26 @@ def forward_walk(state0, sel, gamma_h, eps, rule: str = "slot", state: str = "ex
     return rms_norm_gate(y, gamma_h, sel["g"], eps), y, M
 
 
+# ----------------------------------------------------------------------------
+# Shared learned initial state ([analysis] section on the learned M0: M0 is a
+# parameter of the layer, the same for every sequence; [163] section 三).  A
+# sequence's memory starts as M0; a per-sequence store keeps only the rows that
+# have been touched.  Effective state of slot i: store[i] if touched[i] else
+# M0[i].  A call touches every slot it reads or writes.
+# ----------------------------------------------------------------------------
+def forward_walk_shared(m0_h, store_h, touched_h, sel, gamma_h, eps, rule="slot",
+                        state="exact"):
+    """forward_walk on the effective state of one walk.  Returns (out, y_raw,
+    final effective state [N, d_v], touched after the call [N] bool)."""
+    touched_h = np.asarray(touched_h, bool)
+    m_init = np.where(touched_h[:, None], np.asarray(store_h, F64), np.asarray(m0_h, F64))
+    out, y, M = forward_walk(m_init, sel, gamma_h, eps, rule, state)
+    touched = touched_h.copy()
+    touched[np.asarray(sel["idx_w"]).ravel()] = True
+    touched[np.asarray(sel["idx_r"]).ravel()] = True
+    return out, y, M, touched
+
+
 def forward(x, w_proj, A, b_dt, gamma, state0, H, n, d_v, W, R, eps=1e-6,
             gate_act=GATE_SIGMOID):
     """Full path from x [B, T, d] and state0 [B, H, N, d_v].
