@@ -64,6 +64,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
         part.z = fmaf(w, m.z, part.z);
         part.w = fmaf(w, m.w, part.w);
       }
+      __syncthreads();  // group 0 may still be summing the previous token's reads from red
       red[grp][li] = part;
       __syncthreads();
       float4 pred = red[0][li];

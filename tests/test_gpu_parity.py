@@ -183,6 +183,29 @@ def test_stage_c_gdn_variant(B, T, H, n, W, R, d_v, mode):
         assert np.max(np.abs(slot[(b, h)][2] - ref[(b, h)][2])) > 1e-6
 
 
+@pytest.mark.parametrize("flags", [0, _lib.SDM_FLAG_DELTA_GDN, _lib.SDM_FLAG_STATE_BF16,
+                                   _lib.SDM_FLAG_DELTA_GDN | _lib.SDM_FLAG_STATE_BF16])
+def test_direct_schedule_is_deterministic(flags):
+    """The direct schedule sums in a fixed order (no atomics): repeated runs agree bit
+    for bit in state, y and out -- which also shows the LDS partial sums of one
+    token are never overwritten by the next token's before they are read."""
+    rng = np.random.default_rng(9)
+    B, T, H, n, W, R, d_v = 2, 200, 2, 20, 16, 16, 64
+    prod = _prod_dev(random_products(rng, B, T, H, n, W, R, d_v, "repeat"))
+    m0 = torch.from_numpy((rng.standard_normal((B, H, n * n, d_v)) * 0.02).astype(np.float32))
+    m0 = m0.to(torch.bfloat16 if flags & _lib.SDM_FLAG_STATE_BF16 else torch.float32).cuda()
+    d = _dims(B=B, T=T, H=H, n=n, W=W, R=R, d_v=d_v, flags=_lib.SDM_FLAG_SCAN_DIRECT | flags)
+    runs = []
+    for _ in range(3):
+        st = m0.clone()
+        out, y = ops.scan(d, prod, None, st, with_y_raw=True)
+        runs.append((st, out, y))
+    torch.cuda.synchronize()
+    for st, out, y in runs[1:]:
+        assert torch.equal(st, runs[0][0]) and torch.equal(y, runs[0][2])
+        assert torch.equal(out, runs[0][1])
+
+
 @pytest.mark.parametrize("schedule", ["direct", "stream", "two_phase"])
 def test_stage_c_identity_and_overwrite_exact(schedule):
     rng = np.random.default_rng(7)
