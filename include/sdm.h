@@ -237,6 +237,31 @@ SDM_API int32_t sdm_forward(const sdm_dims* dims, const void* x, const void* w_p
                     const sdm_sel* debug, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Shared learned initial state, copied into a sequence's store on first touch.  M0 is
+ * one parameter of the layer, the same for every sequence ([analysis] section on the
+ * learned M0; m.163.com article on arXiv 2607.07386, section 三), so a batch need not
+ * carry B copies of it: the store holds only the rows each sequence has touched.
+ * The effective state of (b, h) slot i is state[b][h][i] if bit i of touched[b][h] is
+ * set, else m0[h][i].  Results equal sdm_scan / sdm_forward run on the effective state
+ * (bit for bit: the same kernels run on the same values).
+ *   m0       [H, N, d_v] fp32 (bf16 with SDM_FLAG_STATE_BF16), read only
+ *   state    [B, H, N, d_v] same type, IN/OUT: only rows whose bit is set are read; the
+ *            call writes rows it touches and no others
+ *   touched  [B, H, ceil(N/32)] uint32 bitmaps (bit i of word i/32), IN/OUT: the call
+ *            sets the bit of every slot it reads or writes.  All zero starts every
+ *            sequence from M0 without initialising `state`.
+ * Other arguments as in sdm_scan / sdm_forward (same workspace sizes).  Ids must lie
+ * in [0, N) (as sdm_select returns them).
+ */
+SDM_API int32_t sdm_scan_shared_m0(const sdm_dims* dims, const sdm_sel* in, const float* norm_w,
+                                   const void* m0, void* state, uint32_t* touched, float* out,
+                                   float* y_raw, void* ws, size_t ws_bytes, void* stream);
+SDM_API int32_t sdm_forward_shared_m0(const sdm_dims* dims, const void* x, const void* w_proj,
+                                      const float* A, const float* b_dt, const float* norm_w,
+                                      const void* m0, void* state, uint32_t* touched, float* out,
+                                      void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Slot-update histogram (monitoring; not a step of the layer): the papers.ananclaw.com
  * summary (engineering-risks section, risk 3) watches how often each slot is updated
  * to catch writes collapsing onto a few slots.

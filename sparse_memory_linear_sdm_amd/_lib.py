@@ -26,8 +26,8 @@ SDM_FLAG_DELTA_GDN = 16
 SDM_FLAG_STATE_BF16 = 32
 
 EXPORTS = ("sdm_abi_version", "sdm_status_string", "sdm_workspace_bytes", "sdm_select",
-           "sdm_select_from_scores", "sdm_scan", "sdm_forward", "sdm_slot_histogram",
-           "sdm_timing_read")
+           "sdm_select_from_scores", "sdm_scan", "sdm_forward", "sdm_scan_shared_m0",
+           "sdm_forward_shared_m0", "sdm_slot_histogram", "sdm_timing_read")
 
 
 class SdmDims(ctypes.Structure):
@@ -81,6 +81,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                 ctypes.c_size_t, VP]
     lib.sdm_timing_read.restype = I32
     lib.sdm_timing_read.argtypes = [P(SdmKernelTime), I32]
+    lib.sdm_scan_shared_m0.restype = I32
+    lib.sdm_scan_shared_m0.argtypes = [P(SdmDims), P(SdmSel), VP, VP, VP, VP, VP, VP, VP,
+                                       ctypes.c_size_t, VP]
+    lib.sdm_forward_shared_m0.restype = I32
+    lib.sdm_forward_shared_m0.argtypes = [P(SdmDims), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP,
+                                          ctypes.c_size_t, VP]
     lib.sdm_slot_histogram.restype = I32
     lib.sdm_slot_histogram.argtypes = [P(SdmDims), VP, VP, VP]
     del I64
@@ -152,6 +158,21 @@ def sdm_forward(d: SdmDims, x, w_proj, A, b_dt, norm_w, state, out, debug: SdmSe
                               _ptr(norm_w), _ptr(state), _ptr(out),
                               ctypes.byref(debug) if debug is not None else None, _ptr(ws),
                               ws_bytes, _stream(stream)))
+
+
+def sdm_scan_shared_m0(d: SdmDims, inp: SdmSel, norm_w, m0, state, touched, out, y_raw=None,
+                       ws=None, ws_bytes=0, stream=None):
+    _check(load().sdm_scan_shared_m0(ctypes.byref(d), ctypes.byref(inp), _ptr(norm_w), _ptr(m0),
+                                     _ptr(state), _ptr(touched), _ptr(out), _ptr(y_raw), _ptr(ws),
+                                     ws_bytes, _stream(stream)))
+
+
+def sdm_forward_shared_m0(d: SdmDims, x, w_proj, A, b_dt, norm_w, m0, state, touched, out,
+                          ws=None, ws_bytes=0, stream=None):
+    _check(load().sdm_forward_shared_m0(ctypes.byref(d), _ptr(x), _ptr(w_proj), _ptr(A),
+                                        _ptr(b_dt), _ptr(norm_w), _ptr(m0), _ptr(state),
+                                        _ptr(touched), _ptr(out), _ptr(ws), ws_bytes,
+                                        _stream(stream)))
 
 
 def sdm_slot_histogram(d: SdmDims, idx_w, counts, stream=None):

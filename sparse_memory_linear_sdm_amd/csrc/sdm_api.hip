@@ -176,6 +176,82 @@ struct TimingScope {
   ~TimingScope() { timing_enable(prev); }
 };
 
+// sdm_scan, and with m0 / touched the shared-initial-state form.
+int32_t scan_entry(const sdm_dims* d, const sdm_sel* in, const float* norm_w, const void* m0,
+                   void* state, uint32_t* touched, float* out, float* y_raw, void* ws,
+                   size_t ws_bytes, void* stream, bool shared) {
+  Derived dv;
+  int32_t st = check_dims(d, &dv);
+  if (st != SDM_OK) return st;
+  if (dv.M == 0) return SDM_OK;
+  if ((st = check_sel(in, false)) != SDM_OK) return st;
+  if (!state || !out || (shared && (!m0 || !touched))) return SDM_ERR_NULL;
+  if (!aligned16(state) || !aligned16(out) || (y_raw && !aligned16(y_raw)) ||
+      (norm_w && !aligned16(norm_w)) || (m0 && !aligned16(m0)) ||
+      (touched && !aligned16(touched)))
+    return SDM_ERR_ALIGN;
+  const size_t need = align_up(scan_workspace_bytes(*d));
+  if (need && (!ws || ws_bytes < need)) return SDM_ERR_WORKSPACE;
+  TimingScope timing(d);
+  (void)hipGetLastError();
+  if (m0 && launch_materialize(*d, dv.N, in->idx_w, in->idx_r, m0, state, touched,
+                               (hipStream_t)stream) != hipSuccess)
+    return SDM_ERR_HIP;
+  return run_scan(d, dv, in, norm_w, state, out, y_raw, ws, ws_bytes, (hipStream_t)stream);
+}
+
+// sdm_forward, and with m0 / touched the shared-initial-state form.
+int32_t forward_entry(const sdm_dims* d, const void* x, const void* w_proj, const float* A,
+                      const float* b_dt, const float* norm_w, const void* m0, void* state,
+                      uint32_t* touched, float* out, const sdm_sel* debug, void* ws,
+                      size_t ws_bytes, void* stream, bool shared) {
+  Derived dv;
+  int32_t st = check_dims(d, &dv);
+  if (st != SDM_OK) return st;
+  if (dv.M == 0) return SDM_OK;
+  if (!x || !w_proj || !A || !b_dt || !state || !out || (shared && (!m0 || !touched)))
+    return SDM_ERR_NULL;
+  if (debug && (st = check_sel(debug, false)) != SDM_OK) return st;
+  if (!aligned16(x) || !aligned16(w_proj) || !aligned16(A) || !aligned16(b_dt) ||
+      !aligned16(state) || !aligned16(out) || (norm_w && !aligned16(norm_w)) ||
+      (m0 && !aligned16(m0)) || (touched && !aligned16(touched)))
+    return SDM_ERR_ALIGN;
+  const ProductSizes ps = product_sizes(d, dv.M);
+  const size_t sel_ws = select_ws_bytes(d, dv, false);
+  const size_t scan_ws = align_up(scan_workspace_bytes(*d));
+  const size_t need = ps.total + sel_ws + scan_ws;
+  if (!ws || ws_bytes < need) return SDM_ERR_WORKSPACE;
+  if (!aligned16(ws)) return SDM_ERR_ALIGN;
+
+  char* base = static_cast<char*>(ws);
+  sdm_sel prod;
+  if (debug) {
+    prod = *debug;
+  } else {
+    char* p = base;
+    prod.idx_w = reinterpret_cast<int32_t*>(p); p += ps.idx_w;
+    prod.wt_w = reinterpret_cast<float*>(p); p += ps.wt_w;
+    prod.idx_r = reinterpret_cast<int32_t*>(p); p += ps.idx_r;
+    prod.wt_r = reinterpret_cast<float*>(p); p += ps.wt_r;
+    prod.v = reinterpret_cast<float*>(p); p += ps.v;
+    prod.gate = reinterpret_cast<float*>(p); p += ps.gate;
+    prod.alpha = reinterpret_cast<float*>(p); p += ps.alpha;
+    prod.beta = reinterpret_cast<float*>(p); p += ps.beta;
+    prod.scores = nullptr;
+  }
+  void* sel_space = base + ps.total;
+  void* scan_space = base + ps.total + sel_ws;
+  hipStream_t s = (hipStream_t)stream;
+  TimingScope timing(d);
+  (void)hipGetLastError();
+  st = run_select(d, dv, x, w_proj, A, b_dt, &prod, sel_space, s);
+  if (st != SDM_OK) return st;
+  if (m0 && launch_materialize(*d, dv.N, prod.idx_w, prod.idx_r, m0, state, touched, s) !=
+                hipSuccess)
+    return SDM_ERR_HIP;
+  return run_scan(d, dv, &prod, norm_w, state, out, nullptr, scan_space, scan_ws, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -246,20 +322,14 @@ int32_t sdm_select_from_scores(const sdm_dims* d, const float* scores, int32_t* 
 
 int32_t sdm_scan(const sdm_dims* d, const sdm_sel* in, const float* norm_w, void* state,
                  float* out, float* y_raw, void* ws, size_t ws_bytes, void* stream) {
-  Derived dv;
-  int32_t st = check_dims(d, &dv);
-  if (st != SDM_OK) return st;
-  if (dv.M == 0) return SDM_OK;
-  if ((st = check_sel(in, false)) != SDM_OK) return st;
-  if (!state || !out) return SDM_ERR_NULL;
-  if (!aligned16(state) || !aligned16(out) || (y_raw && !aligned16(y_raw)) ||
-      (norm_w && !aligned16(norm_w)))
-    return SDM_ERR_ALIGN;
-  const size_t need = align_up(scan_workspace_bytes(*d));
-  if (need && (!ws || ws_bytes < need)) return SDM_ERR_WORKSPACE;
-  TimingScope timing(d);
-  (void)hipGetLastError();
-  return run_scan(d, dv, in, norm_w, state, out, y_raw, ws, ws_bytes, (hipStream_t)stream);
+  return scan_entry(d, in, norm_w, nullptr, state, nullptr, out, y_raw, ws, ws_bytes, stream,
+                    false);
+}
+
+int32_t sdm_scan_shared_m0(const sdm_dims* d, const sdm_sel* in, const float* norm_w,
+                           const void* m0, void* state, uint32_t* touched, float* out,
+                           float* y_raw, void* ws, size_t ws_bytes, void* stream) {
+  return scan_entry(d, in, norm_w, m0, state, touched, out, y_raw, ws, ws_bytes, stream, true);
 }
 
 int32_t sdm_slot_histogram(const sdm_dims* d, const int32_t* idx_w, int32_t* counts,
@@ -278,46 +348,16 @@ int32_t sdm_slot_histogram(const sdm_dims* d, const int32_t* idx_w, int32_t* cou
 int32_t sdm_forward(const sdm_dims* d, const void* x, const void* w_proj, const float* A,
                     const float* b_dt, const float* norm_w, void* state, float* out,
                     const sdm_sel* debug, void* ws, size_t ws_bytes, void* stream) {
-  Derived dv;
-  int32_t st = check_dims(d, &dv);
-  if (st != SDM_OK) return st;
-  if (dv.M == 0) return SDM_OK;
-  if (!x || !w_proj || !A || !b_dt || !state || !out) return SDM_ERR_NULL;
-  if (debug && (st = check_sel(debug, false)) != SDM_OK) return st;
-  if (!aligned16(x) || !aligned16(w_proj) || !aligned16(A) || !aligned16(b_dt) ||
-      !aligned16(state) || !aligned16(out) || (norm_w && !aligned16(norm_w)))
-    return SDM_ERR_ALIGN;
-  const ProductSizes ps = product_sizes(d, dv.M);
-  const size_t sel_ws = select_ws_bytes(d, dv, false);
-  const size_t scan_ws = align_up(scan_workspace_bytes(*d));
-  const size_t need = ps.total + sel_ws + scan_ws;
-  if (!ws || ws_bytes < need) return SDM_ERR_WORKSPACE;
-  if (!aligned16(ws)) return SDM_ERR_ALIGN;
+  return forward_entry(d, x, w_proj, A, b_dt, norm_w, nullptr, state, nullptr, out, debug, ws,
+                       ws_bytes, stream, false);
+}
 
-  char* base = static_cast<char*>(ws);
-  sdm_sel prod;
-  if (debug) {
-    prod = *debug;
-  } else {
-    char* p = base;
-    prod.idx_w = reinterpret_cast<int32_t*>(p); p += ps.idx_w;
-    prod.wt_w = reinterpret_cast<float*>(p); p += ps.wt_w;
-    prod.idx_r = reinterpret_cast<int32_t*>(p); p += ps.idx_r;
-    prod.wt_r = reinterpret_cast<float*>(p); p += ps.wt_r;
-    prod.v = reinterpret_cast<float*>(p); p += ps.v;
-    prod.gate = reinterpret_cast<float*>(p); p += ps.gate;
-    prod.alpha = reinterpret_cast<float*>(p); p += ps.alpha;
-    prod.beta = reinterpret_cast<float*>(p); p += ps.beta;
-    prod.scores = nullptr;
-  }
-  void* sel_space = base + ps.total;
-  void* scan_space = base + ps.total + sel_ws;
-  hipStream_t s = (hipStream_t)stream;
-  TimingScope timing(d);
-  (void)hipGetLastError();
-  st = run_select(d, dv, x, w_proj, A, b_dt, &prod, sel_space, s);
-  if (st != SDM_OK) return st;
-  return run_scan(d, dv, &prod, norm_w, state, out, nullptr, scan_space, scan_ws, s);
+int32_t sdm_forward_shared_m0(const sdm_dims* d, const void* x, const void* w_proj,
+                              const float* A, const float* b_dt, const float* norm_w,
+                              const void* m0, void* state, uint32_t* touched, float* out,
+                              void* ws, size_t ws_bytes, void* stream) {
+  return forward_entry(d, x, w_proj, A, b_dt, norm_w, m0, state, touched, out, nullptr, ws,
+                       ws_bytes, stream, true);
 }
 
 }  // extern "C"

@@ -110,6 +110,12 @@ size_t stream_workspace_bytes(const sdm_dims& d, const StreamPlan& pl);
 hipError_t launch_stream_scan(const ScanArgs& a, const StreamPlan& pl, void* ws, hipStream_t s);
 bool scan_uses_stream(const sdm_dims& d);
 
+// Shared initial state (shared_m0.hip): set the touched bit of every id the call
+// reads or writes; copy M0[h][id] into the store on the first touch.
+hipError_t launch_materialize(const sdm_dims& d, int64_t N, const int32_t* idx_w,
+                              const int32_t* idx_r, const void* m0, void* store,
+                              uint32_t* touched, hipStream_t s);
+
 // Slot-update histogram (monitor.hip): counts[h][id] += 1 for every write id.
 hipError_t launch_slot_histogram(const sdm_dims& d, int64_t N, const int32_t* idx_w,
                                  int32_t* counts, hipStream_t s);

@@ -124,6 +124,48 @@ def forward(d: SdmDims, x, w_proj, A, b_dt, norm_w, state, debug=False, with_sco
     return (o, prod) if debug else o
 
 
+def alloc_touched(d: SdmDims, device):
+    """All-zero touched bitmaps [B, H, ceil(N/32)] (int32 words): every sequence at M0."""
+    return torch.zeros((d.B, d.H, (d.n * d.n + 31) // 32), dtype=torch.int32, device=device)
+
+
+def _check_shared(d: SdmDims, m0, state, touched):
+    N = d.n * d.n
+    _need(m0, state_dtype(d), (d.H, N, d.d_v), "m0")
+    _need(state, state_dtype(d), (d.B, d.H, N, d.d_v), "state")
+    _need(touched, torch.int32, (d.B, d.H, (N + 31) // 32), "touched")
+
+
+def scan_shared_m0(d: SdmDims, products: dict, norm_w, m0, state, touched, with_y_raw=False,
+                   out=None, ws=None, stream=None):
+    """scan() on the effective state (store rows whose touched bit is set, else m0)."""
+    _check_products(d, products)
+    _check_shared(d, m0, state, touched)
+    if norm_w is not None:
+        _need(norm_w, torch.float32, (d.H, d.d_v), "norm_w")
+    o = out if out is not None else torch.empty((d.B, d.T, d.H, d.d_v), device=state.device)
+    _need(o, torch.float32, (d.B, d.T, d.H, d.d_v), "out")
+    y = torch.empty_like(o) if with_y_raw else None
+    ws, nb = _workspace(d, _lib.SDM_ENTRY_SCAN, state.device, ws)
+    _lib.sdm_scan_shared_m0(d, _sel(products), norm_w, m0, state, touched, o, y, ws, nb, stream)
+    return (o, y) if with_y_raw else o
+
+
+def forward_shared_m0(d: SdmDims, x, w_proj, A, b_dt, norm_w, m0, state, touched, out=None,
+                      ws=None, stream=None):
+    """forward() on the effective state; state and touched are updated in place."""
+    _check_params(d, x, w_proj, A, b_dt)
+    _check_shared(d, m0, state, touched)
+    if norm_w is not None:
+        _need(norm_w, torch.float32, (d.H, d.d_v), "norm_w")
+    o = out if out is not None else torch.empty((d.B, d.T, d.H, d.d_v), device=x.device)
+    _need(o, torch.float32, (d.B, d.T, d.H, d.d_v), "out")
+    ws, nb = _workspace(d, _lib.SDM_ENTRY_FORWARD, x.device, ws)
+    _lib.sdm_forward_shared_m0(d, x, w_proj, A, b_dt, norm_w, m0, state, touched, o, ws, nb,
+                               stream)
+    return o
+
+
 def slot_histogram(d: SdmDims, idx_w, counts=None, stream=None):
     """Per-head slot-update counts [H, N] int32; accumulates into `counts` if given."""
     _need(idx_w, torch.int32, (d.B, d.T, d.H, d.W), "idx_w")

@@ -122,6 +122,25 @@ def test_bf16_state_flag_is_accepted_everywhere(lib):
     assert _select(lib, d) == _lib.SDM_ERR_UNSUPPORTED
 
 
+def test_shared_m0_entries_validate_first(lib):
+    d = _d(T=64)
+    s = _sel()
+    # sdm_scan_shared_m0(dims, in, norm_w, m0, state, touched, out, y_raw, ws, ws_bytes, stream)
+    scan = lambda m0=FAKE, st=FAKE, tch=FAKE, dd=d: lib.sdm_scan_shared_m0(
+        ctypes.byref(dd), ctypes.byref(s), None, m0, st, tch, FAKE, None, FAKE, 1 << 40, None)
+    assert scan(m0=None) == _lib.SDM_ERR_NULL
+    assert scan(tch=None) == _lib.SDM_ERR_NULL
+    assert scan(tch=FAKE + 4) == _lib.SDM_ERR_ALIGN
+    assert scan(m0=FAKE + 8) == _lib.SDM_ERR_ALIGN
+    assert scan(m0=None, dd=_d(T=0)) == _lib.SDM_OK          # empty call: nothing to do
+    assert scan(dd=_d(H=0)) == _lib.SDM_ERR_SHAPE
+    fwd = lambda m0=FAKE, tch=FAKE, dd=d: lib.sdm_forward_shared_m0(
+        ctypes.byref(dd), FAKE, FAKE, FAKE, FAKE, None, m0, FAKE, tch, FAKE, FAKE, 1 << 40, None)
+    assert fwd(m0=None) == _lib.SDM_ERR_NULL
+    assert fwd(tch=FAKE + 2) == _lib.SDM_ERR_ALIGN
+    assert fwd(tch=None, dd=_d(B=0)) == _lib.SDM_OK
+
+
 def test_null_dims(lib):
     assert lib.sdm_select(None, FAKE, FAKE, FAKE, FAKE, None, FAKE, 0, None) == _lib.SDM_ERR_NULL
     assert lib.sdm_workspace_bytes(None, 0) == 0
