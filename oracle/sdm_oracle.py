@@ -177,7 +177,7 @@ def select(half1, half2, count: int):
 # [rainbus] step 3: y_t = sum_{i in I_r} q^(i) M_t[i]  (reads the state after
 # this token's write).
 # ----------------------------------------------------------------------------
-def scan(state0, idx_w, wt_w, idx_r, wt_r, v, alpha, beta, store=None):
+def scan(state0, idx_w, wt_w, idx_r, wt_r, v, alpha, beta, store=None, record=False):
     """Walk tokens in order over one memory.
 
     state0 [N, d_v]; idx_w/wt_w [T, W]; idx_r/wt_r [T, R]; v [T, d_v];
@@ -185,6 +185,8 @@ def scan(state0, idx_w, wt_w, idx_r, wt_r, v, alpha, beta, store=None):
     store: None (the state holds the exact values), or a rounding function applied
     to every written row, the state then holding only its results (round_bf16 for
     a bf16 state); state0 must then be representable already.
+    record: also return the rows each token overwrote, log [T, W, d_v] (the values
+    of M[idx_w[t]] just before token t's write), as a third result.
     """
     M = np.array(state0, dtype=F64, copy=True)
     keep = store if store is not None else (lambda z: z)
@@ -198,13 +200,16 @@ def scan(state0, idx_w, wt_w, idx_r, wt_r, v, alpha, beta, store=None):
     beta = np.asarray(beta, F64)
     T = idx_w.shape[0]
     y = np.zeros((T, M.shape[1]), F64)
+    log = np.zeros((T, idx_w.shape[1], M.shape[1]), F64) if record else None
     for t in range(T):
         rows = idx_w[t]
         assert np.unique(rows).size == rows.size, "write slots of one token must be distinct"
+        if record:
+            log[t] = M[rows]
         m_tilde = alpha[t] * M[rows]                                   # forget gate
         M[rows] = keep(m_tilde + (beta[t] * wt_w[t])[:, None] * (v[t][None, :] - m_tilde))
         y[t] = wt_r[t] @ M[idx_r[t]]                                   # sparse read
-    return y, M
+    return (y, M, log) if record else (y, M)
 
 
 # ----------------------------------------------------------------------------
@@ -340,6 +345,69 @@ def forward_walk(state0, sel, gamma_h, eps, rule: str = "slot", state: str = "ex
     y, M = walk(state0, sel["idx_w"], sel["wt_w"], sel["idx_r"], sel["wt_r"],
                 sel["v"], sel["alpha"], sel["beta"], store=store)
     return rms_norm_gate(y, gamma_h, sel["g"], eps), y, M
+
+
+# ----------------------------------------------------------------------------
+# Backward of the scan and the norm/gate (steps 2-4), reverse-mode by the chain
+# rule.  The training scheme of [163] section 八 (memory-efficiency paragraph):
+# the sparse update is applied in place and undone in backward, which needs the
+# N x d state plus the T x W x d rows the writes overwrote.  So the forward
+# records, per token, the rows before its write (scan(..., record=True)), and
+# the backward walks tokens in reverse: the read of token t first (it saw the
+# state after t's write), then the write, restoring the overwritten rows.
+# For one written row, with c = beta k and m the row before the write,
+#   M' = m~ + c (v - m~),  m~ = alpha m:
+#   dM'/dm = alpha (1 - c),  dM'/dv = c,  dM'/dc = v - alpha m,
+#   dM'/dalpha = (1 - c) m,  dc/dbeta = k,  dc/dk = beta.
+# For the read y = sum_r q_r M[r]: dq_r = <dy, M[r]>, dM[r] += q_r dy.
+# For out = y s gamma g with s = (mean(y^2) + eps)^(-1/2), u = d_out gamma g:
+#   dy = s (u - yhat mean(u yhat)),  yhat = y s;  d_gate = d_out yhat gamma;
+#   d_gamma = sum over tokens of d_out yhat g.
+# ----------------------------------------------------------------------------
+def scan_backward(state_T, log, idx_w, wt_w, idx_r, wt_r, v, alpha, beta, y, gate,
+                  gamma_h, eps, d_out, d_state):
+    """Gradients of one walk.
+
+    state_T [N, d_v] the state after the forward; log [T, W, d_v] from
+    scan(..., record=True); y [T, d_v] the forward's read vectors; d_out [T, d_v]
+    and d_state [N, d_v] (gradient of the final state) are the incoming gradients.
+    Returns (grads, state_0, d_state_0) with grads holding d_v, d_gate [T, d_v],
+    d_alpha, d_beta [T], d_wt_w [T, W], d_wt_r [T, R], d_gamma [d_v]; state_0 is the
+    restored initial state and d_state_0 the gradient of the initial state.
+    """
+    M = np.array(state_T, F64, copy=True)
+    dM = np.array(d_state, F64, copy=True)
+    idx_w, idx_r = np.asarray(idx_w), np.asarray(idx_r)
+    wt_w, wt_r = np.asarray(wt_w, F64), np.asarray(wt_r, F64)
+    v, y, gate = np.asarray(v, F64), np.asarray(y, F64), np.asarray(gate, F64)
+    alpha, beta = np.asarray(alpha, F64), np.asarray(beta, F64)
+    gamma_h, d_out, log = np.asarray(gamma_h, F64), np.asarray(d_out, F64), np.asarray(log, F64)
+    T, d_v = y.shape
+    g = dict(d_v=np.zeros((T, d_v)), d_gate=np.zeros((T, d_v)), d_alpha=np.zeros(T),
+             d_beta=np.zeros(T), d_wt_w=np.zeros(idx_w.shape), d_wt_r=np.zeros(idx_r.shape),
+             d_gamma=np.zeros(d_v))
+    for t in range(T - 1, -1, -1):
+        s = 1.0 / np.sqrt(np.mean(y[t] * y[t]) + eps)                # step 4
+        yhat = y[t] * s
+        g["d_gate"][t] = d_out[t] * yhat * gamma_h
+        g["d_gamma"] += d_out[t] * yhat * gate[t]
+        u = d_out[t] * gamma_h * gate[t]
+        dy = s * (u - yhat * np.mean(u * yhat))
+        rows = idx_r[t]                                              # step 3
+        g["d_wt_r"][t] = M[rows] @ dy
+        dM[rows] += wt_r[t][:, None] * dy[None, :]
+        rows = idx_w[t]                                              # step 2, undone
+        m = log[t]
+        c = beta[t] * wt_w[t]
+        G = dM[rows]
+        g["d_v"][t] = c @ G
+        dc = np.sum(G * (v[t][None, :] - alpha[t] * m), axis=1)
+        g["d_alpha"][t] = np.sum((1.0 - c)[:, None] * G * m)
+        g["d_beta"][t] = wt_w[t] @ dc
+        g["d_wt_w"][t] = beta[t] * dc
+        dM[rows] = (alpha[t] * (1.0 - c))[:, None] * G
+        M[rows] = m
+    return g, M, dM
 
 
 # ----------------------------------------------------------------------------
