@@ -74,6 +74,7 @@ extern "C" {
 #define SDM_ENTRY_SELECT 0
 #define SDM_ENTRY_SCAN 1
 #define SDM_ENTRY_FORWARD 2
+#define SDM_ENTRY_SCAN_BACKWARD 3
 
 /* scan schedule flags (sdm_dims.flags) */
 #define SDM_FLAG_SCAN_DIRECT 1    /* one workgroup per (b,h), tokens in lock-step */
@@ -235,6 +236,53 @@ SDM_API int32_t sdm_scan(const sdm_dims* dims, const sdm_sel* in, const float* n
 SDM_API int32_t sdm_forward(const sdm_dims* dims, const void* x, const void* w_proj, const float* A,
                     const float* b_dt, const float* norm_w, void* state, float* out,
                     const sdm_sel* debug, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Training (the m.163.com article on arXiv 2607.07386, section 八, memory-efficiency
+ * paragraph: the sparse update is applied in place and undone in backward, keeping
+ * the N x d state plus the T x W x d rows the writes overwrote).
+ *
+ * sdm_scan_train: sdm_scan (direct schedule) that also records the write log.
+ *   log     [B, T, H, W, d_v] fp32 OUT: log[b][t][h][k] = the state row idx_w[..][k]
+ *           just before token t's write
+ *   y_raw   required here (the backward needs it)
+ *   Other arguments as in sdm_scan; state, out and y_raw equal sdm_scan's with
+ *   SDM_FLAG_SCAN_DIRECT bit for bit.  fp32 state and the per-slot rule only:
+ *   SDM_FLAG_STATE_BF16, SDM_FLAG_DELTA_GDN, SDM_FLAG_SCAN_STREAM or
+ *   SDM_FLAG_SCAN_TWO_PHASE give SDM_ERR_UNSUPPORTED.  No workspace.
+ *
+ * sdm_scan_backward: gradients of that call, walking the tokens in reverse (per
+ * token: the norm and gate, the read, then the write, whose overwritten rows are
+ * restored from the log).
+ *   state   [B, H, N, d_v] IN: the state sdm_scan_train returned; OUT: the state it
+ *           started from, bit for bit
+ *   d_state [B, H, N, d_v] IN: gradient of the final state (zeros if the loss does
+ *           not see it); OUT: gradient of the initial state
+ *   y_raw, log   as sdm_scan_train wrote them; d_out [B, T, H, d_v] gradient of out
+ *   grads   outputs, overwritten: d_wt_w [B,T,H,W], d_wt_r [B,T,H,R], d_v and d_gate
+ *           [B,T,H,d_v], d_alpha and d_beta [B,T,H]; d_norm_w [H, d_v] (summed over
+ *           the batch) or NULL
+ *   ws      >= sdm_workspace_bytes(dims, SDM_ENTRY_SCAN_BACKWARD) bytes
+ * Every sum runs in a fixed order: results are bit-reproducible.  Flags as for
+ * sdm_scan_train.  One workgroup per (b, h), tokens in lock-step.
+ */
+typedef struct sdm_scan_grads {
+  float* d_wt_w;
+  float* d_wt_r;
+  float* d_v;
+  float* d_gate;
+  float* d_alpha;
+  float* d_beta;
+  float* d_norm_w;  /* nullable */
+} sdm_scan_grads;
+
+SDM_API int32_t sdm_scan_train(const sdm_dims* dims, const sdm_sel* in, const float* norm_w,
+                               float* state, float* out, float* y_raw, float* log, void* stream);
+SDM_API int32_t sdm_scan_backward(const sdm_dims* dims, const sdm_sel* in, const float* norm_w,
+                                  float* state, float* d_state, const float* y_raw,
+                                  const float* log, const float* d_out,
+                                  const sdm_scan_grads* grads, void* ws, size_t ws_bytes,
+                                  void* stream);
 
 /*
  * Shared learned initial state, copied into a sequence's store on first touch.  M0 is

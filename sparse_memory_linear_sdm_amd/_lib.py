@@ -18,7 +18,7 @@ SDM_ERR_NULL, SDM_ERR_SHAPE, SDM_ERR_DTYPE, SDM_ERR_ALIGN = -1, -2, -3, -4
 SDM_ERR_WORKSPACE, SDM_ERR_UNSUPPORTED, SDM_ERR_HIP = -5, -6, -7
 SDM_DTYPE_F32, SDM_DTYPE_BF16 = 0, 1
 SDM_GATE_NONE, SDM_GATE_SIGMOID, SDM_GATE_SILU = 0, 1, 2
-SDM_ENTRY_SELECT, SDM_ENTRY_SCAN, SDM_ENTRY_FORWARD = 0, 1, 2
+SDM_ENTRY_SELECT, SDM_ENTRY_SCAN, SDM_ENTRY_FORWARD, SDM_ENTRY_SCAN_BACKWARD = 0, 1, 2, 3
 SDM_MAX_COUNT, SDM_MAX_HALF = 128, 1024
 SDM_FLAG_SCAN_DIRECT, SDM_FLAG_SCAN_STREAM, SDM_FLAG_SCAN_TWO_PHASE = 1, 2, 4
 SDM_FLAG_TIMING = 8
@@ -27,7 +27,8 @@ SDM_FLAG_STATE_BF16 = 32
 
 EXPORTS = ("sdm_abi_version", "sdm_status_string", "sdm_workspace_bytes", "sdm_select",
            "sdm_select_from_scores", "sdm_scan", "sdm_forward", "sdm_scan_shared_m0",
-           "sdm_forward_shared_m0", "sdm_slot_histogram", "sdm_timing_read")
+           "sdm_forward_shared_m0", "sdm_scan_train", "sdm_scan_backward",
+           "sdm_slot_histogram", "sdm_timing_read")
 
 
 class SdmDims(ctypes.Structure):
@@ -40,6 +41,13 @@ class SdmDims(ctypes.Structure):
 class SdmSel(ctypes.Structure):
     _fields_ = [(name, ctypes.c_void_p) for name in
                 ("idx_w", "wt_w", "idx_r", "wt_r", "v", "gate", "alpha", "beta", "scores")]
+
+
+GRAD_FIELDS = ("d_wt_w", "d_wt_r", "d_v", "d_gate", "d_alpha", "d_beta", "d_norm_w")
+
+
+class SdmScanGrads(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in GRAD_FIELDS]
 
 
 class SdmKernelTime(ctypes.Structure):
@@ -87,6 +95,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sdm_forward_shared_m0.restype = I32
     lib.sdm_forward_shared_m0.argtypes = [P(SdmDims), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP,
                                           ctypes.c_size_t, VP]
+    lib.sdm_scan_train.restype = I32
+    lib.sdm_scan_train.argtypes = [P(SdmDims), P(SdmSel), VP, VP, VP, VP, VP, VP]
+    lib.sdm_scan_backward.restype = I32
+    lib.sdm_scan_backward.argtypes = [P(SdmDims), P(SdmSel), VP, VP, VP, VP, VP, VP,
+                                      P(SdmScanGrads), VP, ctypes.c_size_t, VP]
     lib.sdm_slot_histogram.restype = I32
     lib.sdm_slot_histogram.argtypes = [P(SdmDims), VP, VP, VP]
     del I64
@@ -173,6 +186,19 @@ def sdm_forward_shared_m0(d: SdmDims, x, w_proj, A, b_dt, norm_w, m0, state, tou
                                         _ptr(b_dt), _ptr(norm_w), _ptr(m0), _ptr(state),
                                         _ptr(touched), _ptr(out), _ptr(ws), ws_bytes,
                                         _stream(stream)))
+
+
+def sdm_scan_train(d: SdmDims, inp: SdmSel, norm_w, state, out, y_raw, log, stream=None):
+    _check(load().sdm_scan_train(ctypes.byref(d), ctypes.byref(inp), _ptr(norm_w), _ptr(state),
+                                 _ptr(out), _ptr(y_raw), _ptr(log), _stream(stream)))
+
+
+def sdm_scan_backward(d: SdmDims, inp: SdmSel, norm_w, state, d_state, y_raw, log, d_out,
+                      grads: SdmScanGrads, ws=None, ws_bytes=0, stream=None):
+    _check(load().sdm_scan_backward(ctypes.byref(d), ctypes.byref(inp), _ptr(norm_w),
+                                    _ptr(state), _ptr(d_state), _ptr(y_raw), _ptr(log),
+                                    _ptr(d_out), ctypes.byref(grads), _ptr(ws), ws_bytes,
+                                    _stream(stream)))
 
 
 def sdm_slot_histogram(d: SdmDims, idx_w, counts, stream=None):

@@ -93,6 +93,8 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
       const float oc = 1.0f - c;
       char* p = row(iw[k]);
       float4 m = state_load<BF>(p);
+      if (a.log)  // training forward: the row as it was before this write
+        reinterpret_cast<float4*>(a.log + (tok * a.W + k) * DV)[li] = m;
       m.x = fmaf(c, vv.x, oc * (al * m.x));
       m.y = fmaf(c, vv.y, oc * (al * m.y));
       m.z = fmaf(c, vv.z, oc * (al * m.z));

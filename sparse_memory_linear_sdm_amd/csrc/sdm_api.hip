@@ -139,9 +139,8 @@ int32_t run_select(const sdm_dims* d, const Derived& dv, const void* x, const vo
   return SDM_OK;
 }
 
-int32_t run_scan(const sdm_dims* d, const Derived& dv, const sdm_sel* in, const float* norm_w,
-                 void* state, float* out, float* y_raw, void* ws, size_t ws_bytes,
-                 hipStream_t st) {
+ScanArgs scan_args(const sdm_dims* d, const Derived& dv, const sdm_sel* in,
+                   const float* norm_w, void* state, float* out, float* y_raw) {
   ScanArgs a;
   a.idx_w = in->idx_w;
   a.wt_w = in->wt_w;
@@ -155,6 +154,7 @@ int32_t run_scan(const sdm_dims* d, const Derived& dv, const sdm_sel* in, const 
   a.state = state;
   a.out = out;
   a.y_raw = y_raw;
+  a.log = nullptr;
   a.B = d->B;
   a.T = d->T;
   a.H = d->H;
@@ -164,6 +164,13 @@ int32_t run_scan(const sdm_dims* d, const Derived& dv, const sdm_sel* in, const 
   a.d_v = d->d_v;
   a.eps = d->eps;
   a.state_bf16 = (d->flags & SDM_FLAG_STATE_BF16) != 0;
+  return a;
+}
+
+int32_t run_scan(const sdm_dims* d, const Derived& dv, const sdm_sel* in, const float* norm_w,
+                 void* state, float* out, float* y_raw, void* ws, size_t ws_bytes,
+                 hipStream_t st) {
+  const ScanArgs a = scan_args(d, dv, in, norm_w, state, out, y_raw);
   return hip_status(launch_scan(*d, a, ws, ws_bytes, st));
 }
 
@@ -281,6 +288,7 @@ size_t sdm_workspace_bytes(const sdm_dims* d, int32_t entry) {
     case SDM_ENTRY_FORWARD:
       return product_sizes(d, dv.M).total + select_ws_bytes(d, dv, false) +
              align_up(scan_workspace_bytes(*d));
+    case SDM_ENTRY_SCAN_BACKWARD: return align_up((size_t)d->B * d->H * d->d_v * 4);
     default: return 0;
   }
 }
@@ -324,6 +332,92 @@ int32_t sdm_scan(const sdm_dims* d, const sdm_sel* in, const float* norm_w, void
                  float* out, float* y_raw, void* ws, size_t ws_bytes, void* stream) {
   return scan_entry(d, in, norm_w, nullptr, state, nullptr, out, y_raw, ws, ws_bytes, stream,
                     false);
+}
+
+// The training entries run the direct schedule, fp32 state, per-slot rule.
+int32_t check_train_flags(const sdm_dims* d) {
+  if (d->flags & (SDM_FLAG_STATE_BF16 | SDM_FLAG_DELTA_GDN | SDM_FLAG_SCAN_STREAM |
+                  SDM_FLAG_SCAN_TWO_PHASE))
+    return SDM_ERR_UNSUPPORTED;
+  return SDM_OK;
+}
+
+int32_t sdm_scan_train(const sdm_dims* d, const sdm_sel* in, const float* norm_w, float* state,
+                       float* out, float* y_raw, float* log, void* stream) {
+  Derived dv;
+  int32_t st = check_dims(d, &dv);
+  if (st != SDM_OK) return st;
+  if ((st = check_train_flags(d)) != SDM_OK) return st;
+  if (dv.M == 0) return SDM_OK;
+  if ((st = check_sel(in, false)) != SDM_OK) return st;
+  if (!state || !out || !y_raw || !log) return SDM_ERR_NULL;
+  if (!aligned16(state) || !aligned16(out) || !aligned16(y_raw) || !aligned16(log) ||
+      (norm_w && !aligned16(norm_w)))
+    return SDM_ERR_ALIGN;
+  sdm_dims dd = *d;
+  dd.flags |= SDM_FLAG_SCAN_DIRECT;
+  ScanArgs a = scan_args(&dd, dv, in, norm_w, state, out, y_raw);
+  a.log = log;
+  TimingScope timing(d);
+  (void)hipGetLastError();
+  return hip_status(launch_scan(dd, a, nullptr, 0, (hipStream_t)stream));
+}
+
+int32_t sdm_scan_backward(const sdm_dims* d, const sdm_sel* in, const float* norm_w,
+                          float* state, float* d_state, const float* y_raw, const float* log,
+                          const float* d_out, const sdm_scan_grads* g, void* ws,
+                          size_t ws_bytes, void* stream) {
+  Derived dv;
+  int32_t st = check_dims(d, &dv);
+  if (st != SDM_OK) return st;
+  if ((st = check_train_flags(d)) != SDM_OK) return st;
+  if (dv.M == 0) return SDM_OK;
+  if ((st = check_sel(in, false)) != SDM_OK) return st;
+  if (!state || !d_state || !y_raw || !log || !d_out || !g) return SDM_ERR_NULL;
+  if (!g->d_wt_w || !g->d_wt_r || !g->d_v || !g->d_gate || !g->d_alpha || !g->d_beta)
+    return SDM_ERR_NULL;
+  const void* ptrs[] = {state, d_state, y_raw, log, d_out, g->d_wt_w, g->d_wt_r, g->d_v,
+                        g->d_gate, g->d_alpha, g->d_beta};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return SDM_ERR_ALIGN;
+  if ((norm_w && !aligned16(norm_w)) || (g->d_norm_w && !aligned16(g->d_norm_w)))
+    return SDM_ERR_ALIGN;
+  const size_t need = align_up((size_t)d->B * d->H * d->d_v * 4);
+  if (!ws || ws_bytes < need) return SDM_ERR_WORKSPACE;
+  if (!aligned16(ws)) return SDM_ERR_ALIGN;
+  ScanBackArgs a;
+  a.idx_w = in->idx_w;
+  a.wt_w = in->wt_w;
+  a.idx_r = in->idx_r;
+  a.wt_r = in->wt_r;
+  a.v = in->v;
+  a.gate = in->gate;
+  a.alpha = in->alpha;
+  a.beta = in->beta;
+  a.norm_w = norm_w;
+  a.state = state;
+  a.d_state = d_state;
+  a.y_raw = y_raw;
+  a.log = log;
+  a.d_out = d_out;
+  a.g_wt_w = g->d_wt_w;
+  a.g_wt_r = g->d_wt_r;
+  a.g_v = g->d_v;
+  a.g_gate = g->d_gate;
+  a.g_alpha = g->d_alpha;
+  a.g_beta = g->d_beta;
+  a.g_gamma_part = static_cast<float*>(ws);
+  a.B = d->B;
+  a.T = d->T;
+  a.H = d->H;
+  a.N = (int32_t)dv.N;
+  a.W = d->W;
+  a.R = d->R;
+  a.d_v = d->d_v;
+  a.eps = d->eps;
+  TimingScope timing(d);
+  (void)hipGetLastError();
+  return hip_status(launch_scan_backward(a, g->d_norm_w, (hipStream_t)stream));
 }
 
 int32_t sdm_scan_shared_m0(const sdm_dims* d, const sdm_sel* in, const float* norm_w,

@@ -46,6 +46,7 @@ struct ScanArgs {
   void* state;          // fp32, or bf16 when state_bf16
   float* out;
   float* y_raw;         // nullable
+  float* log;           // nullable: [B, T, H, W, d_v] rows before each write (direct, fp32)
   int64_t B, T;
   int32_t H, N, W, R, d_v;
   float eps;
@@ -109,6 +110,35 @@ StreamPlan plan_stream(const sdm_dims& d, int64_t N);
 size_t stream_workspace_bytes(const sdm_dims& d, const StreamPlan& pl);
 hipError_t launch_stream_scan(const ScanArgs& a, const StreamPlan& pl, void* ws, hipStream_t s);
 bool scan_uses_stream(const sdm_dims& d);
+
+// Backward of the scan and norm/gate (scan_backward.hip): reverse walk per (b, h).
+struct ScanBackArgs {
+  const int32_t* idx_w;
+  const float* wt_w;
+  const int32_t* idx_r;
+  const float* wt_r;
+  const float* v;
+  const float* gate;
+  const float* alpha;
+  const float* beta;
+  const float* norm_w;  // nullable (ones)
+  float* state;         // IN M_T, OUT M_0
+  float* d_state;       // IN dL/dM_T, OUT dL/dM_0
+  const float* y_raw;
+  const float* log;     // [B, T, H, W, d_v]
+  const float* d_out;
+  float* g_wt_w;
+  float* g_wt_r;
+  float* g_v;
+  float* g_gate;
+  float* g_alpha;
+  float* g_beta;
+  float* g_gamma_part;  // [B, H, d_v] per-walk partials (workspace)
+  int64_t B, T;
+  int32_t H, N, W, R, d_v;
+  float eps;
+};
+hipError_t launch_scan_backward(const ScanBackArgs& a, float* d_norm_w, hipStream_t s);
 
 // Shared initial state (shared_m0.hip): set the touched bit of every id the call
 // reads or writes; copy M0[h][id] into the store on the first touch.

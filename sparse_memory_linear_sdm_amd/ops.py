@@ -124,6 +124,48 @@ def forward(d: SdmDims, x, w_proj, A, b_dt, norm_w, state, debug=False, with_sco
     return (o, prod) if debug else o
 
 
+def scan_train(d: SdmDims, products: dict, norm_w, state, out=None, stream=None):
+    """Training forward: scan() that also records the write log.  Returns
+    (out, y_raw, log [B, T, H, W, d_v])."""
+    _check_products(d, products)
+    N = d.n * d.n
+    _need(state, torch.float32, (d.B, d.H, N, d.d_v), "state")
+    if norm_w is not None:
+        _need(norm_w, torch.float32, (d.H, d.d_v), "norm_w")
+    dev = state.device
+    o = out if out is not None else torch.empty((d.B, d.T, d.H, d.d_v), device=dev)
+    _need(o, torch.float32, (d.B, d.T, d.H, d.d_v), "out")
+    y = torch.empty_like(o)
+    log = torch.empty((d.B, d.T, d.H, d.W, d.d_v), device=dev)
+    _lib.sdm_scan_train(d, _sel(products), norm_w, state, o, y, log, stream)
+    return o, y, log
+
+
+def scan_backward(d: SdmDims, products: dict, norm_w, state, d_state, y_raw, log, d_out,
+                  with_d_norm_w=True, ws=None, stream=None):
+    """Gradients of scan_train's call.  state (M_T -> M_0) and d_state (dL/dM_T ->
+    dL/dM_0) are updated in place.  Returns a dict of gradient tensors."""
+    _check_products(d, products)
+    N = d.n * d.n
+    B, T, H = d.B, d.T, d.H
+    _need(state, torch.float32, (B, H, N, d.d_v), "state")
+    _need(d_state, torch.float32, (B, H, N, d.d_v), "d_state")
+    _need(y_raw, torch.float32, (B, T, H, d.d_v), "y_raw")
+    _need(log, torch.float32, (B, T, H, d.W, d.d_v), "log")
+    _need(d_out, torch.float32, (B, T, H, d.d_v), "d_out")
+    if norm_w is not None:
+        _need(norm_w, torch.float32, (H, d.d_v), "norm_w")
+    e = lambda *s: torch.empty(s, dtype=torch.float32, device=state.device)
+    g = dict(d_wt_w=e(B, T, H, d.W), d_wt_r=e(B, T, H, d.R), d_v=e(B, T, H, d.d_v),
+             d_gate=e(B, T, H, d.d_v), d_alpha=e(B, T, H), d_beta=e(B, T, H),
+             d_norm_w=e(H, d.d_v) if with_d_norm_w else None)
+    ws, nb = _workspace(d, _lib.SDM_ENTRY_SCAN_BACKWARD, state.device, ws)
+    gs = _lib.SdmScanGrads(*[_lib._ptr(g[k]) for k in _lib.GRAD_FIELDS])
+    _lib.sdm_scan_backward(d, _sel(products), norm_w, state, d_state, y_raw, log, d_out, gs, ws,
+                           nb, stream)
+    return g
+
+
 def alloc_touched(d: SdmDims, device):
     """All-zero touched bitmaps [B, H, ceil(N/32)] (int32 words): every sequence at M0."""
     return torch.zeros((d.B, d.H, (d.n * d.n + 31) // 32), dtype=torch.int32, device=device)

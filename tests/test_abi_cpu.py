@@ -141,6 +141,31 @@ def test_shared_m0_entries_validate_first(lib):
     assert fwd(tch=None, dd=_d(B=0)) == _lib.SDM_OK
 
 
+def test_training_entries_validate_first(lib):
+    d = _d(T=64)
+    s = _sel()
+    train = lambda dd=d, log=FAKE, y=FAKE: lib.sdm_scan_train(
+        ctypes.byref(dd), ctypes.byref(s), None, FAKE, FAKE, y, log, None)
+    for bad in (_lib.SDM_FLAG_STATE_BF16, _lib.SDM_FLAG_DELTA_GDN, _lib.SDM_FLAG_SCAN_STREAM,
+                _lib.SDM_FLAG_SCAN_TWO_PHASE):
+        assert train(dd=_d(T=64, flags=bad)) == _lib.SDM_ERR_UNSUPPORTED
+    assert train(log=None) == _lib.SDM_ERR_NULL
+    assert train(y=None) == _lib.SDM_ERR_NULL        # the backward needs y_raw
+    assert train(log=FAKE + 4) == _lib.SDM_ERR_ALIGN
+    assert train(dd=_d(T=0), log=None) == _lib.SDM_OK
+    g = _lib.SdmScanGrads(*([FAKE] * 6 + [None]))
+    back = lambda dd=d, grads=g, ws=FAKE, nb=1 << 40: lib.sdm_scan_backward(
+        ctypes.byref(dd), ctypes.byref(s), None, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(grads),
+        ws, nb, None)
+    assert back(dd=_d(T=64, flags=_lib.SDM_FLAG_DELTA_GDN)) == _lib.SDM_ERR_UNSUPPORTED
+    assert back(grads=_lib.SdmScanGrads(*([FAKE] * 5 + [None, None]))) == _lib.SDM_ERR_NULL
+    assert back(ws=None) == _lib.SDM_ERR_WORKSPACE
+    need = lib.sdm_workspace_bytes(ctypes.byref(d), _lib.SDM_ENTRY_SCAN_BACKWARD)
+    assert need == d.B * d.H * d.d_v * 4
+    assert back(nb=need - 1) == _lib.SDM_ERR_WORKSPACE
+    assert back(grads=_lib.SdmScanGrads(*([FAKE] * 6 + [FAKE + 8]))) == _lib.SDM_ERR_ALIGN
+
+
 def test_null_dims(lib):
     assert lib.sdm_select(None, FAKE, FAKE, FAKE, FAKE, None, FAKE, 0, None) == _lib.SDM_ERR_NULL
     assert lib.sdm_workspace_bytes(None, 0) == 0

@@ -1,0 +1,160 @@
+"""Training path (sdm_scan_train + sdm_scan_backward) against the oracle.
+
+* The training forward equals sdm_scan with the direct schedule bit for bit (state,
+  y, out), and its write log holds the rows each write replaced (oracle log within
+  the fp32 tolerance).
+* The backward, given the GPU's forward results, the log and random incoming
+  gradients (of out and of the final state), matches the oracle's scan_backward
+  run on the same values: every gradient within 1e-4 of its tensor's scale (fp32
+  sums over up to T tokens against fp64), the initial state restored bit for bit,
+  and the gradients bit-reproducible across runs (fixed summation order).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import sdm_oracle as O
+from sparse_memory_linear_sdm_amd import _lib, dims_for, ops, synth
+from tests.gpu_util import assert_close, host, layer_inputs, random_products, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    say(f"\n[gpu] {request.node.nodeid}")
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    yield
+    torch.cuda.synchronize()
+
+
+def _dims(**kw):
+    base = dict(B=1, T=64, d_model=64, H=1, n=16, W=8, R=8, d_v=16, in_dtype=_lib.SDM_DTYPE_F32,
+                gate_act=_lib.SDM_GATE_SIGMOID, eps=1e-6)
+    base.update(kw)
+    return _lib.dims(**base)
+
+
+def _close_to_scale(got, exp, what, rel=1e-4):
+    got = np.asarray(got, np.float64)
+    exp = np.asarray(exp, np.float64)
+    scale = max(np.abs(exp).max(), 1e-30)
+    err = np.abs(got - exp)
+    bad = err > rel * (np.abs(exp) + scale)
+    assert not bad.any(), (f"{what}: {bad.sum()} elements beyond {rel} of the scale {scale:.3e}; "
+                           f"max err {err.max():.3e}")
+
+
+def _run(d, prod, gamma, m0, rng, walks):
+    """GPU forward + backward; oracle backward of the listed walks from the GPU's values."""
+    B, T, H, N, dv = d.B, d.T, d.H, d.n * d.n, d.d_v
+    pd = {k: to_dev(v) for k, v in prod.items()}
+    gam = to_dev(gamma) if gamma is not None else None
+    state = to_dev(m0)
+    out, y, log = ops.scan_train(d, pd, gam, state)
+    torch.cuda.synchronize()
+    st_T, y_h, log_h = host(state), host(y), host(log)
+    d_out = rng.standard_normal((B, T, H, dv)).astype(np.float32)
+    d_st = (rng.standard_normal((B, H, N, dv)) * 0.1).astype(np.float32)
+    dS = to_dev(d_st)
+    g = ops.scan_backward(d, pd, gam, state, dS, y, log, to_dev(d_out))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(state), m0), "initial state not restored bit for bit"
+    gh = {k: host(v) for k, v in g.items() if v is not None}
+    gamma_h = gamma if gamma is not None else np.ones((H, dv), np.float32)
+    d_gamma = np.zeros((H, dv))
+    for b in range(B):
+        for h in range(H):
+            sel = {k: prod[k][b, :, h] for k in ("idx_w", "wt_w", "idx_r", "wt_r", "v", "gate",
+                                                  "alpha", "beta")}
+            og, oM0, odM = O.scan_backward(st_T[b, h], log_h[b, :, h], sel["idx_w"], sel["wt_w"],
+                                           sel["idx_r"], sel["wt_r"], sel["v"], sel["alpha"],
+                                           sel["beta"], y_h[b, :, h], sel["gate"], gamma_h[h],
+                                           d.eps, d_out[b, :, h], d_st[b, h])
+            d_gamma[h] += og["d_gamma"]
+            if (b, h) not in walks:
+                continue
+            assert np.array_equal(oM0, m0[b, h])
+            for k in ("d_v", "d_gate", "d_alpha", "d_beta", "d_wt_w", "d_wt_r"):
+                _close_to_scale(gh[k][b, :, h], og[k], f"{k} walk {(b, h)}")
+            _close_to_scale(host(dS)[b, h], odM, f"d_state walk {(b, h)}")
+    _close_to_scale(gh["d_norm_w"], d_gamma, "d_norm_w")
+    return out, y, log, state, g, pd, gam, dS
+
+
+@pytest.mark.parametrize("B,T,H,n,W,R,d_v,mode", [
+    (1, 64, 1, 16, 8, 8, 16, "random"),
+    (2, 120, 2, 8, 16, 16, 32, "repeat"),     # N = 64: slots rewritten and re-read constantly
+    (2, 50, 3, 8, 32, 32, 64, "random"),
+    (1, 40, 2, 12, 16, 8, 128, "same"),       # every token the same selection
+    (1, 30, 1, 16, 64, 128, 256, "random"),
+    (2, 17, 1, 4, 16, 16, 16, "random"),      # every slot written and read by every token
+])
+def test_backward_matches_oracle(B, T, H, n, W, R, d_v, mode):
+    rng = np.random.default_rng(B * 1000 + T + W + R + d_v)
+    prod = random_products(rng, B, T, H, n, W, R, d_v, mode)
+    m0 = (rng.standard_normal((B, H, n * n, d_v)) * 0.3).astype(np.float32)
+    gamma = rng.uniform(0.5, 1.5, (H, d_v)).astype(np.float32)
+    d = _dims(B=B, T=T, H=H, n=n, W=W, R=R, d_v=d_v)
+    _run(d, prod, gamma, m0, rng, [(b, h) for b in range(B) for h in range(H)])
+
+
+def test_training_forward_equals_scan_and_log_is_the_replaced_rows():
+    rng = np.random.default_rng(61)
+    B, T, H, n, W, R, d_v = 2, 80, 2, 10, 16, 16, 64
+    prod = random_products(rng, B, T, H, n, W, R, d_v, "repeat")
+    m0 = (rng.standard_normal((B, H, n * n, d_v)) * 0.3).astype(np.float32)
+    gamma = rng.uniform(0.5, 1.5, (H, d_v)).astype(np.float32)
+    d = _dims(B=B, T=T, H=H, n=n, W=W, R=R, d_v=d_v)
+    pd = {k: to_dev(v) for k, v in prod.items()}
+    st_a, st_b = to_dev(m0), to_dev(m0)
+    out_a, y_a, log = ops.scan_train(d, pd, to_dev(gamma), st_a)
+    d.flags = _lib.SDM_FLAG_SCAN_DIRECT
+    out_b, y_b = ops.scan(d, pd, to_dev(gamma), st_b, with_y_raw=True)
+    torch.cuda.synchronize()
+    assert torch.equal(st_a, st_b) and torch.equal(y_a, y_b) and torch.equal(out_a, out_b)
+    lh = host(log)
+    for b in range(B):
+        for h in range(H):
+            _, _, olog = O.scan(m0[b, h], prod["idx_w"][b, :, h], prod["wt_w"][b, :, h],
+                                prod["idx_r"][b, :, h], prod["wt_r"][b, :, h], prod["v"][b, :, h],
+                                prod["alpha"][b, :, h], prod["beta"][b, :, h], record=True)
+            assert_close(lh[b, :, h], olog, f"log walk {(b, h)}")
+
+
+def test_backward_is_bit_reproducible_and_without_norm_weight():
+    rng = np.random.default_rng(62)
+    B, T, H, n, W, R, d_v = 2, 60, 2, 8, 16, 16, 32
+    prod = random_products(rng, B, T, H, n, W, R, d_v, "repeat")
+    m0 = (rng.standard_normal((B, H, n * n, d_v)) * 0.3).astype(np.float32)
+    d = _dims(B=B, T=T, H=H, n=n, W=W, R=R, d_v=d_v)
+    out, y, log, state, g, pd, gam, dS = _run(d, prod, None, m0, rng, [(0, 0), (1, 1)])
+    # the backward left M_0 in `state`: redo the forward to get M_T back, then run the
+    # backward twice with the same incoming gradients
+    state2 = state.clone()
+    ops.scan_train(d, pd, None, state2)
+    torch.cuda.synchronize()
+    runs = []
+    for _ in range(2):
+        s_ = state2.clone()
+        ds = torch.ones_like(s_) * 0.25
+        dout = torch.full_like(y, 0.5)
+        runs.append((ops.scan_backward(d, pd, None, s_, ds, y, log, dout), ds))
+    torch.cuda.synchronize()
+    for k in runs[0][0]:
+        assert torch.equal(runs[0][0][k], runs[1][0][k]), k
+    assert torch.equal(runs[0][1], runs[1][1])
+
+
+def test_bench_layer_shape_reduced_tokens():
+    """The 1.4B-like layer's N, W, R, d_v and H with 256 tokens per sequence, products
+    from the GPU's own selection pass."""
+    wl = synth.small("layer1p4b", B=2, T=256)
+    h, dd = layer_inputs(wl, seed=5)
+    dm = dims_for(wl)
+    p = ops.select(dm, dd["x"], dd["w_proj"], dd["A"], dd["b_dt"])
+    prod = {k: host(v) for k, v in p.items()}
+    m0 = np.broadcast_to(h["m0"], (wl.B,) + h["m0"].shape).copy()
+    rng = np.random.default_rng(63)
+    _run(dm, prod, h["gamma"], m0, rng, [(0, 0), (wl.B - 1, wl.H - 1)])
