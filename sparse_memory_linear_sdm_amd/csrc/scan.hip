@@ -29,6 +29,7 @@ __device__ __forceinline__ float4 f4(float a) { return make_float4(a, a, a, a); 
 template <int DV, bool GDN, bool BF>
 __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   constexpr uint32_t ES = StateT<BF>::ES;
+  constexpr int BQ = 8;  // rows a group keeps in flight
   constexpr int LPR = DV / 4;
   constexpr int G = 256 / LPR;
   __shared__ float4 red[G][LPR];
@@ -88,30 +89,55 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
         state_store<BF>(reinterpret_cast<uint64_t>(p), state_round<BF>(m));
       }
     } else
-    for (int k = grp; k < a.W; k += G) {
-      const float c = be * ww[k];
-      const float oc = 1.0f - c;
-      char* p = row(iw[k]);
-      float4 m = state_load<BF>(p);
-      if (a.log)  // training forward: the row as it was before this write
-        reinterpret_cast<float4*>(a.log + (tok * a.W + k) * DV)[li] = m;
-      m.x = fmaf(c, vv.x, oc * (al * m.x));
-      m.y = fmaf(c, vv.y, oc * (al * m.y));
-      m.z = fmaf(c, vv.z, oc * (al * m.z));
-      m.w = fmaf(c, vv.w, oc * (al * m.w));
-      state_store<BF>(reinterpret_cast<uint64_t>(p), state_round<BF>(m));
+    // A token's write ids are distinct, so a group's rows never alias: their loads
+    // are all issued before the first store (BQ rows in flight per lane).
+    for (int k0 = grp; k0 < a.W; k0 += G * BQ) {
+      char* p[BQ];
+      float4 m[BQ];
+#pragma unroll
+      for (int j = 0; j < BQ; ++j) {
+        const int k = k0 + j * G;
+        p[j] = row(iw[k < a.W ? k : k0]);
+      }
+#pragma unroll
+      for (int j = 0; j < BQ; ++j) m[j] = state_load<BF>(p[j]);
+#pragma unroll
+      for (int j = 0; j < BQ; ++j) {
+        const int k = k0 + j * G;
+        if (k >= a.W) break;
+        const float c = be * ww[k];
+        const float oc = 1.0f - c;
+        if (a.log)  // training forward: the row as it was before this write
+          reinterpret_cast<float4*>(a.log + (tok * a.W + k) * DV)[li] = m[j];
+        float4 n;
+        n.x = fmaf(c, vv.x, oc * (al * m[j].x));
+        n.y = fmaf(c, vv.y, oc * (al * m[j].y));
+        n.z = fmaf(c, vv.z, oc * (al * m[j].z));
+        n.w = fmaf(c, vv.w, oc * (al * m[j].w));
+        state_store<BF>(reinterpret_cast<uint64_t>(p[j]), state_round<BF>(n));
+      }
     }
     __syncthreads();
     const int32_t* ir = a.idx_r + tok * a.R;
     const float* wr = a.wt_r + tok * a.R;
     float4 acc = f4(0.0f);
-    for (int k = grp; k < a.R; k += G) {
-      const float q = wr[k];
-      const float4 m = state_load<BF>(row(ir[k]));
-      acc.x = fmaf(q, m.x, acc.x);
-      acc.y = fmaf(q, m.y, acc.y);
-      acc.z = fmaf(q, m.z, acc.z);
-      acc.w = fmaf(q, m.w, acc.w);
+    for (int k0 = grp; k0 < a.R; k0 += G * BQ) {  // same order of the sum, rows batched
+      float4 m[BQ];
+#pragma unroll
+      for (int j = 0; j < BQ; ++j) {
+        const int k = k0 + j * G;
+        m[j] = state_load<BF>(row(ir[k < a.R ? k : k0]));
+      }
+#pragma unroll
+      for (int j = 0; j < BQ; ++j) {
+        const int k = k0 + j * G;
+        if (k >= a.R) break;
+        const float q = wr[k];
+        acc.x = fmaf(q, m[j].x, acc.x);
+        acc.y = fmaf(q, m[j].y, acc.y);
+        acc.z = fmaf(q, m[j].z, acc.z);
+        acc.w = fmaf(q, m[j].w, acc.w);
+      }
     }
     red[grp][li] = acc;
     __syncthreads();

@@ -43,6 +43,7 @@ template <int DV>
 __global__ __launch_bounds__(256) void scan_backward_kernel(ScanBackArgs a) {
   constexpr int LPR = DV / 4;
   constexpr int G = 256 / LPR;
+  constexpr int BQ = 8;           // rows a group keeps in flight
   __shared__ float4 red[G][LPR];  // per-group partial d_v of the token
   __shared__ float2 sab[G];       // per-group partial (d_alpha, d_beta)
 
@@ -83,19 +84,33 @@ __global__ __launch_bounds__(256) void scan_backward_kernel(ScanBackArgs a) {
     // ---- read (the state after token t's writes) ----
     const int32_t* ir = a.idx_r + tok * a.R;
     const float* wr = a.wt_r + tok * a.R;
-    for (int k = grp; k < a.R; k += G) {
-      const int64_t row = ir[k];
-      const float4 m = reinterpret_cast<const float4*>(M + row * DV)[li];
-      const float dq = group_sum<LPR>(dot4(dy, m));
-      if (li == 0) a.g_wt_r[tok * a.R + k] = dq;
-      const float q = wr[k];
-      float4* p = reinterpret_cast<float4*>(dM + row * DV) + li;
-      float4 g = *p;
-      g.x = fmaf(q, dy.x, g.x);
-      g.y = fmaf(q, dy.y, g.y);
-      g.z = fmaf(q, dy.z, g.z);
-      g.w = fmaf(q, dy.w, g.w);
-      *p = g;
+    for (int k0 = grp; k0 < a.R; k0 += G * BQ) {  // distinct ids: batch the row loads
+      int64_t rows[BQ];
+      float4 m[BQ], g[BQ];
+#pragma unroll
+      for (int j = 0; j < BQ; ++j) {
+        const int k = k0 + j * G;
+        rows[j] = ir[k < a.R ? k : k0];
+      }
+#pragma unroll
+      for (int j = 0; j < BQ; ++j) {
+        m[j] = reinterpret_cast<const float4*>(M + rows[j] * DV)[li];
+        g[j] = reinterpret_cast<const float4*>(dM + rows[j] * DV)[li];
+      }
+#pragma unroll
+      for (int j = 0; j < BQ; ++j) {
+        const int k = k0 + j * G;
+        if (k >= a.R) break;
+        const float dq = group_sum<LPR>(dot4(dy, m[j]));
+        if (li == 0) a.g_wt_r[tok * a.R + k] = dq;
+        const float q = wr[k];
+        float4 n = g[j];
+        n.x = fmaf(q, dy.x, n.x);
+        n.y = fmaf(q, dy.y, n.y);
+        n.z = fmaf(q, dy.z, n.z);
+        n.w = fmaf(q, dy.w, n.w);
+        reinterpret_cast<float4*>(dM + rows[j] * DV)[li] = n;
+      }
     }
     __syncthreads();  // the write phase below may take rows this phase updated
     // ---- write, undone ----
@@ -106,27 +121,46 @@ __global__ __launch_bounds__(256) void scan_backward_kernel(ScanBackArgs a) {
     const float* ww = a.wt_w + tok * a.W;
     float4 dv = f4s(0.0f);
     float da = 0.0f, db = 0.0f;
-    for (int k = grp; k < a.W; k += G) {
-      const int64_t row = iw[k];
-      const float kw = ww[k];
-      const float c = be * kw;
-      const float oc = 1.0f - c;
-      const float4 m = reinterpret_cast<const float4*>(a.log + (tok * a.W + k) * DV)[li];
-      float4* pg = reinterpret_cast<float4*>(dM + row * DV) + li;
-      const float4 g = *pg;
-      dv.x = fmaf(c, g.x, dv.x);
-      dv.y = fmaf(c, g.y, dv.y);
-      dv.z = fmaf(c, g.z, dv.z);
-      dv.w = fmaf(c, g.w, dv.w);
-      const float4 e = make_float4(vv.x - al * m.x, vv.y - al * m.y, vv.z - al * m.z,
-                                   vv.w - al * m.w);
-      const float dc = group_sum<LPR>(dot4(g, e));
-      da += oc * group_sum<LPR>(dot4(g, m));
-      db += kw * dc;
-      if (li == 0) a.g_wt_w[tok * a.W + k] = be * dc;
-      const float f = al * oc;
-      *pg = make_float4(f * g.x, f * g.y, f * g.z, f * g.w);
-      reinterpret_cast<float4*>(M + row * DV)[li] = m;
+    for (int k0 = grp; k0 < a.W; k0 += G * BQ) {
+      int64_t rows[BQ];
+      float4 ms[BQ], gs[BQ];
+#pragma unroll
+      for (int j = 0; j < BQ; ++j) {
+        const int k = k0 + j * G;
+        rows[j] = iw[k < a.W ? k : k0];
+      }
+#pragma unroll
+      for (int j = 0; j < BQ; ++j) {
+        const int k = k0 + j * G;
+        const int kk = k < a.W ? k : k0;
+        ms[j] = reinterpret_cast<const float4*>(a.log + (tok * a.W + kk) * DV)[li];
+        gs[j] = reinterpret_cast<const float4*>(dM + rows[j] * DV)[li];
+      }
+#pragma unroll
+      for (int j = 0; j < BQ; ++j) {
+        const int k = k0 + j * G;
+        if (k >= a.W) break;
+        const int64_t row = rows[j];
+        const float kw = ww[k];
+        const float c = be * kw;
+        const float oc = 1.0f - c;
+        const float4 m = ms[j];
+        float4* pg = reinterpret_cast<float4*>(dM + row * DV) + li;
+        const float4 g = gs[j];
+        dv.x = fmaf(c, g.x, dv.x);
+        dv.y = fmaf(c, g.y, dv.y);
+        dv.z = fmaf(c, g.z, dv.z);
+        dv.w = fmaf(c, g.w, dv.w);
+        const float4 e = make_float4(vv.x - al * m.x, vv.y - al * m.y, vv.z - al * m.z,
+                                     vv.w - al * m.w);
+        const float dc = group_sum<LPR>(dot4(g, e));
+        da += oc * group_sum<LPR>(dot4(g, m));
+        db += kw * dc;
+        if (li == 0) a.g_wt_w[tok * a.W + k] = be * dc;
+        const float f = al * oc;
+        *pg = make_float4(f * g.x, f * g.y, f * g.z, f * g.w);
+        reinterpret_cast<float4*>(M + row * DV)[li] = m;
+      }
     }
     red[grp][li] = dv;
     if (li == 0) sab[grp] = make_float2(da, db);
