@@ -411,6 +411,78 @@ def scan_backward(state_T, log, idx_w, wt_w, idx_r, wt_r, v, alpha, beta, y, gat
 
 
 # ----------------------------------------------------------------------------
+# Quantised write log.  For long fine-tuning the pages store the state
+# checkpoints of training in fp8 or int4 and report no harm to the loss ([163]
+# section 八, memory-efficiency paragraph; [analysis] section "训练效率").  Here
+# the checkpoint is the write log, quantised per logged row of d_v values with one
+# absmax scale.  The code of each element is decided in fp32, as the kernels do:
+#   fp8:  v = x * (448 / absmax) in fp32, then the nearest OCP E4M3 value (1 sign,
+#         4 exponent bits with bias 7, 3 fraction bits; largest 448, subnormals
+#         spaced 2^-9; ties to even), saturating at 448;
+#   int4: v = x * (7 / absmax) in fp32, rounded to nearest even, in [-7, 7].
+# Decoding: value(code) * (absmax / 448) or code * (absmax / 7), in fp32.
+# ----------------------------------------------------------------------------
+F32 = np.float32
+
+
+def e4m3_encode(v):
+    """fp32 values (|v| <= 448 up to rounding) -> E4M3 byte codes, ties to even,
+    saturating at 448."""
+    v = np.asarray(v, F32)
+    a = np.abs(v).astype(np.float64)
+    sign = np.signbit(v).astype(np.uint8) << 7
+    code = np.zeros(v.shape, np.int64)
+    sub = a < 2.0 ** -6
+    code[sub] = np.rint(a[sub] * 512.0).astype(np.int64)       # 2^-9 steps; 8 -> 2^-6
+    _, e = np.frexp(a[~sub])                                    # a = m 2^e, m in [0.5, 1)
+    e = e - 1                                                   # a in [2^e, 2^(e+1))
+    q = np.rint(np.ldexp(a[~sub], 3 - e)).astype(np.int64)      # in [8, 16]
+    up = q == 16
+    e = np.where(up, e + 1, e)
+    q = np.where(up, 8, q)
+    field = e + 7
+    big = (field > 15) | ((field == 15) & (q - 8 == 7))         # above 448: saturate
+    code[~sub] = np.where(big, (15 << 3) | 6, (field << 3) | (q - 8))
+    return (code.astype(np.uint8) | sign).astype(np.uint8)
+
+
+def e4m3_decode(code):
+    code = np.asarray(code, np.uint8).astype(np.int64)
+    field, frac = (code >> 3) & 15, code & 7
+    mag = np.where(field == 0, np.ldexp(frac.astype(np.float64), -9),
+                   np.ldexp((8 + frac).astype(np.float64), field - 10))
+    return np.where(code >> 7, -mag, mag)
+
+
+def quantize_rows(rows, fmt: str):
+    """rows [..., d] fp32 -> (codes, absmax [...] fp32); fmt "fp8" (one byte per
+    element) or "int4" (signed codes -7..7, two per byte, low nibble first)."""
+    x = np.asarray(rows, F32)
+    amax = np.max(np.abs(x), axis=-1).astype(F32)
+    top = F32(448.0) if fmt == "fp8" else F32(7.0)
+    with np.errstate(divide="ignore"):
+        inv = np.where(amax > 0, top / np.where(amax > 0, amax, F32(1)), F32(0)).astype(F32)
+    v = (x * inv[..., None]).astype(F32)                        # fp32, as the kernels
+    if fmt == "fp8":
+        return e4m3_encode(v), amax
+    q = np.clip(np.rint(v), -7, 7).astype(np.int64) & 15
+    return (q[..., 0::2] | (q[..., 1::2] << 4)).astype(np.uint8), amax
+
+
+def dequantize_rows(codes, amax, fmt: str):
+    amax = np.asarray(amax, F32)
+    if fmt == "fp8":
+        unit = (amax / F32(448.0)).astype(F32)
+        return (e4m3_decode(codes).astype(F32) * unit[..., None]).astype(F32)
+    c = np.asarray(codes, np.uint8).astype(np.int64)
+    lo, hi = c & 15, c >> 4
+    q = np.stack([lo, hi], axis=-1).reshape(c.shape[:-1] + (2 * c.shape[-1],))
+    q = np.where(q >= 8, q - 16, q).astype(F32)
+    unit = (amax / F32(7.0)).astype(F32)
+    return (q * unit[..., None]).astype(F32)
+
+
+# ----------------------------------------------------------------------------
 # Shared learned initial state ([analysis] section on the learned M0: M0 is a
 # parameter of the layer, the same for every sequence; [163] section 三).  A
 # sequence's memory starts as M0; a per-sequence store keeps only the rows that
