@@ -105,6 +105,20 @@ extern "C" {
    ai-paper-analysis.pages.dev, section "训练效率"; m.163.com article on arXiv
    2607.07386, section 八).  Every schedule and both write rules support it. */
 #define SDM_FLAG_STATE_BF16 32
+/* write-log format flags (sdm_dims.flags; sdm_scan_train / sdm_scan_backward only,
+   at most one): the training checkpoints quantised as the pages do for long
+   fine-tuning (fp8 or int4: m.163.com article on arXiv 2607.07386, section 八;
+   ai-paper-analysis.pages.dev, section "训练效率").  One absmax per logged row of d_v
+   values, the codes decided in fp32:
+     SDM_FLAG_LOG_FP8   v = x * (448 / absmax), nearest OCP E4M3 value (ties to even,
+                        saturating at 448); one byte per element
+     SDM_FLAG_LOG_INT4  v = x * (7 / absmax), nearest integer (ties to even) in
+                        [-7, 7]; two per byte, low nibble first
+   Decoded as value * (absmax / 448) or code * (absmax / 7).  The backward then
+   computes with, and restores, the decoded rows: the initial state comes back only
+   as closely as the format holds it. */
+#define SDM_FLAG_LOG_FP8 64
+#define SDM_FLAG_LOG_INT4 128
 
 /* Limits of this build (SDM_ERR_UNSUPPORTED beyond them). */
 #define SDM_MAX_COUNT 128   /* W and R */
@@ -243,8 +257,11 @@ SDM_API int32_t sdm_forward(const sdm_dims* dims, const void* x, const void* w_p
  * the N x d state plus the T x W x d rows the writes overwrote).
  *
  * sdm_scan_train: sdm_scan (direct schedule) that also records the write log.
- *   log     [B, T, H, W, d_v] fp32 OUT: log[b][t][h][k] = the state row idx_w[..][k]
- *           just before token t's write
+ *   log     OUT: log[b][t][h][k] = the state row idx_w[..][k] just before token t's
+ *           write: [B, T, H, W, d_v] fp32, or uint8 codes ([.., d_v] with
+ *           SDM_FLAG_LOG_FP8, [.., d_v / 2] with SDM_FLAG_LOG_INT4)
+ *   log_scale [B, T, H, W] fp32 OUT: each logged row's absmax (quantised formats;
+ *           may be NULL for fp32)
  *   y_raw   required here (the backward needs it)
  *   Other arguments as in sdm_scan; state, out and y_raw equal sdm_scan's with
  *   SDM_FLAG_SCAN_DIRECT bit for bit.  fp32 state and the per-slot rule only:
@@ -255,10 +272,11 @@ SDM_API int32_t sdm_forward(const sdm_dims* dims, const void* x, const void* w_p
  * token: the norm and gate, the read, then the write, whose overwritten rows are
  * restored from the log).
  *   state   [B, H, N, d_v] IN: the state sdm_scan_train returned; OUT: the state it
- *           started from, bit for bit
+ *           started from, bit for bit (with a quantised log: the decoded rows)
  *   d_state [B, H, N, d_v] IN: gradient of the final state (zeros if the loss does
  *           not see it); OUT: gradient of the initial state
- *   y_raw, log   as sdm_scan_train wrote them; d_out [B, T, H, d_v] gradient of out
+ *   y_raw, log, log_scale   as sdm_scan_train wrote them (same flags); d_out
+ *           [B, T, H, d_v] gradient of out
  *   grads   outputs, overwritten: d_wt_w [B,T,H,W], d_wt_r [B,T,H,R], d_v and d_gate
  *           [B,T,H,d_v], d_alpha and d_beta [B,T,H]; d_norm_w [H, d_v] (summed over
  *           the batch) or NULL
@@ -277,10 +295,11 @@ typedef struct sdm_scan_grads {
 } sdm_scan_grads;
 
 SDM_API int32_t sdm_scan_train(const sdm_dims* dims, const sdm_sel* in, const float* norm_w,
-                               float* state, float* out, float* y_raw, float* log, void* stream);
+                               float* state, float* out, float* y_raw, void* log,
+                               float* log_scale, void* stream);
 SDM_API int32_t sdm_scan_backward(const sdm_dims* dims, const sdm_sel* in, const float* norm_w,
                                   float* state, float* d_state, const float* y_raw,
-                                  const float* log, const float* d_out,
+                                  const void* log, const float* log_scale, const float* d_out,
                                   const sdm_scan_grads* grads, void* ws, size_t ws_bytes,
                                   void* stream);
 

@@ -24,6 +24,7 @@ SDM_FLAG_SCAN_DIRECT, SDM_FLAG_SCAN_STREAM, SDM_FLAG_SCAN_TWO_PHASE = 1, 2, 4
 SDM_FLAG_TIMING = 8
 SDM_FLAG_DELTA_GDN = 16
 SDM_FLAG_STATE_BF16 = 32
+SDM_FLAG_LOG_FP8, SDM_FLAG_LOG_INT4 = 64, 128
 
 EXPORTS = ("sdm_abi_version", "sdm_status_string", "sdm_workspace_bytes", "sdm_select",
            "sdm_select_from_scores", "sdm_scan", "sdm_forward", "sdm_scan_shared_m0",
@@ -96,9 +97,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sdm_forward_shared_m0.argtypes = [P(SdmDims), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP,
                                           ctypes.c_size_t, VP]
     lib.sdm_scan_train.restype = I32
-    lib.sdm_scan_train.argtypes = [P(SdmDims), P(SdmSel), VP, VP, VP, VP, VP, VP]
+    lib.sdm_scan_train.argtypes = [P(SdmDims), P(SdmSel), VP, VP, VP, VP, VP, VP, VP]
     lib.sdm_scan_backward.restype = I32
-    lib.sdm_scan_backward.argtypes = [P(SdmDims), P(SdmSel), VP, VP, VP, VP, VP, VP,
+    lib.sdm_scan_backward.argtypes = [P(SdmDims), P(SdmSel), VP, VP, VP, VP, VP, VP, VP,
                                       P(SdmScanGrads), VP, ctypes.c_size_t, VP]
     lib.sdm_slot_histogram.restype = I32
     lib.sdm_slot_histogram.argtypes = [P(SdmDims), VP, VP, VP]
@@ -188,17 +189,19 @@ def sdm_forward_shared_m0(d: SdmDims, x, w_proj, A, b_dt, norm_w, m0, state, tou
                                         _stream(stream)))
 
 
-def sdm_scan_train(d: SdmDims, inp: SdmSel, norm_w, state, out, y_raw, log, stream=None):
+def sdm_scan_train(d: SdmDims, inp: SdmSel, norm_w, state, out, y_raw, log, log_scale=None,
+                   stream=None):
     _check(load().sdm_scan_train(ctypes.byref(d), ctypes.byref(inp), _ptr(norm_w), _ptr(state),
-                                 _ptr(out), _ptr(y_raw), _ptr(log), _stream(stream)))
+                                 _ptr(out), _ptr(y_raw), _ptr(log), _ptr(log_scale),
+                                 _stream(stream)))
 
 
-def sdm_scan_backward(d: SdmDims, inp: SdmSel, norm_w, state, d_state, y_raw, log, d_out,
-                      grads: SdmScanGrads, ws=None, ws_bytes=0, stream=None):
+def sdm_scan_backward(d: SdmDims, inp: SdmSel, norm_w, state, d_state, y_raw, log, log_scale,
+                      d_out, grads: SdmScanGrads, ws=None, ws_bytes=0, stream=None):
     _check(load().sdm_scan_backward(ctypes.byref(d), ctypes.byref(inp), _ptr(norm_w),
                                     _ptr(state), _ptr(d_state), _ptr(y_raw), _ptr(log),
-                                    _ptr(d_out), ctypes.byref(grads), _ptr(ws), ws_bytes,
-                                    _stream(stream)))
+                                    _ptr(log_scale), _ptr(d_out), ctypes.byref(grads), _ptr(ws),
+                                    ws_bytes, _stream(stream)))
 
 
 def sdm_slot_histogram(d: SdmDims, idx_w, counts, stream=None):

@@ -26,8 +26,10 @@ struct Derived {
 int32_t check_dims(const sdm_dims* d, Derived* out) {
   if (!d) return SDM_ERR_NULL;
   const int32_t sched = SDM_FLAG_SCAN_DIRECT | SDM_FLAG_SCAN_STREAM | SDM_FLAG_SCAN_TWO_PHASE;
-  if (d->flags & ~(sched | SDM_FLAG_TIMING | SDM_FLAG_DELTA_GDN | SDM_FLAG_STATE_BF16))
+  if (d->flags & ~(sched | SDM_FLAG_TIMING | SDM_FLAG_DELTA_GDN | SDM_FLAG_STATE_BF16 |
+                   SDM_FLAG_LOG_FP8 | SDM_FLAG_LOG_INT4))
     return SDM_ERR_UNSUPPORTED;
+  if ((d->flags & SDM_FLAG_LOG_FP8) && (d->flags & SDM_FLAG_LOG_INT4)) return SDM_ERR_SHAPE;
   if (__builtin_popcount((unsigned)(d->flags & sched)) > 1) return SDM_ERR_SHAPE;  // one schedule
   if ((d->flags & SDM_FLAG_DELTA_GDN) &&
       (d->flags & (SDM_FLAG_SCAN_STREAM | SDM_FLAG_SCAN_TWO_PHASE)))
@@ -155,6 +157,8 @@ ScanArgs scan_args(const sdm_dims* d, const Derived& dv, const sdm_sel* in,
   a.out = out;
   a.y_raw = y_raw;
   a.log = nullptr;
+  a.log_scale = nullptr;
+  a.log_fmt = LOG_F32;
   a.B = d->B;
   a.T = d->T;
   a.H = d->H;
@@ -342,45 +346,56 @@ int32_t check_train_flags(const sdm_dims* d) {
   return SDM_OK;
 }
 
+int32_t log_format(const sdm_dims* d) {
+  return (d->flags & SDM_FLAG_LOG_FP8) ? LOG_FP8 : (d->flags & SDM_FLAG_LOG_INT4) ? LOG_INT4
+                                                                                   : LOG_F32;
+}
+
 int32_t sdm_scan_train(const sdm_dims* d, const sdm_sel* in, const float* norm_w, float* state,
-                       float* out, float* y_raw, float* log, void* stream) {
+                       float* out, float* y_raw, void* log, float* log_scale, void* stream) {
   Derived dv;
   int32_t st = check_dims(d, &dv);
   if (st != SDM_OK) return st;
   if ((st = check_train_flags(d)) != SDM_OK) return st;
   if (dv.M == 0) return SDM_OK;
   if ((st = check_sel(in, false)) != SDM_OK) return st;
-  if (!state || !out || !y_raw || !log) return SDM_ERR_NULL;
+  const int32_t fmt = log_format(d);
+  if (!state || !out || !y_raw || !log || (fmt != LOG_F32 && !log_scale)) return SDM_ERR_NULL;
   if (!aligned16(state) || !aligned16(out) || !aligned16(y_raw) || !aligned16(log) ||
-      (norm_w && !aligned16(norm_w)))
+      (norm_w && !aligned16(norm_w)) || (log_scale && !aligned16(log_scale)))
     return SDM_ERR_ALIGN;
   sdm_dims dd = *d;
   dd.flags |= SDM_FLAG_SCAN_DIRECT;
   ScanArgs a = scan_args(&dd, dv, in, norm_w, state, out, y_raw);
   a.log = log;
+  a.log_scale = log_scale;
+  a.log_fmt = fmt;
   TimingScope timing(d);
   (void)hipGetLastError();
   return hip_status(launch_scan(dd, a, nullptr, 0, (hipStream_t)stream));
 }
 
 int32_t sdm_scan_backward(const sdm_dims* d, const sdm_sel* in, const float* norm_w,
-                          float* state, float* d_state, const float* y_raw, const float* log,
-                          const float* d_out, const sdm_scan_grads* g, void* ws,
-                          size_t ws_bytes, void* stream) {
+                          float* state, float* d_state, const float* y_raw, const void* log,
+                          const float* log_scale, const float* d_out, const sdm_scan_grads* g,
+                          void* ws, size_t ws_bytes, void* stream) {
   Derived dv;
   int32_t st = check_dims(d, &dv);
   if (st != SDM_OK) return st;
   if ((st = check_train_flags(d)) != SDM_OK) return st;
   if (dv.M == 0) return SDM_OK;
   if ((st = check_sel(in, false)) != SDM_OK) return st;
-  if (!state || !d_state || !y_raw || !log || !d_out || !g) return SDM_ERR_NULL;
+  const int32_t fmt = log_format(d);
+  if (!state || !d_state || !y_raw || !log || !d_out || !g || (fmt != LOG_F32 && !log_scale))
+    return SDM_ERR_NULL;
   if (!g->d_wt_w || !g->d_wt_r || !g->d_v || !g->d_gate || !g->d_alpha || !g->d_beta)
     return SDM_ERR_NULL;
   const void* ptrs[] = {state, d_state, y_raw, log, d_out, g->d_wt_w, g->d_wt_r, g->d_v,
                         g->d_gate, g->d_alpha, g->d_beta};
   for (const void* p : ptrs)
     if (!aligned16(p)) return SDM_ERR_ALIGN;
-  if ((norm_w && !aligned16(norm_w)) || (g->d_norm_w && !aligned16(g->d_norm_w)))
+  if ((norm_w && !aligned16(norm_w)) || (g->d_norm_w && !aligned16(g->d_norm_w)) ||
+      (log_scale && !aligned16(log_scale)))
     return SDM_ERR_ALIGN;
   const size_t need = align_up((size_t)d->B * d->H * d->d_v * 4);
   if (!ws || ws_bytes < need) return SDM_ERR_WORKSPACE;
@@ -399,6 +414,8 @@ int32_t sdm_scan_backward(const sdm_dims* d, const sdm_sel* in, const float* nor
   a.d_state = d_state;
   a.y_raw = y_raw;
   a.log = log;
+  a.log_scale = log_scale;
+  a.log_fmt = fmt;
   a.d_out = d_out;
   a.g_wt_w = g->d_wt_w;
   a.g_wt_r = g->d_wt_r;

@@ -46,7 +46,9 @@ struct ScanArgs {
   void* state;          // fp32, or bf16 when state_bf16
   float* out;
   float* y_raw;         // nullable
-  float* log;           // nullable: [B, T, H, W, d_v] rows before each write (direct, fp32)
+  void* log;            // nullable: rows before each write (direct schedule), see log_fmt
+  float* log_scale;     // [B, T, H, W] absmax of each logged row (quantised formats)
+  int32_t log_fmt;      // LOG_F32, LOG_FP8, LOG_INT4
   int64_t B, T;
   int32_t H, N, W, R, d_v;
   float eps;
@@ -111,6 +113,38 @@ size_t stream_workspace_bytes(const sdm_dims& d, const StreamPlan& pl);
 hipError_t launch_stream_scan(const ScanArgs& a, const StreamPlan& pl, void* ws, hipStream_t s);
 bool scan_uses_stream(const sdm_dims& d);
 
+// Write-log storage (training): one row of d_v values per write, fp32, or quantised
+// with one absmax per row -- fp8 (OCP E4M3, v = x * 448 / absmax) or int4 (v = x * 7 /
+// absmax, codes -7..7, two per byte, low nibble first).  Codes are decided in fp32.
+enum { LOG_F32 = 0, LOG_FP8 = 1, LOG_INT4 = 2 };
+
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fabsf(v);
+  uint32_t code;
+  if (a < 0.015625f) {  // below 2^-6: steps of 2^-9 (8 steps reach the smallest normal)
+    code = (uint32_t)__builtin_rintf(a * 512.0f);
+  } else {
+    int e = (int)((__float_as_uint(a) >> 23) & 0xff) - 127;  // a in [2^e, 2^(e+1))
+    float q = __builtin_rintf(__builtin_ldexpf(a, 3 - e));   // in [8, 16], exact scaling
+    if (q == 16.0f) {
+      q = 8.0f;
+      ++e;
+    }
+    const int field = e + 7;
+    const uint32_t frac = (uint32_t)q - 8u;
+    code = (field > 15 || (field == 15 && frac == 7)) ? 0x7Eu : ((uint32_t)field << 3) | frac;
+  }
+  return code | sign;
+}
+
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  const uint32_t field = (c >> 3) & 15u, frac = c & 7u;
+  const float mag = field == 0 ? (float)frac * 0.001953125f  // 2^-9
+                               : __builtin_ldexpf((float)(8u + frac), (int)field - 10);
+  return (c & 0x80u) ? -mag : mag;
+}
+
 // Backward of the scan and norm/gate (scan_backward.hip): reverse walk per (b, h).
 struct ScanBackArgs {
   const int32_t* idx_w;
@@ -125,7 +159,9 @@ struct ScanBackArgs {
   float* state;         // IN M_T, OUT M_0
   float* d_state;       // IN dL/dM_T, OUT dL/dM_0
   const float* y_raw;
-  const float* log;     // [B, T, H, W, d_v]
+  const void* log;      // [B, T, H, W, d_v] in log_fmt
+  const float* log_scale;
+  int32_t log_fmt;
   const float* d_out;
   float* g_wt_w;
   float* g_wt_r;

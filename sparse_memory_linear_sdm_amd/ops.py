@@ -124,9 +124,16 @@ def forward(d: SdmDims, x, w_proj, A, b_dt, norm_w, state, debug=False, with_sco
     return (o, prod) if debug else o
 
 
+def log_format(d: SdmDims) -> str:
+    if d.flags & _lib.SDM_FLAG_LOG_FP8:
+        return "fp8"
+    return "int4" if d.flags & _lib.SDM_FLAG_LOG_INT4 else "fp32"
+
+
 def scan_train(d: SdmDims, products: dict, norm_w, state, out=None, stream=None):
     """Training forward: scan() that also records the write log.  Returns
-    (out, y_raw, log [B, T, H, W, d_v])."""
+    (out, y_raw, log) with log a dict: "rows" ([B, T, H, W, d_v] fp32, or uint8 codes
+    [.., d_v] (fp8) / [.., d_v / 2] (int4)) and "scale" ([B, T, H, W] absmax, or None)."""
     _check_products(d, products)
     N = d.n * d.n
     _need(state, torch.float32, (d.B, d.H, N, d.d_v), "state")
@@ -136,8 +143,15 @@ def scan_train(d: SdmDims, products: dict, norm_w, state, out=None, stream=None)
     o = out if out is not None else torch.empty((d.B, d.T, d.H, d.d_v), device=dev)
     _need(o, torch.float32, (d.B, d.T, d.H, d.d_v), "out")
     y = torch.empty_like(o)
-    log = torch.empty((d.B, d.T, d.H, d.W, d.d_v), device=dev)
-    _lib.sdm_scan_train(d, _sel(products), norm_w, state, o, y, log, stream)
+    fmt = log_format(d)
+    lead = (d.B, d.T, d.H, d.W)
+    if fmt == "fp32":
+        log = dict(rows=torch.empty(lead + (d.d_v,), device=dev), scale=None)
+    else:
+        width = d.d_v if fmt == "fp8" else d.d_v // 2
+        log = dict(rows=torch.empty(lead + (width,), dtype=torch.uint8, device=dev),
+                   scale=torch.empty(lead, device=dev))
+    _lib.sdm_scan_train(d, _sel(products), norm_w, state, o, y, log["rows"], log["scale"], stream)
     return o, y, log
 
 
@@ -151,7 +165,13 @@ def scan_backward(d: SdmDims, products: dict, norm_w, state, d_state, y_raw, log
     _need(state, torch.float32, (B, H, N, d.d_v), "state")
     _need(d_state, torch.float32, (B, H, N, d.d_v), "d_state")
     _need(y_raw, torch.float32, (B, T, H, d.d_v), "y_raw")
-    _need(log, torch.float32, (B, T, H, d.W, d.d_v), "log")
+    fmt = log_format(d)
+    if fmt == "fp32":
+        _need(log["rows"], torch.float32, (B, T, H, d.W, d.d_v), "log rows")
+    else:
+        _need(log["rows"], torch.uint8,
+              (B, T, H, d.W, d.d_v if fmt == "fp8" else d.d_v // 2), "log rows")
+        _need(log["scale"], torch.float32, (B, T, H, d.W), "log scale")
     _need(d_out, torch.float32, (B, T, H, d.d_v), "d_out")
     if norm_w is not None:
         _need(norm_w, torch.float32, (H, d.d_v), "norm_w")
@@ -161,8 +181,8 @@ def scan_backward(d: SdmDims, products: dict, norm_w, state, d_state, y_raw, log
              d_norm_w=e(H, d.d_v) if with_d_norm_w else None)
     ws, nb = _workspace(d, _lib.SDM_ENTRY_SCAN_BACKWARD, state.device, ws)
     gs = _lib.SdmScanGrads(*[_lib._ptr(g[k]) for k in _lib.GRAD_FIELDS])
-    _lib.sdm_scan_backward(d, _sel(products), norm_w, state, d_state, y_raw, log, d_out, gs, ws,
-                           nb, stream)
+    _lib.sdm_scan_backward(d, _sel(products), norm_w, state, d_state, y_raw, log["rows"],
+                           log["scale"], d_out, gs, ws, nb, stream)
     return g
 
 

@@ -76,7 +76,7 @@ def _select(lib, d, x=FAKE, w=FAKE, A=FAKE, b=FAKE, sel=None, ws=FAKE, nb=1 << 4
     (dict(eps=-1.0), _lib.SDM_ERR_SHAPE), (dict(eps=float("nan")), _lib.SDM_ERR_SHAPE),
     (dict(n=16, W=129), _lib.SDM_ERR_UNSUPPORTED), (dict(n=1025), _lib.SDM_ERR_UNSUPPORTED),
     (dict(d_v=48), _lib.SDM_ERR_UNSUPPORTED), (dict(d_model=60), _lib.SDM_ERR_UNSUPPORTED),
-    (dict(flags=64), _lib.SDM_ERR_UNSUPPORTED), (dict(flags=3), _lib.SDM_ERR_SHAPE),
+    (dict(flags=256), _lib.SDM_ERR_UNSUPPORTED), (dict(flags=3), _lib.SDM_ERR_SHAPE),
     (dict(flags=16 | 2), _lib.SDM_ERR_UNSUPPORTED), (dict(flags=16 | 4), _lib.SDM_ERR_UNSUPPORTED),
     (dict(flags=6), _lib.SDM_ERR_SHAPE), (dict(flags=8 | 5), _lib.SDM_ERR_SHAPE),
     (dict(in_dtype=7), _lib.SDM_ERR_DTYPE), (dict(gate_act=3), _lib.SDM_ERR_DTYPE),
@@ -144,8 +144,8 @@ def test_shared_m0_entries_validate_first(lib):
 def test_training_entries_validate_first(lib):
     d = _d(T=64)
     s = _sel()
-    train = lambda dd=d, log=FAKE, y=FAKE: lib.sdm_scan_train(
-        ctypes.byref(dd), ctypes.byref(s), None, FAKE, FAKE, y, log, None)
+    train = lambda dd=d, log=FAKE, y=FAKE, sc=None: lib.sdm_scan_train(
+        ctypes.byref(dd), ctypes.byref(s), None, FAKE, FAKE, y, log, sc, None)
     for bad in (_lib.SDM_FLAG_STATE_BF16, _lib.SDM_FLAG_DELTA_GDN, _lib.SDM_FLAG_SCAN_STREAM,
                 _lib.SDM_FLAG_SCAN_TWO_PHASE):
         assert train(dd=_d(T=64, flags=bad)) == _lib.SDM_ERR_UNSUPPORTED
@@ -153,13 +153,18 @@ def test_training_entries_validate_first(lib):
     assert train(y=None) == _lib.SDM_ERR_NULL        # the backward needs y_raw
     assert train(log=FAKE + 4) == _lib.SDM_ERR_ALIGN
     assert train(dd=_d(T=0), log=None) == _lib.SDM_OK
+    fp8, int4 = _lib.SDM_FLAG_LOG_FP8, _lib.SDM_FLAG_LOG_INT4
+    assert train(dd=_d(T=64, flags=fp8)) == _lib.SDM_ERR_NULL          # scales needed
+    assert train(dd=_d(T=64, flags=int4), sc=FAKE + 4) == _lib.SDM_ERR_ALIGN
+    assert train(dd=_d(T=64, flags=fp8 | int4), sc=FAKE) == _lib.SDM_ERR_SHAPE
     g = _lib.SdmScanGrads(*([FAKE] * 6 + [None]))
-    back = lambda dd=d, grads=g, ws=FAKE, nb=1 << 40: lib.sdm_scan_backward(
-        ctypes.byref(dd), ctypes.byref(s), None, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(grads),
-        ws, nb, None)
+    back = lambda dd=d, grads=g, ws=FAKE, nb=1 << 40, sc=None: lib.sdm_scan_backward(
+        ctypes.byref(dd), ctypes.byref(s), None, FAKE, FAKE, FAKE, FAKE, sc, FAKE,
+        ctypes.byref(grads), ws, nb, None)
     assert back(dd=_d(T=64, flags=_lib.SDM_FLAG_DELTA_GDN)) == _lib.SDM_ERR_UNSUPPORTED
     assert back(grads=_lib.SdmScanGrads(*([FAKE] * 5 + [None, None]))) == _lib.SDM_ERR_NULL
     assert back(ws=None) == _lib.SDM_ERR_WORKSPACE
+    assert back(dd=_d(T=64, flags=_lib.SDM_FLAG_LOG_INT4)) == _lib.SDM_ERR_NULL
     need = lib.sdm_workspace_bytes(ctypes.byref(d), _lib.SDM_ENTRY_SCAN_BACKWARD)
     assert need == d.B * d.H * d.d_v * 4
     assert back(nb=need - 1) == _lib.SDM_ERR_WORKSPACE
