@@ -1,5 +1,7 @@
 /*
- * sdm.h -- C ABI of the Sparse Delta Memory (SDM) forward path on MI355X (gfx950).
+ * sdm.h -- C ABI of the Sparse Delta Memory (SDM) layer on MI355X (gfx950): the forward
+ * path (selection pass and recurrent sparse scan), its variants, the scan's training
+ * backward and a slot-update monitor.
  *
  * The method (no published code; defined by these pages):
  *   [rainbus]  "稀疏增量记忆：通过稀疏性扩展线性RNN的状态 / Sparse Delta Memory: Scaling
@@ -15,8 +17,9 @@
  * ---------------------------------------
  *  - Every pointer argument is a DEVICE pointer (allocated by the caller, e.g. as a
  *    torch tensor) unless stated otherwise; `dims` and `sel` structs live in host
- *    memory.  The library never allocates, frees or keeps device memory, keeps no
- *    global mutable state, and is reentrant across streams.
+ *    memory.  The library never allocates, frees or keeps device memory and is
+ *    reentrant across streams.  Its only global state is the host-side record of
+ *    SDM_FLAG_TIMING (HIP events, created on first use).
  *  - `stream` is a hipStream_t (NULL = the default stream).  All work is enqueued on it
  *    asynchronously; no call synchronises the host, allocates, or copies through
  *    pageable memory, so calls may be captured into a HIP graph.
@@ -140,8 +143,9 @@ extern "C" {
  *   eps       RMSNorm epsilon (>= 0)
  *   flags     0, or one SDM_FLAG_SCAN_* bit to force a scan schedule (all schedules
  *             compute the same recurrence; by default the library picks by shape),
- *             optionally OR-ed with SDM_FLAG_TIMING, SDM_FLAG_DELTA_GDN and
- *             SDM_FLAG_STATE_BF16
+ *             optionally OR-ed with SDM_FLAG_TIMING, SDM_FLAG_DELTA_GDN,
+ *             SDM_FLAG_STATE_BF16 and one SDM_FLAG_LOG_* bit (each flag's comment
+ *             names the entries it applies to; other entries ignore it)
  */
 typedef struct sdm_dims {
   int64_t B, T, d_model;
