@@ -31,25 +31,6 @@ __device__ __forceinline__ float dot4(float4 a, float4 b) {
   return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
 }
 
-// Logged row r (this lane's 4 columns): fp32, or decoded with the row's absmax.
-template <int DV>
-__device__ __forceinline__ float4 log_load(const ScanBackArgs& a, int64_t r, int li) {
-  if (a.log_fmt == LOG_F32)
-    return reinterpret_cast<const float4*>(static_cast<const float*>(a.log) + r * DV)[li];
-  const uint8_t* base = static_cast<const uint8_t*>(a.log);
-  const float mx = a.log_scale[r];
-  if (a.log_fmt == LOG_FP8) {
-    const uint32_t w = reinterpret_cast<const uint32_t*>(base + r * DV)[li];
-    const float unit = mx / 448.0f;
-    return make_float4(e4m3_decode(w & 0xff) * unit, e4m3_decode((w >> 8) & 0xff) * unit,
-                       e4m3_decode((w >> 16) & 0xff) * unit, e4m3_decode(w >> 24) * unit);
-  }
-  const uint32_t w = reinterpret_cast<const uint16_t*>(base + r * (DV / 2))[li];
-  const float unit = mx / 7.0f;
-  auto q = [&](uint32_t s) { return (float)(((int)((w >> s) & 15u) ^ 8) - 8) * unit; };
-  return make_float4(q(0), q(4), q(8), q(12));
-}
-
 // Sum over the LPR lanes of one row group (xor butterfly: every lane gets the sum).
 template <int LPR>
 __device__ __forceinline__ float group_sum(float x) {
@@ -152,7 +133,7 @@ __global__ __launch_bounds__(256) void scan_backward_kernel(ScanBackArgs a) {
       for (int j = 0; j < BQ; ++j) {
         const int k = k0 + j * G;
         const int kk = k < a.W ? k : k0;
-        ms[j] = log_load<DV>(a, tok * a.W + kk, li);
+        ms[j] = log_load(a.log, a.log_scale, a.log_fmt, tok * a.W + kk, DV, li);
         gs[j] = reinterpret_cast<const float4*>(dM + rows[j] * DV)[li];
       }
 #pragma unroll

@@ -34,8 +34,8 @@
 namespace sdm {
 namespace {
 
-constexpr int ROUND = 256;       // tokens per round (ring half)
-constexpr int MAX_GT = 4096;     // lane groups per walk
+constexpr int ROUND = kStreamRound;  // tokens per round (ring half)
+constexpr int MAX_GT = kStreamMaxGT;  // lane groups per walk
 constexpr uint32_t SLOT_MASK = 0xFFFFFFu;
 static_assert(ROUND <= 256, "token-in-round must fit the entry's top 8 bits");
 
@@ -48,26 +48,6 @@ __device__ __forceinline__ uint2 make_entry(uint32_t slot, int tt, float q, bool
 
 __device__ __forceinline__ uint32_t group_of(uint32_t slot, int log2gt) {
   return (slot * 2654435761u) >> (32 - log2gt);
-}
-
-// Value of lane `src` of this lane's LPG-lane group (LPG = 4 or 8), moved by DPP in
-// the vector ALU (no LDS traffic).  quad_perm broadcasts within each quad; for
-// 8-lane groups row_half_mirror brings the other quad's broadcast across.
-template <int LPG>
-__device__ __forceinline__ uint32_t group_bcast(uint32_t v, int src) {
-  const int q = src & 3;
-  const int qp = q | (q << 2) | (q << 4) | (q << 6);  // quad_perm(q,q,q,q)
-  uint32_t x;
-  switch (qp) {
-    case 0x00: x = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x00, 0xf, 0xf, false); break;
-    case 0x55: x = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x55, 0xf, 0xf, false); break;
-    case 0xaa: x = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xaa, 0xf, 0xf, false); break;
-    default: x = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xff, 0xf, 0xf, false); break;
-  }
-  if (LPG == 4) return x;
-  const uint32_t m = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xf, 0xf, false);  // row_half_mirror
-  const bool own_quad = ((threadIdx.x >> 2) & 1) == ((src >> 2) & 1);
-  return own_quad ? x : m;
 }
 
 // ---------------------------------------------------------------------------
@@ -154,8 +134,10 @@ __global__ __launch_bounds__(1024) void bucket_offsets_kernel(StreamArgs a) {
 // wavefront walks the round's tokens in order; LDS cursors hand out positions.
 // Within one instruction all slots are distinct (a token's write ids are distinct,
 // and so are its read ids), and writes are issued before reads, so accesses of
-// one slot keep token order with writes first.
+// one slot keep token order with writes first.  TRAIN: the entry's second word
+// holds the access's position in the token's id list instead of its weight.
 // ---------------------------------------------------------------------------
+template <bool TRAIN>
 __global__ __launch_bounds__(64) void bucket_scatter_kernel(StreamArgs a) {
   __shared__ int cur[MAX_GT];
   const int64_t w = blockIdx.x / a.rounds;
@@ -174,13 +156,13 @@ __global__ __launch_bounds__(64) void bucket_scatter_kernel(StreamArgs a) {
     const int tt = (int)(t - t_lo);
     for (int k = lane; k < a.W; k += 64) {
       const int32_t s = a.idx_w[tok * a.W + k];
-      const float q = a.wt_w[tok * a.W + k];
+      const float q = TRAIN ? __uint_as_float((uint32_t)k) : a.wt_w[tok * a.W + k];
       const int pos = atomicAdd(&cur[group_of((uint32_t)s, a.log2GT)], 1);
       ent[pos] = make_entry((uint32_t)s, tt, q, false);
     }
     for (int k = lane; k < a.R; k += 64) {
       const int32_t s = a.idx_r[tok * a.R + k];
-      const float q = a.wt_r[tok * a.R + k];
+      const float q = TRAIN ? __uint_as_float((uint32_t)k) : a.wt_r[tok * a.R + k];
       const int pos = atomicAdd(&cur[group_of((uint32_t)s, a.log2GT)], 1);
       ent[pos] = make_entry((uint32_t)s, tt, q, true);
     }
@@ -784,6 +766,27 @@ StreamLayout stream_layout(const sdm_dims& d, const StreamPlan& pl) {
 
 }  // namespace
 
+hipError_t launch_stream_buckets(const StreamArgs& a, int64_t walks, bool train,
+                                 hipStream_t st) {
+  {
+    KernelTimer kt("bucket_count", st);
+    hipLaunchKernelGGL(bucket_count_kernel, dim3((unsigned)(walks * a.rounds)), dim3(256), 0, st,
+                       a);
+  }
+  {
+    KernelTimer kt("bucket_offsets", st);
+    hipLaunchKernelGGL(bucket_offsets_kernel, dim3((unsigned)walks), dim3(1024), 0, st, a);
+  }
+  KernelTimer kt("bucket_scatter", st);
+  if (train)
+    hipLaunchKernelGGL(bucket_scatter_kernel<true>, dim3((unsigned)(walks * a.rounds)), dim3(64),
+                       0, st, a);
+  else
+    hipLaunchKernelGGL(bucket_scatter_kernel<false>, dim3((unsigned)(walks * a.rounds)),
+                       dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
 size_t stream_workspace_bytes(const sdm_dims& d, const StreamPlan& pl) {
   return stream_layout(d, pl).total;
 }
@@ -880,8 +883,8 @@ hipError_t launch_stream_scan(const ScanArgs& sa, const StreamPlan& pl, void* ws
     } else {
       {
         KernelTimer kt("bucket_scatter", st);
-        hipLaunchKernelGGL(bucket_scatter_kernel, dim3((unsigned)(walks * a.rounds)), dim3(64), 0,
-                           st, a);
+        hipLaunchKernelGGL(bucket_scatter_kernel<false>, dim3((unsigned)(walks * a.rounds)),
+                           dim3(64), 0, st, a);
       }
       const dim3 grid((unsigned)(walks * pl.S * pl.parts));
       KernelTimer kt("stream_scan", st);

@@ -283,6 +283,13 @@ const char* sdm_status_string(int32_t status) {
   }
 }
 
+// Backward workspace: per-walk d_gamma partials (direct schedule), or the stream
+// schedule's buckets, dy, per-slice partial dots and per-part d_v.
+static size_t backward_ws_bytes(const sdm_dims* d) {
+  if (backward_uses_stream(*d)) return align_up(stream_backward_workspace_bytes(*d));
+  return align_up((size_t)d->B * d->H * d->d_v * 4);
+}
+
 size_t sdm_workspace_bytes(const sdm_dims* d, int32_t entry) {
   Derived dv;
   if (check_dims(d, &dv) != SDM_OK || dv.M == 0) return 0;
@@ -292,7 +299,7 @@ size_t sdm_workspace_bytes(const sdm_dims* d, int32_t entry) {
     case SDM_ENTRY_FORWARD:
       return product_sizes(d, dv.M).total + select_ws_bytes(d, dv, false) +
              align_up(scan_workspace_bytes(*d));
-    case SDM_ENTRY_SCAN_BACKWARD: return align_up((size_t)d->B * d->H * d->d_v * 4);
+    case SDM_ENTRY_SCAN_BACKWARD: return backward_ws_bytes(d);
     default: return 0;
   }
 }
@@ -338,15 +345,16 @@ int32_t sdm_scan(const sdm_dims* d, const sdm_sel* in, const float* norm_w, void
                     false);
 }
 
-// The training entries run the direct schedule, fp32 state, per-slot rule.
-int32_t check_train_flags(const sdm_dims* d) {
-  if (d->flags & (SDM_FLAG_STATE_BF16 | SDM_FLAG_DELTA_GDN | SDM_FLAG_SCAN_STREAM |
-                  SDM_FLAG_SCAN_TWO_PHASE))
+// The training entries take fp32 state and the per-slot rule.  The training forward
+// runs the direct schedule; the backward runs the direct or the stream schedule.
+static int32_t check_train_flags(const sdm_dims* d, bool backward) {
+  if (d->flags & (SDM_FLAG_STATE_BF16 | SDM_FLAG_DELTA_GDN | SDM_FLAG_SCAN_TWO_PHASE))
     return SDM_ERR_UNSUPPORTED;
+  if (!backward && (d->flags & SDM_FLAG_SCAN_STREAM)) return SDM_ERR_UNSUPPORTED;
   return SDM_OK;
 }
 
-int32_t log_format(const sdm_dims* d) {
+static int32_t log_format(const sdm_dims* d) {
   return (d->flags & SDM_FLAG_LOG_FP8) ? LOG_FP8 : (d->flags & SDM_FLAG_LOG_INT4) ? LOG_INT4
                                                                                    : LOG_F32;
 }
@@ -356,7 +364,7 @@ int32_t sdm_scan_train(const sdm_dims* d, const sdm_sel* in, const float* norm_w
   Derived dv;
   int32_t st = check_dims(d, &dv);
   if (st != SDM_OK) return st;
-  if ((st = check_train_flags(d)) != SDM_OK) return st;
+  if ((st = check_train_flags(d, false)) != SDM_OK) return st;
   if (dv.M == 0) return SDM_OK;
   if ((st = check_sel(in, false)) != SDM_OK) return st;
   const int32_t fmt = log_format(d);
@@ -382,7 +390,7 @@ int32_t sdm_scan_backward(const sdm_dims* d, const sdm_sel* in, const float* nor
   Derived dv;
   int32_t st = check_dims(d, &dv);
   if (st != SDM_OK) return st;
-  if ((st = check_train_flags(d)) != SDM_OK) return st;
+  if ((st = check_train_flags(d, true)) != SDM_OK) return st;
   if (dv.M == 0) return SDM_OK;
   if ((st = check_sel(in, false)) != SDM_OK) return st;
   const int32_t fmt = log_format(d);
@@ -397,7 +405,7 @@ int32_t sdm_scan_backward(const sdm_dims* d, const sdm_sel* in, const float* nor
   if ((norm_w && !aligned16(norm_w)) || (g->d_norm_w && !aligned16(g->d_norm_w)) ||
       (log_scale && !aligned16(log_scale)))
     return SDM_ERR_ALIGN;
-  const size_t need = align_up((size_t)d->B * d->H * d->d_v * 4);
+  const size_t need = backward_ws_bytes(d);
   if (!ws || ws_bytes < need) return SDM_ERR_WORKSPACE;
   if (!aligned16(ws)) return SDM_ERR_ALIGN;
   ScanBackArgs a;
@@ -434,6 +442,8 @@ int32_t sdm_scan_backward(const sdm_dims* d, const sdm_sel* in, const float* nor
   a.eps = d->eps;
   TimingScope timing(d);
   (void)hipGetLastError();
+  if (backward_uses_stream(*d))
+    return hip_status(launch_stream_backward(*d, a, g->d_norm_w, ws, (hipStream_t)stream));
   return hip_status(launch_scan_backward(a, g->d_norm_w, (hipStream_t)stream));
 }
 

@@ -103,6 +103,37 @@ struct StreamArgs {
   float eps;
   int32_t S, parts, GT, log2GT, log2GW, rounds;
 };
+// Tokens per round of the slot-owner stream schedules (entries keep the token's
+// place in its round in 8 bits), and the most lane groups one walk's slots are
+// hashed over.
+constexpr int kStreamRound = 256;
+constexpr int kStreamMaxGT = 4096;
+
+// Value of lane `src` of this lane's LPG-lane group (LPG = 4 or 8), moved by DPP in
+// the vector ALU (no LDS traffic).  quad_perm broadcasts within each quad; for
+// 8-lane groups row_half_mirror brings the other quad's broadcast across.
+template <int LPG>
+__device__ __forceinline__ uint32_t group_bcast(uint32_t v, int src) {
+  const int q = src & 3;
+  const int qp = q | (q << 2) | (q << 4) | (q << 6);  // quad_perm(q,q,q,q)
+  uint32_t x;
+  switch (qp) {
+    case 0x00: x = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x00, 0xf, 0xf, false); break;
+    case 0x55: x = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x55, 0xf, 0xf, false); break;
+    case 0xaa: x = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xaa, 0xf, 0xf, false); break;
+    default: x = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xff, 0xf, 0xf, false); break;
+  }
+  if (LPG == 4) return x;
+  const uint32_t m = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xf, 0xf, false);  // row_half_mirror
+  const bool own_quad = ((threadIdx.x >> 2) & 1) == ((src >> 2) & 1);
+  return own_quad ? x : m;
+}
+
+// Bucketing pre-passes of the stream schedules (count, offsets, scatter) for one
+// token chunk; train: entries carry the access's position in its token's id list
+// in place of the weight.
+hipError_t launch_stream_buckets(const StreamArgs& a, int64_t walks, bool train, hipStream_t st);
+
 struct StreamPlan {
   int SW, S, NT, parts, GT, log2GT, rounds;
   bool two_phase;  // clean reads summed in registers after each round's writes
@@ -145,6 +176,26 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
   return (c & 0x80u) ? -mag : mag;
 }
 
+// Logged row r (rows of dv values), columns 4 li .. 4 li + 3: fp32, or decoded with the
+// row's absmax.
+__device__ __forceinline__ float4 log_load(const void* log, const float* log_scale, int fmt,
+                                           int64_t r, int dv, int li) {
+  if (fmt == LOG_F32)
+    return reinterpret_cast<const float4*>(static_cast<const float*>(log) + r * dv)[li];
+  const uint8_t* base = static_cast<const uint8_t*>(log);
+  const float mx = log_scale[r];
+  if (fmt == LOG_FP8) {
+    const uint32_t w = reinterpret_cast<const uint32_t*>(base + r * dv)[li];
+    const float unit = mx / 448.0f;
+    return make_float4(e4m3_decode(w & 0xff) * unit, e4m3_decode((w >> 8) & 0xff) * unit,
+                       e4m3_decode((w >> 16) & 0xff) * unit, e4m3_decode(w >> 24) * unit);
+  }
+  const uint32_t w = reinterpret_cast<const uint16_t*>(base + r * (dv / 2))[li];
+  const float unit = mx / 7.0f;
+  auto q = [&](uint32_t s) { return (float)(((int)((w >> s) & 15u) ^ 8) - 8) * unit; };
+  return make_float4(q(0), q(4), q(8), q(12));
+}
+
 // Backward of the scan and norm/gate (scan_backward.hip): reverse walk per (b, h).
 struct ScanBackArgs {
   const int32_t* idx_w;
@@ -175,6 +226,12 @@ struct ScanBackArgs {
   float eps;
 };
 hipError_t launch_scan_backward(const ScanBackArgs& a, float* d_norm_w, hipStream_t s);
+// The same backward on the slot-owner stream schedule (scan_stream_backward.hip), for
+// long token runs; needs stream_backward_workspace_bytes(d) of workspace.
+bool backward_uses_stream(const sdm_dims& d);
+size_t stream_backward_workspace_bytes(const sdm_dims& d);
+hipError_t launch_stream_backward(const sdm_dims& d, const ScanBackArgs& a, float* d_norm_w,
+                                  void* ws, hipStream_t s);
 
 // Shared initial state (shared_m0.hip): set the touched bit of every id the call
 // reads or writes; copy M0[h][id] into the store on the first touch.

@@ -169,6 +169,15 @@ def test_training_entries_validate_first(lib):
     assert need == d.B * d.H * d.d_v * 4
     assert back(nb=need - 1) == _lib.SDM_ERR_WORKSPACE
     assert back(grads=_lib.SdmScanGrads(*([FAKE] * 6 + [FAKE + 8]))) == _lib.SDM_ERR_ALIGN
+    # the stream schedule (forced, or by default from 256 tokens) takes its buckets,
+    # dy, per-slice partial dots and per-part d_v from the workspace
+    assert back(dd=_d(T=64, flags=_lib.SDM_FLAG_SCAN_TWO_PHASE)) == _lib.SDM_ERR_UNSUPPORTED
+    for ds in (_d(T=64, flags=_lib.SDM_FLAG_SCAN_STREAM), _d(T=256)):
+        ns = lib.sdm_workspace_bytes(ctypes.byref(ds), _lib.SDM_ENTRY_SCAN_BACKWARD)
+        assert ns > ds.B * ds.T * ds.H * (ds.W + ds.R) * 8
+        assert back(dd=ds, nb=ns - 1) == _lib.SDM_ERR_WORKSPACE
+    dd = _d(T=256, flags=_lib.SDM_FLAG_SCAN_DIRECT)
+    assert lib.sdm_workspace_bytes(ctypes.byref(dd), _lib.SDM_ENTRY_SCAN_BACKWARD) == need
 
 
 def test_null_dims(lib):

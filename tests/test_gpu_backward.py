@@ -1,5 +1,9 @@
 """Training path (sdm_scan_train + sdm_scan_backward) against the oracle.
 
+The backward runs on either schedule: the direct reverse walk (one workgroup per
+memory) and the slot-owner stream schedule (the default from 256 tokens); every
+parity case runs on both.
+
 * The training forward equals sdm_scan with the direct schedule bit for bit (state,
   y, out), and its write log holds the rows each write replaced (oracle log within
   the fp32 tolerance).
@@ -7,7 +11,9 @@
   gradients (of out and of the final state), matches the oracle's scan_backward
   run on the same values: every gradient within 1e-4 of its tensor's scale (fp32
   sums over up to T tokens against fp64), the initial state restored bit for bit,
-  and the gradients bit-reproducible across runs (fixed summation order).
+  and the gradients bit-reproducible across runs (fixed summation order; on the
+  stream schedule d_v is summed with LDS float atomics and is reproducible up to
+  summation order only).
 """
 import numpy as np
 import pytest
@@ -46,9 +52,21 @@ def _close_to_scale(got, exp, what, rel=1e-4):
                            f"max err {err.max():.3e}")
 
 
-def _run(d, prod, gamma, m0, rng, walks):
+SCHED = {"direct": _lib.SDM_FLAG_SCAN_DIRECT, "stream": _lib.SDM_FLAG_SCAN_STREAM}
+
+
+def _back_dims(d, sched):
+    db = _lib.dims(**{k: getattr(d, k) for k in ("B", "T", "d_model", "H", "n", "W", "R", "d_v",
+                                                  "in_dtype", "gate_act", "eps", "flags")})
+    if sched is not None:
+        db.flags |= SCHED[sched]
+    return db
+
+
+def _run(d, prod, gamma, m0, rng, walks, sched=None):
     """GPU forward + backward; oracle backward of the listed walks from the GPU's values."""
     B, T, H, N, dv = d.B, d.T, d.H, d.n * d.n, d.d_v
+    db = _back_dims(d, sched)
     pd = {k: to_dev(v) for k, v in prod.items()}
     gam = to_dev(gamma) if gamma is not None else None
     state = to_dev(m0)
@@ -61,7 +79,7 @@ def _run(d, prod, gamma, m0, rng, walks):
     d_out = rng.standard_normal((B, T, H, dv)).astype(np.float32)
     d_st = (rng.standard_normal((B, H, N, dv)) * 0.1).astype(np.float32)
     dS = to_dev(d_st)
-    g = ops.scan_backward(d, pd, gam, state, dS, y, log, to_dev(d_out))
+    g = ops.scan_backward(db, pd, gam, state, dS, y, log, to_dev(d_out))
     torch.cuda.synchronize()
     if fmt == "fp32":
         assert np.array_equal(host(state), m0), "initial state not restored bit for bit"
@@ -89,21 +107,30 @@ def _run(d, prod, gamma, m0, rng, walks):
     return out, y, log, state, g, pd, gam, dS
 
 
-@pytest.mark.parametrize("B,T,H,n,W,R,d_v,mode", [
+CASES = [
     (1, 64, 1, 16, 8, 8, 16, "random"),
     (2, 120, 2, 8, 16, 16, 32, "repeat"),     # N = 64: slots rewritten and re-read constantly
     (2, 50, 3, 8, 32, 32, 64, "random"),
     (1, 40, 2, 12, 16, 8, 128, "same"),       # every token the same selection
     (1, 30, 1, 16, 64, 128, 256, "random"),
     (2, 17, 1, 4, 16, 16, 16, "random"),      # every slot written and read by every token
-])
-def test_backward_matches_oracle(B, T, H, n, W, R, d_v, mode):
+    # several stream rounds (256 tokens) with a ragged last one
+    (1, 700, 2, 8, 16, 16, 32, "repeat"),
+    (2, 300, 1, 16, 64, 64, 128, "random"),
+    (1, 520, 1, 6, 16, 32, 16, "same"),
+    (1, 260, 1, 12, 32, 16, 256, "repeat"),
+]
+
+
+@pytest.mark.parametrize("sched", ["direct", "stream"])
+@pytest.mark.parametrize("B,T,H,n,W,R,d_v,mode", CASES)
+def test_backward_matches_oracle(B, T, H, n, W, R, d_v, mode, sched):
     rng = np.random.default_rng(B * 1000 + T + W + R + d_v)
     prod = random_products(rng, B, T, H, n, W, R, d_v, mode)
     m0 = (rng.standard_normal((B, H, n * n, d_v)) * 0.3).astype(np.float32)
     gamma = rng.uniform(0.5, 1.5, (H, d_v)).astype(np.float32)
     d = _dims(B=B, T=T, H=H, n=n, W=W, R=R, d_v=d_v)
-    _run(d, prod, gamma, m0, rng, [(b, h) for b in range(B) for h in range(H)])
+    _run(d, prod, gamma, m0, rng, [(b, h) for b in range(B) for h in range(H)], sched)
 
 
 def test_training_forward_equals_scan_and_log_is_the_replaced_rows():
@@ -129,13 +156,15 @@ def test_training_forward_equals_scan_and_log_is_the_replaced_rows():
             assert_close(lh[b, :, h], olog, f"log walk {(b, h)}")
 
 
-def test_backward_is_bit_reproducible_and_without_norm_weight():
+@pytest.mark.parametrize("sched", ["direct", "stream"])
+def test_backward_is_bit_reproducible_and_without_norm_weight(sched):
     rng = np.random.default_rng(62)
-    B, T, H, n, W, R, d_v = 2, 60, 2, 8, 16, 16, 32
+    B, T, H, n, W, R, d_v = 2, 300, 2, 8, 16, 16, 32
     prod = random_products(rng, B, T, H, n, W, R, d_v, "repeat")
     m0 = (rng.standard_normal((B, H, n * n, d_v)) * 0.3).astype(np.float32)
     d = _dims(B=B, T=T, H=H, n=n, W=W, R=R, d_v=d_v)
-    out, y, log, state, g, pd, gam, dS = _run(d, prod, None, m0, rng, [(0, 0), (1, 1)])
+    out, y, log, state, g, pd, gam, dS = _run(d, prod, None, m0, rng, [(0, 0), (1, 1)], sched)
+    db = _back_dims(d, sched)
     # the backward left M_0 in `state`: redo the forward to get M_T back, then run the
     # backward twice with the same incoming gradients
     state2 = state.clone()
@@ -146,14 +175,18 @@ def test_backward_is_bit_reproducible_and_without_norm_weight():
         s_ = state2.clone()
         ds = torch.ones_like(s_) * 0.25
         dout = torch.full_like(y, 0.5)
-        runs.append((ops.scan_backward(d, pd, None, s_, ds, y, log, dout), ds))
+        runs.append((ops.scan_backward(db, pd, None, s_, ds, y, log, dout), s_, ds))
     torch.cuda.synchronize()
     for k in runs[0][0]:
-        assert torch.equal(runs[0][0][k], runs[1][0][k]), k
-    assert torch.equal(runs[0][1], runs[1][1])
+        if sched == "stream" and k == "d_v":
+            assert_close(host(runs[0][0][k]), host(runs[1][0][k]), k)
+        else:
+            assert torch.equal(runs[0][0][k], runs[1][0][k]), k
+    assert torch.equal(runs[0][1], runs[1][1]) and torch.equal(runs[0][2], runs[1][2])
 
 
-def test_bench_layer_shape_reduced_tokens():
+@pytest.mark.parametrize("sched", ["direct", "stream"])
+def test_bench_layer_shape_reduced_tokens(sched):
     """The 1.4B-like layer's N, W, R, d_v and H with 256 tokens per sequence, products
     from the GPU's own selection pass."""
     wl = synth.small("layer1p4b", B=2, T=256)
@@ -163,7 +196,7 @@ def test_bench_layer_shape_reduced_tokens():
     prod = {k: host(v) for k, v in p.items()}
     m0 = np.broadcast_to(h["m0"], (wl.B,) + h["m0"].shape).copy()
     rng = np.random.default_rng(63)
-    _run(dm, prod, h["gamma"], m0, rng, [(0, 0), (wl.B - 1, wl.H - 1)])
+    _run(dm, prod, h["gamma"], m0, rng, [(0, 0), (wl.B - 1, wl.H - 1)], sched)
 
 
 # ---- quantised write log (fp8 / int4) ----------------------------------------------
@@ -193,12 +226,14 @@ def test_quantised_log_codes_equal_the_oracle(fmt):
     assert np.array_equal(host(log_b["rows"]), codes)
 
 
+@pytest.mark.parametrize("sched", ["direct", "stream"])
 @pytest.mark.parametrize("fmt", ["fp8", "int4"])
 @pytest.mark.parametrize("B,T,H,n,W,R,d_v,mode", [
     (2, 120, 2, 8, 16, 16, 32, "repeat"),
     (1, 30, 1, 16, 64, 128, 256, "random"),
+    (1, 300, 2, 8, 16, 16, 64, "repeat"),
 ])
-def test_backward_with_quantised_log(B, T, H, n, W, R, d_v, mode, fmt):
+def test_backward_with_quantised_log(B, T, H, n, W, R, d_v, mode, fmt, sched):
     """Against the oracle's backward on the decoded rows; both restore the same
     decoded rows.  The distance to the fp32-log gradients is reported."""
     rng = np.random.default_rng(B * 100 + T + d_v)
@@ -207,9 +242,71 @@ def test_backward_with_quantised_log(B, T, H, n, W, R, d_v, mode, fmt):
     gamma = rng.uniform(0.5, 1.5, (H, d_v)).astype(np.float32)
     d = _dims(B=B, T=T, H=H, n=n, W=W, R=R, d_v=d_v, flags=LOG_FLAGS[fmt])
     _, _, _, state, g, _, _, _ = _run(d, prod, gamma, m0, np.random.default_rng(7),
-                                      [(b, h) for b in range(B) for h in range(H)])
+                                      [(b, h) for b in range(B) for h in range(H)], sched)
     d32 = _dims(B=B, T=T, H=H, n=n, W=W, R=R, d_v=d_v)
-    _, _, _, _, g32, _, _, _ = _run(d32, prod, gamma, m0, np.random.default_rng(7), [(0, 0)])
+    _, _, _, _, g32, _, _, _ = _run(d32, prod, gamma, m0, np.random.default_rng(7), [(0, 0)],
+                                    sched)
     rel = {k: float((g[k] - g32[k]).abs().max() / g32[k].abs().max()) for k in ("d_v", "d_alpha")}
     drift = float(np.abs(host(state) - m0).max() / np.abs(m0).max())
     say(f"  {fmt} log: gradient distance to the fp32 log {rel}; restored state off by {drift:.2e}")
+
+
+def _strided_products(rng, B, T, H, n, W, R, d_v):
+    """Distinct ids per token without a per-token loop: an offset and an odd stride
+    modulo N = n^2 (a power of two), ascending."""
+    N = n * n
+    assert N & (N - 1) == 0 and max(W, R) <= N
+    shp = (B, T, H)
+
+    def ids(count):
+        o = rng.integers(0, N, shp + (1,))
+        st = rng.integers(0, N // 2, shp + (1,)) * 2 + 1
+        return np.sort((o + st * np.arange(count)) % N, axis=-1).astype(np.int32)
+
+    def wts(count):
+        w = rng.uniform(0.05, 1.0, shp + (count,)).astype(np.float32)
+        return (w / w.sum(-1, keepdims=True)).astype(np.float32)
+
+    return dict(idx_w=ids(W), wt_w=wts(W), idx_r=ids(R), wt_r=wts(R),
+                v=rng.standard_normal(shp + (d_v,)).astype(np.float32),
+                gate=rng.uniform(0, 1, shp + (d_v,)).astype(np.float32),
+                alpha=rng.uniform(0.3, 1.0, shp).astype(np.float32),
+                beta=rng.uniform(0.0, 1.0, shp).astype(np.float32))
+
+
+def test_stream_backward_over_several_token_chunks():
+    """A run long enough that the stream schedule splits it into token chunks (its
+    per-token buffers are bounded near 2 GiB): sampled walks against the oracle,
+    the initial state restored bit for bit, d_norm_w against the direct schedule."""
+    B, T, H, n, W, R, d_v = 8, 66000, 4, 8, 16, 16, 16
+    rng = np.random.default_rng(65)
+    prod = _strided_products(rng, B, T, H, n, W, R, d_v)
+    m0 = (rng.standard_normal((B, H, n * n, d_v)) * 0.3).astype(np.float32)
+    gamma = rng.uniform(0.5, 1.5, (H, d_v)).astype(np.float32)
+    d = _dims(B=B, T=T, H=H, n=n, W=W, R=R, d_v=d_v)
+    pd = {k: to_dev(v) for k, v in prod.items()}
+    gam = to_dev(gamma)
+    state = to_dev(m0)
+    _, y, log = ops.scan_train(d, pd, gam, state)
+    d_out = to_dev(rng.standard_normal((B, T, H, d_v)).astype(np.float32))
+    d_st = to_dev((rng.standard_normal((B, H, n * n, d_v)) * 0.1).astype(np.float32))
+    st_T = state.clone()
+    runs = {}
+    for sched in ("stream", "direct"):
+        s_, ds = st_T.clone(), d_st.clone()
+        g = ops.scan_backward(_back_dims(d, sched), pd, gam, s_, ds, y, log, d_out)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(s_), m0), f"{sched}: initial state not restored"
+        runs[sched] = (g, ds)
+    say(f"  stream workspace {_lib.workspace_bytes(_back_dims(d, 'stream'), _lib.SDM_ENTRY_SCAN_BACKWARD) / 2**30:.2f} GiB")
+    g, ds = runs["stream"]
+    for b, h in [(0, 0), (B - 1, H - 1)]:
+        sel = {k: prod[k][b, :, h] for k in prod}
+        og, _, odM = O.scan_backward(host(st_T[b, h]), host(log["rows"][b, :, h]), sel["idx_w"],
+                                     sel["wt_w"], sel["idx_r"], sel["wt_r"], sel["v"],
+                                     sel["alpha"], sel["beta"], host(y[b, :, h]), sel["gate"],
+                                     gamma[h], d.eps, host(d_out[b, :, h]), host(d_st[b, h]))
+        for k in ("d_v", "d_gate", "d_alpha", "d_beta", "d_wt_w", "d_wt_r"):
+            _close_to_scale(host(g[k][b, :, h]), og[k], f"{k} walk {(b, h)}")
+        _close_to_scale(host(ds[b, h]), odM, f"d_state walk {(b, h)}")
+    _close_to_scale(host(g["d_norm_w"]), host(runs["direct"][0]["d_norm_w"]), "d_norm_w")
