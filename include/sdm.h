@@ -52,7 +52,7 @@ extern "C" {
 #define SDM_API
 #endif
 
-#define SDM_ABI_VERSION 1
+#define SDM_ABI_VERSION 2
 
 /* status codes */
 #define SDM_OK 0
@@ -78,6 +78,7 @@ extern "C" {
 #define SDM_ENTRY_SCAN 1
 #define SDM_ENTRY_FORWARD 2
 #define SDM_ENTRY_SCAN_BACKWARD 3
+#define SDM_ENTRY_SCAN_TRAIN 4
 
 /* scan schedule flags (sdm_dims.flags) */
 #define SDM_FLAG_SCAN_DIRECT 1    /* one workgroup per (b,h), tokens in lock-step */
@@ -260,17 +261,23 @@ SDM_API int32_t sdm_forward(const sdm_dims* dims, const void* x, const void* w_p
  * paragraph: the sparse update is applied in place and undone in backward, keeping
  * the N x d state plus the T x W x d rows the writes overwrote).
  *
- * sdm_scan_train: sdm_scan (direct schedule) that also records the write log.
+ * sdm_scan_train: sdm_scan that also records the write log.
  *   log     OUT: log[b][t][h][k] = the state row idx_w[..][k] just before token t's
  *           write: [B, T, H, W, d_v] fp32, or uint8 codes ([.., d_v] with
  *           SDM_FLAG_LOG_FP8, [.., d_v / 2] with SDM_FLAG_LOG_INT4)
  *   log_scale [B, T, H, W] fp32 OUT: each logged row's absmax (quantised formats;
  *           may be NULL for fp32)
  *   y_raw   required here (the backward needs it)
- *   Other arguments as in sdm_scan; state, out and y_raw equal sdm_scan's with
- *   SDM_FLAG_SCAN_DIRECT bit for bit.  fp32 state and the per-slot rule only:
- *   SDM_FLAG_STATE_BF16, SDM_FLAG_DELTA_GDN, SDM_FLAG_SCAN_STREAM or
- *   SDM_FLAG_SCAN_TWO_PHASE give SDM_ERR_UNSUPPORTED.  No workspace.
+ *   ws      >= sdm_workspace_bytes(dims, SDM_ENTRY_SCAN_TRAIN) bytes (may be NULL
+ *           if 0)
+ *   Schedules: with an fp32 log, the stream schedule from 256 tokens (or with
+ *   SDM_FLAG_SCAN_STREAM), else the direct one (SDM_FLAG_SCAN_DIRECT forces it); a
+ *   quantised log is written by the direct schedule (SDM_FLAG_SCAN_STREAM with one
+ *   is SDM_ERR_UNSUPPORTED).  The state and the log equal those of sdm_scan and of
+ *   either schedule bit for bit; y_raw and out equal sdm_scan's on the same
+ *   schedule, bit for bit on the direct one and up to fp32 summation order on the
+ *   stream one.  fp32 state and the per-slot rule only: SDM_FLAG_STATE_BF16,
+ *   SDM_FLAG_DELTA_GDN or SDM_FLAG_SCAN_TWO_PHASE give SDM_ERR_UNSUPPORTED.
  *
  * sdm_scan_backward: gradients of that call, walking the tokens in reverse (per
  * token: the norm and gate, the read, then the write, whose overwritten rows are
@@ -285,8 +292,12 @@ SDM_API int32_t sdm_forward(const sdm_dims* dims, const void* x, const void* w_p
  *           [B,T,H,d_v], d_alpha and d_beta [B,T,H]; d_norm_w [H, d_v] (summed over
  *           the batch) or NULL
  *   ws      >= sdm_workspace_bytes(dims, SDM_ENTRY_SCAN_BACKWARD) bytes
- * Every sum runs in a fixed order: results are bit-reproducible.  Flags as for
- * sdm_scan_train.  One workgroup per (b, h), tokens in lock-step.
+ * Schedules: the stream schedule from 256 tokens (or with SDM_FLAG_SCAN_STREAM):
+ * slot-owner lane groups walk the accesses of each slot in reverse, any log format;
+ * else (or with SDM_FLAG_SCAN_DIRECT) one workgroup per (b, h), tokens in lock-step.
+ * Every sum runs in a fixed order, so results are bit-reproducible, except d_v on
+ * the stream schedule (summed with float atomics: reproducible up to fp32 summation
+ * order).  Other flags as for sdm_scan_train.
  */
 typedef struct sdm_scan_grads {
   float* d_wt_w;
@@ -300,7 +311,7 @@ typedef struct sdm_scan_grads {
 
 SDM_API int32_t sdm_scan_train(const sdm_dims* dims, const sdm_sel* in, const float* norm_w,
                                float* state, float* out, float* y_raw, void* log,
-                               float* log_scale, void* stream);
+                               float* log_scale, void* ws, size_t ws_bytes, void* stream);
 SDM_API int32_t sdm_scan_backward(const sdm_dims* dims, const sdm_sel* in, const float* norm_w,
                                   float* state, float* d_state, const float* y_raw,
                                   const void* log, const float* log_scale, const float* d_out,

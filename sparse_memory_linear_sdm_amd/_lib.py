@@ -19,6 +19,7 @@ SDM_ERR_WORKSPACE, SDM_ERR_UNSUPPORTED, SDM_ERR_HIP = -5, -6, -7
 SDM_DTYPE_F32, SDM_DTYPE_BF16 = 0, 1
 SDM_GATE_NONE, SDM_GATE_SIGMOID, SDM_GATE_SILU = 0, 1, 2
 SDM_ENTRY_SELECT, SDM_ENTRY_SCAN, SDM_ENTRY_FORWARD, SDM_ENTRY_SCAN_BACKWARD = 0, 1, 2, 3
+SDM_ENTRY_SCAN_TRAIN = 4
 SDM_MAX_COUNT, SDM_MAX_HALF = 128, 1024
 SDM_FLAG_SCAN_DIRECT, SDM_FLAG_SCAN_STREAM, SDM_FLAG_SCAN_TWO_PHASE = 1, 2, 4
 SDM_FLAG_TIMING = 8
@@ -97,7 +98,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sdm_forward_shared_m0.argtypes = [P(SdmDims), VP, VP, VP, VP, VP, VP, VP, VP, VP, VP,
                                           ctypes.c_size_t, VP]
     lib.sdm_scan_train.restype = I32
-    lib.sdm_scan_train.argtypes = [P(SdmDims), P(SdmSel), VP, VP, VP, VP, VP, VP, VP]
+    lib.sdm_scan_train.argtypes = [P(SdmDims), P(SdmSel), VP, VP, VP, VP, VP, VP, VP, ctypes.c_size_t,
+                                   VP]
     lib.sdm_scan_backward.restype = I32
     lib.sdm_scan_backward.argtypes = [P(SdmDims), P(SdmSel), VP, VP, VP, VP, VP, VP, VP,
                                       P(SdmScanGrads), VP, ctypes.c_size_t, VP]
@@ -190,10 +192,10 @@ def sdm_forward_shared_m0(d: SdmDims, x, w_proj, A, b_dt, norm_w, m0, state, tou
 
 
 def sdm_scan_train(d: SdmDims, inp: SdmSel, norm_w, state, out, y_raw, log, log_scale=None,
-                   stream=None):
+                   ws=None, ws_bytes=0, stream=None):
     _check(load().sdm_scan_train(ctypes.byref(d), ctypes.byref(inp), _ptr(norm_w), _ptr(state),
-                                 _ptr(out), _ptr(y_raw), _ptr(log), _ptr(log_scale),
-                                 _stream(stream)))
+                                 _ptr(out), _ptr(y_raw), _ptr(log), _ptr(log_scale), _ptr(ws),
+                                 ws_bytes, _stream(stream)))
 
 
 def sdm_scan_backward(d: SdmDims, inp: SdmSel, norm_w, state, d_state, y_raw, log, log_scale,

@@ -174,9 +174,13 @@ __global__ __launch_bounds__(64) void bucket_scatter_kernel(StreamArgs a) {
 // slice; LPG = SW/4 lanes per group; GW = NT/LPG groups; batches of BQ accesses.
 // Per round the slice of v and the gates of the round's tokens are staged in LDS,
 // so a batch only holds its BQ state rows in registers while they are in flight.
+// TRAIN (training forward, fp32 state): entries carry each access's position in its
+// token's id list; the weight is loaded by (token, position), and every write also
+// stores the row it replaces to the write log.
 // ---------------------------------------------------------------------------
-template <int NT, int SW, int BQ, bool BF>
+template <int NT, int SW, int BQ, bool BF, bool TRAIN>
 __global__ __launch_bounds__(NT) void stream_scan_kernel(StreamArgs a) {
+  static_assert(!(TRAIN && BF), "the write log is kept for fp32 state");
   constexpr uint32_t ES = StateT<BF>::ES;
   constexpr int LPG = SW / 4;
   constexpr int GW = NT / LPG;
@@ -245,6 +249,7 @@ __global__ __launch_bounds__(NT) void stream_scan_kernel(StreamArgs a) {
       for (int q = 0; q < EPL; ++q) en[q] = ent[min(i + BQ + q * LPG + li, end - 1)];
       uint32_t slot[BQ], tk[BQ];
       float wq[BQ];
+      int kk[BQ];                 // TRAIN: position in the token's id list
       uint32_t wrm = 0, vam = 0;  // bit j: access j is a valid write / is valid
       float4 mv[BQ];
 #pragma unroll
@@ -254,7 +259,14 @@ __global__ __launch_bounds__(NT) void stream_scan_kernel(StreamArgs a) {
         const uint32_t ey = group_bcast<LPG>(e[q].y, src);
         slot[j] = min(ex & SLOT_MASK, (uint32_t)a.N - 1u);  // stays in bounds
         tk[j] = ex >> 24;                                   // token within the round
-        wq[j] = __uint_as_float(ey & 0x7fffffffu);
+        if constexpr (TRAIN) {
+          tk[j] = min(tk[j], (uint32_t)nt - 1u);
+          kk[j] = min((int)(ey & 0x7fffffffu), ((ey >> 31) ? a.R : a.W) - 1);
+          const int64_t tok = tok_base + (t_lo + tk[j]) * a.H;
+          wq[j] = (ey >> 31) ? a.wt_r[tok * a.R + kk[j]] : a.wt_w[tok * a.W + kk[j]];
+        } else {
+          wq[j] = __uint_as_float(ey & 0x7fffffffu);
+        }
         const bool valid = i + j < end;
         vam |= (uint32_t)valid << j;
         wrm |= (uint32_t)(valid && !(ey >> 31)) << j;
@@ -274,6 +286,12 @@ __global__ __launch_bounds__(NT) void stream_scan_kernel(StreamArgs a) {
           val.w = fwd ? mv[jj].w : val.w;
         }
         const bool isw = (wrm >> j) & 1u;
+        if constexpr (TRAIN) {
+          if (isw) {
+            const int64_t tok = tok_base + (t_lo + tk[j]) * a.H;
+            *reinterpret_cast<float4*>(a.log + (tok * a.W + kk[j]) * dv + sl * SW + li * 4) = val;
+          }
+        }
         {
           // every access stores once (the vector-memory counter then stays static);
           // accesses that do not write go to this lane's trash slot
@@ -806,6 +824,12 @@ hipError_t launch_stream_scan(const ScanArgs& sa, const StreamPlan& pl, void* ws
   a.state = sa.state;
   a.out = sa.out;
   a.y_raw = sa.y_raw;
+  // training forward: the fp32 write log, on the stream schedule (rows replaced by
+  // each write, stored by the slot's owner)
+  const bool train = sa.log != nullptr;
+  if (train && (sa.log_fmt != LOG_F32 || sa.state_bf16 || pl.two_phase))
+    return hipErrorInvalidValue;
+  a.log = static_cast<float*>(sa.log);
   a.B = sa.B;
   a.T = sa.T;
   a.H = sa.H;
@@ -883,19 +907,29 @@ hipError_t launch_stream_scan(const ScanArgs& sa, const StreamPlan& pl, void* ws
     } else {
       {
         KernelTimer kt("bucket_scatter", st);
-        hipLaunchKernelGGL(bucket_scatter_kernel<false>, dim3((unsigned)(walks * a.rounds)),
-                           dim3(64), 0, st, a);
+        if (train)
+          hipLaunchKernelGGL(bucket_scatter_kernel<true>, dim3((unsigned)(walks * a.rounds)),
+                             dim3(64), 0, st, a);
+        else
+          hipLaunchKernelGGL(bucket_scatter_kernel<false>, dim3((unsigned)(walks * a.rounds)),
+                             dim3(64), 0, st, a);
       }
       const dim3 grid((unsigned)(walks * pl.S * pl.parts));
       KernelTimer kt("stream_scan", st);
-      if (pl.SW == 32 && sa.state_bf16)
-        hipLaunchKernelGGL((stream_scan_kernel<1024, 32, 8, true>), grid, dim3(1024), 0, st, a);
+      if (train && pl.SW == 32)
+        hipLaunchKernelGGL((stream_scan_kernel<1024, 32, 6, false, true>), grid, dim3(1024), 0, st,
+                           a);
+      else if (train)
+        hipLaunchKernelGGL((stream_scan_kernel<1024, 16, 6, false, true>), grid, dim3(1024), 0, st,
+                           a);
+      else if (pl.SW == 32 && sa.state_bf16)
+        hipLaunchKernelGGL((stream_scan_kernel<1024, 32, 8, true, false>), grid, dim3(1024), 0, st, a);
       else if (pl.SW == 32)
-        hipLaunchKernelGGL((stream_scan_kernel<1024, 32, 8, false>), grid, dim3(1024), 0, st, a);
+        hipLaunchKernelGGL((stream_scan_kernel<1024, 32, 8, false, false>), grid, dim3(1024), 0, st, a);
       else if (sa.state_bf16)
-        hipLaunchKernelGGL((stream_scan_kernel<1024, 16, 8, true>), grid, dim3(1024), 0, st, a);
+        hipLaunchKernelGGL((stream_scan_kernel<1024, 16, 8, true, false>), grid, dim3(1024), 0, st, a);
       else
-        hipLaunchKernelGGL((stream_scan_kernel<1024, 16, 8, false>), grid, dim3(1024), 0, st, a);
+        hipLaunchKernelGGL((stream_scan_kernel<1024, 16, 8, false, false>), grid, dim3(1024), 0, st, a);
     }
     const int64_t rows = sa.B * a.Tc * sa.H;
     // rows per 256-thread block: 4 wavefronts x (64 / lanes per row)

@@ -283,6 +283,32 @@ const char* sdm_status_string(int32_t status) {
   }
 }
 
+static int32_t log_format(const sdm_dims* d) {
+  return (d->flags & SDM_FLAG_LOG_FP8) ? LOG_FP8 : (d->flags & SDM_FLAG_LOG_INT4) ? LOG_INT4
+                                                                                   : LOG_F32;
+}
+
+// The training entries take fp32 state and the per-slot rule, on the direct or the
+// stream schedule; the training forward keeps a quantised log on the direct one.
+static int32_t check_train_flags(const sdm_dims* d, bool backward) {
+  if (d->flags & (SDM_FLAG_STATE_BF16 | SDM_FLAG_DELTA_GDN | SDM_FLAG_SCAN_TWO_PHASE))
+    return SDM_ERR_UNSUPPORTED;
+  if (!backward && (d->flags & SDM_FLAG_SCAN_STREAM) && log_format(d) != LOG_F32)
+    return SDM_ERR_UNSUPPORTED;
+  return SDM_OK;
+}
+
+// Schedule of the training forward as scan flags: the stream schedule for an fp32 log
+// from 256 tokens (or when asked for), else the direct one.
+static sdm_dims train_dims(const sdm_dims* d) {
+  sdm_dims dd = *d;
+  const bool stream = log_format(d) == LOG_F32 && !(d->flags & SDM_FLAG_SCAN_DIRECT) &&
+                      ((d->flags & SDM_FLAG_SCAN_STREAM) || d->T >= kStreamRound);
+  dd.flags = (d->flags & ~(SDM_FLAG_SCAN_DIRECT | SDM_FLAG_SCAN_STREAM)) |
+             (stream ? SDM_FLAG_SCAN_STREAM : SDM_FLAG_SCAN_DIRECT);
+  return dd;
+}
+
 // Backward workspace: per-walk d_gamma partials (direct schedule), or the stream
 // schedule's buckets, dy, per-slice partial dots and per-part d_v.
 static size_t backward_ws_bytes(const sdm_dims* d) {
@@ -300,6 +326,10 @@ size_t sdm_workspace_bytes(const sdm_dims* d, int32_t entry) {
       return product_sizes(d, dv.M).total + select_ws_bytes(d, dv, false) +
              align_up(scan_workspace_bytes(*d));
     case SDM_ENTRY_SCAN_BACKWARD: return backward_ws_bytes(d);
+    case SDM_ENTRY_SCAN_TRAIN: {
+      const sdm_dims dd = train_dims(d);
+      return align_up(scan_workspace_bytes(dd));
+    }
     default: return 0;
   }
 }
@@ -345,22 +375,9 @@ int32_t sdm_scan(const sdm_dims* d, const sdm_sel* in, const float* norm_w, void
                     false);
 }
 
-// The training entries take fp32 state and the per-slot rule.  The training forward
-// runs the direct schedule; the backward runs the direct or the stream schedule.
-static int32_t check_train_flags(const sdm_dims* d, bool backward) {
-  if (d->flags & (SDM_FLAG_STATE_BF16 | SDM_FLAG_DELTA_GDN | SDM_FLAG_SCAN_TWO_PHASE))
-    return SDM_ERR_UNSUPPORTED;
-  if (!backward && (d->flags & SDM_FLAG_SCAN_STREAM)) return SDM_ERR_UNSUPPORTED;
-  return SDM_OK;
-}
-
-static int32_t log_format(const sdm_dims* d) {
-  return (d->flags & SDM_FLAG_LOG_FP8) ? LOG_FP8 : (d->flags & SDM_FLAG_LOG_INT4) ? LOG_INT4
-                                                                                   : LOG_F32;
-}
-
 int32_t sdm_scan_train(const sdm_dims* d, const sdm_sel* in, const float* norm_w, float* state,
-                       float* out, float* y_raw, void* log, float* log_scale, void* stream) {
+                       float* out, float* y_raw, void* log, float* log_scale, void* ws,
+                       size_t ws_bytes, void* stream) {
   Derived dv;
   int32_t st = check_dims(d, &dv);
   if (st != SDM_OK) return st;
@@ -372,15 +389,17 @@ int32_t sdm_scan_train(const sdm_dims* d, const sdm_sel* in, const float* norm_w
   if (!aligned16(state) || !aligned16(out) || !aligned16(y_raw) || !aligned16(log) ||
       (norm_w && !aligned16(norm_w)) || (log_scale && !aligned16(log_scale)))
     return SDM_ERR_ALIGN;
-  sdm_dims dd = *d;
-  dd.flags |= SDM_FLAG_SCAN_DIRECT;
+  const sdm_dims dd = train_dims(d);
+  const size_t need = align_up(scan_workspace_bytes(dd));
+  if (need && (!ws || ws_bytes < need)) return SDM_ERR_WORKSPACE;
+  if (need && !aligned16(ws)) return SDM_ERR_ALIGN;
   ScanArgs a = scan_args(&dd, dv, in, norm_w, state, out, y_raw);
   a.log = log;
   a.log_scale = log_scale;
   a.log_fmt = fmt;
   TimingScope timing(d);
   (void)hipGetLastError();
-  return hip_status(launch_scan(dd, a, nullptr, 0, (hipStream_t)stream));
+  return hip_status(launch_scan(dd, a, ws, ws_bytes, (hipStream_t)stream));
 }
 
 int32_t sdm_scan_backward(const sdm_dims* d, const sdm_sel* in, const float* norm_w,

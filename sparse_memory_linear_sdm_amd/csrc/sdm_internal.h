@@ -89,6 +89,7 @@ struct StreamArgs {
   void* state;     // fp32, or bf16 when state_bf16
   float* out;
   float* y_raw;
+  float* log;      // training forward: fp32 write log [B, T, H, W, d_v], else null
   int* counts;     // [walks][rounds][GT]
   int* offsets;    // [walks][GT][rounds + 1]
   // owner-stream entry: {slot | token-in-round << 24, weight bits | read << 31}

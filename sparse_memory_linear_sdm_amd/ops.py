@@ -130,7 +130,7 @@ def log_format(d: SdmDims) -> str:
     return "int4" if d.flags & _lib.SDM_FLAG_LOG_INT4 else "fp32"
 
 
-def scan_train(d: SdmDims, products: dict, norm_w, state, out=None, stream=None):
+def scan_train(d: SdmDims, products: dict, norm_w, state, out=None, ws=None, stream=None):
     """Training forward: scan() that also records the write log.  Returns
     (out, y_raw, log) with log a dict: "rows" ([B, T, H, W, d_v] fp32, or uint8 codes
     [.., d_v] (fp8) / [.., d_v / 2] (int4)) and "scale" ([B, T, H, W] absmax, or None)."""
@@ -151,7 +151,9 @@ def scan_train(d: SdmDims, products: dict, norm_w, state, out=None, stream=None)
         width = d.d_v if fmt == "fp8" else d.d_v // 2
         log = dict(rows=torch.empty(lead + (width,), dtype=torch.uint8, device=dev),
                    scale=torch.empty(lead, device=dev))
-    _lib.sdm_scan_train(d, _sel(products), norm_w, state, o, y, log["rows"], log["scale"], stream)
+    ws, nb = _workspace(d, _lib.SDM_ENTRY_SCAN_TRAIN, dev, ws)
+    _lib.sdm_scan_train(d, _sel(products), norm_w, state, o, y, log["rows"], log["scale"], ws, nb,
+                        stream)
     return o, y, log
 
 

@@ -43,7 +43,7 @@ def test_header_constants_match_binding():
 
 
 def test_version_and_status_strings(lib):
-    assert _lib.abi_version() == 1
+    assert _lib.abi_version() == 2
     for code in (0, -1, -2, -3, -4, -5, -6, -7, 12345):
         assert isinstance(_lib.status_string(code), str) and _lib.status_string(code)
     assert _lib.status_string(-5) == "workspace missing or too small"
@@ -144,11 +144,21 @@ def test_shared_m0_entries_validate_first(lib):
 def test_training_entries_validate_first(lib):
     d = _d(T=64)
     s = _sel()
-    train = lambda dd=d, log=FAKE, y=FAKE, sc=None: lib.sdm_scan_train(
-        ctypes.byref(dd), ctypes.byref(s), None, FAKE, FAKE, y, log, sc, None)
-    for bad in (_lib.SDM_FLAG_STATE_BF16, _lib.SDM_FLAG_DELTA_GDN, _lib.SDM_FLAG_SCAN_STREAM,
-                _lib.SDM_FLAG_SCAN_TWO_PHASE):
-        assert train(dd=_d(T=64, flags=bad)) == _lib.SDM_ERR_UNSUPPORTED
+    train = lambda dd=d, log=FAKE, y=FAKE, sc=None, ws=FAKE, nb=1 << 40: lib.sdm_scan_train(
+        ctypes.byref(dd), ctypes.byref(s), None, FAKE, FAKE, y, log, sc, ws, nb, None)
+    for bad in (_lib.SDM_FLAG_STATE_BF16, _lib.SDM_FLAG_DELTA_GDN, _lib.SDM_FLAG_SCAN_TWO_PHASE,
+                _lib.SDM_FLAG_SCAN_STREAM | _lib.SDM_FLAG_LOG_FP8):
+        assert train(dd=_d(T=64, flags=bad), sc=FAKE) == _lib.SDM_ERR_UNSUPPORTED
+    # the direct schedule needs no workspace; the stream schedule (an fp32 log from 256
+    # tokens, or asked for) takes its buckets from the workspace
+    assert lib.sdm_workspace_bytes(ctypes.byref(d), _lib.SDM_ENTRY_SCAN_TRAIN) == 0
+    for ds in (_d(T=64, flags=_lib.SDM_FLAG_SCAN_STREAM), _d(T=256)):
+        nt = lib.sdm_workspace_bytes(ctypes.byref(ds), _lib.SDM_ENTRY_SCAN_TRAIN)
+        assert nt > ds.B * ds.T * ds.H * (ds.W + ds.R) * 8
+        assert train(dd=ds, nb=nt - 1) == _lib.SDM_ERR_WORKSPACE
+        assert train(dd=ds, ws=None) == _lib.SDM_ERR_WORKSPACE
+    for dq in (_d(T=256, flags=_lib.SDM_FLAG_LOG_INT4), _d(T=256, flags=_lib.SDM_FLAG_SCAN_DIRECT)):
+        assert lib.sdm_workspace_bytes(ctypes.byref(dq), _lib.SDM_ENTRY_SCAN_TRAIN) == 0
     assert train(log=None) == _lib.SDM_ERR_NULL
     assert train(y=None) == _lib.SDM_ERR_NULL        # the backward needs y_raw
     assert train(log=FAKE + 4) == _lib.SDM_ERR_ALIGN
