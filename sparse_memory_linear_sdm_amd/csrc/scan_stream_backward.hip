@@ -35,6 +35,14 @@ namespace {
 constexpr int ROUND = kStreamRound;
 constexpr uint32_t SLOT_MASK = 0xFFFFFFu;
 constexpr int PREP_TOK = 256;  // tokens per norm/gate block (d_gamma partial granule)
+constexpr int kNT = 1024;      // threads of a reverse-walk workgroup
+// accesses a lane group keeps in flight: fp32 log / quantised log (decoding takes
+// registers)
+#ifndef SDM_BACK_BQ
+#define SDM_BACK_BQ 4
+#endif
+constexpr int BQ_F32 = SDM_BACK_BQ;
+constexpr int BQ_Q = 4;
 
 struct BackStreamArgs {
   ScanBackArgs s;
@@ -136,7 +144,7 @@ __global__ __launch_bounds__(256) void back_prep_kernel(BackStreamArgs A) {
 // slice; LPG = SW/4 lanes per group; GW = NT/LPG groups; batches of BQ accesses
 // taken from the end of the group's round segment backwards.
 // ---------------------------------------------------------------------------
-template <int NT, int SW, int BQ>
+template <int NT, int SW, int BQ, int LF>
 __global__ __launch_bounds__(NT) void stream_backward_kernel(BackStreamArgs A) {
   constexpr int LPG = SW / 4;
   constexpr int GW = NT / LPG;
@@ -229,7 +237,7 @@ __global__ __launch_bounds__(NT) void stream_backward_kernel(BackStreamArgs A) {
         const int64_t tok = tok_base + (t_lo + tk[j]) * a.H;
         wq[j] = rd ? a.wt_r[tok * a.R + kk[j]] : a.wt_w[tok * a.W + kk[j]];
         const uint32_t off = slot[j] * row_bytes + col_bytes;
-        if (a.log_fmt == LOG_F32) {
+        if constexpr (LF == LOG_F32) {
           const float4* src =
               rd ? reinterpret_cast<const float4*>(Mb + off)
                  : reinterpret_cast<const float4*>(static_cast<const float*>(a.log) +
@@ -238,7 +246,7 @@ __global__ __launch_bounds__(NT) void stream_backward_kernel(BackStreamArgs A) {
           X[j] = *src;
         } else {
           X[j] = rd ? *reinterpret_cast<const float4*>(Mb + off)
-                    : log_load(a.log, a.log_scale, a.log_fmt, tok * a.W + kk[j], dv, c4);
+                    : log_load(a.log, a.log_scale, LF, tok * a.W + kk[j], dv, c4);
         }
         Gd[j] = *reinterpret_cast<const float4*>(Gb + off);
       }
@@ -391,6 +399,25 @@ __global__ __launch_bounds__(256) void gamma_blocks_kernel(const float* __restri
   d_norm_w[e] = s;
 }
 
+template <int SW>
+void launch_walk_sw(int fmt, dim3 grid, hipStream_t st, const BackStreamArgs& A) {
+  if (fmt == LOG_F32)
+    hipLaunchKernelGGL((stream_backward_kernel<kNT, SW, BQ_F32, LOG_F32>), grid, dim3(kNT), 0, st,
+                       A);
+  else if (fmt == LOG_FP8)
+    hipLaunchKernelGGL((stream_backward_kernel<kNT, SW, BQ_Q, LOG_FP8>), grid, dim3(kNT), 0, st, A);
+  else
+    hipLaunchKernelGGL((stream_backward_kernel<kNT, SW, BQ_Q, LOG_INT4>), grid, dim3(kNT), 0, st,
+                       A);
+}
+
+void launch_walk(int sw, int fmt, dim3 grid, hipStream_t st, const BackStreamArgs& A) {
+  if (sw == 32)
+    launch_walk_sw<32>(fmt, grid, st, A);
+  else
+    launch_walk_sw<16>(fmt, grid, st, A);
+}
+
 struct BackPlan {
   int SW, S, parts, GT, log2GT, rounds, gblocks;
   int64_t Tc;
@@ -401,8 +428,6 @@ int ilog2i(int x) {
   while ((1 << l) < x) ++l;
   return l;
 }
-
-constexpr int kNT = 1024;
 
 BackPlan back_plan(const sdm_dims& d) {
   BackPlan pl;
@@ -540,10 +565,7 @@ hipError_t launch_stream_backward(const sdm_dims& d, const ScanBackArgs& sa, flo
     {
       const dim3 grid((unsigned)(walks * pl.S * pl.parts));
       KernelTimer kt("stream_backward", st);
-      if (pl.SW == 32)
-        hipLaunchKernelGGL((stream_backward_kernel<kNT, 32, 4>), grid, dim3(kNT), 0, st, A);
-      else
-        hipLaunchKernelGGL((stream_backward_kernel<kNT, 16, 4>), grid, dim3(kNT), 0, st, A);
+      launch_walk(pl.SW, sa.log_fmt, grid, st, A);
     }
     {
       KernelTimer kt("back_reduce", st);
