@@ -1,12 +1,18 @@
 """Benchmark of the SDM layer forward path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload layer1p4b]
+                    [--mode forward|train]
 
 A step is one pass of the whole path (projection GEMM + gates, product-key
 selection, recurrent sparse scan, RMSNorm + gate) over one batch of synthetic
 input already resident in HBM.  Prints one JSON line with tokens/s, the
 roofline of the dominant kernel (the scan, HBM-bound) and a CPU baseline (the
 fp64 oracle timed on a bounded sample of the same workload on the host).
+
+--mode train times the training path instead: a step is the selection pass, the
+training forward of the scan (with the fp32 write log) and the scan backward
+(random incoming gradients of out and of the final state), which leaves the state
+at M0 again.  Its roofline is the reverse-walk kernel's; no CPU baseline.
 """
 from __future__ import annotations
 
@@ -22,6 +28,8 @@ sys.path.insert(0, ROOT)
 import numpy as np  # noqa: E402
 
 METRIC = "SDM layer tokens/s at N=131072,W=R=64,d_v=128; effective HBM GB/s vs peak"
+METRIC_TRAIN = ("SDM layer training tokens/s (selection, scan forward with write log, scan "
+                "backward); reverse-walk HBM GB/s vs peak")
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_traffic_layer1p4b.txt")
 SCAN_SOURCE = os.path.join(ROOT, "sparse_memory_linear_sdm_amd", "csrc", "scan_stream.hip")
@@ -52,6 +60,7 @@ def parse():
     p.add_argument("--state", choices=("fp32", "bf16"), default="fp32",
                    help="state storage: fp32 (the method's precision) or bf16 with fp32 "
                         "arithmetic (SDM_FLAG_STATE_BF16)")
+    p.add_argument("--mode", choices=("forward", "train"), default="forward")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-tokens", type=int, default=2048,
                    help="tokens of batch entry 0 in the oracle's timed sample")
@@ -94,6 +103,8 @@ def main():
 
     from sparse_memory_linear_sdm_amd import _lib, dims_for, ops, synth
 
+    if args.mode == "train":
+        return train_main(args)
     wl = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -205,6 +216,102 @@ def main():
         res["copy_calibration_bytes"] = {"read": nb, "write": nb}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_tokens)
+    print(json.dumps(res), flush=True)
+
+
+def train_main(args):
+    import torch
+
+    from sparse_memory_linear_sdm_amd import _lib, dims_for, ops, synth
+
+    if args.state != "fp32":
+        print("--mode train keeps fp32 state", file=sys.stderr)
+        sys.exit(2)
+    wl = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = dims_for(wl)
+    _, x_store = synth.gen_x(wl, seed=0)
+    prm = synth.gen_params(wl, seed=0)
+    m0 = synth.gen_m0(wl, seed=0)
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    x = to_dev(x_store)
+    w = to_dev(prm["w_proj_store"])
+    A, b_dt, gamma = to_dev(prm["A"]), to_dev(prm["b_dt"]), to_dev(prm["gamma"])
+    state = to_dev(m0).unsqueeze(0).expand(wl.B, *m0.shape).contiguous()
+    del m0
+    gen = torch.Generator(device=dev).manual_seed(0)
+    d_out = torch.randn((wl.B, wl.T, wl.H, wl.d_v), device=dev, generator=gen)
+    d_state0 = torch.randn(state.shape, device=dev, generator=gen) * 0.1
+    d_state = torch.empty_like(d_state0)
+    prod = ops.alloc_products(d, dev)
+    out = torch.empty((wl.B, wl.T, wl.H, wl.d_v), device=dev)
+    ws_sel = torch.empty(max(_lib.workspace_bytes(d, _lib.SDM_ENTRY_SELECT), 1), dtype=torch.uint8,
+                         device=dev)
+    ws_fwd = torch.empty(max(_lib.workspace_bytes(d, _lib.SDM_ENTRY_SCAN_TRAIN), 1),
+                         dtype=torch.uint8, device=dev)
+    ws_bwd = torch.empty(max(_lib.workspace_bytes(d, _lib.SDM_ENTRY_SCAN_BACKWARD), 1),
+                         dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        d_state.copy_(d_state0)
+        ops.select(d, x, w, A, b_dt, out=prod, ws=ws_sel, stream=stream)
+        _, y, log = ops.scan_train(d, prod, gamma, state, out=out, ws=ws_fwd, stream=stream)
+        ops.scan_backward(d, prod, gamma, state, d_state, y, log, d_out, ws=ws_bwd, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    _lib.timing_read()
+    d.flags |= _lib.SDM_FLAG_TIMING
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    d.flags &= ~_lib.SDM_FLAG_TIMING
+    ms_wall = wall * 1e3 / args.steps
+    per_kernel = {}
+    for name, ms in _lib.timing_read(1 << 16):
+        per_kernel.setdefault(name, []).append(ms)
+    kernels_ms = {k: {"avg": float(np.mean(v)), "launches": len(v)} for k, v in per_kernel.items()}
+    back = next(k for k in ("stream_backward", "scan_backward") if k in kernels_ms)
+    back_ms = kernels_ms[back]["avg"] * kernels_ms[back]["launches"] / args.steps
+    tokens = wl.tokens
+    # per token and head: M and dM read, dM written per read; log and dM read, dM and M
+    # written per write
+    back_bytes = tokens * wl.H * (3 * wl.R + 4 * wl.W) * wl.d_v * 4
+    achieved = back_bytes / (back_ms * 1e-3) / 1e9
+    res = {
+        "metric": METRIC_TRAIN,
+        "value": tokens / (ms_wall * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_wall,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 projection, fp32 selection/scan/gradients, fp32 write log",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "d_model": wl.d_model, "H": wl.H,
+                   "N": wl.N, "n": wl.n, "W": wl.W, "R": wl.R, "d_v": wl.d_v,
+                   "state": "fp32 [B,H,N,d_v]", "tokens_per_step": tokens,
+                   "step": "select + scan_train + scan_backward"},
+        "kernels_ms": kernels_ms,
+        "roofline": {"bound": "hbm", "kernel": back, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch":
+                         back_bytes * args.steps / kernels_ms[back]["launches"]},
+    }
     print(json.dumps(res), flush=True)
 
 
