@@ -270,14 +270,15 @@ SDM_API int32_t sdm_forward(const sdm_dims* dims, const void* x, const void* w_p
  *   y_raw   required here (the backward needs it)
  *   ws      >= sdm_workspace_bytes(dims, SDM_ENTRY_SCAN_TRAIN) bytes (may be NULL
  *           if 0)
- *   Schedules: with an fp32 log, the stream schedule from 256 tokens (or with
- *   SDM_FLAG_SCAN_STREAM), else the direct one (SDM_FLAG_SCAN_DIRECT forces it); a
- *   quantised log is written by the direct schedule (SDM_FLAG_SCAN_STREAM with one
- *   is SDM_ERR_UNSUPPORTED).  The state and the log equal those of sdm_scan and of
- *   either schedule bit for bit; y_raw and out equal sdm_scan's on the same
- *   schedule, bit for bit on the direct one and up to fp32 summation order on the
- *   stream one.  fp32 state and the per-slot rule only: SDM_FLAG_STATE_BF16,
- *   SDM_FLAG_DELTA_GDN or SDM_FLAG_SCAN_TWO_PHASE give SDM_ERR_UNSUPPORTED.
+ *   Schedules: the stream schedule from 256 tokens (or with SDM_FLAG_SCAN_STREAM),
+ *   else the direct one (SDM_FLAG_SCAN_DIRECT forces it).  On the stream schedule a
+ *   quantised log is staged in fp32 in the workspace (token chunks bounded near
+ *   2 GiB) and encoded after each chunk's walk.  The state, the log and its scales
+ *   equal those of sdm_scan and of either schedule bit for bit; y_raw and out equal
+ *   sdm_scan's on the same schedule, bit for bit on the direct one and up to fp32
+ *   summation order on the stream one.  fp32 state and the per-slot rule only:
+ *   SDM_FLAG_STATE_BF16, SDM_FLAG_DELTA_GDN or SDM_FLAG_SCAN_TWO_PHASE give
+ *   SDM_ERR_UNSUPPORTED.
  *
  * sdm_scan_backward: gradients of that call, walking the tokens in reverse (per
  * token: the norm and gate, the read, then the write, whose overwritten rows are

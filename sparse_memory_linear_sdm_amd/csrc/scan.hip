@@ -21,35 +21,6 @@ namespace {
 
 __device__ __forceinline__ float4 f4(float a) { return make_float4(a, a, a, a); }
 
-// Training forward: log row r (this lane's 4 columns of the row before the write),
-// fp32 or quantised with the row's absmax (max over the row group's lanes).
-template <int LPR, int DV>
-__device__ __forceinline__ void log_row(const ScanArgs& a, int64_t r, float4 m, int li) {
-  if (a.log_fmt == LOG_F32) {
-    reinterpret_cast<float4*>(static_cast<float*>(a.log) + r * DV)[li] = m;
-    return;
-  }
-  float mx = fmaxf(fmaxf(fabsf(m.x), fabsf(m.y)), fmaxf(fabsf(m.z), fabsf(m.w)));
-#pragma unroll
-  for (int off = LPR / 2; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, LPR));
-  if (li == 0) a.log_scale[r] = mx;
-  uint8_t* base = static_cast<uint8_t*>(a.log);
-  if (a.log_fmt == LOG_FP8) {
-    const float inv = mx > 0.0f ? 448.0f / mx : 0.0f;
-    reinterpret_cast<uint32_t*>(base + r * DV)[li] =
-        e4m3_encode(m.x * inv) | e4m3_encode(m.y * inv) << 8 | e4m3_encode(m.z * inv) << 16 |
-        e4m3_encode(m.w * inv) << 24;
-  } else {
-    const float inv = mx > 0.0f ? 7.0f / mx : 0.0f;
-    auto q = [&](float x) {
-      const float t = fminf(fmaxf(__builtin_rintf(x * inv), -7.0f), 7.0f);
-      return (uint32_t)(int)t & 15u;
-    };
-    reinterpret_cast<uint16_t*>(base + r * (DV / 2))[li] =
-        (uint16_t)(q(m.x) | q(m.y) << 4 | q(m.z) << 8 | q(m.w) << 12);
-  }
-}
-
 // One workgroup of 256 threads per (b, h).  A row of d_v floats is handled by
 // LPR = d_v/4 lanes (one float4 each); the G = 256/LPR row groups split the W
 // writes and R reads of a token.  Barriers order the write phase, the read phase
@@ -137,7 +108,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
         const float c = be * ww[k];
         const float oc = 1.0f - c;
         if (a.log)  // training forward: the row as it was before this write
-          log_row<LPR, DV>(a, tok * a.W + k, m[j], li);
+          log_store<LPR>(a.log, a.log_scale, a.log_fmt, tok * a.W + k, DV, m[j], li);
         float4 n;
         n.x = fmaf(c, vv.x, oc * (al * m[j].x));
         n.y = fmaf(c, vv.y, oc * (al * m[j].y));
@@ -214,13 +185,22 @@ bool scan_uses_stream(const sdm_dims& d) {
   return d.T >= 16;
 }
 
-size_t scan_workspace_bytes(const sdm_dims& d) {
+// Workspace per token and walk of a training forward whose quantised log is staged
+// in fp32 (stream schedule).
+static int64_t stage_bytes(const sdm_dims& d, bool quantised_log) {
+  return quantised_log ? (int64_t)d.W * d.d_v * 4 : 0;
+}
+
+size_t scan_workspace_bytes(const sdm_dims& d, bool train) {
   if (!scan_uses_stream(d)) return 0;
-  return stream_workspace_bytes(d, plan_stream(d, (int64_t)d.n * d.n));
+  const bool q = train && (d.flags & (SDM_FLAG_LOG_FP8 | SDM_FLAG_LOG_INT4));
+  return stream_workspace_bytes(d, plan_stream(d, (int64_t)d.n * d.n, stage_bytes(d, q)));
 }
 
 hipError_t launch_scan(const sdm_dims& d, const ScanArgs& a, void* ws, size_t, hipStream_t s) {
-  if (scan_uses_stream(d)) return launch_stream_scan(a, plan_stream(d, a.N), ws, s);
+  if (scan_uses_stream(d))
+    return launch_stream_scan(
+        a, plan_stream(d, a.N, stage_bytes(d, a.log != nullptr && a.log_fmt != LOG_F32)), ws, s);
   const dim3 grid((unsigned)(a.B * a.H));
   KernelTimer kt("scan_direct", s);
   const bool gdn = (d.flags & SDM_FLAG_DELTA_GDN) != 0;

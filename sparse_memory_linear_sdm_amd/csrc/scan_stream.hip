@@ -215,6 +215,7 @@ __global__ __launch_bounds__(NT) void stream_scan_kernel(StreamArgs a) {
   const uint2* ent = a.entries + w * a.walk_entries;
   const int* offs = a.offsets + ((int64_t)w * a.GT + gg) * (a.rounds + 1);
   const int64_t tok_base = (b * a.T + a.t0) * a.H + h;  // token t -> tok_base + t*H
+  const int64_t log_base = (b * a.log_T + a.log_t0) * a.H + h;  // TRAIN: log row of t
   float4* trash = a.trash + wg * NT + tid;
 
   for (int r = 0; r < a.rounds; ++r) {
@@ -288,8 +289,8 @@ __global__ __launch_bounds__(NT) void stream_scan_kernel(StreamArgs a) {
         const bool isw = (wrm >> j) & 1u;
         if constexpr (TRAIN) {
           if (isw) {
-            const int64_t tok = tok_base + (t_lo + tk[j]) * a.H;
-            *reinterpret_cast<float4*>(a.log + (tok * a.W + kk[j]) * dv + sl * SW + li * 4) = val;
+            const int64_t lr = log_base + (t_lo + tk[j]) * a.H;
+            *reinterpret_cast<float4*>(a.log + (lr * a.W + kk[j]) * dv + sl * SW + li * 4) = val;
           }
         }
         {
@@ -712,6 +713,28 @@ __global__ __launch_bounds__(256) void norm_gate_kernel(StreamArgs a) {
   }
 }
 
+// Training forward with a quantised log: the walk left the chunk's replaced rows in
+// fp32 in the staging area ([B][Tc of the plan][H][W] rows); encode each row with its
+// absmax into the caller's log at its global place.  LPR lanes per row.
+template <int DV>
+__global__ __launch_bounds__(256) void log_quantize_kernel(StreamArgs a, ScanArgs sa) {
+  constexpr int LPR = DV / 4;  // one float4 per lane (at most a wavefront per row)
+  const int li = threadIdx.x % LPR;
+  const int64_t row = (int64_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+  const int64_t rows = a.B * a.Tc * a.H * a.W;
+  if (row >= rows) return;  // whole row groups
+  const int64_t k = row % a.W;
+  const int64_t bth = row / a.W;
+  const int64_t h = bth % a.H;
+  const int64_t bt = bth / a.H;
+  const int64_t t = bt % a.Tc;
+  const int64_t b = bt / a.Tc;
+  const float4 m = reinterpret_cast<const float4*>(
+      a.log + (((b * a.log_T + t) * a.H + h) * a.W + k) * DV)[li];
+  const int64_t r = ((b * a.T + a.t0 + t) * a.H + h) * a.W + k;
+  log_store<LPR>(sa.log, sa.log_scale, sa.log_fmt, r, DV, m, li);
+}
+
 int ilog2(int x) {
   int l = 0;
   while ((1 << l) < x) ++l;
@@ -720,9 +743,10 @@ int ilog2(int x) {
 
 }  // namespace
 
-StreamPlan plan_stream(const sdm_dims& d, int64_t N) {
+StreamPlan plan_stream(const sdm_dims& d, int64_t N, int64_t stage_bytes) {
   (void)N;
   StreamPlan pl;
+  pl.stage_bytes = stage_bytes;
   pl.SW = d.d_v >= 32 ? 32 : d.d_v;
   pl.S = d.d_v / pl.SW;
   pl.NT = 1024;
@@ -739,7 +763,7 @@ StreamPlan plan_stream(const sdm_dims& d, int64_t N) {
   pl.log2GT = ilog2(pl.GT);
   // token chunk: bound the per-token buffers to ~2 GiB
   const int64_t per_tok = walks * ((d.W + d.R) * 8 + (int64_t)parts * d.d_v * 4 +
-                                   (pl.two_phase ? d.R * 8 + (parts + 1) * 4 : 0));
+                                   (pl.two_phase ? d.R * 8 + (parts + 1) * 4 : 0) + stage_bytes);
   int64_t tc = (2ll << 30) / per_tok;
   tc = tc < ROUND ? ROUND : (tc / ROUND) * ROUND;
   pl.Tc = d.T < tc ? d.T : tc;
@@ -751,7 +775,7 @@ namespace {
 
 // Byte offsets of the scan's buffers inside the workspace (256-byte aligned).
 struct StreamLayout {
-  size_t counts, offsets, entries, y_part, trash, begins, clean, cstart, total;
+  size_t counts, offsets, entries, y_part, trash, begins, clean, cstart, stage, total;
 };
 
 StreamLayout stream_layout(const sdm_dims& d, const StreamPlan& pl) {
@@ -778,6 +802,8 @@ StreamLayout stream_layout(const sdm_dims& d, const StreamPlan& pl) {
     L.cstart = s;
     s += al((size_t)walks * pl.Tc * (pl.parts + 1) * 4);
   }
+  L.stage = s;
+  s += al((size_t)walks * pl.Tc * pl.stage_bytes);
   L.total = s;
   return L;
 }
@@ -824,12 +850,13 @@ hipError_t launch_stream_scan(const ScanArgs& sa, const StreamPlan& pl, void* ws
   a.state = sa.state;
   a.out = sa.out;
   a.y_raw = sa.y_raw;
-  // training forward: the fp32 write log, on the stream schedule (rows replaced by
-  // each write, stored by the slot's owner)
+  // training forward: the rows replaced by each write, stored by the slot's owner, in
+  // fp32 to the caller's log, or (quantised formats) to a chunk-sized staging area that
+  // log_quantize_kernel encodes into the caller's log after the walk
   const bool train = sa.log != nullptr;
-  if (train && (sa.log_fmt != LOG_F32 || sa.state_bf16 || pl.two_phase))
-    return hipErrorInvalidValue;
-  a.log = static_cast<float*>(sa.log);
+  const bool qlog = train && sa.log_fmt != LOG_F32;
+  if (train && (sa.state_bf16 || pl.two_phase)) return hipErrorInvalidValue;
+  if (qlog && pl.stage_bytes < (int64_t)sa.W * sa.d_v * 4) return hipErrorInvalidValue;
   a.B = sa.B;
   a.T = sa.T;
   a.H = sa.H;
@@ -860,9 +887,12 @@ hipError_t launch_stream_scan(const ScanArgs& sa, const StreamPlan& pl, void* ws
   a.begins = reinterpret_cast<int*>(base + L.begins);
   a.clean = reinterpret_cast<uint2*>(base + L.clean);
   a.cstart = reinterpret_cast<int*>(base + L.cstart);
+  a.log = qlog ? reinterpret_cast<float*>(base + L.stage) : static_cast<float*>(sa.log);
   for (int64_t t0 = 0; t0 < sa.T; t0 += pl.Tc) {
     a.t0 = t0;
     a.Tc = sa.T - t0 < pl.Tc ? sa.T - t0 : pl.Tc;
+    a.log_T = qlog ? pl.Tc : sa.T;
+    a.log_t0 = qlog ? 0 : t0;
     a.rounds = (int)((a.Tc + ROUND - 1) / ROUND);
     a.walk_entries = a.Tc * (sa.W + sa.R);
 
@@ -930,6 +960,20 @@ hipError_t launch_stream_scan(const ScanArgs& sa, const StreamPlan& pl, void* ws
         hipLaunchKernelGGL((stream_scan_kernel<1024, 16, 8, true, false>), grid, dim3(1024), 0, st, a);
       else
         hipLaunchKernelGGL((stream_scan_kernel<1024, 16, 8, false, false>), grid, dim3(1024), 0, st, a);
+    }
+    if (qlog) {
+      const int64_t rows = sa.B * a.Tc * sa.H * sa.W;
+      const int64_t rpb = 256 / (sa.d_v / 4);
+      const dim3 qg((unsigned)((rows + rpb - 1) / rpb));
+      KernelTimer kt("log_quantize", st);
+      switch (sa.d_v) {
+        case 16: hipLaunchKernelGGL(log_quantize_kernel<16>, qg, dim3(256), 0, st, a, sa); break;
+        case 32: hipLaunchKernelGGL(log_quantize_kernel<32>, qg, dim3(256), 0, st, a, sa); break;
+        case 64: hipLaunchKernelGGL(log_quantize_kernel<64>, qg, dim3(256), 0, st, a, sa); break;
+        case 128: hipLaunchKernelGGL(log_quantize_kernel<128>, qg, dim3(256), 0, st, a, sa); break;
+        case 256: hipLaunchKernelGGL(log_quantize_kernel<256>, qg, dim3(256), 0, st, a, sa); break;
+        default: return hipErrorInvalidValue;
+      }
     }
     const int64_t rows = sa.B * a.Tc * sa.H;
     // rows per 256-thread block: 4 wavefronts x (64 / lanes per row)

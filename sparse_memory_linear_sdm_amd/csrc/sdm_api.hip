@@ -289,20 +289,18 @@ static int32_t log_format(const sdm_dims* d) {
 }
 
 // The training entries take fp32 state and the per-slot rule, on the direct or the
-// stream schedule; the training forward keeps a quantised log on the direct one.
-static int32_t check_train_flags(const sdm_dims* d, bool backward) {
+// stream schedule.
+static int32_t check_train_flags(const sdm_dims* d) {
   if (d->flags & (SDM_FLAG_STATE_BF16 | SDM_FLAG_DELTA_GDN | SDM_FLAG_SCAN_TWO_PHASE))
-    return SDM_ERR_UNSUPPORTED;
-  if (!backward && (d->flags & SDM_FLAG_SCAN_STREAM) && log_format(d) != LOG_F32)
     return SDM_ERR_UNSUPPORTED;
   return SDM_OK;
 }
 
-// Schedule of the training forward as scan flags: the stream schedule for an fp32 log
-// from 256 tokens (or when asked for), else the direct one.
+// Schedule of the training forward as scan flags: the stream schedule from 256 tokens
+// (or when asked for), else the direct one.
 static sdm_dims train_dims(const sdm_dims* d) {
   sdm_dims dd = *d;
-  const bool stream = log_format(d) == LOG_F32 && !(d->flags & SDM_FLAG_SCAN_DIRECT) &&
+  const bool stream = !(d->flags & SDM_FLAG_SCAN_DIRECT) &&
                       ((d->flags & SDM_FLAG_SCAN_STREAM) || d->T >= kStreamRound);
   dd.flags = (d->flags & ~(SDM_FLAG_SCAN_DIRECT | SDM_FLAG_SCAN_STREAM)) |
              (stream ? SDM_FLAG_SCAN_STREAM : SDM_FLAG_SCAN_DIRECT);
@@ -328,7 +326,7 @@ size_t sdm_workspace_bytes(const sdm_dims* d, int32_t entry) {
     case SDM_ENTRY_SCAN_BACKWARD: return backward_ws_bytes(d);
     case SDM_ENTRY_SCAN_TRAIN: {
       const sdm_dims dd = train_dims(d);
-      return align_up(scan_workspace_bytes(dd));
+      return align_up(scan_workspace_bytes(dd, true));
     }
     default: return 0;
   }
@@ -381,7 +379,7 @@ int32_t sdm_scan_train(const sdm_dims* d, const sdm_sel* in, const float* norm_w
   Derived dv;
   int32_t st = check_dims(d, &dv);
   if (st != SDM_OK) return st;
-  if ((st = check_train_flags(d, false)) != SDM_OK) return st;
+  if ((st = check_train_flags(d)) != SDM_OK) return st;
   if (dv.M == 0) return SDM_OK;
   if ((st = check_sel(in, false)) != SDM_OK) return st;
   const int32_t fmt = log_format(d);
@@ -390,7 +388,7 @@ int32_t sdm_scan_train(const sdm_dims* d, const sdm_sel* in, const float* norm_w
       (norm_w && !aligned16(norm_w)) || (log_scale && !aligned16(log_scale)))
     return SDM_ERR_ALIGN;
   const sdm_dims dd = train_dims(d);
-  const size_t need = align_up(scan_workspace_bytes(dd));
+  const size_t need = align_up(scan_workspace_bytes(dd, true));
   if (need && (!ws || ws_bytes < need)) return SDM_ERR_WORKSPACE;
   if (need && !aligned16(ws)) return SDM_ERR_ALIGN;
   ScanArgs a = scan_args(&dd, dv, in, norm_w, state, out, y_raw);
@@ -409,7 +407,7 @@ int32_t sdm_scan_backward(const sdm_dims* d, const sdm_sel* in, const float* nor
   Derived dv;
   int32_t st = check_dims(d, &dv);
   if (st != SDM_OK) return st;
-  if ((st = check_train_flags(d, true)) != SDM_OK) return st;
+  if ((st = check_train_flags(d)) != SDM_OK) return st;
   if (dv.M == 0) return SDM_OK;
   if ((st = check_sel(in, false)) != SDM_OK) return st;
   const int32_t fmt = log_format(d);

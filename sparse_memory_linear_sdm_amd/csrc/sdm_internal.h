@@ -56,7 +56,9 @@ struct ScanArgs {
 };
 hipError_t launch_scan(const sdm_dims& d, const ScanArgs& a, void* ws, size_t ws_bytes,
                        hipStream_t s);
-size_t scan_workspace_bytes(const sdm_dims& d);
+// train: the training forward (sdm_scan_train), whose quantised log formats stage fp32
+// rows in the workspace on the stream schedule.
+size_t scan_workspace_bytes(const sdm_dims& d, bool train = false);
 
 // Slot-owner stream schedule of the scan (scan_stream.hip).
 // Instrumentation (SDM_FLAG_TIMING): the C entry points switch recording on for
@@ -89,7 +91,9 @@ struct StreamArgs {
   void* state;     // fp32, or bf16 when state_bf16
   float* out;
   float* y_raw;
-  float* log;      // training forward: fp32 write log [B, T, H, W, d_v], else null
+  float* log;      // training forward: fp32 rows replaced by writes, else null; row of
+                   // (b, t, h, k) at ((b * log_T + log_t0 + t) * H + h) * W + k
+  int64_t log_T, log_t0;
   int* counts;     // [walks][rounds][GT]
   int* offsets;    // [walks][GT][rounds + 1]
   // owner-stream entry: {slot | token-in-round << 24, weight bits | read << 31}
@@ -139,8 +143,11 @@ struct StreamPlan {
   int SW, S, NT, parts, GT, log2GT, rounds;
   bool two_phase;  // clean reads summed in registers after each round's writes
   int64_t Tc;
+  int64_t stage_bytes;  // per token and walk: fp32 log rows staged for quantisation
 };
-StreamPlan plan_stream(const sdm_dims& d, int64_t N);
+// stage_bytes: workspace per token and walk for a training forward whose log is
+// quantised after the walk (W * d_v * 4), else 0.
+StreamPlan plan_stream(const sdm_dims& d, int64_t N, int64_t stage_bytes = 0);
 size_t stream_workspace_bytes(const sdm_dims& d, const StreamPlan& pl);
 hipError_t launch_stream_scan(const ScanArgs& a, const StreamPlan& pl, void* ws, hipStream_t s);
 bool scan_uses_stream(const sdm_dims& d);
@@ -175,6 +182,37 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
   const float mag = field == 0 ? (float)frac * 0.001953125f  // 2^-9
                                : __builtin_ldexpf((float)(8u + frac), (int)field - 10);
   return (c & 0x80u) ? -mag : mag;
+}
+
+// Stores logged row r (rows of dv values), this lane's columns 4 li .. 4 li + 3, the
+// row held by LPR lanes: fp32, or quantised with the row's absmax (a max over the
+// row's lanes), the codes decided in fp32.
+template <int LPR>
+__device__ __forceinline__ void log_store(void* log, float* log_scale, int fmt, int64_t r, int dv,
+                                          float4 m, int li) {
+  if (fmt == LOG_F32) {
+    reinterpret_cast<float4*>(static_cast<float*>(log) + r * dv)[li] = m;
+    return;
+  }
+  float mx = fmaxf(fmaxf(fabsf(m.x), fabsf(m.y)), fmaxf(fabsf(m.z), fabsf(m.w)));
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, LPR));
+  if (li == 0) log_scale[r] = mx;
+  uint8_t* base = static_cast<uint8_t*>(log);
+  if (fmt == LOG_FP8) {
+    const float inv = mx > 0.0f ? 448.0f / mx : 0.0f;
+    reinterpret_cast<uint32_t*>(base + r * dv)[li] =
+        e4m3_encode(m.x * inv) | e4m3_encode(m.y * inv) << 8 | e4m3_encode(m.z * inv) << 16 |
+        e4m3_encode(m.w * inv) << 24;
+  } else {
+    const float inv = mx > 0.0f ? 7.0f / mx : 0.0f;
+    auto q = [&](float x) {
+      const float t = fminf(fmaxf(__builtin_rintf(x * inv), -7.0f), 7.0f);
+      return (uint32_t)(int)t & 15u;
+    };
+    reinterpret_cast<uint16_t*>(base + r * (dv / 2))[li] =
+        (uint16_t)(q(m.x) | q(m.y) << 4 | q(m.z) << 8 | q(m.w) << 12);
+  }
 }
 
 // Logged row r (rows of dv values), columns 4 li .. 4 li + 3: fp32, or decoded with the

@@ -146,8 +146,7 @@ def test_training_entries_validate_first(lib):
     s = _sel()
     train = lambda dd=d, log=FAKE, y=FAKE, sc=None, ws=FAKE, nb=1 << 40: lib.sdm_scan_train(
         ctypes.byref(dd), ctypes.byref(s), None, FAKE, FAKE, y, log, sc, ws, nb, None)
-    for bad in (_lib.SDM_FLAG_STATE_BF16, _lib.SDM_FLAG_DELTA_GDN, _lib.SDM_FLAG_SCAN_TWO_PHASE,
-                _lib.SDM_FLAG_SCAN_STREAM | _lib.SDM_FLAG_LOG_FP8):
+    for bad in (_lib.SDM_FLAG_STATE_BF16, _lib.SDM_FLAG_DELTA_GDN, _lib.SDM_FLAG_SCAN_TWO_PHASE):
         assert train(dd=_d(T=64, flags=bad), sc=FAKE) == _lib.SDM_ERR_UNSUPPORTED
     # the direct schedule needs no workspace; the stream schedule (an fp32 log from 256
     # tokens, or asked for) takes its buckets from the workspace
@@ -157,8 +156,15 @@ def test_training_entries_validate_first(lib):
         assert nt > ds.B * ds.T * ds.H * (ds.W + ds.R) * 8
         assert train(dd=ds, nb=nt - 1) == _lib.SDM_ERR_WORKSPACE
         assert train(dd=ds, ws=None) == _lib.SDM_ERR_WORKSPACE
-    for dq in (_d(T=256, flags=_lib.SDM_FLAG_LOG_INT4), _d(T=256, flags=_lib.SDM_FLAG_SCAN_DIRECT)):
-        assert lib.sdm_workspace_bytes(ctypes.byref(dq), _lib.SDM_ENTRY_SCAN_TRAIN) == 0
+    dd = _d(T=256, flags=_lib.SDM_FLAG_SCAN_DIRECT | _lib.SDM_FLAG_LOG_INT4)
+    assert lib.sdm_workspace_bytes(ctypes.byref(dd), _lib.SDM_ENTRY_SCAN_TRAIN) == 0
+    # a quantised log on the stream schedule stages the fp32 rows in the workspace
+    for fl in (_lib.SDM_FLAG_LOG_INT4, _lib.SDM_FLAG_LOG_FP8):
+        dq = _d(T=256, flags=fl)
+        nq = lib.sdm_workspace_bytes(ctypes.byref(dq), _lib.SDM_ENTRY_SCAN_TRAIN)
+        n32 = lib.sdm_workspace_bytes(ctypes.byref(_d(T=256)), _lib.SDM_ENTRY_SCAN_TRAIN)
+        assert nq >= n32 + dq.B * dq.T * dq.H * dq.W * dq.d_v * 4
+        assert train(dd=dq, sc=FAKE, nb=nq - 1) == _lib.SDM_ERR_WORKSPACE
     assert train(log=None) == _lib.SDM_ERR_NULL
     assert train(y=None) == _lib.SDM_ERR_NULL        # the backward needs y_raw
     assert train(log=FAKE + 4) == _lib.SDM_ERR_ALIGN

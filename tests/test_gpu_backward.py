@@ -216,12 +216,15 @@ LOG_FLAGS = {"fp8": _lib.SDM_FLAG_LOG_FP8, "int4": _lib.SDM_FLAG_LOG_INT4}
 
 
 @pytest.mark.parametrize("fmt", ["fp8", "int4"])
-def test_quantised_log_codes_equal_the_oracle(fmt):
+@pytest.mark.parametrize("T,d_v", [(70, 64), (300, 64), (520, 256), (260, 16)])
+def test_quantised_log_codes_equal_the_oracle(fmt, T, d_v):
     """The same forward with an fp32 and a quantised log: identical state, y and out;
     the codes and scales equal the oracle's quantisation of the fp32 rows bit for bit
-    (both decide the codes in fp32)."""
-    rng = np.random.default_rng(64)
-    B, T, H, n, W, R, d_v = 2, 70, 2, 10, 16, 16, 64
+    (both decide the codes in fp32).  From 256 tokens both run the stream schedule,
+    the quantised one staging fp32 rows in the workspace and encoding them after the
+    walk."""
+    rng = np.random.default_rng(64 + T)
+    B, H, n, W, R = 2, 2, 10, 16, 16
     prod = random_products(rng, B, T, H, n, W, R, d_v, "repeat")
     m0 = (rng.standard_normal((B, H, n * n, d_v)) * 0.3).astype(np.float32)
     m0[0, 0, :5] = 0.0  # rows that log as all zeros
@@ -232,7 +235,12 @@ def test_quantised_log_codes_equal_the_oracle(fmt):
     out_a, y_a, log_a = ops.scan_train(d32, pd, None, st_a)
     out_b, y_b, log_b = ops.scan_train(dq, pd, None, st_b)
     torch.cuda.synchronize()
-    assert torch.equal(st_a, st_b) and torch.equal(y_a, y_b) and torch.equal(out_a, out_b)
+    assert torch.equal(st_a, st_b)
+    if T < 256:
+        assert torch.equal(y_a, y_b) and torch.equal(out_a, out_b)
+    else:  # reads summed with LDS atomics: equal up to fp32 summation order
+        assert_close(host(y_a), host(y_b), "y_raw")
+        assert_close(host(out_a), host(out_b), "out")
     codes, amax = O.quantize_rows(host(log_a["rows"]), fmt)
     assert np.array_equal(host(log_b["scale"]), amax)
     assert np.array_equal(host(log_b["rows"]), codes)
@@ -322,3 +330,32 @@ def test_stream_backward_over_several_token_chunks():
             _close_to_scale(host(g[k][b, :, h]), og[k], f"{k} walk {(b, h)}")
         _close_to_scale(host(ds[b, h]), odM, f"d_state walk {(b, h)}")
     _close_to_scale(host(g["d_norm_w"]), host(runs["direct"][0]["d_norm_w"]), "d_norm_w")
+
+
+def test_quantised_log_over_several_token_chunks():
+    """A quantised log on the stream schedule long enough to be staged in several token
+    chunks (the staging area counts against the per-chunk bound): state equal to the
+    fp32-log run, codes and scales of sampled walks equal to the oracle's quantisation
+    of that run's fp32 rows."""
+    B, T, H, n, W, R, d_v = 8, 80000, 4, 8, 16, 16, 16
+    rng = np.random.default_rng(66)
+    prod = _strided_products(rng, B, T, H, n, W, R, d_v)
+    m0 = (rng.standard_normal((B, H, n * n, d_v)) * 0.3).astype(np.float32)
+    pd = {k: to_dev(v) for k, v in prod.items()}
+    d32 = _dims(B=B, T=T, H=H, n=n, W=W, R=R, d_v=d_v)
+    dq = _dims(B=B, T=T, H=H, n=n, W=W, R=R, d_v=d_v, flags=_lib.SDM_FLAG_LOG_FP8)
+    nq = _lib.workspace_bytes(dq, _lib.SDM_ENTRY_SCAN_TRAIN)
+    staged = B * T * H * W * d_v * 4
+    # one chunk would hold at least the staged rows, the entries and one read partial
+    # per token and walk
+    assert nq < B * T * H * (W * d_v * 4 + (W + R) * 8 + d_v * 4), "expected token chunks"
+    st_a, st_b = to_dev(m0), to_dev(m0)
+    _, _, log_a = ops.scan_train(d32, pd, None, st_a)
+    _, _, log_b = ops.scan_train(dq, pd, None, st_b)
+    torch.cuda.synchronize()
+    say(f"  workspace {nq / 2**30:.2f} GiB for {staged / 2**30:.2f} GiB of fp32 rows")
+    assert torch.equal(st_a, st_b)
+    for b, h in [(0, 0), (3, 2), (B - 1, H - 1)]:
+        codes, amax = O.quantize_rows(host(log_a["rows"][b, :, h]), "fp8")
+        assert np.array_equal(host(log_b["scale"][b, :, h]), amax), (b, h)
+        assert np.array_equal(host(log_b["rows"][b, :, h]), codes), (b, h)
