@@ -35,6 +35,9 @@ namespace sdm {
 namespace {
 
 constexpr int ROUND = kStreamRound;  // tokens per round (ring half)
+// two-phase training forward: accesses in flight per lane group (32- / 16-float slices;
+// 8 spills registers at 16)
+constexpr int BQ_TRAIN32 = 8, BQ_TRAIN16 = 6;
 constexpr int MAX_GT = kStreamMaxGT;  // lane groups per walk
 constexpr uint32_t SLOT_MASK = 0xFFFFFFu;
 static_assert(ROUND <= 256, "token-in-round must fit the entry's top 8 bits");
@@ -359,8 +362,10 @@ __global__ __launch_bounds__(NT) void stream_scan_kernel(StreamArgs a) {
 // ---------------------------------------------------------------------------
 // The token loop is latency-bound (one wavefront, one token at a time), so the ids
 // and weights of the next D tokens are loaded while the current D are placed.
-// KC = number of 64-wide chunks of W and R (1 or 2).
-template <int KC, int D>
+// KC = number of 64-wide chunks of W and R (1 or 2).  TRAIN: owner-stream entries
+// carry the access's position in its token's id list instead of its weight (clean
+// reads keep their weights).
+template <int KC, int D, bool TRAIN>
 __global__ __launch_bounds__(64) void bucket_scatter_rev_kernel(StreamArgs a) {
   extern __shared__ uint32_t dyn[];
   int* cur = reinterpret_cast<int*>(dyn);
@@ -417,7 +422,9 @@ __global__ __launch_bounds__(64) void bucket_scatter_rev_kernel(StreamArgs a) {
           const uint32_t grp = group_of(sr, a.log2GT);
           if ((bm[sr >> 5] >> (sr & 31u)) & 1u) {
             const int pos = atomicSub(&cur[grp], 1) - 1;
-            ent[pos] = make_entry(sr, tt, __uint_as_float(rq[u][c]), true);
+            ent[pos] = make_entry(sr, tt,
+                                  __uint_as_float(TRAIN ? (uint32_t)(c * 64 + lane) : rq[u][c]),
+                                  true);
           } else {
             pk[c] = (int)(grp >> a.log2GW);
           }
@@ -443,7 +450,9 @@ __global__ __launch_bounds__(64) void bucket_scatter_rev_kernel(StreamArgs a) {
         if (c * 64 + lane < a.W) {
           const uint32_t sw = xs[u][c];
           const int pos = atomicSub(&cur[group_of(sw, a.log2GT)], 1) - 1;
-          ent[pos] = make_entry(sw, tt, __uint_as_float(xq[u][c]), false);
+          ent[pos] = make_entry(sw, tt,
+                                __uint_as_float(TRAIN ? (uint32_t)(c * 64 + lane) : xq[u][c]),
+                                false);
           atomicOr(&bm[sw >> 5], 1u << (sw & 31u));
         }
       }
@@ -475,8 +484,9 @@ __global__ __launch_bounds__(64) void bucket_scatter_rev_kernel(StreamArgs a) {
 //                round's writes come after the reads).  Parts never touch each
 //                other's slots, so they need no synchronisation with one another.
 // ---------------------------------------------------------------------------
-template <int NT, int SW, int BQ, int BR, bool BF>
+template <int NT, int SW, int BQ, int BR, bool BF, bool TRAIN>
 __global__ __launch_bounds__(NT) void two_phase_scan_kernel(StreamArgs a) {
+  static_assert(!(TRAIN && BF), "the write log is kept for fp32 state");
   constexpr uint32_t ES = StateT<BF>::ES;
   constexpr int LPG = SW / 4;
   constexpr int GW = NT / LPG;
@@ -509,6 +519,7 @@ __global__ __launch_bounds__(NT) void two_phase_scan_kernel(StreamArgs a) {
   const int* offs = a.offsets + ((int64_t)w * a.GT + gg) * (a.rounds + 1);
   const int* begs = a.begins + ((int64_t)w * a.GT + gg) * a.rounds;
   const int64_t tok_base = (b * a.T + a.t0) * a.H + h;  // token t -> tok_base + t*H
+  const int64_t log_base = (b * a.log_T + a.log_t0) * a.H + h;  // TRAIN: log row of t
   float* y_out = a.y_part + (int64_t)p * a.B * a.Tc * a.H * dv + sl * SW + li * 4;
   float4* trash = a.trash + wg * NT + tid;
 
@@ -540,6 +551,7 @@ __global__ __launch_bounds__(NT) void two_phase_scan_kernel(StreamArgs a) {
       for (int q = 0; q < EPL; ++q) en[q] = ent[min(i + BQ + q * LPG + li, end - 1)];
       uint32_t slot[BQ], tk[BQ];
       float wq[BQ];
+      int kk[BQ];  // TRAIN: position in the token's id list
       uint32_t wrm = 0, vam = 0;
       float4 mv[BQ];
 #pragma unroll
@@ -549,7 +561,14 @@ __global__ __launch_bounds__(NT) void two_phase_scan_kernel(StreamArgs a) {
         const uint32_t ey = group_bcast<LPG>(e[q].y, src);
         slot[j] = min(ex & SLOT_MASK, (uint32_t)a.N - 1u);
         tk[j] = ex >> 24;
-        wq[j] = __uint_as_float(ey & 0x7fffffffu);
+        if constexpr (TRAIN) {
+          tk[j] = min(tk[j], (uint32_t)nt - 1u);
+          kk[j] = min((int)(ey & 0x7fffffffu), ((ey >> 31) ? a.R : a.W) - 1);
+          const int64_t tok = tok_base + (t_lo + tk[j]) * a.H;
+          wq[j] = (ey >> 31) ? a.wt_r[tok * a.R + kk[j]] : a.wt_w[tok * a.W + kk[j]];
+        } else {
+          wq[j] = __uint_as_float(ey & 0x7fffffffu);
+        }
         const bool valid = i + j < end;
         vam |= (uint32_t)valid << j;
         wrm |= (uint32_t)(valid && !(ey >> 31)) << j;
@@ -569,6 +588,12 @@ __global__ __launch_bounds__(NT) void two_phase_scan_kernel(StreamArgs a) {
           val.w = fwd ? mv[jj].w : val.w;
         }
         const bool isw = (wrm >> j) & 1u;
+        if constexpr (TRAIN) {  // the row as it was before this write, to the log
+          if (isw) {
+            const int64_t lr = log_base + (t_lo + tk[j]) * a.H;
+            *reinterpret_cast<float4*>(a.log + (lr * a.W + kk[j]) * dv + sl * SW + li * 4) = val;
+          }
+        }
         {
           const float2 ab = gab[tk[j]];
           const float4 vv = *reinterpret_cast<const float4*>(vs + tk[j] * SW + li * 4);
@@ -855,7 +880,7 @@ hipError_t launch_stream_scan(const ScanArgs& sa, const StreamPlan& pl, void* ws
   // log_quantize_kernel encodes into the caller's log after the walk
   const bool train = sa.log != nullptr;
   const bool qlog = train && sa.log_fmt != LOG_F32;
-  if (train && (sa.state_bf16 || pl.two_phase)) return hipErrorInvalidValue;
+  if (train && sa.state_bf16) return hipErrorInvalidValue;
   if (qlog && pl.stage_bytes < (int64_t)sa.W * sa.d_v * 4) return hipErrorInvalidValue;
   a.B = sa.B;
   a.T = sa.T;
@@ -907,32 +932,45 @@ hipError_t launch_stream_scan(const ScanArgs& sa, const StreamPlan& pl, void* ws
     }
     if (pl.two_phase) {
       const size_t lds = (size_t)pl.GT * 4 + (size_t)((sa.N + 31) / 32) * 4;
-      const void* rev = sa.W <= 64 && sa.R <= 64
-                            ? reinterpret_cast<const void*>(bucket_scatter_rev_kernel<1, 8>)
-                            : reinterpret_cast<const void*>(bucket_scatter_rev_kernel<2, 4>);
+      const bool narrow = sa.W <= 64 && sa.R <= 64;
+      const void* rev =
+          narrow ? (train ? reinterpret_cast<const void*>(bucket_scatter_rev_kernel<1, 8, true>)
+                          : reinterpret_cast<const void*>(bucket_scatter_rev_kernel<1, 8, false>))
+                 : (train ? reinterpret_cast<const void*>(bucket_scatter_rev_kernel<2, 4, true>)
+                          : reinterpret_cast<const void*>(bucket_scatter_rev_kernel<2, 4, false>));
       if (lds > 65536)  // slot bitmaps beyond 64 KiB (N > ~500k) need the larger LDS limit
         (void)hipFuncSetAttribute(rev, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       const dim3 rg((unsigned)(walks * a.rounds));
       {
         KernelTimer kt("bucket_scatter_rev", st);
-        if (sa.W <= 64 && sa.R <= 64)
-          hipLaunchKernelGGL((bucket_scatter_rev_kernel<1, 8>), rg, dim3(64), lds, st, a);
+        if (narrow && train)
+          hipLaunchKernelGGL((bucket_scatter_rev_kernel<1, 8, true>), rg, dim3(64), lds, st, a);
+        else if (narrow)
+          hipLaunchKernelGGL((bucket_scatter_rev_kernel<1, 8, false>), rg, dim3(64), lds, st, a);
+        else if (train)
+          hipLaunchKernelGGL((bucket_scatter_rev_kernel<2, 4, true>), rg, dim3(64), lds, st, a);
         else
-          hipLaunchKernelGGL((bucket_scatter_rev_kernel<2, 4>), rg, dim3(64), lds, st, a);
+          hipLaunchKernelGGL((bucket_scatter_rev_kernel<2, 4, false>), rg, dim3(64), lds, st, a);
       }
       const dim3 grid((unsigned)(walks * pl.S * pl.parts));
       KernelTimer kt("two_phase_scan", st);
-      if (pl.SW == 32 && sa.state_bf16)
-        hipLaunchKernelGGL((two_phase_scan_kernel<1024, 32, 8, 8, true>), grid, dim3(1024), 0, st,
+      if (train && pl.SW == 32)
+        hipLaunchKernelGGL((two_phase_scan_kernel<1024, 32, BQ_TRAIN32, 8, false, true>), grid,
+                           dim3(1024), 0, st, a);
+      else if (train)
+        hipLaunchKernelGGL((two_phase_scan_kernel<1024, 16, BQ_TRAIN16, 8, false, true>), grid,
+                           dim3(1024), 0, st, a);
+      else if (pl.SW == 32 && sa.state_bf16)
+        hipLaunchKernelGGL((two_phase_scan_kernel<1024, 32, 8, 8, true, false>), grid, dim3(1024), 0, st,
                            a);
       else if (pl.SW == 32)
-        hipLaunchKernelGGL((two_phase_scan_kernel<1024, 32, 8, 8, false>), grid, dim3(1024), 0, st,
+        hipLaunchKernelGGL((two_phase_scan_kernel<1024, 32, 8, 8, false, false>), grid, dim3(1024), 0, st,
                            a);
       else if (sa.state_bf16)
-        hipLaunchKernelGGL((two_phase_scan_kernel<1024, 16, 8, 8, true>), grid, dim3(1024), 0, st,
+        hipLaunchKernelGGL((two_phase_scan_kernel<1024, 16, 8, 8, true, false>), grid, dim3(1024), 0, st,
                            a);
       else
-        hipLaunchKernelGGL((two_phase_scan_kernel<1024, 16, 8, 8, false>), grid, dim3(1024), 0, st,
+        hipLaunchKernelGGL((two_phase_scan_kernel<1024, 16, 8, 8, false, false>), grid, dim3(1024), 0, st,
                            a);
     } else {
       {

@@ -483,9 +483,11 @@ BackLayout back_layout(const sdm_dims& d, const BackPlan& pl) {
 
 }  // namespace
 
+// The backward has one slot-owner schedule: SDM_FLAG_SCAN_STREAM and
+// SDM_FLAG_SCAN_TWO_PHASE both select it.
 bool backward_uses_stream(const sdm_dims& d) {
   if (d.flags & SDM_FLAG_SCAN_DIRECT) return false;
-  if (d.flags & SDM_FLAG_SCAN_STREAM) return true;
+  if (d.flags & (SDM_FLAG_SCAN_STREAM | SDM_FLAG_SCAN_TWO_PHASE)) return true;
   return d.T >= ROUND;
 }
 

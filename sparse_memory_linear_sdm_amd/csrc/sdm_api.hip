@@ -288,22 +288,19 @@ static int32_t log_format(const sdm_dims* d) {
                                                                                    : LOG_F32;
 }
 
-// The training entries take fp32 state and the per-slot rule, on the direct or the
-// stream schedule.
+// The training entries take fp32 state and the per-slot rule, on any schedule.
 static int32_t check_train_flags(const sdm_dims* d) {
-  if (d->flags & (SDM_FLAG_STATE_BF16 | SDM_FLAG_DELTA_GDN | SDM_FLAG_SCAN_TWO_PHASE))
-    return SDM_ERR_UNSUPPORTED;
+  if (d->flags & (SDM_FLAG_STATE_BF16 | SDM_FLAG_DELTA_GDN)) return SDM_ERR_UNSUPPORTED;
   return SDM_OK;
 }
 
-// Schedule of the training forward as scan flags: the stream schedule from 256 tokens
-// (or when asked for), else the direct one.
+// Schedule of the training forward as scan flags: a schedule asked for, else the
+// two-phase one from 256 tokens and the direct one below.
 static sdm_dims train_dims(const sdm_dims* d) {
+  const int32_t sched = SDM_FLAG_SCAN_DIRECT | SDM_FLAG_SCAN_STREAM | SDM_FLAG_SCAN_TWO_PHASE;
   sdm_dims dd = *d;
-  const bool stream = !(d->flags & SDM_FLAG_SCAN_DIRECT) &&
-                      ((d->flags & SDM_FLAG_SCAN_STREAM) || d->T >= kStreamRound);
-  dd.flags = (d->flags & ~(SDM_FLAG_SCAN_DIRECT | SDM_FLAG_SCAN_STREAM)) |
-             (stream ? SDM_FLAG_SCAN_STREAM : SDM_FLAG_SCAN_DIRECT);
+  if (!(d->flags & sched))
+    dd.flags |= d->T >= kStreamRound ? SDM_FLAG_SCAN_TWO_PHASE : SDM_FLAG_SCAN_DIRECT;
   return dd;
 }
 

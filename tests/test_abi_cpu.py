@@ -146,12 +146,13 @@ def test_training_entries_validate_first(lib):
     s = _sel()
     train = lambda dd=d, log=FAKE, y=FAKE, sc=None, ws=FAKE, nb=1 << 40: lib.sdm_scan_train(
         ctypes.byref(dd), ctypes.byref(s), None, FAKE, FAKE, y, log, sc, ws, nb, None)
-    for bad in (_lib.SDM_FLAG_STATE_BF16, _lib.SDM_FLAG_DELTA_GDN, _lib.SDM_FLAG_SCAN_TWO_PHASE):
+    for bad in (_lib.SDM_FLAG_STATE_BF16, _lib.SDM_FLAG_DELTA_GDN):
         assert train(dd=_d(T=64, flags=bad), sc=FAKE) == _lib.SDM_ERR_UNSUPPORTED
     # the direct schedule needs no workspace; the stream schedule (an fp32 log from 256
     # tokens, or asked for) takes its buckets from the workspace
     assert lib.sdm_workspace_bytes(ctypes.byref(d), _lib.SDM_ENTRY_SCAN_TRAIN) == 0
-    for ds in (_d(T=64, flags=_lib.SDM_FLAG_SCAN_STREAM), _d(T=256)):
+    for ds in (_d(T=64, flags=_lib.SDM_FLAG_SCAN_STREAM), _d(T=256),
+               _d(T=64, flags=_lib.SDM_FLAG_SCAN_TWO_PHASE)):
         nt = lib.sdm_workspace_bytes(ctypes.byref(ds), _lib.SDM_ENTRY_SCAN_TRAIN)
         assert nt > ds.B * ds.T * ds.H * (ds.W + ds.R) * 8
         assert train(dd=ds, nb=nt - 1) == _lib.SDM_ERR_WORKSPACE
@@ -187,8 +188,8 @@ def test_training_entries_validate_first(lib):
     assert back(grads=_lib.SdmScanGrads(*([FAKE] * 6 + [FAKE + 8]))) == _lib.SDM_ERR_ALIGN
     # the stream schedule (forced, or by default from 256 tokens) takes its buckets,
     # dy, per-slice partial dots and per-part d_v from the workspace
-    assert back(dd=_d(T=64, flags=_lib.SDM_FLAG_SCAN_TWO_PHASE)) == _lib.SDM_ERR_UNSUPPORTED
-    for ds in (_d(T=64, flags=_lib.SDM_FLAG_SCAN_STREAM), _d(T=256)):
+    for ds in (_d(T=64, flags=_lib.SDM_FLAG_SCAN_STREAM), _d(T=256),
+               _d(T=64, flags=_lib.SDM_FLAG_SCAN_TWO_PHASE)):
         ns = lib.sdm_workspace_bytes(ctypes.byref(ds), _lib.SDM_ENTRY_SCAN_BACKWARD)
         assert ns > ds.B * ds.T * ds.H * (ds.W + ds.R) * 8
         assert back(dd=ds, nb=ns - 1) == _lib.SDM_ERR_WORKSPACE

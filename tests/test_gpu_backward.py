@@ -52,7 +52,8 @@ def _close_to_scale(got, exp, what, rel=1e-4):
                            f"max err {err.max():.3e}")
 
 
-SCHED = {"direct": _lib.SDM_FLAG_SCAN_DIRECT, "stream": _lib.SDM_FLAG_SCAN_STREAM}
+SCHED = {"direct": _lib.SDM_FLAG_SCAN_DIRECT, "stream": _lib.SDM_FLAG_SCAN_STREAM,
+         "two_phase": _lib.SDM_FLAG_SCAN_TWO_PHASE}
 
 
 def _back_dims(d, sched):
@@ -133,12 +134,12 @@ def test_backward_matches_oracle(B, T, H, n, W, R, d_v, mode, sched):
     _run(d, prod, gamma, m0, rng, [(b, h) for b in range(B) for h in range(H)], sched)
 
 
-@pytest.mark.parametrize("sched", ["direct", "stream"])
-@pytest.mark.parametrize("T,d_v", [(80, 64), (600, 32), (300, 16)])
+@pytest.mark.parametrize("sched", ["direct", "stream", "two_phase"])
+@pytest.mark.parametrize("T,d_v", [(80, 64), (600, 32), (300, 16), (270, 256)])
 def test_training_forward_equals_scan_and_log_is_the_replaced_rows(sched, T, d_v):
-    """State and log equal the direct scan's bit for bit on either schedule (one owner
+    """State and log equal the direct scan's bit for bit on every schedule (one owner
     applies each slot's writes in token order, the same arithmetic); y and out equal
-    sdm_scan's on the direct schedule bit for bit, on the stream one up to fp32
+    sdm_scan's on the direct schedule bit for bit, on the slot-owner ones up to fp32
     summation order; the log holds the oracle's replaced rows."""
     rng = np.random.default_rng(61 + T)
     B, H, n, W, R = 2, 2, 10, 16, 16
