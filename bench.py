@@ -129,7 +129,7 @@ def main():
     m0_d = to_dev(m0)
     if bf16_state:
         m0_d = m0_d.to(torch.bfloat16)
-    state = m0_d.unsqueeze(0).expand(wl.B, *m0_d.shape).contiguous()
+    state = m0_d.unsqueeze(0).repeat(wl.B, *([1] * m0_d.dim()))  # a copy, also for B = 1
     del m0
     prod = ops.alloc_products(d, dev)
     out = torch.empty((wl.B, wl.T, wl.H, wl.d_v), device=dev)

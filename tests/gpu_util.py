@@ -51,7 +51,9 @@ def layer_inputs(wl: synth.Workload, seed=0, with_state=True):
 
 
 def broadcast_state(m0_dev, B):
-    return m0_dev.unsqueeze(0).expand(B, *m0_dev.shape).contiguous()
+    """A new [B, ...] state tensor holding B copies of m0 (never a view of m0: for
+    B = 1 an expanded view would already be contiguous and alias it)."""
+    return m0_dev.unsqueeze(0).repeat(B, *([1] * m0_dev.dim()))
 
 
 def assert_close(got, exp, what, rtol=RTOL, atol=ATOL):

@@ -449,6 +449,65 @@ def test_timing_flag_records_every_launch_and_changes_nothing(T):
     assert _lib.timing_read() == []
 
 
+@pytest.mark.parametrize("wl", [
+    synth.WORKLOADS["tiny"],
+    synth.small("layer1p4b", B=2, T=300, d_model=256, H=2, n=24, W=16, R=24, d_v=32),
+])
+def test_slot_relabelling_permutes_ids_and_keeps_outputs(wl):
+    """Permuting the columns of each half-key block (the same permutation for the write
+    and the read half) and the rows of M0 to match relabels every slot: each output
+    column of the projection is the same dot product, so the half-scores move
+    bitwise and the ids map through the relabelling exactly.  The softmax weights are
+    summed in id order, so they, and with them the state and out, agree up to
+    rounding."""
+    h, d = layer_inputs(wl, seed=8)
+    n, P = wl.n, wl.P
+    rng = np.random.default_rng(9)
+    p1, p2 = rng.permutation(n), rng.permutation(n)
+    relabel = (p1[:, None] * n + p2[None, :]).reshape(-1)  # old id -> new id
+    w = d["w_proj"].clone()
+    for hh in range(wl.H):
+        for blk, perm in ((0, p1), (1, p2), (2, p1), (3, p2)):
+            base = hh * P + blk * n
+            w[base + torch.as_tensor(perm, device=w.device)] = d["w_proj"][base:base + n]
+    m0 = d["m0"].clone()
+    m0[:, torch.as_tensor(relabel, device=m0.device)] = d["m0"]
+    res = []
+    for wp, mm in ((d["w_proj"], d["m0"]), (w, m0)):
+        st = broadcast_state(mm, wl.B)
+        out, pr = ops.forward(dims_for(wl), d["x"], wp, d["A"], d["b_dt"], d["gamma"], st,
+                              debug=True, with_scores=True)
+        res.append((host(out), host(st), {k: host(v) for k, v in pr.items()}))
+    (o_a, s_a, p_a), (o_b, s_b, p_b) = res
+    sc_a = p_a["scores"].reshape(wl.B, wl.T, wl.H, 4, n)
+    sc_b = p_b["scores"].reshape(wl.B, wl.T, wl.H, 4, n)
+    for blk, perm in ((0, p1), (1, p2), (2, p1), (3, p2)):
+        assert np.array_equal(sc_b[..., blk, perm], sc_a[..., blk, :]), f"half-score block {blk}"
+    for role in ("w", "r"):
+        ids_a, wt_a = p_a[f"idx_{role}"], p_a[f"wt_{role}"]
+        mapped = relabel[ids_a]
+        order = np.argsort(mapped, axis=-1, kind="stable")
+        assert np.array_equal(np.take_along_axis(mapped, order, -1), p_b[f"idx_{role}"]), role
+        assert_close(p_b[f"wt_{role}"], np.take_along_axis(wt_a, order, -1), f"wt_{role}")
+    assert_close(s_b[:, :, relabel], s_a, "state", rtol=1e-5, atol=1e-6)
+    assert_close(o_b, o_a, "out", rtol=1e-5, atol=1e-6)
+
+
+def test_batch_entries_are_independent():
+    """A batch of sequences equals each sequence run alone: the state bit for bit, out
+    up to the order of the read sums (the slot-owner plan depends on the batch)."""
+    wl = synth.small("layer1p4b", B=3, T=300, d_model=128, H=2, n=16, W=16, R=16, d_v=32)
+    _, d = layer_inputs(wl, seed=10)
+    st = broadcast_state(d["m0"], wl.B)
+    out = host(ops.forward(dims_for(wl), d["x"], d["w_proj"], d["A"], d["b_dt"], d["gamma"], st))
+    for b in range(wl.B):
+        s1 = broadcast_state(d["m0"], 1)
+        o1 = ops.forward(dims_for(wl, B=1), d["x"][b:b + 1].contiguous(), d["w_proj"], d["A"],
+                         d["b_dt"], d["gamma"], s1)
+        assert torch.equal(s1[0], st[b]), b
+        assert_close(host(o1)[0], out[b], f"out {b}", rtol=1e-5, atol=1e-6)
+
+
 def test_empty_call_changes_nothing():
     wl = synth.small("tiny", T=0)
     _, d = layer_inputs(synth.WORKLOADS["tiny"], seed=4)
