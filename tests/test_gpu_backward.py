@@ -110,6 +110,7 @@ def _run(d, prod, gamma, m0, rng, walks, sched=None):
 
 CASES = [
     (1, 64, 1, 16, 8, 8, 16, "random"),
+    (1, 300, 2, 12, 64, 128, 64, "repeat"),   # more than 64 ids per token
     (2, 120, 2, 8, 16, 16, 32, "repeat"),     # N = 64: slots rewritten and re-read constantly
     (2, 50, 3, 8, 32, 32, 64, "random"),
     (1, 40, 2, 12, 16, 8, 128, "same"),       # every token the same selection
@@ -135,14 +136,16 @@ def test_backward_matches_oracle(B, T, H, n, W, R, d_v, mode, sched):
 
 
 @pytest.mark.parametrize("sched", ["direct", "stream", "two_phase"])
-@pytest.mark.parametrize("T,d_v", [(80, 64), (600, 32), (300, 16), (270, 256)])
-def test_training_forward_equals_scan_and_log_is_the_replaced_rows(sched, T, d_v):
+@pytest.mark.parametrize("T,d_v,W,R", [(80, 64, 16, 16), (600, 32, 16, 16), (300, 16, 16, 16),
+                                       (270, 256, 16, 16), (300, 64, 64, 128),
+                                       (260, 32, 128, 32)])
+def test_training_forward_equals_scan_and_log_is_the_replaced_rows(sched, T, d_v, W, R):
     """State and log equal the direct scan's bit for bit on every schedule (one owner
     applies each slot's writes in token order, the same arithmetic); y and out equal
     sdm_scan's on the direct schedule bit for bit, on the slot-owner ones up to fp32
     summation order; the log holds the oracle's replaced rows."""
     rng = np.random.default_rng(61 + T)
-    B, H, n, W, R = 2, 2, 10, 16, 16
+    B, H, n = 2, 2, 10 if max(W, R) <= 64 else 12
     prod = random_products(rng, B, T, H, n, W, R, d_v, "repeat")
     m0 = (rng.standard_normal((B, H, n * n, d_v)) * 0.3).astype(np.float32)
     gamma = rng.uniform(0.5, 1.5, (H, d_v)).astype(np.float32)
