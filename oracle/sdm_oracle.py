@@ -1,4 +1,5 @@
-"""Plain, slow, fp64 CPU oracle of the Sparse Delta Memory (SDM) forward path.
+"""Plain, slow, fp64 CPU oracle of the Sparse Delta Memory (SDM) hot path: the
+forward pass, and the training pass (write log and reverse walk).
 
 TEST INFRASTRUCTURE.  Only the tests, the package's smoke check and the
 benchmark's CPU-baseline leg may import or run this module.  It shares no code
@@ -38,9 +39,26 @@ Storage variant: scan(..., store=round_bf16) keeps a bf16 state (every written
 row rounded to nearest-even bf16 from the exact value); round_bf16 is pinned
 against torch's float32 -> bfloat16 conversion and hand-worked halfway cases.
 
-Pins: every function here is checked by tests/test_oracle_pins.py against
-hand-worked fixtures (tests/golden/), closed forms, exact rational arithmetic
-and brute force.  No function of this module is "parity unpinned".
+Training (the [163] article, section 八: the sparse update applied in place and
+undone in backward from the rows it overwrote): scan(..., record=True) keeps those
+rows; scan_backward walks the tokens in reverse; quantize_rows / e4m3_encode keep
+them in fp8 (OCP E4M3) or int4 with one absmax per row (the pages' fp8/int4
+training checkpoints; the format details are a reading).
+
+Pins (every function is checked against something other than itself):
+  tests/test_oracle_pins.py            selection, gates, scan, norm, whole layer:
+                                       hand-worked fixtures (tests/golden/), closed
+                                       forms, exact rationals, brute force,
+                                       invariants
+  tests/test_oracle_mutations.py       planted mistakes, each caught by a pin
+  tests/test_oracle_gdn_pins.py        scan_gdn against a dense matrix recurrence
+  tests/test_oracle_bf16_pins.py       round_bf16 and the bf16-storage scan
+  tests/test_oracle_histogram_pins.py  slot_update_counts by brute force
+  tests/test_oracle_shared_m0_pins.py  forward_walk_shared against plain walks
+  tests/test_oracle_backward_pins.py   scan_backward against central differences
+  tests/test_oracle_quant_pins.py      E4M3 against torch's float8_e4m3fn, int4
+                                       packing by hand, error bounds
+No function of this module is "parity unpinned".
 """
 from __future__ import annotations
 
