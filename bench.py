@@ -31,24 +31,40 @@ METRIC = "SDM layer tokens/s at N=131072,W=R=64,d_v=128; effective HBM GB/s vs p
 METRIC_TRAIN = ("SDM layer training tokens/s (selection, scan forward with write log, scan "
                 "backward); reverse-walk HBM GB/s vs peak")
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+CSRC = os.path.join(ROOT, "sparse_memory_linear_sdm_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_traffic_layer1p4b.txt")
-SCAN_SOURCE = os.path.join(ROOT, "sparse_memory_linear_sdm_amd", "csrc", "scan_stream.hip")
+SCAN_SOURCE = os.path.join(CSRC, "scan_stream.hip")
+MFMA_FILE = os.path.join(ROOT, "profiles", "proj_gemm_mfma_layer1p4b.txt")
+GEMM_SOURCE = os.path.join(CSRC, "proj_gemm.hip")
+
+
+def _profile_fields(path: str, source: str):
+    """Fields of a committed counter summary, if it was taken on the current source."""
+    import hashlib
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.split()[0] if v.split() else ""
+    cur = hashlib.sha256(open(source, "rb").read()).hexdigest()
+    if fields.get("source_sha256") != cur:
+        return None  # the kernel changed since the counters were taken
+    return fields
 
 
 def measured_traffic(workload: str):
     """Counter-measured HBM bytes of one scan launch, if taken on the current source."""
-    import hashlib
-    if workload != "layer1p4b" or not os.path.exists(TRAFFIC_FILE):
-        return None
-    fields = {}
-    for line in open(TRAFFIC_FILE):
-        if ":" in line and not line.startswith("#"):
-            k, v = line.split(":", 1)
-            fields[k.strip()] = v.split()[0] if v.split() else ""
-    cur = hashlib.sha256(open(SCAN_SOURCE, "rb").read()).hexdigest()
-    if fields.get("source_sha256") != cur:
-        return None  # the kernel changed since the counters were taken
-    return int(float(fields["traffic_bytes"]))
+    f = _profile_fields(TRAFFIC_FILE, SCAN_SOURCE) if workload == "layer1p4b" else None
+    return int(float(f["traffic_bytes"])) if f else None
+
+
+def measured_mfma_util(workload: str):
+    """Counter-measured MFMA busy fraction of the projection GEMM (current source)."""
+    f = _profile_fields(MFMA_FILE, GEMM_SOURCE) if workload == "layer1p4b" else None
+    return float(f["mfma_util"]) if f else None
 
 
 def parse():
@@ -89,6 +105,20 @@ def cpu_baseline(wl, ntok: int) -> dict:
             "sample": f"{wl.name}: tokens 0..{ntok - 1} of batch entry 0, all {wl.H} heads, "
                       f"from x (fp64 projection, brute-force top-{wl.W}/{wl.R} over "
                       f"N={wl.N}, sequential scan, norm+gate); {dt:.1f} s on 1 host thread"}
+
+
+def gemm_line(wl, kernels_ms, kernel, steps):
+    """The projection GEMM against the dense MFMA peak of its dtype: algorithmic
+    2 M N K flops over its event-timed duration per step, and the counted MFMA busy
+    fraction from the committed rocprofv3 summary."""
+    if kernel is None:
+        return None
+    ms = kernels_ms[kernel]["avg"] * kernels_ms[kernel]["launches"] / steps
+    flops = 2.0 * wl.tokens * wl.H * wl.P * wl.d_model
+    tf = flops / (ms * 1e-3) / 1e12
+    peak = MFMA_BF16_PEAK_TFLOPS if kernel == "proj_gemm_bf16" else 157.3
+    return {"kernel": kernel, "achieved": tf, "peak": peak, "unit": "TFLOP/s", "frac": tf / peak,
+            "ms": ms, "mfma_util_counted": measured_mfma_util(wl.name)}
 
 
 def main():
@@ -174,6 +204,7 @@ def main():
         per_kernel.setdefault(name, []).append(ms)
     kernels_ms = {k: {"avg": float(np.mean(v)), "launches": len(v)} for k, v in per_kernel.items()}
     scan_kernel = next(k for k in ("two_phase_scan", "stream_scan", "scan_direct") if k in kernels_ms)
+    gemm_kernel = next((k for k in ("proj_gemm_bf16", "proj_gemm_f32") if k in kernels_ms), None)
     # launches per step (the scan can run in token chunks): time per step of that kernel
     scan_ms = kernels_ms[scan_kernel]["avg"] * kernels_ms[scan_kernel]["launches"] / args.steps
 
@@ -198,6 +229,7 @@ def main():
                    "N": wl.N, "n": wl.n, "W": wl.W, "R": wl.R, "d_v": wl.d_v,
                    "state": f"{args.state} [B,H,N,d_v]", "tokens_per_step": tokens},
         "phases_ms": {"select": ms_sel, "scan": ms_scan, "step_events": ms_step},
+        "gemm": gemm_line(wl, kernels_ms, gemm_kernel, args.steps),
         "kernels_ms": kernels_ms,
         "effective_hbm_gbs_step": slot_bytes / (ms_wall * 1e-3) / 1e9,
         "roofline": {"bound": "hbm", "kernel": scan_kernel, "achieved": achieved,
