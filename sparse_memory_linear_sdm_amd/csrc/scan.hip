@@ -26,7 +26,9 @@ __device__ __forceinline__ float4 f4(float a) { return make_float4(a, a, a, a); 
 // writes and R reads of a token.  Barriers order the write phase, the read phase
 // and the next token's writes (all accesses stay inside one workgroup, whose
 // waves share the CU's vector L1).
-template <int DV, bool GDN, bool BF>
+// LOG: the training forward's write log (a separate instantiation keeps the
+// encoder's registers out of the inference kernel).
+template <int DV, bool GDN, bool BF, bool LOG>
 __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   constexpr uint32_t ES = StateT<BF>::ES;
   constexpr int BQ = 8;  // rows a group keeps in flight
@@ -53,6 +55,8 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     const float4 vv = reinterpret_cast<const float4*>(a.v + tok * DV)[li];
     const int32_t* iw = a.idx_w + tok * a.W;
     const float* ww = a.wt_w + tok * a.W;
+    const int32_t* ir = a.idx_r + tok * a.R;
+    const float* wr = a.wt_r + tok * a.R;
     if constexpr (GDN) {
       // key-weighted prediction of the write set from the rows before this
       // token's writes; row k is read here and written below by the same thread
@@ -107,7 +111,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
         if (k >= a.W) break;
         const float c = be * ww[k];
         const float oc = 1.0f - c;
-        if (a.log)  // training forward: the row as it was before this write
+        if constexpr (LOG)  // training forward: the row as it was before this write
           log_store<LPR>(a.log, a.log_scale, a.log_fmt, tok * a.W + k, DV, m[j], li);
         float4 n;
         n.x = fmaf(c, vv.x, oc * (al * m[j].x));
@@ -118,8 +122,6 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
       }
     }
     __syncthreads();
-    const int32_t* ir = a.idx_r + tok * a.R;
-    const float* wr = a.wt_r + tok * a.R;
     float4 acc = f4(0.0f);
     for (int k0 = grp; k0 < a.R; k0 += G * BQ) {  // same order of the sum, rows batched
       float4 m[BQ];
@@ -167,14 +169,16 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
 
 template <int DV>
 void launch_direct(bool gdn, dim3 grid, hipStream_t s, const ScanArgs& a) {
-  if (gdn && a.state_bf16)
-    hipLaunchKernelGGL((scan_kernel<DV, true, true>), grid, dim3(256), 0, s, a);
+  if (a.log)  // training forward: fp32 state, per-slot rule
+    hipLaunchKernelGGL((scan_kernel<DV, false, false, true>), grid, dim3(256), 0, s, a);
+  else if (gdn && a.state_bf16)
+    hipLaunchKernelGGL((scan_kernel<DV, true, true, false>), grid, dim3(256), 0, s, a);
   else if (gdn)
-    hipLaunchKernelGGL((scan_kernel<DV, true, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((scan_kernel<DV, true, false, false>), grid, dim3(256), 0, s, a);
   else if (a.state_bf16)
-    hipLaunchKernelGGL((scan_kernel<DV, false, true>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((scan_kernel<DV, false, true, false>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((scan_kernel<DV, false, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((scan_kernel<DV, false, false, false>), grid, dim3(256), 0, s, a);
 }
 
 }  // namespace
