@@ -132,6 +132,80 @@ __global__ __launch_bounds__(1024) void bucket_offsets_kernel(StreamArgs a) {
   }
 }
 
+// Pre-pass 2 for walks with many groups x rounds (few long walks: one workgroup per
+// walk would sum them alone): the same offsets from two kernels over blocks of 256
+// groups.  2a: each thread sums one group's counts over the rounds.  2b: each block
+// adds up the totals of the walk's earlier groups, scans its own 256, and writes its
+// groups' running sums over the rounds.  Integer sums: the result is the one above.
+__global__ __launch_bounds__(256) void bucket_totals_kernel(StreamArgs a) {
+  const int nb = (a.GT + 255) / 256;
+  const int64_t w = blockIdx.x / nb;
+  const int g = (int)(blockIdx.x - w * nb) * 256 + (int)threadIdx.x;
+  if (g >= a.GT) return;
+  const int* cnt = a.counts + (int64_t)w * a.rounds * a.GT + g;
+  int acc = 0;
+  for (int r = 0; r < a.rounds; ++r) acc += cnt[(int64_t)r * a.GT];
+  a.totals[(int64_t)w * a.GT + g] = acc;
+}
+
+__global__ __launch_bounds__(256) void bucket_offsets_wide_kernel(StreamArgs a) {
+  __shared__ int sh[256];
+  const int nb = (a.GT + 255) / 256;
+  const int64_t w = blockIdx.x / nb;
+  const int g0 = (int)(blockIdx.x - w * nb) * 256;
+  const int tid = threadIdx.x;
+  const int* tot = a.totals + (int64_t)w * a.GT;
+  // totals of the walk's groups before this block
+  int before = 0;
+  for (int g = tid; g < g0; g += 256) before += tot[g];
+  sh[tid] = before;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (tid < off) sh[tid] += sh[tid + off];
+    __syncthreads();
+  }
+  const int base0 = sh[0];
+  __syncthreads();
+  // exclusive prefix of this block's totals
+  const int g = g0 + tid;
+  const int mine = g < a.GT ? tot[g] : 0;
+  sh[tid] = mine;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int v = tid >= off ? sh[tid - off] : 0;
+    __syncthreads();
+    sh[tid] += v;
+    __syncthreads();
+  }
+  if (g >= a.GT) return;
+  int acc = base0 + sh[tid] - mine;
+  const int* cnt = a.counts + (int64_t)w * a.rounds * a.GT + g;
+  int* o = a.offsets + ((int64_t)w * a.GT + g) * (a.rounds + 1);
+  for (int r = 0; r < a.rounds; ++r) {
+    o[r] = acc;
+    acc += cnt[(int64_t)r * a.GT];
+  }
+  o[a.rounds] = acc;
+}
+
+// Offsets pass: one workgroup per walk, or the two-kernel form when a walk has many
+// groups x rounds.
+hipError_t launch_offsets(const StreamArgs& a, int64_t walks, hipStream_t st) {
+  if ((int64_t)a.GT * a.rounds <= 65536) {
+    KernelTimer kt("bucket_offsets", st);
+    hipLaunchKernelGGL(bucket_offsets_kernel, dim3((unsigned)walks), dim3(1024), 0, st, a);
+    return hipGetLastError();
+  }
+  const dim3 grid((unsigned)(walks * ((a.GT + 255) / 256)));
+  {
+    KernelTimer kt("bucket_totals", st);
+    hipLaunchKernelGGL(bucket_totals_kernel, grid, dim3(256), 0, st, a);
+  }
+  KernelTimer kt("bucket_offsets", st);
+  hipLaunchKernelGGL(bucket_offsets_wide_kernel, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // Pre-pass 3: scatter the accesses of one (walk, round) into the streams.  One
 // wavefront walks the round's tokens in order; LDS cursors hand out positions.
@@ -800,7 +874,7 @@ namespace {
 
 // Byte offsets of the scan's buffers inside the workspace (256-byte aligned).
 struct StreamLayout {
-  size_t counts, offsets, entries, y_part, trash, begins, clean, cstart, stage, total;
+  size_t counts, offsets, totals, entries, y_part, trash, begins, clean, cstart, stage, total;
 };
 
 StreamLayout stream_layout(const sdm_dims& d, const StreamPlan& pl) {
@@ -812,6 +886,8 @@ StreamLayout stream_layout(const sdm_dims& d, const StreamPlan& pl) {
   s += al((size_t)walks * pl.rounds * pl.GT * 4);
   L.offsets = s;
   s += al((size_t)walks * pl.GT * (pl.rounds + 1) * 4);
+  L.totals = s;
+  s += al((size_t)walks * pl.GT * 4);
   L.entries = s;
   s += al((size_t)walks * pl.Tc * (d.W + d.R) * 8);
   L.y_part = s;
@@ -842,10 +918,8 @@ hipError_t launch_stream_buckets(const StreamArgs& a, int64_t walks, bool train,
     hipLaunchKernelGGL(bucket_count_kernel, dim3((unsigned)(walks * a.rounds)), dim3(256), 0, st,
                        a);
   }
-  {
-    KernelTimer kt("bucket_offsets", st);
-    hipLaunchKernelGGL(bucket_offsets_kernel, dim3((unsigned)walks), dim3(1024), 0, st, a);
-  }
+  const hipError_t e = launch_offsets(a, walks, st);
+  if (e != hipSuccess) return e;
   KernelTimer kt("bucket_scatter", st);
   if (train)
     hipLaunchKernelGGL(bucket_scatter_kernel<true>, dim3((unsigned)(walks * a.rounds)), dim3(64),
@@ -906,6 +980,7 @@ hipError_t launch_stream_scan(const ScanArgs& sa, const StreamPlan& pl, void* ws
   char* base = static_cast<char*>(ws);
   a.counts = reinterpret_cast<int*>(base + L.counts);
   a.offsets = reinterpret_cast<int*>(base + L.offsets);
+  a.totals = reinterpret_cast<int*>(base + L.totals);
   a.entries = reinterpret_cast<uint2*>(base + L.entries);
   a.y_part = reinterpret_cast<float*>(base + L.y_part);
   a.trash = reinterpret_cast<float4*>(base + L.trash);
@@ -927,8 +1002,8 @@ hipError_t launch_stream_scan(const ScanArgs& sa, const StreamPlan& pl, void* ws
                          st, a);
     }
     {
-      KernelTimer kt("bucket_offsets", st);
-      hipLaunchKernelGGL(bucket_offsets_kernel, dim3((unsigned)walks), dim3(1024), 0, st, a);
+      const hipError_t e = launch_offsets(a, walks, st);
+      if (e != hipSuccess) return e;
     }
     if (pl.two_phase) {
       const size_t lds = (size_t)pl.GT * 4 + (size_t)((sa.N + 31) / 32) * 4;

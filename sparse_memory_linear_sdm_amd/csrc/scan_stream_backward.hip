@@ -453,7 +453,7 @@ BackPlan back_plan(const sdm_dims& d) {
 }
 
 struct BackLayout {
-  size_t counts, offsets, entries, dy, pw, pr, dv_part, gpart, total;
+  size_t counts, offsets, totals, entries, dy, pw, pr, dv_part, gpart, total;
 };
 
 BackLayout back_layout(const sdm_dims& d, const BackPlan& pl) {
@@ -465,6 +465,8 @@ BackLayout back_layout(const sdm_dims& d, const BackPlan& pl) {
   s += al((size_t)walks * pl.rounds * pl.GT * 4);
   L.offsets = s;
   s += al((size_t)walks * pl.GT * (pl.rounds + 1) * 4);
+  L.totals = s;
+  s += al((size_t)walks * pl.GT * 4);
   L.entries = s;
   s += al((size_t)walks * pl.Tc * (d.W + d.R) * 8);
   L.dy = s;
@@ -509,6 +511,7 @@ hipError_t launch_stream_backward(const sdm_dims& d, const ScanBackArgs& sa, flo
   k.wt_r = sa.wt_r;
   k.counts = reinterpret_cast<int*>(base + L.counts);
   k.offsets = reinterpret_cast<int*>(base + L.offsets);
+  k.totals = reinterpret_cast<int*>(base + L.totals);
   k.entries = reinterpret_cast<uint2*>(base + L.entries);
   k.B = sa.B;
   k.T = sa.T;

@@ -96,6 +96,7 @@ struct StreamArgs {
   int64_t log_T, log_t0;
   int* counts;     // [walks][rounds][GT]
   int* offsets;    // [walks][GT][rounds + 1]
+  int* totals;     // [walks][GT] per-group totals (offsets pass over many groups x rounds)
   // owner-stream entry: {slot | token-in-round << 24, weight bits | read << 31}
   uint2* entries;  // [walks][walk_entries]
   float* y_part;   // [parts][B][Tc][H][d_v]
