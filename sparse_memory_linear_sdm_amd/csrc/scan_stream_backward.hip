@@ -49,8 +49,8 @@ struct BackStreamArgs {
   const uint2* entries;  // [walks][walk_entries]
   const int* offsets;    // [walks][GT][rounds + 1]
   float* dy;             // [B][Tc][H][d_v]
-  float2* pw;            // [S][B][Tc][H][W]  per-slice (dc, gm) of each write
-  float* pr;             // [S][B][Tc][H][R]  per-slice d_q of each read
+  float2* pw;            // [S*parts][B][Tc][H][W]  per (slice, part) (dc, gm) of each write
+  float* pr;             // [S*parts][B][Tc][H][R]  per (slice, part) d_q of each read
   float* dv_part;        // [parts][B][Tc][H][d_v]
   float* gpart;          // [B*H][gblocks][d_v]  d_gamma partials
   int64_t t0, Tc, walk_entries, rows_c;  // rows_c = B*Tc*H
@@ -143,17 +143,26 @@ __global__ __launch_bounds__(256) void back_prep_kernel(BackStreamArgs A) {
 // The reverse walk.  Workgroup = (walk, slice, part); NT threads; SW floats per
 // slice; LPG = SW/4 lanes per group; GW = NT/LPG groups; batches of BQ accesses
 // taken from the end of the group's round segment backwards.
+// Each round is walked in sub-rounds of SUB tokens, last first.  A group's segment
+// is in token order, so a sub-round's accesses are the next run of it going down.
+// Per sub-round the workgroup stages dy, v and the gates of its tokens, collects the
+// partial dots of every access in LDS at (token, id position) -- each access has one
+// owner, so no atomics -- and d_v in an LDS ring, then writes them out as whole rows.
 // ---------------------------------------------------------------------------
+constexpr int SUB = 64;  // tokens per sub-round
+
 template <int NT, int SW, int BQ, int LF>
 __global__ __launch_bounds__(NT) void stream_backward_kernel(BackStreamArgs A) {
   constexpr int LPG = SW / 4;
   constexpr int GW = NT / LPG;
   constexpr int EPL = (BQ + LPG - 1) / LPG;  // entries loaded per lane per batch
   constexpr int YS = SW + 8;  // padded d_v ring row (column 4l + c of lane l at c*LPG + l)
-  __shared__ __attribute__((aligned(16))) float dvr[ROUND * YS];
-  __shared__ __attribute__((aligned(16))) float dys[ROUND * SW];
-  __shared__ __attribute__((aligned(16))) float vs[ROUND * SW];
-  __shared__ float2 gab[ROUND];  // (alpha, beta)
+  __shared__ __attribute__((aligned(16))) float dvr[SUB * YS];
+  __shared__ __attribute__((aligned(16))) float dys[SUB * SW];
+  __shared__ __attribute__((aligned(16))) float vs[SUB * SW];
+  __shared__ float2 gab[SUB];                                        // (alpha, beta)
+  __shared__ float pdq[SUB * SDM_MAX_COUNT];                         // [token][R] d_q
+  __shared__ __attribute__((aligned(8))) float2 pdc[SUB * SDM_MAX_COUNT];  // [token][W] (dc, gm)
 
   const ScanBackArgs& a = A.s;
   const int tid = threadIdx.x;
@@ -169,7 +178,9 @@ __global__ __launch_bounds__(NT) void stream_backward_kernel(BackStreamArgs A) {
   const int gg = p * GW + g;
   const int dv = a.d_v;
 
-  for (int x = tid; x < ROUND * YS; x += NT) dvr[x] = 0.0f;
+  for (int x = tid; x < SUB * YS; x += NT) dvr[x] = 0.0f;
+  for (int x = tid; x < SUB * a.R; x += NT) pdq[x] = 0.0f;
+  for (int x = tid; x < SUB * a.W; x += NT) pdc[x] = make_float2(0.0f, 0.0f);
 
   char* Mb = reinterpret_cast<char*>(a.state + w * (int64_t)a.N * dv);
   char* Gb = reinterpret_cast<char*>(a.d_state + w * (int64_t)a.N * dv);
@@ -181,145 +192,168 @@ __global__ __launch_bounds__(NT) void stream_backward_kernel(BackStreamArgs A) {
   const int* offs = A.offsets + ((int64_t)w * A.GT + gg) * (A.rounds + 1);
   const int64_t tok_base = (b * a.T + A.t0) * a.H + h;  // chunk token t -> tok_base + t*H
   const int64_t tokc_base = b * A.Tc * a.H + h;         // chunk row of t: tokc_base + t*H
-  float2* pw = A.pw + (int64_t)sl * A.rows_c * a.W;
-  float* pr = A.pr + (int64_t)sl * A.rows_c * a.R;
+  const int64_t u = (int64_t)sl * A.parts + p;         // this workgroup's partial-dot plane
+  float2* pw = A.pw + u * A.rows_c * a.W;
+  float* pr = A.pr + u * A.rows_c * a.R;
 
   for (int r = A.rounds - 1; r >= 0; --r) {
     const int64_t t_lo = (int64_t)r * ROUND;
     const int nt = (int)min<int64_t>(ROUND, A.Tc - t_lo);
-    for (int x = tid; x < nt * LPG; x += NT) {
-      const int tt = x / LPG, q4 = x % LPG;
-      const int64_t tok = tok_base + (t_lo + tt) * a.H;
-      const int64_t tokc = tokc_base + (t_lo + tt) * a.H;
-      *reinterpret_cast<float4*>(vs + tt * SW + q4 * 4) =
-          *reinterpret_cast<const float4*>(a.v + tok * dv + sl * SW + q4 * 4);
-      *reinterpret_cast<float4*>(dys + tt * SW + q4 * 4) =
-          *reinterpret_cast<const float4*>(A.dy + tokc * dv + sl * SW + q4 * 4);
-    }
-    for (int x = tid; x < nt; x += NT) {
-      const int64_t tok = tok_base + (t_lo + x) * a.H;
-      gab[x] = make_float2(a.alpha[tok], a.beta[tok]);
-    }
-    __syncthreads();
-
     const int beg = offs[r];
     const int end = offs[r + 1];
-    // entry at stream position i - 1 - j of the batch starting at i (clamped into
-    // the walk's entries; positions below beg are masked off)
+    // entry at stream position pos, clamped into the walk's entries
     auto at = [&](int pos) { return max(min(max(pos, beg), min(end - 1, last)), 0); };
-    uint2 e[EPL];
-#pragma unroll
-    for (int q = 0; q < EPL; ++q) e[q] = ent[at(end - 1 - q * LPG - li)];
-    for (int i = end; i > beg; i -= BQ) {
-      uint2 en[EPL];
-#pragma unroll
-      for (int q = 0; q < EPL; ++q) en[q] = ent[at(i - BQ - 1 - q * LPG - li)];
-      uint32_t slot[BQ];
-      int tk[BQ], kk[BQ];
-      uint32_t rdm = 0, vam = 0;  // bit j: access j is a read / is valid
-      float wq[BQ];
-      float4 X[BQ], Gd[BQ];  // M (reads) or the logged row (writes); dM
-#pragma unroll
-      for (int j = 0; j < BQ; ++j) {
-        const int src = j % LPG, q = j / LPG;
-        const uint32_t ex = group_bcast<LPG>(e[q].x, src);
-        const uint32_t ey = group_bcast<LPG>(e[q].y, src);
-        const bool rd = ey >> 31;
-        slot[j] = min(ex & SLOT_MASK, (uint32_t)a.N - 1u);
-        tk[j] = min((int)(ex >> 24), nt - 1);
-        kk[j] = min((int)(ey & 0x7fffffffu), (rd ? a.R : a.W) - 1);
-        rdm |= (uint32_t)rd << j;
-        vam |= (uint32_t)(i - 1 - j >= beg) << j;
+    int i = end;  // this group's accesses below i are still to be undone
+    for (int s_lo = ((nt - 1) / SUB) * SUB; s_lo >= 0; s_lo -= SUB) {
+      const int ns = min(SUB, nt - s_lo);
+      for (int x = tid; x < ns * LPG; x += NT) {
+        const int tt = x / LPG, q4 = x % LPG;
+        const int64_t tok = tok_base + (t_lo + s_lo + tt) * a.H;
+        const int64_t tokc = tokc_base + (t_lo + s_lo + tt) * a.H;
+        *reinterpret_cast<float4*>(vs + tt * SW + q4 * 4) =
+            *reinterpret_cast<const float4*>(a.v + tok * dv + sl * SW + q4 * 4);
+        *reinterpret_cast<float4*>(dys + tt * SW + q4 * 4) =
+            *reinterpret_cast<const float4*>(A.dy + tokc * dv + sl * SW + q4 * 4);
       }
-#pragma unroll
-      for (int j = 0; j < BQ; ++j) {
-        const bool rd = (rdm >> j) & 1u;
-        const int64_t tok = tok_base + (t_lo + tk[j]) * a.H;
-        wq[j] = rd ? a.wt_r[tok * a.R + kk[j]] : a.wt_w[tok * a.W + kk[j]];
-        const uint32_t off = slot[j] * row_bytes + col_bytes;
-        if constexpr (LF == LOG_F32) {
-          const float4* src =
-              rd ? reinterpret_cast<const float4*>(Mb + off)
-                 : reinterpret_cast<const float4*>(static_cast<const float*>(a.log) +
-                                                   (tok * a.W + kk[j]) * dv) +
-                       c4;
-          X[j] = *src;
-        } else {
-          X[j] = rd ? *reinterpret_cast<const float4*>(Mb + off)
-                    : log_load(a.log, a.log_scale, LF, tok * a.W + kk[j], dv, c4);
-        }
-        Gd[j] = *reinterpret_cast<const float4*>(Gb + off);
+      for (int x = tid; x < ns; x += NT) {
+        const int64_t tok = tok_base + (t_lo + s_lo + x) * a.H;
+        gab[x] = make_float2(a.alpha[tok], a.beta[tok]);
       }
+      __syncthreads();
+
+      uint2 e[EPL];
 #pragma unroll
-      for (int j = 0; j < BQ; ++j) {
-        if (!((vam >> j) & 1u)) continue;
-        // the latest earlier access of this slot in the batch left M in X and dM in Gd
-        float4 mv = X[j], gv = Gd[j];
+      for (int q = 0; q < EPL; ++q) e[q] = ent[at(i - 1 - q * LPG - li)];
+      while (i > beg) {
+        uint2 en[EPL];
 #pragma unroll
-        for (int jj = 0; jj < j; ++jj) {
-          const bool fwd = ((vam >> jj) & 1u) && slot[jj] == slot[j];
-          mv.x = fwd ? X[jj].x : mv.x;
-          mv.y = fwd ? X[jj].y : mv.y;
-          mv.z = fwd ? X[jj].z : mv.z;
-          mv.w = fwd ? X[jj].w : mv.w;
-          gv.x = fwd ? Gd[jj].x : gv.x;
-          gv.y = fwd ? Gd[jj].y : gv.y;
-          gv.z = fwd ? Gd[jj].z : gv.z;
-          gv.w = fwd ? Gd[jj].w : gv.w;
+        for (int q = 0; q < EPL; ++q) en[q] = ent[at(i - BQ - 1 - q * LPG - li)];
+        uint32_t slot[BQ];
+        int tk[BQ], kk[BQ];
+        uint32_t rdm = 0, vam = 0;  // bit j: access j is a read / belongs to this sub-round
+        float wq[BQ];
+        float4 X[BQ], Gd[BQ];  // M (reads) or the logged row (writes); dM
+#pragma unroll
+        for (int j = 0; j < BQ; ++j) {
+          const int src = j % LPG, q = j / LPG;
+          const uint32_t ex = group_bcast<LPG>(e[q].x, src);
+          const uint32_t ey = group_bcast<LPG>(e[q].y, src);
+          const bool rd = ey >> 31;
+          const int tr = min((int)(ex >> 24), nt - 1);  // token within the round
+          slot[j] = min(ex & SLOT_MASK, (uint32_t)a.N - 1u);
+          tk[j] = min(max(tr - s_lo, 0), ns - 1);       // token within the sub-round
+          kk[j] = min((int)(ey & 0x7fffffffu), (rd ? a.R : a.W) - 1);
+          rdm |= (uint32_t)rd << j;
+          // tokens never increase going down a segment: the valid accesses are a prefix
+          vam |= (uint32_t)(i - 1 - j >= beg && tr >= s_lo) << j;
         }
-        const uint32_t off = slot[j] * row_bytes + col_bytes;
-        const int64_t tokc = tokc_base + (t_lo + tk[j]) * a.H;
-        if ((rdm >> j) & 1u) {
-          const float4 d = *reinterpret_cast<const float4*>(dys + tk[j] * SW + li * 4);
-          const float dq = group_sum<LPG>(dot4(d, mv));
-          const float q = wq[j];
-          float4 n;
-          n.x = fmaf(q, d.x, gv.x);
-          n.y = fmaf(q, d.y, gv.y);
-          n.z = fmaf(q, d.z, gv.z);
-          n.w = fmaf(q, d.w, gv.w);
-          *reinterpret_cast<float4*>(Gb + off) = n;
-          if (li == 0) pr[tokc * a.R + kk[j]] = dq;
-          X[j] = mv;
-          Gd[j] = n;
-        } else {
-          const float4 m = X[j];
-          const float2 ab = gab[tk[j]];
-          const float4 vv = *reinterpret_cast<const float4*>(vs + tk[j] * SW + li * 4);
-          const float c = ab.y * wq[j];
-          const float oc = 1.0f - c;
-          const float4 er = make_float4(vv.x - ab.x * m.x, vv.y - ab.x * m.y,
-                                        vv.z - ab.x * m.z, vv.w - ab.x * m.w);
-          const float dc = group_sum<LPG>(dot4(gv, er));
-          const float gm = group_sum<LPG>(dot4(gv, m));
-          float* y = dvr + tk[j] * YS + li;
-          atomicAdd(y + 0 * LPG, c * gv.x);
-          atomicAdd(y + 1 * LPG, c * gv.y);
-          atomicAdd(y + 2 * LPG, c * gv.z);
-          atomicAdd(y + 3 * LPG, c * gv.w);
-          const float f = ab.x * oc;
-          const float4 n = make_float4(f * gv.x, f * gv.y, f * gv.z, f * gv.w);
-          *reinterpret_cast<float4*>(Gb + off) = n;
-          *reinterpret_cast<float4*>(Mb + off) = m;
-          if (li == 0) pw[tokc * a.W + kk[j]] = make_float2(dc, gm);
-          Gd[j] = n;
+        const int m = __builtin_ctz(~vam);  // accesses of this sub-round in the batch
+        if (m == 0) break;
+#pragma unroll
+        for (int j = 0; j < BQ; ++j) {
+          const bool rd = (rdm >> j) & 1u;
+          const int64_t tok = tok_base + (t_lo + s_lo + tk[j]) * a.H;
+          wq[j] = rd ? a.wt_r[tok * a.R + kk[j]] : a.wt_w[tok * a.W + kk[j]];
+          const uint32_t off = slot[j] * row_bytes + col_bytes;
+          if constexpr (LF == LOG_F32) {
+            const float4* src =
+                rd ? reinterpret_cast<const float4*>(Mb + off)
+                   : reinterpret_cast<const float4*>(static_cast<const float*>(a.log) +
+                                                     (tok * a.W + kk[j]) * dv) +
+                         c4;
+            X[j] = *src;
+          } else {
+            X[j] = rd ? *reinterpret_cast<const float4*>(Mb + off)
+                      : log_load(a.log, a.log_scale, LF, tok * a.W + kk[j], dv, c4);
+          }
+          Gd[j] = *reinterpret_cast<const float4*>(Gb + off);
         }
+#pragma unroll
+        for (int j = 0; j < BQ; ++j) {
+          if (!((vam >> j) & 1u)) continue;
+          // the latest earlier access of this slot in the batch left M in X and dM in Gd
+          float4 mv = X[j], gv = Gd[j];
+#pragma unroll
+          for (int jj = 0; jj < j; ++jj) {
+            const bool fwd = ((vam >> jj) & 1u) && slot[jj] == slot[j];
+            mv.x = fwd ? X[jj].x : mv.x;
+            mv.y = fwd ? X[jj].y : mv.y;
+            mv.z = fwd ? X[jj].z : mv.z;
+            mv.w = fwd ? X[jj].w : mv.w;
+            gv.x = fwd ? Gd[jj].x : gv.x;
+            gv.y = fwd ? Gd[jj].y : gv.y;
+            gv.z = fwd ? Gd[jj].z : gv.z;
+            gv.w = fwd ? Gd[jj].w : gv.w;
+          }
+          const uint32_t off = slot[j] * row_bytes + col_bytes;
+          if ((rdm >> j) & 1u) {
+            const float4 d = *reinterpret_cast<const float4*>(dys + tk[j] * SW + li * 4);
+            const float dq = group_sum<LPG>(dot4(d, mv));
+            const float q = wq[j];
+            float4 n;
+            n.x = fmaf(q, d.x, gv.x);
+            n.y = fmaf(q, d.y, gv.y);
+            n.z = fmaf(q, d.z, gv.z);
+            n.w = fmaf(q, d.w, gv.w);
+            *reinterpret_cast<float4*>(Gb + off) = n;
+            if (li == 0) pdq[tk[j] * a.R + kk[j]] = dq;
+            X[j] = mv;
+            Gd[j] = n;
+          } else {
+            const float4 mm = X[j];
+            const float2 ab = gab[tk[j]];
+            const float4 vv = *reinterpret_cast<const float4*>(vs + tk[j] * SW + li * 4);
+            const float c = ab.y * wq[j];
+            const float oc = 1.0f - c;
+            const float4 er = make_float4(vv.x - ab.x * mm.x, vv.y - ab.x * mm.y,
+                                          vv.z - ab.x * mm.z, vv.w - ab.x * mm.w);
+            const float dc = group_sum<LPG>(dot4(gv, er));
+            const float gm = group_sum<LPG>(dot4(gv, mm));
+            float* y = dvr + tk[j] * YS + li;
+            atomicAdd(y + 0 * LPG, c * gv.x);
+            atomicAdd(y + 1 * LPG, c * gv.y);
+            atomicAdd(y + 2 * LPG, c * gv.z);
+            atomicAdd(y + 3 * LPG, c * gv.w);
+            const float f = ab.x * oc;
+            const float4 n = make_float4(f * gv.x, f * gv.y, f * gv.z, f * gv.w);
+            *reinterpret_cast<float4*>(Gb + off) = n;
+            *reinterpret_cast<float4*>(Mb + off) = mm;
+            if (li == 0) pdc[tk[j] * a.W + kk[j]] = make_float2(dc, gm);
+            Gd[j] = n;
+          }
+        }
+        i -= m;
+        if (m < BQ) break;  // the rest of the segment belongs to earlier sub-rounds
+#pragma unroll
+        for (int q = 0; q < EPL; ++q) e[q] = en[q];
       }
-#pragma unroll
-      for (int q = 0; q < EPL; ++q) e[q] = en[q];
-    }
-    __syncthreads();
-    // this part's d_v of the round's tokens; the ring is cleared for the next round
-    for (int x = tid; x < nt * LPG; x += NT) {
-      const int tt = x / LPG, q4 = x % LPG;
-      float* src = dvr + tt * YS + q4;
-      const int64_t tokc = tokc_base + (t_lo + tt) * a.H;
-      *reinterpret_cast<float4*>(A.dv_part + ((int64_t)p * A.rows_c + tokc) * dv + sl * SW +
-                                 q4 * 4) = make_float4(src[0], src[LPG], src[2 * LPG], src[3 * LPG]);
-      src[0] = 0.f;
-      src[LPG] = 0.f;
-      src[2 * LPG] = 0.f;
-      src[3 * LPG] = 0.f;
+      __syncthreads();
+      // this workgroup's d_v and partial dots of the sub-round's tokens, whole rows;
+      // the LDS rows are cleared for the next sub-round
+      for (int x = tid; x < ns * LPG; x += NT) {
+        const int tt = x / LPG, q4 = x % LPG;
+        float* src = dvr + tt * YS + q4;
+        const int64_t tokc = tokc_base + (t_lo + s_lo + tt) * a.H;
+        *reinterpret_cast<float4*>(A.dv_part + ((int64_t)p * A.rows_c + tokc) * dv + sl * SW +
+                                   q4 * 4) = make_float4(src[0], src[LPG], src[2 * LPG], src[3 * LPG]);
+        src[0] = 0.f;
+        src[LPG] = 0.f;
+        src[2 * LPG] = 0.f;
+        src[3 * LPG] = 0.f;
+      }
+      for (int x = tid; x < ns * a.R; x += NT) {
+        const int tt = x / a.R, k = x - tt * a.R;
+        const int64_t tokc = tokc_base + (t_lo + s_lo + tt) * a.H;
+        pr[tokc * a.R + k] = pdq[x];
+        pdq[x] = 0.0f;
+      }
+      for (int x = tid; x < ns * a.W; x += NT) {
+        const int tt = x / a.W, k = x - tt * a.W;
+        const int64_t tokc = tokc_base + (t_lo + s_lo + tt) * a.H;
+        pw[tokc * a.W + k] = pdc[x];
+        pdc[x] = make_float2(0.0f, 0.0f);
+      }
+      // the next sub-round's staging writes only dys / vs / gab, which nothing reads now
     }
   }
 }
@@ -349,8 +383,8 @@ __global__ __launch_bounds__(256) void back_reduce_kernel(BackStreamArgs A) {
   float db = 0.0f, da = 0.0f;
   for (int k = lane; k < a.W; k += 64) {
     float dc = 0.0f, gm = 0.0f;
-    for (int s = 0; s < A.S; ++s) {
-      const float2 x = A.pw[((int64_t)s * A.rows_c + row) * a.W + k];
+    for (int u = 0; u < A.S * A.parts; ++u) {
+      const float2 x = A.pw[((int64_t)u * A.rows_c + row) * a.W + k];
       dc += x.x;
       gm += x.y;
     }
@@ -367,7 +401,7 @@ __global__ __launch_bounds__(256) void back_reduce_kernel(BackStreamArgs A) {
   }
   for (int k = lane; k < a.R; k += 64) {
     float dq = 0.0f;
-    for (int s = 0; s < A.S; ++s) dq += A.pr[((int64_t)s * A.rows_c + row) * a.R + k];
+    for (int u = 0; u < A.S * A.parts; ++u) dq += A.pr[((int64_t)u * A.rows_c + row) * a.R + k];
     a.g_wt_r[tok * a.R + k] = dq;
   }
   const int dv = a.d_v;
@@ -442,7 +476,7 @@ BackPlan back_plan(const sdm_dims& d) {
   pl.log2GT = ilog2i(pl.GT);
   // token chunk: bound the per-token buffers to ~2 GiB
   const int64_t per_tok = walks * ((int64_t)(d.W + d.R) * 8 + (int64_t)d.d_v * 4 +
-                                   (int64_t)pl.S * (d.W * 8 + d.R * 4) +
+                                   (int64_t)pl.S * parts * (d.W * 8 + d.R * 4) +
                                    (int64_t)parts * d.d_v * 4);
   int64_t tc = (2ll << 30) / per_tok;
   tc = tc < ROUND ? ROUND : (tc / ROUND) * ROUND;
@@ -472,9 +506,9 @@ BackLayout back_layout(const sdm_dims& d, const BackPlan& pl) {
   L.dy = s;
   s += al((size_t)walks * pl.Tc * d.d_v * 4);
   L.pw = s;
-  s += al((size_t)pl.S * walks * pl.Tc * d.W * 8);
+  s += al((size_t)pl.S * pl.parts * walks * pl.Tc * d.W * 8);
   L.pr = s;
-  s += al((size_t)pl.S * walks * pl.Tc * d.R * 4);
+  s += al((size_t)pl.S * pl.parts * walks * pl.Tc * d.R * 4);
   L.dv_part = s;
   s += al((size_t)pl.parts * walks * pl.Tc * d.d_v * 4);
   L.gpart = s;
