@@ -65,15 +65,23 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(StreamArgs a) {
   for (int g = threadIdx.x; g < a.GT; g += 256) cnt[g] = 0;
   __syncthreads();
   const int64_t t_lo = (int64_t)r * ROUND;
-  const int64_t t_hi = min<int64_t>(a.Tc, t_lo + ROUND);
+  const int nt = (int)min<int64_t>(ROUND, a.Tc - t_lo);
   const int per = a.W + a.R;
-  const int64_t n = (t_hi - t_lo) * per;
-  for (int64_t e = threadIdx.x; e < n; e += 256) {
-    const int64_t t = t_lo + e / per;
-    const int k = (int)(e % per);
-    const int64_t tok = (b * a.T + a.t0 + t) * a.H + h;
-    const int32_t s = k < a.W ? a.idx_w[tok * a.W + k] : a.idx_r[tok * a.R + (k - a.W)];
-    atomicAdd(&cnt[group_of((uint32_t)s, a.log2GT)], 1);
+  const int n = nt * per;  // at most 256 x 256 accesses: 32-bit indexing
+  const int64_t tok0 = (b * a.T + a.t0 + t_lo) * a.H + h;
+  constexpr int U = 4;  // ids loaded per thread before their atomics
+  for (int e0 = threadIdx.x; e0 < n; e0 += 256 * U) {
+    uint32_t s[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = min(e0 + u * 256, n - 1);
+      const int t = e / per, k = e - t * per;
+      const int64_t tok = tok0 + (int64_t)t * a.H;
+      s[u] = (uint32_t)(k < a.W ? a.idx_w[tok * a.W + k] : a.idx_r[tok * a.R + (k - a.W)]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (e0 + u * 256 < n) atomicAdd(&cnt[group_of(s[u], a.log2GT)], 1);
   }
   __syncthreads();
   int* out = a.counts + ((int64_t)w * a.rounds + r) * a.GT;
@@ -216,6 +224,8 @@ hipError_t launch_offsets(const StreamArgs& a, int64_t walks, hipStream_t st) {
 // ---------------------------------------------------------------------------
 template <bool TRAIN>
 __global__ __launch_bounds__(64) void bucket_scatter_kernel(StreamArgs a) {
+  constexpr int D = 4;   // tokens whose ids are loaded ahead of their placement
+  constexpr int KC = 2;  // 64-wide chunks of W and R (up to 128)
   __shared__ int cur[MAX_GT];
   const int64_t w = blockIdx.x / a.rounds;
   const int r = (int)(blockIdx.x - w * a.rounds);
@@ -227,22 +237,57 @@ __global__ __launch_bounds__(64) void bucket_scatter_kernel(StreamArgs a) {
   __syncthreads();
   uint2* ent = a.entries + w * a.walk_entries;
   const int64_t t_lo = (int64_t)r * ROUND;
-  const int64_t t_hi = min<int64_t>(a.Tc, t_lo + ROUND);
-  for (int64_t t = t_lo; t < t_hi; ++t) {
-    const int64_t tok = (b * a.T + a.t0 + t) * a.H + h;
-    const int tt = (int)(t - t_lo);
-    for (int k = lane; k < a.W; k += 64) {
-      const int32_t s = a.idx_w[tok * a.W + k];
-      const float q = TRAIN ? __uint_as_float((uint32_t)k) : a.wt_w[tok * a.W + k];
-      const int pos = atomicAdd(&cur[group_of((uint32_t)s, a.log2GT)], 1);
-      ent[pos] = make_entry((uint32_t)s, tt, q, false);
+  const int nt = (int)min<int64_t>(ROUND, a.Tc - t_lo);
+  const int64_t tok0 = (b * a.T + a.t0 + t_lo) * a.H + h;  // token tt -> tok0 + tt*H
+  // ids and entry words (weight bits, or the position) of the writes (x*) and reads
+  // (r*) of D tokens
+  uint32_t xs[D][KC], xq[D][KC], rs[D][KC], rq[D][KC];
+  auto fetch = [&](int tb, uint32_t (&fs)[D][KC], uint32_t (&fq)[D][KC], uint32_t (&gs)[D][KC],
+                   uint32_t (&gq)[D][KC]) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      const int64_t tok = tok0 + (int64_t)min(tb + u, nt - 1) * a.H;
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        const int kw = min(c * 64 + lane, a.W - 1), kr = min(c * 64 + lane, a.R - 1);
+        fs[u][c] = (uint32_t)a.idx_w[tok * a.W + kw];
+        fq[u][c] = TRAIN ? (uint32_t)kw : __float_as_uint(a.wt_w[tok * a.W + kw]);
+        gs[u][c] = (uint32_t)a.idx_r[tok * a.R + kr];
+        gq[u][c] = TRAIN ? (uint32_t)kr : __float_as_uint(a.wt_r[tok * a.R + kr]);
+      }
     }
-    for (int k = lane; k < a.R; k += 64) {
-      const int32_t s = a.idx_r[tok * a.R + k];
-      const float q = TRAIN ? __uint_as_float((uint32_t)k) : a.wt_r[tok * a.R + k];
-      const int pos = atomicAdd(&cur[group_of((uint32_t)s, a.log2GT)], 1);
-      ent[pos] = make_entry((uint32_t)s, tt, q, true);
+  };
+  fetch(0, xs, xq, rs, rq);
+  for (int tb = 0; tb < nt; tb += D) {
+    uint32_t ns[D][KC], nq[D][KC], ms[D][KC], mq[D][KC];
+    fetch(tb + D, ns, nq, ms, mq);
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      const int tt = tb + u;
+      if (tt >= nt) break;
+      // writes before reads: a slot's accesses keep token order, writes first
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+        if (c * 64 + lane < a.W) {
+          const int pos = atomicAdd(&cur[group_of(xs[u][c], a.log2GT)], 1);
+          ent[pos] = make_entry(xs[u][c], tt, __uint_as_float(xq[u][c]), false);
+        }
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+        if (c * 64 + lane < a.R) {
+          const int pos = atomicAdd(&cur[group_of(rs[u][c], a.log2GT)], 1);
+          ent[pos] = make_entry(rs[u][c], tt, __uint_as_float(rq[u][c]), true);
+        }
     }
+#pragma unroll
+    for (int u = 0; u < D; ++u)
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        xs[u][c] = ns[u][c];
+        xq[u][c] = nq[u][c];
+        rs[u][c] = ms[u][c];
+        rq[u][c] = mq[u][c];
+      }
   }
 }
 
