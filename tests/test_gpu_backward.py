@@ -363,3 +363,41 @@ def test_quantised_log_over_several_token_chunks():
         codes, amax = O.quantize_rows(host(log_a["rows"][b, :, h]), "fp8")
         assert np.array_equal(host(log_b["scale"][b, :, h]), amax), (b, h)
         assert np.array_equal(host(log_b["rows"][b, :, h]), codes), (b, h)
+
+
+def test_training_at_the_full_bench_size():
+    """The 1.4B-like layer at full size (8 x 4096 tokens, 4 heads, N = 131,044), products
+    from the GPU's own selection, the default schedules (two-phase training forward,
+    slot-owner backward): two complete walks against the oracle's reverse walk from
+    the GPU's final state, log and y; M0 restored bit for bit for every walk."""
+    wl = synth.WORKLOADS["layer1p4b"]
+    h, dd = layer_inputs(wl, seed=11)
+    dm = dims_for(wl)
+    p = ops.select(dm, dd["x"], dd["w_proj"], dd["A"], dd["b_dt"])
+    del dd["x"]
+    gam = dd["gamma"]
+    st = dd["m0"].unsqueeze(0).repeat(wl.B, 1, 1, 1)
+    _, y, log = ops.scan_train(dm, p, gam, st)
+    gen = torch.Generator(device=st.device).manual_seed(12)
+    d_out = torch.randn(y.shape, device=st.device, generator=gen)
+    d_st = torch.randn(st.shape, device=st.device, generator=gen) * 0.1
+    walks = [(0, 0), (wl.B - 1, wl.H - 1)]
+    keep = {(b, hh): (host(st[b, hh]), host(log["rows"][b, :, hh]), host(y[b, :, hh]),
+                      host(d_out[b, :, hh]), host(d_st[b, hh])) for b, hh in walks}
+    dS = d_st.clone()
+    g = ops.scan_backward(dm, p, gam, st, dS, y, log, d_out)
+    torch.cuda.synchronize()
+    m0_h = host(dd["m0"])
+    for b in range(wl.B):
+        for hh in range(wl.H):
+            assert torch.equal(st[b, hh], dd["m0"][hh]), f"M0 not restored for walk {(b, hh)}"
+    for (b, hh), (mT, lg, yy, do, ds) in keep.items():
+        sel = {k: host(p[k][b, :, hh]) for k in ("idx_w", "wt_w", "idx_r", "wt_r", "v", "gate",
+                                                 "alpha", "beta")}
+        og, oM0, odM = O.scan_backward(mT, lg, sel["idx_w"], sel["wt_w"], sel["idx_r"],
+                                       sel["wt_r"], sel["v"], sel["alpha"], sel["beta"], yy,
+                                       sel["gate"], h["gamma"][hh], wl.eps, do, ds)
+        assert np.array_equal(oM0, m0_h[hh])
+        for k in ("d_v", "d_gate", "d_alpha", "d_beta", "d_wt_w", "d_wt_r"):
+            _close_to_scale(host(g[k][b, :, hh]), og[k], f"{k} walk {(b, hh)}")
+        _close_to_scale(host(dS[b, hh]), odM, f"d_state walk {(b, hh)}")
