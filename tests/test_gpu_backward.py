@@ -121,6 +121,7 @@ CASES = [
     (2, 300, 1, 16, 64, 64, 128, "random"),
     (1, 520, 1, 6, 16, 32, 16, "same"),
     (1, 260, 1, 12, 32, 16, 256, "repeat"),
+    (1, 300, 1, 1024, 16, 16, 16, "random"),  # N = 1024^2: the largest slot bitmaps
 ]
 
 
@@ -136,16 +137,18 @@ def test_backward_matches_oracle(B, T, H, n, W, R, d_v, mode, sched):
 
 
 @pytest.mark.parametrize("sched", ["direct", "stream", "two_phase"])
-@pytest.mark.parametrize("T,d_v,W,R", [(80, 64, 16, 16), (600, 32, 16, 16), (300, 16, 16, 16),
-                                       (270, 256, 16, 16), (300, 64, 64, 128),
-                                       (260, 32, 128, 32)])
-def test_training_forward_equals_scan_and_log_is_the_replaced_rows(sched, T, d_v, W, R):
+@pytest.mark.parametrize("T,d_v,W,R,n", [(80, 64, 16, 16, 0), (600, 32, 16, 16, 0),
+                                         (300, 16, 16, 16, 0), (270, 256, 16, 16, 0),
+                                         (300, 64, 64, 128, 0), (260, 32, 128, 32, 0),
+                                         (280, 16, 16, 16, 1024)])  # n = 0: the default
+def test_training_forward_equals_scan_and_log_is_the_replaced_rows(sched, T, d_v, W, R, n):
     """State and log equal the direct scan's bit for bit on every schedule (one owner
     applies each slot's writes in token order, the same arithmetic); y and out equal
     sdm_scan's on the direct schedule bit for bit, on the slot-owner ones up to fp32
     summation order; the log holds the oracle's replaced rows."""
     rng = np.random.default_rng(61 + T)
-    B, H, n = 2, 2, 10 if max(W, R) <= 64 else 12
+    B, H = 2, 2
+    n = n or (10 if max(W, R) <= 64 else 12)
     prod = random_products(rng, B, T, H, n, W, R, d_v, "repeat")
     m0 = (rng.standard_normal((B, H, n * n, d_v)) * 0.3).astype(np.float32)
     gamma = rng.uniform(0.5, 1.5, (H, d_v)).astype(np.float32)
