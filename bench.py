@@ -36,6 +36,8 @@ CSRC = os.path.join(ROOT, "sparse_memory_linear_sdm_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_traffic_layer1p4b.txt")
 SCAN_SOURCE = os.path.join(CSRC, "scan_stream.hip")
 MFMA_FILE = os.path.join(ROOT, "profiles", "proj_gemm_mfma_layer1p4b.txt")
+BACK_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_backward_traffic_layer1p4b.txt")
+BACK_SOURCE = os.path.join(CSRC, "scan_stream_backward.hip")
 GEMM_SOURCE = os.path.join(CSRC, "proj_gemm.hip")
 
 
@@ -58,6 +60,12 @@ def _profile_fields(path: str, source: str):
 def measured_traffic(workload: str):
     """Counter-measured HBM bytes of one scan launch, if taken on the current source."""
     f = _profile_fields(TRAFFIC_FILE, SCAN_SOURCE) if workload == "layer1p4b" else None
+    return int(float(f["traffic_bytes"])) if f else None
+
+
+def measured_back_traffic(workload: str):
+    """Counter-measured HBM bytes of one reverse-walk launch (current source)."""
+    f = _profile_fields(BACK_TRAFFIC_FILE, BACK_SOURCE) if workload == "layer1p4b" else None
     return int(float(f["traffic_bytes"])) if f else None
 
 
@@ -105,6 +113,19 @@ def cpu_baseline(wl, ntok: int) -> dict:
             "sample": f"{wl.name}: tokens 0..{ntok - 1} of batch entry 0, all {wl.H} heads, "
                       f"from x (fp64 projection, brute-force top-{wl.W}/{wl.R} over "
                       f"N={wl.N}, sequential scan, norm+gate); {dt:.1f} s on 1 host thread"}
+
+
+def copy_calibration(mib: int, dev, res: dict) -> None:
+    """A device-to-device copy of known size after the timed steps: the reference
+    kernel for scaling hardware byte counters."""
+    import torch
+    nb = mib << 20
+    src = torch.empty(nb // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    res["copy_calibration_bytes"] = {"read": nb, "write": nb}
 
 
 def gemm_line(wl, kernels_ms, kernel, steps):
@@ -239,13 +260,7 @@ def main():
                          slot_bytes * args.steps / kernels_ms[scan_kernel]["launches"]},
     }
     if args.copy_calibration:
-        nb = args.copy_calibration << 20
-        src = torch.empty(nb // 4, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        res["copy_calibration_bytes"] = {"read": nb, "write": nb}
+        copy_calibration(args.copy_calibration, dev, res)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_tokens)
     print(json.dumps(res), flush=True)
@@ -340,10 +355,13 @@ def train_main(args):
                    "step": "select + scan_train + scan_backward"},
         "kernels_ms": kernels_ms,
         "roofline": {"bound": "hbm", "kernel": back, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_back_traffic(wl.name) if back == "stream_backward" else None,
                      "algorithmic_bytes_per_launch":
                          back_bytes * args.steps / kernels_ms[back]["launches"]},
     }
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, dev, res)
     print(json.dumps(res), flush=True)
 
 
