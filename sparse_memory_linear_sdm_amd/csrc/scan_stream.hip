@@ -549,20 +549,29 @@ __global__ __launch_bounds__(64) void bucket_scatter_rev_kernel(StreamArgs a) {
           }
         }
       }
+      // clean reads grouped by owning part: a ballot per part gives every lane its
+      // place, then one store per lane; lane p records where part p's run starts
       int* cs = a.cstart + ltok * (a.parts + 1);
       uint2* cl = a.clean + ltok * a.R;
-      int base = 0;
-      for (int p = 0; p < a.parts; ++p) {
-        if (lane == 0) cs[p] = base;
+      int base = 0, csv = 0;
+      int cpos[KC];
+#pragma unroll
+      for (int c = 0; c < KC; ++c) cpos[c] = 0;
+      for (int p = 0; p < a.parts; ++p) {  // parts < 64 (plan_stream)
+        csv = lane == p ? base : csv;
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
           const bool mine = pk[c] == p;
           const unsigned long long m = __ballot(mine);
-          if (mine) cl[base + __popcll(m & below)] = make_uint2(rs[u][c], rq[u][c]);
+          cpos[c] = mine ? base + __popcll(m & below) : cpos[c];
           base += __popcll(m);
         }
       }
-      if (lane == 0) cs[a.parts] = base;
+      csv = lane == a.parts ? base : csv;
+      if (lane <= a.parts) cs[lane] = csv;
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+        if (pk[c] >= 0) cl[cpos[c]] = make_uint2(rs[u][c], rq[u][c]);
       __syncthreads();
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
@@ -822,6 +831,7 @@ __global__ __launch_bounds__(256) void norm_gate_kernel(StreamArgs a) {
   float y[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) y[c] = 0.0f;
+#pragma unroll 4
   for (int p = 0; p < a.parts; ++p) {
     const float* src = a.y_part + ((int64_t)p * rows + rr) * DV + li * CPL;
 #pragma unroll
@@ -891,17 +901,22 @@ StreamPlan plan_stream(const sdm_dims& d, int64_t N, int64_t stage_bytes) {
   (void)N;
   StreamPlan pl;
   pl.stage_bytes = stage_bytes;
+  const int64_t walks = d.B * (int64_t)d.H;
+  pl.two_phase = !(d.flags & SDM_FLAG_SCAN_STREAM);
   pl.SW = d.d_v >= 32 ? 32 : d.d_v;
+  // Two-phase: 256-byte column slices (fp32) where the grid still reaches one
+  // workgroup per CU with at most 4 parts.  Longer row segments per access move
+  // faster through HBM; more parts would multiply the partial read vectors.
+  if (pl.two_phase && d.d_v % 64 == 0 && walks * (d.d_v / 64) * 4 >= 256) pl.SW = 64;
   pl.S = d.d_v / pl.SW;
   pl.NT = 1024;
   const int lpg = pl.SW / 4;
   const int gw = pl.NT / lpg;
-  const int64_t walks = d.B * (int64_t)d.H;
-  pl.two_phase = !(d.flags & SDM_FLAG_SCAN_STREAM);
   // the lane groups of a walk are split over `parts` workgroups until the grid
   // reaches one workgroup per CU
   int parts = 1;
-  while (walks * pl.S * parts < 256 && gw * parts * 2 <= MAX_GT) parts *= 2;
+  // (parts stay below 64: the reverse bucketing pass gives each part's start a lane)
+  while (walks * pl.S * parts < 256 && gw * parts * 2 <= MAX_GT && parts * 2 < 64) parts *= 2;
   pl.parts = parts;
   pl.GT = gw * parts;
   pl.log2GT = ilog2(pl.GT);
@@ -1074,12 +1089,21 @@ hipError_t launch_stream_scan(const ScanArgs& sa, const StreamPlan& pl, void* ws
       }
       const dim3 grid((unsigned)(walks * pl.S * pl.parts));
       KernelTimer kt("two_phase_scan", st);
-      if (train && pl.SW == 32)
+      if (train && pl.SW == 64)
+        hipLaunchKernelGGL((two_phase_scan_kernel<1024, 64, BQ_TRAIN32, 8, false, true>), grid,
+                           dim3(1024), 0, st, a);
+      else if (train && pl.SW == 32)
         hipLaunchKernelGGL((two_phase_scan_kernel<1024, 32, BQ_TRAIN32, 8, false, true>), grid,
                            dim3(1024), 0, st, a);
       else if (train)
         hipLaunchKernelGGL((two_phase_scan_kernel<1024, 16, BQ_TRAIN16, 8, false, true>), grid,
                            dim3(1024), 0, st, a);
+      else if (pl.SW == 64 && sa.state_bf16)
+        hipLaunchKernelGGL((two_phase_scan_kernel<1024, 64, 8, 8, true, false>), grid, dim3(1024), 0, st,
+                           a);
+      else if (pl.SW == 64)
+        hipLaunchKernelGGL((two_phase_scan_kernel<1024, 64, 8, 8, false, false>), grid, dim3(1024), 0, st,
+                           a);
       else if (pl.SW == 32 && sa.state_bf16)
         hipLaunchKernelGGL((two_phase_scan_kernel<1024, 32, 8, 8, true, false>), grid, dim3(1024), 0, st,
                            a);

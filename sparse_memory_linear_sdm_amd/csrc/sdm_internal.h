@@ -115,11 +115,38 @@ struct StreamArgs {
 constexpr int kStreamRound = 256;
 constexpr int kStreamMaxGT = 4096;
 
-// Value of lane `src` of this lane's LPG-lane group (LPG = 4 or 8), moved by DPP in
-// the vector ALU (no LDS traffic).  quad_perm broadcasts within each quad; for
-// 8-lane groups row_half_mirror brings the other quad's broadcast across.
+// Lane `src` of a 16-lane row to the whole row (DPP row_newbcast, gfx90a and later).
+template <int SRC>
+__device__ __forceinline__ uint32_t row_bcast16(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x150 + SRC, 0xf, 0xf, false);
+}
+
+// Value of lane `src` of this lane's LPG-lane group (LPG = 4, 8 or 16), moved by DPP
+// in the vector ALU (no LDS traffic).  quad_perm broadcasts within each quad; for
+// 8-lane groups row_half_mirror brings the other quad's broadcast across; a 16-lane
+// group is a DPP row.  `src` is a constant once the callers' loops are unrolled.
 template <int LPG>
 __device__ __forceinline__ uint32_t group_bcast(uint32_t v, int src) {
+  if constexpr (LPG == 16) {
+    switch (src & 15) {
+      case 0: return row_bcast16<0>(v);
+      case 1: return row_bcast16<1>(v);
+      case 2: return row_bcast16<2>(v);
+      case 3: return row_bcast16<3>(v);
+      case 4: return row_bcast16<4>(v);
+      case 5: return row_bcast16<5>(v);
+      case 6: return row_bcast16<6>(v);
+      case 7: return row_bcast16<7>(v);
+      case 8: return row_bcast16<8>(v);
+      case 9: return row_bcast16<9>(v);
+      case 10: return row_bcast16<10>(v);
+      case 11: return row_bcast16<11>(v);
+      case 12: return row_bcast16<12>(v);
+      case 13: return row_bcast16<13>(v);
+      case 14: return row_bcast16<14>(v);
+      default: return row_bcast16<15>(v);
+    }
+  }
   const int q = src & 3;
   const int qp = q | (q << 2) | (q << 4) | (q << 6);  // quad_perm(q,q,q,q)
   uint32_t x;

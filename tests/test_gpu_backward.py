@@ -175,6 +175,39 @@ def test_training_forward_equals_scan_and_log_is_the_replaced_rows(sched, T, d_v
             assert_close(lh[b, :, h], olog, f"log walk {(b, h)}")
 
 
+@pytest.mark.parametrize("fmt", ["fp32", "fp8", "int4"])
+def test_training_forward_with_wide_slices(fmt):
+    """32 walks of d_v = 128: the two-phase training forward runs 256-byte column
+    slices (4 parts).  State and log equal the direct schedule's bit for bit (a
+    quantised log: the same codes and scales); y and out up to fp32 summation order."""
+    rng = np.random.default_rng(67)
+    B, T, H, n, W, R, d_v = 8, 300, 4, 12, 32, 32, 128
+    prod = random_products(rng, B, T, H, n, W, R, d_v, "repeat")
+    m0 = (rng.standard_normal((B, H, n * n, d_v)) * 0.3).astype(np.float32)
+    gamma = rng.uniform(0.5, 1.5, (H, d_v)).astype(np.float32)
+    lf = 0 if fmt == "fp32" else LOG_FLAGS[fmt]
+    d = _dims(B=B, T=T, H=H, n=n, W=W, R=R, d_v=d_v, flags=SCHED["two_phase"] | lf)
+    dd = _dims(B=B, T=T, H=H, n=n, W=W, R=R, d_v=d_v, flags=_lib.SDM_FLAG_SCAN_DIRECT | lf)
+    pd = {k: to_dev(v) for k, v in prod.items()}
+    st_a, st_b = to_dev(m0), to_dev(m0)
+    out_a, y_a, log_a = ops.scan_train(d, pd, to_dev(gamma), st_a)
+    out_b, y_b, log_b = ops.scan_train(dd, pd, to_dev(gamma), st_b)
+    torch.cuda.synchronize()
+    assert torch.equal(st_a, st_b)
+    assert torch.equal(log_a["rows"], log_b["rows"])
+    if fmt != "fp32":
+        assert torch.equal(log_a["scale"], log_b["scale"])
+    assert_close(host(y_a), host(y_b), "y_raw")
+    assert_close(host(out_a), host(out_b), "out")
+    if fmt == "fp32":  # the log against the oracle's replaced rows, two walks
+        lh = host(log_a["rows"])
+        for b, h in ((0, 0), (B - 1, H - 1)):
+            _, _, olog = O.scan(m0[b, h], prod["idx_w"][b, :, h], prod["wt_w"][b, :, h],
+                                prod["idx_r"][b, :, h], prod["wt_r"][b, :, h], prod["v"][b, :, h],
+                                prod["alpha"][b, :, h], prod["beta"][b, :, h], record=True)
+            assert_close(lh[b, :, h], olog, f"log walk {(b, h)}")
+
+
 @pytest.mark.parametrize("sched", ["direct", "stream"])
 def test_backward_is_bit_reproducible_and_without_norm_weight(sched):
     rng = np.random.default_rng(62)

@@ -151,6 +151,56 @@ def test_stage_c_scan(B, T, H, n, W, R, d_v, mode, schedule):
         assert np.array_equal(st[b, h][untouched], m0[b, h][untouched]), "unwritten rows changed"
 
 
+# Enough walks that the two-phase plan takes 256-byte column slices (64 floats per
+# slice, at most 4 parts): 16-lane owner groups, several rounds, ragged tails.
+@pytest.mark.parametrize("state_dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("B,T,H,n,W,R,d_v,mode", [
+    (16, 300, 4, 16, 16, 16, 64, "random"),    # 64 walks, one slice, 4 parts
+    (8, 520, 4, 24, 32, 32, 128, "repeat"),    # 32 walks, two slices, 4 parts
+    (4, 100, 4, 12, 16, 48, 256, "random"),    # 16 walks, four slices, 4 parts
+    (8, 270, 8, 8, 32, 32, 128, "repeat"),     # 64 walks, two slices, 2 parts; N = 64
+])
+def test_stage_c_scan_wide_slices(B, T, H, n, W, R, d_v, mode, state_dtype):
+    rng = np.random.default_rng(B * 100 + T + W + 3)
+    N = n * n
+    prod = random_products(rng, B, T, H, n, W, R, d_v, mode)
+    gamma = rng.uniform(0.5, 1.5, (H, d_v)).astype(np.float32)
+    flags = SCHEDULES["two_phase"]
+    if state_dtype == "bf16":
+        m0, state = _bf16_state(rng, (B, H, N, d_v))
+        flags |= _lib.SDM_FLAG_STATE_BF16
+    else:
+        m0 = (rng.standard_normal((B, H, N, d_v)) * 0.02).astype(np.float32)
+        state = to_dev(m0)
+    d = _dims(B=B, T=T, H=H, n=n, W=W, R=R, d_v=d_v, flags=flags)
+    out, y = ops.scan(d, _prod_dev(prod), to_dev(gamma), state, with_y_raw=True)
+    # the direct schedule on the same inputs: the same state bit for bit
+    st_d = to_dev(m0) if state_dtype == "fp32" else to_dev(m0).to(torch.bfloat16)
+    dd = _dims(B=B, T=T, H=H, n=n, W=W, R=R, d_v=d_v,
+               flags=(flags & ~SCHEDULES["two_phase"]) | _lib.SDM_FLAG_SCAN_DIRECT)
+    out_d, _ = ops.scan(dd, _prod_dev(prod), to_dev(gamma), st_d, with_y_raw=True)
+    torch.cuda.synchronize()
+    assert torch.equal(state, st_d), "two-phase state differs from the direct schedule's"
+    walks = [(b, h) for b in range(B) for h in range(H)]
+    oh, yh = host(out), host(y)
+    if state_dtype == "bf16":
+        st = state.to(torch.float64).cpu().numpy()
+        ref = oracle_walks(prod, m0, gamma, 1e-6, walks, state="bf16")
+        for (b, h), (o_out, o_y, o_M) in ref.items():
+            scale = max(np.abs(o_M).max(), np.abs(m0[b, h]).max())
+            check_bf16_state(st[b, h], o_M, scale, f"state walk {(b, h)}")
+            check_bf16_reads(yh[b, :, h], o_y, oh[b, :, h], gamma[h], prod["gate"][b, :, h],
+                             1e-6, scale, R, f"walk {(b, h)}")
+        return
+    st = host(state)
+    ref = oracle_walks(prod, m0, gamma, 1e-6, walks)
+    for (b, h), (o_out, o_y, o_M) in ref.items():
+        assert_close(yh[b, :, h], o_y, f"y_raw walk {(b, h)}")
+        assert_close(oh[b, :, h], o_out, f"out walk {(b, h)}")
+        assert_close(st[b, h], o_M, f"state walk {(b, h)}")
+    assert_close(oh, host(out_d), "out against the direct schedule")
+
+
 @pytest.mark.parametrize("B,T,H,n,W,R,d_v,mode", [
     (2, 64, 2, 8, 64, 64, 32, "random"),       # every slot selected (the GDN-reduction shape)
     (1, 300, 2, 16, 32, 128, 64, "random"),    # W = 32 / R = 128
