@@ -69,8 +69,10 @@ template <int LPG>
 __device__ __forceinline__ float group_sum(float x) {
   x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xf, 0xf, false));
   x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xf, 0xf, false));
-  if (LPG == 8)
+  if (LPG >= 8)  // row_half_mirror: the other quad of the 8-lane half-row
     x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xf, 0xf, false));
+  if (LPG == 16)  // row_mirror: the other half of the 16-lane row
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xf, 0xf, false));
   return x;
 }
 
@@ -446,7 +448,9 @@ void launch_walk_sw(int fmt, dim3 grid, hipStream_t st, const BackStreamArgs& A)
 }
 
 void launch_walk(int sw, int fmt, dim3 grid, hipStream_t st, const BackStreamArgs& A) {
-  if (sw == 32)
+  if (sw == 64)
+    launch_walk_sw<64>(fmt, grid, st, A);
+  else if (sw == 32)
     launch_walk_sw<32>(fmt, grid, st, A);
   else
     launch_walk_sw<16>(fmt, grid, st, A);
@@ -465,10 +469,12 @@ int ilog2i(int x) {
 
 BackPlan back_plan(const sdm_dims& d) {
   BackPlan pl;
+  const int64_t walks = d.B * (int64_t)d.H;
   pl.SW = d.d_v >= 32 ? 32 : d.d_v;
+  // 256-byte column slices where at most 4 parts fill the grid (as the forward)
+  if (d.d_v % 64 == 0 && walks * (d.d_v / 64) * 4 >= 256) pl.SW = 64;
   pl.S = d.d_v / pl.SW;
   const int gw = kNT / (pl.SW / 4);
-  const int64_t walks = d.B * (int64_t)d.H;
   int parts = 1;
   while (walks * pl.S * parts < 256 && gw * parts * 2 <= kStreamMaxGT) parts *= 2;
   pl.parts = parts;

@@ -311,6 +311,22 @@ def test_backward_with_quantised_log(B, T, H, n, W, R, d_v, mode, fmt, sched):
     say(f"  {fmt} log: gradient distance to the fp32 log {rel}; restored state off by {drift:.2e}")
 
 
+@pytest.mark.parametrize("fmt", ["fp32", "fp8", "int4"])
+@pytest.mark.parametrize("B,T,H,n,W,R,d_v,mode", [
+    (8, 260, 4, 8, 16, 16, 128, "repeat"),     # 32 walks: two 256-byte slices, 4 parts
+    (16, 130, 4, 10, 16, 16, 64, "random"),    # 64 walks: one slice, 4 parts
+])
+def test_stream_backward_with_wide_slices(B, T, H, n, W, R, d_v, mode, fmt):
+    """Walk counts at which the reverse walk takes 256-byte column slices (16-lane
+    owner groups): every walk against the oracle, the state restored."""
+    rng = np.random.default_rng(B * 10 + T + d_v)
+    prod = random_products(rng, B, T, H, n, W, R, d_v, mode)
+    m0 = (rng.standard_normal((B, H, n * n, d_v)) * 0.3).astype(np.float32)
+    gamma = rng.uniform(0.5, 1.5, (H, d_v)).astype(np.float32)
+    d = _dims(B=B, T=T, H=H, n=n, W=W, R=R, d_v=d_v, flags=LOG_FLAGS.get(fmt, 0))
+    _run(d, prod, gamma, m0, rng, [(b, h) for b in range(B) for h in range(H)], "stream")
+
+
 def _strided_products(rng, B, T, H, n, W, R, d_v):
     """Distinct ids per token without a per-token loop: an offset and an odd stride
     modulo N = n^2 (a power of two), ascending."""
