@@ -823,11 +823,13 @@ __global__ __launch_bounds__(256) void norm_gate_kernel(StreamArgs a) {
   const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + sub;
   const int64_t rows = a.B * a.Tc * a.H;
   const bool ok = row < rows;
-  const int64_t rr = ok ? row : 0;
-  const int64_t h = rr % a.H;
-  const int64_t bt = rr / a.H;
-  const int64_t b = bt / a.Tc, t = bt % a.Tc;
-  const int64_t grow = (b * a.T + a.t0 + t) * a.H + h;  // row of the full [B,T,H] arrays
+  // a chunk's rows fit 32 bits (its buffers are bounded near 2 GiB): 32-bit index
+  // arithmetic, far cheaper per lane than 64-bit division
+  const uint32_t rr = ok ? (uint32_t)row : 0u;
+  const uint32_t h = rr % (uint32_t)a.H;
+  const uint32_t bt = rr / (uint32_t)a.H;
+  const uint32_t b = bt / (uint32_t)a.Tc, t = bt - b * (uint32_t)a.Tc;
+  const int64_t grow = ((int64_t)b * a.T + a.t0 + t) * a.H + h;  // row of the full [B,T,H] arrays
   float y[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) y[c] = 0.0f;
@@ -869,24 +871,22 @@ __global__ __launch_bounds__(256) void norm_gate_kernel(StreamArgs a) {
 
 // Training forward with a quantised log: the walk left the chunk's replaced rows in
 // fp32 in the staging area ([B][Tc of the plan][H][W] rows); encode each row with its
-// absmax into the caller's log at its global place.  LPR lanes per row.
+// absmax into the caller's log at its global place.  One workgroup per (b, t, h) of
+// the chunk, its W rows RPB at a time, LPR lanes per row.
 template <int DV>
 __global__ __launch_bounds__(256) void log_quantize_kernel(StreamArgs a, ScanArgs sa) {
-  constexpr int LPR = DV / 4;  // one float4 per lane (at most a wavefront per row)
+  constexpr int LPR = DV / 4;      // one float4 per lane (at most a wavefront per row)
+  constexpr int RPB = 256 / LPR;   // rows per pass
+  const uint32_t bth = blockIdx.x;  // (b * Tc + t) * H + h; a chunk's count fits 32 bits
+  const uint32_t h = bth % (uint32_t)a.H;
+  const uint32_t bt = bth / (uint32_t)a.H;
+  const uint32_t b = bt / (uint32_t)a.Tc, t = bt - b * (uint32_t)a.Tc;
+  const float4* src =
+      reinterpret_cast<const float4*>(a.log + (((int64_t)b * a.log_T + t) * a.H + h) * a.W * DV);
+  const int64_t r0 = (((int64_t)b * a.T + a.t0 + t) * a.H + h) * a.W;
   const int li = threadIdx.x % LPR;
-  const int64_t row = (int64_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
-  const int64_t rows = a.B * a.Tc * a.H * a.W;
-  if (row >= rows) return;  // whole row groups
-  const int64_t k = row % a.W;
-  const int64_t bth = row / a.W;
-  const int64_t h = bth % a.H;
-  const int64_t bt = bth / a.H;
-  const int64_t t = bt % a.Tc;
-  const int64_t b = bt / a.Tc;
-  const float4 m = reinterpret_cast<const float4*>(
-      a.log + (((b * a.log_T + t) * a.H + h) * a.W + k) * DV)[li];
-  const int64_t r = ((b * a.T + a.t0 + t) * a.H + h) * a.W + k;
-  log_store<LPR>(sa.log, sa.log_scale, sa.log_fmt, r, DV, m, li);
+  for (int k = threadIdx.x / LPR; k < a.W; k += RPB)  // a row's lanes share k
+    log_store<LPR>(sa.log, sa.log_scale, sa.log_fmt, r0 + k, DV, src[k * LPR + li], li);
 }
 
 int ilog2(int x) {
@@ -1144,9 +1144,7 @@ hipError_t launch_stream_scan(const ScanArgs& sa, const StreamPlan& pl, void* ws
         hipLaunchKernelGGL((stream_scan_kernel<1024, 16, 8, false, false>), grid, dim3(1024), 0, st, a);
     }
     if (qlog) {
-      const int64_t rows = sa.B * a.Tc * sa.H * sa.W;
-      const int64_t rpb = 256 / (sa.d_v / 4);
-      const dim3 qg((unsigned)((rows + rpb - 1) / rpb));
+      const dim3 qg((unsigned)(sa.B * a.Tc * sa.H));
       KernelTimer kt("log_quantize", st);
       switch (sa.d_v) {
         case 16: hipLaunchKernelGGL(log_quantize_kernel<16>, qg, dim3(256), 0, st, a, sa); break;

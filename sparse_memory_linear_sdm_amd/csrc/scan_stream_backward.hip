@@ -373,14 +373,18 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 __global__ __launch_bounds__(256) void back_reduce_kernel(BackStreamArgs A) {
   const ScanBackArgs& a = A.s;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  // one row per wavefront (uniform, so the index arithmetic is scalar); a chunk's
+  // rows fit 32 bits
+  const uint32_t row32 =
+      (uint32_t)__builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
+  const int64_t row = row32;
   if (row >= A.rows_c) return;
   const int lane = threadIdx.x & 63;
-  const int64_t bt = row / a.H;
-  const int h = (int)(row - bt * a.H);
-  const int64_t b = bt / A.Tc;
-  const int64_t t = bt - b * A.Tc;
-  const int64_t tok = (b * a.T + A.t0 + t) * a.H + h;
+  const uint32_t bt = row32 / (uint32_t)a.H;
+  const int h = (int)(row32 - bt * (uint32_t)a.H);
+  const uint32_t b = bt / (uint32_t)A.Tc;
+  const uint32_t t = bt - b * (uint32_t)A.Tc;
+  const int64_t tok = ((int64_t)b * a.T + A.t0 + t) * a.H + h;
   const float be = a.beta[tok];
   float db = 0.0f, da = 0.0f;
   for (int k = lane; k < a.W; k += 64) {
