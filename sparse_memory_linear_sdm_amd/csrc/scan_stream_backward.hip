@@ -433,9 +433,14 @@ __global__ __launch_bounds__(256) void gamma_blocks_kernel(const float* __restri
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= (int64_t)H * DV) return;
   const int64_t h = e / DV, c = e - h * DV;
+  // partials in (batch, block) order; the loads of 8 terms are issued together (the
+  // sum keeps its order, so the result is the same bit for bit)
   float s = 0.0f;
-  for (int64_t b = 0; b < B; ++b)
-    for (int q = 0; q < gblocks; ++q) s += part[((b * H + h) * gblocks + q) * DV + c];
+  for (int64_t b = 0; b < B; ++b) {
+    const float* pb = part + (b * H + h) * gblocks * DV + c;
+#pragma unroll 8
+    for (int q = 0; q < gblocks; ++q) s += pb[(int64_t)q * DV];
+  }
   d_norm_w[e] = s;
 }
 
