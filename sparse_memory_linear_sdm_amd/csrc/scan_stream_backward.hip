@@ -103,6 +103,7 @@ __global__ __launch_bounds__(256) void back_prep_kernel(BackStreamArgs A) {
                               : f4s(1.0f);
   float4 dgam = f4s(0.0f);
   const int64_t t_hi = min<int64_t>(A.Tc, (int64_t)(blk + 1) * PREP_TOK);
+#pragma unroll 4  // several tokens' loads in flight; d_gamma keeps its summation order
   for (int64_t t = (int64_t)blk * PREP_TOK + grp; t < t_hi; t += G) {
     const int64_t tok = (b * a.T + A.t0 + t) * a.H + h;
     const int64_t tokc = (b * A.Tc + t) * a.H + h;
@@ -389,6 +390,7 @@ __global__ __launch_bounds__(256) void back_reduce_kernel(BackStreamArgs A) {
   float db = 0.0f, da = 0.0f;
   for (int k = lane; k < a.W; k += 64) {
     float dc = 0.0f, gm = 0.0f;
+#pragma unroll 8  // the planes' loads go out together; the sums keep their order
     for (int u = 0; u < A.S * A.parts; ++u) {
       const float2 x = A.pw[((int64_t)u * A.rows_c + row) * a.W + k];
       dc += x.x;
@@ -407,12 +409,14 @@ __global__ __launch_bounds__(256) void back_reduce_kernel(BackStreamArgs A) {
   }
   for (int k = lane; k < a.R; k += 64) {
     float dq = 0.0f;
+#pragma unroll 8
     for (int u = 0; u < A.S * A.parts; ++u) dq += A.pr[((int64_t)u * A.rows_c + row) * a.R + k];
     a.g_wt_r[tok * a.R + k] = dq;
   }
   const int dv = a.d_v;
   for (int q4 = lane; q4 < dv / 4; q4 += 64) {
     float4 sv = f4s(0.0f);
+#pragma unroll 4
     for (int p = 0; p < A.parts; ++p) {
       const float4 o =
           *reinterpret_cast<const float4*>(A.dv_part + ((int64_t)p * A.rows_c + row) * dv + q4 * 4);
