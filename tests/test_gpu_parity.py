@@ -159,6 +159,8 @@ def test_stage_c_scan(B, T, H, n, W, R, d_v, mode, schedule):
     (8, 520, 4, 24, 32, 32, 128, "repeat"),    # 32 walks, two slices, 4 parts
     (4, 100, 4, 12, 16, 48, 256, "random"),    # 16 walks, four slices, 4 parts
     (8, 270, 8, 8, 32, 32, 128, "repeat"),     # 64 walks, two slices, 2 parts; N = 64
+    (16, 270, 4, 4, 1, 1, 64, "random"),       # W = R = 1 (most lanes idle), N = 16
+    (8, 260, 4, 12, 64, 128, 128, "repeat"),   # R > 64: two id chunks per token when bucketing
 ])
 def test_stage_c_scan_wide_slices(B, T, H, n, W, R, d_v, mode, state_dtype):
     rng = np.random.default_rng(B * 100 + T + W + 3)
