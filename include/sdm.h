@@ -270,15 +270,15 @@ SDM_API int32_t sdm_forward(const sdm_dims* dims, const void* x, const void* w_p
  *   y_raw   required here (the backward needs it)
  *   ws      >= sdm_workspace_bytes(dims, SDM_ENTRY_SCAN_TRAIN) bytes (may be NULL
  *           if 0)
- *   Schedules: the stream schedule from 256 tokens (or with SDM_FLAG_SCAN_STREAM),
- *   else the direct one (SDM_FLAG_SCAN_DIRECT forces it).  On the stream schedule a
- *   quantised log is staged in fp32 in the workspace (token chunks bounded near
- *   2 GiB) and encoded after each chunk's walk.  The state, the log and its scales
- *   equal those of sdm_scan and of either schedule bit for bit; y_raw and out equal
- *   sdm_scan's on the same schedule, bit for bit on the direct one and up to fp32
- *   summation order on the stream one.  fp32 state and the per-slot rule only:
- *   SDM_FLAG_STATE_BF16, SDM_FLAG_DELTA_GDN or SDM_FLAG_SCAN_TWO_PHASE give
- *   SDM_ERR_UNSUPPORTED.
+ *   Schedules: a schedule flag picks one (SDM_FLAG_SCAN_DIRECT, _STREAM or
+ *   _TWO_PHASE); without one, the two-phase schedule from 256 tokens and the direct
+ *   one below.  On the slot-owner (stream, two-phase) schedules a quantised log is
+ *   staged in fp32 in the workspace (token chunks bounded near 2 GiB) and encoded
+ *   after each chunk's walk.  The state, the log and its scales equal those of
+ *   sdm_scan and of every schedule bit for bit; y_raw and out equal sdm_scan's on
+ *   the same schedule, bit for bit on the direct one and up to fp32 summation order
+ *   on the slot-owner ones.  fp32 state and the per-slot rule only:
+ *   SDM_FLAG_STATE_BF16 or SDM_FLAG_DELTA_GDN give SDM_ERR_UNSUPPORTED.
  *
  * sdm_scan_backward: gradients of that call, walking the tokens in reverse (per
  * token: the norm and gate, the read, then the write, whose overwritten rows are
@@ -293,8 +293,9 @@ SDM_API int32_t sdm_forward(const sdm_dims* dims, const void* x, const void* w_p
  *           [B,T,H,d_v], d_alpha and d_beta [B,T,H]; d_norm_w [H, d_v] (summed over
  *           the batch) or NULL
  *   ws      >= sdm_workspace_bytes(dims, SDM_ENTRY_SCAN_BACKWARD) bytes
- * Schedules: the stream schedule from 256 tokens (or with SDM_FLAG_SCAN_STREAM):
- * slot-owner lane groups walk the accesses of each slot in reverse, any log format;
+ * Schedules: the slot-owner walk from 256 tokens (or with SDM_FLAG_SCAN_STREAM or
+ * SDM_FLAG_SCAN_TWO_PHASE, which both select it): slot-owner lane groups walk the
+ * accesses of each slot in reverse, any log format;
  * else (or with SDM_FLAG_SCAN_DIRECT) one workgroup per (b, h), tokens in lock-step.
  * Every sum runs in a fixed order, so results are bit-reproducible, except d_v on
  * the stream schedule (summed with float atomics: reproducible up to fp32 summation
