@@ -108,6 +108,29 @@ def random_products(rng, B, T, H, n, W, R, d_v, mode="random"):
                 beta=rng.uniform(0.0, 1.0, shp).astype(np.float32))
 
 
+def strided_products(rng, B, T, H, n, W, R, d_v):
+    """Distinct ids per token without a per-token loop: an offset and an odd stride
+    modulo N = n^2 (a power of two), ascending."""
+    N = n * n
+    assert N & (N - 1) == 0 and max(W, R) <= N
+    shp = (B, T, H)
+
+    def ids(count):
+        o = rng.integers(0, N, shp + (1,))
+        st = rng.integers(0, N // 2, shp + (1,)) * 2 + 1
+        return np.sort((o + st * np.arange(count)) % N, axis=-1).astype(np.int32)
+
+    def wts(count):
+        w = rng.uniform(0.05, 1.0, shp + (count,)).astype(np.float32)
+        return (w / w.sum(-1, keepdims=True)).astype(np.float32)
+
+    return dict(idx_w=ids(W), wt_w=wts(W), idx_r=ids(R), wt_r=wts(R),
+                v=rng.standard_normal(shp + (d_v,)).astype(np.float32),
+                gate=rng.uniform(0, 1, shp + (d_v,)).astype(np.float32),
+                alpha=rng.uniform(0.3, 1.0, shp).astype(np.float32),
+                beta=rng.uniform(0.0, 1.0, shp).astype(np.float32))
+
+
 def oracle_walks(prod_h, m0_h, gamma, eps, walks, rule="slot", state="exact"):
     """Oracle scan + norm for the listed (b, h) walks from given products."""
     res = {}

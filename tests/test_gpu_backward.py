@@ -21,7 +21,8 @@ import torch
 
 from oracle import sdm_oracle as O
 from sparse_memory_linear_sdm_amd import _lib, dims_for, ops, synth
-from tests.gpu_util import assert_close, host, layer_inputs, random_products, say, to_dev
+from tests.gpu_util import (assert_close, host, layer_inputs, random_products, say,
+                            strided_products, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -327,36 +328,13 @@ def test_stream_backward_with_wide_slices(B, T, H, n, W, R, d_v, mode, fmt):
     _run(d, prod, gamma, m0, rng, [(b, h) for b in range(B) for h in range(H)], "stream")
 
 
-def _strided_products(rng, B, T, H, n, W, R, d_v):
-    """Distinct ids per token without a per-token loop: an offset and an odd stride
-    modulo N = n^2 (a power of two), ascending."""
-    N = n * n
-    assert N & (N - 1) == 0 and max(W, R) <= N
-    shp = (B, T, H)
-
-    def ids(count):
-        o = rng.integers(0, N, shp + (1,))
-        st = rng.integers(0, N // 2, shp + (1,)) * 2 + 1
-        return np.sort((o + st * np.arange(count)) % N, axis=-1).astype(np.int32)
-
-    def wts(count):
-        w = rng.uniform(0.05, 1.0, shp + (count,)).astype(np.float32)
-        return (w / w.sum(-1, keepdims=True)).astype(np.float32)
-
-    return dict(idx_w=ids(W), wt_w=wts(W), idx_r=ids(R), wt_r=wts(R),
-                v=rng.standard_normal(shp + (d_v,)).astype(np.float32),
-                gate=rng.uniform(0, 1, shp + (d_v,)).astype(np.float32),
-                alpha=rng.uniform(0.3, 1.0, shp).astype(np.float32),
-                beta=rng.uniform(0.0, 1.0, shp).astype(np.float32))
-
-
 def test_stream_backward_over_several_token_chunks():
     """A run long enough that the stream schedule splits it into token chunks (its
     per-token buffers are bounded near 2 GiB): sampled walks against the oracle,
     the initial state restored bit for bit, d_norm_w against the direct schedule."""
     B, T, H, n, W, R, d_v = 8, 66000, 4, 8, 16, 16, 16
     rng = np.random.default_rng(65)
-    prod = _strided_products(rng, B, T, H, n, W, R, d_v)
+    prod = strided_products(rng, B, T, H, n, W, R, d_v)
     m0 = (rng.standard_normal((B, H, n * n, d_v)) * 0.3).astype(np.float32)
     gamma = rng.uniform(0.5, 1.5, (H, d_v)).astype(np.float32)
     d = _dims(B=B, T=T, H=H, n=n, W=W, R=R, d_v=d_v)
@@ -395,7 +373,7 @@ def test_quantised_log_over_several_token_chunks():
     of that run's fp32 rows."""
     B, T, H, n, W, R, d_v = 8, 80000, 4, 8, 16, 16, 16
     rng = np.random.default_rng(66)
-    prod = _strided_products(rng, B, T, H, n, W, R, d_v)
+    prod = strided_products(rng, B, T, H, n, W, R, d_v)
     m0 = (rng.standard_normal((B, H, n * n, d_v)) * 0.3).astype(np.float32)
     pd = {k: to_dev(v) for k, v in prod.items()}
     d32 = _dims(B=B, T=T, H=H, n=n, W=W, R=R, d_v=d_v)

@@ -19,7 +19,7 @@ from oracle import sdm_oracle as O
 from sparse_memory_linear_sdm_amd import _lib, dims_for, ops, synth
 from tests.gpu_util import (ATOL, NEAR_TIE, RTOL, assert_close, broadcast_state, check_bf16_reads,
                             check_bf16_state, gemm_bound, host, layer_inputs, oracle_walks,
-                            random_products, say, to_dev)
+                            random_products, say, strided_products, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -440,6 +440,42 @@ def test_stage_d_forward_from_x(wl):
         for (b, hh), (oo, _, oM) in ref.items():
             assert_close(host(out)[b, :, hh], oo, f"out {(b, hh)}")
             assert_close(host(state)[b, hh], oM, f"state {(b, hh)}")
+
+
+def test_forward_scan_over_several_token_chunks():
+    """A run long enough that both slot-owner schedules split it into token chunks
+    (their per-token buffers are bounded near 2 GiB): 32 walks of d_v = 128, which the
+    two-phase schedule runs in 256-byte slices (3 chunks) and the stream schedule in
+    128-byte ones (2 chunks).  The state equals the direct schedule's bit for bit, y
+    and out agree within tolerance, and one walk's final state and reads match the
+    oracle."""
+    B, T, H, n, W, R, d_v = 8, 56000, 4, 8, 16, 16, 128
+    rng = np.random.default_rng(66)
+    prod = strided_products(rng, B, T, H, n, W, R, d_v)
+    m0 = (rng.standard_normal((B, H, n * n, d_v)) * 0.3).astype(np.float32)
+    gamma = rng.uniform(0.5, 1.5, (H, d_v)).astype(np.float32)
+    pd = _prod_dev(prod)
+    gam = to_dev(gamma)
+    res = {}
+    for sched in ("direct", "stream", "two_phase"):
+        d = _dims(B=B, T=T, H=H, n=n, W=W, R=R, d_v=d_v, flags=SCHEDULES[sched])
+        st = to_dev(m0)
+        out, y = ops.scan(d, pd, gam, st, with_y_raw=True)
+        torch.cuda.synchronize()
+        res[sched] = (st, out, y)
+        say(f"  {sched}: workspace {_lib.workspace_bytes(d, _lib.SDM_ENTRY_SCAN) / 2**30:.2f} GiB")
+    st_d, out_d, y_d = res["direct"]
+    for sched in ("stream", "two_phase"):
+        st, out, y = res[sched]
+        assert torch.equal(st, st_d), f"{sched}: state differs from the direct schedule's"
+        for what, a, b in (("y_raw", y, y_d), ("out", out, out_d)):
+            bad = int(((a - b).abs() > ATOL + RTOL * b.abs()).sum())
+            assert bad == 0, f"{sched} {what}: {bad} elements outside tolerance"
+    b, h = B - 1, H - 1
+    o_y, o_M = O.scan(m0[b, h], *(prod[k][b, :, h] for k in ("idx_w", "wt_w", "idx_r", "wt_r",
+                                                               "v", "alpha", "beta")))
+    assert_close(host(st_d[b, h]), o_M, f"final state walk {(b, h)}")
+    assert_close(host(res["two_phase"][2][b, :, h]), o_y, f"y_raw walk {(b, h)}")
 
 
 def test_chunked_calls_equal_one_call():
