@@ -47,8 +47,9 @@ training checkpoints; the format details are a reading).
 
 Pins (every function is checked against something other than itself):
   tests/test_oracle_pins.py            selection, gates, scan, norm, whole layer:
-                                       hand-worked fixtures (tests/golden/), closed
-                                       forms, exact rationals, brute force,
+                                       hand-worked fixtures (tests/golden/, the
+                                       layer's wiring from x in layer_wiring.json),
+                                       closed forms, exact rationals, brute force,
                                        invariants
   tests/test_oracle_mutations.py       planted mistakes, each caught by a pin
   tests/test_oracle_gdn_pins.py        scan_gdn against a dense matrix recurrence

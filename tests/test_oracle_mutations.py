@@ -13,7 +13,8 @@ F64 = np.float64
 
 
 def _scan_variant(decay_all=False, read_first=False, no_forget=False, sign=1.0):
-    def scan(state0, idx_w, wt_w, idx_r, wt_r, v, alpha, beta):
+    def scan(state0, idx_w, wt_w, idx_r, wt_r, v, alpha, beta, store=None, record=False):
+        assert store is None and not record, "mutant covers the exact-state forward only"
         M = np.array(state0, dtype=F64, copy=True)
         idx_w, idx_r = np.asarray(idx_w), np.asarray(idx_r)
         wt_w, wt_r = np.asarray(wt_w, F64), np.asarray(wt_r, F64)
@@ -81,6 +82,45 @@ def _beta_tanh(b):
     return np.tanh(np.asarray(b, F64))
 
 
+def _select_roles_swapped(scores, n, W, R):
+    """Write slots taken from the read halves and read slots from the write halves."""
+    s = np.asarray(scores, F64)
+    swapped = np.concatenate([s[..., 2 * n:4 * n], s[..., 0:2 * n]], axis=-1)
+    return O.__dict__["_orig_select_from_scores"](swapped, n, W, R)
+
+
+def _pass_a_variant(swap_ab=False, swap_vg=False):
+    def pass_a(x, w_proj, A, b_dt, H, n, d_v, W, R, gate_act=O.GATE_SIGMOID):
+        p = O.split_heads(O.project(x, w_proj), H, n, d_v)
+        a, b = (p["b"], p["a"]) if swap_ab else (p["a"], p["b"])
+        v, g = (p["g"], p["v"]) if swap_vg else (p["v"], p["g"])
+        out = dict(v=v, g=O.gate_activation(g, gate_act),
+                   alpha=O.forget_gate(a, np.asarray(A, F64), np.asarray(b_dt, F64)),
+                   beta=O.input_gate(b),
+                   scores=np.concatenate([p["kw1"], p["kw2"], p["kr1"], p["kr2"]], axis=-1))
+        out.update(O.select_from_scores(out["scores"], n, W, R))
+        return out
+    return pass_a
+
+
+def _forward_head0_gamma(x, w_proj, A, b_dt, gamma, state0, H, n, d_v, W, R, eps=1e-6,
+                         gate_act=O.GATE_SIGMOID):
+    """Every head normalised with head 0's weight."""
+    x = np.asarray(x, F64)
+    B, T = x.shape[:2]
+    a = O.pass_a(x, w_proj, A, b_dt, H, n, d_v, W, R, gate_act)
+    out = np.zeros((B, T, H, d_v))
+    st = np.zeros(np.shape(state0))
+    for b in range(B):
+        for h in range(H):
+            walk = {k: a[k][b, :, h] for k in ("idx_w", "wt_w", "idx_r", "wt_r", "v", "g",
+                                               "alpha", "beta")}
+            o, _, M = O.forward_walk(state0[b][h], walk, np.asarray(gamma, F64)[0], eps)
+            out[b, :, h] = o
+            st[b, h] = M
+    return out, st, a
+
+
 MUTANTS = {
     "forget gate decays every slot": ("scan", _scan_variant(decay_all=True)),
     "read before write": ("scan", _scan_variant(read_first=True)),
@@ -94,6 +134,10 @@ MUTANTS = {
     "b_dt dropped": ("forget_gate", _forget_no_bias),
     "rms uses sum not mean": ("rms_norm_gate", _norm_sum),
     "input gate tanh": ("input_gate", _beta_tanh),
+    "write and read halves swapped": ("select_from_scores", _select_roles_swapped),
+    "a and b pre-gates swapped": ("pass_a", _pass_a_variant(swap_ab=True)),
+    "v and gate swapped": ("pass_a", _pass_a_variant(swap_vg=True)),
+    "every head normalised with head 0's weight": ("forward", _forward_head0_gamma),
 }
 
 PIN_CALLS = [
@@ -109,6 +153,8 @@ PIN_CALLS = [
     (pins.test_unselected_rows_bit_identical, {}),
     (pins.test_single_slot_closed_form_constant_gates, {}),
     (pins.test_norm_gate_scale_invariance_and_rms, {}),
+    (pins.test_golden_layer_wiring_pass_a, {}),
+    (pins.test_golden_layer_wiring_forward, {}),
 ]
 
 
@@ -116,6 +162,7 @@ PIN_CALLS = [
 def test_pins_catch_mutant(name, monkeypatch):
     attr, fn = MUTANTS[name]
     monkeypatch.setitem(O.__dict__, "_orig_split", O.split_heads)
+    monkeypatch.setitem(O.__dict__, "_orig_select_from_scores", O.select_from_scores)
     monkeypatch.setattr(O, attr, fn)
     failures = 0
     for call, kw in PIN_CALLS:

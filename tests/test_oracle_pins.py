@@ -416,3 +416,50 @@ def test_gate_ranges():
     assert np.all(O.forget_gate(a, 0.0, -2.0) == 1.0)
     be = O.input_gate(np.linspace(-20, 20, 41))
     assert np.all((be > 0) & (be < 1)) and np.all(np.diff(be) > 0)
+
+
+# --------------------------------------------------------------------------
+# Whole layer from x: a hand-worked fixture in which every column block, every
+# head's gates and every head's norm weight carries its own value, so that a
+# mix-up of write and read halves, of the a and b pre-gates, of v and the gate
+# vector, or of one head's norm weight for another's changes the expected output
+# --------------------------------------------------------------------------
+def _val(s):
+    """Value of a fixture entry: an integer or fraction, or +-ln3."""
+    s = s.strip()
+    if s.lstrip("-") == "ln3":
+        return -math.log(3.0) if s.startswith("-") else math.log(3.0)
+    return float(Fraction(s))
+
+
+def _vals(a):
+    return np.vectorize(_val, otypes=[float])(np.array(a, dtype=object))
+
+
+def _wiring():
+    g = _load("layer_wiring.json")
+    H, n, d_v = g["H"], g["n"], g["d_v"]
+    P = 4 * n + 2 * d_v + 2
+    x = _vals(g["x"]).reshape(1, len(g["x"]), H * P)     # [B=1, T, H*P]
+    return g, x, np.eye(H * P)
+
+
+def test_golden_layer_wiring_pass_a():
+    g, x, w = _wiring()
+    e = g["expected"]
+    a = O.pass_a(x, w, _vals(g["A"]), _vals(g["b_dt"]), g["H"], g["n"], g["d_v"], g["W"], g["R"])
+    assert a["idx_w"][0].tolist() == e["idx_w"]
+    assert a["idx_r"][0].tolist() == e["idx_r"]
+    assert np.all(a["wt_w"] == 1.0) and np.all(a["wt_r"] == 1.0)
+    for k, key in (("alpha", "alpha"), ("beta", "beta"), ("v", "v"), ("g", "gate")):
+        np.testing.assert_allclose(a[k][0], _vals(e[key]), rtol=1e-12, atol=1e-12, err_msg=k)
+
+
+def test_golden_layer_wiring_forward():
+    g, x, w = _wiring()
+    e = g["expected"]
+    out, st, _ = O.forward(x, w, _vals(g["A"]), _vals(g["b_dt"]), _vals(g["gamma"]),
+                           _vals(g["state0"])[None], g["H"], g["n"], g["d_v"], g["W"], g["R"],
+                           eps=_val(g["eps"]))
+    np.testing.assert_allclose(out[0], _vals(e["out"]), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(st[0], _vals(e["state_final"]), rtol=1e-12, atol=1e-12)
