@@ -52,7 +52,7 @@ extern "C" {
 #define SDM_API
 #endif
 
-#define SDM_ABI_VERSION 2
+#define SDM_ABI_VERSION 3
 
 /* status codes */
 #define SDM_OK 0
@@ -79,6 +79,7 @@ extern "C" {
 #define SDM_ENTRY_FORWARD 2
 #define SDM_ENTRY_SCAN_BACKWARD 3
 #define SDM_ENTRY_SCAN_TRAIN 4
+#define SDM_ENTRY_SELECT_FROM_SCORES 5
 
 /* scan schedule flags (sdm_dims.flags) */
 #define SDM_FLAG_SCAN_DIRECT 1    /* one workgroup per (b,h), tokens in lock-step */
@@ -217,11 +218,15 @@ SDM_API int32_t sdm_select(const sdm_dims* dims, const void* x, const void* w_pr
 
 /*
  * Selection from given half-scores (diagnostic entry, same ranking as sdm_select):
+ * [rainbus] step 1 (top-W / top-R of the outer sums, softmax weights).
  *   scores [B, T, H, 4n] fp32 -> idx_w/wt_w [B,T,H,W], idx_r/wt_r [B,T,H,R].
+ *   ws     >= sdm_workspace_bytes(dims, SDM_ENTRY_SELECT_FROM_SCORES) bytes (may be
+ *          NULL if 0; this build needs none: the ranking runs in registers and LDS)
  * Given identical scores, the ids are bit-identical to the fp64 brute-force top-W.
  */
 SDM_API int32_t sdm_select_from_scores(const sdm_dims* dims, const float* scores, int32_t* idx_w,
-                               float* wt_w, int32_t* idx_r, float* wt_r, void* stream);
+                                       float* wt_w, int32_t* idx_r, float* wt_r, void* ws,
+                                       size_t ws_bytes, void* stream);
 
 /*
  * Recurrent sparse scan: [rainbus] steps 2-4 without the head-mixing projection.

@@ -19,7 +19,7 @@ SDM_ERR_WORKSPACE, SDM_ERR_UNSUPPORTED, SDM_ERR_HIP = -5, -6, -7
 SDM_DTYPE_F32, SDM_DTYPE_BF16 = 0, 1
 SDM_GATE_NONE, SDM_GATE_SIGMOID, SDM_GATE_SILU = 0, 1, 2
 SDM_ENTRY_SELECT, SDM_ENTRY_SCAN, SDM_ENTRY_FORWARD, SDM_ENTRY_SCAN_BACKWARD = 0, 1, 2, 3
-SDM_ENTRY_SCAN_TRAIN = 4
+SDM_ENTRY_SCAN_TRAIN, SDM_ENTRY_SELECT_FROM_SCORES = 4, 5
 SDM_MAX_COUNT, SDM_MAX_HALF = 128, 1024
 SDM_FLAG_SCAN_DIRECT, SDM_FLAG_SCAN_STREAM, SDM_FLAG_SCAN_TWO_PHASE = 1, 2, 4
 SDM_FLAG_TIMING = 8
@@ -83,7 +83,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sdm_select.restype = I32
     lib.sdm_select.argtypes = [P(SdmDims), VP, VP, VP, VP, P(SdmSel), VP, ctypes.c_size_t, VP]
     lib.sdm_select_from_scores.restype = I32
-    lib.sdm_select_from_scores.argtypes = [P(SdmDims), VP, VP, VP, VP, VP, VP]
+    lib.sdm_select_from_scores.argtypes = [P(SdmDims), VP, VP, VP, VP, VP, VP, ctypes.c_size_t,
+                                           VP]
     lib.sdm_scan.restype = I32
     lib.sdm_scan.argtypes = [P(SdmDims), P(SdmSel), VP, VP, VP, VP, VP, ctypes.c_size_t, VP]
     lib.sdm_forward.restype = I32
@@ -157,9 +158,11 @@ def sdm_select(d: SdmDims, x, w_proj, A, b_dt, out: SdmSel, ws=None, ws_bytes=0,
                              ctypes.byref(out), _ptr(ws), ws_bytes, _stream(stream)))
 
 
-def sdm_select_from_scores(d: SdmDims, scores, idx_w, wt_w, idx_r, wt_r, stream=None):
+def sdm_select_from_scores(d: SdmDims, scores, idx_w, wt_w, idx_r, wt_r, ws=None, ws_bytes=0,
+                           stream=None):
     _check(load().sdm_select_from_scores(ctypes.byref(d), _ptr(scores), _ptr(idx_w), _ptr(wt_w),
-                                         _ptr(idx_r), _ptr(wt_r), _stream(stream)))
+                                         _ptr(idx_r), _ptr(wt_r), _ptr(ws), ws_bytes,
+                                         _stream(stream)))
 
 
 def sdm_scan(d: SdmDims, inp: SdmSel, norm_w, state, out, y_raw=None, ws=None, ws_bytes=0,

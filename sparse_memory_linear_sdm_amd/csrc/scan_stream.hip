@@ -1073,8 +1073,11 @@ hipError_t launch_stream_scan(const ScanArgs& sa, const StreamPlan& pl, void* ws
                           : reinterpret_cast<const void*>(bucket_scatter_rev_kernel<1, 8, false>))
                  : (train ? reinterpret_cast<const void*>(bucket_scatter_rev_kernel<2, 4, true>)
                           : reinterpret_cast<const void*>(bucket_scatter_rev_kernel<2, 4, false>));
-      if (lds > 65536)  // slot bitmaps beyond 64 KiB (N > ~500k) need the larger LDS limit
-        (void)hipFuncSetAttribute(rev, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (lds > 65536) {  // slot bitmaps beyond 64 KiB (N > ~500k) need the larger LDS limit
+        const hipError_t e = hipFuncSetAttribute(rev, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)lds);
+        if (e != hipSuccess) return e;
+      }
       const dim3 rg((unsigned)(walks * a.rounds));
       {
         KernelTimer kt("bucket_scatter_rev", st);
@@ -1086,6 +1089,10 @@ hipError_t launch_stream_scan(const ScanArgs& sa, const StreamPlan& pl, void* ws
           hipLaunchKernelGGL((bucket_scatter_rev_kernel<2, 4, true>), rg, dim3(64), lds, st, a);
         else
           hipLaunchKernelGGL((bucket_scatter_rev_kernel<2, 4, false>), rg, dim3(64), lds, st, a);
+      }
+      {  // the walk takes its loop bounds from the bucketing outputs: launch it only on them
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
       }
       const dim3 grid((unsigned)(walks * pl.S * pl.parts));
       KernelTimer kt("two_phase_scan", st);
@@ -1125,6 +1132,10 @@ hipError_t launch_stream_scan(const ScanArgs& sa, const StreamPlan& pl, void* ws
         else
           hipLaunchKernelGGL(bucket_scatter_kernel<false>, dim3((unsigned)(walks * a.rounds)),
                              dim3(64), 0, st, a);
+      }
+      {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
       }
       const dim3 grid((unsigned)(walks * pl.S * pl.parts));
       KernelTimer kt("stream_scan", st);

@@ -620,6 +620,7 @@ hipError_t launch_stream_backward(const sdm_dims& d, const ScanBackArgs& sa, flo
         default: return hipErrorInvalidValue;
       }
     }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     {
       const dim3 grid((unsigned)(walks * pl.S * pl.parts));
       KernelTimer kt("stream_backward", st);

@@ -321,6 +321,7 @@ size_t sdm_workspace_bytes(const sdm_dims* d, int32_t entry) {
       return product_sizes(d, dv.M).total + select_ws_bytes(d, dv, false) +
              align_up(scan_workspace_bytes(*d));
     case SDM_ENTRY_SCAN_BACKWARD: return backward_ws_bytes(d);
+    case SDM_ENTRY_SELECT_FROM_SCORES: return 0;
     case SDM_ENTRY_SCAN_TRAIN: {
       const sdm_dims dd = train_dims(d);
       return align_up(scan_workspace_bytes(dd, true));
@@ -349,15 +350,17 @@ int32_t sdm_select(const sdm_dims* d, const void* x, const void* w_proj, const f
 }
 
 int32_t sdm_select_from_scores(const sdm_dims* d, const float* scores, int32_t* idx_w,
-                               float* wt_w, int32_t* idx_r, float* wt_r, void* stream) {
+                               float* wt_w, int32_t* idx_r, float* wt_r, void* ws,
+                               size_t ws_bytes, void* stream) {
   Derived dv;
   int32_t st = check_dims(d, &dv);
   if (st != SDM_OK) return st;
   if (dv.M == 0) return SDM_OK;
   if (!scores || !idx_w || !wt_w || !idx_r || !wt_r) return SDM_ERR_NULL;
   if (!aligned16(scores) || !aligned16(idx_w) || !aligned16(wt_w) || !aligned16(idx_r) ||
-      !aligned16(wt_r))
+      !aligned16(wt_r) || (ws && !aligned16(ws)))
     return SDM_ERR_ALIGN;
+  (void)ws_bytes;  // the ranking needs no workspace (sdm_workspace_bytes returns 0)
   TimingScope timing(d);
   (void)hipGetLastError();
   return hip_status(

@@ -6,12 +6,33 @@ same name in libsdm.so.  Nothing here computes any part of the method.
 """
 from __future__ import annotations
 
+import contextlib
+import functools
+
 import torch
 
 from . import _lib
 from ._lib import SdmDims
 
 PRODUCT_FIELDS = ("idx_w", "wt_w", "idx_r", "wt_r", "v", "gate", "alpha", "beta")
+
+
+def _stream_ctx(stream):
+    if stream is None:
+        return contextlib.nullcontext()
+    s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(stream)
+    return torch.cuda.stream(s)
+
+
+def _on_stream(fn):
+    """Run the call with `stream` (when given) as torch's current stream, so that every
+    tensor it allocates (outputs, workspace) belongs to the stream its kernels run on:
+    the caching allocator then reuses that memory only after the stream's work."""
+    @functools.wraps(fn)
+    def call(*args, stream=None, **kw):
+        with _stream_ctx(stream):
+            return fn(*args, stream=stream, **kw)
+    return call
 
 
 def _need(t, dtype, shape, name):
@@ -71,6 +92,7 @@ def _workspace(d: SdmDims, entry: int, device, ws=None):
     return ws, ws.numel() * ws.element_size()
 
 
+@_on_stream
 def select(d: SdmDims, x, w_proj, A, b_dt, with_scores=False, out=None, ws=None, stream=None):
     _check_params(d, x, w_proj, A, b_dt)
     p = out if out is not None else alloc_products(d, x.device, with_scores)
@@ -80,10 +102,13 @@ def select(d: SdmDims, x, w_proj, A, b_dt, with_scores=False, out=None, ws=None,
     return p
 
 
+@_on_stream
 def select_from_scores(d: SdmDims, scores, stream=None):
     _need(scores, torch.float32, (d.B, d.T, d.H, 4 * d.n), "scores")
     p = alloc_products(d, scores.device)
-    _lib.sdm_select_from_scores(d, scores, p["idx_w"], p["wt_w"], p["idx_r"], p["wt_r"], stream)
+    ws, nb = _workspace(d, _lib.SDM_ENTRY_SELECT_FROM_SCORES, scores.device)
+    _lib.sdm_select_from_scores(d, scores, p["idx_w"], p["wt_w"], p["idx_r"], p["wt_r"], ws, nb,
+                                stream)
     return {k: p[k] for k in ("idx_w", "wt_w", "idx_r", "wt_r")}
 
 
@@ -91,6 +116,7 @@ def state_dtype(d: SdmDims):
     return torch.bfloat16 if d.flags & _lib.SDM_FLAG_STATE_BF16 else torch.float32
 
 
+@_on_stream
 def scan(d: SdmDims, products: dict, norm_w, state, with_y_raw=False, out=None, ws=None,
          stream=None):
     _check_products(d, products)
@@ -107,6 +133,7 @@ def scan(d: SdmDims, products: dict, norm_w, state, with_y_raw=False, out=None, 
     return (o, y) if with_y_raw else o
 
 
+@_on_stream
 def forward(d: SdmDims, x, w_proj, A, b_dt, norm_w, state, debug=False, with_scores=False,
             out=None, ws=None, stream=None):
     """Whole path; state is updated in place.  Returns out (and the products if debug)."""
@@ -130,6 +157,7 @@ def log_format(d: SdmDims) -> str:
     return "int4" if d.flags & _lib.SDM_FLAG_LOG_INT4 else "fp32"
 
 
+@_on_stream
 def scan_train(d: SdmDims, products: dict, norm_w, state, out=None, ws=None, stream=None):
     """Training forward: scan() that also records the write log.  Returns
     (out, y_raw, log) with log a dict: "rows" ([B, T, H, W, d_v] fp32, or uint8 codes
@@ -157,6 +185,7 @@ def scan_train(d: SdmDims, products: dict, norm_w, state, out=None, ws=None, str
     return o, y, log
 
 
+@_on_stream
 def scan_backward(d: SdmDims, products: dict, norm_w, state, d_state, y_raw, log, d_out,
                   with_d_norm_w=True, ws=None, stream=None):
     """Gradients of scan_train's call.  state (M_T -> M_0) and d_state (dL/dM_T ->
@@ -200,6 +229,7 @@ def _check_shared(d: SdmDims, m0, state, touched):
     _need(touched, torch.int32, (d.B, d.H, (N + 31) // 32), "touched")
 
 
+@_on_stream
 def scan_shared_m0(d: SdmDims, products: dict, norm_w, m0, state, touched, with_y_raw=False,
                    out=None, ws=None, stream=None):
     """scan() on the effective state (store rows whose touched bit is set, else m0)."""
@@ -215,6 +245,7 @@ def scan_shared_m0(d: SdmDims, products: dict, norm_w, m0, state, touched, with_
     return (o, y) if with_y_raw else o
 
 
+@_on_stream
 def forward_shared_m0(d: SdmDims, x, w_proj, A, b_dt, norm_w, m0, state, touched, out=None,
                       ws=None, stream=None):
     """forward() on the effective state; state and touched are updated in place."""
@@ -230,6 +261,7 @@ def forward_shared_m0(d: SdmDims, x, w_proj, A, b_dt, norm_w, m0, state, touched
     return o
 
 
+@_on_stream
 def slot_histogram(d: SdmDims, idx_w, counts=None, stream=None):
     """Per-head slot-update counts [H, N] int32; accumulates into `counts` if given."""
     _need(idx_w, torch.int32, (d.B, d.T, d.H, d.W), "idx_w")

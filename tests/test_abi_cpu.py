@@ -43,7 +43,7 @@ def test_header_constants_match_binding():
 
 
 def test_version_and_status_strings(lib):
-    assert _lib.abi_version() == 2
+    assert _lib.abi_version() == 3
     for code in (0, -1, -2, -3, -4, -5, -6, -7, 12345):
         assert isinstance(_lib.status_string(code), str) and _lib.status_string(code)
     assert _lib.status_string(-5) == "workspace missing or too small"
@@ -84,13 +84,24 @@ def _select(lib, d, x=FAKE, w=FAKE, A=FAKE, b=FAKE, sel=None, ws=FAKE, nb=1 << 4
 def test_bad_dims_rejected_by_every_entry(lib, kw, code):
     d = _d(**kw)
     assert _select(lib, d) == code
-    assert lib.sdm_select_from_scores(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None) == code
+    assert lib.sdm_select_from_scores(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, 0,
+                                      None) == code
     s = _sel()
     assert lib.sdm_scan(ctypes.byref(d), ctypes.byref(s), None, FAKE, FAKE, None, FAKE, 1 << 40,
                         None) == code
     assert lib.sdm_forward(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, FAKE,
                            1 << 40, None) == code
     assert lib.sdm_workspace_bytes(ctypes.byref(d), 2) == 0
+
+
+def test_select_from_scores_needs_no_workspace(lib):
+    d = _d()
+    assert lib.sdm_workspace_bytes(ctypes.byref(d), _lib.SDM_ENTRY_SELECT_FROM_SCORES) == 0
+    # a workspace may still be passed; a misaligned one is rejected before any launch
+    assert lib.sdm_select_from_scores(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 4, 64,
+                                      None) == _lib.SDM_ERR_ALIGN
+    assert lib.sdm_select_from_scores(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, None, 0,
+                                      None) == _lib.SDM_ERR_NULL
 
 
 def test_timing_flag_is_accepted_and_read_is_safe_without_records(lib):
