@@ -9,6 +9,10 @@ input already resident in HBM.  Prints one JSON line with tokens/s, the
 roofline of the dominant kernel (the scan, HBM-bound) and a CPU baseline (the
 fp64 oracle timed on a bounded sample of the same workload on the host).
 
+--decode-steps (decode workload) times the decode configuration as defined: each
+step is one T=1 sdm_forward of all 256 sequences, the 64 steps captured in one HIP
+graph and replayed; it reports microseconds per step and slot-row GB/s.
+
 --mode train times the training path instead: a step is the selection pass, the
 training forward of the scan (with the fp32 write log) and the scan backward
 (random incoming gradients of out and of the final state), which leaves the state
@@ -28,6 +32,8 @@ sys.path.insert(0, ROOT)
 import numpy as np  # noqa: E402
 
 METRIC = "SDM layer tokens/s at N=131072,W=R=64,d_v=128; effective HBM GB/s vs peak"
+METRIC_DECODE = ("SDM decode tokens/s (256 sequences, one token per step, N=65536, W=R=64, "
+                 "d_v=128; graph-replayed steps); slot-row HBM GB/s vs peak")
 METRIC_TRAIN = ("SDM layer training tokens/s (selection, scan forward with write log, scan "
                 "backward); reverse-walk HBM GB/s vs peak")
 HBM_PEAK_GBS = 8000.0
@@ -86,33 +92,88 @@ def parse():
                         "arithmetic (SDM_FLAG_STATE_BF16)")
     p.add_argument("--mode", choices=("forward", "train"), default="forward")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-tokens", type=int, default=2048,
-                   help="tokens of batch entry 0 in the oracle's timed sample")
+    p.add_argument("--cpu-tokens-per-core", type=int, default=2048,
+                   help="tokens of batch entry 0 per host core in the oracle's timed sample")
+    p.add_argument("--decode-steps", action="store_true",
+                   help="decode workload as defined: every step one T=1 sdm_forward of all "
+                        "sequences, the steps captured in one HIP graph and replayed")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="after the timed steps, copy MIB MiB device-to-device (the reference "
                         "kernel of known traffic for scaling hardware byte counters)")
     return p.parse_args()
 
 
-def cpu_baseline(wl, ntok: int) -> dict:
-    """The fp64 oracle, as it stands, on the first `ntok` tokens of batch entry 0."""
+# ---- CPU baseline: the fp64 oracle as it stands, spread over the host's cores ----------
+# Worker processes (one BLAS thread each) regenerate the seeded inputs they need.  The
+# selection pass runs the oracle's pass_a on token blocks; the scan runs the oracle's
+# forward_walk, one (batch, head) walk per process.  Nothing of the oracle is changed.
+_CPU = {}
+
+
+def _cpu_init(name: str, with_m0: bool):
     from threadpoolctl import threadpool_limits
 
+    from sparse_memory_linear_sdm_amd import synth
+    threadpool_limits(limits=1)
+    wl = synth.WORKLOADS[name]
+    _CPU.update(wl=wl, prm=synth.gen_params(wl, seed=0))
+    if with_m0:
+        _CPU["m0"] = synth.gen_m0(wl, seed=0)
+
+
+def _cpu_pass_a(block):
     from oracle import sdm_oracle as O
     from sparse_memory_linear_sdm_amd import synth
+    wl, prm = _CPU["wl"], _CPU["prm"]
+    b, t0, t1 = block
+    x, _ = synth.gen_x(wl, seed=0, t0=t0, t1=t1, batches=[b])
+    a = O.pass_a(x[0], prm["w_proj"], prm["A"], prm["b_dt"], wl.H, wl.n, wl.d_v, wl.W, wl.R)
+    return {k: a[k] for k in ("idx_w", "wt_w", "idx_r", "wt_r", "v", "g", "alpha", "beta")}
 
-    x, _ = synth.gen_x(wl, seed=0, t0=0, t1=ntok, batches=[0])
-    prm = synth.gen_params(wl, seed=0)
-    m0 = synth.gen_m0(wl, seed=0)[None]
-    with threadpool_limits(limits=1):
+
+def _cpu_walk(job):
+    from oracle import sdm_oracle as O
+    wl, prm = _CPU["wl"], _CPU["prm"]
+    h, sel = job
+    out, _, _ = O.forward_walk(_CPU["m0"][h], sel, prm["gamma"][h], wl.eps)
+    return out.shape[0]
+
+
+def cpu_baseline(wl, tokens_per_core: int) -> dict:
+    """The fp64 oracle on the first tokens of the batch (whole sequences from entry 0 on,
+    all heads, from x) over min(affinity, 16) processes: the selection by token blocks,
+    then one process per (batch entry, head) walk."""
+    import multiprocessing as mp
+
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    ntok = min(wl.tokens, tokens_per_core * cores)
+    nb = (ntok + wl.T - 1) // wl.T
+    blocks = []
+    per = max(1, -(-ntok // cores))
+    for b in range(nb):
+        tb = min(wl.T, ntok - b * wl.T)
+        blocks += [(b, t, min(t + per, tb)) for t in range(0, tb, per)]
+    ctx = mp.get_context("spawn")   # fresh interpreters: nothing of the GPU process is inherited
+    with ctx.Pool(cores, initializer=_cpu_init, initargs=(wl.name, True)) as pool:
+        pool.map(abs, range(cores))  # every worker started and initialised before timing
         t0 = time.perf_counter()
-        O.forward(x, prm["w_proj"], prm["A"], prm["b_dt"], prm["gamma"], m0, wl.H, wl.n, wl.d_v,
-                  wl.W, wl.R, wl.eps)
-        dt = time.perf_counter() - t0
-    return {"value": ntok / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{wl.name}: tokens 0..{ntok - 1} of batch entry 0, all {wl.H} heads, "
-                      f"from x (fp64 projection, brute-force top-{wl.W}/{wl.R} over "
-                      f"N={wl.N}, sequential scan, norm+gate); {dt:.1f} s on 1 host thread"}
+        parts = pool.map(_cpu_pass_a, blocks)
+        t1 = time.perf_counter()
+        jobs = []
+        for b in range(nb):
+            mine = [p for blk, p in zip(blocks, parts) if blk[0] == b]
+            sel = {k: np.concatenate([p[k] for p in mine]) for k in mine[0]}
+            jobs += [(h, {k: v[:, h] for k, v in sel.items()}) for h in range(wl.H)]
+        pool.map(_cpu_walk, jobs)
+        t2 = time.perf_counter()
+    dt = t2 - t0
+    return {"value": ntok / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{wl.name}: the first {ntok} tokens ({nb} batch entr"
+                      f"{'y' if nb == 1 else 'ies'} from entry 0), all {wl.H} heads, from x "
+                      f"(fp64 projection, brute-force top-{wl.W}/{wl.R} over N={wl.N}, "
+                      f"sequential scan, norm+gate); {dt:.1f} s on {cores} processes "
+                      f"(selection over {len(blocks)} token blocks {t1 - t0:.1f} s, then "
+                      f"{len(jobs)} walks {t2 - t1:.1f} s), one BLAS thread each"}
 
 
 def copy_calibration(mib: int, dev, res: dict) -> None:
@@ -156,6 +217,8 @@ def main():
 
     if args.mode == "train":
         return train_main(args)
+    if args.decode_steps:
+        return decode_main(args)
     wl = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -262,8 +325,115 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, dev, res)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_tokens)
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_tokens_per_core)
     print(json.dumps(res), flush=True)
+
+
+def decode_main(args):
+    """The decode workload as defined: each step is one sdm_forward with T = 1 for all
+    B sequences, continuing their states.  The wl.T steps (each with its own input
+    token) are captured in one HIP graph; a timed repetition replays the graph."""
+    import torch
+
+    from sparse_memory_linear_sdm_amd import _lib, dims_for, ops, synth
+
+    wl = synth.WORKLOADS[args.workload]
+    if args.state != "fp32":
+        print("--decode-steps keeps fp32 state", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d1 = dims_for(wl, T=1)
+    _, x_store = synth.gen_x(wl, seed=0)
+    prm = synth.gen_params(wl, seed=0)
+    m0 = synth.gen_m0(wl, seed=0)
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    # per-step inputs [steps, B, 1, d_model], each step's slice contiguous
+    xs = to_dev(x_store).transpose(0, 1).contiguous().unsqueeze(2)
+    w = to_dev(prm["w_proj_store"])
+    A, b_dt, gamma = to_dev(prm["A"]), to_dev(prm["b_dt"]), to_dev(prm["gamma"])
+    m0_d = to_dev(m0)
+    del m0
+    state = m0_d.unsqueeze(0).repeat(wl.B, *([1] * m0_d.dim()))
+    outs = torch.empty((wl.T, wl.B, 1, wl.H, wl.d_v), device=dev)
+    ws = torch.empty(max(_lib.workspace_bytes(d1, _lib.SDM_ENTRY_FORWARD), 1), dtype=torch.uint8,
+                     device=dev)
+
+    def steps(stream):
+        for t in range(wl.T):
+            ops.forward(d1, xs[t], w, A, b_dt, gamma, state, out=outs[t], ws=ws, stream=stream)
+
+    # eager pass with kernel timing (HIP events around every launch on the stream)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    _lib.timing_read()
+    d1.flags |= _lib.SDM_FLAG_TIMING
+    with torch.cuda.stream(side):
+        steps(side)
+    torch.cuda.synchronize()
+    d1.flags &= ~_lib.SDM_FLAG_TIMING
+    per_kernel = {}
+    for name, ms in _lib.timing_read(1 << 16):
+        per_kernel.setdefault(name, []).append(ms)
+    kernels_ms = {k: {"avg": float(np.mean(v)), "launches": len(v)} for k, v in per_kernel.items()}
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        steps(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    n_steps = args.steps * wl.T
+    us_step = wall * 1e6 / n_steps
+    step_bytes = wl.B * wl.H * wl.slot_bytes_per_token_head(4)
+    scan_kernel = next(k for k in ("scan_direct", "two_phase_scan", "stream_scan") if k in kernels_ms)
+    scan_ms = kernels_ms[scan_kernel]["avg"] * kernels_ms[scan_kernel]["launches"] / wl.T
+    achieved = step_bytes / (scan_ms * 1e-3) / 1e9
+    gemm_kernel = next((k for k in ("proj_gemm_bf16", "proj_gemm_f32") if k in kernels_ms), None)
+    res = {
+        "metric": METRIC_DECODE,
+        "value": wl.B / (us_step * 1e-6),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": n_steps,
+        "warmup": args.warmup * wl.T,
+        "ms_per_step": us_step * 1e-3,
+        "us_per_step": us_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 projection, fp32 selection/scan",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "T": 1, "decode_steps": wl.T,
+                   "d_model": wl.d_model, "H": wl.H, "N": wl.N, "n": wl.n, "W": wl.W, "R": wl.R,
+                   "d_v": wl.d_v, "state": "fp32 [B,H,N,d_v]", "tokens_per_step": wl.B,
+                   "replays": args.steps, "steps_per_replay": wl.T},
+        "effective_hbm_gbs_step": step_bytes / (us_step * 1e-6) / 1e9,
+        "step_frac_of_peak": step_bytes / (us_step * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "kernels_ms_eager": kernels_ms,
+        "gemm": gemm_line(dataclass_replace(wl, T=1), kernels_ms, gemm_kernel, wl.T),
+        "roofline": {"bound": "hbm", "kernel": scan_kernel, "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None, "algorithmic_bytes_per_launch": step_bytes},
+    }
+    print(json.dumps(res), flush=True)
+
+
+def dataclass_replace(wl, **kw):
+    import dataclasses
+    return dataclasses.replace(wl, **kw)
 
 
 def train_main(args):
