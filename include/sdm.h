@@ -262,6 +262,32 @@ SDM_API int32_t sdm_forward(const sdm_dims* dims, const void* x, const void* w_p
                     const sdm_sel* debug, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * sdm_forward without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops (a decode step), harnesses
+ * that forbid allocation.  The workspace is one fixed array of
+ * SDM_NOALLOC_SCRATCH_BYTES per GPU, part of the library's device code (each GPU the
+ * library runs on holds it until the process ends).  The call allocates nothing and
+ * frees nothing.  Arguments and results as in sdm_forward (no `debug` products).
+ *  - Sizes whose sdm_workspace_bytes(dims, SDM_ENTRY_FORWARD) exceed
+ *    SDM_NOALLOC_SCRATCH_BYTES: SDM_ERR_WORKSPACE, nothing enqueued.  (The decode
+ *    workload's step, 256 sequences x 1 token, N = 65536, W = R = 64, d_v = 128,
+ *    needs about 6 MiB.)
+ *  - SDM_FLAG_TIMING is not accepted here (SDM_ERR_UNSUPPORTED): its record creates
+ *    HIP events.
+ *  - Every call on one GPU uses that GPU's single array: calls that overlap in time
+ *    on one GPU (two streams, two threads) race and give undefined results.  Calls
+ *    ordered on one stream are fine; the array's contents between calls do not
+ *    matter.
+ *  - The first call on each device looks up the array's device address
+ *    (hipGetSymbolAddress, with that device current); make that first call outside
+ *    graph capture.  SDM_ERR_HIP if the lookup fails.
+ */
+#define SDM_NOALLOC_SCRATCH_BYTES 67108864 /* 64 MiB */
+SDM_API int32_t sdm_forward_noalloc(const sdm_dims* dims, const void* x, const void* w_proj,
+                                    const float* A, const float* b_dt, const float* norm_w,
+                                    void* state, float* out, void* stream);
+
+/*
  * Training (the m.163.com article on arXiv 2607.07386, section 八, memory-efficiency
  * paragraph: the sparse update is applied in place and undone in backward, keeping
  * the N x d state plus the T x W x d rows the writes overwrote).

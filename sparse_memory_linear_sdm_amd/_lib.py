@@ -21,6 +21,7 @@ SDM_GATE_NONE, SDM_GATE_SIGMOID, SDM_GATE_SILU = 0, 1, 2
 SDM_ENTRY_SELECT, SDM_ENTRY_SCAN, SDM_ENTRY_FORWARD, SDM_ENTRY_SCAN_BACKWARD = 0, 1, 2, 3
 SDM_ENTRY_SCAN_TRAIN, SDM_ENTRY_SELECT_FROM_SCORES = 4, 5
 SDM_MAX_COUNT, SDM_MAX_HALF = 128, 1024
+SDM_NOALLOC_SCRATCH_BYTES = 64 << 20
 SDM_FLAG_SCAN_DIRECT, SDM_FLAG_SCAN_STREAM, SDM_FLAG_SCAN_TWO_PHASE = 1, 2, 4
 SDM_FLAG_TIMING = 8
 SDM_FLAG_DELTA_GDN = 16
@@ -30,7 +31,7 @@ SDM_FLAG_LOG_FP8, SDM_FLAG_LOG_INT4 = 64, 128
 EXPORTS = ("sdm_abi_version", "sdm_status_string", "sdm_workspace_bytes", "sdm_select",
            "sdm_select_from_scores", "sdm_scan", "sdm_forward", "sdm_scan_shared_m0",
            "sdm_forward_shared_m0", "sdm_scan_train", "sdm_scan_backward",
-           "sdm_slot_histogram", "sdm_timing_read")
+           "sdm_slot_histogram", "sdm_timing_read", "sdm_forward_noalloc")
 
 
 class SdmDims(ctypes.Structure):
@@ -104,6 +105,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sdm_scan_backward.restype = I32
     lib.sdm_scan_backward.argtypes = [P(SdmDims), P(SdmSel), VP, VP, VP, VP, VP, VP, VP,
                                       P(SdmScanGrads), VP, ctypes.c_size_t, VP]
+    lib.sdm_forward_noalloc.restype = I32
+    lib.sdm_forward_noalloc.argtypes = [P(SdmDims), VP, VP, VP, VP, VP, VP, VP, VP]
     lib.sdm_slot_histogram.restype = I32
     lib.sdm_slot_histogram.argtypes = [P(SdmDims), VP, VP, VP]
     del I64
@@ -177,6 +180,11 @@ def sdm_forward(d: SdmDims, x, w_proj, A, b_dt, norm_w, state, out, debug: SdmSe
                               _ptr(norm_w), _ptr(state), _ptr(out),
                               ctypes.byref(debug) if debug is not None else None, _ptr(ws),
                               ws_bytes, _stream(stream)))
+
+
+def sdm_forward_noalloc(d: SdmDims, x, w_proj, A, b_dt, norm_w, state, out, stream=None):
+    _check(load().sdm_forward_noalloc(ctypes.byref(d), _ptr(x), _ptr(w_proj), _ptr(A), _ptr(b_dt),
+                                      _ptr(norm_w), _ptr(state), _ptr(out), _stream(stream)))
 
 
 def sdm_scan_shared_m0(d: SdmDims, inp: SdmSel, norm_w, m0, state, touched, out, y_raw=None,

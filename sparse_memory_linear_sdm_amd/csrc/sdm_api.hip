@@ -4,6 +4,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "sdm_internal.h"
 
 using namespace sdm;
@@ -263,6 +266,35 @@ int32_t forward_entry(const sdm_dims* d, const void* x, const void* w_proj, cons
   return run_scan(d, dv, &prod, norm_w, state, out, nullptr, scan_space, scan_ws, s);
 }
 
+// ---------------------------------------------------------------------------
+// Workspace of sdm_forward_noalloc: one fixed array per GPU in the code object's
+// device memory, so that the entry point needs no allocation.  Host code must not
+// pass the array's name to a kernel (on the host it is a stand-in, not a device
+// address): the address comes from hipGetSymbolAddress, taken once per device with
+// that device current and kept in `g_scratch_ptr`.
+// ---------------------------------------------------------------------------
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[SDM_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's array (resolved on the first call there),
+// or nullptr if the device cannot be queried.
+void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -496,6 +528,27 @@ int32_t sdm_forward_shared_m0(const sdm_dims* d, const void* x, const void* w_pr
                               void* ws, size_t ws_bytes, void* stream) {
   return forward_entry(d, x, w_proj, A, b_dt, norm_w, m0, state, touched, out, nullptr, ws,
                        ws_bytes, stream, true);
+}
+
+int32_t sdm_forward_noalloc(const sdm_dims* d, const void* x, const void* w_proj,
+                            const float* A, const float* b_dt, const float* norm_w, void* state,
+                            float* out, void* stream) {
+  Derived dv;
+  int32_t st = check_dims(d, &dv);
+  if (st != SDM_OK) return st;
+  // the timing record creates HIP events on first use: not part of this entry
+  if (d->flags & SDM_FLAG_TIMING) return SDM_ERR_UNSUPPORTED;
+  if (dv.M == 0) return SDM_OK;
+  if (!x || !w_proj || !A || !b_dt || !state || !out) return SDM_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w_proj) || !aligned16(A) || !aligned16(b_dt) ||
+      !aligned16(state) || !aligned16(out) || (norm_w && !aligned16(norm_w)))
+    return SDM_ERR_ALIGN;
+  const size_t need = sdm_workspace_bytes(d, SDM_ENTRY_FORWARD);
+  if (need > (size_t)SDM_NOALLOC_SCRATCH_BYTES) return SDM_ERR_WORKSPACE;
+  void* ws = scratch_address();  // validated arguments only: the first call resolves it
+  if (!ws) return SDM_ERR_HIP;
+  return forward_entry(d, x, w_proj, A, b_dt, norm_w, nullptr, state, nullptr, out, nullptr, ws,
+                       (size_t)SDM_NOALLOC_SCRATCH_BYTES, stream, false);
 }
 
 }  // extern "C"

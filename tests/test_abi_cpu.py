@@ -262,3 +262,22 @@ def test_workspace_sizes_of_the_workloads(lib):
         assert fwd >= wl.tokens * wl.H * per_th, name
         sel = lib.sdm_workspace_bytes(ctypes.byref(d), _lib.SDM_ENTRY_SELECT)
         assert 0 < sel <= (1 << 30) + 256 or sel == wl.tokens * wl.H * 16 * wl.n, name
+
+
+def test_noalloc_forward_validates_before_touching_the_device(lib):
+    fwd = lambda d, x=FAKE: lib.sdm_forward_noalloc(ctypes.byref(d), x, FAKE, FAKE, FAKE, None,
+                                                    FAKE, FAKE, None)
+    assert fwd(_d(H=0)) == _lib.SDM_ERR_SHAPE
+    assert fwd(_d(flags=_lib.SDM_FLAG_TIMING)) == _lib.SDM_ERR_UNSUPPORTED
+    assert fwd(_d(), x=None) == _lib.SDM_ERR_NULL
+    assert fwd(_d(), x=FAKE + 8) == _lib.SDM_ERR_ALIGN
+    assert fwd(_d(B=0)) == _lib.SDM_OK                      # empty call: nothing enqueued
+    # sizes whose forward workspace exceeds the fixed array are refused
+    big = _d(B=8, T=4096, d_model=2048, H=4, n=362, W=64, R=64, d_v=128)
+    assert lib.sdm_workspace_bytes(ctypes.byref(big), _lib.SDM_ENTRY_FORWARD) > \
+        _lib.SDM_NOALLOC_SCRATCH_BYTES
+    assert fwd(big) == _lib.SDM_ERR_WORKSPACE
+    # the decode step (256 sequences x 1 token, N = 65536) fits
+    dec = _d(B=256, T=1, d_model=2048, H=4, n=256, W=64, R=64, d_v=128)
+    assert lib.sdm_workspace_bytes(ctypes.byref(dec), _lib.SDM_ENTRY_FORWARD) <= \
+        _lib.SDM_NOALLOC_SCRATCH_BYTES
