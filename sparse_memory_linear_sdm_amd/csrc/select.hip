@@ -181,16 +181,19 @@ __device__ __forceinline__ bool better(uint64_t ka, uint32_t ia, uint64_t kb, ui
 }
 
 // Choose exactly `need` of the valid elements (bit q of `valid`, KPL per lane): the best
-// under `better` on (key, id).  fv[q] is a float that never decreases along that order;
-// it is only used to bin.  Each round bins the remaining candidates into 256 equal-width
+// under `better` on (key, id), where key(q) gives element q's 64-bit key (evaluated only
+// for the few elements that reach the exact ranking).  fv[q] is a float that never
+// decreases along that order; it is only used to bin.  Each round bins the remaining candidates into 256 equal-width
 // bins over their [min, max]; the bins above the one holding the need-th best are taken,
 // the bins below are dropped, and the rest continue.  Whatever remains after three rounds
 // (or once few are left) is ranked exactly.  Binning is monotone, so the result is exact.
 // hist: 256 words of LDS; tk/ti: LDS room for 64*KPL (key, id) pairs.
-template <int KPL>
-__device__ uint32_t select_exact(const float (&fv)[KPL], const uint64_t (&key)[KPL],
-                                 const uint32_t (&id)[KPL], uint32_t valid, int need,
-                                 uint32_t* hist, uint64_t* tk, uint32_t* ti) {
+template <int KPL, class KeyF>
+__device__ __attribute__((always_inline)) uint32_t select_exact(const float (&fv)[KPL], KeyF key,
+                                                                const uint32_t (&id)[KPL],
+                                                                uint32_t valid, int need,
+                                                                uint32_t* hist, uint64_t* tk,
+                                                                uint32_t* ti) {
   const int lane = lane_id();
   uint32_t sel = 0, cand = valid;
   for (int round = 0; round < 3; ++round) {
@@ -262,7 +265,7 @@ __device__ uint32_t select_exact(const float (&fv)[KPL], const uint64_t (&key)[K
 #pragma unroll
   for (int q = 0; q < KPL; ++q)
     if ((cand >> q) & 1u) {
-      tk[pos] = key[q];
+      tk[pos] = key(q);
       ti[pos] = id[q];
       ++pos;
     }
@@ -294,9 +297,11 @@ __device__ uint32_t select_exact(const float (&fv)[KPL], const uint64_t (&key)[K
 }
 
 // Bitonic sort of NE = 64*EPL unsigned keys (element e = lane + 64*r in v[r]) so
-// that larger keys come first.
+// that larger keys come first.  Keys are distinct except for equal padding keys, so
+// each exchange takes the partner's key exactly when it is larger and this position
+// keeps the larger of the pair, or smaller and this position keeps the smaller.
 template <int EPL, class K>
-__device__ void bitonic_desc(K (&v)[EPL]) {
+__device__ __attribute__((always_inline)) void bitonic_desc(K (&v)[EPL]) {
   const int lane = lane_id();
   constexpr int NE = 64 * EPL;
 #pragma unroll
@@ -311,7 +316,7 @@ __device__ void bitonic_desc(K (&v)[EPL]) {
           if (pr > r) {
             const bool desc = (e & size) == 0;
             const K lo = v[r], hi = v[pr];
-            const bool sw = desc ? (hi > lo) : (lo > hi);
+            const bool sw = (hi > lo) == desc;
             v[r] = sw ? hi : lo;
             v[pr] = sw ? lo : hi;
           }
@@ -325,7 +330,7 @@ __device__ void bitonic_desc(K (&v)[EPL]) {
           const bool lower = (e & stride) == 0;
           // in a descending run the lower position keeps the larger key
           const bool keep_max = (desc == lower);
-          v[r] = keep_max ? (o > v[r] ? o : v[r]) : (o < v[r] ? o : v[r]);
+          v[r] = ((o > v[r]) == keep_max) ? o : v[r];
         }
       }
     }
@@ -335,7 +340,7 @@ __device__ void bitonic_desc(K (&v)[EPL]) {
 // Best k (<= 128) of the n values of one half, by (value desc, index asc).
 // Writes the sorted survivors to val[0..k) / idx[0..k) (LDS).
 template <int KPL>
-__device__ void half_topk(const float* __restrict__ src, int n, int k, uint32_t* hist,
+__device__ __attribute__((always_inline)) void half_topk(const float* __restrict__ src, int n, int k, uint32_t* hist,
                           uint64_t* stage, float* val, uint32_t* idx) {
   const int lane = lane_id();
   uint32_t key[KPL];
@@ -355,7 +360,8 @@ __device__ void half_topk(const float* __restrict__ src, int n, int k, uint32_t*
   }
   uint64_t* tk = stage;
   uint32_t* ti = reinterpret_cast<uint32_t*>(stage + 64 * KPL);
-  const uint32_t sel = select_exact<KPL>(fv, ek, ei, valid, k, hist, tk, ti);
+  const uint32_t sel =
+      select_exact<KPL>(fv, [&](int q) { return ek[q]; }, ei, valid, k, hist, tk, ti);
   const int sel_local = __popc(sel);
   int pos = wave_incl_scan(sel_local) - sel_local;
 #pragma unroll
@@ -390,15 +396,13 @@ __device__ void half_topk(const float* __restrict__ src, int n, int k, uint32_t*
 // Combine the two sorted top-k lists into the best `count` slots; KPC candidates
 // per lane.  Writes ascending ids and softmax weights to oi / ow.
 template <int KPC>
-__device__ void combine(int n, int k, int count, const float* av, const uint32_t* ai,
+__device__ __attribute__((always_inline)) void combine(int n, int k, int count, const float* av, const uint32_t* ai,
                         const float* bv, const uint32_t* bi, uint32_t* hist, uint64_t* stage,
                         int32_t* __restrict__ oi, float* __restrict__ ow) {
   const int lane = lane_id();
   const int c0 = kCand.off[count];
   const int nc = kCand.off[count + 1] - c0;
-  float fv[KPC];
-  double sc[KPC];
-  uint64_t ek[KPC];
+  float fa[KPC], fb[KPC], fv[KPC];
   uint32_t id[KPC];
   uint32_t valid = 0;
 #pragma unroll
@@ -407,16 +411,18 @@ __device__ void combine(int n, int k, int count, const float* av, const uint32_t
     const uint32_t rc = c < nc ? kCand.rc[c0 + c] : 0xffffu;
     const int r1 = (int)(rc >> 8), r2 = (int)(rc & 255u);
     const bool ok = c < nc && r1 < k && r2 < k;
-    const float a = ok ? av[r1] : 0.0f, b = ok ? bv[r2] : 0.0f;
-    fv[q] = a + b;                        // fp32-rounded sum: never decreases with the exact one
-    sc[q] = (double)a + (double)b;        // exact
-    ek[q] = ord64(sc[q]);
+    fa[q] = ok ? av[r1] : 0.0f;
+    fb[q] = ok ? bv[r2] : 0.0f;
+    fv[q] = fa[q] + fb[q];  // fp32-rounded sum: never decreases with the exact one
     id[q] = ok ? ai[r1] * (uint32_t)n + bi[r2] : 0u;
     valid |= (uint32_t)ok << q;
   }
+  // the exact sum of two fp32 values in fp64
+  auto exact = [&](int q) { return (double)fa[q] + (double)fb[q]; };
   uint64_t* tk = stage;
   uint32_t* ti = reinterpret_cast<uint32_t*>(stage + 64 * KPC);
-  const uint32_t sel = select_exact<KPC>(fv, ek, id, valid, count, hist, tk, ti);
+  const uint32_t sel = select_exact<KPC>(
+      fv, [&](int q) { return ord64(exact(q)); }, id, valid, count, hist, tk, ti);
   // compaction of the `count` survivors as (id, exact score)
   uint32_t* cid = reinterpret_cast<uint32_t*>(stage);
   double* csc = reinterpret_cast<double*>(stage + 64);  // after 128 ids
@@ -426,7 +432,7 @@ __device__ void combine(int n, int k, int count, const float* av, const uint32_t
   for (int q = 0; q < KPC; ++q)
     if ((sel >> q) & 1u) {
       cid[pos] = id[q];
-      csc[pos] = sc[q];
+      csc[pos] = exact(q);
       ++pos;
     }
   __syncthreads();
