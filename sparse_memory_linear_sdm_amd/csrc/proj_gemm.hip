@@ -108,6 +108,87 @@ using SmallTile = Tile<2, 2, 1, 1, 128>;
 constexpr int GROUP_M = 4;
 constexpr int NXCD = 8;
 
+// XCD-aware grouped tile order: consecutive workgroups go to different XCDs, so
+// each XCD gets a contiguous range of tiles, walked GROUP_M row tiles at a time.
+// Returns false for the padding blocks of the grid.
+template <int BM, int BN>
+__device__ __forceinline__ bool tile_of_block(int64_t M, int Ncol, int64_t& tile_m, int& tile_n) {
+  const int ntn = (Ncol + BN - 1) / BN;
+  const int64_t ntm = (M + BM - 1) / BM;
+  const int64_t total = ntm * ntn;
+  const int64_t per_xcd = (total + NXCD - 1) / NXCD;
+  const int64_t t = (int64_t)(blockIdx.x % NXCD) * per_xcd + blockIdx.x / NXCD;
+  if (t >= total) return false;
+  const int64_t grp = t / ((int64_t)GROUP_M * ntn);
+  const int64_t first_m = grp * GROUP_M;
+  const int gm_rows = (int)min<int64_t>(GROUP_M, ntm - first_m);
+  const int64_t in_grp = t - grp * GROUP_M * ntn;
+  tile_m = (first_m + in_grp % gm_rows) * BM;  // local row within [0, M)
+  tile_n = (int)(in_grp / gm_rows) * BN;
+  return true;
+}
+
+// Epilogue through LDS: each wave writes one 32x32 block at a time into a private
+// padded LDS patch (32 rows of 36 floats; register r of lane l of a 32x32 MFMA
+// block holds row (r/4)*8 + (l/32)*4 + r%4, column l%32), then every lane stores
+// 4-column row segments: one 16-byte store where the 4 columns are plain copies
+// into consecutive addresses, else one routed store per column.  `lds` is free
+// (every wave is past its last read of the tile buffers) and holds 32*36 floats
+// per wave.
+template <int FM, int FN, int WN>
+__device__ __forceinline__ void epilogue(floatx16 (&acc)[FM][FN], float* lds, int64_t tile_m,
+                                         int tile_n, int64_t row0, int64_t M, int Ncol,
+                                         const ProjDst& dst) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  float* patch = lds + wave * (32 * 36);
+  const int sr = lane >> 3;        // row within an 8-row group
+  const int sc = (lane & 7) * 4;   // first of this lane's 4 columns
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int cb = tile_n + wn * FN * 32 + j * 32;  // first column of the block
+    // this lane's 4 columns: contiguous float4 destination if all are plain copies
+    // of one region of one head
+    const int c0 = cb + sc;
+    ColDst od[4];
+    bool vec = c0 + 3 < Ncol;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      od[e] = column_dst(dst, min(c0 + e, Ncol - 1));
+      vec = vec && od[e].kind == 0 && od[e].stride == od[0].stride &&
+            od[e].base == od[0].base + e;
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        patch[((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * 36 + (lane & 31)] = acc[i][j][r];
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int rr = q * 8 + sr;
+        const int64_t lm = tile_m + wm * FM * 32 + i * 32 + rr;
+        const float4 v = *reinterpret_cast<const float4*>(patch + rr * 36 + sc);
+        if (lm < M) {
+          if (vec) {
+            *reinterpret_cast<float4*>(od[0].base + (row0 + lm) * od[0].stride) = v;
+          } else {
+            const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (c0 + e < Ncol) od[e].base[(row0 + lm) * od[e].stride] = column_value(od[e], vv[e]);
+          }
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+}
+
 template <class TL>
 __global__ __launch_bounds__(TL::NTH) void proj_gemm_bf16_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wp, int64_t row0, int64_t M,
@@ -123,20 +204,9 @@ __global__ __launch_bounds__(TL::NTH) void proj_gemm_bf16_kernel(
     return reinterpret_cast<uint16_t*>(smem + buf * (TL::A_BYTES + TL::B_BYTES) + TL::A_BYTES);
   };
 
-  // XCD-aware grouped tile order: consecutive workgroups go to different XCDs,
-  // so give each XCD a contiguous range of tiles, walked GROUP_M rows at a time.
-  const int ntn = (Ncol + BN - 1) / BN;
-  const int64_t ntm = (M + BM - 1) / BM;
-  const int64_t total = ntm * ntn;
-  const int64_t per_xcd = (total + NXCD - 1) / NXCD;
-  const int64_t t = (int64_t)(blockIdx.x % NXCD) * per_xcd + blockIdx.x / NXCD;
-  if (t >= total) return;
-  const int64_t grp = t / ((int64_t)GROUP_M * ntn);
-  const int64_t first_m = grp * GROUP_M;
-  const int gm_rows = (int)min<int64_t>(GROUP_M, ntm - first_m);
-  const int64_t in_grp = t - grp * GROUP_M * ntn;
-  const int64_t tile_m = (first_m + in_grp % gm_rows) * BM;  // local row within [0, M)
-  const int tile_n = (int)(in_grp / gm_rows) * BN;
+  int64_t tile_m;
+  int tile_n;
+  if (!tile_of_block<BM, BN>(M, Ncol, tile_m, tile_n)) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -219,56 +289,123 @@ __global__ __launch_bounds__(TL::NTH) void proj_gemm_bf16_kernel(
     cur ^= 1;
   }
 
-  // Epilogue through LDS: each wave writes one 32x32 block at a time into a private
-  // padded LDS patch (32 rows of 36 floats; register r of lane l of a 32x32 MFMA
-  // block holds row (r/4)*8 + (l/32)*4 + r%4, column l%32), then every lane stores
-  // 4-column row segments: one 16-byte store where the 4 columns are plain copies
-  // into consecutive addresses, else one routed store per column.  The A/B buffers
-  // are free after the last barrier.
-  float* patch = reinterpret_cast<float*>(smem) + wave * (32 * 36);
-  const int sr = lane >> 3;        // row within an 8-row group
-  const int sc = (lane & 7) * 4;   // first of this lane's 4 columns
+  epilogue<FM, FN, TL::WN>(acc, reinterpret_cast<float*>(smem), tile_m, tile_n, row0, M, Ncol,
+                           dst);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 path for K a multiple of 64: the same 256x256 tile and 8-wave layout, its
+// operands brought into LDS by direct global->LDS loads (16 bytes per lane) instead
+// of through registers, in two stages of K = 64.  A wave's load fills 1 KB of LDS at
+// consecutive addresses, 8 tile rows of 128 bytes; lane l fetches the 16-byte chunk
+// that lands at row l/8, slot l%8, i.e. chunk (l%8) ^ ((row >> 1) & 7) of that row.
+// This XOR spreads the MFMA fragment reads (16 lanes read 16 rows at one chunk) over
+// all LDS banks.  The loads are issued by inline assembly so that the compiler's
+// wait-count pass, which cannot tell the two stages apart, does not wait for the
+// stage in flight; the kernel waits for exactly the stage it is about to read, and
+// synchronises with a bare barrier (no memory fence, which would also wait for it).
+// The MFMA sequence per output is the one of proj_gemm_bf16_kernel: same results.
+// ---------------------------------------------------------------------------
+constexpr int DMA_BK = 64;
+
+__global__ __launch_bounds__(512) void proj_gemm_bf16_dma_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wp, int64_t row0, int64_t M,
+    int Ncol, int K, ProjDst dst) {
+  constexpr int BM = 256, BN = 256, BK = DMA_BK, FM = 4, FN = 2, WN = 4;
+  constexpr int ROWB = BK * 2;               // 128 bytes per tile row per stage
+  constexpr int NI = BM * ROWB / 1024 / 8;   // loads per wave per operand per stage (4)
+  constexpr int A_BYTES = BM * ROWB, ST_BYTES = (BM + BN) * ROWB;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * ST_BYTES];
+  static_assert(2 * ST_BYTES >= 8 * 32 * 36 * 4, "epilogue patches fit in the stages");
+
+  int64_t tile_m;
+  int tile_n;
+  if (!tile_of_block<BM, BN>(M, Ncol, tile_m, tile_n)) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  auto swz = [](int r) { return (r >> 1) & 7; };
+
+  // this lane's source rows: rows beyond M or Ncol read the last valid row instead
+  // (their products are never stored)
+  const uint16_t* ga[NI];
+  const uint16_t* gb[NI];
 #pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int cb = tile_n + wn * FN * 32 + j * 32;  // first column of the block
-    // this lane's 4 columns: contiguous float4 destination if all are plain copies
-    // of one region of one head
-    const int c0 = cb + sc;
-    ColDst od[4];
-    bool vec = c0 + 3 < Ncol;
+  for (int j = 0; j < NI; ++j) {
+    const int r = (wave * NI + j) * 8 + lane / 8;
+    const int c = (lane & 7) ^ swz(r);
+    const int64_t gm = tile_m + r < M ? tile_m + r : M - 1;
+    const int gn = tile_n + r < Ncol ? tile_n + r : Ncol - 1;
+    ga[j] = X + (row0 + gm) * (int64_t)K + c * 8;
+    gb[j] = Wp + (int64_t)gn * K + c * 8;
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
+  // M0 holds the wave's LDS destination; one wait state between writing M0 and the
+  // load that reads it
+  auto dma = [](const uint16_t* g, uint32_t l) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(g), "s"(__builtin_amdgcn_readfirstlane(l))
+                 : "memory", "m0");
+  };
+  auto issue = [&](int ks) {
+    const uint32_t st = lds0 + (uint32_t)((ks & 1) * ST_BYTES);
+    const int k0 = ks * BK;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      od[e] = column_dst(dst, min(c0 + e, Ncol - 1));
-      vec = vec && od[e].kind == 0 && od[e].stride == od[0].stride &&
-            od[e].base == od[0].base + e;
+    for (int j = 0; j < NI; ++j) {
+      dma(ga[j] + k0, st + (wave * NI + j) * 1024);
+      dma(gb[j] + k0, st + A_BYTES + (wave * NI + j) * 1024);
     }
+  };
+
+  floatx16 acc[FM][FN];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        patch[((r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)) * 36 + (lane & 31)] = acc[i][j][r];
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-      __builtin_amdgcn_wave_barrier();
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int rr = q * 8 + sr;
-        const int64_t lm = tile_m + wm * FM * 32 + i * 32 + rr;
-        const float4 v = *reinterpret_cast<const float4*>(patch + rr * 36 + sc);
-        if (lm < M) {
-          if (vec) {
-            *reinterpret_cast<float4*>(od[0].base + (row0 + lm) * od[0].stride) = v;
-          } else {
-            const float vv[4] = {v.x, v.y, v.z, v.w};
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int nk = K / BK;
+  issue(0);
+  const int lr = lane & 31, hf = lane >> 5;
+  for (int ks = 0; ks < nk; ++ks) {
+    // stage ks is the only one in flight: wait for it, then the barrier makes every
+    // wave's part visible and ensures every wave has finished reading stage ks - 1,
+    // whose buffer the next issue overwrites
+    __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (ks + 1 < nk) issue(ks + 1);
+    const char* st = smem + (ks & 1) * ST_BYTES;
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (c0 + e < Ncol) od[e].base[(row0 + lm) * od[e].stride] = column_value(od[e], vv[e]);
-          }
-        }
+    for (int sl = 0; sl < BK / 16; ++sl) {
+      const int c = sl * 2 + hf;
+      bf16x8 af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int r = wm * FM * 32 + i * 32 + lr;
+        const uint4 u = *reinterpret_cast<const uint4*>(st + r * ROWB + ((c ^ swz(r)) << 4));
+        __builtin_memcpy(&af[i], &u, 16);
       }
-      __builtin_amdgcn_s_waitcnt(0xC07F);
-      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int r = wn * FN * 32 + j * 32 + lr;
+        const uint4 u =
+            *reinterpret_cast<const uint4*>(st + A_BYTES + r * ROWB + ((c ^ swz(r)) << 4));
+        __builtin_memcpy(&bfr[j], &u, 16);
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
   }
+  __syncthreads();  // the stages are free for the epilogue's patches
+  epilogue<FM, FN, WN>(acc, reinterpret_cast<float*>(smem), tile_m, tile_n, row0, M, Ncol, dst);
 }
 
 // ---------------------------------------------------------------------------
@@ -342,10 +479,17 @@ hipError_t launch_proj_gemm(const sdm_dims& d, const void* x, const void* w_proj
                          static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_proj),
                          row0, rows, Ncol, K, dst);
     };
-    if (big >= 256)
+    if (big >= 256 && K % DMA_BK == 0) {
+      const dim3 grid((unsigned)(((big + NXCD - 1) / NXCD) * NXCD));
+      KernelTimer kt("proj_gemm_bf16", s);
+      hipLaunchKernelGGL(proj_gemm_bf16_dma_kernel, grid, dim3(512), 0, s,
+                         static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_proj),
+                         row0, rows, Ncol, K, dst);
+    } else if (big >= 256) {
       go(BigTile{});
-    else
+    } else {
       go(SmallTile{});
+    }
   } else {
     dim3 grid((Ncol + 63) / 64, (unsigned)((rows + 63) / 64));
     KernelTimer kt("proj_gemm_f32", s);
