@@ -187,7 +187,7 @@ __device__ __forceinline__ bool better(uint64_t ka, uint32_t ia, uint64_t kb, ui
 // bins over their [min, max]; the bins above the one holding the need-th best are taken,
 // the bins below are dropped, and the rest continue.  Whatever remains after three rounds
 // (or once few are left) is ranked exactly.  Binning is monotone, so the result is exact.
-// hist: 256 words of LDS; tk/ti: LDS room for 64*KPL (key, id) pairs.
+// hist: 256 words of LDS; tk/ti: LDS room for 64 (key, id) pairs.
 template <int KPL, class KeyF>
 __device__ __attribute__((always_inline)) uint32_t select_exact(const float (&fv)[KPL], KeyF key,
                                                                 const uint32_t (&id)[KPL],
@@ -209,7 +209,8 @@ __device__ __attribute__((always_inline)) uint32_t select_exact(const float (&fv
       }
     lo = wave_min(lo);
     hi = wave_max(hi);
-    const float scale = 256.0f / (hi - lo);
+    // any positive scale keeps the binning monotone, so the hardware reciprocal will do
+    const float scale = 256.0f * __builtin_amdgcn_rcpf(hi - lo);
     if (!(hi > lo) || !(scale > 0.0f) || !(scale < __builtin_inff())) break;
     int bin[KPL];
 #pragma unroll
@@ -255,44 +256,80 @@ __device__ __attribute__((always_inline)) uint32_t select_exact(const float (&fv
       cand &= ~((uint32_t)(!(c && bin[q] == bstar)) << q);
     }
   }
-  // Exact ranking of the remaining candidates: compacted into LDS, each ranked by
-  // one lane against all of them, the verdicts handed back through LDS.
+  // Exact ranking of the remaining candidates.
   const int cl = __popc(cand);
   const int nc = wave_sum(cl);
   if (nc == need) return sel | cand;
-  const int p0 = wave_incl_scan(cl) - cl;
-  int pos = p0;
+  if (nc <= 64) {
+    // compacted into LDS, each ranked by one lane against all of them, the verdicts
+    // handed back through LDS
+    const int p0 = wave_incl_scan(cl) - cl;
+    int pos = p0;
 #pragma unroll
-  for (int q = 0; q < KPL; ++q)
-    if ((cand >> q) & 1u) {
-      tk[pos] = key(q);
-      ti[pos] = id[q];
-      ++pos;
-    }
-  __syncthreads();
-  uint32_t verdict = 0;  // bit c: compacted entry 64 c + lane is among the `need` best
-  for (int c0 = 0, c = 0; c0 < nc; c0 += 64, ++c) {
-    const int e = c0 + lane;
-    if (e < nc) {
-      const uint64_t ke = tk[e];
-      const uint32_t ie = ti[e];
+    for (int q = 0; q < KPL; ++q)
+      if ((cand >> q) & 1u) {
+        tk[pos] = key(q);
+        ti[pos] = id[q];
+        ++pos;
+      }
+    __syncthreads();
+    bool verdict = false;
+    if (lane < nc) {
+      const uint64_t ke = tk[lane];
+      const uint32_t ie = ti[lane];
       int rank = 0;
       for (int u = 0; u < nc; ++u) rank += better(tk[u], ti[u], ke, ie) ? 1 : 0;
-      verdict |= (uint32_t)(rank < need) << c;
+      verdict = rank < need;
+    }
+    __syncthreads();
+    if (lane < nc) ti[lane] = verdict;
+    __syncthreads();
+    pos = p0;
+#pragma unroll
+    for (int q = 0; q < KPL; ++q)
+      if ((cand >> q) & 1u) {
+        if (ti[pos]) sel |= 1u << q;
+        ++pos;
+      }
+    __syncthreads();
+    return sel;
+  }
+  // More than 64 left (many equal or nearly equal keys): take the best remaining one
+  // `need` times, each by a wave-wide reduction under `better`.  Ids are distinct, so
+  // every round has one winner, which its lane moves from `cand` to `sel`.
+  for (int r = 0; r < need; ++r) {
+    bool has = false;
+    uint64_t bk = 0;
+    uint32_t bi = 0;
+    int bq = 0;
+#pragma unroll
+    for (int q = 0; q < KPL; ++q)
+      if ((cand >> q) & 1u) {
+        const uint64_t k = key(q);
+        if (!has || better(k, id[q], bk, bi)) {
+          bk = k;
+          bi = id[q];
+          bq = q;
+          has = true;
+        }
+      }
+    uint64_t wk = bk;
+    uint32_t wi = bi, wh = has;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint64_t ok = xor_lane(wk, o);
+      const uint32_t oi = xor_lane(wi, o), oh = xor_lane(wh, o);
+      if (oh && (!wh || better(ok, oi, wk, wi))) {
+        wk = ok;
+        wi = oi;
+        wh = 1;
+      }
+    }
+    if (has && bk == wk && bi == wi) {
+      sel |= 1u << bq;
+      cand &= ~(1u << bq);
     }
   }
-  __syncthreads();
-  for (int c0 = 0, c = 0; c0 < nc; c0 += 64, ++c)
-    if (c0 + lane < nc) ti[c0 + lane] = (verdict >> c) & 1u;
-  __syncthreads();
-  pos = p0;
-#pragma unroll
-  for (int q = 0; q < KPL; ++q)
-    if ((cand >> q) & 1u) {
-      if (ti[pos]) sel |= 1u << q;
-      ++pos;
-    }
-  __syncthreads();
   return sel;
 }
 
@@ -359,7 +396,7 @@ __device__ __attribute__((always_inline)) void half_topk(const float* __restrict
     valid |= (uint32_t)ok << q;
   }
   uint64_t* tk = stage;
-  uint32_t* ti = reinterpret_cast<uint32_t*>(stage + 64 * KPL);
+  uint32_t* ti = reinterpret_cast<uint32_t*>(stage + 64);
   const uint32_t sel =
       select_exact<KPL>(fv, [&](int q) { return ek[q]; }, ei, valid, k, hist, tk, ti);
   const int sel_local = __popc(sel);
@@ -420,7 +457,7 @@ __device__ __attribute__((always_inline)) void combine(int n, int k, int count, 
   // the exact sum of two fp32 values in fp64
   auto exact = [&](int q) { return (double)fa[q] + (double)fb[q]; };
   uint64_t* tk = stage;
-  uint32_t* ti = reinterpret_cast<uint32_t*>(stage + 64 * KPC);
+  uint32_t* ti = reinterpret_cast<uint32_t*>(stage + 64);
   const uint32_t sel = select_exact<KPC>(
       fv, [&](int q) { return ord64(exact(q)); }, id, valid, count, hist, tk, ti);
   // compaction of the `count` survivors as (id, exact score)
@@ -486,13 +523,9 @@ __device__ __attribute__((always_inline)) void combine(int n, int k, int count, 
   }
 }
 
-// 64-bit staging words: exact-ranking room for 64*K (key, id) pairs (K = max of the
-// per-lane element counts of the halves and the candidates), the half top-k survivors
-// (128 keys) or the combine's survivors (128 ids + 128 doubles).
-constexpr int stage_words(int kpl, int kpc) {
-  const int k = kpl > kpc ? kpl : kpc;
-  return 96 * k > 192 ? 96 * k : 192;
-}
+// 64-bit staging words: exact-ranking room for 64 (key, id) pairs (96 words), the half
+// top-k survivors (128 keys) or the combine's survivors (128 ids + 128 doubles).
+constexpr int kStageWords = 192;
 
 // One wavefront per (row, head, role).  LDS: histogram, staging, two top-k lists.
 template <int KPL, int KPC>
@@ -503,7 +536,7 @@ __global__ __launch_bounds__(64) void select_kernel(const float* __restrict__ sc
                                                     int32_t* __restrict__ idx_r,
                                                     float* __restrict__ wt_r) {
   __shared__ __attribute__((aligned(16))) uint32_t hist[256];
-  __shared__ __attribute__((aligned(16))) uint64_t stage[stage_words(KPL, KPC)];
+  __shared__ __attribute__((aligned(16))) uint64_t stage[kStageWords];
   __shared__ float tv[2][SDM_MAX_COUNT];
   __shared__ uint32_t ti[2][SDM_MAX_COUNT];
 
