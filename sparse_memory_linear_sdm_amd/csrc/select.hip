@@ -527,9 +527,14 @@ __device__ __attribute__((always_inline)) void combine(int n, int k, int count, 
 // top-k survivors (128 keys) or the combine's survivors (128 ids + 128 doubles).
 constexpr int kStageWords = 192;
 
+// Waves per SIMD to compile for: 8 (at most 64 VGPRs, which the instantiations for
+// n <= 384 and counts whose candidates fit 5 per lane, W and R up to about 66, meet
+// without spilling; 4.5 KB of LDS per wave lets 8 fit), else no bound.
+constexpr int sel_waves(int kpl, int kpc) { return kpl <= 6 && kpc <= 5 ? 8 : 1; }
+
 // One wavefront per (row, head, role).  LDS: histogram, staging, two top-k lists.
 template <int KPL, int KPC>
-__global__ __launch_bounds__(64) void select_kernel(const float* __restrict__ scores, int64_t rows,
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sel_waves(KPL, KPC)))) void select_kernel(const float* __restrict__ scores, int64_t rows,
                                                     int H, int n, int W, int R,
                                                     int64_t out_row0, int32_t* __restrict__ idx_w,
                                                     float* __restrict__ wt_w,
