@@ -45,6 +45,12 @@ MFMA_FILE = os.path.join(ROOT, "profiles", "proj_gemm_mfma_layer1p4b.txt")
 BACK_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_backward_traffic_layer1p4b.txt")
 BACK_SOURCE = os.path.join(CSRC, "scan_stream_backward.hip")
 GEMM_SOURCE = os.path.join(CSRC, "proj_gemm.hip")
+SELECT_FILE = os.path.join(ROOT, "profiles", "select_valu_layer1p4b.txt")
+SELECT_SOURCE = os.path.join(CSRC, "select.hip")
+# VALU issue peak of MI355X: 256 CUs x 4 SIMDs, each issuing one wave64 VALU instruction
+# every 2 cycles (32 lanes per cycle: the 157.3 TFLOP/s fp32 vector peak is 32 FMA lanes
+# x 1024 SIMDs x 2.4 GHz), in wave64 instructions per second
+VALU_PEAK_WAVE_INSTR_PER_S = 1024 * 2.4e9 / 2
 
 
 def _profile_fields(path: str, source: str):
@@ -73,6 +79,30 @@ def measured_back_traffic(workload: str):
     """Counter-measured HBM bytes of one reverse-walk launch (current source)."""
     f = _profile_fields(BACK_TRAFFIC_FILE, BACK_SOURCE) if workload == "layer1p4b" else None
     return int(float(f["traffic_bytes"])) if f else None
+
+
+def measured_select_valu(workload: str):
+    """Counted VALU instructions per launch of the selection kernel (current source)."""
+    f = _profile_fields(SELECT_FILE, SELECT_SOURCE) if workload == "layer1p4b" else None
+    return float(f["valu_instructions_per_launch"]) if f else None
+
+
+def select_line(wl, kernels_ms, steps):
+    """The selection kernel against the VALU issue roofline: counted VALU wave
+    instructions per launch (committed rocprofv3 summary, current source) over the
+    kernel's event-timed duration, against 1024 SIMDs x 2.4 GHz / 2 cycles."""
+    if "select" not in kernels_ms:
+        return None
+    ms = kernels_ms["select"]["avg"]
+    valu = measured_select_valu(wl.name)
+    res = {"kernel": "select", "bound": "alu", "ms": ms,
+           "problems_per_launch": wl.tokens * wl.H * 2 * steps // kernels_ms["select"]["launches"],
+           "peak": VALU_PEAK_WAVE_INSTR_PER_S / 1e12, "unit": "T wave64 VALU instr/s"}
+    if valu is not None:
+        ach = valu / (ms * 1e-3)
+        res.update(valu_instructions_per_launch=valu, achieved=ach / 1e12,
+                   frac=ach / VALU_PEAK_WAVE_INSTR_PER_S)
+    return res
 
 
 def measured_mfma_util(workload: str):
@@ -314,8 +344,10 @@ def main():
                    "state": f"{args.state} [B,H,N,d_v]", "tokens_per_step": tokens},
         "phases_ms": {"select": ms_sel, "scan": ms_scan, "step_events": ms_step},
         "gemm": gemm_line(wl, kernels_ms, gemm_kernel, args.steps),
+        "select": select_line(wl, kernels_ms, args.steps),
         "kernels_ms": kernels_ms,
         "effective_hbm_gbs_step": slot_bytes / (ms_wall * 1e-3) / 1e9,
+        "step_frac_of_peak": slot_bytes / (ms_wall * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "roofline": {"bound": "hbm", "kernel": scan_kernel, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": None if bf16_state else measured_traffic(wl.name),
