@@ -35,6 +35,11 @@ Variant (not the pages' printed rule): scan_gdn uses Gated DeltaNet's
 key-weighted error term on the write set; it is pinned against a dense
 matrix-form gated delta recurrence with every slot selected.
 
+Selection-pass backward (training): softmax_backward and pass_a_backward take the
+gradients of the selection products (weights, value, gate, forget and input gates)
+back to the projection output Y = x W_proj^T, to A and b_dt, and through the linear
+projection to x and W_proj; the selected sets carry no gradient.
+
 Storage variant: scan(..., store=round_bf16) keeps a bf16 state (every written
 row rounded to nearest-even bf16 from the exact value); round_bf16 is pinned
 against torch's float32 -> bfloat16 conversion and hand-worked halfway cases.
@@ -57,6 +62,10 @@ Pins (every function is checked against something other than itself):
   tests/test_oracle_histogram_pins.py  slot_update_counts by brute force
   tests/test_oracle_shared_m0_pins.py  forward_walk_shared against plain walks
   tests/test_oracle_backward_pins.py   scan_backward against central differences
+  tests/test_oracle_select_backward_pins.py
+                                       pass_a_backward chained after scan_backward
+                                       against central differences of the whole
+                                       layer from x (x, W_proj, A, b_dt)
   tests/test_oracle_quant_pins.py      E4M3 against torch's float8_e4m3fn, int4
                                        packing by hand, error bounds
 No function of this module is "parity unpinned".
@@ -329,6 +338,7 @@ def pass_a(x, w_proj, A, b_dt, H, n, d_v, W, R, gate_act=GATE_SIGMOID):
         alpha=forget_gate(parts["a"], np.asarray(A, F64), np.asarray(b_dt, F64)),
         beta=input_gate(parts["b"]),
         scores=np.concatenate([parts["kw1"], parts["kw2"], parts["kr1"], parts["kr2"]], axis=-1),
+        a_pre=parts["a"], b_pre=parts["b"], g_pre=parts["g"],
     )
     out.update(select_from_scores(out["scores"], n, W, R))
     assert out["idx_w"].shape[:-1] == lead
@@ -427,6 +437,85 @@ def scan_backward(state_T, log, idx_w, wt_w, idx_r, wt_r, v, alpha, beta, y, gat
         dM[rows] = (alpha[t] * (1.0 - c))[:, None] * G
         M[rows] = m
     return g, M, dM
+
+
+# ----------------------------------------------------------------------------
+# Backward of the selection pass (steps 1-2 and the gate of step 4), reverse mode
+# by the chain rule, down to the gradient of the projection output Y = x W_proj^T.
+# The selected slot sets are piecewise constant in the scores, so the gradient
+# reaches the half-scores only through the softmax weights of the selected slots
+# ([rainbus] step 1; [analysis] "步骤 2": k^(i) and q^(i) are softmax-normalised
+# scores of the selected slots).  For weights w = softmax(s) over the selected
+# scores s_k = h1[i_k] + h2[j_k] (slot id i_k n + j_k):
+#   ds_k = w_k (dw_k - sum_l w_l dw_l),   dh1[i] += sum_{k: i_k = i} ds_k,
+#   dh2[j] += sum_{k: j_k = j} ds_k.
+# Gates ([rainbus] step 2): alpha = exp(-A softplus(z)), z = a + b_dt:
+#   dalpha/dz = -A alpha sigma(z),  dalpha/dA = -softplus(z) alpha,  dz/db_dt = 1;
+#   beta = sigma(b): dbeta/db = beta (1 - beta).
+# Output gate (step 4): sigmoid g = sigma(p): dg/dp = g (1 - g); SiLU g = p sigma(p):
+#   dg/dp = sigma(p) (1 + p (1 - sigma(p))); none: 1.
+# The value columns pass their gradient through.  Then dx = dY W_proj and
+# dW_proj = dY^T x (the projection is linear).
+# ----------------------------------------------------------------------------
+def softmax_backward(w, dw):
+    """Gradient of the scores of w = softmax(s) given dL/dw."""
+    w = np.asarray(w, F64)
+    dw = np.asarray(dw, F64)
+    return w * (dw - np.sum(w * dw, axis=-1, keepdims=True))
+
+
+def pass_a_backward(a, grads, A, b_dt, H, n, d_v, gate_act=GATE_SIGMOID, x=None, w_proj=None):
+    """Gradients of pass_a's products back to the projection output.
+
+    a: pass_a's result for tokens [..]; grads: dL/d of its products, [.., H, *]:
+    d_wt_w, d_wt_r, d_v, d_g (of the activated gate), d_alpha, d_beta.
+    Returns dY [.., H*P] (the gradient of Y = x W_proj^T, per head in the column
+    order of split_heads), dA [H], db_dt [H], and, when x and w_proj are given,
+    dx [.., d] and dW_proj [H*P, d].
+    """
+    A = np.asarray(A, F64)
+    b_dt = np.asarray(b_dt, F64)
+    lead = np.shape(a["alpha"])[:-1]                    # [..]
+    P = 4 * n + 2 * d_v + 2
+    dY = np.zeros(lead + (H, P))
+    blocks = {"w": (0, n), "r": (2 * n, 3 * n)}          # offsets of the two halves
+    for role, (o1, o2) in blocks.items():
+        ids = np.asarray(a[f"idx_{role}"])
+        ds = softmax_backward(a[f"wt_{role}"], grads[f"d_wt_{role}"])
+        for idx in np.ndindex(*(lead + (H,))):
+            for k in range(ids.shape[-1]):
+                i, j = divmod(int(ids[idx][k]), n)
+                dY[idx + (o1 + i,)] += ds[idx][k]
+                dY[idx + (o2 + j,)] += ds[idx][k]
+    o = 4 * n
+    dY[..., o:o + d_v] = np.asarray(grads["d_v"], F64)
+    p = np.asarray(a["g_pre"], F64)
+    if gate_act == GATE_SIGMOID:
+        g = sigmoid(p)
+        dgp = g * (1.0 - g)
+    elif gate_act == GATE_SILU:
+        sg = sigmoid(p)
+        dgp = sg * (1.0 + p * (1.0 - sg))
+    else:
+        dgp = np.ones_like(p)
+    dY[..., o + d_v:o + 2 * d_v] = np.asarray(grads["d_g"], F64) * dgp
+    z = np.asarray(a["a_pre"], F64) + b_dt
+    alpha = forget_gate(a["a_pre"], A, b_dt)
+    d_alpha = np.asarray(grads["d_alpha"], F64)
+    dz = d_alpha * (-A * alpha * sigmoid(z))
+    dY[..., o + 2 * d_v] = dz
+    beta = input_gate(a["b_pre"])
+    dY[..., o + 2 * d_v + 1] = np.asarray(grads["d_beta"], F64) * beta * (1.0 - beta)
+    red = tuple(range(len(lead)))
+    res = dict(dY=dY.reshape(lead + (H * P,)),
+               dA=np.sum(d_alpha * (-softplus(z) * alpha), axis=red),
+               db_dt=np.sum(dz, axis=red))
+    if x is not None and w_proj is not None:
+        dYf = res["dY"].reshape(-1, H * P)
+        xf = np.asarray(x, F64).reshape(dYf.shape[0], -1)
+        res["dx"] = (dYf @ np.asarray(w_proj, F64)).reshape(lead + (xf.shape[1],))
+        res["dW_proj"] = dYf.T @ xf
+    return res
 
 
 # ----------------------------------------------------------------------------
