@@ -14,9 +14,11 @@ step is one T=1 sdm_forward of all 256 sequences, the 64 steps captured in one H
 graph and replayed; it reports microseconds per step and slot-row GB/s.
 
 --mode train times the training path instead: a step is the selection pass, the
-training forward of the scan (with the fp32 write log) and the scan backward
-(random incoming gradients of out and of the final state), which leaves the state
-at M0 again.  Its roofline is the reverse-walk kernel's; no CPU baseline.
+training forward of the scan (with the fp32 write log), the scan backward (random
+incoming gradients of out and of the final state), which leaves the state at M0
+again, the selection-pass backward down to dY, and the two projection-gradient
+GEMMs (dx, dW_proj; bf16 through the platform BLAS).  Its roofline is the
+reverse-walk kernel's; no CPU baseline.
 """
 from __future__ import annotations
 
@@ -35,7 +37,8 @@ METRIC = "SDM layer tokens/s at N=131072,W=R=64,d_v=128; effective HBM GB/s vs p
 METRIC_DECODE = ("SDM decode tokens/s (256 sequences, one token per step, N=65536, W=R=64, "
                  "d_v=128; graph-replayed steps); slot-row HBM GB/s vs peak")
 METRIC_TRAIN = ("SDM layer training tokens/s (selection, scan forward with write log, scan "
-                "backward); reverse-walk HBM GB/s vs peak")
+                "backward, selection backward, projection gradients); reverse-walk HBM GB/s "
+                "vs peak")
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 CSRC = os.path.join(ROOT, "sparse_memory_linear_sdm_amd", "csrc")
@@ -506,13 +509,29 @@ def train_main(args):
                          dtype=torch.uint8, device=dev)
     ws_bwd = torch.empty(max(_lib.workspace_bytes(d, _lib.SDM_ENTRY_SCAN_BACKWARD), 1),
                          dtype=torch.uint8, device=dev)
+    ws_sb = torch.empty(max(_lib.workspace_bytes(d, _lib.SDM_ENTRY_SELECT_BACKWARD), 1),
+                        dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
+    gemm_ms = []
 
-    def step():
+    def step(timed=False):
         d_state.copy_(d_state0)
         ops.select(d, x, w, A, b_dt, out=prod, ws=ws_sel, stream=stream)
         _, y, log = ops.scan_train(d, prod, gamma, state, out=out, ws=ws_fwd, stream=stream)
-        ops.scan_backward(d, prod, gamma, state, d_state, y, log, d_out, ws=ws_bwd, stream=stream)
+        g = ops.scan_backward(d, prod, gamma, state, d_state, y, log, d_out, ws=ws_bwd,
+                              stream=stream)
+        d_y, _, _ = ops.select_backward(d, prod, x, w, A, b_dt, g, ws=ws_sb, stream=stream)
+        # dx = dY W_proj and dW_proj = dY^T x: plain GEMMs of the projection, in bf16
+        # through the platform BLAS
+        if timed:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        dyb = d_y.view(-1, d_y.shape[-1]).to(w.dtype)
+        torch.mm(dyb, w)
+        torch.mm(dyb.t(), x.view(-1, x.shape[-1]))
+        if timed:
+            e1.record(stream)
+            gemm_ms.append((e0, e1))
 
     for _ in range(args.warmup):
         step()
@@ -522,7 +541,7 @@ def train_main(args):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        step(timed=True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     d.flags &= ~_lib.SDM_FLAG_TIMING
@@ -531,6 +550,8 @@ def train_main(args):
     for name, ms in _lib.timing_read(1 << 16):
         per_kernel.setdefault(name, []).append(ms)
     kernels_ms = {k: {"avg": float(np.mean(v)), "launches": len(v)} for k, v in per_kernel.items()}
+    kernels_ms["proj_grad_gemms_blas"] = {
+        "avg": float(np.mean([a.elapsed_time(b) for a, b in gemm_ms])), "launches": len(gemm_ms)}
     back = next(k for k in ("stream_backward", "scan_backward") if k in kernels_ms)
     back_ms = kernels_ms[back]["avg"] * kernels_ms[back]["launches"] / args.steps
     tokens = wl.tokens
@@ -554,7 +575,8 @@ def train_main(args):
         "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "d_model": wl.d_model, "H": wl.H,
                    "N": wl.N, "n": wl.n, "W": wl.W, "R": wl.R, "d_v": wl.d_v,
                    "state": "fp32 [B,H,N,d_v]", "tokens_per_step": tokens,
-                   "step": "select + scan_train + scan_backward"},
+                   "step": "select + scan_train + scan_backward + select_backward + "
+                           "dx/dW_proj GEMMs (bf16, platform BLAS)"},
         "kernels_ms": kernels_ms,
         "roofline": {"bound": "hbm", "kernel": back, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,

@@ -52,7 +52,7 @@ extern "C" {
 #define SDM_API
 #endif
 
-#define SDM_ABI_VERSION 3
+#define SDM_ABI_VERSION 4
 
 /* status codes */
 #define SDM_OK 0
@@ -80,6 +80,7 @@ extern "C" {
 #define SDM_ENTRY_SCAN_BACKWARD 3
 #define SDM_ENTRY_SCAN_TRAIN 4
 #define SDM_ENTRY_SELECT_FROM_SCORES 5
+#define SDM_ENTRY_SELECT_BACKWARD 6
 
 /* scan schedule flags (sdm_dims.flags) */
 #define SDM_FLAG_SCAN_DIRECT 1    /* one workgroup per (b,h), tokens in lock-step */
@@ -350,6 +351,48 @@ SDM_API int32_t sdm_scan_backward(const sdm_dims* dims, const sdm_sel* in, const
                                   const void* log, const float* log_scale, const float* d_out,
                                   const sdm_scan_grads* grads, void* ws, size_t ws_bytes,
                                   void* stream);
+
+/*
+ * Backward of the selection pass (training): [rainbus] steps 1, 2 and 4 differentiated
+ * down to the projection output Y = x W_proj^T.  The selected slot sets are piecewise
+ * constant in the scores, so the gradient reaches the half-scores only through the
+ * softmax weights of the selected slots ([analysis] "步骤 2": k^(i), q^(i) are the
+ * normalised scores of the selected slots).  Per (token, head):
+ *   ds_k = w_k (dw_k - sum_l w_l dw_l) for the selected slots k (id i_k n + j_k);
+ *   dY[half 1, i] = sum_{k: i_k = i} ds_k, dY[half 2, j] = sum_{k: j_k = j} ds_k (per role);
+ *   dY[v] = d_v;  dY[gate] = d_gate g (1 - g) (sigmoid) or d_gate (no activation);
+ *   dY[a] = d_alpha (-A alpha sigmoid(a + b_dt));  dY[b] = d_beta beta (1 - beta);
+ *   d_A = sum over tokens of d_alpha (-softplus(a + b_dt) alpha);  d_b_dt = sum of dY[a].
+ * The forget pre-gate a is recomputed from x and W_proj in fp32.  The remaining
+ * gradients are plain GEMMs of dY for the caller: dx = dY W_proj, dW_proj = dY^T x.
+ *   fwd      the forward's products: idx_w, wt_w, idx_r, wt_r, alpha, beta, gate
+ *            (v and scores unused)
+ *   x, w_proj, A, b_dt   as given to sdm_select
+ *   g        incoming gradients [B, T, H, ...]: d_wt_w [.., W], d_wt_r [.., R], d_v and
+ *            d_gate [.., d_v] (d_gate of the activated gate), d_alpha, d_beta [..]
+ *            (as sdm_scan_backward returns them)
+ *   d_y      [B*T, H*P] fp32 OUT, overwritten: per head the P columns in W_proj's row
+ *            order (write half 1 | write half 2 | read half 1 | read half 2 | v | gate |
+ *            a | b)
+ *   d_A, d_b_dt  [H] fp32 OUT, overwritten (summed over every token of the call)
+ *   ws       >= sdm_workspace_bytes(dims, SDM_ENTRY_SELECT_BACKWARD) bytes
+ * gate_act SDM_GATE_SILU needs the gate's pre-activation: SDM_ERR_UNSUPPORTED.
+ * Deterministic: sums over repeated half indices run in slot order, the other
+ * reductions in fixed trees; results are reproducible bit for bit.
+ */
+typedef struct sdm_select_grads {
+  const float* d_wt_w;
+  const float* d_wt_r;
+  const float* d_v;
+  const float* d_gate;
+  const float* d_alpha;
+  const float* d_beta;
+} sdm_select_grads;
+
+SDM_API int32_t sdm_select_backward(const sdm_dims* dims, const sdm_sel* fwd, const void* x,
+                                    const void* w_proj, const float* A, const float* b_dt,
+                                    const sdm_select_grads* g, float* d_y, float* d_A,
+                                    float* d_b_dt, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Shared learned initial state, copied into a sequence's store on first touch.  M0 is

@@ -19,7 +19,7 @@ SDM_ERR_WORKSPACE, SDM_ERR_UNSUPPORTED, SDM_ERR_HIP = -5, -6, -7
 SDM_DTYPE_F32, SDM_DTYPE_BF16 = 0, 1
 SDM_GATE_NONE, SDM_GATE_SIGMOID, SDM_GATE_SILU = 0, 1, 2
 SDM_ENTRY_SELECT, SDM_ENTRY_SCAN, SDM_ENTRY_FORWARD, SDM_ENTRY_SCAN_BACKWARD = 0, 1, 2, 3
-SDM_ENTRY_SCAN_TRAIN, SDM_ENTRY_SELECT_FROM_SCORES = 4, 5
+SDM_ENTRY_SCAN_TRAIN, SDM_ENTRY_SELECT_FROM_SCORES, SDM_ENTRY_SELECT_BACKWARD = 4, 5, 6
 SDM_MAX_COUNT, SDM_MAX_HALF = 128, 1024
 SDM_NOALLOC_SCRATCH_BYTES = 64 << 20
 SDM_FLAG_SCAN_DIRECT, SDM_FLAG_SCAN_STREAM, SDM_FLAG_SCAN_TWO_PHASE = 1, 2, 4
@@ -31,7 +31,8 @@ SDM_FLAG_LOG_FP8, SDM_FLAG_LOG_INT4 = 64, 128
 EXPORTS = ("sdm_abi_version", "sdm_status_string", "sdm_workspace_bytes", "sdm_select",
            "sdm_select_from_scores", "sdm_scan", "sdm_forward", "sdm_scan_shared_m0",
            "sdm_forward_shared_m0", "sdm_scan_train", "sdm_scan_backward",
-           "sdm_slot_histogram", "sdm_timing_read", "sdm_forward_noalloc")
+           "sdm_slot_histogram", "sdm_timing_read", "sdm_forward_noalloc",
+           "sdm_select_backward")
 
 
 class SdmDims(ctypes.Structure):
@@ -51,6 +52,13 @@ GRAD_FIELDS = ("d_wt_w", "d_wt_r", "d_v", "d_gate", "d_alpha", "d_beta", "d_norm
 
 class SdmScanGrads(ctypes.Structure):
     _fields_ = [(name, ctypes.c_void_p) for name in GRAD_FIELDS]
+
+
+SELECT_GRAD_FIELDS = ("d_wt_w", "d_wt_r", "d_v", "d_gate", "d_alpha", "d_beta")
+
+
+class SdmSelectGrads(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in SELECT_GRAD_FIELDS]
 
 
 class SdmKernelTime(ctypes.Structure):
@@ -105,6 +113,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sdm_scan_backward.restype = I32
     lib.sdm_scan_backward.argtypes = [P(SdmDims), P(SdmSel), VP, VP, VP, VP, VP, VP, VP,
                                       P(SdmScanGrads), VP, ctypes.c_size_t, VP]
+    lib.sdm_select_backward.restype = I32
+    lib.sdm_select_backward.argtypes = [P(SdmDims), P(SdmSel), VP, VP, VP, VP, P(SdmSelectGrads),
+                                        VP, VP, VP, VP, ctypes.c_size_t, VP]
     lib.sdm_forward_noalloc.restype = I32
     lib.sdm_forward_noalloc.argtypes = [P(SdmDims), VP, VP, VP, VP, VP, VP, VP, VP]
     lib.sdm_slot_histogram.restype = I32
@@ -180,6 +191,14 @@ def sdm_forward(d: SdmDims, x, w_proj, A, b_dt, norm_w, state, out, debug: SdmSe
                               _ptr(norm_w), _ptr(state), _ptr(out),
                               ctypes.byref(debug) if debug is not None else None, _ptr(ws),
                               ws_bytes, _stream(stream)))
+
+
+def sdm_select_backward(d: SdmDims, fwd: SdmSel, x, w_proj, A, b_dt, grads: SdmSelectGrads,
+                        d_y, d_A, d_b_dt, ws=None, ws_bytes=0, stream=None):
+    _check(load().sdm_select_backward(ctypes.byref(d), ctypes.byref(fwd), _ptr(x), _ptr(w_proj),
+                                      _ptr(A), _ptr(b_dt), ctypes.byref(grads), _ptr(d_y),
+                                      _ptr(d_A), _ptr(d_b_dt), _ptr(ws), ws_bytes,
+                                      _stream(stream)))
 
 
 def sdm_forward_noalloc(d: SdmDims, x, w_proj, A, b_dt, norm_w, state, out, stream=None):

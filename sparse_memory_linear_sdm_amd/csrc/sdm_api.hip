@@ -354,6 +354,7 @@ size_t sdm_workspace_bytes(const sdm_dims* d, int32_t entry) {
              align_up(scan_workspace_bytes(*d));
     case SDM_ENTRY_SCAN_BACKWARD: return backward_ws_bytes(d);
     case SDM_ENTRY_SELECT_FROM_SCORES: return 0;
+    case SDM_ENTRY_SELECT_BACKWARD: return align_up(select_backward_ws_bytes(*d));
     case SDM_ENTRY_SCAN_TRAIN: {
       const sdm_dims dd = train_dims(d);
       return align_up(scan_workspace_bytes(dd, true));
@@ -494,6 +495,34 @@ int32_t sdm_scan_backward(const sdm_dims* d, const sdm_sel* in, const float* nor
   if (backward_uses_stream(*d))
     return hip_status(launch_stream_backward(*d, a, g->d_norm_w, ws, (hipStream_t)stream));
   return hip_status(launch_scan_backward(a, g->d_norm_w, (hipStream_t)stream));
+}
+
+int32_t sdm_select_backward(const sdm_dims* d, const sdm_sel* fwd, const void* x,
+                            const void* w_proj, const float* A, const float* b_dt,
+                            const sdm_select_grads* g, float* d_y, float* d_A, float* d_b_dt,
+                            void* ws, size_t ws_bytes, void* stream) {
+  Derived dv;
+  int32_t st = check_dims(d, &dv);
+  if (st != SDM_OK) return st;
+  if (d->gate_act == SDM_GATE_SILU) return SDM_ERR_UNSUPPORTED;
+  if (dv.M == 0) return SDM_OK;
+  if (!fwd || !g) return SDM_ERR_NULL;
+  const void* req[] = {fwd->idx_w, fwd->wt_w, fwd->idx_r, fwd->wt_r, fwd->alpha, fwd->beta,
+                       fwd->gate, x, w_proj, A, b_dt, g->d_wt_w, g->d_wt_r, g->d_v,
+                       g->d_gate, g->d_alpha, g->d_beta, d_y, d_A, d_b_dt};
+  for (const void* p : req)
+    if (!p) return SDM_ERR_NULL;
+  for (const void* p : req)
+    if (!aligned16(p)) return SDM_ERR_ALIGN;
+  const size_t need = align_up(select_backward_ws_bytes(*d));
+  if (!ws || ws_bytes < need) return SDM_ERR_WORKSPACE;
+  if (!aligned16(ws)) return SDM_ERR_ALIGN;
+  // one (token, head) per workgroup; its dY row is staged in LDS
+  if ((int64_t)dv.M * d->H > INT32_MAX || dv.P * 4 > 60 * 1024) return SDM_ERR_UNSUPPORTED;
+  TimingScope timing(d);
+  (void)hipGetLastError();
+  return hip_status(launch_select_backward(*d, *fwd, x, w_proj, A, b_dt, *g, d_y, d_A, d_b_dt,
+                                           ws, (hipStream_t)stream));
 }
 
 int32_t sdm_scan_shared_m0(const sdm_dims* d, const sdm_sel* in, const float* norm_w,

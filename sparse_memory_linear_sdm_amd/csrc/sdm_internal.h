@@ -32,6 +32,13 @@ hipError_t launch_select(const sdm_dims& d, const float* scores, int64_t rows, i
                          int32_t* idx_w, float* wt_w, int32_t* idx_r, float* wt_r,
                          hipStream_t s);
 
+// Backward of the selection pass down to dY (select_backward.hip).
+size_t select_backward_ws_bytes(const sdm_dims& d);
+hipError_t launch_select_backward(const sdm_dims& d, const sdm_sel& fwd, const void* x,
+                                  const void* w_proj, const float* A, const float* b_dt,
+                                  const sdm_select_grads& g, float* d_y, float* d_A,
+                                  float* d_b_dt, void* ws, hipStream_t s);
+
 // Recurrent scan over all (b, h) walks.
 struct ScanArgs {
   const int32_t* idx_w;

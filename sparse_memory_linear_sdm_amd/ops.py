@@ -217,6 +217,32 @@ def scan_backward(d: SdmDims, products: dict, norm_w, state, d_state, y_raw, log
     return g
 
 
+@_on_stream
+def select_backward(d: SdmDims, products: dict, x, w_proj, A, b_dt, grads: dict, ws=None,
+                    stream=None):
+    """Backward of the selection pass: gradients of its products (grads: d_wt_w, d_wt_r,
+    d_v, d_gate, d_alpha, d_beta, as scan_backward returns them) to the projection output.
+    Returns (d_y [B, T, H*P], d_A [H], d_b_dt [H]); dx = d_y W_proj and dW_proj =
+    d_y^T x are plain GEMMs left to the caller."""
+    _check_params(d, x, w_proj, A, b_dt)
+    _check_products(d, products)
+    B, T, H = d.B, d.T, d.H
+    shapes = dict(d_wt_w=(d.W,), d_wt_r=(d.R,), d_v=(d.d_v,), d_gate=(d.d_v,), d_alpha=(),
+                  d_beta=())
+    for k in _lib.SELECT_GRAD_FIELDS:
+        _need(grads[k], torch.float32, (B, T, H) + shapes[k], k)
+    P = 4 * d.n + 2 * d.d_v + 2
+    dev = x.device
+    d_y = torch.empty((B, T, H * P), dtype=torch.float32, device=dev)
+    d_A = torch.empty((H,), dtype=torch.float32, device=dev)
+    d_b_dt = torch.empty((H,), dtype=torch.float32, device=dev)
+    ws, nb = _workspace(d, _lib.SDM_ENTRY_SELECT_BACKWARD, dev, ws)
+    gs = _lib.SdmSelectGrads(*[_lib._ptr(grads[k]) for k in _lib.SELECT_GRAD_FIELDS])
+    _lib.sdm_select_backward(d, _sel(products), x, w_proj, A, b_dt, gs, d_y, d_A, d_b_dt, ws, nb,
+                             stream)
+    return d_y, d_A, d_b_dt
+
+
 def alloc_touched(d: SdmDims, device):
     """All-zero touched bitmaps [B, H, ceil(N/32)] (int32 words): every sequence at M0."""
     return torch.zeros((d.B, d.H, (d.n * d.n + 31) // 32), dtype=torch.int32, device=device)

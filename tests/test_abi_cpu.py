@@ -43,7 +43,7 @@ def test_header_constants_match_binding():
 
 
 def test_version_and_status_strings(lib):
-    assert _lib.abi_version() == 3
+    assert _lib.abi_version() == 4
     for code in (0, -1, -2, -3, -4, -5, -6, -7, 12345):
         assert isinstance(_lib.status_string(code), str) and _lib.status_string(code)
     assert _lib.status_string(-5) == "workspace missing or too small"
@@ -281,3 +281,28 @@ def test_noalloc_forward_validates_before_touching_the_device(lib):
     dec = _d(B=256, T=1, d_model=2048, H=4, n=256, W=64, R=64, d_v=128)
     assert lib.sdm_workspace_bytes(ctypes.byref(dec), _lib.SDM_ENTRY_FORWARD) <= \
         _lib.SDM_NOALLOC_SCRATCH_BYTES
+
+
+def test_select_backward_validates_first(lib):
+    s = _sel()
+    g = _lib.SdmSelectGrads(*([FAKE] * 6))
+    back = lambda dd, fwd=s, grads=g, x=FAKE, dy=FAKE, ws=FAKE, nb=1 << 40: \
+        lib.sdm_select_backward(ctypes.byref(dd), ctypes.byref(fwd), x, FAKE, FAKE, FAKE,
+                                ctypes.byref(grads), dy, FAKE, FAKE, ws, nb, None)
+    d = _d(T=64)
+    # the SiLU gate's derivative needs its pre-activation, which the forward keeps not
+    assert back(_d(T=64, gate_act=_lib.SDM_GATE_SILU)) == _lib.SDM_ERR_UNSUPPORTED
+    assert back(d, x=None) == _lib.SDM_ERR_NULL
+    assert back(d, dy=None) == _lib.SDM_ERR_NULL
+    assert back(d, fwd=_sel(gate=None)) == _lib.SDM_ERR_NULL
+    assert back(d, grads=_lib.SdmSelectGrads(*([FAKE] * 5 + [None]))) == _lib.SDM_ERR_NULL
+    assert back(d, x=FAKE + 2) == _lib.SDM_ERR_ALIGN
+    assert back(d, grads=_lib.SdmSelectGrads(*([FAKE] * 2 + [FAKE + 4] + [FAKE] * 3))) == \
+        _lib.SDM_ERR_ALIGN
+    need = lib.sdm_workspace_bytes(ctypes.byref(d), _lib.SDM_ENTRY_SELECT_BACKWARD)
+    assert need >= d.B * d.T * d.H * 2 * 4
+    assert back(d, ws=None) == _lib.SDM_ERR_WORKSPACE
+    assert back(d, nb=need - 1) == _lib.SDM_ERR_WORKSPACE
+    assert back(d, ws=FAKE + 8) == _lib.SDM_ERR_ALIGN
+    assert back(_d(T=0), x=None, dy=None, ws=None, nb=0) == _lib.SDM_OK
+    assert back(_d(H=0)) == _lib.SDM_ERR_SHAPE
