@@ -40,6 +40,11 @@ gradients of the selection products (weights, value, gate, forget and input gate
 back to the projection output Y = x W_proj^T, to A and b_dt, and through the linear
 projection to x and W_proj; the selected sets carry no gradient.
 
+Chunkwise form ([163] section 八): scan_chunkwise computes scan / scan_gdn chunk by
+chunk from the chunk-start state and the tokens' pairwise sparse inner products
+(sparse_inner, a two-pointer merge over ascending slot ids); it is pinned against
+the sequential scans, which define the result, and sparse_inner by brute force.
+
 Storage variant: scan(..., store=round_bf16) keeps a bf16 state (every written
 row rounded to nearest-even bf16 from the exact value); round_bf16 is pinned
 against torch's float32 -> bfloat16 conversion and hand-worked halfway cases.
@@ -66,6 +71,8 @@ Pins (every function is checked against something other than itself):
                                        pass_a_backward chained after scan_backward
                                        against central differences of the whole
                                        layer from x (x, W_proj, A, b_dt)
+  tests/test_oracle_chunk_pins.py      scan_chunkwise against scan / scan_gdn for
+                                       many chunk sizes, sparse_inner by brute force
   tests/test_oracle_quant_pins.py      E4M3 against torch's float8_e4m3fn, int4
                                        packing by hand, error bounds
 No function of this module is "parity unpinned".
@@ -273,6 +280,107 @@ def scan_gdn(state0, idx_w, wt_w, idx_r, wt_r, v, alpha, beta, store=None):
         pred = k @ m_tilde                                             # key-weighted prediction
         M[rows] = keep(m_tilde + (beta[t] * k)[:, None] * (v[t] - pred)[None, :])
         y[t] = wt_r[t] @ M[idx_r[t]]                                   # sparse read
+    return y, M
+
+
+# ----------------------------------------------------------------------------
+# Chunkwise-parallel form of the same recurrences ([163] section 八, training
+# paragraph; [rainbus] the paragraph on novelty, chunk-wise parallelism through
+# the WY representation).  The sequence is cut into fixed-size chunks; inside a
+# chunk the tokens' mutual influence is a sparse inner product of their sorted
+# slot lists, found by a two-pointer merge; across chunks the state is carried
+# serially.  Derivation (exact, a reordering of the same arithmetic):
+#   every written slot j of token u evolves as M[j] <- a_{u,j} M[j] + k_{u,j} x_u,
+#   with a_{u,j} = alpha_u (1 - beta_u k_{u,j}), x_u = beta_u v_u   (scan), or
+#        a_{u,j} = alpha_u,
+#        x_u = beta_u (v_u - alpha_u sum_{j in W_u} k_{u,j} M_{u-1}[j])   (scan_gdn).
+#   With G_j(s, t] = product of a_{u,j} over chunk tokens s < u <= t writing j
+#   (1 if none) and M0 the state at the chunk start (token c0 - 1):
+#     M_t[j] = G_j(c0-1, t] M0[j] + sum_{s <= t, j in W_s} G_j(s, t] k_{s,j} x_s
+#     y_t    = sum_{j in R_t} q_{t,j} G_j(c0-1, t] M0[j] + sum_{s <= t} A_{t,s} x_s,
+#              A_{t,s} = sum_{j in R_t and W_s} q_{t,j} G_j(s, t] k_{s,j}
+#   and for scan_gdn, since alpha_t G_j(s, t-1] = G_j(s, t] on j in W_t,
+#     x_t = beta_t (v_t - sum_{j in W_t} k_{t,j} G_j(c0-1, t] M0[j]
+#                        - sum_{s < t} B_{t,s} x_s),
+#              B_{t,s} = sum_{j in W_t and W_s} k_{t,j} G_j(s, t] k_{s,j},
+#   a unit lower-triangular system in the chunk's x (the WY/UT form), solved by
+#   forward substitution.  The chunk-end state follows from M_t at the last token.
+# ----------------------------------------------------------------------------
+def sparse_inner(ids_a, ids_b, term):
+    """Two-pointer merge of two ascending id lists: the sum of term(p, q) over the
+    positions p, q with ids_a[p] == ids_b[q] (each common id once)."""
+    p = q = 0
+    acc = 0.0
+    while p < len(ids_a) and q < len(ids_b):
+        if ids_a[p] < ids_b[q]:
+            p += 1
+        elif ids_a[p] > ids_b[q]:
+            q += 1
+        else:
+            acc += term(p, q)
+            p += 1
+            q += 1
+    return acc
+
+
+def scan_chunkwise(state0, idx_w, wt_w, idx_r, wt_r, v, alpha, beta, C: int, rule: str = "slot"):
+    """scan() (rule "slot") or scan_gdn() (rule "gdn") in the chunkwise form above,
+    with chunks of C tokens (the last one ragged).  Returns (y_raw, final state)."""
+    M = np.array(state0, dtype=F64, copy=True)
+    idx_w = np.asarray(idx_w)
+    idx_r = np.asarray(idx_r)
+    wt_w = np.asarray(wt_w, F64)
+    wt_r = np.asarray(wt_r, F64)
+    v = np.asarray(v, F64)
+    alpha = np.asarray(alpha, F64)
+    beta = np.asarray(beta, F64)
+    T = idx_w.shape[0]
+    y = np.zeros((T, M.shape[1]), F64)
+    for c0 in range(0, T, C):
+        toks = range(c0, min(c0 + C, T))
+        pos = {u: {int(j): k for k, j in enumerate(idx_w[u])} for u in toks}   # slot -> k
+
+        def a(u, j):                       # decay of slot j by token u, if u writes j
+            k = pos[u].get(j)
+            if k is None:
+                return 1.0
+            return alpha[u] * (1.0 - beta[u] * wt_w[u, k]) if rule == "slot" else alpha[u]
+
+        def G(j, s, t):                    # product of a(u, j) over s < u <= t
+            g = 1.0
+            for u in range(s + 1, t + 1):
+                g *= a(u, j)
+            return g
+
+        M0 = M.copy()
+        x = {}
+        for t in toks:
+            if rule == "slot":
+                x[t] = beta[t] * v[t]
+            else:
+                rhs = v[t].copy()
+                for k, j in enumerate(idx_w[t]):
+                    rhs -= wt_w[t, k] * G(int(j), c0 - 1, t) * M0[j]
+                for s in range(c0, t):
+                    b_ts = sparse_inner(idx_w[t], idx_w[s], lambda p, q, t=t, s=s:
+                                        wt_w[t, p] * G(int(idx_w[t, p]), s, t) * wt_w[s, q])
+                    rhs -= b_ts * x[s]
+                x[t] = beta[t] * rhs
+        for t in toks:
+            for k, j in enumerate(idx_r[t]):
+                y[t] += wt_r[t, k] * G(int(j), c0 - 1, t) * M0[j]
+            for s in range(c0, t + 1):
+                a_ts = sparse_inner(idx_r[t], idx_w[s], lambda p, q, t=t, s=s:
+                                    wt_r[t, p] * G(int(idx_r[t, p]), s, t) * wt_w[s, q])
+                y[t] += a_ts * x[s]
+        end = toks[-1]
+        for j in sorted({int(j) for u in toks for j in idx_w[u]}):
+            row = G(j, c0 - 1, end) * M0[j]
+            for s in toks:
+                k = pos[s].get(j)
+                if k is not None:
+                    row = row + G(j, s, end) * wt_w[s, k] * x[s]
+            M[j] = row
     return y, M
 
 
