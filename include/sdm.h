@@ -125,6 +125,20 @@ extern "C" {
    as closely as the format holds it. */
 #define SDM_FLAG_LOG_FP8 64
 #define SDM_FLAG_LOG_INT4 128
+/* schedule flag (sdm_dims.flags; sdm_scan, sdm_forward and their shared-M0 forms):
+   the chunkwise-parallel form of the scan that the m.163.com article on arXiv
+   2607.07386 (section 八, training paragraph) and the paper.rainbus.top summary (the
+   novelty paragraph: chunk-wise parallelism through the WY representation)
+   describe.  Tokens are cut into chunks of 32; inside a chunk every output follows
+   from the chunk-start state and the tokens' pairwise sparse inner products (a
+   two-pointer merge over the ascending slot lists), with a unit lower-triangular
+   solve for the SDM_FLAG_DELTA_GDN rule; the state is carried from chunk to chunk.
+   The same results as the other schedules up to fp32 rounding order (the decays of
+   a chunk are summed as logarithms, each floored at -80).  Needs each token's write
+   and read ids ascending (the selection's order), fp32 state (with
+   SDM_FLAG_STATE_BF16 it is SDM_ERR_UNSUPPORTED) and a workspace; the training
+   entries do not take it (SDM_ERR_UNSUPPORTED). */
+#define SDM_FLAG_SCAN_CHUNK 256
 
 /* Limits of this build (SDM_ERR_UNSUPPORTED beyond them). */
 #define SDM_MAX_COUNT 128   /* W and R */

@@ -27,6 +27,7 @@ SDM_FLAG_TIMING = 8
 SDM_FLAG_DELTA_GDN = 16
 SDM_FLAG_STATE_BF16 = 32
 SDM_FLAG_LOG_FP8, SDM_FLAG_LOG_INT4 = 64, 128
+SDM_FLAG_SCAN_CHUNK = 256
 
 EXPORTS = ("sdm_abi_version", "sdm_status_string", "sdm_workspace_bytes", "sdm_select",
            "sdm_select_from_scores", "sdm_scan", "sdm_forward", "sdm_scan_shared_m0",

@@ -184,7 +184,7 @@ void launch_direct(bool gdn, dim3 grid, hipStream_t s, const ScanArgs& a) {
 }  // namespace
 
 bool scan_uses_stream(const sdm_dims& d) {
-  if (d.flags & (SDM_FLAG_SCAN_DIRECT | SDM_FLAG_DELTA_GDN)) return false;
+  if (d.flags & (SDM_FLAG_SCAN_DIRECT | SDM_FLAG_DELTA_GDN | SDM_FLAG_SCAN_CHUNK)) return false;
   if (d.flags & (SDM_FLAG_SCAN_STREAM | SDM_FLAG_SCAN_TWO_PHASE)) return true;
   return d.T >= 16;
 }
@@ -196,12 +196,14 @@ static int64_t stage_bytes(const sdm_dims& d, bool quantised_log) {
 }
 
 size_t scan_workspace_bytes(const sdm_dims& d, bool train) {
+  if (!train && scan_uses_chunk(d)) return chunk_workspace_bytes(d);
   if (!scan_uses_stream(d)) return 0;
   const bool q = train && (d.flags & (SDM_FLAG_LOG_FP8 | SDM_FLAG_LOG_INT4));
   return stream_workspace_bytes(d, plan_stream(d, (int64_t)d.n * d.n, stage_bytes(d, q)));
 }
 
 hipError_t launch_scan(const sdm_dims& d, const ScanArgs& a, void* ws, size_t, hipStream_t s) {
+  if (scan_uses_chunk(d) && a.log == nullptr) return launch_chunk_scan(d, a, ws, s);
   if (scan_uses_stream(d))
     return launch_stream_scan(
         a, plan_stream(d, a.N, stage_bytes(d, a.log != nullptr && a.log_fmt != LOG_F32)), ws, s);

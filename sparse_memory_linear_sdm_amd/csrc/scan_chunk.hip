@@ -1,0 +1,526 @@
+// Chunkwise-parallel schedule of the scan (SDM_FLAG_SCAN_CHUNK), both write rules.
+//
+// The form is the one the m.163.com article on arXiv 2607.07386 (section 八,
+// training paragraph) and the paper.rainbus.top summary (the novelty paragraph:
+// chunk-wise parallelism through the WY representation) describe: fixed-size
+// chunks, parallel inside a chunk and serial across chunks, with the mutual
+// influence of two tokens a sparse inner product of their ascending slot lists,
+// found by a two-pointer merge.  For both rules every slot j written by token u
+// evolves as M[j] <- a_{u,j} M[j] + k_{u,j} x_u, where
+//   per-slot rule:  a_{u,j} = alpha_u (1 - beta_u k_{u,j}),  x_u = beta_u v_u
+//   GDN rule:       a_{u,j} = alpha_u,
+//                   x_u = beta_u (v_u - alpha_u sum_{j in W_u} k_{u,j} M_{u-1}[j]).
+// With L_j(t) the sum of log a_{u,j} over the chunk's writers u <= t of slot j,
+// G_j(s, t] = exp(L_j(t) - L_j(s)) and M0 the state at the chunk start:
+//   y_t = sum_{j in R_t} q_{t,j} exp(L_j(t)) M0[j] + sum_{s <= t} A_{t,s} x_s,
+//   A_{t,s} = sum over j in R_t and W_s of q_{t,j} k_{s,j} G_j(s, t]        (merge)
+//   GDN:  x = Tm (v - r),  r_t = sum_{j in W_t} k_{t,j} exp(L_j(t)) M0[j],
+//         Tm = (I + diag(beta) B)^-1 diag(beta),
+//         B_{t,s} = sum over j in W_t and W_s of k_{t,j} k_{s,j} G_j(s, t]  (merge, s < t)
+//   chunk end, per slot j written in the chunk (its last writer e):
+//         M[j] = exp(L_j(e)) M0[j] + sum over j's writers s of G_j(s, e] k_{s,j} x_s.
+// Every log a is floored at -80: a forget gate that is exactly 0 (or beta k = 1)
+// decays by e^-80 instead of to 0, which keeps the differences of L finite.
+// Token ids must be ascending within each list (the selection's output order).
+//
+// chunk_prep: one workgroup per (walk, chunk), all chunks at once: the links
+//   between a slot's writers inside the chunk (binary search of the earlier tokens'
+//   sorted lists), L at every write and read entry, A and, for GDN, B and Tm
+//   (forward substitution).
+// chunk_walk: one workgroup per (walk, 16-column slice of d_v), the walk's chunks in
+//   order: x, the reads and the chunk-end rows.  The columns of the state evolve
+//   independently under both rules, so slices need no communication.  y then goes
+//   through the norm/gate kernel.
+#include "sdm_internal.h"
+
+namespace sdm {
+namespace {
+
+constexpr int kChunk = 32;
+constexpr float kLogFloor = -80.0f;
+constexpr int32_t kNextBit = 1 << 16;  // link word: a later writer of the slot exists
+constexpr int kSlice = 16;             // state columns per chunk_walk workgroup
+constexpr int kBatch = 8;              // rows a lane group keeps in flight
+
+struct ChunkArgs {
+  const int32_t* idx_w;
+  const float* wt_w;
+  const int32_t* idx_r;
+  const float* wt_r;
+  const float* v;
+  const float* alpha;
+  const float* beta;
+  float* Lw;       // [B, T, H, W] L at each write entry (through its own token)
+  float* Lr;       // [B, T, H, R] L at each read entry
+  int32_t* link;   // [B, T, H, W] low 16 bits: previous writer (s W + k) + 1, 0 if none
+  float* Am;       // [walks][chunks][C][C] A_{t,s}, zero above the diagonal
+  float* Tm;       // [walks][chunks][C][C] GDN only
+  float* state;    // [B, H, N, d_v] fp32
+  float* y;        // [B, T, H, d_v]
+  int64_t B, T;
+  int32_t H, N, W, R, d_v, chunks;
+};
+
+// Position of key in the ascending list ids[0..n), or -1.
+__device__ __forceinline__ int find_sorted(const int32_t* ids, int n, int32_t key) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (ids[mid] < key)
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  return (lo < n && ids[lo] == key) ? lo : -1;
+}
+
+// Sparse inner product of two ascending id lists: the sum of f(p, q) over the
+// positions with a[p] == b[q], by a two-pointer merge.
+template <class F>
+__device__ __forceinline__ float merge_sum(const int32_t* a, int na, const int32_t* b, int nb,
+                                           F f) {
+  int p = 0, q = 0;
+  float acc = 0.0f;
+  while (p < na && q < nb) {
+    const int32_t x = a[p], y = b[q];
+    if (x == y) {
+      acc += f(p, q);
+      ++p;
+      ++q;
+    } else if (x < y) {
+      ++p;
+    } else {
+      ++q;
+    }
+  }
+  return acc;
+}
+
+__device__ __forceinline__ float4 fma4(float s, float4 m, float4 acc) {
+  acc.x = fmaf(s, m.x, acc.x);
+  acc.y = fmaf(s, m.y, acc.y);
+  acc.z = fmaf(s, m.z, acc.z);
+  acc.w = fmaf(s, m.w, acc.w);
+  return acc;
+}
+__device__ __forceinline__ float4 add4(float4 a, float4 b) {
+  return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+
+// LDS words of chunk_prep: write lists (ids, k, L, links), read lists (ids, q, L),
+// B and Tm, beta.
+size_t prep_lds_bytes(int W, int R) {
+  return ((size_t)4 * kChunk * W + 3 * kChunk * R + 2 * kChunk * kChunk + kChunk) * 4;
+}
+
+template <bool GDN>
+__global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs a) {
+  constexpr int C = kChunk;
+  extern __shared__ int32_t lds[];
+  const int W = a.W, R = a.R;
+  int32_t* iw = lds;
+  float* kw = reinterpret_cast<float*>(iw + C * W);
+  float* lw = kw + C * W;
+  int32_t* lk = reinterpret_cast<int32_t*>(lw + C * W);
+  int32_t* ir = lk + C * W;
+  float* qr = reinterpret_cast<float*>(ir + C * R);
+  float* lr = qr + C * R;
+  float* Bm = lr + C * R;
+  float* Tl = Bm + C * C;
+  float* be = Tl + C * C;
+
+  const int tid = threadIdx.x;
+  const int64_t w = blockIdx.x / a.chunks;
+  const int c = (int)(blockIdx.x - w * a.chunks);
+  const int64_t b = w / a.H;
+  const int h = (int)(w - b * a.H);
+  const int64_t t0 = (int64_t)c * C;
+  const int Cc = (int)(a.T - t0 < C ? a.T - t0 : C);
+  auto tok = [&](int t) { return (b * a.T + t0 + t) * a.H + h; };
+
+  // the chunk's lists; the log decay of each write entry
+  for (int e = tid; e < Cc * W; e += 256) {
+    const int t = e / W, k = e - t * W;
+    const int64_t gi = tok(t) * W + k;
+    const float kk = a.wt_w[gi];
+    iw[e] = a.idx_w[gi];
+    kw[e] = kk;
+    float la = logf(a.alpha[tok(t)]);
+    if (!GDN) la += log1pf(-a.beta[tok(t)] * kk);
+    lw[e] = fmaxf(la, kLogFloor);
+    lk[e] = 0;
+  }
+  for (int e = tid; e < Cc * R; e += 256) {
+    const int t = e / R, k = e - t * R;
+    const int64_t gi = tok(t) * R + k;
+    ir[e] = a.idx_r[gi];
+    qr[e] = a.wt_r[gi];
+  }
+  if (tid < Cc) be[tid] = a.beta[tok(tid)];
+  __syncthreads();
+
+  // links: the latest earlier token of the chunk writing the same slot (ORs commute,
+  // so the words do not depend on the threads' order)
+  for (int e = tid; e < Cc * W; e += 256) {
+    const int t = e / W;
+    const int32_t j = iw[e];
+    for (int u = t - 1; u >= 0; --u) {
+      const int p = find_sorted(iw + u * W, W, j);
+      if (p >= 0) {
+        atomicOr(&lk[e], u * W + p + 1);
+        atomicOr(&lk[u * W + p], kNextBit);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+
+  // L at each write entry: its own log decay plus those of the earlier writers
+  constexpr int kMaxPer = C * SDM_MAX_COUNT / 256;
+  float run[kMaxPer];
+#pragma unroll
+  for (int i = 0; i < kMaxPer; ++i) {
+    const int e = tid + 256 * i;
+    float s = 0.0f;
+    if (e < Cc * W) {
+      s = lw[e];
+      int p = lk[e] & 0xffff;
+      while (p) {
+        s += lw[p - 1];
+        p = lk[p - 1] & 0xffff;
+      }
+    }
+    run[i] = s;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kMaxPer; ++i) {
+    const int e = tid + 256 * i;
+    if (e < Cc * W) lw[e] = run[i];
+  }
+  __syncthreads();
+
+  // L at each read entry: that of the slot's latest writer at or before the token
+  for (int e = tid; e < Cc * R; e += 256) {
+    const int t = e / R;
+    const int32_t j = ir[e];
+    float L = 0.0f;
+    for (int u = t; u >= 0; --u) {
+      const int p = find_sorted(iw + u * W, W, j);
+      if (p >= 0) {
+        L = lw[u * W + p];
+        break;
+      }
+    }
+    lr[e] = L;
+  }
+  __syncthreads();
+
+  // pairwise sparse inner products
+  float* Ag = a.Am + ((int64_t)w * a.chunks + c) * C * C;
+  for (int pi = tid; pi < C * C; pi += 256) {
+    const int t = pi / C, s = pi - t * C;
+    float av = 0.0f, bv = 0.0f;
+    if (t < Cc && s <= t) {
+      const int32_t* ws = iw + s * W;
+      av = merge_sum(ir + t * R, R, ws, W, [&](int p, int q) {
+        return qr[t * R + p] * kw[s * W + q] * expf(lr[t * R + p] - lw[s * W + q]);
+      });
+      if (GDN && s < t)
+        bv = merge_sum(iw + t * W, W, ws, W, [&](int p, int q) {
+          return kw[t * W + p] * kw[s * W + q] * expf(lw[t * W + p] - lw[s * W + q]);
+        });
+    }
+    Ag[pi] = av;
+    if (GDN) Bm[pi] = bv;
+  }
+
+  if (GDN) {
+    __syncthreads();
+    // Tm = (I + diag(beta) B)^-1 diag(beta), row by row; lane m owns column m
+    if (tid < C) {
+      const int m = tid;
+      for (int t = 0; t < C; ++t) {
+        float acc = t == m ? 1.0f : 0.0f;
+        for (int s = 0; s < t; ++s) acc = fmaf(-Bm[t * C + s], Tl[s * C + m], acc);
+        Tl[t * C + m] = t < Cc ? be[t] * acc : 0.0f;
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_wave_barrier();
+      }
+    }
+    __syncthreads();
+    float* Tg = a.Tm + ((int64_t)w * a.chunks + c) * C * C;
+    for (int pi = tid; pi < C * C; pi += 256) Tg[pi] = Tl[pi];
+  }
+
+  for (int e = tid; e < Cc * W; e += 256) {
+    const int t = e / W, k = e - t * W;
+    const int64_t gi = tok(t) * W + k;
+    a.Lw[gi] = lw[e];
+    a.link[gi] = lk[e];
+  }
+  for (int e = tid; e < Cc * R; e += 256) {
+    const int t = e / R, k = e - t * R;
+    a.Lr[tok(t) * R + k] = lr[e];
+  }
+}
+
+size_t walk_lds_bytes(int W, int R) {
+  return ((size_t)4 * kChunk * W + 3 * kChunk * R + 2 * kChunk * kChunk) * 4 +
+         (size_t)(2 * kChunk + 64) * (kSlice / 4) * 16;
+}
+
+// Weighted sum of rows ids[e] (e = e0 + 2 i, i < cnt) of this lane's 4 columns, weight
+// wt[e] exp(L[e]), kBatch rows in flight.
+__device__ __forceinline__ float4 gather_sum(const float* Mb, int d_v, const int32_t* ids,
+                                             const float* wt, const float* L, int e0, int cnt) {
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i0 = 0; i0 < cnt; i0 += kBatch) {
+    float4 m[kBatch];
+    float s[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const bool ok = i0 + u < cnt;
+      const int e = ok ? e0 + 2 * (i0 + u) : e0;
+      s[u] = ok ? wt[e] * expf(L[e]) : 0.0f;
+      m[u] = *reinterpret_cast<const float4*>(Mb + (int64_t)ids[e] * d_v);
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) acc = fma4(s[u], m[u], acc);
+  }
+  return acc;
+}
+
+template <bool GDN>
+__global__ __launch_bounds__(256) void chunk_walk_kernel(ChunkArgs a) {
+  constexpr int C = kChunk;
+  constexpr int LPR = kSlice / 4;  // lanes per row slice (one float4 each)
+  constexpr int G = 256 / LPR;     // lane groups: two per token
+  static_assert(G == 2 * C, "two lane groups per token");
+  extern __shared__ int32_t lds[];
+  const int W = a.W, R = a.R;
+  int32_t* iw = lds;
+  float* kw = reinterpret_cast<float*>(iw + C * W);
+  float* lw = kw + C * W;
+  int32_t* lk = reinterpret_cast<int32_t*>(lw + C * W);
+  int32_t* ir = lk + C * W;
+  float* qr = reinterpret_cast<float*>(ir + C * R);
+  float* lr = qr + C * R;
+  float* Am = lr + C * R;
+  float* Tl = Am + C * C;
+  float4* xs = reinterpret_cast<float4*>(Tl + C * C);  // [C][LPR] x_t
+  float4* vr = xs + C * LPR;                            // [C][LPR] v_t - r_t (GDN)
+  float4* part = vr + C * LPR;                          // [G][LPR]
+
+  const int tid = threadIdx.x;
+  const int li = tid % LPR, g = tid / LPR;
+  const int tl = g >> 1, half = g & 1;  // the token and half of its lists this group takes
+  const int64_t walks = a.B * a.H;
+  const int64_t w = blockIdx.x % walks;
+  const int slice = (int)(blockIdx.x / walks);
+  const int64_t b = w / a.H;
+  const int h = (int)(w - b * a.H);
+  const int d_v = a.d_v;
+  float* const Mb = a.state + w * (int64_t)a.N * d_v + slice * kSlice + li * 4;
+  const int col = slice * kSlice;
+
+  for (int c = 0; c < a.chunks; ++c) {
+    const int64_t t0 = (int64_t)c * C;
+    const int Cc = (int)(a.T - t0 < C ? a.T - t0 : C);
+    auto tok = [&](int t) { return (b * a.T + t0 + t) * a.H + h; };
+    const int64_t cm = ((int64_t)w * a.chunks + c) * C * C;
+    for (int e = tid; e < Cc * W; e += 256) {
+      const int t = e / W, k = e - t * W;
+      const int64_t gi = tok(t) * W + k;
+      iw[e] = a.idx_w[gi];
+      kw[e] = a.wt_w[gi];
+      lw[e] = a.Lw[gi];
+      lk[e] = a.link[gi];
+    }
+    for (int e = tid; e < Cc * R; e += 256) {
+      const int t = e / R, k = e - t * R;
+      const int64_t gi = tok(t) * R + k;
+      ir[e] = a.idx_r[gi];
+      qr[e] = a.wt_r[gi];
+      lr[e] = a.Lr[gi];
+    }
+    for (int pi = tid; pi < C * C; pi += 256) {
+      Am[pi] = a.Am[cm + pi];
+      if (GDN) Tl[pi] = a.Tm[cm + pi];
+    }
+    __syncthreads();
+
+    // x_t for this slice
+    if (GDN) {
+      float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (tl < Cc) r = gather_sum(Mb, d_v, iw, kw, lw, tl * W + half, (W - half + 1) / 2);
+      part[g * LPR + li] = r;
+      __syncthreads();
+      if (tid < C * LPR) {
+        const int t = tid / LPR, q = tid % LPR;
+        float4 d = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (t < Cc) {
+          const float4 vv = reinterpret_cast<const float4*>(a.v + tok(t) * d_v + col)[q];
+          const float4 rr = add4(part[(2 * t) * LPR + q], part[(2 * t + 1) * LPR + q]);
+          d = make_float4(vv.x - rr.x, vv.y - rr.y, vv.z - rr.z, vv.w - rr.w);
+        }
+        vr[t * LPR + q] = d;
+      }
+      __syncthreads();
+      if (tid < C * LPR) {
+        const int t = tid / LPR, q = tid % LPR;
+        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int s = 0; s <= t; ++s) x = fma4(Tl[t * C + s], vr[s * LPR + q], x);
+        xs[t * LPR + q] = x;
+      }
+    } else if (tid < C * LPR) {
+      const int t = tid / LPR, q = tid % LPR;
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (t < Cc) {
+        const float be = a.beta[tok(t)];
+        const float4 vv = reinterpret_cast<const float4*>(a.v + tok(t) * d_v + col)[q];
+        x = make_float4(be * vv.x, be * vv.y, be * vv.z, be * vv.w);
+      }
+      xs[t * LPR + q] = x;
+    }
+
+    // reads: the chunk-start rows, then the chunk's own writes through A
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (tl < Cc) acc = gather_sum(Mb, d_v, ir, qr, lr, tl * R + half, (R - half + 1) / 2);
+    part[g * LPR + li] = acc;
+    __syncthreads();  // every read of the chunk-start rows is done past this point
+    if (tid < C * LPR) {
+      const int t = tid / LPR, q = tid % LPR;
+      if (t < Cc) {
+        float4 y = add4(part[(2 * t) * LPR + q], part[(2 * t + 1) * LPR + q]);
+        for (int s = 0; s <= t; ++s) y = fma4(Am[t * C + s], xs[s * LPR + q], y);
+        reinterpret_cast<float4*>(a.y + tok(t) * d_v + col)[q] = y;
+      }
+    }
+
+    // chunk-end rows: the last writer of each slot folds its chain of writers
+    for (int e0 = g; e0 < Cc * W; e0 += G * kBatch) {
+      float4 m[kBatch];
+      bool last[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int e = e0 + G * u;
+        last[u] = e < Cc * W && !(lk[e] & kNextBit);
+        m[u] = *reinterpret_cast<const float4*>(Mb + (int64_t)iw[last[u] ? e : e0] * d_v);
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (!last[u]) continue;
+        const int e = e0 + G * u;
+        const float le = lw[e];
+        float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
+        r = fma4(expf(le), m[u], r);
+        int p = e + 1;
+        while (p) {
+          const int s = (p - 1) / W;
+          r = fma4(expf(le - lw[p - 1]) * kw[p - 1], xs[s * LPR + li], r);
+          p = lk[p - 1] & 0xffff;
+        }
+        *reinterpret_cast<float4*>(Mb + (int64_t)iw[e] * d_v) = r;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+int64_t chunks_of(const sdm_dims& d) { return (d.T + kChunk - 1) / kChunk; }
+
+struct ChunkWs {
+  size_t lw, lr, link, am, tm, y, total;
+};
+ChunkWs chunk_ws(const sdm_dims& d) {
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t th = (size_t)d.B * d.T * d.H;
+  const size_t mats = (size_t)d.B * d.H * chunks_of(d) * kChunk * kChunk * 4;
+  ChunkWs s;
+  s.lw = al(th * d.W * 4);
+  s.lr = al(th * d.R * 4);
+  s.link = al(th * d.W * 4);
+  s.am = al(mats);
+  s.tm = (d.flags & SDM_FLAG_DELTA_GDN) ? al(mats) : 0;
+  s.y = al(th * d.d_v * 4);
+  s.total = s.lw + s.lr + s.link + s.am + s.tm + s.y;
+  return s;
+}
+
+}  // namespace
+
+bool scan_uses_chunk(const sdm_dims& d) { return (d.flags & SDM_FLAG_SCAN_CHUNK) != 0; }
+
+size_t chunk_workspace_bytes(const sdm_dims& d) { return chunk_ws(d).total; }
+
+hipError_t launch_chunk_scan(const sdm_dims& d, const ScanArgs& sa, void* ws, hipStream_t st) {
+  const ChunkWs s = chunk_ws(d);
+  char* p = static_cast<char*>(ws);
+  ChunkArgs a;
+  a.idx_w = sa.idx_w;
+  a.wt_w = sa.wt_w;
+  a.idx_r = sa.idx_r;
+  a.wt_r = sa.wt_r;
+  a.v = sa.v;
+  a.alpha = sa.alpha;
+  a.beta = sa.beta;
+  a.Lw = reinterpret_cast<float*>(p); p += s.lw;
+  a.Lr = reinterpret_cast<float*>(p); p += s.lr;
+  a.link = reinterpret_cast<int32_t*>(p); p += s.link;
+  a.Am = reinterpret_cast<float*>(p); p += s.am;
+  a.Tm = s.tm ? reinterpret_cast<float*>(p) : nullptr; p += s.tm;
+  a.y = reinterpret_cast<float*>(p);
+  a.state = static_cast<float*>(sa.state);
+  a.B = sa.B;
+  a.T = sa.T;
+  a.H = sa.H;
+  a.N = sa.N;
+  a.W = sa.W;
+  a.R = sa.R;
+  a.d_v = sa.d_v;
+  a.chunks = (int32_t)chunks_of(d);
+  const bool gdn = (d.flags & SDM_FLAG_DELTA_GDN) != 0;
+  const int64_t walks = sa.B * sa.H;
+  {
+    const size_t lds = prep_lds_bytes(a.W, a.R);
+    const dim3 grid((unsigned)(walks * a.chunks));
+    KernelTimer kt("chunk_prep", st);
+    if (gdn) {
+      hipError_t e = hipFuncSetAttribute((const void*)chunk_prep_kernel<true>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(chunk_prep_kernel<true>, grid, dim3(256), lds, st, a);
+    } else {
+      hipError_t e = hipFuncSetAttribute((const void*)chunk_prep_kernel<false>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(chunk_prep_kernel<false>, grid, dim3(256), lds, st, a);
+    }
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  {
+    const size_t lds = walk_lds_bytes(a.W, a.R);
+    // a walk's slices sit walks apart, so with a multiple of 8 walks they share an
+    // XCD (and its L2 copy of the chunk's lists)
+    const dim3 grid((unsigned)(walks * (a.d_v / kSlice)));
+    KernelTimer kt("chunk_walk", st);
+    if (gdn) {
+      e = hipFuncSetAttribute((const void*)chunk_walk_kernel<true>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(chunk_walk_kernel<true>, grid, dim3(256), lds, st, a);
+    } else {
+      e = hipFuncSetAttribute((const void*)chunk_walk_kernel<false>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(chunk_walk_kernel<false>, grid, dim3(256), lds, st, a);
+    }
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_norm_gate(sa, a.y, st);
+}
+
+}  // namespace sdm

@@ -1186,4 +1186,36 @@ hipError_t launch_stream_scan(const ScanArgs& sa, const StreamPlan& pl, void* ws
   return hipSuccess;
 }
 
+
+hipError_t launch_norm_gate(const ScanArgs& sa, const float* y, hipStream_t st) {
+  StreamArgs a = {};
+  a.gate = sa.gate;
+  a.norm_w = sa.norm_w;
+  a.out = sa.out;
+  a.y_raw = sa.y_raw;
+  a.y_part = const_cast<float*>(y);
+  a.B = sa.B;
+  a.T = sa.T;
+  a.t0 = 0;
+  a.Tc = sa.T;
+  a.H = sa.H;
+  a.d_v = sa.d_v;
+  a.eps = sa.eps;
+  a.parts = 1;
+  const int64_t rows = sa.B * sa.T * sa.H;
+  const int lpr = sa.d_v / 4 < 64 ? sa.d_v / 4 : 64;
+  const int64_t rpb = 4 * (64 / lpr);
+  const dim3 ng((unsigned)((rows + rpb - 1) / rpb));
+  KernelTimer kt("norm_gate", st);
+  switch (sa.d_v) {
+    case 16: hipLaunchKernelGGL(norm_gate_kernel<16>, ng, dim3(256), 0, st, a); break;
+    case 32: hipLaunchKernelGGL(norm_gate_kernel<32>, ng, dim3(256), 0, st, a); break;
+    case 64: hipLaunchKernelGGL(norm_gate_kernel<64>, ng, dim3(256), 0, st, a); break;
+    case 128: hipLaunchKernelGGL(norm_gate_kernel<128>, ng, dim3(256), 0, st, a); break;
+    case 256: hipLaunchKernelGGL(norm_gate_kernel<256>, ng, dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace sdm

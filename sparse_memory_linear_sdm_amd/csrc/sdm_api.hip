@@ -28,7 +28,8 @@ struct Derived {
 
 int32_t check_dims(const sdm_dims* d, Derived* out) {
   if (!d) return SDM_ERR_NULL;
-  const int32_t sched = SDM_FLAG_SCAN_DIRECT | SDM_FLAG_SCAN_STREAM | SDM_FLAG_SCAN_TWO_PHASE;
+  const int32_t sched = SDM_FLAG_SCAN_DIRECT | SDM_FLAG_SCAN_STREAM | SDM_FLAG_SCAN_TWO_PHASE |
+                        SDM_FLAG_SCAN_CHUNK;
   if (d->flags & ~(sched | SDM_FLAG_TIMING | SDM_FLAG_DELTA_GDN | SDM_FLAG_STATE_BF16 |
                    SDM_FLAG_LOG_FP8 | SDM_FLAG_LOG_INT4))
     return SDM_ERR_UNSUPPORTED;
@@ -36,7 +37,9 @@ int32_t check_dims(const sdm_dims* d, Derived* out) {
   if (__builtin_popcount((unsigned)(d->flags & sched)) > 1) return SDM_ERR_SHAPE;  // one schedule
   if ((d->flags & SDM_FLAG_DELTA_GDN) &&
       (d->flags & (SDM_FLAG_SCAN_STREAM | SDM_FLAG_SCAN_TWO_PHASE)))
-    return SDM_ERR_UNSUPPORTED;  // the variant runs the direct schedule only
+    return SDM_ERR_UNSUPPORTED;  // the variant runs the direct or the chunk schedule
+  if ((d->flags & SDM_FLAG_SCAN_CHUNK) && (d->flags & SDM_FLAG_STATE_BF16))
+    return SDM_ERR_UNSUPPORTED;
   if (d->in_dtype != SDM_DTYPE_F32 && d->in_dtype != SDM_DTYPE_BF16) return SDM_ERR_DTYPE;
   if (d->gate_act < SDM_GATE_NONE || d->gate_act > SDM_GATE_SILU) return SDM_ERR_DTYPE;
   if (d->B < 0 || d->T < 0 || d->d_model < 1 || d->H < 1 || d->n < 1 || d->W < 1 || d->R < 1 ||
@@ -320,9 +323,11 @@ static int32_t log_format(const sdm_dims* d) {
                                                                                    : LOG_F32;
 }
 
-// The training entries take fp32 state and the per-slot rule, on any schedule.
+// The training entries take fp32 state and the per-slot rule, on the direct and
+// slot-owner schedules.
 static int32_t check_train_flags(const sdm_dims* d) {
-  if (d->flags & (SDM_FLAG_STATE_BF16 | SDM_FLAG_DELTA_GDN)) return SDM_ERR_UNSUPPORTED;
+  if (d->flags & (SDM_FLAG_STATE_BF16 | SDM_FLAG_DELTA_GDN | SDM_FLAG_SCAN_CHUNK))
+    return SDM_ERR_UNSUPPORTED;
   return SDM_OK;
 }
 

@@ -186,6 +186,13 @@ StreamPlan plan_stream(const sdm_dims& d, int64_t N, int64_t stage_bytes = 0);
 size_t stream_workspace_bytes(const sdm_dims& d, const StreamPlan& pl);
 hipError_t launch_stream_scan(const ScanArgs& a, const StreamPlan& pl, void* ws, hipStream_t s);
 bool scan_uses_stream(const sdm_dims& d);
+// y [B, T, H, d_v] (one part) through the RMSNorm and gate into a.out (and a.y_raw).
+hipError_t launch_norm_gate(const ScanArgs& a, const float* y, hipStream_t st);
+
+// Chunkwise schedule (scan_chunk.hip, SDM_FLAG_SCAN_CHUNK): fp32 state, forward only.
+bool scan_uses_chunk(const sdm_dims& d);
+size_t chunk_workspace_bytes(const sdm_dims& d);
+hipError_t launch_chunk_scan(const sdm_dims& d, const ScanArgs& a, void* ws, hipStream_t st);
 
 // Write-log storage (training): one row of d_v values per write, fp32, or quantised
 // with one absmax per row -- fp8 (OCP E4M3, v = x * 448 / absmax) or int4 (v = x * 7 /
