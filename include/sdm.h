@@ -99,8 +99,9 @@ extern "C" {
    pages say the layer reduces to when every slot is selected with a dense key:
    ai-paper-analysis.pages.dev, section "与 GDN 的关系"; m.163.com article on
    arXiv 2607.07386, section 二).  It needs every row of a token's write set before
-   any is written, so it runs the direct schedule; combined with
-   SDM_FLAG_SCAN_STREAM or SDM_FLAG_SCAN_TWO_PHASE it is SDM_ERR_UNSUPPORTED. */
+   any is written, so it runs the direct schedule or the chunk schedule
+   (SDM_FLAG_SCAN_CHUNK, its default from 256 tokens with an fp32 state); combined
+   with SDM_FLAG_SCAN_STREAM or SDM_FLAG_SCAN_TWO_PHASE it is SDM_ERR_UNSUPPORTED. */
 #define SDM_FLAG_DELTA_GDN 16
 /* storage flag (sdm_dims.flags; sdm_scan and sdm_forward): the state buffer holds
    bf16 values.  The arithmetic stays fp32; each written row element is rounded to

@@ -25,8 +25,11 @@
 //
 // chunk_prep: one workgroup per (walk, chunk), all chunks at once: the links
 //   between a slot's writers inside the chunk (binary search of the earlier tokens'
-//   sorted lists), L at every write and read entry, A and, for GDN, B and Tm
-//   (forward substitution).
+//   sorted lists, only for slots that a hashed bitmap shows may repeat), L at every
+//   write and read entry, A and, for GDN, B and Tm (forward substitution).  The
+//   pairwise sparse inner products are summed through those links rather than by
+//   merging every pair of lists: the same sums, but a merge walks all 2W entries of
+//   each of the C^2/2 pairs although, with N >> C W, almost no pair shares a slot.
 // chunk_walk: one workgroup per (walk, 16-column slice of d_v), the walk's chunks in
 //   order: x, the reads and the chunk-end rows.  The columns of the state evolve
 //   independently under both rules, so slices need no communication.  y then goes
@@ -40,7 +43,16 @@ constexpr int kChunk = 32;
 constexpr float kLogFloor = -80.0f;
 constexpr int32_t kNextBit = 1 << 16;  // link word: a later writer of the slot exists
 constexpr int kSlice = 16;             // state columns per chunk_walk workgroup
-constexpr int kBatch = 8;              // rows a lane group keeps in flight
+constexpr int kBatch = 16;             // rows a lane group keeps in flight
+constexpr int kWalkThreads = 512;      // chunk_walk: four lane groups per token
+// chunk_prep marks each written slot in two hashed bitmaps (seen once, seen again),
+// so that only entries whose slot may occur twice in the chunk search for it
+constexpr int kFilterBits = 16;
+constexpr int kFilterWords = (1 << kFilterBits) / 32;
+
+__device__ __forceinline__ uint32_t slot_hash(int32_t j) {
+  return ((uint32_t)j * 2654435761u) >> (32 - kFilterBits);
+}
 
 struct ChunkArgs {
   const int32_t* idx_w;
@@ -74,28 +86,6 @@ __device__ __forceinline__ int find_sorted(const int32_t* ids, int n, int32_t ke
   return (lo < n && ids[lo] == key) ? lo : -1;
 }
 
-// Sparse inner product of two ascending id lists: the sum of f(p, q) over the
-// positions with a[p] == b[q], by a two-pointer merge.
-template <class F>
-__device__ __forceinline__ float merge_sum(const int32_t* a, int na, const int32_t* b, int nb,
-                                           F f) {
-  int p = 0, q = 0;
-  float acc = 0.0f;
-  while (p < na && q < nb) {
-    const int32_t x = a[p], y = b[q];
-    if (x == y) {
-      acc += f(p, q);
-      ++p;
-      ++q;
-    } else if (x < y) {
-      ++p;
-    } else {
-      ++q;
-    }
-  }
-  return acc;
-}
-
 __device__ __forceinline__ float4 fma4(float s, float4 m, float4 acc) {
   acc.x = fmaf(s, m.x, acc.x);
   acc.y = fmaf(s, m.y, acc.y);
@@ -107,10 +97,11 @@ __device__ __forceinline__ float4 add4(float4 a, float4 b) {
   return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
 }
 
-// LDS words of chunk_prep: write lists (ids, k, L, links), read lists (ids, q, L),
-// B and Tm, beta.
+// LDS words of chunk_prep: write lists (ids, k, L, links), read-side L and latest
+// writers, A, B and Tm, beta, the two slot bitmaps.
 size_t prep_lds_bytes(int W, int R) {
-  return ((size_t)4 * kChunk * W + 3 * kChunk * R + 2 * kChunk * kChunk + kChunk) * 4;
+  return ((size_t)4 * kChunk * W + 2 * kChunk * R + 3 * kChunk * kChunk + kChunk +
+          2 * kFilterWords) * 4;
 }
 
 template <bool GDN>
@@ -122,12 +113,14 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs a) {
   float* kw = reinterpret_cast<float*>(iw + C * W);
   float* lw = kw + C * W;
   int32_t* lk = reinterpret_cast<int32_t*>(lw + C * W);
-  int32_t* ir = lk + C * W;
-  float* qr = reinterpret_cast<float*>(ir + C * R);
-  float* lr = qr + C * R;
-  float* Bm = lr + C * R;
+  float* lr = reinterpret_cast<float*>(lk + C * W);
+  int32_t* rl = reinterpret_cast<int32_t*>(lr + C * R);  // latest writer + 1, 0 if none
+  float* Al = reinterpret_cast<float*>(rl + C * R);
+  float* Bm = Al + C * C;
   float* Tl = Bm + C * C;
   float* be = Tl + C * C;
+  uint32_t* seen1 = reinterpret_cast<uint32_t*>(be + C);
+  uint32_t* seen2 = seen1 + kFilterWords;
 
   const int tid = threadIdx.x;
   const int64_t w = blockIdx.x / a.chunks;
@@ -138,7 +131,8 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs a) {
   const int Cc = (int)(a.T - t0 < C ? a.T - t0 : C);
   auto tok = [&](int t) { return (b * a.T + t0 + t) * a.H + h; };
 
-  // the chunk's lists; the log decay of each write entry
+  // the chunk's write lists; the log decay of each write entry
+#pragma unroll 4
   for (int e = tid; e < Cc * W; e += 256) {
     const int t = e / W, k = e - t * W;
     const int64_t gi = tok(t) * W + k;
@@ -150,26 +144,45 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs a) {
     lw[e] = fmaxf(la, kLogFloor);
     lk[e] = 0;
   }
-  for (int e = tid; e < Cc * R; e += 256) {
-    const int t = e / R, k = e - t * R;
-    const int64_t gi = tok(t) * R + k;
-    ir[e] = a.idx_r[gi];
-    qr[e] = a.wt_r[gi];
-  }
   if (tid < Cc) be[tid] = a.beta[tok(tid)];
+  for (int i = tid; i < 2 * kFilterWords; i += 256) seen1[i] = 0u;
+  __syncthreads();
+  for (int e = tid; e < Cc * W; e += 256) {
+    const uint32_t hs = slot_hash(iw[e]);
+    const uint32_t bit = 1u << (hs & 31);
+    if (atomicOr(&seen1[hs >> 5], bit) & bit) atomicOr(&seen2[hs >> 5], bit);
+  }
   __syncthreads();
 
   // links: the latest earlier token of the chunk writing the same slot (ORs commute,
-  // so the words do not depend on the threads' order)
-  for (int e = tid; e < Cc * W; e += 256) {
-    const int t = e / W;
-    const int32_t j = iw[e];
-    for (int u = t - 1; u >= 0; --u) {
-      const int p = find_sorted(iw + u * W, W, j);
-      if (p >= 0) {
-        atomicOr(&lk[e], u * W + p + 1);
-        atomicOr(&lk[u * W + p], kNextBit);
-        break;
+  // so the words do not depend on the threads' order).  A slot whose hash was
+  // written once has no other writer; for the others the whole wavefront searches
+  // together, lane u in token u's list, and the highest lane that finds it wins.
+  const int lane = tid & 63;
+  for (int e0 = tid - lane; e0 < Cc * W; e0 += 256) {
+    const int e = e0 + lane;
+    int32_t j = 0;
+    bool maybe = false;
+    if (e < Cc * W) {
+      j = iw[e];
+      const uint32_t hs = slot_hash(j);
+      maybe = (seen2[hs >> 5] >> (hs & 31)) & 1u;
+    }
+    uint64_t m = __ballot(maybe);
+    while (m) {
+      const int l = __builtin_ctzll(m);
+      m &= m - 1;
+      const int32_t jj = __shfl(j, l);
+      const int te = (e0 + l) / W;
+      const int pos = lane < te ? find_sorted(iw + lane * W, W, jj) : -1;
+      const uint64_t hit = __ballot(pos >= 0);
+      if (hit) {
+        const int u = 63 - __builtin_clzll(hit);
+        const int p = __shfl(pos, u);
+        if (lane == 0) {
+          atomicOr(&lk[e0 + l], u * W + p + 1);
+          atomicOr(&lk[u * W + p], kNextBit);
+        }
       }
     }
   }
@@ -200,43 +213,87 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs a) {
   }
   __syncthreads();
 
-  // L at each read entry: that of the slot's latest writer at or before the token
-  for (int e = tid; e < Cc * R; e += 256) {
-    const int t = e / R;
-    const int32_t j = ir[e];
+  // each read entry: the slot's latest writer at or before the token and its L (none
+  // if the slot's hash was never written), searched by the whole wavefront as above
+  for (int e0 = tid - lane; e0 < Cc * R; e0 += 256) {
+    const int e = e0 + lane;
+    int32_t j = 0;
+    bool maybe = false;
+    if (e < Cc * R) {
+      const int t = e / R, k = e - t * R;
+      j = a.idx_r[tok(t) * R + k];
+      const uint32_t hs = slot_hash(j);
+      maybe = (seen1[hs >> 5] >> (hs & 31)) & 1u;
+    }
     float L = 0.0f;
-    for (int u = t; u >= 0; --u) {
-      const int p = find_sorted(iw + u * W, W, j);
-      if (p >= 0) {
-        L = lw[u * W + p];
-        break;
+    int lat = 0;
+    uint64_t m = __ballot(maybe);
+    while (m) {
+      const int l = __builtin_ctzll(m);
+      m &= m - 1;
+      const int32_t jj = __shfl(j, l);
+      const int te = (e0 + l) / R;
+      const int pos = lane <= te ? find_sorted(iw + lane * W, W, jj) : -1;
+      const uint64_t hit = __ballot(pos >= 0);
+      if (hit) {
+        const int u = 63 - __builtin_clzll(hit);
+        const int p = __shfl(pos, u);
+        if (lane == l) {
+          L = lw[u * W + p];
+          lat = u * W + p + 1;
+        }
       }
     }
-    lr[e] = L;
+    if (e < Cc * R) {
+      lr[e] = L;
+      rl[e] = lat;
+    }
   }
   __syncthreads();
 
-  // pairwise sparse inner products
-  float* Ag = a.Am + ((int64_t)w * a.chunks + c) * C * C;
-  for (int pi = tid; pi < C * C; pi += 256) {
-    const int t = pi / C, s = pi - t * C;
-    float av = 0.0f, bv = 0.0f;
-    if (t < Cc && s <= t) {
-      const int32_t* ws = iw + s * W;
-      av = merge_sum(ir + t * R, R, ws, W, [&](int p, int q) {
-        return qr[t * R + p] * kw[s * W + q] * expf(lr[t * R + p] - lw[s * W + q]);
-      });
-      if (GDN && s < t)
-        bv = merge_sum(iw + t * W, W, ws, W, [&](int p, int q) {
-          return kw[t * W + p] * kw[s * W + q] * expf(lw[t * W + p] - lw[s * W + q]);
-        });
+  // The tokens' pairwise sparse inner products.  A pair shares a slot exactly when
+  // the reading (or later writing) token's entry links to a writer of the other one,
+  // so each sum runs over the links instead of merging the two full lists: row t of
+  // A over t's read entries in order, each through its slot's writers s <= t (latest
+  // first); row t of B over t's write entries, each through the earlier writers.
+  if (tid < C) {
+    const int t = tid;
+    for (int s = 0; s < C; ++s) Al[t * C + s] = 0.0f;
+    if (t < Cc) {
+      for (int k = 0; k < R; ++k) {
+        int p = rl[t * R + k];
+        if (!p) continue;
+        const float q = a.wt_r[tok(t) * R + k];
+        const float L = lr[t * R + k];
+        while (p) {
+          const int s = (p - 1) / W;
+          Al[t * C + s] += q * kw[p - 1] * expf(L - lw[p - 1]);
+          p = lk[p - 1] & 0xffff;
+        }
+      }
     }
-    Ag[pi] = av;
-    if (GDN) Bm[pi] = bv;
+  } else if (GDN && tid >= 64 && tid < 64 + C) {
+    const int t = tid - 64;
+    for (int s = 0; s < C; ++s) Bm[t * C + s] = 0.0f;
+    if (t < Cc) {
+      for (int k = 0; k < W; ++k) {
+        const int e = t * W + k;
+        int p = lk[e] & 0xffff;
+        if (!p) continue;
+        const float kt = kw[e], L = lw[e];
+        while (p) {
+          const int s = (p - 1) / W;
+          Bm[t * C + s] += kt * kw[p - 1] * expf(L - lw[p - 1]);
+          p = lk[p - 1] & 0xffff;
+        }
+      }
+    }
   }
+  __syncthreads();
+  float* Ag = a.Am + ((int64_t)w * a.chunks + c) * C * C;
+  for (int pi = tid; pi < C * C; pi += 256) Ag[pi] = Al[pi];
 
   if (GDN) {
-    __syncthreads();
     // Tm = (I + diag(beta) B)^-1 diag(beta), row by row; lane m owns column m
     if (tid < C) {
       const int m = tid;
@@ -267,11 +324,12 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(ChunkArgs a) {
 
 size_t walk_lds_bytes(int W, int R) {
   return ((size_t)4 * kChunk * W + 3 * kChunk * R + 2 * kChunk * kChunk) * 4 +
-         (size_t)(2 * kChunk + 64) * (kSlice / 4) * 16;
+         (size_t)(2 * kChunk + kWalkThreads / (kSlice / 4)) * (kSlice / 4) * 16;
 }
 
-// Weighted sum of rows ids[e] (e = e0 + 2 i, i < cnt) of this lane's 4 columns, weight
-// wt[e] exp(L[e]), kBatch rows in flight.
+// Weighted sum of rows ids[e] (e = e0 + GPT i, i < cnt) of this lane's 4 columns,
+// weight wt[e] exp(L[e]), kBatch rows in flight.
+template <int GPT>
 __device__ __forceinline__ float4 gather_sum(const float* Mb, int d_v, const int32_t* ids,
                                              const float* wt, const float* L, int e0, int cnt) {
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -281,7 +339,7 @@ __device__ __forceinline__ float4 gather_sum(const float* Mb, int d_v, const int
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const bool ok = i0 + u < cnt;
-      const int e = ok ? e0 + 2 * (i0 + u) : e0;
+      const int e = ok ? e0 + GPT * (i0 + u) : e0;
       s[u] = ok ? wt[e] * expf(L[e]) : 0.0f;
       m[u] = *reinterpret_cast<const float4*>(Mb + (int64_t)ids[e] * d_v);
     }
@@ -292,11 +350,13 @@ __device__ __forceinline__ float4 gather_sum(const float* Mb, int d_v, const int
 }
 
 template <bool GDN>
-__global__ __launch_bounds__(256) void chunk_walk_kernel(ChunkArgs a) {
+__global__ __launch_bounds__(kWalkThreads) void chunk_walk_kernel(ChunkArgs a) {
   constexpr int C = kChunk;
+  constexpr int NT = kWalkThreads;
   constexpr int LPR = kSlice / 4;  // lanes per row slice (one float4 each)
-  constexpr int G = 256 / LPR;     // lane groups: two per token
-  static_assert(G == 2 * C, "two lane groups per token");
+  constexpr int G = NT / LPR;      // lane groups
+  constexpr int GPT = G / C;       // lane groups per token
+  static_assert(GPT * C == G, "whole lane groups per token");
   extern __shared__ int32_t lds[];
   const int W = a.W, R = a.R;
   int32_t* iw = lds;
@@ -314,7 +374,7 @@ __global__ __launch_bounds__(256) void chunk_walk_kernel(ChunkArgs a) {
 
   const int tid = threadIdx.x;
   const int li = tid % LPR, g = tid / LPR;
-  const int tl = g >> 1, half = g & 1;  // the token and half of its lists this group takes
+  const int tl = g / GPT, sub = g % GPT;  // the token and share of its lists this group takes
   const int64_t walks = a.B * a.H;
   const int64_t w = blockIdx.x % walks;
   const int slice = (int)(blockIdx.x / walks);
@@ -329,22 +389,55 @@ __global__ __launch_bounds__(256) void chunk_walk_kernel(ChunkArgs a) {
     const int Cc = (int)(a.T - t0 < C ? a.T - t0 : C);
     auto tok = [&](int t) { return (b * a.T + t0 + t) * a.H + h; };
     const int64_t cm = ((int64_t)w * a.chunks + c) * C * C;
-    for (int e = tid; e < Cc * W; e += 256) {
-      const int t = e / W, k = e - t * W;
-      const int64_t gi = tok(t) * W + k;
-      iw[e] = a.idx_w[gi];
-      kw[e] = a.wt_w[gi];
-      lw[e] = a.Lw[gi];
-      lk[e] = a.link[gi];
+    // stage the chunk's lists: every load of a round issued before its LDS stores
+    constexpr int kRounds = C * SDM_MAX_COUNT / NT;
+    {
+      int32_t v0[kRounds], v3[kRounds];
+      float v1[kRounds], v2[kRounds];
+#pragma unroll
+      for (int i = 0; i < kRounds; ++i) {
+        const int e = tid + NT * i;
+        if (e < Cc * W) {
+          const int t = e / W, k = e - t * W;
+          const int64_t gi = tok(t) * W + k;
+          v0[i] = a.idx_w[gi];
+          v1[i] = a.wt_w[gi];
+          v2[i] = a.Lw[gi];
+          v3[i] = a.link[gi];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kRounds; ++i) {
+        const int e = tid + NT * i;
+        if (e < Cc * W) {
+          iw[e] = v0[i];
+          kw[e] = v1[i];
+          lw[e] = v2[i];
+          lk[e] = v3[i];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kRounds; ++i) {
+        const int e = tid + NT * i;
+        if (e < Cc * R) {
+          const int t = e / R, k = e - t * R;
+          const int64_t gi = tok(t) * R + k;
+          v0[i] = a.idx_r[gi];
+          v1[i] = a.wt_r[gi];
+          v2[i] = a.Lr[gi];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kRounds; ++i) {
+        const int e = tid + NT * i;
+        if (e < Cc * R) {
+          ir[e] = v0[i];
+          qr[e] = v1[i];
+          lr[e] = v2[i];
+        }
+      }
     }
-    for (int e = tid; e < Cc * R; e += 256) {
-      const int t = e / R, k = e - t * R;
-      const int64_t gi = tok(t) * R + k;
-      ir[e] = a.idx_r[gi];
-      qr[e] = a.wt_r[gi];
-      lr[e] = a.Lr[gi];
-    }
-    for (int pi = tid; pi < C * C; pi += 256) {
+    for (int pi = tid; pi < C * C; pi += NT) {
       Am[pi] = a.Am[cm + pi];
       if (GDN) Tl[pi] = a.Tm[cm + pi];
     }
@@ -353,7 +446,7 @@ __global__ __launch_bounds__(256) void chunk_walk_kernel(ChunkArgs a) {
     // x_t for this slice
     if (GDN) {
       float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (tl < Cc) r = gather_sum(Mb, d_v, iw, kw, lw, tl * W + half, (W - half + 1) / 2);
+      if (tl < Cc) r = gather_sum<GPT>(Mb, d_v, iw, kw, lw, tl * W + sub, (W - sub + GPT - 1) / GPT);
       part[g * LPR + li] = r;
       __syncthreads();
       if (tid < C * LPR) {
@@ -361,7 +454,9 @@ __global__ __launch_bounds__(256) void chunk_walk_kernel(ChunkArgs a) {
         float4 d = make_float4(0.f, 0.f, 0.f, 0.f);
         if (t < Cc) {
           const float4 vv = reinterpret_cast<const float4*>(a.v + tok(t) * d_v + col)[q];
-          const float4 rr = add4(part[(2 * t) * LPR + q], part[(2 * t + 1) * LPR + q]);
+          float4 rr = part[(GPT * t) * LPR + q];
+#pragma unroll
+          for (int u = 1; u < GPT; ++u) rr = add4(rr, part[(GPT * t + u) * LPR + q]);
           d = make_float4(vv.x - rr.x, vv.y - rr.y, vv.z - rr.z, vv.w - rr.w);
         }
         vr[t * LPR + q] = d;
@@ -386,13 +481,15 @@ __global__ __launch_bounds__(256) void chunk_walk_kernel(ChunkArgs a) {
 
     // reads: the chunk-start rows, then the chunk's own writes through A
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (tl < Cc) acc = gather_sum(Mb, d_v, ir, qr, lr, tl * R + half, (R - half + 1) / 2);
+    if (tl < Cc) acc = gather_sum<GPT>(Mb, d_v, ir, qr, lr, tl * R + sub, (R - sub + GPT - 1) / GPT);
     part[g * LPR + li] = acc;
     __syncthreads();  // every read of the chunk-start rows is done past this point
     if (tid < C * LPR) {
       const int t = tid / LPR, q = tid % LPR;
       if (t < Cc) {
-        float4 y = add4(part[(2 * t) * LPR + q], part[(2 * t + 1) * LPR + q]);
+        float4 y = part[(GPT * t) * LPR + q];
+#pragma unroll
+        for (int u = 1; u < GPT; ++u) y = add4(y, part[(GPT * t + u) * LPR + q]);
         for (int s = 0; s <= t; ++s) y = fma4(Am[t * C + s], xs[s * LPR + q], y);
         reinterpret_cast<float4*>(a.y + tok(t) * d_v + col)[q] = y;
       }
@@ -450,7 +547,13 @@ ChunkWs chunk_ws(const sdm_dims& d) {
 
 }  // namespace
 
-bool scan_uses_chunk(const sdm_dims& d) { return (d.flags & SDM_FLAG_SCAN_CHUNK) != 0; }
+// Asked for, or the key-weighted rule on an fp32 state from 256 tokens (where it is
+// several times faster than the direct walk).
+bool scan_uses_chunk(const sdm_dims& d) {
+  if (d.flags & SDM_FLAG_SCAN_CHUNK) return true;
+  return (d.flags & SDM_FLAG_DELTA_GDN) && !(d.flags & (SDM_FLAG_SCAN_DIRECT | SDM_FLAG_STATE_BF16)) &&
+         d.T >= kStreamRound;
+}
 
 size_t chunk_workspace_bytes(const sdm_dims& d) { return chunk_ws(d).total; }
 
@@ -510,12 +613,12 @@ hipError_t launch_chunk_scan(const sdm_dims& d, const ScanArgs& sa, void* ws, hi
       e = hipFuncSetAttribute((const void*)chunk_walk_kernel<true>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(chunk_walk_kernel<true>, grid, dim3(256), lds, st, a);
+      hipLaunchKernelGGL(chunk_walk_kernel<true>, grid, dim3(kWalkThreads), lds, st, a);
     } else {
       e = hipFuncSetAttribute((const void*)chunk_walk_kernel<false>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(chunk_walk_kernel<false>, grid, dim3(256), lds, st, a);
+      hipLaunchKernelGGL(chunk_walk_kernel<false>, grid, dim3(kWalkThreads), lds, st, a);
     }
   }
   e = hipGetLastError();
