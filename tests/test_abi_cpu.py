@@ -307,3 +307,31 @@ def test_select_backward_validates_first(lib):
     assert back(d, ws=FAKE + 8) == _lib.SDM_ERR_ALIGN
     assert back(_d(T=0), x=None, dy=None, ws=None, nb=0) == _lib.SDM_OK
     assert back(_d(H=0)) == _lib.SDM_ERR_SHAPE
+
+
+def test_chunk_schedule_flag(lib):
+    chunk, gdn = _lib.SDM_FLAG_SCAN_CHUNK, _lib.SDM_FLAG_DELTA_GDN
+    d = _d(T=100, flags=chunk)
+    need = lib.sdm_workspace_bytes(ctypes.byref(d), _lib.SDM_ENTRY_SCAN)
+    # per token and head: L and links of the writes, L of the reads, y; per chunk A
+    th = d.B * d.T * d.H
+    assert need >= th * (2 * d.W + d.R + d.d_v) * 4 + d.B * d.H * 4 * 32 * 32 * 4
+    assert lib.sdm_workspace_bytes(ctypes.byref(d), _lib.SDM_ENTRY_FORWARD) > need
+    # the key-weighted rule adds the solve's matrices; it takes the schedule by default
+    # from 256 tokens with an fp32 state, and not with a bf16 one or the direct flag
+    dg = _d(T=100, flags=chunk | gdn)
+    assert lib.sdm_workspace_bytes(ctypes.byref(dg), _lib.SDM_ENTRY_SCAN) > need
+    assert lib.sdm_workspace_bytes(ctypes.byref(_d(T=256, flags=gdn)), _lib.SDM_ENTRY_SCAN) > 0
+    assert lib.sdm_workspace_bytes(ctypes.byref(_d(T=255, flags=gdn)), _lib.SDM_ENTRY_SCAN) == 0
+    for fl in (gdn | _lib.SDM_FLAG_SCAN_DIRECT, gdn | _lib.SDM_FLAG_STATE_BF16):
+        assert lib.sdm_workspace_bytes(ctypes.byref(_d(T=512, flags=fl)), _lib.SDM_ENTRY_SCAN) == 0
+    s = _sel()
+    scan = lambda dd, ws=FAKE, nb=1 << 40: lib.sdm_scan(ctypes.byref(dd), ctypes.byref(s), None,
+                                                        FAKE, FAKE, None, ws, nb, None)
+    assert scan(d, ws=None) == _lib.SDM_ERR_WORKSPACE
+    assert scan(d, nb=need - 1) == _lib.SDM_ERR_WORKSPACE
+    assert scan(_d(T=100, flags=chunk | _lib.SDM_FLAG_STATE_BF16)) == _lib.SDM_ERR_UNSUPPORTED
+    assert scan(_d(T=100, flags=chunk | _lib.SDM_FLAG_SCAN_TWO_PHASE)) == _lib.SDM_ERR_SHAPE
+    # the training entries take the slot-owner and direct schedules only
+    assert lib.sdm_scan_train(ctypes.byref(d), ctypes.byref(s), None, FAKE, FAKE, FAKE, FAKE,
+                              None, FAKE, 1 << 40, None) == _lib.SDM_ERR_UNSUPPORTED
