@@ -13,6 +13,10 @@ fp64 oracle timed on a bounded sample of the same workload on the host).
 step is one T=1 sdm_forward of all 256 sequences, the 64 steps captured in one HIP
 graph and replayed; it reports microseconds per step and slot-row GB/s.
 
+--rule gdn times the key-weighted (Gated DeltaNet form) write rule instead of the
+pages' per-slot rule (its default scan schedule from 256 tokens is the chunkwise one);
+--schedule forces a scan schedule.
+
 --mode train times the training path instead: a step is the selection pass, the
 training forward of the scan (with the fp32 write log), the scan backward (random
 incoming gradients of out and of the final state), which leaves the state at M0
@@ -120,6 +124,11 @@ def parse():
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--workload", default="layer1p4b")
+    p.add_argument("--rule", choices=("slot", "gdn"), default="slot",
+                   help="write rule: the pages' per-slot delta rule, or the key-weighted "
+                        "(Gated DeltaNet form) variant")
+    p.add_argument("--schedule", choices=("default", "direct", "stream", "two_phase", "chunk"),
+                   default="default", help="scan schedule (default: the library's choice)")
     p.add_argument("--state", choices=("fp32", "bf16"), default="fp32",
                    help="state storage: fp32 (the method's precision) or bf16 with fp32 "
                         "arithmetic (SDM_FLAG_STATE_BF16)")
@@ -259,6 +268,12 @@ def main():
     bf16_state = args.state == "bf16"
     if bf16_state:
         d.flags |= _lib.SDM_FLAG_STATE_BF16
+    gdn = args.rule == "gdn"
+    if gdn:
+        d.flags |= _lib.SDM_FLAG_DELTA_GDN
+    d.flags |= {"default": 0, "direct": _lib.SDM_FLAG_SCAN_DIRECT,
+                "stream": _lib.SDM_FLAG_SCAN_STREAM, "two_phase": _lib.SDM_FLAG_SCAN_TWO_PHASE,
+                "chunk": _lib.SDM_FLAG_SCAN_CHUNK}[args.schedule]
 
     # inputs resident in HBM before timing
     _, x_store = synth.gen_x(wl, seed=0)
@@ -320,13 +335,16 @@ def main():
     for name, ms in _lib.timing_read(1 << 16):
         per_kernel.setdefault(name, []).append(ms)
     kernels_ms = {k: {"avg": float(np.mean(v)), "launches": len(v)} for k, v in per_kernel.items()}
-    scan_kernel = next(k for k in ("two_phase_scan", "stream_scan", "scan_direct") if k in kernels_ms)
+    scan_kernel = next(k for k in ("two_phase_scan", "stream_scan", "chunk_walk", "scan_direct")
+                       if k in kernels_ms)
     gemm_kernel = next((k for k in ("proj_gemm_bf16", "proj_gemm_f32") if k in kernels_ms), None)
     # launches per step (the scan can run in token chunks): time per step of that kernel
     scan_ms = kernels_ms[scan_kernel]["avg"] * kernels_ms[scan_kernel]["launches"] / args.steps
 
     tokens = wl.tokens
     slot_bytes = tokens * wl.H * wl.slot_bytes_per_token_head(2 if bf16_state else 4)
+    if gdn:  # the key-weighted prediction reads the W rows once more before the write
+        slot_bytes += tokens * wl.H * wl.W * wl.d_v * (2 if bf16_state else 4)
     achieved = slot_bytes / (scan_ms * 1e-3) / 1e9
     res = {
         "metric": METRIC,
@@ -341,6 +359,7 @@ def main():
         "vs_baseline": None,
         "dtype": ("bf16 projection, fp32 selection/scan, bf16 state storage" if bf16_state
                   else "bf16 projection, fp32 selection/scan"),
+        "rule": args.rule,
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "d_model": wl.d_model, "H": wl.H,
                    "N": wl.N, "n": wl.n, "W": wl.W, "R": wl.R, "d_v": wl.d_v,
@@ -353,7 +372,9 @@ def main():
         "step_frac_of_peak": slot_bytes / (ms_wall * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "roofline": {"bound": "hbm", "kernel": scan_kernel, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None if bf16_state else measured_traffic(wl.name),
+                     "traffic": (measured_traffic(wl.name)
+                                 if not bf16_state and not gdn and scan_kernel == "two_phase_scan"
+                                 else None),
                      "algorithmic_bytes_per_launch":
                          slot_bytes * args.steps / kernels_ms[scan_kernel]["launches"]},
     }
