@@ -126,7 +126,7 @@ def test_chunk_schedule_forward_from_x():
         dd = dims_for(wl)
         dd.flags = _lib.SDM_FLAG_SCAN_DIRECT | extra
         st2 = d["m0"].unsqueeze(0).clone()
-        out2 = ops.scan(dd, prod, d["gamma"], st2)[0]
+        out2 = ops.scan(dd, prod, d["gamma"], st2)
         torch.cuda.synchronize()
         assert_close(host(out), host(out2), f"forward out flags {extra}")
         assert_close(host(st), host(st2), f"forward state flags {extra}")

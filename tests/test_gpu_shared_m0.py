@@ -23,7 +23,7 @@ from oracle import sdm_oracle as O
 pytestmark = pytest.mark.gpu
 
 SCHEDULES = {"direct": _lib.SDM_FLAG_SCAN_DIRECT, "stream": _lib.SDM_FLAG_SCAN_STREAM,
-             "two_phase": _lib.SDM_FLAG_SCAN_TWO_PHASE}
+             "two_phase": _lib.SDM_FLAG_SCAN_TWO_PHASE, "chunk": _lib.SDM_FLAG_SCAN_CHUNK}
 
 
 @pytest.fixture(autouse=True)
@@ -94,7 +94,8 @@ def test_fresh_sequences_match_the_oracle(B, T, H, n, W, R, d_v, mode, schedule)
 @pytest.mark.parametrize("schedule,flags", [
     ("direct", 0), ("stream", 0), ("two_phase", 0), ("direct", _lib.SDM_FLAG_DELTA_GDN),
     ("two_phase", _lib.SDM_FLAG_STATE_BF16), ("direct", _lib.SDM_FLAG_STATE_BF16 |
-                                              _lib.SDM_FLAG_DELTA_GDN)])
+                                              _lib.SDM_FLAG_DELTA_GDN),
+    ("chunk", 0), ("chunk", _lib.SDM_FLAG_DELTA_GDN)])
 def test_equals_the_plain_entry_on_a_broadcast_copy(schedule, flags):
     rng = np.random.default_rng(5)
     B, T, H, n, W, R, d_v = 2, 200, 2, 20, 16, 16, 64
@@ -115,7 +116,7 @@ def test_equals_the_plain_entry_on_a_broadcast_copy(schedule, flags):
     t = torch.from_numpy(_bits(touched, N)).cuda()
     eff = torch.where(t[..., None], store, m0.unsqueeze(0))
     assert torch.equal(eff, plain)
-    if schedule == "direct":   # fixed summation order: identical reads
+    if schedule in ("direct", "chunk"):   # fixed summation order: identical reads
         assert torch.equal(y_s, y_p) and torch.equal(out_s, out_p)
     assert_close(host(y_s), host(y_p), "y", rtol=1e-5, atol=1e-6)
     assert_close(host(out_s), host(out_p), "out", rtol=1e-5, atol=1e-6)
