@@ -196,8 +196,8 @@ __device__ __attribute__((always_inline)) uint32_t select_exact(const float (&fv
                                                                 uint32_t* ti) {
   const int lane = lane_id();
   uint32_t sel = 0, cand = valid;
+  int nc = wave_sum(__popc(cand));
   for (int round = 0; round < 3; ++round) {
-    const int nc = wave_sum(__popc(cand));
     if (nc == need) return sel | cand;
     if (nc <= 32) break;
     float lo = __builtin_inff(), hi = -__builtin_inff();
@@ -212,12 +212,13 @@ __device__ __attribute__((always_inline)) uint32_t select_exact(const float (&fv
     // any positive scale keeps the binning monotone, so the hardware reciprocal will do
     const float scale = 256.0f * __builtin_amdgcn_rcpf(hi - lo);
     if (!(hi > lo) || !(scale > 0.0f) || !(scale < __builtin_inff())) break;
+    // bin = clamp(fv * scale - lo * scale, 0, 255): a correctly rounded fma is monotone
+    // in fv, and the conversion of whatever med3 makes of a NaN stays in [0, 255]
+    const float off = -lo * scale;
     int bin[KPL];
 #pragma unroll
-    for (int q = 0; q < KPL; ++q) {
-      const float f = (fv[q] - lo) * scale;
-      bin[q] = f >= 255.0f ? 255 : (f > 0.0f ? (int)f : 0);  // NaN -> 0
-    }
+    for (int q = 0; q < KPL; ++q)
+      bin[q] = (int)__builtin_amdgcn_fmed3f(fmaf(fv[q], scale, off), 0.0f, 255.0f);
     reinterpret_cast<uint4*>(hist)[lane] = make_uint4(0, 0, 0, 0);
     __syncthreads();
 #pragma unroll
@@ -230,24 +231,29 @@ __device__ __attribute__((always_inline)) uint32_t select_exact(const float (&fv
     const int incl = wave_incl_scan(local);
     const int excl = incl - local;
     const int L = __ffsll((long long)__ballot(incl >= need)) - 1;
-    int bstar = 0, rest = 0;
+    int bstar = 0, rest = 0, inbin = 0;
     if (lane == L) {
       int acc = excl;
-      const int c3 = (int)hv.w, c2 = (int)hv.z, c1 = (int)hv.y;
+      const int c3 = (int)hv.w, c2 = (int)hv.z, c1 = (int)hv.y, c0 = (int)hv.x;
       if (acc + c3 >= need) {
         bstar = 255 - 4 * lane;
+        inbin = c3;
       } else if ((acc += c3) + c2 >= need) {
         bstar = 254 - 4 * lane;
+        inbin = c2;
       } else if ((acc += c2) + c1 >= need) {
         bstar = 253 - 4 * lane;
+        inbin = c1;
       } else {
         acc += c1;
         bstar = 252 - 4 * lane;
+        inbin = c0;
       }
       rest = need - acc;
     }
     bstar = __builtin_amdgcn_readlane(bstar, L);
     need = __builtin_amdgcn_readlane(rest, L);
+    nc = __builtin_amdgcn_readlane(inbin, L);  // the candidates left for the next round
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < KPL; ++q) {
@@ -258,7 +264,6 @@ __device__ __attribute__((always_inline)) uint32_t select_exact(const float (&fv
   }
   // Exact ranking of the remaining candidates.
   const int cl = __popc(cand);
-  const int nc = wave_sum(cl);
   if (nc == need) return sel | cand;
   if (nc <= 64) {
     // compacted into LDS, each ranked by one lane against all of them, the verdicts
