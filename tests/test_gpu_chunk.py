@@ -61,6 +61,8 @@ def _close_dev(got, exp, what):
     (1, 96, 1, 16, 16, 16, 256, "random"),
     (1, 50, 2, 8, 16, 8, 64, "same"),          # every token the same slots
     (3, 31, 1, 4, 16, 16, 32, "random"),       # every slot written by every token, T < 32
+    (1, 70, 1, 12, 128, 128, 256, "repeat"),   # the largest LDS use of both kernels
+    (4, 1, 2, 8, 16, 16, 32, "random"),        # one token per walk
 ])
 def test_chunk_schedule_matches_oracle(rule, B, T, H, n, W, R, d_v, mode):
     rng = np.random.default_rng(B * 1000 + T * 7 + W + (rule == "gdn"))

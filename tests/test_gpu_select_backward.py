@@ -114,6 +114,8 @@ CASES = [
     synth.small("layer1p4b", B=1, T=48, d_model=128, H=3, n=12, W=128, R=100, d_v=64,
                 gate_act=O.GATE_NONE),
     synth.small("layer1p4b", B=1, T=200, d_model=2048, H=2, n=362, W=64, R=64, d_v=128),
+    # the largest counts and half size: 128 entries per role, a 4354-column head row
+    synth.small("layer1p4b", B=1, T=24, d_model=256, H=2, n=1024, W=128, R=128, d_v=128),
 ]
 
 
