@@ -375,10 +375,12 @@ SDM_API int32_t sdm_scan_backward(const sdm_dims* dims, const sdm_sel* in, const
  * normalised scores of the selected slots).  Per (token, head):
  *   ds_k = w_k (dw_k - sum_l w_l dw_l) for the selected slots k (id i_k n + j_k);
  *   dY[half 1, i] = sum_{k: i_k = i} ds_k, dY[half 2, j] = sum_{k: j_k = j} ds_k (per role);
- *   dY[v] = d_v;  dY[gate] = d_gate g (1 - g) (sigmoid) or d_gate (no activation);
+ *   dY[v] = d_v;  dY[gate] = d_gate g (1 - g) (sigmoid), d_gate s (1 + p (1 - s)) with
+ *   s = sigmoid(p) (SiLU, p the gate's pre-activation), or d_gate (no activation);
  *   dY[a] = d_alpha (-A alpha sigmoid(a + b_dt));  dY[b] = d_beta beta (1 - beta);
  *   d_A = sum over tokens of d_alpha (-softplus(a + b_dt) alpha);  d_b_dt = sum of dY[a].
- * The forget pre-gate a is recomputed from x and W_proj in fp32.  The remaining
+ * The forget pre-gate a (and with SiLU the gate's pre-activations) is recomputed from
+ * x and W_proj in fp32.  The remaining
  * gradients are plain GEMMs of dY for the caller: dx = dY W_proj, dW_proj = dY^T x.
  *   fwd      the forward's products: idx_w, wt_w, idx_r, wt_r, alpha, beta, gate
  *            (v and scores unused)
@@ -391,7 +393,7 @@ SDM_API int32_t sdm_scan_backward(const sdm_dims* dims, const sdm_sel* in, const
  *            a | b)
  *   d_A, d_b_dt  [H] fp32 OUT, overwritten (summed over every token of the call)
  *   ws       >= sdm_workspace_bytes(dims, SDM_ENTRY_SELECT_BACKWARD) bytes
- * gate_act SDM_GATE_SILU needs the gate's pre-activation: SDM_ERR_UNSUPPORTED.
+ * Ids must lie in [0, N) (as sdm_select returns them).
  * Deterministic: sums over repeated half indices run in slot order, the other
  * reductions in fixed trees; results are reproducible bit for bit.
  */

@@ -509,7 +509,6 @@ int32_t sdm_select_backward(const sdm_dims* d, const sdm_sel* fwd, const void* x
   Derived dv;
   int32_t st = check_dims(d, &dv);
   if (st != SDM_OK) return st;
-  if (d->gate_act == SDM_GATE_SILU) return SDM_ERR_UNSUPPORTED;
   if (dv.M == 0) return SDM_OK;
   if (!fwd || !g) return SDM_ERR_NULL;
   const void* req[] = {fwd->idx_w, fwd->wt_w, fwd->idx_r, fwd->wt_r, fwd->alpha, fwd->beta,

@@ -9,9 +9,11 @@
 //   ds_k = w_k (dw_k - sum_l w_l dw_l);  dY[h1 i] = sum_{k: i_k = i} ds_k, dY[h2 j] alike;
 //   dY[v] = dv;  dY[g] = dgate act'(g);  dY[a] = dalpha (-A alpha sigmoid(z)), z = a + b_dt;
 //   dY[b] = dbeta beta (1 - beta);  dA += dalpha (-softplus(z) alpha);  db_dt += dY[a].
+// SiLU output gate: dY[g] = dgate sigma(p) (1 + p (1 - sigma(p))) at the pre-activation p.
 // The selected sets are piecewise constant in the scores: no gradient flows through
 // the choice.  The forget pre-gate a is recomputed as x . W_a in fp32 (softplus and
-// sigmoid of it are needed; the stored alpha alone loses them as alpha -> 1).
+// sigmoid of it are needed; the stored alpha alone loses them as alpha -> 1), and so
+// is the SiLU gate's pre-activation (SiLU cannot be inverted from its output).
 // Deterministic: the sums over repeated half indices run in slot order, the
 // reductions over lanes and over tokens in fixed trees.
 #include "sdm_internal.h"
@@ -170,11 +172,32 @@ __global__ __launch_bounds__(64) void select_backward_kernel(SelBackArgs a) {
     a.part[mh * 2 + 1] = dz;
   }
   for (int c = lane; c < n4; c += 64) row[c] = 0.0f;
+  if (a.gate_act == SDM_GATE_SILU) {
+    // SiLU's derivative needs the pre-activation p: recomputed as x . W_g in fp32 and
+    // parked in the gate columns of the row until the gradient replaces it
+    for (int c = 0; c < a.d_v; ++c) {
+      const float pre = dot_row<BF16>(a.x, a.w_proj, m, (int64_t)h * a.P + n4 + a.d_v + c,
+                                      a.d_model);
+      if (lane == 0) row[n4 + a.d_v + c] = pre;
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_wave_barrier();
+  }
   for (int c = lane; c < a.d_v; c += 64) {
     row[n4 + c] = a.g_v[mh * a.d_v + c];
     const float g = a.gate[mh * a.d_v + c];
     const float dg = a.d_gate[mh * a.d_v + c];
-    row[n4 + a.d_v + c] = a.gate_act == SDM_GATE_SIGMOID ? dg * g * (1.0f - g) : dg;
+    float dgp;  // d gate / d pre-activation
+    if (a.gate_act == SDM_GATE_SIGMOID) {
+      dgp = g * (1.0f - g);
+    } else if (a.gate_act == SDM_GATE_SILU) {
+      const float p = row[n4 + a.d_v + c];
+      const float sg = sigmoid_b(p);
+      dgp = sg * (1.0f + p * (1.0f - sg));
+    } else {
+      dgp = 1.0f;
+    }
+    row[n4 + a.d_v + c] = dg * dgp;
   }
   if (lane == 0) {
     row[n4 + 2 * a.d_v] = dz;

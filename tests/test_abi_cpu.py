@@ -291,8 +291,8 @@ def test_select_backward_validates_first(lib):
         lib.sdm_select_backward(ctypes.byref(dd), ctypes.byref(fwd), x, FAKE, FAKE, FAKE,
                                 ctypes.byref(grads), dy, FAKE, FAKE, ws, nb, None)
     d = _d(T=64)
-    # the SiLU gate's derivative needs its pre-activation, which the forward keeps not
-    assert back(_d(T=64, gate_act=_lib.SDM_GATE_SILU)) == _lib.SDM_ERR_UNSUPPORTED
+    # every gate activation is taken (SiLU's pre-activation is recomputed)
+    assert back(_d(T=64, gate_act=_lib.SDM_GATE_SILU), x=None) == _lib.SDM_ERR_NULL
     assert back(d, x=None) == _lib.SDM_ERR_NULL
     assert back(d, dy=None) == _lib.SDM_ERR_NULL
     assert back(d, fwd=_sel(gate=None)) == _lib.SDM_ERR_NULL

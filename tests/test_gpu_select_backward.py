@@ -109,6 +109,9 @@ def _run(wl, d, grads_h, prod=None):
 CASES = [
     synth.WORKLOADS["tiny"],
     synth.small("tiny", gate_act=O.GATE_NONE, B=2, T=37),
+    synth.small("tiny", gate_act=O.GATE_SILU, T=50),
+    synth.small("layer1p4b", B=1, T=40, d_model=512, H=2, n=40, W=16, R=16, d_v=64,
+                gate_act=O.GATE_SILU),
     synth.small("layer1p4b", B=2, T=160, d_model=256, n=40, W=16, R=16, d_v=32),
     # n = 12: 128 of 144 slots written, every half index repeated about ten times
     synth.small("layer1p4b", B=1, T=48, d_model=128, H=3, n=12, W=128, R=100, d_v=64,
@@ -170,15 +173,3 @@ def test_select_backward_full_size_sampled():
     tA, tb = _term_magnitudes(wl, x2, h["w_proj"], h["A"], h["b_dt"], grads["d_alpha"])
     _sums_close(host(dA), eA, tA, "dA")
     _sums_close(host(db), eb, tb, "db_dt")
-
-
-def test_select_backward_empty_and_silu():
-    wl = synth.small("tiny", T=16)
-    h, d = layer_inputs(wl, seed=1, with_state=False)
-    dm = dims_for(wl)
-    prod = ops.select(dm, d["x"], d["w_proj"], d["A"], d["b_dt"])
-    grads = {k: to_dev(v) for k, v in _grads(np.random.default_rng(0), wl).items()}
-    dm.gate_act = O.GATE_SILU
-    with pytest.raises(_lib.SdmError) as e:
-        ops.select_backward(dm, prod, d["x"], d["w_proj"], d["A"], d["b_dt"], grads)
-    assert e.value.code == _lib.SDM_ERR_UNSUPPORTED
