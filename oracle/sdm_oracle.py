@@ -66,6 +66,9 @@ Pins (every function is checked against something other than itself):
   tests/test_oracle_bf16_pins.py       round_bf16 and the bf16-storage scan
   tests/test_oracle_histogram_pins.py  slot_update_counts by brute force
   tests/test_oracle_shared_m0_pins.py  forward_walk_shared against plain walks
+  tests/test_oracle_gdn_backward_pins.py
+                                       scan_backward(rule="gdn") against central
+                                       differences of scan_gdn
   tests/test_oracle_backward_pins.py   scan_backward against central differences
   tests/test_oracle_select_backward_pins.py
                                        pass_a_backward chained after scan_backward
@@ -258,8 +261,9 @@ def scan(state0, idx_w, wt_w, idx_r, wt_r, v, alpha, beta, store=None, record=Fa
 # i.e. the error term subtracts the key-weighted prediction of the whole write
 # set instead of the slot's own value.  Reads are unchanged.
 # ----------------------------------------------------------------------------
-def scan_gdn(state0, idx_w, wt_w, idx_r, wt_r, v, alpha, beta, store=None):
-    """Like scan(), with the key-weighted error term above."""
+def scan_gdn(state0, idx_w, wt_w, idx_r, wt_r, v, alpha, beta, store=None, record=False):
+    """Like scan(), with the key-weighted error term above (record: also the rows each
+    token overwrote, as scan() keeps them)."""
     M = np.array(state0, dtype=F64, copy=True)
     keep = store if store is not None else (lambda z: z)
     assert np.array_equal(keep(M), M), "state0 is not representable in the state's format"
@@ -272,15 +276,18 @@ def scan_gdn(state0, idx_w, wt_w, idx_r, wt_r, v, alpha, beta, store=None):
     beta = np.asarray(beta, F64)
     T = idx_w.shape[0]
     y = np.zeros((T, M.shape[1]), F64)
+    log = np.zeros((T, idx_w.shape[1], M.shape[1]), F64) if record else None
     for t in range(T):
         rows = idx_w[t]
         assert np.unique(rows).size == rows.size, "write slots of one token must be distinct"
+        if record:
+            log[t] = M[rows]
         k = wt_w[t]
         m_tilde = alpha[t] * M[rows]                                   # forget gate
         pred = k @ m_tilde                                             # key-weighted prediction
         M[rows] = keep(m_tilde + (beta[t] * k)[:, None] * (v[t] - pred)[None, :])
         y[t] = wt_r[t] @ M[idx_r[t]]                                   # sparse read
-    return y, M
+    return (y, M, log) if record else (y, M)
 
 
 # ----------------------------------------------------------------------------
@@ -496,17 +503,23 @@ def forward_walk(state0, sel, gamma_h, eps, rule: str = "slot", state: str = "ex
 #   M' = m~ + c (v - m~),  m~ = alpha m:
 #   dM'/dm = alpha (1 - c),  dM'/dv = c,  dM'/dc = v - alpha m,
 #   dM'/dalpha = (1 - c) m,  dc/dbeta = k,  dc/dk = beta.
+# The key-weighted write (scan_gdn), for the write set's rows m_i before the write,
+# m~ = alpha m, e = v - sum_i k_i m~_i, M'_i = m~_i + beta k_i e, and G_i = dL/dM'_i:
+#   de = beta sum_i k_i G_i  (= d_v),   dm~_i = G_i - k_i de,
+#   dk_i = beta <G_i, e> - <de, m~_i>,  dbeta = sum_i k_i <G_i, e>,
+#   dalpha = sum_i <dm~_i, m_i>,        dL/dm_i = alpha dm~_i.
 # For the read y = sum_r q_r M[r]: dq_r = <dy, M[r]>, dM[r] += q_r dy.
 # For out = y s gamma g with s = (mean(y^2) + eps)^(-1/2), u = d_out gamma g:
 #   dy = s (u - yhat mean(u yhat)),  yhat = y s;  d_gate = d_out yhat gamma;
 #   d_gamma = sum over tokens of d_out yhat g.
 # ----------------------------------------------------------------------------
 def scan_backward(state_T, log, idx_w, wt_w, idx_r, wt_r, v, alpha, beta, y, gate,
-                  gamma_h, eps, d_out, d_state):
+                  gamma_h, eps, d_out, d_state, rule: str = "slot"):
     """Gradients of one walk.
 
     state_T [N, d_v] the state after the forward; log [T, W, d_v] from
-    scan(..., record=True); y [T, d_v] the forward's read vectors; d_out [T, d_v]
+    scan(..., record=True) (rule "slot") or scan_gdn(..., record=True) (rule "gdn");
+    y [T, d_v] the forward's read vectors; d_out [T, d_v]
     and d_state [N, d_v] (gradient of the final state) are the incoming gradients.
     Returns (grads, state_0, d_state_0) with grads holding d_v, d_gate [T, d_v],
     d_alpha, d_beta [T], d_wt_w [T, W], d_wt_r [T, R], d_gamma [d_v]; state_0 is the
@@ -535,8 +548,21 @@ def scan_backward(state_T, log, idx_w, wt_w, idx_r, wt_r, v, alpha, beta, y, gat
         dM[rows] += wt_r[t][:, None] * dy[None, :]
         rows = idx_w[t]                                              # step 2, undone
         m = log[t]
-        c = beta[t] * wt_w[t]
         G = dM[rows]
+        if rule == "gdn":
+            k = wt_w[t]
+            mt = alpha[t] * m
+            e = v[t] - k @ mt
+            de = beta[t] * (k @ G)
+            dmt = G - np.outer(k, de)
+            g["d_v"][t] = de
+            g["d_wt_w"][t] = beta[t] * (G @ e) - mt @ de
+            g["d_beta"][t] = k @ (G @ e)
+            g["d_alpha"][t] = np.sum(dmt * m)
+            dM[rows] = alpha[t] * dmt
+            M[rows] = m
+            continue
+        c = beta[t] * wt_w[t]
         g["d_v"][t] = c @ G
         dc = np.sum(G * (v[t][None, :] - alpha[t] * m), axis=1)
         g["d_alpha"][t] = np.sum((1.0 - c)[:, None] * G * m)
