@@ -504,6 +504,9 @@ def train_main(args):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     d = dims_for(wl)
+    gdn = args.rule == "gdn"
+    if gdn:  # the key-weighted rule trains on the direct schedule
+        d.flags |= _lib.SDM_FLAG_DELTA_GDN
     _, x_store = synth.gen_x(wl, seed=0)
     prm = synth.gen_params(wl, seed=0)
     m0 = synth.gen_m0(wl, seed=0)
@@ -579,6 +582,8 @@ def train_main(args):
     # per token and head: M and dM read, dM written per read; log and dM read, dM and M
     # written per write
     back_bytes = tokens * wl.H * (3 * wl.R + 4 * wl.W) * wl.d_v * 4
+    if gdn:  # the key-weighted write reads its rows and their gradients twice
+        back_bytes += tokens * wl.H * 2 * wl.W * wl.d_v * 4
     achieved = back_bytes / (back_ms * 1e-3) / 1e9
     res = {
         "metric": METRIC_TRAIN,
@@ -592,6 +597,7 @@ def train_main(args):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16 projection, fp32 selection/scan/gradients, fp32 write log",
+        "rule": args.rule,
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "d_model": wl.d_model, "H": wl.H,
                    "N": wl.N, "n": wl.n, "W": wl.W, "R": wl.R, "d_v": wl.d_v,

@@ -86,6 +86,8 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
         const float c = be * ww[k];
         char* p = row(iw[k]);
         float4 m = state_load<BF>(p);
+        if constexpr (LOG)  // training forward: the row as it was before this write
+          log_store<LPR>(a.log, a.log_scale, a.log_fmt, tok * a.W + k, DV, m, li);
         m.x = fmaf(c, err.x, al * m.x);
         m.y = fmaf(c, err.y, al * m.y);
         m.z = fmaf(c, err.z, al * m.z);
@@ -169,7 +171,9 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
 
 template <int DV>
 void launch_direct(bool gdn, dim3 grid, hipStream_t s, const ScanArgs& a) {
-  if (a.log)  // training forward: fp32 state, per-slot rule
+  if (a.log && gdn)  // training forward: fp32 state
+    hipLaunchKernelGGL((scan_kernel<DV, true, false, true>), grid, dim3(256), 0, s, a);
+  else if (a.log)
     hipLaunchKernelGGL((scan_kernel<DV, false, false, true>), grid, dim3(256), 0, s, a);
   else if (gdn && a.state_bf16)
     hipLaunchKernelGGL((scan_kernel<DV, true, true, false>), grid, dim3(256), 0, s, a);

@@ -323,11 +323,10 @@ static int32_t log_format(const sdm_dims* d) {
                                                                                    : LOG_F32;
 }
 
-// The training entries take fp32 state and the per-slot rule, on the direct and
-// slot-owner schedules.
+// The training entries take fp32 state: the per-slot rule on the direct and slot-owner
+// schedules, the key-weighted rule on the direct one.
 static int32_t check_train_flags(const sdm_dims* d) {
-  if (d->flags & (SDM_FLAG_STATE_BF16 | SDM_FLAG_DELTA_GDN | SDM_FLAG_SCAN_CHUNK))
-    return SDM_ERR_UNSUPPORTED;
+  if (d->flags & (SDM_FLAG_STATE_BF16 | SDM_FLAG_SCAN_CHUNK)) return SDM_ERR_UNSUPPORTED;
   return SDM_OK;
 }
 
@@ -337,14 +336,17 @@ static sdm_dims train_dims(const sdm_dims* d) {
   const int32_t sched = SDM_FLAG_SCAN_DIRECT | SDM_FLAG_SCAN_STREAM | SDM_FLAG_SCAN_TWO_PHASE;
   sdm_dims dd = *d;
   if (!(d->flags & sched))
-    dd.flags |= d->T >= kStreamRound ? SDM_FLAG_SCAN_TWO_PHASE : SDM_FLAG_SCAN_DIRECT;
+    dd.flags |= d->T >= kStreamRound && !(d->flags & SDM_FLAG_DELTA_GDN)
+                    ? SDM_FLAG_SCAN_TWO_PHASE
+                    : SDM_FLAG_SCAN_DIRECT;
   return dd;
 }
 
 // Backward workspace: per-walk d_gamma partials (direct schedule), or the stream
 // schedule's buckets, dy, per-slice partial dots and per-part d_v.
 static size_t backward_ws_bytes(const sdm_dims* d) {
-  if (backward_uses_stream(*d)) return align_up(stream_backward_workspace_bytes(*d));
+  if (!(d->flags & SDM_FLAG_DELTA_GDN) && backward_uses_stream(*d))
+    return align_up(stream_backward_workspace_bytes(*d));
   return align_up((size_t)d->B * d->H * d->d_v * 4);
 }
 
@@ -495,9 +497,10 @@ int32_t sdm_scan_backward(const sdm_dims* d, const sdm_sel* in, const float* nor
   a.R = d->R;
   a.d_v = d->d_v;
   a.eps = d->eps;
+  a.gdn = (d->flags & SDM_FLAG_DELTA_GDN) != 0;
   TimingScope timing(d);
   (void)hipGetLastError();
-  if (backward_uses_stream(*d))
+  if (!a.gdn && backward_uses_stream(*d))
     return hip_status(launch_stream_backward(*d, a, g->d_norm_w, ws, (hipStream_t)stream));
   return hip_status(launch_scan_backward(a, g->d_norm_w, (hipStream_t)stream));
 }

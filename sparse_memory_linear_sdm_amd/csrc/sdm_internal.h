@@ -305,6 +305,7 @@ struct ScanBackArgs {
   int64_t B, T;
   int32_t H, N, W, R, d_v;
   float eps;
+  bool gdn;             // key-weighted write rule (direct schedule only)
 };
 hipError_t launch_scan_backward(const ScanBackArgs& a, float* d_norm_w, hipStream_t s);
 // The same backward on the slot-owner stream schedule (scan_stream_backward.hip), for

@@ -158,8 +158,14 @@ def test_training_entries_validate_first(lib):
     s = _sel()
     train = lambda dd=d, log=FAKE, y=FAKE, sc=None, ws=FAKE, nb=1 << 40: lib.sdm_scan_train(
         ctypes.byref(dd), ctypes.byref(s), None, FAKE, FAKE, y, log, sc, ws, nb, None)
-    for bad in (_lib.SDM_FLAG_STATE_BF16, _lib.SDM_FLAG_DELTA_GDN):
-        assert train(dd=_d(T=64, flags=bad), sc=FAKE) == _lib.SDM_ERR_UNSUPPORTED
+    assert train(dd=_d(T=64, flags=_lib.SDM_FLAG_STATE_BF16), sc=FAKE) == _lib.SDM_ERR_UNSUPPORTED
+    # the key-weighted rule trains on the direct schedule only
+    gdn = _lib.SDM_FLAG_DELTA_GDN
+    for fl in (_lib.SDM_FLAG_SCAN_STREAM, _lib.SDM_FLAG_SCAN_TWO_PHASE, _lib.SDM_FLAG_SCAN_CHUNK):
+        assert train(dd=_d(T=64, flags=gdn | fl)) == _lib.SDM_ERR_UNSUPPORTED
+    assert train(dd=_d(T=512, flags=gdn), log=None) == _lib.SDM_ERR_NULL
+    assert lib.sdm_workspace_bytes(ctypes.byref(_d(T=512, flags=gdn)),
+                                   _lib.SDM_ENTRY_SCAN_TRAIN) == 0
     # the direct schedule needs no workspace; the stream schedule (an fp32 log from 256
     # tokens, or asked for) takes its buckets from the workspace
     assert lib.sdm_workspace_bytes(ctypes.byref(d), _lib.SDM_ENTRY_SCAN_TRAIN) == 0
@@ -190,7 +196,11 @@ def test_training_entries_validate_first(lib):
     back = lambda dd=d, grads=g, ws=FAKE, nb=1 << 40, sc=None: lib.sdm_scan_backward(
         ctypes.byref(dd), ctypes.byref(s), None, FAKE, FAKE, FAKE, FAKE, sc, FAKE,
         ctypes.byref(grads), ws, nb, None)
-    assert back(dd=_d(T=64, flags=_lib.SDM_FLAG_DELTA_GDN)) == _lib.SDM_ERR_UNSUPPORTED
+    assert back(dd=_d(T=64, flags=_lib.SDM_FLAG_DELTA_GDN), ws=None) == _lib.SDM_ERR_WORKSPACE
+    # its reverse walk is the direct one from any length: per-walk d_gamma partials only
+    dg = _d(T=512, flags=_lib.SDM_FLAG_DELTA_GDN)
+    assert lib.sdm_workspace_bytes(ctypes.byref(dg), _lib.SDM_ENTRY_SCAN_BACKWARD) == \
+        dg.B * dg.H * dg.d_v * 4
     assert back(grads=_lib.SdmScanGrads(*([FAKE] * 5 + [None, None]))) == _lib.SDM_ERR_NULL
     assert back(ws=None) == _lib.SDM_ERR_WORKSPACE
     assert back(dd=_d(T=64, flags=_lib.SDM_FLAG_LOG_INT4)) == _lib.SDM_ERR_NULL
