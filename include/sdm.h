@@ -324,8 +324,10 @@ SDM_API int32_t sdm_forward_noalloc(const sdm_dims* dims, const void* x, const v
  *   after each chunk's walk.  The state, the log and its scales equal those of
  *   sdm_scan and of every schedule bit for bit; y_raw and out equal sdm_scan's on
  *   the same schedule, bit for bit on the direct one and up to fp32 summation order
- *   on the slot-owner ones.  fp32 state and the per-slot rule only:
- *   SDM_FLAG_STATE_BF16 or SDM_FLAG_DELTA_GDN give SDM_ERR_UNSUPPORTED.
+ *   on the slot-owner ones.  fp32 state only (SDM_FLAG_STATE_BF16 gives
+ *   SDM_ERR_UNSUPPORTED).  The key-weighted rule (SDM_FLAG_DELTA_GDN) trains on the
+ *   direct schedule, its default at every length; with SDM_FLAG_SCAN_STREAM,
+ *   _TWO_PHASE or _CHUNK it is SDM_ERR_UNSUPPORTED.
  *
  * sdm_scan_backward: gradients of that call, walking the tokens in reverse (per
  * token: the norm and gate, the read, then the write, whose overwritten rows are
@@ -343,7 +345,11 @@ SDM_API int32_t sdm_forward_noalloc(const sdm_dims* dims, const void* x, const v
  * Schedules: the slot-owner walk from 256 tokens (or with SDM_FLAG_SCAN_STREAM or
  * SDM_FLAG_SCAN_TWO_PHASE, which both select it): slot-owner lane groups walk the
  * accesses of each slot in reverse, any log format;
- * else (or with SDM_FLAG_SCAN_DIRECT) one workgroup per (b, h), tokens in lock-step.
+ * else (or with SDM_FLAG_SCAN_DIRECT, and always for SDM_FLAG_DELTA_GDN) one
+ * workgroup per (b, h), tokens in lock-step.  The key-weighted write is undone in two
+ * passes over the write set: with m the logged rows, m~ = alpha m, e = v - sum k m~,
+ * G = dL/dM rows: d_v = beta sum k G = de, dm~ = G - k de, d_k = beta <G, e> -
+ * <de, m~>, d_beta = sum k <G, e>, d_alpha = sum <dm~, m>, dL/dm = alpha dm~.
  * Every sum runs in a fixed order, so results are bit-reproducible, except d_v on
  * the stream schedule (summed with float atomics: reproducible up to fp32 summation
  * order).  Other flags as for sdm_scan_train.
