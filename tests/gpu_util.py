@@ -191,6 +191,22 @@ def check_bf16_reads(y_got, y_exp, out_got, gamma_h, gate, eps, scale, R, what):
     fp32 = 2 * R * 2.0 ** -24 * scale + 1e-12
     ok = np.all(err <= fp32, axis=-1)
     assert (~ok).mean() <= 0.25, f"{what}: {(~ok).sum()} of {ok.size} tokens beyond the fp32 bound"
-    assert np.all(err <= fp32 + 2 * bf16_spacing(scale)), f"{what}: read beyond the bf16 bound"
+    delta = fp32 + 2 * bf16_spacing(scale)
+    assert np.all(err <= delta), f"{what}: read beyond the bf16 bound"
     assert_close(out_got, O.rms_norm_gate(y_got, gamma_h, gate, eps), f"{what} norm/gate")
+    # out against the oracle's out: with s = (mean(y^2) + eps)^(-1/2) and yhat = y s, the
+    # norm's Jacobian d out_i / d y_j = gamma_i g_i s (delta_ij - yhat_i yhat_j / d_v)
+    # bounds the change from a read error of at most delta per element by
+    # |gamma_i g_i| s delta (1 + |yhat_i| mean_j |yhat_j|); half again for the second
+    # order, plus the fp32 tolerance of the norm itself
+    gate = np.asarray(gate, np.float64)
+    o_exp = O.rms_norm_gate(y_exp, gamma_h, gate, eps)
+    s = 1.0 / np.sqrt(np.mean(y_exp * y_exp, axis=-1, keepdims=True) + eps)
+    yh = np.abs(y_exp) * s
+    lim = (np.abs(np.asarray(gamma_h, np.float64) * gate) * s * delta *
+           (1.0 + yh * np.mean(yh, axis=-1, keepdims=True)))
+    oerr = np.abs(np.asarray(out_got, np.float64) - o_exp)
+    okout = oerr <= 1.5 * lim + RTOL * np.abs(o_exp) + ATOL
+    assert okout.all(), (f"{what}: out beyond the bound from the reads at "
+                         f"{np.argwhere(~okout)[0]}, err {oerr[~okout].max():.3e}")
     return int((~ok).sum())
