@@ -187,13 +187,15 @@ __device__ __forceinline__ bool better(uint64_t ka, uint32_t ia, uint64_t kb, ui
 // bins over their [min, max]; the bins above the one holding the need-th best are taken,
 // the bins below are dropped, and the rest continue.  Whatever remains after three rounds
 // (or once few are left) is ranked exactly.  Binning is monotone, so the result is exact.
-// hist: 256 words of LDS; tk/ti: LDS room for 64 (key, id) pairs.
-template <int KPL, class KeyF>
+// hist: 256 words of LDS; tk/ti: LDS room for 64 (key, id) pairs.  RANGE: lo0 / hi0 are
+// the wave's min / max of the valid elements already (used by the first round).
+template <int KPL, bool RANGE, class KeyF>
 __device__ __attribute__((always_inline)) uint32_t select_exact(const float (&fv)[KPL], KeyF key,
                                                                 const uint32_t (&id)[KPL],
                                                                 uint32_t valid, int need,
                                                                 uint32_t* hist, uint64_t* tk,
-                                                                uint32_t* ti) {
+                                                                uint32_t* ti, float lo0 = 0.0f,
+                                                                float hi0 = 0.0f) {
   const int lane = lane_id();
   uint32_t sel = 0, cand = valid;
   int nc = wave_sum(__popc(cand));
@@ -201,14 +203,19 @@ __device__ __attribute__((always_inline)) uint32_t select_exact(const float (&fv
     if (nc == need) return sel | cand;
     if (nc <= 32) break;
     float lo = __builtin_inff(), hi = -__builtin_inff();
+    if (RANGE && round == 0) {
+      lo = lo0;
+      hi = hi0;
+    } else {
 #pragma unroll
-    for (int q = 0; q < KPL; ++q)
-      if ((cand >> q) & 1u) {
-        lo = fminf(lo, fv[q]);
-        hi = fmaxf(hi, fv[q]);
-      }
-    lo = wave_min(lo);
-    hi = wave_max(hi);
+      for (int q = 0; q < KPL; ++q)
+        if ((cand >> q) & 1u) {
+          lo = fminf(lo, fv[q]);
+          hi = fmaxf(hi, fv[q]);
+        }
+      lo = wave_min(lo);
+      hi = wave_max(hi);
+    }
     // any positive scale keeps the binning monotone, so the hardware reciprocal will do
     const float scale = 256.0f * __builtin_amdgcn_rcpf(hi - lo);
     if (!(hi > lo) || !(scale > 0.0f) || !(scale < __builtin_inff())) break;
@@ -380,9 +387,11 @@ __device__ __attribute__((always_inline)) void bitonic_desc(K (&v)[EPL]) {
 }
 
 // Best k (<= 128) of the n values of one half, by (value desc, index asc).
-// Writes the sorted survivors to val[0..k) / idx[0..k) (LDS).
+// Writes the sorted survivors to val[0..k) / idx[0..k) (LDS).  A half whose values all
+// tie has the closed form indices 0..k-1 (the exact ranking would compare every pair);
+// returns whether that was the case.
 template <int KPL>
-__device__ __attribute__((always_inline)) void half_topk(const float* __restrict__ src, int n, int k, uint32_t* hist,
+__device__ __attribute__((always_inline)) bool half_topk(const float* __restrict__ src, int n, int k, uint32_t* hist,
                           uint64_t* stage, float* val, uint32_t* idx) {
   const int lane = lane_id();
   uint32_t key[KPL];
@@ -400,10 +409,27 @@ __device__ __attribute__((always_inline)) void half_topk(const float* __restrict
     ei[q] = (uint32_t)i;
     valid |= (uint32_t)ok << q;
   }
+  float lo = __builtin_inff(), hi = -__builtin_inff();
+#pragma unroll
+  for (int q = 0; q < KPL; ++q)
+    if ((valid >> q) & 1u) {
+      lo = fminf(lo, fv[q]);
+      hi = fmaxf(hi, fv[q]);
+    }
+  lo = wave_min(lo);
+  hi = wave_max(hi);
+  if (lo == hi) {  // every value ties (an all-zero input row): indices 0..k-1
+    for (int e = lane; e < k; e += 64) {
+      val[e] = lo;
+      idx[e] = (uint32_t)e;
+    }
+    __syncthreads();
+    return true;
+  }
   uint64_t* tk = stage;
   uint32_t* ti = reinterpret_cast<uint32_t*>(stage + 64);
-  const uint32_t sel =
-      select_exact<KPL>(fv, [&](int q) { return ek[q]; }, ei, valid, k, hist, tk, ti);
+  const uint32_t sel = select_exact<KPL, true>(fv, [&](int q) { return ek[q]; }, ei, valid, k,
+                                               hist, tk, ti, lo, hi);
   const int sel_local = __popc(sel);
   int pos = wave_incl_scan(sel_local) - sel_local;
 #pragma unroll
@@ -433,6 +459,7 @@ __device__ __attribute__((always_inline)) void half_topk(const float* __restrict
     }
   }
   __syncthreads();
+  return false;
 }
 
 // Combine the two sorted top-k lists into the best `count` slots; KPC candidates
@@ -463,7 +490,7 @@ __device__ __attribute__((always_inline)) void combine(int n, int k, int count, 
   auto exact = [&](int q) { return (double)fa[q] + (double)fb[q]; };
   uint64_t* tk = stage;
   uint32_t* ti = reinterpret_cast<uint32_t*>(stage + 64);
-  const uint32_t sel = select_exact<KPC>(
+  const uint32_t sel = select_exact<KPC, false>(
       fv, [&](int q) { return ord64(exact(q)); }, id, valid, count, hist, tk, ti);
   // compaction of the `count` survivors as (id, exact score)
   uint32_t* cid = reinterpret_cast<uint32_t*>(stage);
@@ -559,11 +586,19 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(sel_waves(KP
   const int count = role ? R : W;
   const int k = count < n ? count : n;
   const float* half = scores + (r * H + h) * (int64_t)(4 * n) + role * 2 * n;
-  half_topk<KPL>(half, n, k, hist, stage, tv[0], ti[0]);
-  half_topk<KPL>(half + n, n, k, hist, stage, tv[1], ti[1]);
+  const bool flat0 = half_topk<KPL>(half, n, k, hist, stage, tv[0], ti[0]);
+  const bool flat1 = half_topk<KPL>(half + n, n, k, hist, stage, tv[1], ti[1]);
   const int64_t base = ((out_row0 + r) * H + h) * (int64_t)count;
-  combine<KPC>(n, k, count, tv[0], ti[0], tv[1], ti[1], hist, stage,
-               (role ? idx_r : idx_w) + base, (role ? wt_r : wt_w) + base);
+  int32_t* const oi = (role ? idx_r : idx_w) + base;
+  float* const ow = (role ? wt_r : wt_w) + base;
+  if (flat0 && flat1) {  // every slot score ties: slots 0..count-1, equal weights
+    for (int e = lane_id(); e < count; e += 64) {
+      oi[e] = e;
+      ow[e] = 1.0f / (float)count;
+    }
+    return;
+  }
+  combine<KPC>(n, k, count, tv[0], ti[0], tv[1], ti[1], hist, stage, oi, ow);
 }
 
 template <int KPL>

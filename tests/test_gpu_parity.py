@@ -87,6 +87,11 @@ def _scores_case(rng, B, T, H, n, kind):
         return s
     if kind == "wide":        # magnitudes across many binades
         return (rng.standard_normal(shp) * np.exp2(rng.integers(-30, 30, shp))).astype(np.float32)
+    if kind == "flat_half":   # each role's first half constant, its second half not
+        s = rng.standard_normal(shp).astype(np.float32)
+        s[..., 0:n] = 1.25
+        s[..., 2 * n:3 * n] = -0.5
+        return s
     raise ValueError(kind)
 
 
@@ -95,6 +100,8 @@ def _scores_case(rng, B, T, H, n, kind):
     (40, 128, 100, "normal"), (40, 128, 128, "ties"), (8, 64, 20, "normal"),
     (4, 16, 16, "normal"), (16, 1, 1, "ties"), (16, 8, 8, "zeros"), (64, 64, 64, "wide"),
     (1024, 64, 64, "normal"), (1000, 33, 65, "ties"), (1, 1, 1, "normal"),
+    (362, 64, 64, "zeros"), (362, 64, 64, "flat_half"), (40, 128, 100, "flat_half"),
+    (1024, 64, 64, "zeros"),
 ])
 def test_stage_b_selection_bit_exact(n, W, R, kind):
     rng = np.random.default_rng(n * 1000 + W + R)
