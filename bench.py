@@ -335,16 +335,16 @@ def main():
     for name, ms in _lib.timing_read(1 << 16):
         per_kernel.setdefault(name, []).append(ms)
     kernels_ms = {k: {"avg": float(np.mean(v)), "launches": len(v)} for k, v in per_kernel.items()}
-    scan_kernel = next(k for k in ("two_phase_scan", "stream_scan", "chunk_walk", "scan_direct")
-                       if k in kernels_ms)
+    scan_kernel = next(k for k in ("two_phase_scan", "stream_scan", "chunk_walk", "gdn_slices",
+                                   "scan_direct") if k in kernels_ms)
     gemm_kernel = next((k for k in ("proj_gemm_bf16", "proj_gemm_f32") if k in kernels_ms), None)
     # launches per step (the scan can run in token chunks): time per step of that kernel
     scan_ms = kernels_ms[scan_kernel]["avg"] * kernels_ms[scan_kernel]["launches"] / args.steps
 
     tokens = wl.tokens
+    # (2W + R) rows per token and head for either write rule: the key-weighted
+    # prediction and update use the same W row reads
     slot_bytes = tokens * wl.H * wl.slot_bytes_per_token_head(2 if bf16_state else 4)
-    if gdn:  # the key-weighted prediction reads the W rows once more before the write
-        slot_bytes += tokens * wl.H * wl.W * wl.d_v * (2 if bf16_state else 4)
     achieved = slot_bytes / (scan_ms * 1e-3) / 1e9
     res = {
         "metric": METRIC,
@@ -400,6 +400,8 @@ def decode_main(args):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     d1 = dims_for(wl, T=1)
+    if args.rule == "gdn":
+        d1.flags |= _lib.SDM_FLAG_DELTA_GDN
     _, x_store = synth.gen_x(wl, seed=0)
     prm = synth.gen_params(wl, seed=0)
     m0 = synth.gen_m0(wl, seed=0)
@@ -454,7 +456,8 @@ def decode_main(args):
     n_steps = args.steps * wl.T
     us_step = wall * 1e6 / n_steps
     step_bytes = wl.B * wl.H * wl.slot_bytes_per_token_head(4)
-    scan_kernel = next(k for k in ("scan_direct", "two_phase_scan", "stream_scan") if k in kernels_ms)
+    scan_kernel = next(k for k in ("scan_direct", "gdn_slices", "two_phase_scan", "stream_scan")
+                       if k in kernels_ms)
     scan_ms = kernels_ms[scan_kernel]["avg"] * kernels_ms[scan_kernel]["launches"] / wl.T
     achieved = step_bytes / (scan_ms * 1e-3) / 1e9
     gemm_kernel = next((k for k in ("proj_gemm_bf16", "proj_gemm_f32") if k in kernels_ms), None)
@@ -472,6 +475,7 @@ def decode_main(args):
         "vs_baseline": None,
         "dtype": "bf16 projection, fp32 selection/scan",
         "data": "synthetic",
+        "rule": args.rule,
         "config": {"workload": wl.name, "B": wl.B, "T": 1, "decode_steps": wl.T,
                    "d_model": wl.d_model, "H": wl.H, "N": wl.N, "n": wl.n, "W": wl.W, "R": wl.R,
                    "d_v": wl.d_v, "state": "fp32 [B,H,N,d_v]", "tokens_per_step": wl.B,
@@ -576,14 +580,14 @@ def train_main(args):
     kernels_ms = {k: {"avg": float(np.mean(v)), "launches": len(v)} for k, v in per_kernel.items()}
     kernels_ms["proj_grad_gemms_blas"] = {
         "avg": float(np.mean([a.elapsed_time(b) for a, b in gemm_ms])), "launches": len(gemm_ms)}
-    back = next(k for k in ("stream_backward", "scan_backward") if k in kernels_ms)
+    back = next(k for k in ("stream_backward", "gdn_slices_backward", "scan_backward")
+                if k in kernels_ms)
     back_ms = kernels_ms[back]["avg"] * kernels_ms[back]["launches"] / args.steps
     tokens = wl.tokens
     # per token and head: M and dM read, dM written per read; log and dM read, dM and M
     # written per write
+    # (either write rule)
     back_bytes = tokens * wl.H * (3 * wl.R + 4 * wl.W) * wl.d_v * 4
-    if gdn:  # the key-weighted write reads its rows and their gradients twice
-        back_bytes += tokens * wl.H * 2 * wl.W * wl.d_v * 4
     achieved = back_bytes / (back_ms * 1e-3) / 1e9
     res = {
         "metric": METRIC_TRAIN,

@@ -82,6 +82,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run sparse_memory_linear_sdm_amd.build.build()")
+    # torch carries its own HIP runtime.  Loaded first, it is the one the library binds
+    # to; loaded after the library, it would be a second runtime, whose streams the
+    # library's launches reject.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     P, I32, I64, VP = ctypes.POINTER, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
     lib.sdm_abi_version.restype = I32

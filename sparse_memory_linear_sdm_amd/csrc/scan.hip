@@ -9,11 +9,9 @@
 //   out:   y_t / sqrt(mean(y_t^2) + eps) * gamma_h * gate_t
 // Unselected slots are never touched.  The slot ids of every token are known
 // before the scan starts (selection pass), so the kernel only moves rows.
-// Variant (SDM_FLAG_DELTA_GDN): the error term is the key-weighted prediction of
-// the write set, M[i] <- alpha M[i] + beta k_i (v - alpha sum_j k_j M[j]) -- Gated
-// DeltaNet's rule on the selected slots ("与 GDN 的关系" section of
-// ai-paper-analysis.pages.dev).  Storage (SDM_FLAG_STATE_BF16): bf16 state rows,
-// fp32 arithmetic, each stored element rounded to nearest-even bf16.
+// The key-weighted variant (SDM_FLAG_DELTA_GDN) runs its direct schedule in
+// scan_slices.hip.  Storage (SDM_FLAG_STATE_BF16): bf16 state rows, fp32
+// arithmetic, each stored element rounded to nearest-even bf16.
 #include "sdm_internal.h"
 
 namespace sdm {
@@ -28,7 +26,7 @@ __device__ __forceinline__ float4 f4(float a) { return make_float4(a, a, a, a); 
 // waves share the CU's vector L1).
 // LOG: the training forward's write log (a separate instantiation keeps the
 // encoder's registers out of the inference kernel).
-template <int DV, bool GDN, bool BF, bool LOG>
+template <int DV, bool BF, bool LOG>
 __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   constexpr uint32_t ES = StateT<BF>::ES;
   constexpr int BQ = 8;  // rows a group keeps in flight
@@ -57,44 +55,6 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     const float* ww = a.wt_w + tok * a.W;
     const int32_t* ir = a.idx_r + tok * a.R;
     const float* wr = a.wt_r + tok * a.R;
-    if constexpr (GDN) {
-      // key-weighted prediction of the write set from the rows before this
-      // token's writes; row k is read here and written below by the same thread
-      float4 part = f4(0.0f);
-      for (int k = grp; k < a.W; k += G) {
-        const float w = ww[k];
-        const float4 m = state_load<BF>(row(iw[k]));
-        part.x = fmaf(w, m.x, part.x);
-        part.y = fmaf(w, m.y, part.y);
-        part.z = fmaf(w, m.z, part.z);
-        part.w = fmaf(w, m.w, part.w);
-      }
-      __syncthreads();  // group 0 may still be summing the previous token's reads from red
-      red[grp][li] = part;
-      __syncthreads();
-      float4 pred = red[0][li];
-      for (int g = 1; g < G; ++g) {
-        const float4 o = red[g][li];
-        pred.x += o.x;
-        pred.y += o.y;
-        pred.z += o.z;
-        pred.w += o.w;
-      }
-      const float4 err = make_float4(vv.x - al * pred.x, vv.y - al * pred.y, vv.z - al * pred.z,
-                                     vv.w - al * pred.w);
-      for (int k = grp; k < a.W; k += G) {
-        const float c = be * ww[k];
-        char* p = row(iw[k]);
-        float4 m = state_load<BF>(p);
-        if constexpr (LOG)  // training forward: the row as it was before this write
-          log_store<LPR>(a.log, a.log_scale, a.log_fmt, tok * a.W + k, DV, m, li);
-        m.x = fmaf(c, err.x, al * m.x);
-        m.y = fmaf(c, err.y, al * m.y);
-        m.z = fmaf(c, err.z, al * m.z);
-        m.w = fmaf(c, err.w, al * m.w);
-        state_store<BF>(reinterpret_cast<uint64_t>(p), state_round<BF>(m));
-      }
-    } else
     // A token's write ids are distinct, so a group's rows never alias: their loads
     // are all issued before the first store (BQ rows in flight per lane).
     for (int k0 = grp; k0 < a.W; k0 += G * BQ) {
@@ -170,19 +130,13 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
 }
 
 template <int DV>
-void launch_direct(bool gdn, dim3 grid, hipStream_t s, const ScanArgs& a) {
-  if (a.log && gdn)  // training forward: fp32 state
-    hipLaunchKernelGGL((scan_kernel<DV, true, false, true>), grid, dim3(256), 0, s, a);
-  else if (a.log)
-    hipLaunchKernelGGL((scan_kernel<DV, false, false, true>), grid, dim3(256), 0, s, a);
-  else if (gdn && a.state_bf16)
-    hipLaunchKernelGGL((scan_kernel<DV, true, true, false>), grid, dim3(256), 0, s, a);
-  else if (gdn)
-    hipLaunchKernelGGL((scan_kernel<DV, true, false, false>), grid, dim3(256), 0, s, a);
+void launch_direct(dim3 grid, hipStream_t s, const ScanArgs& a) {
+  if (a.log)  // training forward: fp32 state
+    hipLaunchKernelGGL((scan_kernel<DV, false, true>), grid, dim3(256), 0, s, a);
   else if (a.state_bf16)
-    hipLaunchKernelGGL((scan_kernel<DV, false, true, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((scan_kernel<DV, true, false>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((scan_kernel<DV, false, false, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((scan_kernel<DV, false, false>), grid, dim3(256), 0, s, a);
 }
 
 }  // namespace
@@ -201,6 +155,7 @@ static int64_t stage_bytes(const sdm_dims& d, bool quantised_log) {
 
 size_t scan_workspace_bytes(const sdm_dims& d, bool train) {
   if (!train && scan_uses_chunk(d)) return chunk_workspace_bytes(d);
+  if (d.flags & SDM_FLAG_DELTA_GDN) return gdn_slice_workspace_bytes(d, train);
   if (!scan_uses_stream(d)) return 0;
   const bool q = train && (d.flags & (SDM_FLAG_LOG_FP8 | SDM_FLAG_LOG_INT4));
   return stream_workspace_bytes(d, plan_stream(d, (int64_t)d.n * d.n, stage_bytes(d, q)));
@@ -211,15 +166,15 @@ hipError_t launch_scan(const sdm_dims& d, const ScanArgs& a, void* ws, size_t, h
   if (scan_uses_stream(d))
     return launch_stream_scan(
         a, plan_stream(d, a.N, stage_bytes(d, a.log != nullptr && a.log_fmt != LOG_F32)), ws, s);
+  if (d.flags & SDM_FLAG_DELTA_GDN) return launch_gdn_slices(d, a, ws, s);
   const dim3 grid((unsigned)(a.B * a.H));
   KernelTimer kt("scan_direct", s);
-  const bool gdn = (d.flags & SDM_FLAG_DELTA_GDN) != 0;
   switch (a.d_v) {
-    case 16: launch_direct<16>(gdn, grid, s, a); break;
-    case 32: launch_direct<32>(gdn, grid, s, a); break;
-    case 64: launch_direct<64>(gdn, grid, s, a); break;
-    case 128: launch_direct<128>(gdn, grid, s, a); break;
-    case 256: launch_direct<256>(gdn, grid, s, a); break;
+    case 16: launch_direct<16>(grid, s, a); break;
+    case 32: launch_direct<32>(grid, s, a); break;
+    case 64: launch_direct<64>(grid, s, a); break;
+    case 128: launch_direct<128>(grid, s, a); break;
+    case 256: launch_direct<256>(grid, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -13,12 +13,7 @@
 //   write:      with m the logged row, c = beta k, G = dM[i]:
 //               d_v += c G,  dc = <G, v - alpha m>,  d_alpha += (1 - c) <G, m>,
 //               d_k = beta dc,  d_beta += k dc,  dM[i] = alpha (1 - c) G,  M[i] = m
-// Key-weighted rule (SDM_FLAG_DELTA_GDN), per token over its write set, m the logged
-// rows, m~ = alpha m, e = v - sum_i k_i m~_i, G_i = dM[i]:
-//               de = beta sum_i k_i G_i = d_v,  dm~_i = G_i - k_i de,
-//               d_k_i = beta <G_i, e> - <de, m~_i>,  d_beta = sum_i k_i <G_i, e>,
-//               d_alpha = sum_i <dm~_i, m_i>,  dM[i] = alpha dm~_i,  M[i] = m_i
-// (two passes over the write set: the key-weighted sums first, then the rows).
+// The key-weighted rule (SDM_FLAG_DELTA_GDN) has its reverse walk in scan_slices.hip.
 // The state comes back as M_0 bit for bit and dM as the gradient of M_0.
 //
 // One workgroup of 256 threads per walk, laid out like the direct forward: LPR =
@@ -45,13 +40,12 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-template <int DV, bool GDN>
+template <int DV>
 __global__ __launch_bounds__(256) void scan_backward_kernel(ScanBackArgs a) {
   constexpr int LPR = DV / 4;
   constexpr int G = 256 / LPR;
   constexpr int BQ = 8;           // rows a group keeps in flight
-  __shared__ float4 red[G][LPR];  // per-group partial d_v of the token (GDN: sum k m)
-  __shared__ float4 red2[GDN ? G : 1][LPR];  // GDN: per-group partial sum k G
+  __shared__ float4 red[G][LPR];  // per-group partial d_v of the token
   __shared__ float2 sab[G];       // per-group partial (d_alpha, d_beta)
 
   const int tid = threadIdx.x;
@@ -126,100 +120,6 @@ __global__ __launch_bounds__(256) void scan_backward_kernel(ScanBackArgs a) {
     const float4 vv = reinterpret_cast<const float4*>(a.v + tok * DV)[li];
     const int32_t* iw = a.idx_w + tok * a.W;
     const float* ww = a.wt_w + tok * a.W;
-    if constexpr (GDN) {
-      // pass 1: sum_i k_i m_i and sum_i k_i G_i over this group's rows
-      float4 pk = f4s(0.0f), sg = f4s(0.0f);
-      for (int k0 = grp; k0 < a.W; k0 += G * BQ) {
-        float4 ms[BQ], gs[BQ];
-#pragma unroll
-        for (int j = 0; j < BQ; ++j) {
-          const int k = k0 + j * G;
-          const int kk = k < a.W ? k : k0;
-          ms[j] = log_load(a.log, a.log_scale, a.log_fmt, tok * a.W + kk, DV, li);
-          gs[j] = reinterpret_cast<const float4*>(dM + (int64_t)iw[kk] * DV)[li];
-        }
-#pragma unroll
-        for (int j = 0; j < BQ; ++j) {
-          const int k = k0 + j * G;
-          if (k >= a.W) break;
-          const float kw = ww[k];
-          pk.x = fmaf(kw, ms[j].x, pk.x);
-          pk.y = fmaf(kw, ms[j].y, pk.y);
-          pk.z = fmaf(kw, ms[j].z, pk.z);
-          pk.w = fmaf(kw, ms[j].w, pk.w);
-          sg.x = fmaf(kw, gs[j].x, sg.x);
-          sg.y = fmaf(kw, gs[j].y, sg.y);
-          sg.z = fmaf(kw, gs[j].z, sg.z);
-          sg.w = fmaf(kw, gs[j].w, sg.w);
-        }
-      }
-      red[grp][li] = pk;
-      red2[grp][li] = sg;
-      __syncthreads();
-      // every group forms the same totals, in group order
-      float4 P = red[0][li], S = red2[0][li];
-      for (int q = 1; q < G; ++q) {
-        const float4 o = red[q][li], o2 = red2[q][li];
-        P.x += o.x;
-        P.y += o.y;
-        P.z += o.z;
-        P.w += o.w;
-        S.x += o2.x;
-        S.y += o2.y;
-        S.z += o2.z;
-        S.w += o2.w;
-      }
-      const float4 e = make_float4(vv.x - al * P.x, vv.y - al * P.y, vv.z - al * P.z,
-                                   vv.w - al * P.w);
-      const float4 de = make_float4(be * S.x, be * S.y, be * S.z, be * S.w);
-      // pass 2: each group's own rows again (no other group touches them)
-      float da = 0.0f, db = 0.0f;
-      for (int k0 = grp; k0 < a.W; k0 += G * BQ) {
-        int64_t rows[BQ];
-        float4 ms[BQ], gs[BQ];
-#pragma unroll
-        for (int j = 0; j < BQ; ++j) {
-          const int k = k0 + j * G;
-          const int kk = k < a.W ? k : k0;
-          rows[j] = iw[kk];
-          ms[j] = log_load(a.log, a.log_scale, a.log_fmt, tok * a.W + kk, DV, li);
-          gs[j] = reinterpret_cast<const float4*>(dM + rows[j] * DV)[li];
-        }
-#pragma unroll
-        for (int j = 0; j < BQ; ++j) {
-          const int k = k0 + j * G;
-          if (k >= a.W) break;
-          const float kw = ww[k];
-          const float4 m = ms[j], g = gs[j];
-          const float4 dmt = make_float4(g.x - kw * de.x, g.y - kw * de.y, g.z - kw * de.z,
-                                         g.w - kw * de.w);
-          const float ge = group_sum<LPR>(dot4(g, e));
-          const float dem = group_sum<LPR>(dot4(de, m));
-          da += group_sum<LPR>(dot4(dmt, m));
-          db += kw * ge;
-          if (li == 0) a.g_wt_w[tok * a.W + k] = be * ge - al * dem;
-          reinterpret_cast<float4*>(dM + rows[j] * DV)[li] =
-              make_float4(al * dmt.x, al * dmt.y, al * dmt.z, al * dmt.w);
-          reinterpret_cast<float4*>(M + rows[j] * DV)[li] = m;
-        }
-      }
-      if (li == 0) sab[grp] = make_float2(da, db);
-      __syncthreads();
-      if (grp == 0) {
-        float2 ab = sab[0];
-        for (int q = 1; q < G; ++q) {
-          ab.x += sab[q].x;
-          ab.y += sab[q].y;
-        }
-        reinterpret_cast<float4*>(a.g_v + tok * DV)[li] = de;
-        if (li == 0) {
-          a.g_alpha[tok] = ab.x;
-          a.g_beta[tok] = ab.y;
-        }
-      }
-      __syncthreads();  // red / sab reuse, and the next token's reads see this restore
-      continue;
-    }
     float4 dv = f4s(0.0f);
     float da = 0.0f, db = 0.0f;
     for (int k0 = grp; k0 < a.W; k0 += G * BQ) {
@@ -307,11 +207,8 @@ hipError_t launch_scan_backward(const ScanBackArgs& a, float* d_norm_w, hipStrea
   {
     KernelTimer kt("scan_backward", s);
     switch (a.d_v) {
-#define SDM_BACK(DVV)                                                                        \
-  if (a.gdn)                                                                                  \
-    hipLaunchKernelGGL((scan_backward_kernel<DVV, true>), grid, dim3(256), 0, s, a);          \
-  else                                                                                        \
-    hipLaunchKernelGGL((scan_backward_kernel<DVV, false>), grid, dim3(256), 0, s, a);
+#define SDM_BACK(DVV) \
+  hipLaunchKernelGGL((scan_backward_kernel<DVV>), grid, dim3(256), 0, s, a);
       case 16: SDM_BACK(16) break;
       case 32: SDM_BACK(32) break;
       case 64: SDM_BACK(64) break;

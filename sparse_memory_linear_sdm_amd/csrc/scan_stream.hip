@@ -1187,6 +1187,29 @@ hipError_t launch_stream_scan(const ScanArgs& sa, const StreamPlan& pl, void* ws
 }
 
 
+hipError_t launch_log_quantize(const ScanArgs& sa, const float* stage, int64_t t0, int64_t Tc,
+                               hipStream_t st) {
+  StreamArgs a = {};
+  a.log = const_cast<float*>(stage);
+  a.log_T = Tc;
+  a.T = sa.T;
+  a.t0 = t0;
+  a.Tc = Tc;
+  a.H = sa.H;
+  a.W = sa.W;
+  const dim3 grid((unsigned)(sa.B * Tc * sa.H));
+  KernelTimer kt("log_quantize", st);
+  switch (sa.d_v) {
+    case 16: hipLaunchKernelGGL(log_quantize_kernel<16>, grid, dim3(256), 0, st, a, sa); break;
+    case 32: hipLaunchKernelGGL(log_quantize_kernel<32>, grid, dim3(256), 0, st, a, sa); break;
+    case 64: hipLaunchKernelGGL(log_quantize_kernel<64>, grid, dim3(256), 0, st, a, sa); break;
+    case 128: hipLaunchKernelGGL(log_quantize_kernel<128>, grid, dim3(256), 0, st, a, sa); break;
+    case 256: hipLaunchKernelGGL(log_quantize_kernel<256>, grid, dim3(256), 0, st, a, sa); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_norm_gate(const ScanArgs& sa, const float* y, hipStream_t st) {
   StreamArgs a = {};
   a.gate = sa.gate;

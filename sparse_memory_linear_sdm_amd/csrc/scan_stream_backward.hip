@@ -538,6 +538,39 @@ BackLayout back_layout(const sdm_dims& d, const BackPlan& pl) {
 
 }  // namespace
 
+int norm_backward_blocks(int64_t T) { return (int)((T + PREP_TOK - 1) / PREP_TOK); }
+
+hipError_t launch_norm_backward(const ScanBackArgs& sa, float* dy, float* gpart, hipStream_t st) {
+  BackStreamArgs A{};
+  A.s = sa;
+  A.dy = dy;
+  A.gpart = gpart;
+  A.t0 = 0;
+  A.Tc = sa.T;
+  A.gblocks = norm_backward_blocks(sa.T);
+  A.pblocks = A.gblocks;
+  const dim3 grid((unsigned)(sa.B * (int64_t)sa.H * A.pblocks));
+  KernelTimer kt("back_prep", st);
+  switch (sa.d_v) {
+    case 16: hipLaunchKernelGGL(back_prep_kernel<16>, grid, dim3(256), 0, st, A); break;
+    case 32: hipLaunchKernelGGL(back_prep_kernel<32>, grid, dim3(256), 0, st, A); break;
+    case 64: hipLaunchKernelGGL(back_prep_kernel<64>, grid, dim3(256), 0, st, A); break;
+    case 128: hipLaunchKernelGGL(back_prep_kernel<128>, grid, dim3(256), 0, st, A); break;
+    case 256: hipLaunchKernelGGL(back_prep_kernel<256>, grid, dim3(256), 0, st, A); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gamma_blocks(const ScanBackArgs& sa, const float* gpart, float* d_norm_w,
+                               hipStream_t st) {
+  const int64_t n = (int64_t)sa.H * sa.d_v;
+  KernelTimer kt("gamma_sum", st);
+  hipLaunchKernelGGL(gamma_blocks_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                     gpart, sa.B, sa.H, sa.d_v, norm_backward_blocks(sa.T), d_norm_w);
+  return hipGetLastError();
+}
+
 // The backward has one slot-owner schedule: SDM_FLAG_SCAN_STREAM and
 // SDM_FLAG_SCAN_TWO_PHASE both select it.
 bool backward_uses_stream(const sdm_dims& d) {

@@ -345,7 +345,8 @@ static sdm_dims train_dims(const sdm_dims* d) {
 // Backward workspace: per-walk d_gamma partials (direct schedule), or the stream
 // schedule's buckets, dy, per-slice partial dots and per-part d_v.
 static size_t backward_ws_bytes(const sdm_dims* d) {
-  if (!(d->flags & SDM_FLAG_DELTA_GDN) && backward_uses_stream(*d))
+  if (d->flags & SDM_FLAG_DELTA_GDN) return align_up(gdn_slice_backward_workspace_bytes(*d));
+  if (backward_uses_stream(*d))
     return align_up(stream_backward_workspace_bytes(*d));
   return align_up((size_t)d->B * d->H * d->d_v * 4);
 }
@@ -497,10 +498,11 @@ int32_t sdm_scan_backward(const sdm_dims* d, const sdm_sel* in, const float* nor
   a.R = d->R;
   a.d_v = d->d_v;
   a.eps = d->eps;
-  a.gdn = (d->flags & SDM_FLAG_DELTA_GDN) != 0;
   TimingScope timing(d);
   (void)hipGetLastError();
-  if (!a.gdn && backward_uses_stream(*d))
+  if (d->flags & SDM_FLAG_DELTA_GDN)
+    return hip_status(launch_gdn_slice_backward(*d, a, g->d_norm_w, ws, (hipStream_t)stream));
+  if (backward_uses_stream(*d))
     return hip_status(launch_stream_backward(*d, a, g->d_norm_w, ws, (hipStream_t)stream));
   return hip_status(launch_scan_backward(a, g->d_norm_w, (hipStream_t)stream));
 }

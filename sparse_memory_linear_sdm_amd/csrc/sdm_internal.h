@@ -194,6 +194,16 @@ bool scan_uses_chunk(const sdm_dims& d);
 size_t chunk_workspace_bytes(const sdm_dims& d);
 hipError_t launch_chunk_scan(const sdm_dims& d, const ScanArgs& a, void* ws, hipStream_t st);
 
+// Direct schedule of the key-weighted rule, split over column slices of the state
+// (scan_slices.hip): the inference walk, the training forward (any log format) and
+// its backward.
+int gdn_slices(const sdm_dims& d);
+size_t gdn_slice_workspace_bytes(const sdm_dims& d, bool train);
+hipError_t launch_gdn_slices(const sdm_dims& d, const ScanArgs& a, void* ws, hipStream_t st);
+// Encodes a token chunk's fp32 log rows, staged [B][Tc][H][W][d_v], into a.log.
+hipError_t launch_log_quantize(const ScanArgs& a, const float* stage, int64_t t0, int64_t Tc,
+                               hipStream_t st);
+
 // Write-log storage (training): one row of d_v values per write, fp32, or quantised
 // with one absmax per row -- fp8 (OCP E4M3, v = x * 448 / absmax) or int4 (v = x * 7 /
 // absmax, codes -7..7, two per byte, low nibble first).  Codes are decided in fp32.
@@ -305,9 +315,17 @@ struct ScanBackArgs {
   int64_t B, T;
   int32_t H, N, W, R, d_v;
   float eps;
-  bool gdn;             // key-weighted write rule (direct schedule only)
 };
 hipError_t launch_scan_backward(const ScanBackArgs& a, float* d_norm_w, hipStream_t s);
+size_t gdn_slice_backward_workspace_bytes(const sdm_dims& d);
+hipError_t launch_gdn_slice_backward(const sdm_dims& d, const ScanBackArgs& a, float* d_norm_w,
+                                     void* ws, hipStream_t st);
+// Norm/gate backward of all tokens (scan_stream_backward.hip): dy [B, T, H, d_v],
+// d_gate, and d_gamma partials [B*H][norm_backward_blocks(T)][d_v]; then their sum.
+int norm_backward_blocks(int64_t T);
+hipError_t launch_norm_backward(const ScanBackArgs& a, float* dy, float* gpart, hipStream_t st);
+hipError_t launch_gamma_blocks(const ScanBackArgs& a, const float* gpart, float* d_norm_w,
+                               hipStream_t st);
 // The same backward on the slot-owner stream schedule (scan_stream_backward.hip), for
 // long token runs; needs stream_backward_workspace_bytes(d) of workspace.
 bool backward_uses_stream(const sdm_dims& d);

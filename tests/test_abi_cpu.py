@@ -197,10 +197,21 @@ def test_training_entries_validate_first(lib):
         ctypes.byref(dd), ctypes.byref(s), None, FAKE, FAKE, FAKE, FAKE, sc, FAKE,
         ctypes.byref(grads), ws, nb, None)
     assert back(dd=_d(T=64, flags=_lib.SDM_FLAG_DELTA_GDN), ws=None) == _lib.SDM_ERR_WORKSPACE
-    # its reverse walk is the direct one from any length: per-walk d_gamma partials only
+    # its reverse walk is the sliced direct one from any length: dy and every slice's
+    # share of the dot products (one slice at d_v = 16) come from the workspace
     dg = _d(T=512, flags=_lib.SDM_FLAG_DELTA_GDN)
-    assert lib.sdm_workspace_bytes(ctypes.byref(dg), _lib.SDM_ENTRY_SCAN_BACKWARD) == \
-        dg.B * dg.H * dg.d_v * 4
+    ng = lib.sdm_workspace_bytes(ctypes.byref(dg), _lib.SDM_ENTRY_SCAN_BACKWARD)
+    assert ng >= dg.B * dg.T * dg.H * (dg.d_v * 4 + dg.R * 4 + dg.W * 8 + 4)
+    assert back(dd=dg, nb=ng - 1) == _lib.SDM_ERR_WORKSPACE
+    # 8 slices of 16 columns for 2 x 2 walks of d_v = 128: 8 shares per dot product
+    dg8 = _d(T=64, d_v=128, flags=_lib.SDM_FLAG_DELTA_GDN)
+    ng8 = lib.sdm_workspace_bytes(ctypes.byref(dg8), _lib.SDM_ENTRY_SCAN_BACKWARD)
+    assert ng8 >= dg8.B * dg8.T * dg8.H * (128 * 4 + 8 * (dg8.R * 4 + dg8.W * 8 + 4))
+    # its inference walk keeps the raw read vectors for the norm pass (8 slices)
+    assert lib.sdm_workspace_bytes(ctypes.byref(dg8), _lib.SDM_ENTRY_SCAN) >= \
+        dg8.B * dg8.T * dg8.H * 128 * 4
+    assert lib.sdm_workspace_bytes(ctypes.byref(_d(T=64, flags=_lib.SDM_FLAG_DELTA_GDN)),
+                                   _lib.SDM_ENTRY_SCAN) == 0
     assert back(grads=_lib.SdmScanGrads(*([FAKE] * 5 + [None, None]))) == _lib.SDM_ERR_NULL
     assert back(ws=None) == _lib.SDM_ERR_WORKSPACE
     assert back(dd=_d(T=64, flags=_lib.SDM_FLAG_LOG_INT4)) == _lib.SDM_ERR_NULL

@@ -1,5 +1,7 @@
 """Training of the key-weighted (GDN-form) write rule: sdm_scan_train and
-sdm_scan_backward with SDM_FLAG_DELTA_GDN (direct schedule) against the oracle.
+sdm_scan_backward with SDM_FLAG_DELTA_GDN (direct schedule, split over column slices
+of the state) against the oracle.  The cases cover both slice widths (16 and 32
+columns), one slice per walk (norm and gate inside the walk) and several.
 
 * The training forward gives state, y and out bit-identical to the inference scan of
   the same rule on the direct schedule, and its write log equals the oracle's
@@ -57,6 +59,11 @@ CASES = [
     (1, 30, 1, 16, 16, 16, 256, "same", 0),
     (1, 64, 2, 16, 16, 16, 32, "random", _lib.SDM_FLAG_LOG_FP8),
     (1, 64, 1, 16, 16, 16, 64, "repeat", _lib.SDM_FLAG_LOG_INT4),
+    (16, 6, 4, 8, 16, 16, 128, "random", 0),   # 64 walks: 4 slices of 32 columns
+    (32, 5, 4, 8, 16, 24, 128, "random", 0),   # 128 walks: 32-column slices (the cap)
+    (64, 3, 4, 8, 16, 16, 128, "random", 0),   # 256 walks: 32-column slices (the cap)
+    (64, 3, 4, 8, 16, 16, 64, "repeat", _lib.SDM_FLAG_LOG_FP8),
+    (64, 3, 4, 8, 16, 16, 32, "random", 0),    # one 32-column slice: norm in the walk
 ]
 
 
@@ -130,3 +137,29 @@ def test_gdn_training_refuses_slot_owner_and_chunk_schedules():
         with pytest.raises(_lib.SdmError) as e:
             ops.scan_train(_dims(T=64, flags=GDN | fl), pd, None, st)
         assert e.value.code == _lib.SDM_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "int4"])
+def test_gdn_quantised_log_over_staged_token_chunks(fmt):
+    """A quantised log is staged in fp32 per token chunk of at most 256 MiB and
+    encoded after each chunk's walk: 4 x 300 tokens x 4 heads x W = 128 x d_v = 128
+    takes two chunks.  The codes equal the oracle's encoding of the fp32 log of the
+    same walk, and state, y and out equal the fp32-log run bit for bit."""
+    rng = np.random.default_rng(11)
+    B, T, H, n, W, R, d_v = 4, 300, 4, 16, 128, 64, 128
+    prod = random_products(rng, B, T, H, n, W, R, d_v, "random")
+    m0 = (rng.standard_normal((B, H, n * n, d_v)) * 0.3).astype(np.float32)
+    flag = _lib.SDM_FLAG_LOG_FP8 if fmt == "fp8" else _lib.SDM_FLAG_LOG_INT4
+    pd = {k: to_dev(v) for k, v in prod.items()}
+    st_a, st_b = to_dev(m0), to_dev(m0)
+    out_a, y_a, log_a = ops.scan_train(_dims(B=B, T=T, H=H, n=n, W=W, R=R, d_v=d_v, flags=GDN),
+                                       pd, None, st_a)
+    out_b, y_b, log_b = ops.scan_train(
+        _dims(B=B, T=T, H=H, n=n, W=W, R=R, d_v=d_v, flags=GDN | flag), pd, None, st_b)
+    torch.cuda.synchronize()
+    assert torch.equal(st_a, st_b) and torch.equal(y_a, y_b) and torch.equal(out_a, out_b)
+    rows = host(log_a["rows"])
+    del log_a
+    codes, amax = O.quantize_rows(rows, fmt)
+    assert np.array_equal(host(log_b["scale"]), amax)
+    assert np.array_equal(host(log_b["rows"]), codes)
