@@ -99,9 +99,11 @@ extern "C" {
    pages say the layer reduces to when every slot is selected with a dense key:
    ai-paper-analysis.pages.dev, section "与 GDN 的关系"; m.163.com article on
    arXiv 2607.07386, section 二).  It needs every row of a token's write set before
-   any is written, so it runs the direct schedule or the chunk schedule
-   (SDM_FLAG_SCAN_CHUNK, its default from 256 tokens with an fp32 state); combined
-   with SDM_FLAG_SCAN_STREAM or SDM_FLAG_SCAN_TWO_PHASE it is SDM_ERR_UNSUPPORTED. */
+   any is written, so it runs the direct schedule (each walk split over 16- or
+   32-column slices of the state, which evolve independently under the rule) or the
+   chunk schedule (SDM_FLAG_SCAN_CHUNK, its default from 256 tokens with an fp32
+   state); combined with SDM_FLAG_SCAN_STREAM or SDM_FLAG_SCAN_TWO_PHASE it is
+   SDM_ERR_UNSUPPORTED. */
 #define SDM_FLAG_DELTA_GDN 16
 /* storage flag (sdm_dims.flags; sdm_scan and sdm_forward): the state buffer holds
    bf16 values.  The arithmetic stays fp32; each written row element is rounded to
@@ -319,9 +321,10 @@ SDM_API int32_t sdm_forward_noalloc(const sdm_dims* dims, const void* x, const v
  *           if 0)
  *   Schedules: a schedule flag picks one (SDM_FLAG_SCAN_DIRECT, _STREAM or
  *   _TWO_PHASE); without one, the two-phase schedule from 256 tokens and the direct
- *   one below.  On the slot-owner (stream, two-phase) schedules a quantised log is
- *   staged in fp32 in the workspace (token chunks bounded near 2 GiB) and encoded
- *   after each chunk's walk.  The state, the log and its scales equal those of
+ *   one below.  On the slot-owner (stream, two-phase) schedules, and for the
+ *   key-weighted rule, a quantised log is staged in fp32 in the workspace (token
+ *   chunks bounded near 2 GiB, and 256 MiB) and encoded after each chunk's walk.
+ *   The state, the log and its scales equal those of
  *   sdm_scan and of every schedule bit for bit; y_raw and out equal sdm_scan's on
  *   the same schedule, bit for bit on the direct one and up to fp32 summation order
  *   on the slot-owner ones.  fp32 state only (SDM_FLAG_STATE_BF16 gives
@@ -345,11 +348,13 @@ SDM_API int32_t sdm_forward_noalloc(const sdm_dims* dims, const void* x, const v
  * Schedules: the slot-owner walk from 256 tokens (or with SDM_FLAG_SCAN_STREAM or
  * SDM_FLAG_SCAN_TWO_PHASE, which both select it): slot-owner lane groups walk the
  * accesses of each slot in reverse, any log format;
- * else (or with SDM_FLAG_SCAN_DIRECT, and always for SDM_FLAG_DELTA_GDN) one
- * workgroup per (b, h), tokens in lock-step.  The key-weighted write is undone in two
- * passes over the write set: with m the logged rows, m~ = alpha m, e = v - sum k m~,
- * G = dL/dM rows: d_v = beta sum k G = de, dm~ = G - k de, d_k = beta <G, e> -
- * <de, m~>, d_beta = sum k <G, e>, d_alpha = sum <dm~, m>, dL/dm = alpha dm~.
+ * else (or with SDM_FLAG_SCAN_DIRECT) one workgroup per (b, h), tokens in
+ * lock-step.  The key-weighted rule (SDM_FLAG_DELTA_GDN) always walks directly, one
+ * workgroup per (b, h, column slice) as its forward; its write is undone per token
+ * with m the logged rows, m~ = alpha m, e = v - sum k m~, G = dL/dM rows:
+ * d_v = beta sum k G = de, dm~ = G - k de, d_k = beta <G, e> - <de, m~>,
+ * d_beta = sum k <G, e>, d_alpha = sum <dm~, m>, dL/dm = alpha dm~ (the dot products
+ * over d_v summed from per-slice shares in slice order).
  * Every sum runs in a fixed order, so results are bit-reproducible, except d_v on
  * the stream schedule (summed with float atomics: reproducible up to fp32 summation
  * order).  Other flags as for sdm_scan_train.
