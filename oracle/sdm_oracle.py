@@ -64,6 +64,9 @@ Pins (every function is checked against something other than itself):
   tests/test_oracle_mutations.py       planted mistakes, each caught by a pin
   tests/test_oracle_gdn_pins.py        scan_gdn against a dense matrix recurrence
   tests/test_oracle_bf16_pins.py       round_bf16 and the bf16-storage scan
+  tests/test_oracle_fp8_state_pins.py  the fp8 state format (block exponent, E4M3
+                                       rounding against torch's float8_e4m3fn, a
+                                       hand-worked row) and the fp8-storage scan
   tests/test_oracle_histogram_pins.py  slot_update_counts by brute force
   tests/test_oracle_shared_m0_pins.py  forward_walk_shared against plain walks
   tests/test_oracle_gdn_backward_pins.py
@@ -410,6 +413,62 @@ def round_bf16(x):
     return np.where(np.isfinite(x), q, x)
 
 
+# fp8 state storage (also not a step of the pages; the same caveat as bf16).  Each
+# row of d_v values is cut into blocks of 32 columns; a block keeps one power-of-two
+# scale 2^e (an E8M0 byte, s = e + 127) and each element an OCP E4M3 value c, the
+# element being c 2^e.  e is the least integer >= -127 with absmax <= 448 2^e, so
+# x 2^-e is exact and never beyond E4M3's largest value 448; c is the E4M3 value
+# nearest to x 2^-e (ties to the even significand).  Rounded once from the exact
+# value, as round_bf16.
+# ----------------------------------------------------------------------------
+FP8_BLOCK = 32
+
+
+def fp8_block_exponent(amax):
+    """Least integer e >= -127 with amax <= 448 * 2^e (amax >= 0)."""
+    a = np.asarray(amax, F64)
+    m, k = np.frexp(a)                        # a = m 2^k, 0.5 <= m < 1 (m = 0 for a = 0)
+    e = (k - 1) - 8 + (2.0 * m > 1.75)        # a = (2m) 2^(k-1): 1.75 2^8 = 448
+    return np.where(a > 0, np.maximum(e, -127), -127).astype(np.int64)
+
+
+def round_e4m3(x):
+    """Nearest OCP E4M3 value of each element (|x| <= 448), ties to even, as fp64.
+    E4M3: 3 fraction bits, exponents -6 to 8, subnormals spaced 2^-9."""
+    x = np.asarray(x, F64)
+    a = np.abs(x)
+    _, k = np.frexp(np.where(a > 0, a, 1.0))   # a in [2^(k-1), 2^k)
+    step = np.ldexp(1.0, np.maximum(k - 1, -6) - 3)
+    q = np.rint(a / step) * step               # a / step is exact (a power-of-two step)
+    assert np.all(q <= 448.0), "beyond E4M3's range"
+    return np.copysign(q, x)
+
+
+def round_fp8_blocks(x):
+    """Rows [..., d] (d a multiple of 32) as the fp8 state stores them, fp64."""
+    x = np.asarray(x, F64)
+    blk = x.reshape(x.shape[:-1] + (x.shape[-1] // FP8_BLOCK, FP8_BLOCK))
+    e = fp8_block_exponent(np.max(np.abs(blk), axis=-1))[..., None]
+    return (round_e4m3(np.ldexp(blk, -e)) * np.ldexp(1.0, e)).reshape(x.shape)
+
+
+def fp8_state_encode(x):
+    """Rows [..., d] -> (E4M3 codes [..., d] uint8, E8M0 exponents [..., d/32] uint8)
+    of round_fp8_blocks(x)."""
+    x = np.asarray(x, F64)
+    blk = x.reshape(x.shape[:-1] + (x.shape[-1] // FP8_BLOCK, FP8_BLOCK))
+    e = fp8_block_exponent(np.max(np.abs(blk), axis=-1))
+    c = round_e4m3(np.ldexp(blk, -e[..., None])).astype(np.float32)
+    return e4m3_encode(c).reshape(x.shape), (e + 127).astype(np.uint8)
+
+
+def fp8_state_decode(codes, exps):
+    codes = np.asarray(codes, np.uint8)
+    e = np.asarray(exps, np.int64) - 127
+    c = e4m3_decode(codes).reshape(codes.shape[:-1] + (codes.shape[-1] // FP8_BLOCK, FP8_BLOCK))
+    return (c * np.ldexp(1.0, e)[..., None]).reshape(codes.shape)
+
+
 # ----------------------------------------------------------------------------
 # Slot-update histogram: the collapse monitor of the papers.ananclaw.com summary
 # (engineering-risks section, risk 3 "寻址坍缩"): how often each slot of each
@@ -481,11 +540,12 @@ def forward_walk(state0, sel, gamma_h, eps, rule: str = "slot", state: str = "ex
     sel holds [T, *] arrays for that walk: idx_w, wt_w, idx_r, wt_r, v, g,
     alpha, beta.  rule "slot" is the pages' per-slot error term (scan), "gdn"
     the key-weighted one (scan_gdn).  state "exact" keeps the state in fp64,
-    "bf16" stores every written row rounded to bf16.  Returns (out [T, d_v],
+    "bf16" stores every written row rounded to bf16, "fp8" in 32-column blocks of
+    E4M3 values with a power-of-two scale (round_fp8_blocks).  Returns (out [T, d_v],
     y_raw [T, d_v], final state).
     """
     walk = {"slot": scan, "gdn": scan_gdn}[rule]
-    store = {"exact": None, "bf16": round_bf16}[state]
+    store = {"exact": None, "bf16": round_bf16, "fp8": round_fp8_blocks}[state]
     y, M = walk(state0, sel["idx_w"], sel["wt_w"], sel["idx_r"], sel["wt_r"],
                 sel["v"], sel["alpha"], sel["beta"], store=store)
     return rms_norm_gate(y, gamma_h, sel["g"], eps), y, M
