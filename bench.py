@@ -129,9 +129,10 @@ def parse():
                         "(Gated DeltaNet form) variant")
     p.add_argument("--schedule", choices=("default", "direct", "stream", "two_phase", "chunk"),
                    default="default", help="scan schedule (default: the library's choice)")
-    p.add_argument("--state", choices=("fp32", "bf16"), default="fp32",
-                   help="state storage: fp32 (the method's precision) or bf16 with fp32 "
-                        "arithmetic (SDM_FLAG_STATE_BF16)")
+    p.add_argument("--state", choices=("fp32", "bf16", "fp8"), default="fp32",
+                   help="state storage: fp32 (the method's precision), bf16 with fp32 "
+                        "arithmetic (SDM_FLAG_STATE_BF16), or fp8 E4M3 with a power-of-two "
+                        "exponent per 32-column block (SDM_FLAG_STATE_FP8)")
     p.add_argument("--mode", choices=("forward", "train"), default="forward")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-tokens-per-core", type=int, default=2048,
@@ -266,8 +267,11 @@ def main():
     torch.cuda.set_device(dev)
     d = dims_for(wl)
     bf16_state = args.state == "bf16"
+    fp8_state = args.state == "fp8"
     if bf16_state:
         d.flags |= _lib.SDM_FLAG_STATE_BF16
+    if fp8_state:
+        d.flags |= _lib.SDM_FLAG_STATE_FP8
     gdn = args.rule == "gdn"
     if gdn:
         d.flags |= _lib.SDM_FLAG_DELTA_GDN
@@ -292,6 +296,8 @@ def main():
     if bf16_state:
         m0_d = m0_d.to(torch.bfloat16)
     state = m0_d.unsqueeze(0).repeat(wl.B, *([1] * m0_d.dim()))  # a copy, also for B = 1
+    if fp8_state:
+        state = fp8_state_buffer(state)
     del m0
     prod = ops.alloc_products(d, dev)
     out = torch.empty((wl.B, wl.T, wl.H, wl.d_v), device=dev)
@@ -345,6 +351,8 @@ def main():
     # (2W + R) rows per token and head for either write rule: the key-weighted
     # prediction and update use the same W row reads
     slot_bytes = tokens * wl.H * wl.slot_bytes_per_token_head(2 if bf16_state else 4)
+    if fp8_state:  # a byte per element plus a block exponent byte per 32 columns
+        slot_bytes = tokens * wl.H * (2 * wl.W + wl.R) * wl.d_v * 33 // 32
     achieved = slot_bytes / (scan_ms * 1e-3) / 1e9
     res = {
         "metric": METRIC,
@@ -358,6 +366,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": ("bf16 projection, fp32 selection/scan, bf16 state storage" if bf16_state
+                  else "bf16 projection, fp32 selection/scan, fp8 (E4M3, 32-column block "
+                       "exponents) state storage" if fp8_state
                   else "bf16 projection, fp32 selection/scan"),
         "rule": args.rule,
         "data": "synthetic",
@@ -373,8 +383,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": scan_kernel, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": (measured_traffic(wl.name)
-                                 if not bf16_state and not gdn and scan_kernel == "two_phase_scan"
-                                 else None),
+                                 if args.state == "fp32" and not gdn and
+                                 scan_kernel == "two_phase_scan" else None),
                      "algorithmic_bytes_per_launch":
                          slot_bytes * args.steps / kernels_ms[scan_kernel]["launches"]},
     }
@@ -489,6 +499,20 @@ def decode_main(args):
                      "traffic": None, "algorithmic_bytes_per_launch": step_bytes},
     }
     print(json.dumps(res), flush=True)
+
+
+def fp8_state_buffer(m):
+    """[B, H, N, d_v] fp32 -> the SDM_FLAG_STATE_FP8 buffer of the nearest stored
+    values: E4M3 codes (torch's float8_e4m3fn conversion of x 2^-e, exact scaling),
+    then per 32-column block the E8M0 byte of e, the least e >= -127 with
+    absmax <= 448 2^e."""
+    import torch
+    blk = m.reshape(*m.shape[:-1], m.shape[-1] // 32, 32)
+    mant, k = torch.frexp(blk.abs().amax(-1))
+    e = (k - 1) - 8 + (2 * mant > 1.75).to(k.dtype)
+    e = torch.where(mant > 0, e.clamp(min=-127), torch.full_like(e, -127))
+    codes = torch.ldexp(blk, (-e).unsqueeze(-1).to(blk.dtype)).to(torch.float8_e4m3fn)
+    return torch.cat([codes.view(torch.uint8).reshape(-1), (e + 127).to(torch.uint8).reshape(-1)])
 
 
 def dataclass_replace(wl, **kw):

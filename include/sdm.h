@@ -114,6 +114,20 @@ extern "C" {
    ai-paper-analysis.pages.dev, section "训练效率"; m.163.com article on arXiv
    2607.07386, section 八).  Every schedule and both write rules support it. */
 #define SDM_FLAG_STATE_BF16 32
+/* storage flag (sdm_dims.flags; sdm_scan and sdm_forward): the state buffer holds
+   fp8, B*H*N*d_v*33/32 bytes -- a codes plane [B, H, N, d_v] of OCP E4M3 bytes (the
+   encoding of SDM_FLAG_LOG_FP8's codes), then an exponent plane [B, H, N, d_v / 32]
+   of E8M0 bytes, one per 32-column block of a row.  Element = value(code) *
+   2^(s - 127).  The arithmetic stays fp32; each written row is requantised block by
+   block: e = the least exponent >= -127 with absmax <= 448 * 2^e (read off the fp32
+   absmax's bits: its exponent - 8, plus 1 when its significand exceeds 1.75), then
+   each element's nearest E4M3 value of x * 2^-e (ties to even; the scaling is exact
+   and never saturates).  About a quarter of the fp32 bytes per slot access.  Not a
+   step of the pages (see SDM_FLAG_STATE_BF16).  The per-slot rule on the two-phase
+   and direct schedules with d_v >= 32; SDM_ERR_UNSUPPORTED with SDM_FLAG_DELTA_GDN,
+   SDM_FLAG_SCAN_STREAM or SDM_FLAG_SCAN_CHUNK, d_v < 32, and in the training and
+   shared-M0 entries; SDM_ERR_SHAPE with SDM_FLAG_STATE_BF16. */
+#define SDM_FLAG_STATE_FP8 512
 /* write-log format flags (sdm_dims.flags; sdm_scan_train / sdm_scan_backward only,
    at most one): the training checkpoints quantised as the pages do for long
    fine-tuning (fp8 or int4: m.163.com article on arXiv 2607.07386, section 八;
@@ -258,7 +272,8 @@ SDM_API int32_t sdm_select_from_scores(const sdm_dims* dims, const float* scores
  * Slots never selected for writing are never written (bit-identical on return).
  *   in      pass-(a) products (every field but `scores` required)
  *   norm_w  [H, d_v] fp32 RMSNorm weight, or NULL for ones
- *   state   [B, H, N, d_v] fp32 (bf16 with SDM_FLAG_STATE_BF16), IN/OUT: M_0 on entry
+ *   state   [B, H, N, d_v] fp32 (bf16 with SDM_FLAG_STATE_BF16; fp8 planes with
+ *           SDM_FLAG_STATE_FP8), IN/OUT: M_0 on entry
  *           (e.g. a learned initial state,
  *           [analysis] section on M0), M_T on return.  Calling with T tokens equals
  *           calling on consecutive token chunks with the same state buffer.

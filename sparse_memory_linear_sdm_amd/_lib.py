@@ -26,6 +26,7 @@ SDM_FLAG_SCAN_DIRECT, SDM_FLAG_SCAN_STREAM, SDM_FLAG_SCAN_TWO_PHASE = 1, 2, 4
 SDM_FLAG_TIMING = 8
 SDM_FLAG_DELTA_GDN = 16
 SDM_FLAG_STATE_BF16 = 32
+SDM_FLAG_STATE_FP8 = 512
 SDM_FLAG_LOG_FP8, SDM_FLAG_LOG_INT4 = 64, 128
 SDM_FLAG_SCAN_CHUNK = 256
 

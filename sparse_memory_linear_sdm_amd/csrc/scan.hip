@@ -11,7 +11,9 @@
 // before the scan starts (selection pass), so the kernel only moves rows.
 // The key-weighted variant (SDM_FLAG_DELTA_GDN) runs its direct schedule in
 // scan_slices.hip.  Storage (SDM_FLAG_STATE_BF16): bf16 state rows, fp32
-// arithmetic, each stored element rounded to nearest-even bf16.
+// arithmetic, each stored element rounded to nearest-even bf16.  SDM_FLAG_STATE_FP8:
+// E4M3 codes with one power-of-two exponent per 32-column block (fp8_quantize), each
+// written row's blocks requantised after the update.
 #include "sdm_internal.h"
 
 namespace sdm {
@@ -25,10 +27,12 @@ __device__ __forceinline__ float4 f4(float a) { return make_float4(a, a, a, a); 
 // and the next token's writes (all accesses stay inside one workgroup, whose
 // waves share the CU's vector L1).
 // LOG: the training forward's write log (a separate instantiation keeps the
-// encoder's registers out of the inference kernel).
-template <int DV, bool BF, bool LOG>
+// encoder's registers out of the inference kernel).  F8: fp8 state (codes plane,
+// then one exponent byte per 32-column block of a row; DV >= 32).
+template <int DV, bool BF, bool LOG, bool F8 = false>
 __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
-  constexpr uint32_t ES = StateT<BF>::ES;
+  static_assert(!(F8 && (BF || LOG || DV < 32)), "fp8 state: inference, 32-column blocks");
+  constexpr uint32_t ES = F8 ? 1u : StateT<BF>::ES;
   constexpr int BQ = 8;  // rows a group keeps in flight
   constexpr int LPR = DV / 4;
   constexpr int G = 256 / LPR;
@@ -43,6 +47,16 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
   // row r, this lane's 4 columns
   char* const Mb = static_cast<char*>(a.state) + bh * (int64_t)a.N * DV * ES + li * 4 * ES;
   auto row = [&](int64_t r) { return Mb + r * (DV * ES); };
+  // F8: this lane's block exponent of row r at Eb + r * (DV / 32)
+  uint8_t* const Eb = F8 ? static_cast<uint8_t*>(a.state) + a.B * a.H * (int64_t)a.N * DV +
+                               bh * (int64_t)a.N * (DV / 32) + li / 8
+                         : nullptr;
+  auto load_row = [&](int64_t r) {
+    if constexpr (F8)
+      return fp8_decode4(*reinterpret_cast<const uint32_t*>(row(r)), Eb[r * (DV / 32)]);
+    else
+      return state_load<BF>(row(r));
+  };
   const float4 gam = a.norm_w ? reinterpret_cast<const float4*>(a.norm_w + (int64_t)h * DV)[li]
                               : f4(1.0f);
 
@@ -59,14 +73,21 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     // are all issued before the first store (BQ rows in flight per lane).
     for (int k0 = grp; k0 < a.W; k0 += G * BQ) {
       char* p[BQ];
+      int64_t rid[BQ];
       float4 m[BQ];
 #pragma unroll
       for (int j = 0; j < BQ; ++j) {
         const int k = k0 + j * G;
-        p[j] = row(iw[k < a.W ? k : k0]);
+        rid[j] = iw[k < a.W ? k : k0];
+        p[j] = row(rid[j]);
       }
 #pragma unroll
-      for (int j = 0; j < BQ; ++j) m[j] = state_load<BF>(p[j]);
+      for (int j = 0; j < BQ; ++j) {
+        if constexpr (F8)
+          m[j] = fp8_decode4(*reinterpret_cast<const uint32_t*>(p[j]), Eb[rid[j] * (DV / 32)]);
+        else
+          m[j] = state_load<BF>(p[j]);
+      }
 #pragma unroll
       for (int j = 0; j < BQ; ++j) {
         const int k = k0 + j * G;
@@ -80,7 +101,13 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
         n.y = fmaf(c, vv.y, oc * (al * m[j].y));
         n.z = fmaf(c, vv.z, oc * (al * m[j].z));
         n.w = fmaf(c, vv.w, oc * (al * m[j].w));
-        state_store<BF>(reinterpret_cast<uint64_t>(p[j]), state_round<BF>(n));
+        if constexpr (F8) {
+          const Fp8Row q = fp8_quantize(n);
+          *reinterpret_cast<uint32_t*>(p[j]) = q.codes;
+          if ((li & 7) == 0) Eb[rid[j] * (DV / 32)] = (uint8_t)q.s;
+        } else {
+          state_store<BF>(reinterpret_cast<uint64_t>(p[j]), state_round<BF>(n));
+        }
       }
     }
     __syncthreads();
@@ -90,7 +117,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
 #pragma unroll
       for (int j = 0; j < BQ; ++j) {
         const int k = k0 + j * G;
-        m[j] = state_load<BF>(row(ir[k < a.R ? k : k0]));
+        m[j] = load_row(ir[k < a.R ? k : k0]);
       }
 #pragma unroll
       for (int j = 0; j < BQ; ++j) {
@@ -130,13 +157,18 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
 }
 
 template <int DV>
-void launch_direct(dim3 grid, hipStream_t s, const ScanArgs& a) {
+hipError_t launch_direct(dim3 grid, hipStream_t s, const ScanArgs& a) {
   if (a.log)  // training forward: fp32 state
     hipLaunchKernelGGL((scan_kernel<DV, false, true>), grid, dim3(256), 0, s, a);
+  else if (a.state_fp8 && DV < 32)  // blocks of 32 columns (refused at the entry)
+    return hipErrorInvalidValue;
+  else if (a.state_fp8)
+    hipLaunchKernelGGL((scan_kernel<DV, false, false, (DV >= 32)>), grid, dim3(256), 0, s, a);
   else if (a.state_bf16)
     hipLaunchKernelGGL((scan_kernel<DV, true, false>), grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((scan_kernel<DV, false, false>), grid, dim3(256), 0, s, a);
+  return hipSuccess;
 }
 
 }  // namespace
@@ -169,15 +201,16 @@ hipError_t launch_scan(const sdm_dims& d, const ScanArgs& a, void* ws, size_t, h
   if (d.flags & SDM_FLAG_DELTA_GDN) return launch_gdn_slices(d, a, ws, s);
   const dim3 grid((unsigned)(a.B * a.H));
   KernelTimer kt("scan_direct", s);
+  hipError_t e;
   switch (a.d_v) {
-    case 16: launch_direct<16>(grid, s, a); break;
-    case 32: launch_direct<32>(grid, s, a); break;
-    case 64: launch_direct<64>(grid, s, a); break;
-    case 128: launch_direct<128>(grid, s, a); break;
-    case 256: launch_direct<256>(grid, s, a); break;
+    case 16: e = launch_direct<16>(grid, s, a); break;
+    case 32: e = launch_direct<32>(grid, s, a); break;
+    case 64: e = launch_direct<64>(grid, s, a); break;
+    case 128: e = launch_direct<128>(grid, s, a); break;
+    case 256: e = launch_direct<256>(grid, s, a); break;
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  return e != hipSuccess ? e : hipGetLastError();
 }
 
 }  // namespace sdm

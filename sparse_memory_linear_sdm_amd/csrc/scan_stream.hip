@@ -612,10 +612,12 @@ __global__ __launch_bounds__(64) void bucket_scatter_rev_kernel(StreamArgs a) {
 //                round's writes come after the reads).  Parts never touch each
 //                other's slots, so they need no synchronisation with one another.
 // ---------------------------------------------------------------------------
-template <int NT, int SW, int BQ, int BR, bool BF, bool TRAIN>
+// F8: fp8 state (codes plane, then one exponent byte per 32-column block; SW >= 32).
+template <int NT, int SW, int BQ, int BR, bool BF, bool TRAIN, bool F8 = false>
 __global__ __launch_bounds__(NT) void two_phase_scan_kernel(StreamArgs a) {
   static_assert(!(TRAIN && BF), "the write log is kept for fp32 state");
-  constexpr uint32_t ES = StateT<BF>::ES;
+  static_assert(!(F8 && (BF || TRAIN || SW < 32)), "fp8 state: inference, 32-column blocks");
+  constexpr uint32_t ES = F8 ? 1u : StateT<BF>::ES;
   constexpr int LPG = SW / 4;
   constexpr int GW = NT / LPG;
   constexpr int EPL = (BQ + LPG - 1) / LPG;
@@ -643,6 +645,18 @@ __global__ __launch_bounds__(NT) void two_phase_scan_kernel(StreamArgs a) {
   char* Mb = static_cast<char*>(a.state) + w * (int64_t)a.N * dv * ES;
   const uint32_t col_bytes = (uint32_t)(sl * SW + li * 4) * ES;
   const uint32_t row_bytes = (uint32_t)dv * ES;
+  // F8: this lane's block exponent of row r at Eb + r * erow
+  uint8_t* const Eb = F8 ? static_cast<uint8_t*>(a.state) + a.B * a.H * (int64_t)a.N * dv +
+                               w * (int64_t)a.N * (dv / 32) + (sl * SW + li * 4) / 32
+                         : nullptr;
+  const uint32_t erow = (uint32_t)dv / 32;
+  auto load_row = [&](uint32_t r) {
+    if constexpr (F8)
+      return fp8_decode4(*reinterpret_cast<const uint32_t*>(Mb + (r * row_bytes + col_bytes)),
+                         Eb[r * erow]);
+    else
+      return state_load<BF>(Mb + (r * row_bytes + col_bytes));
+  };
   const uint2* ent = a.entries + w * a.walk_entries;
   const int* offs = a.offsets + ((int64_t)w * a.GT + gg) * (a.rounds + 1);
   const int* begs = a.begins + ((int64_t)w * a.GT + gg) * a.rounds;
@@ -702,8 +716,7 @@ __global__ __launch_bounds__(NT) void two_phase_scan_kernel(StreamArgs a) {
         wrm |= (uint32_t)(valid && !(ey >> 31)) << j;
       }
 #pragma unroll
-      for (int j = 0; j < BQ; ++j)
-        mv[j] = state_load<BF>(Mb + (slot[j] * row_bytes + col_bytes));
+      for (int j = 0; j < BQ; ++j) mv[j] = load_row(slot[j]);
 #pragma unroll
       for (int j = 0; j < BQ; ++j) {
         float4 val = mv[j];
@@ -736,11 +749,22 @@ __global__ __launch_bounds__(NT) void two_phase_scan_kernel(StreamArgs a) {
           val.y = isw ? nv.y : val.y;
           val.z = isw ? nv.z : val.z;
           val.w = isw ? nv.w : val.w;
-          val = state_round<BF>(val);  // the stored value (exact for non-writes)
           uint64_t dst = isw ? reinterpret_cast<uint64_t>(Mb + (slot[j] * row_bytes + col_bytes))
                              : reinterpret_cast<uint64_t>(trash);
-          asm volatile("" : "+v"(dst));  // keep one unconditional store: hide the select
-          state_store<BF>(dst, val);
+          if constexpr (F8) {  // requantised (values of non-writes unchanged)
+            const Fp8Row q = fp8_quantize(val);
+            val = q.val;
+            uint64_t edst = isw ? reinterpret_cast<uint64_t>(Eb + slot[j] * erow)
+                                : reinterpret_cast<uint64_t>(trash) + 8;
+            asm volatile("" : "+v"(dst), "+v"(edst));
+            *reinterpret_cast<__attribute__((address_space(1))) uint32_t*>(dst) = q.codes;
+            if ((li & 7) == 0)
+              *reinterpret_cast<__attribute__((address_space(1))) uint8_t*>(edst) = (uint8_t)q.s;
+          } else {
+            val = state_round<BF>(val);  // the stored value (exact for non-writes)
+            asm volatile("" : "+v"(dst));  // keep one unconditional store: hide the select
+            state_store<BF>(dst, val);
+          }
         }
         if (!isw && ((vam >> j) & 1u)) {  // dirty read: its value at this point of the stream
           float* y = yr + tk[j] * YS + li;
@@ -783,8 +807,7 @@ __global__ __launch_bounds__(NT) void two_phase_scan_kernel(StreamArgs a) {
             rq[j] = i + j < ce ? qi : 0.0f;  // the tail repeats the last row with weight 0
           }
 #pragma unroll
-          for (int j = 0; j < BR; ++j)
-            rv[j] = state_load<BF>(Mb + (rs[j] * row_bytes + col_bytes));
+          for (int j = 0; j < BR; ++j) rv[j] = load_row(rs[j]);
 #pragma unroll
           for (int j = 0; j < BR; ++j) {
             acc.x = fmaf(rq[j], rv[j].x, acc.x);
@@ -1014,7 +1037,8 @@ hipError_t launch_stream_scan(const ScanArgs& sa, const StreamPlan& pl, void* ws
   // log_quantize_kernel encodes into the caller's log after the walk
   const bool train = sa.log != nullptr;
   const bool qlog = train && sa.log_fmt != LOG_F32;
-  if (train && sa.state_bf16) return hipErrorInvalidValue;
+  if (train && (sa.state_bf16 || sa.state_fp8)) return hipErrorInvalidValue;
+  if (sa.state_fp8 && !pl.two_phase) return hipErrorInvalidValue;
   if (qlog && pl.stage_bytes < (int64_t)sa.W * sa.d_v * 4) return hipErrorInvalidValue;
   a.B = sa.B;
   a.T = sa.T;
@@ -1105,6 +1129,14 @@ hipError_t launch_stream_scan(const ScanArgs& sa, const StreamPlan& pl, void* ws
       else if (train)
         hipLaunchKernelGGL((two_phase_scan_kernel<1024, 16, BQ_TRAIN16, 8, false, true>), grid,
                            dim3(1024), 0, st, a);
+      else if (pl.SW == 64 && sa.state_fp8)
+        hipLaunchKernelGGL((two_phase_scan_kernel<1024, 64, 8, 8, false, false, true>), grid,
+                           dim3(1024), 0, st, a);
+      else if (pl.SW == 32 && sa.state_fp8)
+        hipLaunchKernelGGL((two_phase_scan_kernel<1024, 32, 8, 8, false, false, true>), grid,
+                           dim3(1024), 0, st, a);
+      else if (sa.state_fp8)
+        return hipErrorInvalidValue;  // blocks of 32 columns need 32-column slices
       else if (pl.SW == 64 && sa.state_bf16)
         hipLaunchKernelGGL((two_phase_scan_kernel<1024, 64, 8, 8, true, false>), grid, dim3(1024), 0, st,
                            a);

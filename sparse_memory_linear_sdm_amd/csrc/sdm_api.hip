@@ -31,9 +31,15 @@ int32_t check_dims(const sdm_dims* d, Derived* out) {
   const int32_t sched = SDM_FLAG_SCAN_DIRECT | SDM_FLAG_SCAN_STREAM | SDM_FLAG_SCAN_TWO_PHASE |
                         SDM_FLAG_SCAN_CHUNK;
   if (d->flags & ~(sched | SDM_FLAG_TIMING | SDM_FLAG_DELTA_GDN | SDM_FLAG_STATE_BF16 |
-                   SDM_FLAG_LOG_FP8 | SDM_FLAG_LOG_INT4))
+                   SDM_FLAG_STATE_FP8 | SDM_FLAG_LOG_FP8 | SDM_FLAG_LOG_INT4))
     return SDM_ERR_UNSUPPORTED;
   if ((d->flags & SDM_FLAG_LOG_FP8) && (d->flags & SDM_FLAG_LOG_INT4)) return SDM_ERR_SHAPE;
+  if ((d->flags & SDM_FLAG_STATE_FP8) && (d->flags & SDM_FLAG_STATE_BF16)) return SDM_ERR_SHAPE;
+  // fp8 state: the per-slot rule on the two-phase and direct schedules, d_v >= 32
+  if ((d->flags & SDM_FLAG_STATE_FP8) &&
+      ((d->flags & (SDM_FLAG_DELTA_GDN | SDM_FLAG_SCAN_STREAM | SDM_FLAG_SCAN_CHUNK)) ||
+       d->d_v < 32))
+    return SDM_ERR_UNSUPPORTED;
   if (__builtin_popcount((unsigned)(d->flags & sched)) > 1) return SDM_ERR_SHAPE;  // one schedule
   if ((d->flags & SDM_FLAG_DELTA_GDN) &&
       (d->flags & (SDM_FLAG_SCAN_STREAM | SDM_FLAG_SCAN_TWO_PHASE)))
@@ -174,6 +180,7 @@ ScanArgs scan_args(const sdm_dims* d, const Derived& dv, const sdm_sel* in,
   a.d_v = d->d_v;
   a.eps = d->eps;
   a.state_bf16 = (d->flags & SDM_FLAG_STATE_BF16) != 0;
+  a.state_fp8 = (d->flags & SDM_FLAG_STATE_FP8) != 0;
   return a;
 }
 
@@ -200,6 +207,7 @@ int32_t scan_entry(const sdm_dims* d, const sdm_sel* in, const float* norm_w, co
   Derived dv;
   int32_t st = check_dims(d, &dv);
   if (st != SDM_OK) return st;
+  if (shared && (d->flags & SDM_FLAG_STATE_FP8)) return SDM_ERR_UNSUPPORTED;
   if (dv.M == 0) return SDM_OK;
   if ((st = check_sel(in, false)) != SDM_OK) return st;
   if (!state || !out || (shared && (!m0 || !touched))) return SDM_ERR_NULL;
@@ -225,6 +233,7 @@ int32_t forward_entry(const sdm_dims* d, const void* x, const void* w_proj, cons
   Derived dv;
   int32_t st = check_dims(d, &dv);
   if (st != SDM_OK) return st;
+  if (shared && (d->flags & SDM_FLAG_STATE_FP8)) return SDM_ERR_UNSUPPORTED;
   if (dv.M == 0) return SDM_OK;
   if (!x || !w_proj || !A || !b_dt || !state || !out || (shared && (!m0 || !touched)))
     return SDM_ERR_NULL;
@@ -326,7 +335,8 @@ static int32_t log_format(const sdm_dims* d) {
 // The training entries take fp32 state: the per-slot rule on the direct and slot-owner
 // schedules, the key-weighted rule on the direct one.
 static int32_t check_train_flags(const sdm_dims* d) {
-  if (d->flags & (SDM_FLAG_STATE_BF16 | SDM_FLAG_SCAN_CHUNK)) return SDM_ERR_UNSUPPORTED;
+  if (d->flags & (SDM_FLAG_STATE_BF16 | SDM_FLAG_STATE_FP8 | SDM_FLAG_SCAN_CHUNK))
+    return SDM_ERR_UNSUPPORTED;
   return SDM_OK;
 }
 

@@ -60,6 +60,7 @@ struct ScanArgs {
   int32_t H, N, W, R, d_v;
   float eps;
   bool state_bf16;
+  bool state_fp8;       // codes plane, then block exponents (see fp8_block_exp)
 };
 hipError_t launch_scan(const sdm_dims& d, const ScanArgs& a, void* ws, size_t ws_bytes,
                        hipStream_t s);
@@ -391,6 +392,58 @@ __device__ __forceinline__ void state_store(uint64_t addr, float4 v) {
     *reinterpret_cast<__attribute__((address_space(1))) gvec4*>(addr) =
         gvec4{v.x, v.y, v.z, v.w};
   }
+}
+
+// fp8 state storage (SDM_FLAG_STATE_FP8): the state buffer holds a codes plane
+// [B, H, N, d_v] of OCP E4M3 bytes (e4m3_encode above), then an exponent plane
+// [B, H, N, d_v / 32] of E8M0 bytes, one per 32-column block of a row.  An element
+// is value(code) * 2^(s - 127).  A block's exponent is the least e >= -127 with
+// absmax <= 448 * 2^e, read off the fp32 bits of the block's absmax, so scaling by
+// 2^-e is exact and never saturates.  Lanes move 4 consecutive elements; a block is
+// 8 consecutive lanes of a wavefront.
+__device__ __forceinline__ int fp8_block_exp(float amax) {
+  const uint32_t u = __float_as_uint(amax);
+  const int field = (int)((u >> 23) & 0xffu);
+  if (field == 0) return -127;  // zero or below 2^-126
+  const int e = field - 127 - 8 + ((u & 0x7fffffu) > 0x600000u ? 1 : 0);  // mantissa > 1.75
+  return e < -127 ? -127 : e;
+}
+// The element conversions are gfx950's fp8 instructions (v_cvt_f32_fp8,
+// v_cvt_pk_fp8_f32), whose format is OCP E4M3 with round-to-nearest-even: on the GPU
+// they give the codes and values of e4m3_encode / e4m3_decode above for every code,
+// every midpoint between codes and the subnormal range.
+__device__ __forceinline__ float4 fp8_decode4(uint32_t w, uint32_t s) {
+  const float unit = __builtin_ldexpf(1.0f, (int)s - 127);
+  return make_float4(__builtin_amdgcn_cvt_f32_fp8((int)w, 0) * unit,
+                     __builtin_amdgcn_cvt_f32_fp8((int)w, 1) * unit,
+                     __builtin_amdgcn_cvt_f32_fp8((int)w, 2) * unit,
+                     __builtin_amdgcn_cvt_f32_fp8((int)w, 3) * unit);
+}
+// The largest of x over the 8 lanes of this lane's block: quad swaps by DPP, then
+// the other quad of the 8 by row_half_mirror; every lane gets it.
+__device__ __forceinline__ float block8_max(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xf, 0xf, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xf, 0xf, false)));
+  return fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xf, 0xf,
+                                                          false)));
+}
+// This lane's 4 elements as stored: their codes, the block's exponent byte, and the
+// values they decode to.  Every lane of the block must take part.
+struct Fp8Row {
+  float4 val;
+  uint32_t codes;
+  uint32_t s;
+};
+__device__ __forceinline__ Fp8Row fp8_quantize(float4 v) {
+  const float a = block8_max(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+  const int e = fp8_block_exp(a);
+  const float inv = __builtin_ldexpf(1.0f, -e);
+  Fp8Row r;
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v.x * inv, v.y * inv, 0, false);
+  r.codes = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v.z * inv, v.w * inv, lo, true);
+  r.s = (uint32_t)(e + 127);
+  r.val = fp8_decode4(r.codes, r.s);
+  return r;
 }
 
 }  // namespace sdm

@@ -113,7 +113,25 @@ def select_from_scores(d: SdmDims, scores, stream=None):
 
 
 def state_dtype(d: SdmDims):
+    if d.flags & _lib.SDM_FLAG_STATE_FP8:
+        return torch.uint8
     return torch.bfloat16 if d.flags & _lib.SDM_FLAG_STATE_BF16 else torch.float32
+
+
+def state_shape(d: SdmDims):
+    """[B, H, N, d_v], or with SDM_FLAG_STATE_FP8 the byte count of its two planes."""
+    N = d.n * d.n
+    if d.flags & _lib.SDM_FLAG_STATE_FP8:
+        return (d.B * d.H * N * d.d_v * 33 // 32,)
+    return (d.B, d.H, N, d.d_v)
+
+
+def fp8_state_planes(d: SdmDims, state):
+    """Views of an fp8 state buffer: E4M3 codes [B, H, N, d_v] and block exponents
+    [B, H, N, d_v / 32]."""
+    N = d.n * d.n
+    k = d.B * d.H * N * d.d_v
+    return (state[:k].view(d.B, d.H, N, d.d_v), state[k:].view(d.B, d.H, N, d.d_v // 32))
 
 
 @_on_stream
@@ -121,7 +139,7 @@ def scan(d: SdmDims, products: dict, norm_w, state, with_y_raw=False, out=None, 
          stream=None):
     _check_products(d, products)
     N = d.n * d.n
-    _need(state, state_dtype(d), (d.B, d.H, N, d.d_v), "state")
+    _need(state, state_dtype(d), state_shape(d), "state")
     if norm_w is not None:
         _need(norm_w, torch.float32, (d.H, d.d_v), "norm_w")
     dev = state.device
@@ -139,7 +157,7 @@ def forward(d: SdmDims, x, w_proj, A, b_dt, norm_w, state, debug=False, with_sco
     """Whole path; state is updated in place.  Returns out (and the products if debug)."""
     _check_params(d, x, w_proj, A, b_dt)
     N = d.n * d.n
-    _need(state, state_dtype(d), (d.B, d.H, N, d.d_v), "state")
+    _need(state, state_dtype(d), state_shape(d), "state")
     if norm_w is not None:
         _need(norm_w, torch.float32, (d.H, d.d_v), "norm_w")
     o = out if out is not None else torch.empty((d.B, d.T, d.H, d.d_v), device=x.device)
@@ -251,7 +269,7 @@ def alloc_touched(d: SdmDims, device):
 def _check_shared(d: SdmDims, m0, state, touched):
     N = d.n * d.n
     _need(m0, state_dtype(d), (d.H, N, d.d_v), "m0")
-    _need(state, state_dtype(d), (d.B, d.H, N, d.d_v), "state")
+    _need(state, state_dtype(d), state_shape(d), "state")
     _need(touched, torch.int32, (d.B, d.H, (N + 31) // 32), "touched")
 
 

@@ -166,19 +166,30 @@ def bf16_spacing(x):
     return np.ldexp(1.0, np.maximum(e, -125) - 8)
 
 
-def check_bf16_state(got, exp, scale, what):
+def fp8_spacing(x):
+    """Distance between adjacent E4M3 values around |x| (3 fraction bits) -- at the
+    walk's scale, a bound for every block's elements (no block scale exceeds it)."""
+    _, e = np.frexp(np.abs(np.asarray(x, np.float64)))
+    return np.ldexp(1.0, e - 4)
+
+
+def check_bf16_state(got, exp, scale, what, spacing=bf16_spacing):
+    """Stored states equal but for a small fraction of elements, each at most two
+    spacings of the format (bf16, or fp8 with spacing=fp8_spacing) at the walk's scale
+    apart: roundings of values that lay within fp32 error of a rounding boundary."""
     got = np.asarray(got, np.float64)
     exp = np.asarray(exp, np.float64)
     diff = got != exp
     frac = float(diff.mean())
     assert frac <= BF16_MAX_DIFF_FRACTION, f"{what}: {frac:.2e} of the elements differ"
     if diff.any():
-        worst = np.max(np.abs(got - exp)) / bf16_spacing(scale)
+        worst = np.max(np.abs(got - exp)) / spacing(scale)
         assert worst <= 2.0, f"{what}: a difference of {worst:.2f} spacings of the state's scale"
     return int(diff.sum())
 
 
-def check_bf16_reads(y_got, y_exp, out_got, gamma_h, gate, eps, scale, R, what):
+def check_bf16_reads(y_got, y_exp, out_got, gamma_h, gate, eps, scale, R, what,
+                     spacing=bf16_spacing):
     """y: within the fp32 summation bound 2R 2^-24 scale (R weighted rows, weights
     summing to 1, plus the schedules' partial sums), or -- for tokens that read an
     element one rounding step apart -- within that plus two spacings of the scale;
@@ -191,8 +202,8 @@ def check_bf16_reads(y_got, y_exp, out_got, gamma_h, gate, eps, scale, R, what):
     fp32 = 2 * R * 2.0 ** -24 * scale + 1e-12
     ok = np.all(err <= fp32, axis=-1)
     assert (~ok).mean() <= 0.25, f"{what}: {(~ok).sum()} of {ok.size} tokens beyond the fp32 bound"
-    delta = fp32 + 2 * bf16_spacing(scale)
-    assert np.all(err <= delta), f"{what}: read beyond the bf16 bound"
+    delta = fp32 + 2 * spacing(scale)
+    assert np.all(err <= delta), f"{what}: read beyond the storage format's bound"
     assert_close(out_got, O.rms_norm_gate(y_got, gamma_h, gate, eps), f"{what} norm/gate")
     # out against the oracle's out: with s = (mean(y^2) + eps)^(-1/2) and yhat = y s, the
     # norm's Jacobian d out_i / d y_j = gamma_i g_i s (delta_ij - yhat_i yhat_j / d_v)

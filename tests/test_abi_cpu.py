@@ -76,7 +76,12 @@ def _select(lib, d, x=FAKE, w=FAKE, A=FAKE, b=FAKE, sel=None, ws=FAKE, nb=1 << 4
     (dict(eps=-1.0), _lib.SDM_ERR_SHAPE), (dict(eps=float("nan")), _lib.SDM_ERR_SHAPE),
     (dict(n=16, W=129), _lib.SDM_ERR_UNSUPPORTED), (dict(n=1025), _lib.SDM_ERR_UNSUPPORTED),
     (dict(d_v=48), _lib.SDM_ERR_UNSUPPORTED), (dict(d_model=60), _lib.SDM_ERR_UNSUPPORTED),
-    (dict(flags=512), _lib.SDM_ERR_UNSUPPORTED), (dict(flags=3), _lib.SDM_ERR_SHAPE),
+    (dict(flags=1024), _lib.SDM_ERR_UNSUPPORTED), (dict(flags=3), _lib.SDM_ERR_SHAPE),
+    (dict(flags=512), _lib.SDM_ERR_UNSUPPORTED),                 # fp8 state with d_v = 16
+    (dict(flags=512 | 32, d_v=32), _lib.SDM_ERR_SHAPE),          # two storage formats
+    (dict(flags=512 | 16, d_v=32), _lib.SDM_ERR_UNSUPPORTED),    # fp8: per-slot rule only
+    (dict(flags=512 | 2, d_v=32), _lib.SDM_ERR_UNSUPPORTED),     # fp8: not the stream schedule
+    (dict(flags=512 | 256, d_v=32), _lib.SDM_ERR_UNSUPPORTED),   # nor the chunk schedule
     (dict(flags=256 | 1), _lib.SDM_ERR_SHAPE), (dict(flags=256 | 32), _lib.SDM_ERR_UNSUPPORTED),
     (dict(flags=16 | 2), _lib.SDM_ERR_UNSUPPORTED), (dict(flags=16 | 4), _lib.SDM_ERR_UNSUPPORTED),
     (dict(flags=6), _lib.SDM_ERR_SHAPE), (dict(flags=8 | 5), _lib.SDM_ERR_SHAPE),
@@ -132,6 +137,32 @@ def test_bf16_state_flag_is_accepted_everywhere(lib):
         assert _select(lib, d1, x=None) == _lib.SDM_ERR_NULL
     d = _d(T=64, flags=bf | _lib.SDM_FLAG_DELTA_GDN | _lib.SDM_FLAG_SCAN_TWO_PHASE)
     assert _select(lib, d) == _lib.SDM_ERR_UNSUPPORTED
+
+
+def test_fp8_state_flag(lib):
+    # storage only: the two-phase and direct schedules accept it with unchanged workspaces
+    f8 = _lib.SDM_FLAG_STATE_FP8
+    for extra in (0, _lib.SDM_FLAG_SCAN_DIRECT, _lib.SDM_FLAG_SCAN_TWO_PHASE):
+        for T in (8, 300):
+            d0, d1 = _d(T=T, d_v=32, flags=extra), _d(T=T, d_v=32, flags=extra | f8)
+            for entry in (_lib.SDM_ENTRY_SELECT, _lib.SDM_ENTRY_SCAN, _lib.SDM_ENTRY_FORWARD):
+                assert (lib.sdm_workspace_bytes(ctypes.byref(d1), entry) ==
+                        lib.sdm_workspace_bytes(ctypes.byref(d0), entry))
+            assert _select(lib, d1, x=None) == _lib.SDM_ERR_NULL
+    d = _d(T=64, d_v=32, flags=f8)
+    s = _sel()
+    # not in training (the log and its reverse walk keep fp32 state) ...
+    assert lib.sdm_scan_train(ctypes.byref(d), ctypes.byref(s), None, FAKE, FAKE, FAKE, FAKE,
+                              None, FAKE, 1 << 40, None) == _lib.SDM_ERR_UNSUPPORTED
+    g = _lib.SdmScanGrads(*([FAKE] * 6 + [None]))
+    assert lib.sdm_scan_backward(ctypes.byref(d), ctypes.byref(s), None, FAKE, FAKE, FAKE, FAKE,
+                                 None, FAKE, ctypes.byref(g), FAKE, 1 << 40,
+                                 None) == _lib.SDM_ERR_UNSUPPORTED
+    # ... nor with a shared initial state (its rows are copied in the fp32/bf16 layouts)
+    assert lib.sdm_scan_shared_m0(ctypes.byref(d), ctypes.byref(s), None, FAKE, FAKE, FAKE, FAKE,
+                                  None, FAKE, 1 << 40, None) == _lib.SDM_ERR_UNSUPPORTED
+    assert lib.sdm_forward_shared_m0(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                                     FAKE, FAKE, FAKE, 1 << 40, None) == _lib.SDM_ERR_UNSUPPORTED
 
 
 def test_shared_m0_entries_validate_first(lib):
