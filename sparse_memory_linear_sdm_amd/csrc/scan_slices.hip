@@ -119,32 +119,33 @@ __device__ __forceinline__ float4 block_groups_sum(float4 v, float4 (*red)[LPR],
   return s;
 }
 
-// Two such sums behind one barrier.
+// A barrier that orders this workgroup's LDS accesses only: global loads and stores
+// still in flight stay in flight (a full __syncthreads() orders them too).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// block_groups_sum in two halves, so that other work can go between them: each
+// wavefront's sums into `red`, then (after a barrier) the four in order.
 template <int LPR>
-__device__ __forceinline__ void block_groups_sum2(float4& v1, float4& v2, float4 (*red1)[LPR],
-                                                  float4 (*red2)[LPR], int lane, int wv, int li) {
-  v1 = wave_groups_sum4<LPR>(v1);
-  v2 = wave_groups_sum4<LPR>(v2);
-  if (lane < LPR) {
-    red1[wv][li] = v1;
-    red2[wv][li] = v2;
-  }
-  __syncthreads();
-  float4 s1 = red1[0][li], s2 = red2[0][li];
+__device__ __forceinline__ void groups_put(float4 v, float4 (*red)[LPR], int lane, int wv, int li) {
+  v = wave_groups_sum4<LPR>(v);
+  if (lane < LPR) red[wv][li] = v;
+}
+template <int LPR>
+__device__ __forceinline__ float4 groups_take(float4 (*red)[LPR], int li) {
+  float4 s = red[0][li];
 #pragma unroll
   for (int q = 1; q < kNW; ++q) {
-    const float4 o1 = red1[q][li], o2 = red2[q][li];
-    s1.x += o1.x;
-    s1.y += o1.y;
-    s1.z += o1.z;
-    s1.w += o1.w;
-    s2.x += o2.x;
-    s2.y += o2.y;
-    s2.z += o2.z;
-    s2.w += o2.w;
+    const float4 o = red[q][li];
+    s.x += o.x;
+    s.y += o.y;
+    s.z += o.z;
+    s.w += o.w;
   }
-  v1 = s1;
-  v2 = s2;
+  return s;
 }
 
 // Forward walk of one (walk, slice): SW columns, LPR = SW/4 lanes per row (a float4
@@ -258,8 +259,28 @@ __global__ __launch_bounds__(256) void gdn_slice_kernel(SliceArgs A) {
   }
 }
 
-// Reverse walk of one (walk, slice); layout as the forward.
-template <int SW>
+// Whether id is in the ascending list s[0..n) (LDS, 1 <= n <= 128): a binary search
+// of fixed length whose reads are unconditional (no branch for the wait-count pass to
+// join loads in flight across).
+__device__ __forceinline__ bool in_sorted(const int32_t* s, int n, int32_t id) {
+  int pos = 0;  // count of entries below id
+#pragma unroll
+  for (int step = 64; step > 0; step >>= 1) {
+    const int q = pos + step;
+    const bool below = s[min(q, n) - 1] < id;
+    pos = (q <= n && below) ? q : pos;
+  }
+  return s[min(pos, n - 1)] == id;
+}
+
+// Reverse walk of one (walk, slice); layout as the forward.  Per token, the rows of
+// the write phase that the token does not also read are loaded together with the
+// read phase's rows and the logged rows (one round trip); the few it does read (a
+// search of its read ids, staged in LDS) are reloaded after the read phase's
+// barrier.  The previous token's small operands are loaded one token ahead.  Loads
+// of padding entries (k beyond W or R) are clamped to a real entry and discarded,
+// so the batch is straight-line code and its loads retire in order.
+template <int SW, int FMT>
 __global__ __launch_bounds__(256) void gdn_slice_backward_kernel(SliceBackArgs A) {
   constexpr int LPR = SW / 4;
   constexpr int G = 256 / LPR;
@@ -267,6 +288,7 @@ __global__ __launch_bounds__(256) void gdn_slice_backward_kernel(SliceBackArgs A
   __shared__ float4 red1[kNW][LPR];
   __shared__ float4 red2[kNW][LPR];
   __shared__ float rda[kNW];
+  __shared__ int32_t rid[128];  // this token's read ids
   const ScanBackArgs& a = A.s;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int li = tid % LPR, grp = tid / LPR;
@@ -281,92 +303,128 @@ __global__ __launch_bounds__(256) void gdn_slice_backward_kernel(SliceBackArgs A
   float* const dM = a.d_state + bh * (int64_t)a.N * DV + c0;
   auto ld = [](const float* p) { return *reinterpret_cast<const float4*>(p); };
   auto st = [](float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; };
+  auto kw_of = [&](int j) { return min(grp + j * G, a.W - 1); };  // clamped entries
+  auto kr_of = [&](int j) { return min(grp + j * G, a.R - 1); };
 
+  struct Ops {
+    float4 dy, vv;
+    float al, be;
+    float ww[RPG], wr[RPG];
+    int32_t iw[RPG], ir[RPG];
+    int32_t rfull;  // read id number tid (staging)
+  };
+  auto load_ops = [&](int64_t t, Ops& o) {
+    const int64_t tok = (b * a.T + t) * a.H + h;
+    o.dy = ld(A.dy + tok * DV + c0);
+    o.vv = ld(a.v + tok * DV + c0);
+    o.al = a.alpha[tok];
+    o.be = a.beta[tok];
+#pragma unroll
+    for (int j = 0; j < RPG; ++j) {
+      o.ww[j] = a.wt_w[tok * a.W + kw_of(j)];
+      o.iw[j] = a.idx_w[tok * a.W + kw_of(j)];
+      o.wr[j] = a.wt_r[tok * a.R + kr_of(j)];
+      o.ir[j] = a.idx_r[tok * a.R + kr_of(j)];
+    }
+    o.rfull = a.idx_r[tok * a.R + min(tid, a.R - 1)];
+  };
+
+  Ops op;
+  load_ops(a.T - 1, op);
   for (int64_t t = a.T - 1; t >= 0; --t) {
     const int64_t tok = (b * a.T + t) * a.H + h;
-    const int32_t* ir = a.idx_r + tok * a.R;
-    const float* wr = a.wt_r + tok * a.R;
-    const int32_t* iw = a.idx_w + tok * a.W;
-    const float* ww = a.wt_w + tok * a.W;
-    const float4 dy = ld(A.dy + tok * DV + c0);
-    // the logged rows of this token's writes (read-only: loaded with the read phase)
-    float4 ms[RPG];
+    if (tid < a.R) rid[tid] = op.rfull;
+    __syncthreads();  // read ids staged; the previous token's restores precede the loads
+    // ---- one batch: logged rows, the read rows, the write rows' gradients ----
+    float4 ms[RPG], m[RPG], g[RPG], gs[RPG];
+#pragma unroll
+    for (int j = 0; j < RPG; ++j) {
+      ms[j] = log_load(a.log, a.log_scale, FMT, tok * a.W + kw_of(j), DV, q0);
+      const int64_t r = (int64_t)op.ir[j] * DV;
+      m[j] = ld(M + r);
+      g[j] = ld(dM + r);
+    }
+    uint32_t late = 0;  // write rows this token also reads: their dM after the read phase
+#pragma unroll
+    for (int j = 0; j < RPG; ++j)
+      late |= (uint32_t)in_sorted(rid, a.R, op.iw[j]) << j;
+#pragma unroll
+    for (int j = 0; j < RPG; ++j) gs[j] = ld(dM + (int64_t)op.iw[j] * DV);
+    Ops on;
+    load_ops(t > 0 ? t - 1 : t, on);
+    // the read rows are used here, whatever entries are real: their loads stay in this
+    // batch (the compiler would otherwise sink some into the branches that store)
+#pragma unroll
+    for (int j = 0; j < RPG; ++j)
+      asm volatile("" ::"v"(m[j].x), "v"(m[j].y), "v"(m[j].z), "v"(m[j].w), "v"(g[j].x),
+                   "v"(g[j].y), "v"(g[j].z), "v"(g[j].w));
+    // ---- read (the state after token t's writes) ----
+    // (every entry computes, padding ones included, so that no load is sunk into a
+    // branch; only real entries store)
+    float dq[RPG];
+    float4 nr[RPG];
+#pragma unroll
+    for (int j = 0; j < RPG; ++j) {
+      dq[j] = slice_sum<LPR>(dot4(op.dy, m[j]));
+      nr[j] = g[j];
+      fma4(op.wr[j], op.dy, nr[j]);
+    }
 #pragma unroll
     for (int j = 0; j < RPG; ++j) {
       const int k = grp + j * G;
-      if (k < a.W) ms[j] = log_load(a.log, a.log_scale, a.log_fmt, tok * a.W + k, DV, q0);
-    }
-    // ---- read (the state after token t's writes) ----
-    {
-      float4 m[RPG], g[RPG];
-#pragma unroll
-      for (int j = 0; j < RPG; ++j) {
-        const int k = grp + j * G;
-        if (k < a.R) {
-          const int64_t r = (int64_t)ir[k] * DV;
-          m[j] = ld(M + r);
-          g[j] = ld(dM + r);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < RPG; ++j) {
-        const int k = grp + j * G;
-        if (k < a.R) {
-          const float dq = slice_sum<LPR>(dot4(dy, m[j]));
-          if (li == 0) A.pr[(sl * A.rows + tok) * a.R + k] = dq;
-          float4 n = g[j];
-          fma4(wr[k], dy, n);
-          st(dM + (int64_t)ir[k] * DV, n);
-        }
+      if (k < a.R) {
+        if (li == 0) A.pr[(sl * A.rows + tok) * a.R + k] = dq[j];
+        st(dM + (int64_t)op.ir[j] * DV, nr[j]);
       }
     }
     __syncthreads();  // the write phase may take rows this phase updated
     // ---- write, undone ----
-    const float al = a.alpha[tok];
-    const float be = a.beta[tok];
-    const float4 vv = ld(a.v + tok * DV + c0);
-    float4 gs[RPG];
+#pragma unroll
+    for (int j = 0; j < RPG; ++j)
+      if (((late >> j) & 1u) && grp + j * G < a.W) gs[j] = ld(dM + (int64_t)op.iw[j] * DV);
     float4 pk = f4z(), sg = f4z();
+    float kwj[RPG];  // the write weights, 0 for padding entries
 #pragma unroll
     for (int j = 0; j < RPG; ++j) {
-      const int k = grp + j * G;
-      if (k < a.W) gs[j] = ld(dM + (int64_t)iw[k] * DV);
+      kwj[j] = grp + j * G < a.W ? op.ww[j] : 0.0f;
+      fma4(kwj[j], ms[j], pk);
+      fma4(kwj[j], gs[j], sg);
     }
-#pragma unroll
-    for (int j = 0; j < RPG; ++j) {
-      const int k = grp + j * G;
-      if (k < a.W) {
-        fma4(ww[k], ms[j], pk);
-        fma4(ww[k], gs[j], sg);
-      }
-    }
-    block_groups_sum2<LPR>(pk, sg, red1, red2, lane, wv, li);  // sum k m, sum k G
-    const float4 e = make_float4(vv.x - al * pk.x, vv.y - al * pk.y, vv.z - al * pk.z,
-                                 vv.w - al * pk.w);
+    groups_put<LPR>(pk, red1, lane, wv, li);
+    groups_put<LPR>(sg, red2, lane, wv, li);
+    lds_barrier();
+    pk = groups_take<LPR>(red1, li);  // sum k m
+    sg = groups_take<LPR>(red2, li);  // sum k G
+    const float al = op.al, be = op.be;
+    const float4 e = make_float4(op.vv.x - al * pk.x, op.vv.y - al * pk.y, op.vv.z - al * pk.z,
+                                 op.vv.w - al * pk.w);
     const float4 de = make_float4(be * sg.x, be * sg.y, be * sg.z, be * sg.w);
     if (tid < LPR) st(a.g_v + tok * DV + c0, de);
     float da = 0.0f;
 #pragma unroll
     for (int j = 0; j < RPG; ++j) {
       const int k = grp + j * G;
-      if (k < a.W) {
-        const float kw = ww[k];
-        const float4 m = ms[j], g = gs[j];
-        const float4 dmt = make_float4(g.x - kw * de.x, g.y - kw * de.y, g.z - kw * de.z,
-                                       g.w - kw * de.w);
-        const float ge = slice_sum<LPR>(dot4(g, e));
-        const float dem = slice_sum<LPR>(dot4(de, m));
-        da += slice_sum<LPR>(dot4(dmt, m));
+      const bool real = k < a.W;
+      const float kw = kwj[j];
+      const float4 mm = ms[j], gg = gs[j];
+      const float4 dmt = make_float4(gg.x - kw * de.x, gg.y - kw * de.y, gg.z - kw * de.z,
+                                     gg.w - kw * de.w);
+      const float ge = slice_sum<LPR>(dot4(gg, e));
+      const float dem = slice_sum<LPR>(dot4(de, mm));
+      const float dj = slice_sum<LPR>(dot4(dmt, mm));
+      da += real ? dj : 0.0f;
+      if (real) {
         if (li == 0) A.pw[(sl * A.rows + tok) * a.W + k] = make_float2(ge, dem);
-        const int64_t r = (int64_t)iw[k] * DV;
+        const int64_t r = (int64_t)op.iw[j] * DV;
         st(dM + r, make_float4(al * dmt.x, al * dmt.y, al * dmt.z, al * dmt.w));
-        st(M + r, m);
+        st(M + r, mm);
       }
     }
     da = wave_groups_sum<LPR>(da);  // every lane of a group holds its group's sum
     if (lane == 0) rda[wv] = da;
-    __syncthreads();  // rda complete; this token's restores precede the next reads
+    lds_barrier();
     if (tid == 0) A.pa[sl * A.rows + tok] = (rda[0] + rda[1]) + (rda[2] + rda[3]);
+    op = on;
   }
 }
 
@@ -401,6 +459,16 @@ __global__ __launch_bounds__(256) void gdn_slice_reduce_kernel(SliceBackArgs A) 
     a.g_alpha[tok] = da;
     a.g_beta[tok] = db;
   }
+}
+
+template <int SW>
+void launch_back_sw(const SliceBackArgs& A, dim3 grid, hipStream_t s) {
+  if (A.s.log_fmt == LOG_FP8)
+    hipLaunchKernelGGL((gdn_slice_backward_kernel<SW, LOG_FP8>), grid, dim3(256), 0, s, A);
+  else if (A.s.log_fmt == LOG_INT4)
+    hipLaunchKernelGGL((gdn_slice_backward_kernel<SW, LOG_INT4>), grid, dim3(256), 0, s, A);
+  else
+    hipLaunchKernelGGL((gdn_slice_backward_kernel<SW, LOG_F32>), grid, dim3(256), 0, s, A);
 }
 
 template <int SW>
@@ -548,15 +616,13 @@ hipError_t launch_gdn_slice_backward(const sdm_dims& d, const ScanBackArgs& a, f
     const dim3 grid((unsigned)(a.B * a.H * S));
     KernelTimer kt("gdn_slices_backward", st);
     switch (a.d_v / S) {
-      case 16: hipLaunchKernelGGL(gdn_slice_backward_kernel<16>, grid, dim3(256), 0, st, A); break;
-      case 32: hipLaunchKernelGGL(gdn_slice_backward_kernel<32>, grid, dim3(256), 0, st, A); break;
+      case 16: launch_back_sw<16>(A, grid, st); break;
+      case 32: launch_back_sw<32>(A, grid, st); break;
 #if SDM_GDN_MAX_SW >= 64
-      case 64: hipLaunchKernelGGL(gdn_slice_backward_kernel<64>, grid, dim3(256), 0, st, A); break;
+      case 64: launch_back_sw<64>(A, grid, st); break;
 #endif
 #if SDM_GDN_MAX_SW >= 128
-      case 128:
-        hipLaunchKernelGGL(gdn_slice_backward_kernel<128>, grid, dim3(256), 0, st, A);
-        break;
+      case 128: launch_back_sw<128>(A, grid, st); break;
 #endif
       default: return hipErrorInvalidValue;
     }
