@@ -22,7 +22,8 @@ training forward of the scan (with the fp32 write log), the scan backward (rando
 incoming gradients of out and of the final state), which leaves the state at M0
 again, the selection-pass backward down to dY, and the two projection-gradient
 GEMMs (dx, dW_proj; bf16 through the platform BLAS).  Its roofline is the
-reverse-walk kernel's; no CPU baseline.
+reverse-walk kernel's; no CPU baseline.  --schedule sets the training forward's
+schedule (and the backward's: chunk picks by length as the default does).
 """
 from __future__ import annotations
 
@@ -533,8 +534,12 @@ def train_main(args):
     torch.cuda.set_device(dev)
     d = dims_for(wl)
     gdn = args.rule == "gdn"
-    if gdn:  # the key-weighted rule trains on the direct schedule
+    if gdn:  # the key-weighted rule: chunk schedule from 256 tokens, else direct
         d.flags |= _lib.SDM_FLAG_DELTA_GDN
+    if args.schedule != "default":  # the training forward's schedule (and the backward's)
+        d.flags |= {"direct": _lib.SDM_FLAG_SCAN_DIRECT, "stream": _lib.SDM_FLAG_SCAN_STREAM,
+                    "two_phase": _lib.SDM_FLAG_SCAN_TWO_PHASE,
+                    "chunk": _lib.SDM_FLAG_SCAN_CHUNK}[args.schedule]
     _, x_store = synth.gen_x(wl, seed=0)
     prm = synth.gen_params(wl, seed=0)
     m0 = synth.gen_m0(wl, seed=0)
@@ -630,6 +635,7 @@ def train_main(args):
         "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "d_model": wl.d_model, "H": wl.H,
                    "N": wl.N, "n": wl.n, "W": wl.W, "R": wl.R, "d_v": wl.d_v,
                    "state": "fp32 [B,H,N,d_v]", "tokens_per_step": tokens,
+                   "schedule": args.schedule,
                    "step": "select + scan_train + scan_backward + select_backward + "
                            "dx/dW_proj GEMMs (bf16, platform BLAS)"},
         "kernels_ms": kernels_ms,

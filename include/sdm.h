@@ -153,8 +153,10 @@ extern "C" {
    The same results as the other schedules up to fp32 rounding order (the decays of
    a chunk are summed as logarithms, each floored at -80).  Needs each token's write
    and read ids ascending (the selection's order), fp32 state (with
-   SDM_FLAG_STATE_BF16 it is SDM_ERR_UNSUPPORTED) and a workspace; the training
-   entries do not take it (SDM_ERR_UNSUPPORTED). */
+   SDM_FLAG_STATE_BF16 it is SDM_ERR_UNSUPPORTED) and a workspace.  sdm_scan_train
+   takes it with an fp32 log (the last writer of each slot in a chunk also logs the
+   row every earlier writer of the chunk replaced); with SDM_FLAG_LOG_FP8 or
+   SDM_FLAG_LOG_INT4 it is SDM_ERR_UNSUPPORTED. */
 #define SDM_FLAG_SCAN_CHUNK 256
 
 /* Limits of this build (SDM_ERR_UNSUPPORTED beyond them). */
@@ -334,18 +336,21 @@ SDM_API int32_t sdm_forward_noalloc(const sdm_dims* dims, const void* x, const v
  *   y_raw   required here (the backward needs it)
  *   ws      >= sdm_workspace_bytes(dims, SDM_ENTRY_SCAN_TRAIN) bytes (may be NULL
  *           if 0)
- *   Schedules: a schedule flag picks one (SDM_FLAG_SCAN_DIRECT, _STREAM or
- *   _TWO_PHASE); without one, the two-phase schedule from 256 tokens and the direct
- *   one below.  On the slot-owner (stream, two-phase) schedules, and for the
- *   key-weighted rule, a quantised log is staged in fp32 in the workspace (token
- *   chunks bounded near 2 GiB, and 256 MiB) and encoded after each chunk's walk.
- *   The state, the log and its scales equal those of
- *   sdm_scan and of every schedule bit for bit; y_raw and out equal sdm_scan's on
- *   the same schedule, bit for bit on the direct one and up to fp32 summation order
- *   on the slot-owner ones.  fp32 state only (SDM_FLAG_STATE_BF16 gives
- *   SDM_ERR_UNSUPPORTED).  The key-weighted rule (SDM_FLAG_DELTA_GDN) trains on the
- *   direct schedule, its default at every length; with SDM_FLAG_SCAN_STREAM,
- *   _TWO_PHASE or _CHUNK it is SDM_ERR_UNSUPPORTED.
+ *   Schedules: a schedule flag picks one (SDM_FLAG_SCAN_DIRECT, _STREAM, _TWO_PHASE
+ *   or _CHUNK, the last with an fp32 log only); without one, the per-slot rule takes
+ *   the two-phase schedule from 256 tokens and the direct one below.  On the
+ *   slot-owner (stream, two-phase) schedules, and for the key-weighted rule on the
+ *   direct one, a quantised log is staged in fp32 in the workspace (token chunks
+ *   bounded near 2 GiB, and 256 MiB) and encoded after each chunk's walk.  State,
+ *   y_raw and out equal sdm_scan's on the same schedule (bit for bit on the direct
+ *   and chunk schedules, up to fp32 summation order on the slot-owner ones).  The
+ *   log and its scales equal those of every per-slot schedule but the chunk one bit
+ *   for bit; the chunk schedule's rows (each a fold of the chunk's earlier writes)
+ *   and the key-weighted rule's equal the others up to fp32 rounding order.  fp32
+ *   state only (SDM_FLAG_STATE_BF16 and SDM_FLAG_STATE_FP8 give
+ *   SDM_ERR_UNSUPPORTED).  The key-weighted rule (SDM_FLAG_DELTA_GDN) takes the
+ *   chunk schedule from 256 tokens with an fp32 log, else the direct one; with
+ *   SDM_FLAG_SCAN_STREAM or _TWO_PHASE it is SDM_ERR_UNSUPPORTED.
  *
  * sdm_scan_backward: gradients of that call, walking the tokens in reverse (per
  * token: the norm and gate, the read, then the write, whose overwritten rows are
@@ -364,7 +369,8 @@ SDM_API int32_t sdm_forward_noalloc(const sdm_dims* dims, const void* x, const v
  * SDM_FLAG_SCAN_TWO_PHASE, which both select it): slot-owner lane groups walk the
  * accesses of each slot in reverse, any log format;
  * else (or with SDM_FLAG_SCAN_DIRECT) one workgroup per (b, h), tokens in
- * lock-step.  The key-weighted rule (SDM_FLAG_DELTA_GDN) always walks directly, one
+ * lock-step; SDM_FLAG_SCAN_CHUNK picks by length as no flag does.  The log of any
+ * forward schedule serves any backward one.  The key-weighted rule (SDM_FLAG_DELTA_GDN) always walks directly, one
  * workgroup per (b, h, column slice) as its forward; its write is undone per token
  * with m the logged rows, m~ = alpha m, e = v - sum k m~, G = dL/dM rows:
  * d_v = beta sum k G = de, dm~ = G - k de, d_k = beta <G, e> - <de, m~>,

@@ -186,7 +186,7 @@ static int64_t stage_bytes(const sdm_dims& d, bool quantised_log) {
 }
 
 size_t scan_workspace_bytes(const sdm_dims& d, bool train) {
-  if (!train && scan_uses_chunk(d)) return chunk_workspace_bytes(d);
+  if (scan_uses_chunk(d)) return chunk_workspace_bytes(d);  // training: fp32 log only
   if (d.flags & SDM_FLAG_DELTA_GDN) return gdn_slice_workspace_bytes(d, train);
   if (!scan_uses_stream(d)) return 0;
   const bool q = train && (d.flags & (SDM_FLAG_LOG_FP8 | SDM_FLAG_LOG_INT4));
@@ -194,7 +194,7 @@ size_t scan_workspace_bytes(const sdm_dims& d, bool train) {
 }
 
 hipError_t launch_scan(const sdm_dims& d, const ScanArgs& a, void* ws, size_t, hipStream_t s) {
-  if (scan_uses_chunk(d) && a.log == nullptr) return launch_chunk_scan(d, a, ws, s);
+  if (scan_uses_chunk(d)) return launch_chunk_scan(d, a, ws, s);
   if (scan_uses_stream(d))
     return launch_stream_scan(
         a, plan_stream(d, a.N, stage_bytes(d, a.log != nullptr && a.log_fmt != LOG_F32)), ws, s);

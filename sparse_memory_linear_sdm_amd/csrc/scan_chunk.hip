@@ -69,6 +69,7 @@ struct ChunkArgs {
   float* Tm;       // [walks][chunks][C][C] GDN only
   float* state;    // [B, H, N, d_v] fp32
   float* y;        // [B, T, H, d_v]
+  float* log;      // training forward: [B, T, H, W, d_v] fp32 rows before each write, or null
   int64_t B, T;
   int32_t H, N, W, R, d_v, chunks;
 };
@@ -349,7 +350,10 @@ __device__ __forceinline__ float4 gather_sum(const float* Mb, int d_v, const int
   return acc;
 }
 
-template <bool GDN>
+// LOG (training forward): each slot's last writer also stores the row every writer of
+// its chain replaced -- the chunk-start row for the first, else the fold above taken
+// at the previous writer -- to the write log.
+template <bool GDN, bool LOG>
 __global__ __launch_bounds__(kWalkThreads) void chunk_walk_kernel(ChunkArgs a) {
   constexpr int C = kChunk;
   constexpr int NT = kWalkThreads;
@@ -505,20 +509,36 @@ __global__ __launch_bounds__(kWalkThreads) void chunk_walk_kernel(ChunkArgs a) {
         last[u] = e < Cc * W && !(lk[e] & kNextBit);
         m[u] = *reinterpret_cast<const float4*>(Mb + (int64_t)iw[last[u] ? e : e0] * d_v);
       }
+      // the row after writer q of a chain: the chunk-start row and every writer of the
+      // chain up to q, each decayed to q
+      auto fold = [&](int q, float4 m0) {
+        const float lq = lw[q];
+        float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
+        r = fma4(expf(lq), m0, r);
+        int p = q + 1;
+        while (p) {
+          const int s = (p - 1) / W;
+          r = fma4(expf(lq - lw[p - 1]) * kw[p - 1], xs[s * LPR + li], r);
+          p = lk[p - 1] & 0xffff;
+        }
+        return r;
+      };
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         if (!last[u]) continue;
         const int e = e0 + G * u;
-        const float le = lw[e];
-        float4 r = make_float4(0.f, 0.f, 0.f, 0.f);
-        r = fma4(expf(le), m[u], r);
-        int p = e + 1;
-        while (p) {
-          const int s = (p - 1) / W;
-          r = fma4(expf(le - lw[p - 1]) * kw[p - 1], xs[s * LPR + li], r);
-          p = lk[p - 1] & 0xffff;
+        *reinterpret_cast<float4*>(Mb + (int64_t)iw[e] * d_v) = fold(e, m[u]);
+        if constexpr (LOG) {
+          for (int c = e;;) {  // the chain backwards: the row each writer replaced
+            const int p = lk[c] & 0xffff;  // previous writer + 1, 0 for the first
+            const float4 before = p ? fold(p - 1, m[u]) : m[u];
+            const int s = c / W;
+            const int64_t lr = tok(s) * W + (c - s * W);
+            *reinterpret_cast<float4*>(a.log + lr * d_v + col + li * 4) = before;
+            if (!p) break;
+            c = p - 1;
+          }
         }
-        *reinterpret_cast<float4*>(Mb + (int64_t)iw[e] * d_v) = r;
       }
     }
     __syncthreads();
@@ -575,6 +595,8 @@ hipError_t launch_chunk_scan(const sdm_dims& d, const ScanArgs& sa, void* ws, hi
   a.Tm = s.tm ? reinterpret_cast<float*>(p) : nullptr; p += s.tm;
   a.y = reinterpret_cast<float*>(p);
   a.state = static_cast<float*>(sa.state);
+  a.log = static_cast<float*>(sa.log);  // fp32 rows (training forward), or null
+  if (a.log && sa.log_fmt != LOG_F32) return hipErrorInvalidValue;
   a.B = sa.B;
   a.T = sa.T;
   a.H = sa.H;
@@ -609,17 +631,22 @@ hipError_t launch_chunk_scan(const sdm_dims& d, const ScanArgs& sa, void* ws, hi
     // XCD (and its L2 copy of the chunk's lists)
     const dim3 grid((unsigned)(walks * (a.d_v / kSlice)));
     KernelTimer kt("chunk_walk", st);
-    if (gdn) {
-      e = hipFuncSetAttribute((const void*)chunk_walk_kernel<true>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(chunk_walk_kernel<true>, grid, dim3(kWalkThreads), lds, st, a);
-    } else {
-      e = hipFuncSetAttribute((const void*)chunk_walk_kernel<false>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(chunk_walk_kernel<false>, grid, dim3(kWalkThreads), lds, st, a);
-    }
+    auto go = [&](auto kern) {
+      const hipError_t r = hipFuncSetAttribute((const void*)kern,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (r != hipSuccess) return r;
+      hipLaunchKernelGGL(kern, grid, dim3(kWalkThreads), lds, st, a);
+      return hipSuccess;
+    };
+    if (gdn && a.log)
+      e = go(chunk_walk_kernel<true, true>);
+    else if (gdn)
+      e = go(chunk_walk_kernel<true, false>);
+    else if (a.log)
+      e = go(chunk_walk_kernel<false, true>);
+    else
+      e = go(chunk_walk_kernel<false, false>);
+    if (e != hipSuccess) return e;
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -332,23 +332,31 @@ static int32_t log_format(const sdm_dims* d) {
                                                                                    : LOG_F32;
 }
 
-// The training entries take fp32 state: the per-slot rule on the direct and slot-owner
-// schedules, the key-weighted rule on the direct one.
+// The training entries take fp32 state: the per-slot rule on the direct, slot-owner and
+// chunk schedules, the key-weighted rule on the direct and chunk ones; the chunk
+// schedule logs fp32 rows only.
 static int32_t check_train_flags(const sdm_dims* d) {
-  if (d->flags & (SDM_FLAG_STATE_BF16 | SDM_FLAG_STATE_FP8 | SDM_FLAG_SCAN_CHUNK))
+  if (d->flags & (SDM_FLAG_STATE_BF16 | SDM_FLAG_STATE_FP8)) return SDM_ERR_UNSUPPORTED;
+  if ((d->flags & SDM_FLAG_SCAN_CHUNK) && (d->flags & (SDM_FLAG_LOG_FP8 | SDM_FLAG_LOG_INT4)))
     return SDM_ERR_UNSUPPORTED;
   return SDM_OK;
 }
 
-// Schedule of the training forward as scan flags: a schedule asked for, else the
-// two-phase one from 256 tokens and the direct one below.
+// Schedule of the training forward as scan flags: a schedule asked for, else from 256
+// tokens the two-phase one (per-slot rule) or the chunk one (key-weighted rule, fp32
+// log), and the direct one below that or for a quantised key-weighted log.
 static sdm_dims train_dims(const sdm_dims* d) {
-  const int32_t sched = SDM_FLAG_SCAN_DIRECT | SDM_FLAG_SCAN_STREAM | SDM_FLAG_SCAN_TWO_PHASE;
+  const int32_t sched = SDM_FLAG_SCAN_DIRECT | SDM_FLAG_SCAN_STREAM | SDM_FLAG_SCAN_TWO_PHASE |
+                        SDM_FLAG_SCAN_CHUNK;
   sdm_dims dd = *d;
-  if (!(d->flags & sched))
-    dd.flags |= d->T >= kStreamRound && !(d->flags & SDM_FLAG_DELTA_GDN)
-                    ? SDM_FLAG_SCAN_TWO_PHASE
-                    : SDM_FLAG_SCAN_DIRECT;
+  if (!(d->flags & sched)) {
+    const bool gdn = (d->flags & SDM_FLAG_DELTA_GDN) != 0;
+    const bool qlog = (d->flags & (SDM_FLAG_LOG_FP8 | SDM_FLAG_LOG_INT4)) != 0;
+    if (d->T < kStreamRound || (gdn && qlog))
+      dd.flags |= SDM_FLAG_SCAN_DIRECT;
+    else
+      dd.flags |= gdn ? SDM_FLAG_SCAN_CHUNK : SDM_FLAG_SCAN_TWO_PHASE;
+  }
   return dd;
 }
 

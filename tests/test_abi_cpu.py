@@ -190,13 +190,17 @@ def test_training_entries_validate_first(lib):
     train = lambda dd=d, log=FAKE, y=FAKE, sc=None, ws=FAKE, nb=1 << 40: lib.sdm_scan_train(
         ctypes.byref(dd), ctypes.byref(s), None, FAKE, FAKE, y, log, sc, ws, nb, None)
     assert train(dd=_d(T=64, flags=_lib.SDM_FLAG_STATE_BF16), sc=FAKE) == _lib.SDM_ERR_UNSUPPORTED
-    # the key-weighted rule trains on the direct schedule only
+    # the key-weighted rule trains on the direct and chunk schedules: the chunk one by
+    # default from 256 tokens with an fp32 log (its workspace), else the direct one
     gdn = _lib.SDM_FLAG_DELTA_GDN
-    for fl in (_lib.SDM_FLAG_SCAN_STREAM, _lib.SDM_FLAG_SCAN_TWO_PHASE, _lib.SDM_FLAG_SCAN_CHUNK):
+    for fl in (_lib.SDM_FLAG_SCAN_STREAM, _lib.SDM_FLAG_SCAN_TWO_PHASE):
         assert train(dd=_d(T=64, flags=gdn | fl)) == _lib.SDM_ERR_UNSUPPORTED
     assert train(dd=_d(T=512, flags=gdn), log=None) == _lib.SDM_ERR_NULL
-    assert lib.sdm_workspace_bytes(ctypes.byref(_d(T=512, flags=gdn)),
-                                   _lib.SDM_ENTRY_SCAN_TRAIN) == 0
+    ws_of = lambda dd: lib.sdm_workspace_bytes(ctypes.byref(dd), _lib.SDM_ENTRY_SCAN_TRAIN)
+    assert ws_of(_d(T=512, flags=gdn)) == ws_of(_d(T=512, flags=gdn | _lib.SDM_FLAG_SCAN_CHUNK)) > 0
+    assert ws_of(_d(T=255, flags=gdn)) == 0
+    assert ws_of(_d(T=512, flags=gdn | _lib.SDM_FLAG_LOG_INT4)) == \
+        ws_of(_d(T=512, flags=gdn | _lib.SDM_FLAG_LOG_INT4 | _lib.SDM_FLAG_SCAN_DIRECT))
     # the direct schedule needs no workspace; the stream schedule (an fp32 log from 256
     # tokens, or asked for) takes its buckets from the workspace
     assert lib.sdm_workspace_bytes(ctypes.byref(d), _lib.SDM_ENTRY_SCAN_TRAIN) == 0
@@ -384,6 +388,12 @@ def test_chunk_schedule_flag(lib):
     assert scan(d, nb=need - 1) == _lib.SDM_ERR_WORKSPACE
     assert scan(_d(T=100, flags=chunk | _lib.SDM_FLAG_STATE_BF16)) == _lib.SDM_ERR_UNSUPPORTED
     assert scan(_d(T=100, flags=chunk | _lib.SDM_FLAG_SCAN_TWO_PHASE)) == _lib.SDM_ERR_SHAPE
-    # the training entries take the slot-owner and direct schedules only
+    # the training entries take it with an fp32 log only (its walk logs fp32 rows), and
+    # size their workspace as the inference scan
+    for lf in (_lib.SDM_FLAG_LOG_FP8, _lib.SDM_FLAG_LOG_INT4):
+        assert lib.sdm_scan_train(ctypes.byref(_d(T=100, flags=chunk | lf)), ctypes.byref(s),
+                                  None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+                                  None) == _lib.SDM_ERR_UNSUPPORTED
+    assert lib.sdm_workspace_bytes(ctypes.byref(d), _lib.SDM_ENTRY_SCAN_TRAIN) == need
     assert lib.sdm_scan_train(ctypes.byref(d), ctypes.byref(s), None, FAKE, FAKE, FAKE, FAKE,
-                              None, FAKE, 1 << 40, None) == _lib.SDM_ERR_UNSUPPORTED
+                              None, None, 0, None) == _lib.SDM_ERR_WORKSPACE

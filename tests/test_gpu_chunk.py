@@ -134,7 +134,7 @@ def test_chunk_schedule_forward_from_x():
         assert_close(host(st), host(st2), f"forward state flags {extra}")
 
 
-def test_chunk_schedule_rejects_bf16_state_and_training():
+def test_chunk_schedule_rejects_bf16_state_and_quantised_training_logs():
     d = _dims(T=64, flags=CHUNK | _lib.SDM_FLAG_STATE_BF16)
     assert _lib.workspace_bytes(_dims(T=64, flags=CHUNK), _lib.SDM_ENTRY_SCAN) > 0
     rng = np.random.default_rng(0)
@@ -143,10 +143,66 @@ def test_chunk_schedule_rejects_bf16_state_and_training():
         ops.scan(d, prod, None, torch.zeros((1, 1, 256, 16), dtype=torch.bfloat16,
                                              device="cuda"))
     assert e.value.code == _lib.SDM_ERR_UNSUPPORTED
-    with pytest.raises(_lib.SdmError) as e:
-        ops.scan_train(_dims(T=64, flags=CHUNK), prod, None,
-                       torch.zeros((1, 1, 256, 16), device="cuda"))
-    assert e.value.code == _lib.SDM_ERR_UNSUPPORTED
+    for lf in (_lib.SDM_FLAG_LOG_FP8, _lib.SDM_FLAG_LOG_INT4):
+        with pytest.raises(_lib.SdmError) as e:
+            ops.scan_train(_dims(T=64, flags=CHUNK | lf), prod, None,
+                           torch.zeros((1, 1, 256, 16), device="cuda"))
+        assert e.value.code == _lib.SDM_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("rule", ["slot", "gdn"])
+@pytest.mark.parametrize("B,T,H,n,W,R,d_v,mode", [
+    (2, 75, 2, 6, 16, 12, 32, "random"),       # N = 36: chains of writers in every chunk
+    (1, 300, 2, 40, 64, 64, 128, "repeat"),    # runs of identical selections
+    (1, 40, 1, 12, 128, 100, 64, "random"),    # the largest W
+])
+def test_chunk_training_forward_and_backward(rule, B, T, H, n, W, R, d_v, mode):
+    """The training forward on the chunk schedule: the last writer of each slot also
+    logs the row every writer of its chain replaced.  State, y and out equal the chunk
+    inference scan bit for bit; the log equals the oracle's log of the walk; the
+    reverse walk on these results matches the oracle's backward and restores M0."""
+    rng = np.random.default_rng(B * 100 + T + W + (rule == "gdn"))
+    N = n * n
+    prod = random_products(rng, B, T, H, n, W, R, d_v, mode)
+    m0 = (rng.standard_normal((B, H, N, d_v)) * 0.02).astype(np.float32)
+    gamma = rng.uniform(0.5, 1.5, (H, d_v)).astype(np.float32)
+    flags = CHUNK | (GDN if rule == "gdn" else 0)
+    d = _dims(B=B, T=T, H=H, n=n, W=W, R=R, d_v=d_v, flags=flags)
+    pd = _prod_dev(prod)
+    g = to_dev(gamma)
+    state = to_dev(m0)
+    out, y, log = ops.scan_train(d, pd, g, state)
+    st_i = to_dev(m0)
+    out_i, y_i = ops.scan(d, pd, g, st_i, with_y_raw=True)
+    torch.cuda.synchronize()
+    assert torch.equal(state, st_i) and torch.equal(y, y_i) and torch.equal(out, out_i)
+    log_h, st_T, y_h = host(log["rows"]), host(state), host(y)
+    d_out = rng.standard_normal((B, T, H, d_v)).astype(np.float32)
+    d_st = (rng.standard_normal((B, H, N, d_v)) * 0.1).astype(np.float32)
+    st, dS = to_dev(st_T), to_dev(d_st)
+    gr = ops.scan_backward(d, pd, g, st, dS, y, log, to_dev(d_out))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(st), m0), "initial state not restored bit for bit"
+    gh = {k: host(v) for k, v in gr.items() if v is not None}
+    walk = O.scan_gdn if rule == "gdn" else O.scan
+    for b in range(B):
+        for h in range(H):
+            sel = {k: prod[k][b, :, h] for k in ("idx_w", "wt_w", "idx_r", "wt_r", "v", "gate",
+                                                  "alpha", "beta")}
+            _, _, o_log = walk(m0[b, h], sel["idx_w"], sel["wt_w"], sel["idx_r"], sel["wt_r"],
+                               sel["v"], sel["alpha"], sel["beta"], record=True)
+            assert_close(log_h[b, :, h], o_log, f"log walk {(b, h)}")
+            og, _, odM = O.scan_backward(st_T[b, h], log_h[b, :, h], sel["idx_w"], sel["wt_w"],
+                                         sel["idx_r"], sel["wt_r"], sel["v"], sel["alpha"],
+                                         sel["beta"], y_h[b, :, h], sel["gate"], gamma[h], 1e-6,
+                                         d_out[b, :, h], d_st[b, h], rule=rule)
+            for k in ("d_v", "d_gate", "d_alpha", "d_beta", "d_wt_w", "d_wt_r"):
+                got, exp = gh[k][b, :, h].astype(np.float64), og[k]
+                scale = max(np.abs(exp).max(), 1e-30)
+                assert np.all(np.abs(got - exp) <= 1e-4 * (np.abs(exp) + scale)), f"{k} {(b, h)}"
+            scale = max(np.abs(odM).max(), 1e-30)
+            assert np.all(np.abs(host(dS)[b, h] - odM) <= 1e-4 * (np.abs(odM) + scale)), \
+                f"d_state {(b, h)}"
 
 
 @pytest.mark.parametrize("rule", ["slot", "gdn"])

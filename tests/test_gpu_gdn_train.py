@@ -1,10 +1,12 @@
 """Training of the key-weighted (GDN-form) write rule: sdm_scan_train and
-sdm_scan_backward with SDM_FLAG_DELTA_GDN (direct schedule, split over column slices
-of the state) against the oracle.  The cases cover both slice widths (16 and 32
-columns), one slice per walk (norm and gate inside the walk) and several.
+sdm_scan_backward with SDM_FLAG_DELTA_GDN against the oracle.  The training forward
+takes the chunk schedule from 256 tokens with an fp32 log, else the direct schedule
+split over column slices of the state; the reverse walk is always the sliced one.  The
+cases cover both slice widths (16 and 32 columns), one slice per walk (norm and gate
+inside the walk) and several.
 
 * The training forward gives state, y and out bit-identical to the inference scan of
-  the same rule on the direct schedule, and its write log equals the oracle's
+  the same rule on the same schedule, and its write log equals the oracle's
   scan_gdn(record=True) log within the fp32 tolerance.
 * The backward, given the GPU's forward results, the log and seeded incoming
   gradients, matches the oracle's scan_backward(rule="gdn") run on the same values:
@@ -54,7 +56,7 @@ CASES = [
     (1, 64, 1, 16, 8, 8, 16, "random", 0),
     (2, 50, 2, 8, 32, 32, 64, "repeat", 0),    # N = 64, W = R = 32: heavy slot reuse
     (1, 40, 1, 12, 128, 100, 64, "random", 0),  # the largest W
-    (1, 300, 2, 40, 64, 64, 128, "random", 0),  # past the slot-owner threshold: still direct
+    (1, 300, 2, 40, 64, 64, 128, "random", 0),  # 300 tokens: the chunk schedule logs the rows
     (2, 17, 1, 4, 16, 16, 16, "random", 0),    # every slot in every write set
     (1, 30, 1, 16, 16, 16, 256, "same", 0),
     (1, 64, 2, 16, 16, 16, 32, "random", _lib.SDM_FLAG_LOG_FP8),
@@ -79,11 +81,12 @@ def test_gdn_training_matches_oracle(B, T, H, n, W, R, d_v, mode, logfl):
     gam = to_dev(gamma)
     state = to_dev(m0)
     out, y, log = ops.scan_train(d, pd, gam, state)
-    # the inference scan of the same rule on the direct schedule: identical results
+    # the inference scan of the same rule on the same schedule (the chunk one from 256
+    # tokens with an fp32 log, else the direct one): identical results
+    sched = (_lib.SDM_FLAG_SCAN_CHUNK if T >= 256 and not logfl else _lib.SDM_FLAG_SCAN_DIRECT)
     st_i = to_dev(m0)
-    out_i, y_i = ops.scan(_dims(B=B, T=T, H=H, n=n, W=W, R=R, d_v=d_v,
-                                flags=GDN | _lib.SDM_FLAG_SCAN_DIRECT), pd, gam, st_i,
-                          with_y_raw=True)
+    out_i, y_i = ops.scan(_dims(B=B, T=T, H=H, n=n, W=W, R=R, d_v=d_v, flags=GDN | sched), pd,
+                          gam, st_i, with_y_raw=True)
     torch.cuda.synchronize()
     assert torch.equal(state, st_i) and torch.equal(y, y_i) and torch.equal(out, out_i)
     fmt = ops.log_format(d)
@@ -129,11 +132,12 @@ def test_gdn_training_matches_oracle(B, T, H, n, W, R, d_v, mode, logfl):
     _close_to_scale(gh["d_norm_w"], d_gamma, "d_norm_w")
 
 
-def test_gdn_training_refuses_slot_owner_and_chunk_schedules():
+def test_gdn_training_refuses_slot_owner_schedules_and_chunk_quantised_logs():
     rng = np.random.default_rng(0)
     pd = {k: to_dev(v) for k, v in random_products(rng, 1, 64, 1, 16, 8, 8, 16).items()}
     st = torch.zeros((1, 1, 256, 16), device="cuda")
-    for fl in (_lib.SDM_FLAG_SCAN_TWO_PHASE, _lib.SDM_FLAG_SCAN_STREAM, _lib.SDM_FLAG_SCAN_CHUNK):
+    for fl in (_lib.SDM_FLAG_SCAN_TWO_PHASE, _lib.SDM_FLAG_SCAN_STREAM,
+               _lib.SDM_FLAG_SCAN_CHUNK | _lib.SDM_FLAG_LOG_FP8):
         with pytest.raises(_lib.SdmError) as e:
             ops.scan_train(_dims(T=64, flags=GDN | fl), pd, None, st)
         assert e.value.code == _lib.SDM_ERR_UNSUPPORTED
@@ -152,8 +156,10 @@ def test_gdn_quantised_log_over_staged_token_chunks(fmt):
     flag = _lib.SDM_FLAG_LOG_FP8 if fmt == "fp8" else _lib.SDM_FLAG_LOG_INT4
     pd = {k: to_dev(v) for k, v in prod.items()}
     st_a, st_b = to_dev(m0), to_dev(m0)
-    out_a, y_a, log_a = ops.scan_train(_dims(B=B, T=T, H=H, n=n, W=W, R=R, d_v=d_v, flags=GDN),
-                                       pd, None, st_a)
+    # quantised logs take the direct schedule: the fp32 run names it
+    out_a, y_a, log_a = ops.scan_train(
+        _dims(B=B, T=T, H=H, n=n, W=W, R=R, d_v=d_v, flags=GDN | _lib.SDM_FLAG_SCAN_DIRECT),
+        pd, None, st_a)
     out_b, y_b, log_b = ops.scan_train(
         _dims(B=B, T=T, H=H, n=n, W=W, R=R, d_v=d_v, flags=GDN | flag), pd, None, st_b)
     torch.cuda.synchronize()
