@@ -44,6 +44,9 @@ Chunkwise form ([163] section 八): scan_chunkwise computes scan / scan_gdn chun
 chunk from the chunk-start state and the tokens' pairwise sparse inner products
 (sparse_inner, a two-pointer merge over ascending slot ids); it is pinned against
 the sequential scans, which define the result, and sparse_inner by brute force.
+scan_backward_chunkwise is the reverse walk in the same chunks (the key-weighted
+rule's de from the transposed triangular system, then each touched slot walked back
+on its own); it is pinned against scan_backward.
 
 Storage variant: scan(..., store=round_bf16) keeps a bf16 state (every written
 row rounded to nearest-even bf16 from the exact value); round_bf16 is pinned
@@ -79,6 +82,9 @@ Pins (every function is checked against something other than itself):
                                        layer from x (x, W_proj, A, b_dt)
   tests/test_oracle_chunk_pins.py      scan_chunkwise against scan / scan_gdn for
                                        many chunk sizes, sparse_inner by brute force
+  tests/test_oracle_chunk_backward_pins.py
+                                       scan_backward_chunkwise against scan_backward
+                                       for many chunk sizes, identity gates
   tests/test_oracle_quant_pins.py      E4M3 against torch's float8_e4m3fn, int4
                                        packing by hand, error bounds
 No function of this module is "parity unpinned".
@@ -630,6 +636,127 @@ def scan_backward(state_T, log, idx_w, wt_w, idx_r, wt_r, v, alpha, beta, y, gat
         g["d_wt_w"][t] = beta[t] * dc
         dM[rows] = (alpha[t] * (1.0 - c))[:, None] * G
         M[rows] = m
+    return g, M, dM
+
+
+# ----------------------------------------------------------------------------
+# The same backward in the chunkwise form ([163] section 八: fixed-size chunks,
+# parallel inside a chunk, serial across chunks; the in-place update undone from
+# the log).  In the reverse walk above the only coupling between different slots
+# of one chunk is the key-weighted rule's de_u = beta_u sum_{j in W_u} k_{u,j} G_{u,j},
+# where G_{u,j} is dL/dM[j] just after token u's write.  Following slot j back from
+# the chunk end (writers u' of j after u, reads (t, j) at tokens t >= u):
+#   G_{u,j} = G_j(u, end] dM_end[j] + sum_t q_{t,j} G_j(u, t] dy_t
+#             - sum_{u'} k_{u',j} G_j(u, u'] de_{u'}          (key-weighted rule only)
+# so, with the forward's A and B (chunkwise form above),
+#   de_u = beta_u (h_u - sum_{t > u} B_{t,u} de_t),
+#   h_u  = sum_{t >= u} A_{t,u} dy_t + sum_{j in W_u} k_{u,j} G_j(u, end] dM_end[j]:
+# the transposed unit triangular system, solved by back substitution.  With de
+# known, every slot touched in the chunk is walked back on its own (reads, then
+# the write, of each token): the read gradients, the G of each write, the restored
+# row and the chunk-start gradient, the same per-entry steps as the reverse walk.
+# ----------------------------------------------------------------------------
+def _norm_gate_backward(y, gate, gamma_h, eps, d_out):
+    """dy, d_gate and the d_gamma terms of out = RMSNorm(y) gamma gate, per token."""
+    s = 1.0 / np.sqrt(np.mean(y * y, axis=1, keepdims=True) + eps)
+    yhat = y * s
+    u = d_out * gamma_h * gate
+    dy = s * (u - yhat * np.mean(u * yhat, axis=1, keepdims=True))
+    return dy, d_out * yhat * gamma_h, d_out * yhat * gate
+
+
+def scan_backward_chunkwise(state_T, log, idx_w, wt_w, idx_r, wt_r, v, alpha, beta, y, gate,
+                            gamma_h, eps, d_out, d_state, C: int, rule: str = "slot"):
+    """scan_backward() in the chunkwise form above, chunks of C tokens (the last one
+    ragged), walked from the last chunk to the first.  Same arguments and results."""
+    M = np.array(state_T, F64, copy=True)
+    dM = np.array(d_state, F64, copy=True)
+    idx_w, idx_r = np.asarray(idx_w), np.asarray(idx_r)
+    wt_w, wt_r = np.asarray(wt_w, F64), np.asarray(wt_r, F64)
+    v, y, gate = np.asarray(v, F64), np.asarray(y, F64), np.asarray(gate, F64)
+    alpha, beta = np.asarray(alpha, F64), np.asarray(beta, F64)
+    gamma_h, d_out, log = np.asarray(gamma_h, F64), np.asarray(d_out, F64), np.asarray(log, F64)
+    T, d_v = y.shape
+    gdn = rule == "gdn"
+    g = dict(d_v=np.zeros((T, d_v)), d_gate=np.zeros((T, d_v)), d_alpha=np.zeros(T),
+             d_beta=np.zeros(T), d_wt_w=np.zeros(idx_w.shape), d_wt_r=np.zeros(idx_r.shape),
+             d_gamma=np.zeros(d_v))
+    dy, g["d_gate"], dgam = _norm_gate_backward(y, gate, gamma_h, eps, d_out)
+    g["d_gamma"] = dgam.sum(axis=0)
+    starts = list(range(0, T, C))
+    for c0 in reversed(starts):
+        toks = range(c0, min(c0 + C, T))
+        end = toks[-1]
+        pos = {u: {int(j): k for k, j in enumerate(idx_w[u])} for u in toks}
+        rpos = {u: {int(j): k for k, j in enumerate(idx_r[u])} for u in toks}
+
+        def a(u, j):
+            k = pos[u].get(j)
+            if k is None:
+                return 1.0
+            return alpha[u] if gdn else alpha[u] * (1.0 - beta[u] * wt_w[u, k])
+
+        def G(j, s, t):                    # product of a(u, j) over s < u <= t
+            out = 1.0
+            for u in range(s + 1, t + 1):
+                out *= a(u, j)
+            return out
+
+        de = {u: np.zeros(d_v) for u in toks}
+        if gdn:
+            h = {}
+            for u in toks:
+                hu = np.zeros(d_v)
+                for t in range(u, end + 1):
+                    a_tu = sparse_inner(idx_r[t], idx_w[u], lambda p, q, t=t, u=u:
+                                        wt_r[t, p] * G(int(idx_r[t, p]), u, t) * wt_w[u, q])
+                    hu += a_tu * dy[t]
+                for k, j in enumerate(idx_w[u]):
+                    hu += wt_w[u, k] * G(int(j), u, end) * dM[j]
+                h[u] = hu
+            for u in reversed(toks):       # back substitution, B transposed
+                rhs = h[u].copy()
+                for t in range(u + 1, end + 1):
+                    b_tu = sparse_inner(idx_w[t], idx_w[u], lambda p, q, t=t, u=u:
+                                        wt_w[t, p] * G(int(idx_w[t, p]), u, t) * wt_w[u, q])
+                    rhs -= b_tu * de[t]
+                de[u] = beta[u] * rhs
+        # every slot the chunk touches, walked back on its own
+        Gw = {}
+        for j in sorted({int(j) for u in toks for j in idx_w[u]} |
+                        {int(j) for u in toks for j in idx_r[u]}):
+            D, F = dM[j].copy(), M[j].copy()
+            for t in reversed(toks):
+                k = rpos[t].get(j)
+                if k is not None:          # the read saw the row after t's write
+                    g["d_wt_r"][t, k] = F @ dy[t]
+                    D += wt_r[t, k] * dy[t]
+                k = pos[t].get(j)
+                if k is not None:
+                    Gw[t, k] = D.copy()
+                    F = log[t, k]
+                    if gdn:
+                        D = alpha[t] * (D - wt_w[t, k] * de[t])
+                    else:
+                        D = alpha[t] * (1.0 - beta[t] * wt_w[t, k]) * D
+            dM[j], M[j] = D, F
+        for u in toks:                     # per-token gradients from the G of each write
+            m = log[u]
+            Gu = np.array([Gw[u, k] for k in range(idx_w.shape[1])])
+            if gdn:
+                k = wt_w[u]
+                e = v[u] - alpha[u] * (k @ m)
+                g["d_v"][u] = de[u]
+                g["d_wt_w"][u] = beta[u] * (Gu @ e) - alpha[u] * (m @ de[u])
+                g["d_beta"][u] = k @ (Gu @ e)
+                g["d_alpha"][u] = np.sum((Gu - np.outer(k, de[u])) * m)
+            else:
+                c = beta[u] * wt_w[u]
+                g["d_v"][u] = c @ Gu
+                dc = np.sum(Gu * (v[u][None, :] - alpha[u] * m), axis=1)
+                g["d_alpha"][u] = np.sum((1.0 - c)[:, None] * Gu * m)
+                g["d_beta"][u] = wt_w[u] @ dc
+                g["d_wt_w"][u] = beta[u] * dc
     return g, M, dM
 
 
