@@ -609,8 +609,8 @@ def train_main(args):
     kernels_ms = {k: {"avg": float(np.mean(v)), "launches": len(v)} for k, v in per_kernel.items()}
     kernels_ms["proj_grad_gemms_blas"] = {
         "avg": float(np.mean([a.elapsed_time(b) for a, b in gemm_ms])), "launches": len(gemm_ms)}
-    back = next(k for k in ("stream_backward", "gdn_slices_backward", "scan_backward")
-                if k in kernels_ms)
+    back = next(k for k in ("stream_backward", "chunk_backward", "gdn_slices_backward",
+                            "scan_backward") if k in kernels_ms)
     back_ms = kernels_ms[back]["avg"] * kernels_ms[back]["launches"] / args.steps
     tokens = wl.tokens
     # per token and head: M and dM read, dM written per read; log and dM read, dM and M

@@ -370,12 +370,19 @@ SDM_API int32_t sdm_forward_noalloc(const sdm_dims* dims, const void* x, const v
  * accesses of each slot in reverse, any log format;
  * else (or with SDM_FLAG_SCAN_DIRECT) one workgroup per (b, h), tokens in
  * lock-step; SDM_FLAG_SCAN_CHUNK picks by length as no flag does.  The log of any
- * forward schedule serves any backward one.  The key-weighted rule (SDM_FLAG_DELTA_GDN) always walks directly, one
- * workgroup per (b, h, column slice) as its forward; its write is undone per token
- * with m the logged rows, m~ = alpha m, e = v - sum k m~, G = dL/dM rows:
- * d_v = beta sum k G = de, dm~ = G - k de, d_k = beta <G, e> - <de, m~>,
- * d_beta = sum k <G, e>, d_alpha = sum <dm~, m>, dL/dm = alpha dm~ (the dot products
- * over d_v summed from per-slice shares in slice order).
+ * forward schedule serves any backward one.  The key-weighted rule
+ * (SDM_FLAG_DELTA_GDN) undoes its write per token with m the logged rows,
+ * m~ = alpha m, e = v - sum k m~, G = dL/dM rows: d_v = beta sum k G = de,
+ * dm~ = G - k de, d_k = beta <G, e> - <de, m~>, d_beta = sum k <G, e>,
+ * d_alpha = sum <dm~, m>, dL/dm = alpha dm~ (the dot products over d_v summed from
+ * per-slice shares in slice order).  From 256 tokens (or with SDM_FLAG_SCAN_CHUNK),
+ * with an fp32 log and W, R <= 64, it walks chunks of 32 tokens in reverse (the m.163.com
+ * article on arXiv 2607.07386, section 八): per chunk de solves the transposed
+ * triangular system of the forward's chunk form, de = Tm^T h with
+ * h_u = sum_{t >= u} A_{t,u} dy_t + sum_j k_{u,j} G_j(u, end] dL/dM_end[j], and then each
+ * slot the chunk touches is walked back on its own (needs ascending ids, as the
+ * chunk forward).  Otherwise (or with SDM_FLAG_SCAN_DIRECT) one workgroup per
+ * (b, h, column slice) walks the tokens in reverse.
  * Every sum runs in a fixed order, so results are bit-reproducible, except d_v on
  * the stream schedule (summed with float atomics: reproducible up to fp32 summation
  * order).  Other flags as for sdm_scan_train.

@@ -627,14 +627,26 @@ hipError_t launch_gdn_slice_backward(const sdm_dims& d, const ScanBackArgs& a, f
       default: return hipErrorInvalidValue;
     }
   }
-  {
-    KernelTimer kt("gdn_back_reduce", st);
-    hipLaunchKernelGGL(gdn_slice_reduce_kernel, dim3((unsigned)((A.rows + 3) / 4)), dim3(256), 0,
-                       st, A);
-  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_gdn_back_reduce(a, A.pr, A.pw, A.pa, S, st)) != hipSuccess) return e;
   if (d_norm_w) return launch_gamma_blocks(a, gpart, d_norm_w, st);
   return hipSuccess;
+}
+
+hipError_t launch_gdn_back_reduce(const ScanBackArgs& a, float* pr, float2* pw, float* pa, int S,
+                                  hipStream_t st) {
+  SliceBackArgs A;
+  A.s = a;
+  A.dy = nullptr;
+  A.pr = pr;
+  A.pw = pw;
+  A.pa = pa;
+  A.rows = a.B * a.T * a.H;
+  A.S = S;
+  KernelTimer kt("gdn_back_reduce", st);
+  hipLaunchKernelGGL(gdn_slice_reduce_kernel, dim3((unsigned)((A.rows + 3) / 4)), dim3(256), 0, st,
+                     A);
+  return hipGetLastError();
 }
 
 }  // namespace sdm

@@ -363,7 +363,9 @@ static sdm_dims train_dims(const sdm_dims* d) {
 // Backward workspace: per-walk d_gamma partials (direct schedule), or the stream
 // schedule's buckets, dy, per-slice partial dots and per-part d_v.
 static size_t backward_ws_bytes(const sdm_dims* d) {
-  if (d->flags & SDM_FLAG_DELTA_GDN) return align_up(gdn_slice_backward_workspace_bytes(*d));
+  if (d->flags & SDM_FLAG_DELTA_GDN)
+    return align_up(gdn_back_uses_chunk(*d) ? chunk_backward_workspace_bytes(*d)
+                                            : gdn_slice_backward_workspace_bytes(*d));
   if (backward_uses_stream(*d))
     return align_up(stream_backward_workspace_bytes(*d));
   return align_up((size_t)d->B * d->H * d->d_v * 4);
@@ -519,7 +521,9 @@ int32_t sdm_scan_backward(const sdm_dims* d, const sdm_sel* in, const float* nor
   TimingScope timing(d);
   (void)hipGetLastError();
   if (d->flags & SDM_FLAG_DELTA_GDN)
-    return hip_status(launch_gdn_slice_backward(*d, a, g->d_norm_w, ws, (hipStream_t)stream));
+    return hip_status(gdn_back_uses_chunk(*d)
+                          ? launch_chunk_backward(*d, a, g->d_norm_w, ws, (hipStream_t)stream)
+                          : launch_gdn_slice_backward(*d, a, g->d_norm_w, ws, (hipStream_t)stream));
   if (backward_uses_stream(*d))
     return hip_status(launch_stream_backward(*d, a, g->d_norm_w, ws, (hipStream_t)stream));
   return hip_status(launch_scan_backward(a, g->d_norm_w, (hipStream_t)stream));

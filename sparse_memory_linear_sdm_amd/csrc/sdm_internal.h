@@ -321,6 +321,16 @@ hipError_t launch_scan_backward(const ScanBackArgs& a, float* d_norm_w, hipStrea
 size_t gdn_slice_backward_workspace_bytes(const sdm_dims& d);
 hipError_t launch_gdn_slice_backward(const sdm_dims& d, const ScanBackArgs& a, float* d_norm_w,
                                      void* ws, hipStream_t st);
+// Per token: the per-slice shares of the key-weighted reverse walks (pr [S][rows][R],
+// pw [S][rows][W] (<G, e>, <de, m>), pa [S][rows]) summed in slice order into d_wt_r,
+// d_wt_w, d_alpha and d_beta.
+hipError_t launch_gdn_back_reduce(const ScanBackArgs& a, float* pr, float2* pw, float* pa, int S,
+                                  hipStream_t st);
+// The key-weighted reverse walk on the chunk schedule (scan_chunk.hip).
+bool gdn_back_uses_chunk(const sdm_dims& d);
+size_t chunk_backward_workspace_bytes(const sdm_dims& d);
+hipError_t launch_chunk_backward(const sdm_dims& d, const ScanBackArgs& a, float* d_norm_w,
+                                 void* ws, hipStream_t st);
 // Norm/gate backward of all tokens (scan_stream_backward.hip): dy [B, T, H, d_v],
 // d_gate, and d_gamma partials [B*H][norm_backward_blocks(T)][d_v]; then their sum.
 int norm_backward_blocks(int64_t T);

@@ -232,12 +232,23 @@ def test_training_entries_validate_first(lib):
         ctypes.byref(dd), ctypes.byref(s), None, FAKE, FAKE, FAKE, FAKE, sc, FAKE,
         ctypes.byref(grads), ws, nb, None)
     assert back(dd=_d(T=64, flags=_lib.SDM_FLAG_DELTA_GDN), ws=None) == _lib.SDM_ERR_WORKSPACE
-    # its reverse walk is the sliced direct one from any length: dy and every slice's
+    # its reverse walks (chunkwise from 256 tokens, else sliced): dy and every slice's
     # share of the dot products (one slice at d_v = 16) come from the workspace
     dg = _d(T=512, flags=_lib.SDM_FLAG_DELTA_GDN)
     ng = lib.sdm_workspace_bytes(ctypes.byref(dg), _lib.SDM_ENTRY_SCAN_BACKWARD)
     assert ng >= dg.B * dg.T * dg.H * (dg.d_v * 4 + dg.R * 4 + dg.W * 8 + 4)
     assert back(dd=dg, nb=ng - 1) == _lib.SDM_ERR_WORKSPACE
+    # which reverse walk: the chunk one from 256 tokens (or with the chunk flag) with an
+    # fp32 log and W, R <= 64, each walk with a workspace of its own size
+    gdn, chunk, direct = (_lib.SDM_FLAG_DELTA_GDN, _lib.SDM_FLAG_SCAN_CHUNK,
+                          _lib.SDM_FLAG_SCAN_DIRECT)
+    bw = lambda **kw: lib.sdm_workspace_bytes(ctypes.byref(_d(**kw)), _lib.SDM_ENTRY_SCAN_BACKWARD)
+    assert bw(T=512, flags=gdn | chunk) == ng != bw(T=512, flags=gdn | direct)
+    assert bw(T=255, flags=gdn) == bw(T=255, flags=gdn | direct) != bw(T=255, flags=gdn | chunk)
+    for fmt in (_lib.SDM_FLAG_LOG_FP8, _lib.SDM_FLAG_LOG_INT4):
+        assert bw(T=512, flags=gdn | fmt) == bw(T=512, flags=gdn | direct | fmt)
+    assert bw(T=512, W=65, flags=gdn) == bw(T=512, W=65, flags=gdn | direct)
+    assert bw(T=512, R=65, flags=gdn | chunk) == bw(T=512, R=65, flags=gdn | direct)
     # 8 slices of 16 columns for 2 x 2 walks of d_v = 128: 8 shares per dot product
     dg8 = _d(T=64, d_v=128, flags=_lib.SDM_FLAG_DELTA_GDN)
     ng8 = lib.sdm_workspace_bytes(ctypes.byref(dg8), _lib.SDM_ENTRY_SCAN_BACKWARD)
