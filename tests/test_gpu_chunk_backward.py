@@ -137,3 +137,58 @@ def test_chunk_backward_matches_oracle(B, T, H, n, W, R, d_v, mode, fwd):
             _close_to_scale(dSh[b, h], odM, f"d_state walk {(b, h)}")
     _close_to_scale(gh["d_norm_w"], d_gamma, "d_norm_w")
 
+
+
+def test_gdn_training_at_the_full_bench_size():
+    """The 1.4B-like layer at full size (8 x 4096 tokens, 4 heads, N = 131,044) with the
+    key-weighted rule, products from the GPU's own selection and the default schedules
+    (chunk training forward with its log, chunkwise reverse walk): two complete walks
+    against the oracle's reverse walk from the GPU's final state, log and y; M0
+    restored bit for bit for every walk; every walk's gradients against the sliced
+    direct reverse walk on the same log."""
+    from sparse_memory_linear_sdm_amd import dims_for, synth
+    from tests.gpu_util import layer_inputs
+    wl = synth.WORKLOADS["layer1p4b"]
+    h, dd = layer_inputs(wl, seed=13)
+    dm = dims_for(wl)
+    dm.flags |= GDN
+    p = ops.select(dm, dd["x"], dd["w_proj"], dd["A"], dd["b_dt"])
+    del dd["x"]
+    gam = dd["gamma"]
+    st = dd["m0"].unsqueeze(0).repeat(wl.B, 1, 1, 1)
+    _, y, log = ops.scan_train(dm, p, gam, st)
+    gen = torch.Generator(device=st.device).manual_seed(14)
+    d_out = torch.randn(y.shape, device=st.device, generator=gen)
+    d_st = torch.randn(st.shape, device=st.device, generator=gen) * 0.1
+    walks = [(0, 0), (wl.B - 1, wl.H - 1)]
+    keep = {(b, hh): (host(st[b, hh]), host(log["rows"][b, :, hh]), host(y[b, :, hh]),
+                      host(d_out[b, :, hh]), host(d_st[b, hh])) for b, hh in walks}
+    st_s = st.clone()
+    dS, dS_s = d_st.clone(), d_st.clone()
+    g = ops.scan_backward(dm, p, gam, st, dS, y, log, d_out)
+    torch.cuda.synchronize()
+    say("  chunkwise reverse walk done")
+    for b in range(wl.B):
+        for hh in range(wl.H):
+            assert torch.equal(st[b, hh], dd["m0"][hh]), f"M0 not restored for walk {(b, hh)}"
+    ds = type(dm).from_buffer_copy(dm)
+    ds.flags = dm.flags | DIRECT
+    g_s = ops.scan_backward(ds, p, gam, st_s, dS_s, y, log, d_out)
+    torch.cuda.synchronize()
+    assert torch.equal(st_s, st)
+    for k in ("d_v", "d_alpha", "d_beta", "d_wt_w", "d_wt_r"):
+        _close_to_scale(host(g[k]), host(g_s[k]), f"{k} vs the sliced walk")
+    _close_to_scale(host(dS), host(dS_s), "d_state vs the sliced walk")
+    del g_s, dS_s, st_s
+    m0_h = host(dd["m0"])
+    for (b, hh), (mT, lg, yy, do, dst) in keep.items():
+        sel = {k: host(p[k][b, :, hh]) for k in ("idx_w", "wt_w", "idx_r", "wt_r", "v", "gate",
+                                                 "alpha", "beta")}
+        og, oM0, odM = O.scan_backward(mT, lg, sel["idx_w"], sel["wt_w"], sel["idx_r"],
+                                       sel["wt_r"], sel["v"], sel["alpha"], sel["beta"], yy,
+                                       sel["gate"], h["gamma"][hh], wl.eps, do, dst, rule="gdn")
+        assert np.array_equal(oM0, m0_h[hh])
+        for k in ("d_v", "d_gate", "d_alpha", "d_beta", "d_wt_w", "d_wt_r"):
+            _close_to_scale(host(g[k][b, :, hh]), og[k], f"{k} walk {(b, hh)}")
+        _close_to_scale(host(dS[b, hh]), odM, f"d_state walk {(b, hh)}")
+        say(f"  walk {(b, hh)} matches the oracle")
