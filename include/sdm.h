@@ -17,9 +17,10 @@
  * ---------------------------------------
  *  - Every pointer argument is a DEVICE pointer (allocated by the caller, e.g. as a
  *    torch tensor) unless stated otherwise; `dims` and `sel` structs live in host
- *    memory.  The library never allocates, frees or keeps device memory and is
- *    reentrant across streams.  Its only global state is the host-side record of
- *    SDM_FLAG_TIMING (HIP events, created on first use).
+ *    memory.  The library never allocates or frees device memory and is reentrant
+ *    across streams.  Its global state: the host-side record of SDM_FLAG_TIMING (HIP
+ *    events, created on first use), and the fixed device array that only
+ *    sdm_forward_noalloc uses as its workspace (with its per-device address).
  *  - `stream` is a hipStream_t (NULL = the default stream).  All work is enqueued on it
  *    asynchronously; no call synchronises the host, allocates, or copies through
  *    pageable memory, so calls may be captured into a HIP graph.
