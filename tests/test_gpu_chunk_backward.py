@@ -192,3 +192,49 @@ def test_gdn_training_at_the_full_bench_size():
             _close_to_scale(host(g[k][b, :, hh]), og[k], f"{k} walk {(b, hh)}")
         _close_to_scale(host(dS[b, hh]), odM, f"d_state walk {(b, hh)}")
         say(f"  walk {(b, hh)} matches the oracle")
+
+
+def test_gdn_chunk_training_at_the_8b_slot_space():
+    """The 8B-like slot space (N = 1024^2, W = R = 64, d_v = 128; the largest row offsets
+    of the chunk kernels) with the key-weighted rule on the chunk schedule, 2 x 2 walks
+    of 1200 tokens (38 chunks, the last ragged): inference state and out against the
+    oracle's walk, then the training forward and the chunkwise reverse walk against the
+    oracle's reverse walk on one walk, M0 restored bit for bit for every walk."""
+    from tests.test_gpu_chunk import random_products_fast
+    rng = np.random.default_rng(17)
+    B, T, H, n, W, R, d_v = 2, 1200, 2, 1024, 64, 64, 128
+    N = n * n
+    prod = random_products_fast(rng, B, T, H, n, W, R, d_v)
+    m0 = (rng.standard_normal((B, H, N, d_v)) * 0.02).astype(np.float32)
+    gamma = rng.uniform(0.5, 1.5, (H, d_v)).astype(np.float32)
+    d = _dims(B=B, T=T, H=H, n=n, W=W, R=R, d_v=d_v, flags=GDN | CHUNK)
+    pd = {k: to_dev(v) for k, v in prod.items()}
+    gam = to_dev(gamma)
+    state = to_dev(m0)
+    out, y, log = ops.scan_train(d, pd, gam, state)
+    torch.cuda.synchronize()
+    b, hh = B - 1, H - 1
+    sel = {k: prod[k][b, :, hh] for k in ("idx_w", "wt_w", "idx_r", "wt_r", "v", "gate", "alpha",
+                                          "beta")}
+    y_o, M_o, log_o = O.scan_gdn(m0[b, hh], sel["idx_w"], sel["wt_w"], sel["idx_r"], sel["wt_r"],
+                                 sel["v"], sel["alpha"], sel["beta"], record=True)
+    st_T = host(state)
+    _close_to_scale(st_T[b, hh], M_o, "state", rel=1e-5)
+    _close_to_scale(host(y)[b, :, hh], y_o, "y", rel=1e-5)
+    log_h = host(log["rows"])
+    _close_to_scale(log_h[b, :, hh], log_o, "log", rel=1e-5)
+    del M_o, log_o
+    d_out = rng.standard_normal((B, T, H, d_v)).astype(np.float32)
+    d_st = (rng.standard_normal((B, H, N, d_v)) * 0.1).astype(np.float32)
+    dS = to_dev(d_st)
+    g = ops.scan_backward(d, pd, gam, state, dS, y, log, to_dev(d_out))
+    torch.cuda.synchronize()
+    assert torch.equal(state, to_dev(m0)), "initial state not restored bit for bit"
+    og, oM0, odM = O.scan_backward(st_T[b, hh], log_h[b, :, hh], sel["idx_w"], sel["wt_w"],
+                                   sel["idx_r"], sel["wt_r"], sel["v"], sel["alpha"], sel["beta"],
+                                   host(y)[b, :, hh], sel["gate"], gamma[hh], 1e-6,
+                                   d_out[b, :, hh], d_st[b, hh], rule="gdn")
+    assert np.array_equal(oM0, m0[b, hh])
+    for k in ("d_v", "d_gate", "d_alpha", "d_beta", "d_wt_w", "d_wt_r"):
+        _close_to_scale(host(g[k][b, :, hh]), og[k], f"{k}")
+    _close_to_scale(host(dS)[b, hh], odM, "d_state")
