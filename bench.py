@@ -52,6 +52,9 @@ SCAN_SOURCE = os.path.join(CSRC, "scan_stream.hip")
 MFMA_FILE = os.path.join(ROOT, "profiles", "proj_gemm_mfma_layer1p4b.txt")
 BACK_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_backward_traffic_layer1p4b.txt")
 BACK_SOURCE = os.path.join(CSRC, "scan_stream_backward.hip")
+CHUNK_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_walk_traffic_layer1p4b_gdn.txt")
+CHUNK_BACK_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_backward_traffic_layer1p4b_gdn.txt")
+CHUNK_SOURCE = os.path.join(CSRC, "scan_chunk.hip")
 GEMM_SOURCE = os.path.join(CSRC, "proj_gemm.hip")
 SELECT_FILE = os.path.join(ROOT, "profiles", "select_valu_layer1p4b.txt")
 SELECT_SOURCE = os.path.join(CSRC, "select.hip")
@@ -86,6 +89,14 @@ def measured_traffic(workload: str):
 def measured_back_traffic(workload: str):
     """Counter-measured HBM bytes of one reverse-walk launch (current source)."""
     f = _profile_fields(BACK_TRAFFIC_FILE, BACK_SOURCE) if workload == "layer1p4b" else None
+    return int(float(f["traffic_bytes"])) if f else None
+
+
+def measured_chunk_traffic(workload: str, backward: bool):
+    """Counter-measured HBM bytes of one key-weighted chunk-walk (or chunkwise reverse
+    walk) launch, if taken on the current source."""
+    path = CHUNK_BACK_TRAFFIC_FILE if backward else CHUNK_TRAFFIC_FILE
+    f = _profile_fields(path, CHUNK_SOURCE) if workload == "layer1p4b" else None
     return int(float(f["traffic_bytes"])) if f else None
 
 
@@ -385,7 +396,10 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": (measured_traffic(wl.name)
                                  if args.state == "fp32" and not gdn and
-                                 scan_kernel == "two_phase_scan" else None),
+                                 scan_kernel == "two_phase_scan" else
+                                 measured_chunk_traffic(wl.name, False)
+                                 if args.state == "fp32" and gdn and scan_kernel == "chunk_walk"
+                                 else None),
                      "algorithmic_bytes_per_launch":
                          slot_bytes * args.steps / kernels_ms[scan_kernel]["launches"]},
     }
@@ -641,7 +655,9 @@ def train_main(args):
         "kernels_ms": kernels_ms,
         "roofline": {"bound": "hbm", "kernel": back, "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_back_traffic(wl.name) if back == "stream_backward" else None,
+                     "traffic": (measured_back_traffic(wl.name) if back == "stream_backward"
+                                 else measured_chunk_traffic(wl.name, True)
+                                 if back == "chunk_backward" else None),
                      "algorithmic_bytes_per_launch":
                          back_bytes * args.steps / kernels_ms[back]["launches"]},
     }
