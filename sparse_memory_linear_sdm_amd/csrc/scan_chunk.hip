@@ -31,9 +31,11 @@
 //   merging every pair of lists: the same sums, but a merge walks all 2W entries of
 //   each of the C^2/2 pairs although, with N >> C W, almost no pair shares a slot.
 // chunk_walk: one workgroup per (walk, 16-column slice of d_v), the walk's chunks in
-//   order: x, the reads and the chunk-end rows.  The columns of the state evolve
-//   independently under both rules, so slices need no communication.  y then goes
-//   through the norm/gate kernel.
+//   order: x, the reads and the chunk-end rows (in training also the write log).  The
+//   columns of the state evolve independently under both rules, so slices need no
+//   communication.  y then goes through the norm/gate kernel.
+// chunk_back (training, key-weighted rule): the reverse walk in the same chunks, from
+//   chunk_prep's matrices and its chains of each slot's reads (see below).
 #include "sdm_internal.h"
 
 namespace sdm {
@@ -685,9 +687,9 @@ __global__ __launch_bounds__(kWalkThreads) void chunk_walk_kernel(ChunkArgs a) {
 // One workgroup of 512 threads per (walk, 16-column slice).  Lane group (token u,
 // share s) owns write and read entries s, s + GPT, ... of u: it gathers the dM_end and
 // logged rows of its write entries for h and for e_u = v_u - alpha_u sum k m, and
-// walks the slots whose last writer they are, loading those rows again (recently
-// read, so mostly from cache; a whole token's rows do not fit in the registers
-// across the solve).  Each slot a token only reads is walked by its last read.  Dot products over d_v go out as per-slice
+// walks the slots whose last writer they are, loading those rows again (a whole
+// token's rows do not fit in the registers across the solve).  Each slot a token
+// only reads is walked by its last read.  Dot products over d_v go out as per-slice
 // shares (d_wt_r, (<G, e>, <de, m>), d_alpha), summed in slice order afterwards.
 constexpr int kBackThreads = 512;
 constexpr int kBackEPG = 16;  // entries of each list a lane group owns: W, R <= 64
