@@ -1,9 +1,9 @@
 """Training of the key-weighted (GDN-form) write rule: sdm_scan_train and
-sdm_scan_backward with SDM_FLAG_DELTA_GDN against the oracle.  The training forward
-takes the chunk schedule from 256 tokens with an fp32 log, else the direct schedule
-split over column slices of the state; the reverse walk is always the sliced one.  The
-cases cover both slice widths (16 and 32 columns), one slice per walk (norm and gate
-inside the walk) and several.
+sdm_scan_backward with SDM_FLAG_DELTA_GDN against the oracle.  Both walks take the
+chunk schedule from 256 tokens with an fp32 log (the reverse walk with W, R <= 64;
+tests/test_gpu_chunk_backward.py covers it on its own), else the direct schedule split
+over column slices of the state.  The cases cover both slice widths (16 and 32
+columns), one slice per walk (norm and gate inside the walk) and several.
 
 * The training forward gives state, y and out bit-identical to the inference scan of
   the same rule on the same schedule, and its write log equals the oracle's
