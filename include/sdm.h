@@ -103,8 +103,9 @@ extern "C" {
    any is written, so it runs the direct schedule (each walk split over 16- or
    32-column slices of the state, which evolve independently under the rule) or the
    chunk schedule (SDM_FLAG_SCAN_CHUNK, its default from 256 tokens with an fp32
-   state); combined with SDM_FLAG_SCAN_STREAM or SDM_FLAG_SCAN_TWO_PHASE it is
-   SDM_ERR_UNSUPPORTED. */
+   state while B H d_v / 16 <= 1024: beyond that many (walk, slice) workgroups the
+   sliced direct walk is faster); combined with SDM_FLAG_SCAN_STREAM or
+   SDM_FLAG_SCAN_TWO_PHASE it is SDM_ERR_UNSUPPORTED. */
 #define SDM_FLAG_DELTA_GDN 16
 /* storage flag (sdm_dims.flags; sdm_scan and sdm_forward): the state buffer holds
    bf16 values.  The arithmetic stays fp32; each written row element is rounded to
@@ -350,8 +351,9 @@ SDM_API int32_t sdm_forward_noalloc(const sdm_dims* dims, const void* x, const v
  *   and the key-weighted rule's equal the others up to fp32 rounding order.  fp32
  *   state only (SDM_FLAG_STATE_BF16 and SDM_FLAG_STATE_FP8 give
  *   SDM_ERR_UNSUPPORTED).  The key-weighted rule (SDM_FLAG_DELTA_GDN) takes the
- *   chunk schedule from 256 tokens with an fp32 log, else the direct one; with
- *   SDM_FLAG_SCAN_STREAM or _TWO_PHASE it is SDM_ERR_UNSUPPORTED.
+ *   schedule sdm_scan would (the chunk one from 256 tokens while B H d_v / 16 <=
+ *   1024) with an fp32 log, else the direct one; with SDM_FLAG_SCAN_STREAM or
+ *   _TWO_PHASE it is SDM_ERR_UNSUPPORTED.
  *
  * sdm_scan_backward: gradients of that call, walking the tokens in reverse (per
  * token: the norm and gate, the read, then the write, whose overwritten rows are
@@ -376,8 +378,9 @@ SDM_API int32_t sdm_forward_noalloc(const sdm_dims* dims, const void* x, const v
  * m~ = alpha m, e = v - sum k m~, G = dL/dM rows: d_v = beta sum k G = de,
  * dm~ = G - k de, d_k = beta <G, e> - <de, m~>, d_beta = sum k <G, e>,
  * d_alpha = sum <dm~, m>, dL/dm = alpha dm~ (the dot products over d_v summed from
- * per-slice shares in slice order).  From 256 tokens (or with SDM_FLAG_SCAN_CHUNK),
- * with an fp32 log and W, R <= 64, it walks chunks of 32 tokens in reverse (the m.163.com
+ * per-slice shares in slice order).  With SDM_FLAG_SCAN_CHUNK, or from 256 tokens
+ * while B H d_v / 16 <= 256 (one workgroup per CU; beyond that the sliced walk is
+ * faster), with an fp32 log and W, R <= 64, it walks chunks of 32 tokens in reverse (the m.163.com
  * article on arXiv 2607.07386, section 八): per chunk de solves the transposed
  * triangular system of the forward's chunk form, de = Tm^T h with
  * h_u = sum_{t >= u} A_{t,u} dy_t + sum_j k_{u,j} G_j(u, end] dL/dM_end[j], and then each

@@ -1056,12 +1056,22 @@ ChunkWs chunk_ws(const sdm_dims& d) {
 
 }  // namespace
 
+// The chunk schedule pays while its (walk, 16-column slice) workgroups run in few
+// rounds: the chunk walk up to 1024 of them (two per CU), the chunkwise reverse walk
+// up to 256 (one per CU).  Beyond that the sliced direct walks, several small
+// workgroups per CU, are faster (32,768 tokens in all: forward 6.6 vs 4.0 ms at 256
+// walks and 4.6 vs 6.0 ms at 128; reverse walk 11.6 vs 9.6 ms at 64 walks and 12.2
+// vs 13.9 ms at 32).
+constexpr int64_t kChunkWalkBlocks = 1024;
+constexpr int64_t kChunkBackBlocks = 256;
+int64_t chunk_blocks(const sdm_dims& d) { return d.B * d.H * (d.d_v / kSlice); }
+
 // Asked for, or the key-weighted rule on an fp32 state from 256 tokens (where it is
-// several times faster than the direct walk).
+// several times faster than the direct walk) while the walks are few enough.
 bool scan_uses_chunk(const sdm_dims& d) {
   if (d.flags & SDM_FLAG_SCAN_CHUNK) return true;
   return (d.flags & SDM_FLAG_DELTA_GDN) && !(d.flags & (SDM_FLAG_SCAN_DIRECT | SDM_FLAG_STATE_BF16)) &&
-         d.T >= kStreamRound;
+         d.T >= kStreamRound && chunk_blocks(d) <= kChunkWalkBlocks;
 }
 
 size_t chunk_workspace_bytes(const sdm_dims& d) { return chunk_ws(d).total; }
@@ -1170,13 +1180,15 @@ ChunkBackWs chunk_back_ws(const sdm_dims& d) {
 }
 }  // namespace
 
-// The key-weighted rule's backward on the chunk schedule: from 256 tokens (or with
-// SDM_FLAG_SCAN_CHUNK) with an fp32 log and W, R <= 64 (the lane groups' entries);
-// otherwise the sliced direct reverse walk.
+// The key-weighted rule's backward on the chunk schedule: with SDM_FLAG_SCAN_CHUNK, or
+// from 256 tokens while the walks are few enough, with an fp32 log and W, R <= 64 (the
+// lane groups' entries); otherwise the sliced direct reverse walk.
 bool gdn_back_uses_chunk(const sdm_dims& d) {
   if (!(d.flags & SDM_FLAG_DELTA_GDN)) return false;
   if (d.flags & (SDM_FLAG_SCAN_DIRECT | SDM_FLAG_LOG_FP8 | SDM_FLAG_LOG_INT4)) return false;
-  if (!(d.flags & SDM_FLAG_SCAN_CHUNK) && d.T < kStreamRound) return false;
+  if (!(d.flags & SDM_FLAG_SCAN_CHUNK) &&
+      (d.T < kStreamRound || chunk_blocks(d) > kChunkBackBlocks))
+    return false;
   constexpr size_t kLds = 160 * 1024;
   return d.W <= 64 && d.R <= 64 && d.d_v % kSlice == 0 && back_lds_bytes(d.W, d.R) <= kLds &&
          prep_lds_bytes(d.W, d.R) <= kLds;

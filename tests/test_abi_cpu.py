@@ -249,6 +249,17 @@ def test_training_entries_validate_first(lib):
         assert bw(T=512, flags=gdn | fmt) == bw(T=512, flags=gdn | direct | fmt)
     assert bw(T=512, W=65, flags=gdn) == bw(T=512, W=65, flags=gdn | direct)
     assert bw(T=512, R=65, flags=gdn | chunk) == bw(T=512, R=65, flags=gdn | direct)
+    # by default the chunk walks run while their (walk, 16-column slice) workgroups are
+    # few enough: at most 256 for the reverse walk, 1024 for the forward walks
+    big = dict(T=512, d_v=128, H=4)
+    assert bw(B=8, flags=gdn, **big) != bw(B=8, flags=gdn | direct, **big)       # 256
+    assert bw(B=16, flags=gdn, **big) == bw(B=16, flags=gdn | direct, **big)     # 512
+    assert bw(B=16, flags=gdn | chunk, **big) != bw(B=16, flags=gdn | direct, **big)
+    for entry in (_lib.SDM_ENTRY_SCAN, _lib.SDM_ENTRY_SCAN_TRAIN):
+        fw = lambda **kw: lib.sdm_workspace_bytes(ctypes.byref(_d(**kw)), entry)
+        assert fw(B=32, flags=gdn, **big) == fw(B=32, flags=gdn | chunk, **big)   # 1024
+        assert fw(B=64, flags=gdn, **big) == fw(B=64, flags=gdn | direct, **big)  # 2048
+        assert fw(B=64, flags=gdn | chunk, **big) != fw(B=64, flags=gdn | direct, **big)
     # 8 slices of 16 columns for 2 x 2 walks of d_v = 128: 8 shares per dot product
     dg8 = _d(T=64, d_v=128, flags=_lib.SDM_FLAG_DELTA_GDN)
     ng8 = lib.sdm_workspace_bytes(ctypes.byref(dg8), _lib.SDM_ENTRY_SCAN_BACKWARD)
