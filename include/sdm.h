@@ -89,6 +89,9 @@ extern "C" {
                                      a walk's groups split over workgroups */
 #define SDM_FLAG_SCAN_TWO_PHASE 4 /* slot-owner writes, then token-major reads of the
                                      slots each workgroup owns */
+/* Without a schedule flag, sdm_scan and sdm_forward run the per-slot rule on the
+   two-phase schedule from 16 tokens, and on the direct one below that or from 1024
+   walks (B H: the lock-step workgroups then fill the chip several times over). */
 /* instrumentation flag (sdm_dims.flags, may be combined with one schedule flag):
    every kernel launch of the call is bracketed by a pair of HIP events recorded on
    the call's stream; sdm_timing_read returns the durations.  Results are the same
