@@ -371,9 +371,9 @@ SDM_API int32_t sdm_forward_noalloc(const sdm_dims* dims, const void* x, const v
  *           [B,T,H,d_v], d_alpha and d_beta [B,T,H]; d_norm_w [H, d_v] (summed over
  *           the batch) or NULL
  *   ws      >= sdm_workspace_bytes(dims, SDM_ENTRY_SCAN_BACKWARD) bytes
- * Schedules: the slot-owner walk from 256 tokens (or with SDM_FLAG_SCAN_STREAM or
- * SDM_FLAG_SCAN_TWO_PHASE, which both select it): slot-owner lane groups walk the
- * accesses of each slot in reverse, any log format;
+ * Schedules: the slot-owner walk from 256 tokens while B H < 512 (or with
+ * SDM_FLAG_SCAN_STREAM or SDM_FLAG_SCAN_TWO_PHASE, which both select it): slot-owner
+ * lane groups walk the accesses of each slot in reverse, any log format;
  * else (or with SDM_FLAG_SCAN_DIRECT) one workgroup per (b, h), tokens in
  * lock-step; SDM_FLAG_SCAN_CHUNK picks by length as no flag does.  The log of any
  * forward schedule serves any backward one.  The key-weighted rule

@@ -343,6 +343,17 @@ def test_default_scan_schedule_by_walks(lib):
     assert ws(B=2, H=2, T=15) == 0
 
 
+def test_default_backward_schedule_by_walks(lib):
+    # the per-slot reverse walk: slot-owner (its workspace holds buckets and partial
+    # dots) from 256 tokens while B H < 512, else the direct one (d_gamma partials only)
+    bw = lambda **kw: lib.sdm_workspace_bytes(ctypes.byref(_d(**kw)), _lib.SDM_ENTRY_SCAN_BACKWARD)
+    direct = lambda B, H, d_v=16: B * H * d_v * 4
+    assert bw(B=64, H=4, T=512) > direct(64, 4)
+    assert bw(B=128, H=4, T=512) == direct(128, 4)
+    assert bw(B=128, H=4, T=512, flags=_lib.SDM_FLAG_SCAN_STREAM) > direct(128, 4)
+    assert bw(B=2, H=2, T=255) == direct(2, 2)
+
+
 def test_workspace_sizes_of_the_workloads(lib):
     for name, wl in synth.WORKLOADS.items():
         d = dims_for(wl)
