@@ -105,7 +105,7 @@ extern "C" {
    arXiv 2607.07386, section 二).  It needs every row of a token's write set before
    any is written, so it runs the direct schedule (each walk split over 16- or
    32-column slices of the state, which evolve independently under the rule) or the
-   chunk schedule (SDM_FLAG_SCAN_CHUNK, its default from 256 tokens with an fp32
+   chunk schedule (SDM_FLAG_SCAN_CHUNK, its default from 64 tokens with an fp32
    state while B H d_v / 16 <= 1024: beyond that many (walk, slice) workgroups the
    sliced direct walk is faster); combined with SDM_FLAG_SCAN_STREAM or
    SDM_FLAG_SCAN_TWO_PHASE it is SDM_ERR_UNSUPPORTED. */
@@ -354,7 +354,7 @@ SDM_API int32_t sdm_forward_noalloc(const sdm_dims* dims, const void* x, const v
  *   and the key-weighted rule's equal the others up to fp32 rounding order.  fp32
  *   state only (SDM_FLAG_STATE_BF16 and SDM_FLAG_STATE_FP8 give
  *   SDM_ERR_UNSUPPORTED).  The key-weighted rule (SDM_FLAG_DELTA_GDN) takes the
- *   schedule sdm_scan would (the chunk one from 256 tokens while B H d_v / 16 <=
+ *   schedule sdm_scan would (the chunk one from 64 tokens while B H d_v / 16 <=
  *   1024) with an fp32 log, else the direct one; with SDM_FLAG_SCAN_STREAM or
  *   _TWO_PHASE it is SDM_ERR_UNSUPPORTED.
  *

@@ -342,10 +342,10 @@ static int32_t check_train_flags(const sdm_dims* d) {
   return SDM_OK;
 }
 
-// Schedule of the training forward as scan flags: a schedule asked for, else from 256
-// tokens the two-phase one (per-slot rule) or the inference scan's choice (key-weighted
-// rule, fp32 log: the chunk one while the walks are few enough), and the direct one
-// below that or for a quantised key-weighted log.
+// Schedule of the training forward as scan flags: a schedule asked for; else for the
+// per-slot rule the two-phase one from 256 tokens and the direct one below; for the
+// key-weighted rule the inference scan's choice with an fp32 log (the chunk one from
+// 64 tokens while the walks are few enough) and the direct one with a quantised log.
 static sdm_dims train_dims(const sdm_dims* d) {
   const int32_t sched = SDM_FLAG_SCAN_DIRECT | SDM_FLAG_SCAN_STREAM | SDM_FLAG_SCAN_TWO_PHASE |
                         SDM_FLAG_SCAN_CHUNK;
@@ -353,12 +353,10 @@ static sdm_dims train_dims(const sdm_dims* d) {
   if (!(d->flags & sched)) {
     const bool gdn = (d->flags & SDM_FLAG_DELTA_GDN) != 0;
     const bool qlog = (d->flags & (SDM_FLAG_LOG_FP8 | SDM_FLAG_LOG_INT4)) != 0;
-    if (d->T < kStreamRound || (gdn && qlog))
-      dd.flags |= SDM_FLAG_SCAN_DIRECT;
-    else if (gdn)  // the inference scan's choice: chunks while the walks are few enough
-      dd.flags |= scan_uses_chunk(*d) ? SDM_FLAG_SCAN_CHUNK : SDM_FLAG_SCAN_DIRECT;
+    if (gdn)
+      dd.flags |= !qlog && scan_uses_chunk(*d) ? SDM_FLAG_SCAN_CHUNK : SDM_FLAG_SCAN_DIRECT;
     else
-      dd.flags |= SDM_FLAG_SCAN_TWO_PHASE;
+      dd.flags |= d->T < kStreamRound ? SDM_FLAG_SCAN_DIRECT : SDM_FLAG_SCAN_TWO_PHASE;
   }
   return dd;
 }

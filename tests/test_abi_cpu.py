@@ -129,7 +129,8 @@ def test_bf16_state_flag_is_accepted_everywhere(lib):
     for extra in (0, _lib.SDM_FLAG_SCAN_DIRECT, _lib.SDM_FLAG_SCAN_STREAM,
                   _lib.SDM_FLAG_SCAN_TWO_PHASE, _lib.SDM_FLAG_DELTA_GDN,
                   _lib.SDM_FLAG_DELTA_GDN | _lib.SDM_FLAG_SCAN_DIRECT):
-        d0, d1 = _d(T=64, flags=extra), _d(T=64, flags=extra | bf)
+        # 32 tokens: the key-weighted rule takes its sliced walk with either storage
+        d0, d1 = _d(T=32, flags=extra), _d(T=32, flags=extra | bf)
         for entry in (_lib.SDM_ENTRY_SELECT, _lib.SDM_ENTRY_SCAN, _lib.SDM_ENTRY_FORWARD):
             assert (lib.sdm_workspace_bytes(ctypes.byref(d1), entry) ==
                     lib.sdm_workspace_bytes(ctypes.byref(d0), entry))
@@ -137,6 +138,12 @@ def test_bf16_state_flag_is_accepted_everywhere(lib):
         assert _select(lib, d1, x=None) == _lib.SDM_ERR_NULL
     d = _d(T=64, flags=bf | _lib.SDM_FLAG_DELTA_GDN | _lib.SDM_FLAG_SCAN_TWO_PHASE)
     assert _select(lib, d) == _lib.SDM_ERR_UNSUPPORTED
+    # from 64 tokens the key-weighted rule's default is the chunk walk, which keeps an
+    # fp32 state: a bf16 state stays on the sliced walk
+    gdn = _lib.SDM_FLAG_DELTA_GDN
+    ws = lambda fl: lib.sdm_workspace_bytes(ctypes.byref(_d(T=64, flags=fl)), _lib.SDM_ENTRY_SCAN)
+    assert ws(gdn | bf) == ws(gdn | bf | _lib.SDM_FLAG_SCAN_DIRECT) != ws(gdn)
+    assert ws(gdn) == ws(gdn | _lib.SDM_FLAG_SCAN_CHUNK)
 
 
 def test_fp8_state_flag(lib):
@@ -191,14 +198,15 @@ def test_training_entries_validate_first(lib):
         ctypes.byref(dd), ctypes.byref(s), None, FAKE, FAKE, y, log, sc, ws, nb, None)
     assert train(dd=_d(T=64, flags=_lib.SDM_FLAG_STATE_BF16), sc=FAKE) == _lib.SDM_ERR_UNSUPPORTED
     # the key-weighted rule trains on the direct and chunk schedules: the chunk one by
-    # default from 256 tokens with an fp32 log (its workspace), else the direct one
+    # default from 64 tokens with an fp32 log (its workspace), else the direct one
     gdn = _lib.SDM_FLAG_DELTA_GDN
     for fl in (_lib.SDM_FLAG_SCAN_STREAM, _lib.SDM_FLAG_SCAN_TWO_PHASE):
         assert train(dd=_d(T=64, flags=gdn | fl)) == _lib.SDM_ERR_UNSUPPORTED
     assert train(dd=_d(T=512, flags=gdn), log=None) == _lib.SDM_ERR_NULL
     ws_of = lambda dd: lib.sdm_workspace_bytes(ctypes.byref(dd), _lib.SDM_ENTRY_SCAN_TRAIN)
     assert ws_of(_d(T=512, flags=gdn)) == ws_of(_d(T=512, flags=gdn | _lib.SDM_FLAG_SCAN_CHUNK)) > 0
-    assert ws_of(_d(T=255, flags=gdn)) == 0
+    assert ws_of(_d(T=64, flags=gdn)) == ws_of(_d(T=64, flags=gdn | _lib.SDM_FLAG_SCAN_CHUNK)) > 0
+    assert ws_of(_d(T=63, flags=gdn)) == 0
     assert ws_of(_d(T=512, flags=gdn | _lib.SDM_FLAG_LOG_INT4)) == \
         ws_of(_d(T=512, flags=gdn | _lib.SDM_FLAG_LOG_INT4 | _lib.SDM_FLAG_SCAN_DIRECT))
     # the direct schedule needs no workspace; the stream schedule (an fp32 log from 256
@@ -267,7 +275,7 @@ def test_training_entries_validate_first(lib):
     # its inference walk keeps the raw read vectors for the norm pass (8 slices)
     assert lib.sdm_workspace_bytes(ctypes.byref(dg8), _lib.SDM_ENTRY_SCAN) >= \
         dg8.B * dg8.T * dg8.H * 128 * 4
-    assert lib.sdm_workspace_bytes(ctypes.byref(_d(T=64, flags=_lib.SDM_FLAG_DELTA_GDN)),
+    assert lib.sdm_workspace_bytes(ctypes.byref(_d(T=63, flags=_lib.SDM_FLAG_DELTA_GDN)),
                                    _lib.SDM_ENTRY_SCAN) == 0
     assert back(grads=_lib.SdmScanGrads(*([FAKE] * 5 + [None, None]))) == _lib.SDM_ERR_NULL
     assert back(ws=None) == _lib.SDM_ERR_WORKSPACE
@@ -417,11 +425,11 @@ def test_chunk_schedule_flag(lib):
     assert need >= th * (2 * d.W + d.R + d.d_v) * 4 + d.B * d.H * 4 * 32 * 32 * 4
     assert lib.sdm_workspace_bytes(ctypes.byref(d), _lib.SDM_ENTRY_FORWARD) > need
     # the key-weighted rule adds the solve's matrices; it takes the schedule by default
-    # from 256 tokens with an fp32 state, and not with a bf16 one or the direct flag
+    # from 64 tokens with an fp32 state, and not with a bf16 one or the direct flag
     dg = _d(T=100, flags=chunk | gdn)
     assert lib.sdm_workspace_bytes(ctypes.byref(dg), _lib.SDM_ENTRY_SCAN) > need
-    assert lib.sdm_workspace_bytes(ctypes.byref(_d(T=256, flags=gdn)), _lib.SDM_ENTRY_SCAN) > 0
-    assert lib.sdm_workspace_bytes(ctypes.byref(_d(T=255, flags=gdn)), _lib.SDM_ENTRY_SCAN) == 0
+    assert lib.sdm_workspace_bytes(ctypes.byref(_d(T=64, flags=gdn)), _lib.SDM_ENTRY_SCAN) > 0
+    assert lib.sdm_workspace_bytes(ctypes.byref(_d(T=63, flags=gdn)), _lib.SDM_ENTRY_SCAN) == 0
     for fl in (gdn | _lib.SDM_FLAG_SCAN_DIRECT, gdn | _lib.SDM_FLAG_STATE_BF16):
         assert lib.sdm_workspace_bytes(ctypes.byref(_d(T=512, flags=fl)), _lib.SDM_ENTRY_SCAN) == 0
     s = _sel()

@@ -1,8 +1,8 @@
 """Training of the key-weighted (GDN-form) write rule: sdm_scan_train and
-sdm_scan_backward with SDM_FLAG_DELTA_GDN against the oracle.  Both walks take the
-chunk schedule from 256 tokens with an fp32 log (the reverse walk with W, R <= 64;
-tests/test_gpu_chunk_backward.py covers it on its own), else the direct schedule split
-over column slices of the state.  The cases cover both slice widths (16 and 32
+sdm_scan_backward with SDM_FLAG_DELTA_GDN against the oracle.  With an fp32 log the
+training forward takes the chunk schedule from 64 tokens and the reverse walk from 256
+(with W, R <= 64; tests/test_gpu_chunk_backward.py covers it on its own), while the
+walks are few enough; else the direct schedule split over column slices of the state.  The cases cover both slice widths (16 and 32
 columns), one slice per walk (norm and gate inside the walk) and several.
 
 * The training forward gives state, y and out bit-identical to the inference scan of
@@ -81,9 +81,11 @@ def test_gdn_training_matches_oracle(B, T, H, n, W, R, d_v, mode, logfl):
     gam = to_dev(gamma)
     state = to_dev(m0)
     out, y, log = ops.scan_train(d, pd, gam, state)
-    # the inference scan of the same rule on the same schedule (the chunk one from 256
-    # tokens with an fp32 log, else the direct one): identical results
-    sched = (_lib.SDM_FLAG_SCAN_CHUNK if T >= 256 and not logfl else _lib.SDM_FLAG_SCAN_DIRECT)
+    # the inference scan of the same rule on the same schedule (the chunk one from 64
+    # tokens with an fp32 log while B H d_v / 16 <= 1024, else the direct one): identical
+    # results
+    chunked = T >= 64 and not logfl and B * H * (d_v // 16) <= 1024
+    sched = _lib.SDM_FLAG_SCAN_CHUNK if chunked else _lib.SDM_FLAG_SCAN_DIRECT
     st_i = to_dev(m0)
     out_i, y_i = ops.scan(_dims(B=B, T=T, H=H, n=n, W=W, R=R, d_v=d_v, flags=GDN | sched), pd,
                           gam, st_i, with_y_raw=True)
