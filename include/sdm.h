@@ -90,8 +90,8 @@ extern "C" {
 #define SDM_FLAG_SCAN_TWO_PHASE 4 /* slot-owner writes, then token-major reads of the
                                      slots each workgroup owns */
 /* Without a schedule flag, sdm_scan and sdm_forward run the per-slot rule on the
-   two-phase schedule from 16 tokens, and on the direct one below that or from 1024
-   walks (B H: the lock-step workgroups then fill the chip several times over). */
+   two-phase schedule from 16 tokens, and on the direct one below that or from 512
+   walks (B H: the lock-step workgroups then fill the chip twice over). */
 /* instrumentation flag (sdm_dims.flags, may be combined with one schedule flag):
    every kernel launch of the call is bracketed by a pair of HIP events recorded on
    the call's stream; sdm_timing_read returns the durations.  Results are the same
@@ -343,7 +343,8 @@ SDM_API int32_t sdm_forward_noalloc(const sdm_dims* dims, const void* x, const v
  *           if 0)
  *   Schedules: a schedule flag picks one (SDM_FLAG_SCAN_DIRECT, _STREAM, _TWO_PHASE
  *   or _CHUNK, the last with an fp32 log only); without one, the per-slot rule takes
- *   the two-phase schedule from 256 tokens and the direct one below.  On the
+ *   the two-phase schedule from 256 tokens and the direct one below that or from 512
+ *   walks (B H).  On the
  *   slot-owner (stream, two-phase) schedules, and for the key-weighted rule on the
  *   direct one, a quantised log is staged in fp32 in the workspace (token chunks
  *   bounded near 2 GiB, and 256 MiB) and encoded after each chunk's walk.  State,

@@ -174,11 +174,7 @@ hipError_t launch_direct(dim3 grid, hipStream_t s, const ScanArgs& a) {
 }  // namespace
 
 // The slot-owner schedules from 16 tokens, unless the walks alone fill the chip
-// several times over (B H >= 1024: four lock-step workgroups per CU).  Then the direct
-// walk, which needs no bucketing passes and no per-part partial reads, is faster:
-// 1024 walks take 1.33 vs 1.50 ms at 64 tokens and 5.21 vs 5.58 ms at 256, while
-// 256 walks take 0.51 vs 0.41 ms and 1.95 vs 1.48 ms.
-constexpr int64_t kDirectWalks = 1024;
+// (kDirectWalks): then the direct walk is faster.
 bool scan_uses_stream(const sdm_dims& d) {
   if (d.flags & (SDM_FLAG_SCAN_DIRECT | SDM_FLAG_DELTA_GDN | SDM_FLAG_SCAN_CHUNK)) return false;
   if (d.flags & (SDM_FLAG_SCAN_STREAM | SDM_FLAG_SCAN_TWO_PHASE)) return true;

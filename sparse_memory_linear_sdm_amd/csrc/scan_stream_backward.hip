@@ -574,13 +574,11 @@ hipError_t launch_gamma_blocks(const ScanBackArgs& sa, const float* gpart, float
 // The backward has one slot-owner schedule: SDM_FLAG_SCAN_STREAM and
 // SDM_FLAG_SCAN_TWO_PHASE both select it.
 // The slot-owner reverse walk from ROUND tokens, unless the walks alone fill the chip
-// (B H >= 512): then one lock-step workgroup per walk is faster (512 walks x 512
-// tokens: 11.3 vs 13.2 ms; 1024 x 256: 11.9 vs 13.0 ms; but 256 x 512: 8.4 vs 6.6 ms).
-constexpr int64_t kBackDirectWalks = 512;
+// (kDirectWalks): then one lock-step workgroup per walk is faster.
 bool backward_uses_stream(const sdm_dims& d) {
   if (d.flags & SDM_FLAG_SCAN_DIRECT) return false;
   if (d.flags & (SDM_FLAG_SCAN_STREAM | SDM_FLAG_SCAN_TWO_PHASE)) return true;
-  return d.T >= ROUND && d.B * d.H < kBackDirectWalks;
+  return d.T >= ROUND && d.B * d.H < kDirectWalks;
 }
 
 size_t stream_backward_workspace_bytes(const sdm_dims& d) {

@@ -343,9 +343,10 @@ static int32_t check_train_flags(const sdm_dims* d) {
 }
 
 // Schedule of the training forward as scan flags: a schedule asked for; else for the
-// per-slot rule the two-phase one from 256 tokens and the direct one below; for the
-// key-weighted rule the inference scan's choice with an fp32 log (the chunk one from
-// 64 tokens while the walks are few enough) and the direct one with a quantised log.
+// per-slot rule the two-phase one from 256 tokens and the direct one below that or from
+// kDirectWalks walks; for the key-weighted rule the inference scan's choice with an
+// fp32 log (the chunk one from 64 tokens while the walks are few enough) and the
+// direct one with a quantised log.
 static sdm_dims train_dims(const sdm_dims* d) {
   const int32_t sched = SDM_FLAG_SCAN_DIRECT | SDM_FLAG_SCAN_STREAM | SDM_FLAG_SCAN_TWO_PHASE |
                         SDM_FLAG_SCAN_CHUNK;
@@ -356,7 +357,8 @@ static sdm_dims train_dims(const sdm_dims* d) {
     if (gdn)
       dd.flags |= !qlog && scan_uses_chunk(*d) ? SDM_FLAG_SCAN_CHUNK : SDM_FLAG_SCAN_DIRECT;
     else
-      dd.flags |= d->T < kStreamRound ? SDM_FLAG_SCAN_DIRECT : SDM_FLAG_SCAN_TWO_PHASE;
+      dd.flags |= d->T < kStreamRound || d->B * d->H >= kDirectWalks ? SDM_FLAG_SCAN_DIRECT
+                                                                      : SDM_FLAG_SCAN_TWO_PHASE;
   }
   return dd;
 }

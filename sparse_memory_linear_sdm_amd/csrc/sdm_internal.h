@@ -122,6 +122,12 @@ struct StreamArgs {
 // hashed over.
 constexpr int kStreamRound = 256;
 constexpr int kStreamMaxGT = 4096;
+// Walks (B H) from which the per-slot rule's lock-step walks, one workgroup per walk,
+// fill the chip twice over and beat the slot-owner schedules by default (no bucketing
+// passes, no per-part partial reads): 512 walks x 512 tokens, training forward 7.28 vs
+// 7.76 ms and reverse walk 11.3 vs 13.2 ms; 1024 walks x 64 tokens, scan 1.33 vs
+// 1.50 ms; but 256 walks x 512 tokens 4.76 vs 3.91 ms and 8.4 vs 6.6 ms.
+constexpr int64_t kDirectWalks = 512;
 
 // Lane `src` of a 16-lane row to the whole row (DPP row_newbcast, gfx90a and later).
 template <int SRC>

@@ -343,12 +343,16 @@ def test_empty_calls_are_noops(lib):
 
 def test_default_scan_schedule_by_walks(lib):
     # the per-slot rule's slot-owner schedules (with their bucketing workspace) from 16
-    # tokens, the direct one (no workspace) below that or from 1024 walks
+    # tokens, the direct one (no workspace) below that or from 512 walks; the training
+    # forward's two-phase one from 256 tokens below 512 walks
     ws = lambda **kw: lib.sdm_workspace_bytes(ctypes.byref(_d(**kw)), _lib.SDM_ENTRY_SCAN)
-    assert ws(B=128, H=4, T=64) > 0 and ws(B=256, H=2, T=64) > 0
-    assert ws(B=256, H=4, T=64) == 0 and ws(B=512, H=4, T=512) == 0
+    assert ws(B=64, H=4, T=64) > 0 and ws(B=255, H=2, T=64) > 0
+    assert ws(B=128, H=4, T=64) == 0 and ws(B=512, H=4, T=512) == 0
     assert ws(B=256, H=4, T=64, flags=_lib.SDM_FLAG_SCAN_TWO_PHASE) > 0
     assert ws(B=2, H=2, T=15) == 0
+    tw = lambda **kw: lib.sdm_workspace_bytes(ctypes.byref(_d(**kw)), _lib.SDM_ENTRY_SCAN_TRAIN)
+    assert tw(B=64, H=4, T=256) > 0
+    assert tw(B=128, H=4, T=256) == 0
 
 
 def test_default_backward_schedule_by_walks(lib):
